@@ -1,0 +1,137 @@
+"""Pins of the oracle's per-channel codebook quantizer (LowRA page, sections
+3 and 4.1) and weighted Lloyd-Max learner (section 5)."""
+import math
+
+import numpy as np
+
+from oracle import codebook, lloyd, nf4
+
+
+def test_four_bit_with_nf4_tables_equals_nf4():
+    rng = np.random.default_rng(0)
+    N, K = 6, 192
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    T = np.tile(nf4.thresholds(), (N, 1))
+    packed, c, codes = codebook.quantize(W, np.full(N, 4), T)
+    p_nf4, c_nf4 = nf4.quantize(W)
+    assert np.array_equal(c, c_nf4)
+    assert np.array_equal(codes.reshape(-1), nf4.unpack_nibbles(p_nf4))
+    L = np.tile(nf4.levels(), (N, 1))
+    assert np.array_equal(codebook.dequant(packed, np.full(N, 4), L, c, N, K),
+                          nf4.dequant(p_nf4, c, (N, K)))
+
+
+def test_one_bit_threshold_zero_is_sign():
+    rng = np.random.default_rng(1)
+    W = (rng.standard_normal((3, 128))).astype(np.float32)
+    W[0, 3] = 0.0
+    T = np.full((3, 15), 3.0, dtype=np.float32); T[:, 0] = 0.0
+    packed, c, codes = codebook.quantize(W, np.ones(3), T)
+    assert np.array_equal(codes, (W > 0).astype(np.uint8))
+    assert packed.size == 3 * 128 // 8
+
+
+def test_bit_plane_layout_by_hand():
+    # one 64-block at 3 bits: element e has code e % 8 -> plane p bit e = bit p of e
+    codes = (np.arange(64) % 8).astype(np.uint8)
+    b = codebook.pack_planes(codes, 3)
+    assert b.size == 24
+    words = b.view("<u8")
+    for p in range(3):
+        want = sum(1 << e for e in range(64) if (e % 8) >> p & 1)
+        assert int(words[p]) == want
+    assert np.array_equal(codebook.unpack_planes(b, 3, 64), codes)
+
+
+def test_codes_bruteforce_with_random_thresholds():
+    rng = np.random.default_rng(2)
+    N, K = 8, 128
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bits = np.array([1, 2, 3, 4, 4, 3, 2, 1])
+    T = np.full((N, 15), 3.0, dtype=np.float32)
+    for i, b in enumerate(bits):
+        T[i, :(1 << b) - 1] = np.sort(rng.uniform(-1, 1, (1 << b) - 1)).astype(np.float32)
+    packed, c, codes = codebook.quantize(W, bits, T)
+    off = codebook.row_offsets(bits, K)
+    assert off[-1] == sum(K * b // 8 for b in bits)
+    for i in range(N):
+        for k in range(K):
+            cj = c[(i * K + k) // 64]
+            x = np.float32(W[i, k] / cj)
+            # scan: the bin whose left edge is the last threshold below x
+            code = 0
+            for m in range((1 << bits[i]) - 1):
+                if x > T[i, m]:
+                    code = m + 1
+            assert codes[i, k] == code
+        assert np.array_equal(codebook.unpack_planes(packed[off[i]:off[i + 1]], bits[i], K), codes[i])
+
+
+def _data(rng, R=4, K=512):
+    x = np.clip(rng.standard_normal((R, K)) / 2.5, -1, 1)
+    w = np.repeat(rng.uniform(0.5, 2.0, (R, K // 64)), 64, axis=1)
+    return x, w
+
+
+def test_lloyd_mse_non_increasing_and_stops():
+    rng = np.random.default_rng(3)
+    x, w = _data(rng)
+    for b in (1, 2, 3, 4):
+        hist = []
+        L, T, it = lloyd.learn(x, w, b, history=hist)
+        per_row = {i: [] for i in range(x.shape[0])}
+        for rows, mse in hist:
+            for i, m in zip(rows, mse):
+                per_row[i].append(m)
+        for i, ms in per_row.items():
+            # every accepted step decreased the MSE; the last one did not
+            assert all(ms[j + 1] < ms[j] for j in range(len(ms) - 2))
+            assert len(ms) == lloyd.MAX_ITERS or ms[-1] >= ms[-2]
+        assert np.all(np.diff(L, axis=1) > 0)
+
+
+def test_lloyd_step_levels_are_weighted_centroids_and_midpoints():
+    rng = np.random.default_rng(4)
+    x, w = _data(rng, R=2, K=256)
+    T0 = np.tile(lloyd.init_thresholds(2), (2, 1))
+    L0 = np.tile(lloyd.init_levels(2), (2, 1))
+    L, T1, mse = lloyd.lloyd_step(x, w, T0, L0)
+    for i in range(2):
+        for k in range(4):
+            lo = -np.inf if k == 0 else T0[i, k - 1]
+            hi = np.inf if k == 3 else T0[i, k]
+            sel = (x[i] > lo) & (x[i] <= hi)
+            num = math.fsum(w[i, sel] * x[i, sel])
+            den = math.fsum(w[i, sel])
+            assert abs(L[i, k] - num / den) < 1e-12
+        assert np.allclose(T1[i], (L[i, :-1] + L[i, 1:]) / 2, rtol=0, atol=0)
+
+
+def test_lloyd_two_clusters_closed_form():
+    # 1 bit, data at two points with weights: the centroids are the points
+    x = np.array([[-0.5] * 64 + [0.25] * 64])
+    w = np.ones_like(x)
+    L, T, it = lloyd.learn(x, w, 1)
+    assert np.allclose(L, [[-0.5, 0.25]]) and np.allclose(T, [[-0.125]])
+
+
+def test_nf_init_tables():
+    # the initial tables follow the NF construction at 2, 3 and 4 bits
+    assert np.array_equal(lloyd.init_levels(4).astype(np.float32), nf4.levels())
+    for b in (2, 3):
+        L = lloyd.init_levels(b)
+        assert L.size == 1 << b and L[0] == -1 and L[-1] == 1 and 0.0 in L
+        assert np.all(np.diff(L) > 0)
+    assert np.array_equal(lloyd.init_thresholds(1), [0.0])
+
+
+def test_learn_codebooks_outputs_valid_tables():
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    bits = np.array([1, 2, 3, 4, 1, 2, 3, 4])
+    L, T = lloyd.learn_codebooks(W, bits)
+    for i, b in enumerate(bits):
+        n = 1 << b
+        assert np.all(np.diff(L[i, :n]) > 0)
+        assert np.all(np.diff(T[i, :n - 1]) > 0)
+        assert np.all(T[i, :n - 1] >= L[i, :n - 1]) and np.all(T[i, :n - 1] < L[i, 1:n])
