@@ -1,0 +1,247 @@
+/*
+ * lq.h -- C ABI of the MI355X (gfx950) quantized-LoRA hot path.
+ *
+ * The operations follow these pages:
+ *   [QLoRA]  Heng's Blog, "QLoRA: Efficient Finetuning of Quantized LLMs":
+ *            the layer equation (introduction), NF4 (section "Contribution 1:
+ *            4-bit NormalFloat (NF4)"), double quantization (section
+ *            "Contribution 2: Double Quantization").
+ *   [LowRA]  cloud.tencent.com.cn write-up of LowRA: per-output-channel
+ *            quantization with custom thresholds and a given precision
+ *            (section 3, workflow; section 4.1 and figure 3).
+ *
+ * Conventions (every entry point):
+ *   - Tensors are dense row-major. W is [N, K] (out x in, the Linear
+ *     convention), X is [M, K], A is [r, K], B is [N, r], H and G are [M, N].
+ *   - All tensor pointers are DEVICE pointers allocated and owned by the
+ *     caller. The library never allocates or frees device memory and holds no
+ *     mutable global state; it is safe to call from several host threads.
+ *   - Scratch memory is a caller-provided device workspace whose size comes
+ *     from the matching *_workspace() query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Every call is asynchronous on that stream and never synchronizes.
+ *   - bfloat16 data is passed as uint16_t bit patterns.
+ *   - Every call returns an lq_status. Arguments are validated before anything
+ *     is launched; on an error nothing is launched and outputs are untouched.
+ *     No C++ exception crosses this boundary.
+ *   - Preconditions not checked: inputs are finite; codebook thresholds are
+ *     strictly increasing per row; device pointers are valid and large enough
+ *     for the stated sizes. Violations give undefined results.
+ */
+#ifndef LQ_H
+#define LQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum lq_status {
+  LQ_OK = 0,
+  LQ_ERR_ARG = -1,          /* null pointer, bad enum value */
+  LQ_ERR_SHAPE = -2,        /* K % 64 != 0, r outside [1, 128], sizes <= 0 */
+  LQ_ERR_UNSUPPORTED = -3,  /* blocksize != 64, dq blocksize != 256, dtype */
+  LQ_ERR_WORKSPACE = -4,    /* workspace missing or too small */
+  LQ_ERR_LAUNCH = -5        /* the HIP runtime reported an error at launch */
+};
+
+/* ---- element types ----------------------------------------------------- */
+enum lq_dtype { LQ_F32 = 0, LQ_BF16 = 1, LQ_F16 = 2 };
+
+/* ---- quantized weight formats ------------------------------------------ */
+enum lq_format {
+  LQ_FMT_NF4 = 0,       /* 4-bit NF4 codes, two per byte, high nibble first */
+  LQ_FMT_CODEBOOK = 1   /* per-row b-bit codes as bit-planes (see below) */
+};
+
+/*
+ * Descriptor of a quantized frozen weight W [N, K] (plain pointers, no
+ * ownership). The 64-element quantization blocks run along K, so block j of
+ * row i covers W[i, 64j .. 64j+63] and its flat index is i*(K/64) + j.
+ *
+ * Block constants, one of:
+ *   absmax != NULL : float32 constant per block [N*K/64];
+ *   absmax == NULL : double-quantized constants -- absmax_q [N*K/64] (OCP
+ *                    E4M3 codes), dq_scale [ceil(N*K/64 / 256)] float32 and
+ *                    dq_mean [1] float32; the constant of block j is
+ *                    fma(E4M3(absmax_q[j]), dq_scale[j / 256], dq_mean[0]).
+ *
+ * LQ_FMT_NF4: codes [N*K/2] bytes; byte e/2 holds flat element e (even) in
+ *   bits 7..4 and element e+1 in bits 3..0.
+ * LQ_FMT_CODEBOOK: row i has row_bits[i] = b in {1,2,3,4}; its bytes start at
+ *   codes + row_offset[i] (row_offset[N+1], row_offset[0] = 0,
+ *   row_offset[i+1] - row_offset[i] = K*b/8). Each 64-block of the row is b
+ *   little-endian uint64 bit-planes; bit e of plane p is bit p of the code of
+ *   the block's element e. levels [N, 16] float32 holds the row's mapping
+ *   (first 2^b entries used); the dequantized weight is
+ *   bfloat16(float32(levels[i, code] * constant)).
+ */
+typedef struct lq_qweight {
+  int32_t format;          /* lq_format */
+  int32_t blocksize;       /* must be 64 */
+  int64_t N;
+  int64_t K;
+  const uint8_t* codes;
+  const float* absmax;
+  const uint8_t* absmax_q;
+  const float* dq_scale;
+  const float* dq_mean;
+  int32_t dq_blocksize;    /* must be 256 when double quantized */
+  int32_t reserved0;       /* set to 0 */
+  const uint8_t* row_bits;   /* LQ_FMT_CODEBOOK only */
+  const int64_t* row_offset; /* LQ_FMT_CODEBOOK only */
+  const float* levels;       /* LQ_FMT_CODEBOOK only */
+} lq_qweight;
+
+/* Storage of one quantized [N, K] weight ([QLoRA] Contribution 2). */
+typedef struct lq_sizes_t {
+  int64_t n;                    /* N*K */
+  int64_t n_blocks;             /* N*K/64 */
+  int64_t n_dq_blocks;          /* ceil(n_blocks/256) */
+  int64_t code_bytes;           /* N*K*bits/8 (NF4: bits = 4) */
+  int64_t dq_const_bytes;       /* n_blocks + 4*n_dq_blocks + 4 */
+  int64_t fp32_const_bytes;     /* 4*n_blocks */
+  double const_bits_per_param_dq;   /* 8/64 + 32/(64*256) = 0.126953125 */
+  double const_bits_per_param_fp32; /* 32/64 = 0.5 */
+} lq_sizes_t;
+
+/* Static description of a status code. Never NULL. */
+const char* lq_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int lq_version(void);
+
+/*
+ * Host-side NF4 tables ([QLoRA] Contribution 1). levels[16]: the 16 NF4 values
+ * in ascending order, float32 (q0 = -1, q7 = +0, q15 = +1): 8 negative-half and
+ * 9 positive-half standard-normal quantiles at equal probability steps from
+ * 1/2 to delta = 1 - (1/32 + 1/30)/2, scaled by 1/Phi^-1(delta), duplicate 0
+ * dropped. thresholds[15]: t_i = largest float32 <= (q_i + q_{i+1})/2, so that
+ * code = #{i : x > t_i} is the nearest level with ties to the lower index.
+ * Either pointer may be NULL. Pure host function; needs no GPU.
+ */
+int lq_nf4_table(float* levels, float* thresholds);
+
+/*
+ * Size arithmetic for an [N, K] weight quantized at `bits` bits per weight
+ * (4 for NF4; 1..4 for a uniform codebook). Pure host function.
+ * LQ_ERR_SHAPE if N <= 0, K <= 0 or K % 64 != 0; LQ_ERR_ARG if out is NULL or
+ * bits is outside 1..4.
+ */
+int lq_sizes(int64_t N, int64_t K, int32_t bits, lq_sizes_t* out);
+
+/*
+ * Blockwise NF4 quantization ([QLoRA] Contribution 1): for each 64-block j,
+ * absmax[j] = max |w| (float32); x = w / absmax[j] (IEEE float32 division,
+ * x = +0 for an all-zero block); code = #{i : x > t_i}; codes packed two per
+ * byte as described for LQ_FMT_NF4.
+ *   W        [N, K] of `dtype` (LQ_F32, LQ_BF16 or LQ_F16; bf16/f16 are widened
+ *            exactly to float32 first)
+ *   codes    [N*K/2] bytes, written
+ *   absmax   [N*K/64] float32, written
+ * Errors: LQ_ERR_ARG (null pointer, bad dtype), LQ_ERR_SHAPE (N, K <= 0,
+ * K % 64 != 0), LQ_ERR_UNSUPPORTED (blocksize != 64), LQ_ERR_LAUNCH.
+ */
+int lq_quantize_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                    uint8_t* codes, float* absmax, void* stream);
+
+/* Workspace bytes for lq_double_quant (float64 partial sums). */
+size_t lq_double_quant_workspace(int64_t n_blocks, int32_t dq_blocksize);
+
+/*
+ * Double quantization of the block constants ([QLoRA] Contribution 2): the
+ * mean mu of all n_blocks constants (float64 sum as a fixed binary tree --
+ * pairwise within each 256-constant block, then pairwise over the block sums
+ * padded with zeros to a power of two -- divided by n_blocks, rounded to
+ * float32) is subtracted; for each 256-block J, a2 = max |c - mu|,
+ * dq_scale[J] = a2 / 448 (float32), and each constant is stored as the OCP
+ * E4M3 code (round to nearest even) of clamp((c - mu) / dq_scale[J], -448, 448)
+ * (code 0 when dq_scale[J] == 0). The last block may be partial.
+ *   absmax    [n_blocks] float32, read
+ *   absmax_q  [n_blocks] E4M3 codes, written
+ *   dq_scale  [ceil(n_blocks/256)] float32, written
+ *   dq_mean   [1] float32, written
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (n_blocks <= 0), LQ_ERR_UNSUPPORTED
+ * (dq_blocksize != 256), LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_double_quant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
+                    uint8_t* absmax_q, float* dq_scale, float* dq_mean,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantization to bfloat16 ([QLoRA] introduction: dequantized to BFloat16 at
+ * use time): out[i, k] = bfloat16_rne(float32(level(code) * constant)).
+ *   w    quantized weight descriptor (NF4 or codebook)
+ *   out  [N, K] bfloat16, written
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_LAUNCH.
+ */
+int lq_dequant(const lq_qweight* w, uint16_t* out, void* stream);
+
+/* Workspace bytes for lq_qlora_forward with M tokens and rank r. */
+size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
+
+/*
+ * QLoRA forward ([QLoRA] introduction): with W' the bfloat16 dequantized
+ * weight and s = alpha / r,
+ *     t = X A^T            (float32, [M, r])
+ *     H = X W'^T + s t B^T (float32 accumulation, stored as h_dtype)
+ * W' is never materialised in memory: packed codes are dequantized inside the
+ * GEMM. M <= 16 uses the memory-bound GEMV kernel, larger M the MFMA GEMM.
+ *   X  [M, K] bf16;  A [r, K] bf16;  B [N, r] bf16
+ *   H  [M, N] of h_dtype (LQ_BF16 or LQ_F32), written
+ *   t_save [M, r] float32, written if not NULL (for the backward)
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (M <= 0, r outside [1, 128]),
+ * LQ_ERR_UNSUPPORTED (h_dtype), LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                     void* H, int32_t h_dtype, float* t_save,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for lq_qlora_backward with M tokens and rank r. */
+size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
+
+/*
+ * QLoRA backward ([QLoRA] introduction: gradients flow through the frozen
+ * 4-bit base into the adapter; W gets none). With G = dL/dH and s = alpha/r:
+ *     u      = G B               (float32 [M, r], internal)
+ *     dB     = s G^T t           [N, r] float32
+ *     grad_X = G W' + s u A      [M, K] bf16
+ *     dA     = s u^T X           [r, K] float32
+ *   G [M, N] bf16; X [M, K] bf16 (needed for dA and when t_saved is NULL)
+ *   t_saved [M, r] float32 from the forward, or NULL to recompute t = X A^T
+ *   grad_X, dA, dB may each be NULL to skip that output.
+ * Errors: as lq_qlora_forward.
+ */
+int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,
+                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                      const float* t_saved, uint16_t* grad_X, float* dA, float* dB,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Per-output-channel codebook quantization ([LowRA] section 3: a quantization
+ * kernel with custom thresholds and a given precision per output channel;
+ * section 4.1: groups of 64 scaled by their absmax). For row i with
+ * b = row_bits[i]: absmax and x as in lq_quantize_nf4; code = #{k < 2^b - 1 :
+ * x > thresholds[i, k]}; packed as bit-planes as described for
+ * LQ_FMT_CODEBOOK.
+ *   W           [N, K] of dtype
+ *   row_bits    [N] uint8 in {1, 2, 3, 4}
+ *   row_offset  [N + 1] int64 byte offsets (prefix sums of K*b/8)
+ *   thresholds  [N, 15] float32, first 2^b - 1 of each row used, increasing
+ *   codes       [row_offset[N]] bytes, written
+ *   absmax      [N*K/64] float32, written
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_LAUNCH.
+ */
+int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                         const uint8_t* row_bits, const int64_t* row_offset,
+                         const float* thresholds, uint8_t* codes, float* absmax, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LQ_H */

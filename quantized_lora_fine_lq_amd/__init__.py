@@ -1,0 +1,273 @@
+"""Python binding of liblq.so, the gfx950 quantized-LoRA hot path (include/lq.h).
+
+Two layers, both argument marshalling only:
+
+* ``lib`` -- the ctypes handle; ``lib.lq_quantize_nf4(...)`` etc. take raw
+  device pointers exactly as declared in include/lq.h;
+* tensor helpers (``quantize_nf4``, ``double_quant``, ``QWeight``,
+  ``dequant``, ``qlora_forward``, ``qlora_backward``, ``quantize_codebook``)
+  that allocate outputs and workspaces with PyTorch (device memory and the
+  current stream are the only things taken from PyTorch) and call the same
+  entry points. All arithmetic runs in the library's HIP kernels.
+
+Importing fails loudly if liblq.so has not been built
+(``python -m quantized_lora_fine_lq_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "liblq.so")
+
+LQ_OK, LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+LQ_F32, LQ_BF16, LQ_F16 = 0, 1, 2
+LQ_FMT_NF4, LQ_FMT_CODEBOOK = 0, 1
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class lq_qweight(ctypes.Structure):
+    _fields_ = [
+        ("format", c_i32), ("blocksize", c_i32), ("N", c_i64), ("K", c_i64),
+        ("codes", c_vp), ("absmax", c_vp), ("absmax_q", c_vp), ("dq_scale", c_vp),
+        ("dq_mean", c_vp), ("dq_blocksize", c_i32), ("reserved0", c_i32),
+        ("row_bits", c_vp), ("row_offset", c_vp), ("levels", c_vp),
+    ]
+
+
+class lq_sizes_t(ctypes.Structure):
+    _fields_ = [
+        ("n", c_i64), ("n_blocks", c_i64), ("n_dq_blocks", c_i64), ("code_bytes", c_i64),
+        ("dq_const_bytes", c_i64), ("fp32_const_bytes", c_i64),
+        ("const_bits_per_param_dq", ctypes.c_double), ("const_bits_per_param_fp32", ctypes.c_double),
+    ]
+
+
+QW_P = ctypes.POINTER(lq_qweight)
+
+# name -> (restype, argtypes); the full export list of include/lq.h
+SIGNATURES = {
+    "lq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lq_version": (ctypes.c_int, []),
+    "lq_nf4_table": (ctypes.c_int, [c_vp, c_vp]),
+    "lq_sizes": (ctypes.c_int, [c_i64, c_i64, c_i32, ctypes.POINTER(lq_sizes_t)]),
+    "lq_quantize_nf4": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
+    "lq_double_quant_workspace": (c_sz, [c_i64, c_i32]),
+    "lq_double_quant": (ctypes.c_int, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lq_dequant": (ctypes.c_int, [QW_P, c_vp, c_vp]),
+    "lq_forward_workspace": (c_sz, [QW_P, c_i64, c_i32]),
+    "lq_qlora_forward": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_i32,
+                                        c_vp, c_vp, c_sz, c_vp]),
+    "lq_backward_workspace": (c_sz, [QW_P, c_i64, c_i32]),
+    "lq_qlora_backward": (ctypes.c_int, [QW_P, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp,
+                                         c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lq_quantize_codebook": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
+                                            c_vp, c_vp, c_vp]),
+}
+
+
+class LqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status} ({status_string(status)})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_lora_fine_lq_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.lq_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != LQ_OK:
+        raise LqError(status, where)
+
+
+def nf4_table():
+    """(levels[16], thresholds[15]) as Python float lists (host call)."""
+    lv = (ctypes.c_float * 16)()
+    th = (ctypes.c_float * 15)()
+    _check(lib.lq_nf4_table(ctypes.cast(lv, c_vp), ctypes.cast(th, c_vp)), "lq_nf4_table")
+    return list(lv), list(th)
+
+
+def sizes(N: int, K: int, bits: int = 4) -> dict:
+    out = lq_sizes_t()
+    _check(lib.lq_sizes(N, K, bits, ctypes.byref(out)), "lq_sizes")
+    return {f: getattr(out, f) for f, _ in lq_sizes_t._fields_}
+
+
+# ---------------------------------------------------------------------------
+# tensor helpers (PyTorch provides memory and the stream only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev=None):
+    torch = _torch()
+    return c_vp(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t) -> c_vp:
+    return c_vp(t.data_ptr()) if t is not None else c_vp(None)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: LQ_F32, torch.bfloat16: LQ_BF16, torch.float16: LQ_F16}[t.dtype]
+
+
+def _contig_cuda(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return t
+
+
+def quantize_nf4(W, blocksize: int = 64):
+    """W [N, K] (f32/bf16/f16) -> (codes uint8 [N*K/2], absmax f32 [N*K/64])."""
+    torch = _torch()
+    _contig_cuda(W, "W")
+    N, K = W.shape
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=W.device)
+    absmax = torch.empty(max(N * K // blocksize, 1), dtype=torch.float32, device=W.device)
+    _check(lib.lq_quantize_nf4(_ptr(W), _dtype_code(W), N, K, blocksize, _ptr(codes), _ptr(absmax),
+                               _stream(W.device)), "lq_quantize_nf4")
+    return codes, absmax
+
+
+def double_quant(absmax, dq_blocksize: int = 256):
+    """absmax f32 [n_b] -> (absmax_q uint8 [n_b], dq_scale f32 [n_d], dq_mean f32 [1])."""
+    torch = _torch()
+    _contig_cuda(absmax, "absmax")
+    n_b = absmax.numel()
+    n_d = (n_b + dq_blocksize - 1) // dq_blocksize
+    q = torch.empty(n_b, dtype=torch.uint8, device=absmax.device)
+    s2 = torch.empty(n_d, dtype=torch.float32, device=absmax.device)
+    mu = torch.empty(1, dtype=torch.float32, device=absmax.device)
+    ws_bytes = lib.lq_double_quant_workspace(n_b, dq_blocksize)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=absmax.device)
+    _check(lib.lq_double_quant(_ptr(absmax), n_b, dq_blocksize, _ptr(q), _ptr(s2), _ptr(mu), _ptr(ws),
+                               ws_bytes, _stream(absmax.device)), "lq_double_quant")
+    return q, s2, mu
+
+
+class QWeight:
+    """A quantized frozen weight: device tensors plus the lq_qweight view."""
+
+    def __init__(self, N: int, K: int, codes, absmax=None, absmax_q=None, dq_scale=None,
+                 dq_mean=None, fmt: int = LQ_FMT_NF4, row_bits=None, row_offset=None, levels=None):
+        self.N, self.K, self.fmt = N, K, fmt
+        self.codes, self.absmax = codes, absmax
+        self.absmax_q, self.dq_scale, self.dq_mean = absmax_q, dq_scale, dq_mean
+        self.row_bits, self.row_offset, self.levels = row_bits, row_offset, levels
+        self.desc = lq_qweight(fmt, 64, N, K, _ptr(codes), _ptr(absmax), _ptr(absmax_q), _ptr(dq_scale),
+                               _ptr(dq_mean), 256, 0, _ptr(row_bits), _ptr(row_offset), _ptr(levels))
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+    @classmethod
+    def from_weight(cls, W, double_quantize: bool = True) -> "QWeight":
+        """Quantize W [N, K] to NF4 (+ double quantization of the constants)."""
+        N, K = W.shape
+        codes, absmax = quantize_nf4(W)
+        if not double_quantize:
+            return cls(N, K, codes, absmax=absmax)
+        q, s2, mu = double_quant(absmax)
+        return cls(N, K, codes, absmax_q=q, dq_scale=s2, dq_mean=mu)
+
+    @classmethod
+    def from_codebook(cls, W, row_bits, thresholds, levels, double_quantize: bool = True) -> "QWeight":
+        N, K = W.shape
+        codes, absmax, row_offset = quantize_codebook(W, row_bits, thresholds)
+        if not double_quantize:
+            return cls(N, K, codes, absmax=absmax, fmt=LQ_FMT_CODEBOOK, row_bits=row_bits,
+                       row_offset=row_offset, levels=levels)
+        q, s2, mu = double_quant(absmax)
+        return cls(N, K, codes, absmax_q=q, dq_scale=s2, dq_mean=mu, fmt=LQ_FMT_CODEBOOK,
+                   row_bits=row_bits, row_offset=row_offset, levels=levels)
+
+
+def dequant(qw: QWeight):
+    torch = _torch()
+    out = torch.empty(qw.N, qw.K, dtype=torch.bfloat16, device=qw.device)
+    _check(lib.lq_dequant(qw.ref(), _ptr(out), _stream(qw.device)), "lq_dequant")
+    return out
+
+
+def qlora_forward(qw: QWeight, X, A, B, alpha: float, out_dtype=None, save_t: bool = True):
+    """H = X W'^T + (alpha/r) (X A^T) B^T. Returns (H [M, N], t [M, r] f32 or None)."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    for n, t in (("X", X), ("A", A), ("B", B)):
+        _contig_cuda(t, n)
+    M, r = X.shape[0], A.shape[0]
+    H = torch.empty(M, qw.N, dtype=out_dtype, device=X.device)
+    t = torch.empty(M, r, dtype=torch.float32, device=X.device) if save_t else None
+    ws_bytes = lib.lq_forward_workspace(qw.ref(), M, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=X.device)
+    h_code = LQ_F32 if out_dtype == torch.float32 else LQ_BF16
+    _check(lib.lq_qlora_forward(qw.ref(), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(H), h_code,
+                                _ptr(t), _ptr(ws), ws_bytes, _stream(X.device)), "lq_qlora_forward")
+    return H, t
+
+
+def qlora_backward(qw: QWeight, X, G, A, B, alpha: float, t=None,
+                   need_grad_x: bool = True, need_dA: bool = True, need_dB: bool = True):
+    """Returns (grad_X bf16 [M, K] | None, dA f32 [r, K] | None, dB f32 [N, r] | None)."""
+    torch = _torch()
+    M, r = G.shape[0], A.shape[0]
+    dev = G.device
+    gx = torch.empty(M, qw.K, dtype=torch.bfloat16, device=dev) if need_grad_x else None
+    dA = torch.empty(r, qw.K, dtype=torch.float32, device=dev) if need_dA else None
+    dB = torch.empty(qw.N, r, dtype=torch.float32, device=dev) if need_dB else None
+    ws_bytes = lib.lq_backward_workspace(qw.ref(), M, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.lq_qlora_backward(qw.ref(), _ptr(X), _ptr(G), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(t),
+                                 _ptr(gx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(dev)),
+           "lq_qlora_backward")
+    return gx, dA, dB
+
+
+def row_offsets(row_bits_host, K: int):
+    """Byte offsets of each row's bit-planes (prefix sums of K*b/8), host list."""
+    off = [0]
+    for b in row_bits_host:
+        off.append(off[-1] + K * int(b) // 8)
+    return off
+
+
+def quantize_codebook(W, row_bits, thresholds, blocksize: int = 64):
+    """W [N, K], row_bits uint8 [N] (device), thresholds f32 [N, 15] (device)
+    -> (codes uint8, absmax f32 [N*K/64], row_offset int64 [N+1])."""
+    torch = _torch()
+    N, K = W.shape
+    offs = row_offsets(row_bits.cpu().tolist(), K)
+    row_offset = torch.tensor(offs, dtype=torch.int64, device=W.device)
+    codes = torch.empty(max(offs[-1], 1), dtype=torch.uint8, device=W.device)
+    absmax = torch.empty(N * K // blocksize, dtype=torch.float32, device=W.device)
+    _check(lib.lq_quantize_codebook(_ptr(W), _dtype_code(W), N, K, blocksize, _ptr(row_bits), _ptr(row_offset),
+                                    _ptr(thresholds), _ptr(codes), _ptr(absmax), _stream(W.device)),
+           "lq_quantize_codebook")
+    return codes, absmax, row_offset

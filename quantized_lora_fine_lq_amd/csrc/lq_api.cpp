@@ -1,0 +1,239 @@
+// The C ABI of include/lq.h: argument validation, workspace carving and
+// kernel dispatch. No device memory is allocated here; every launch goes on
+// the caller's stream.
+#include <cstdlib>
+#include <cstring>
+
+#include "lq_internal.h"
+
+namespace {
+
+using namespace lq;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int32_t d) { return d == LQ_F32 || d == LQ_BF16 || d == LQ_F16; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_LAUNCH; }
+
+// Validate a weight descriptor and turn it into the kernels' view.
+int check_qweight(const lq_qweight* w, QWeight* out) {
+  if (!w) return LQ_ERR_ARG;
+  if (w->format != LQ_FMT_NF4 && w->format != LQ_FMT_CODEBOOK) return LQ_ERR_ARG;
+  if (w->blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  if (w->N <= 0 || w->K <= 0 || w->K % 64 != 0) return LQ_ERR_SHAPE;
+  if (!w->codes) return LQ_ERR_ARG;
+  if (!w->absmax) {
+    if (!w->absmax_q || !w->dq_scale || !w->dq_mean) return LQ_ERR_ARG;
+    if (w->dq_blocksize != 256) return LQ_ERR_UNSUPPORTED;
+  }
+  if (w->format == LQ_FMT_CODEBOOK && (!w->row_bits || !w->row_offset || !w->levels)) return LQ_ERR_ARG;
+  out->format = w->format;
+  out->N = w->N;
+  out->K = w->K;
+  out->codes = w->codes;
+  out->qc.absmax = w->absmax;
+  out->qc.absmax_q = w->absmax ? nullptr : w->absmax_q;
+  out->qc.dq_scale = w->absmax ? nullptr : w->dq_scale;
+  out->qc.dq_mean = w->absmax ? nullptr : w->dq_mean;
+  out->row_bits = w->row_bits;
+  out->row_offset = w->row_offset;
+  out->levels = w->levels;
+  return LQ_OK;
+}
+
+// Forward path choice: the GEMV kernel for decode-sized M (NF4 only), else
+// the MFMA GEMM. LQ_FORCE_PATH=gemm|gemv overrides (for tests).
+bool use_gemv(const QWeight& w, int64_t M) {
+  if (w.format != LQ_FMT_NF4 || M > 16) return false;
+  const char* f = std::getenv("LQ_FORCE_PATH");
+  if (f && std::strcmp(f, "gemm") == 0) return false;
+  return true;
+}
+
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* p) : base((char*)p) {}
+  template <class T> T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base + used);
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
+  return align_up((size_t)M * r * sizeof(float)) + align_up(row_skinny_ws_floats(M, w.K, r) * sizeof(float));
+}
+
+size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
+  size_t part = row_skinny_ws_floats(M, w.K, r);
+  const size_t cands[3] = {row_skinny_ws_floats(M, w.N, r), col_skinny_ws_floats(M, w.K, r),
+                           col_skinny_ws_floats(M, w.N, r)};
+  for (size_t c : cands) part = c > part ? c : part;
+  return 2 * align_up((size_t)M * r * sizeof(float)) + align_up(part * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lq_status_string(int status) {
+  switch (status) {
+    case LQ_OK: return "ok";
+    case LQ_ERR_ARG: return "invalid argument (null pointer or bad enum value)";
+    case LQ_ERR_SHAPE: return "invalid shape (sizes must be positive, K % 64 == 0, r in [1, 128])";
+    case LQ_ERR_UNSUPPORTED: return "unsupported option (blocksize, double-quant blocksize or dtype)";
+    case LQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case LQ_ERR_LAUNCH: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int lq_version(void) { return 100; }
+
+int lq_nf4_table(float* levels, float* thresholds) {
+  const Tables& t = tables();
+  if (levels) std::memcpy(levels, t.levels, sizeof(t.levels));
+  if (thresholds) std::memcpy(thresholds, t.thresholds, sizeof(t.thresholds));
+  return LQ_OK;
+}
+
+int lq_sizes(int64_t N, int64_t K, int32_t bits, lq_sizes_t* out) {
+  if (!out || bits < 1 || bits > 4) return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
+  out->n = N * K;
+  out->n_blocks = out->n / 64;
+  out->n_dq_blocks = (out->n_blocks + 255) / 256;
+  out->code_bytes = out->n * bits / 8;
+  out->dq_const_bytes = out->n_blocks + 4 * out->n_dq_blocks + 4;
+  out->fp32_const_bytes = 4 * out->n_blocks;
+  out->const_bits_per_param_dq = 8.0 / 64.0 + 32.0 / (64.0 * 256.0);
+  out->const_bits_per_param_fp32 = 32.0 / 64.0;
+  return LQ_OK;
+}
+
+int lq_quantize_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                    uint8_t* codes, float* absmax, void* stream) {
+  if (!W || !codes || !absmax || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
+  if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  return launch_status(launch_quantize_nf4(W, dtype, N * K / 64, codes, absmax, (hipStream_t)stream));
+}
+
+size_t lq_double_quant_workspace(int64_t n_blocks, int32_t dq_blocksize) {
+  if (n_blocks <= 0 || dq_blocksize != 256) return 0;
+  return align_up(double_quant_ws_doubles(n_blocks) * sizeof(double));
+}
+
+int lq_double_quant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
+                    uint8_t* absmax_q, float* dq_scale, float* dq_mean, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!absmax || !absmax_q || !dq_scale || !dq_mean) return LQ_ERR_ARG;
+  if (n_blocks <= 0) return LQ_ERR_SHAPE;
+  if (dq_blocksize != 256) return LQ_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < lq_double_quant_workspace(n_blocks, dq_blocksize)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_double_quant(absmax, n_blocks, absmax_q, dq_scale, dq_mean,
+                                           (double*)workspace, (hipStream_t)stream));
+}
+
+int lq_dequant(const lq_qweight* w, uint16_t* out, void* stream) {
+  QWeight q;
+  const int st = check_qweight(w, &q);
+  if (st != LQ_OK) return st;
+  if (!out) return LQ_ERR_ARG;
+  return launch_status(launch_dequant(q, out, (hipStream_t)stream));
+}
+
+size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r) {
+  QWeight q;
+  if (check_qweight(w, &q) != LQ_OK || M <= 0 || r < 1 || r > 128) return 0;
+  return forward_ws(q, M, r);
+}
+
+int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
+                     float* t_save, void* workspace, size_t ws_bytes, void* stream) {
+  QWeight q;
+  int st = check_qweight(w, &q);
+  if (st != LQ_OK) return st;
+  if (!X || !A || !B || !H) return LQ_ERR_ARG;
+  if (M <= 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
+  if (h_dtype != LQ_BF16 && h_dtype != LQ_F32) return LQ_ERR_UNSUPPORTED;
+  const size_t need = forward_ws(q, M, r);
+  if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(workspace);
+  float* t_ws = cv.take<float>((size_t)M * r);
+  float* part = cv.take<float>(row_skinny_ws_floats(M, q.K, r));
+  float* t = t_save ? t_save : t_ws;
+  const float scale = alpha / (float)r;
+  hipError_t e = launch_row_skinny(X, M, q.K, A, false, r, t, part, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  if (use_gemv(q, M)) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
+  else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
+  return launch_status(e);
+}
+
+size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r) {
+  QWeight q;
+  if (check_qweight(w, &q) != LQ_OK || M <= 0 || r < 1 || r > 128) return 0;
+  return backward_ws(q, M, r);
+}
+
+int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,
+                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                      const float* t_saved, uint16_t* grad_X, float* dA, float* dB,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  QWeight q;
+  int st = check_qweight(w, &q);
+  if (st != LQ_OK) return st;
+  if (q.format != LQ_FMT_NF4 && grad_X) return LQ_ERR_UNSUPPORTED;
+  if (!G || !A || !B) return LQ_ERR_ARG;
+  if ((dA || !t_saved) && !X) return LQ_ERR_ARG;
+  if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
+  const size_t need = backward_ws(q, M, r);
+  if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carver cv(workspace);
+  float* u = cv.take<float>((size_t)M * r);
+  float* t_ws = cv.take<float>((size_t)M * r);
+  float* part = reinterpret_cast<float*>(cv.base + cv.used);
+  const float scale = alpha / (float)r;
+  hipError_t e = hipSuccess;
+  const float* t = t_saved;
+  if (!t) {
+    e = launch_row_skinny(X, M, q.K, A, false, r, t_ws, part, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+    t = t_ws;
+  }
+  e = launch_row_skinny(G, M, q.N, B, true, r, u, part, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  if (dB) {
+    e = launch_col_skinny(t, G, M, q.N, r, scale, dB, true, part, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  }
+  if (grad_X) {
+    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  }
+  if (dA) {
+    e = launch_col_skinny(u, X, M, q.K, r, scale, dA, false, part, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  }
+  return LQ_OK;
+}
+
+int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                         const uint8_t* row_bits, const int64_t* row_offset,
+                         const float* thresholds, uint8_t* codes, float* absmax, void* stream) {
+  if (!W || !row_bits || !row_offset || !thresholds || !codes || !absmax || !valid_dtype(dtype))
+    return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
+  if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  return launch_status(launch_quantize_codebook(W, dtype, N, K, row_bits, row_offset, thresholds,
+                                                codes, absmax, (hipStream_t)stream));
+}
+
+}  // extern "C"

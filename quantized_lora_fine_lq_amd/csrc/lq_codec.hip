@@ -1,0 +1,350 @@
+// Codec kernels for gfx950: NF4 quantize, double quantization of the block
+// constants, dequantization to bfloat16, and the per-channel codebook
+// quantizer.
+//
+// QLoRA (Heng's Blog), "Contribution 1: 4-bit NormalFloat (NF4)": divide each
+// block by its absmax, map to the nearest NF4 value, store 4-bit indices and
+// the block constant. "Contribution 2: Double Quantization": FP32 constants per
+// 64 weights, re-quantized with an 8-bit float at block size 256 after
+// subtracting their mean. LowRA (cloud.tencent.com.cn), sections 3 and 4.1:
+// per-output-channel quantization with custom thresholds and precision,
+// groups of 64 scaled by absmax.
+#include <float.h>
+
+#include "lq_device.h"
+
+namespace lq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// NF4 quantize. A 64-weight block is 16 lanes x 4 consecutive weights (one
+// 16-byte load per lane for float32 input). absmax is reduced inside the
+// 16-lane DPP row. The code search uses the reciprocal of the block constant
+// and a 33-bin table: bin j of x' = w * (1/c) holds at most one threshold, so
+// code = base[j] + (x' > T[j]). Whenever x' lies within 2^-21 of that
+// threshold -- closer than the float32 error of x' against the correctly
+// rounded quotient w / c -- the quotient is computed exactly and used
+// instead, so every code equals the one from IEEE division.
+// ---------------------------------------------------------------------------
+constexpr int kQuantPasses = 4;   // 16 blocks per pass per 256-thread WG
+
+template <typename Tin> struct Load4;
+template <> struct Load4<float> {
+  __device__ static f32x4_t go(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+};
+template <> struct Load4<uint16_t> {  // bfloat16 bits
+  __device__ static f32x4_t go(const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return f32x4_t{bf16lo_to_f32(v.x), bf16hi_to_f32(v.x), bf16lo_to_f32(v.y), bf16hi_to_f32(v.y)};
+  }
+};
+template <> struct Load4<_Float16> {
+  __device__ static f32x4_t go(const _Float16* p) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    const h4 v = *reinterpret_cast<const h4*>(p);
+    return f32x4_t{(float)v.x, (float)v.y, (float)v.z, (float)v.w};
+  }
+};
+
+__device__ __forceinline__ uint32_t nf4_code(float w, float c, float r, bool fast_ok,
+                                             const float* sT, const int32_t* sB) {
+  const float xp = w * r;
+  int j = (int)__builtin_fmaf(xp, 16.0f, 16.0f);
+  j = min(max(j, 0), 32);
+  const float T = sT[j];
+  if (fast_ok && fabsf(xp - T) > 0x1p-21f) return (uint32_t)(sB[j] + (xp > T ? 1 : 0));
+  const float x = (c > 0.0f) ? w / c : 0.0f;   // IEEE quotient
+  int jj = (int)__builtin_fmaf(x, 16.0f, 16.0f);
+  jj = min(max(jj, 0), 32);
+  return (uint32_t)(sB[jj] + (x > sT[jj] ? 1 : 0));
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W, int64_t n_blocks,
+                                                      uint8_t* __restrict__ codes,
+                                                      float* __restrict__ absmax, Nf4Lut lut) {
+  __shared__ float sT[33];
+  __shared__ int32_t sB[33];
+  if (threadIdx.x < 33) {
+    sT[threadIdx.x] = lut.T[threadIdx.x];
+    sB[threadIdx.x] = lut.base[threadIdx.x];
+  }
+  __syncthreads();
+  const int i16 = threadIdx.x & 15;
+  const int64_t blk0 = (int64_t)blockIdx.x * (16 * kQuantPasses) + (threadIdx.x >> 4);
+  f32x4_t v[kQuantPasses];
+#pragma unroll
+  for (int p = 0; p < kQuantPasses; ++p) {
+    const int64_t blk = blk0 + 16 * p;
+    v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int p = 0; p < kQuantPasses; ++p) {
+    const int64_t blk = blk0 + 16 * p;
+    float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+    m = row16_max(m);
+    const bool fast_ok = (m >= FLT_MIN) && (m <= 0x1p125f);
+    const float r = fast_ok ? 1.0f / m : 0.0f;
+    const uint32_t c0 = nf4_code(v[p].x, m, r, fast_ok, sT, sB);
+    const uint32_t c1 = nf4_code(v[p].y, m, r, fast_ok, sT, sB);
+    const uint32_t c2 = nf4_code(v[p].z, m, r, fast_ok, sT, sB);
+    const uint32_t c3 = nf4_code(v[p].w, m, r, fast_ok, sT, sB);
+    // two bytes per lane, element 4i in the high nibble of the first byte
+    const uint32_t h = ((c0 << 4) | c1) | (((c2 << 4) | c3) << 8);
+    const uint32_t d = h | (dpp_u32<DPP_QUAD_XOR1>(h) << 16);      // valid on even lanes
+    const uint32_t d2 = dpp_u32<DPP_QUAD_XOR2>(d);                // lane 4k gets lane 4k+2's
+    if (blk < n_blocks) {
+      if ((i16 & 3) == 0)
+        *reinterpret_cast<uint2*>(codes + blk * 32 + (i16 >> 2) * 8) = make_uint2(d, d2);
+      if (i16 == 0) absmax[blk] = m;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Double quantization. (1) per 256-constant block: float64 pairwise tree sum
+// (4 leaves per lane, then a butterfly over the 64 lanes, which pairs
+// neighbouring subtrees level by level). (2) pairwise tree over the block
+// sums, 1024 leaves per workgroup, repeated until one value is left; zero
+// padding to a power of two does not change the sum. (3) per block:
+// d = c - mean, scale = max|d| / 448, code = E4M3(clamp(d / scale)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_dq_block_sums(const float* __restrict__ c, int64_t n_b,
+                                                      double* __restrict__ sums) {
+  const int l = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * 256 + 4 * l;
+  double v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (base + i < n_b) ? (double)c[base + i] : 0.0;
+  double s = (v[0] + v[1]) + (v[2] + v[3]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
+  if (l == 0) sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(1024) void k_tree_reduce(const double* __restrict__ in, int64_t n_in,
+                                                      double* __restrict__ out, int64_t n_b,
+                                                      float* __restrict__ mean_out) {
+  __shared__ double wsum[16];
+  const int t = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 1024 + t;
+  double s = (i < n_in) ? in[i] : 0.0;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
+  if ((t & 63) == 0) wsum[t >> 6] = s;
+  __syncthreads();
+  if (t < 64) {
+    double w = (t < 16) ? wsum[t] : 0.0;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) w = w + __shfl_xor(w, m);
+    if (t == 0) {
+      if (mean_out) *mean_out = (float)(w / (double)n_b);
+      else out[blockIdx.x] = w;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, int64_t n_b,
+                                                   const float* __restrict__ mean,
+                                                   uint8_t* __restrict__ absmax_q,
+                                                   float* __restrict__ dq_scale) {
+  __shared__ float wmax[4];
+  const int t = threadIdx.x;
+  const int64_t j = (int64_t)blockIdx.x * 256 + t;
+  const float mu = *mean;
+  const float d = (j < n_b) ? c[j] - mu : 0.0f;
+  float a = wave_max(fabsf(d));
+  if ((t & 63) == 0) wmax[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s2 = a / 448.0f;
+  if (t == 0) dq_scale[blockIdx.x] = s2;
+  uint32_t code = 0;
+  if (s2 > 0.0f) {
+    float v = d / s2;
+    v = fminf(fmaxf(v, -448.0f), 448.0f);
+    code = e4m3_encode(v);
+  }
+  if (j < n_b) absmax_q[j] = (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------
+// Dequant to bfloat16. One thread turns 32 codes (16 bytes) into 32 bf16.
+// NF4: a 256-entry table in LDS maps a code byte to its two float32 levels.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__ codes, QConst qc,
+                                                     int64_t n_groups, uint16_t* __restrict__ out,
+                                                     Nf4Levels lv) {
+  __shared__ f32x2_t pair[256];
+  pair[threadIdx.x] = f32x2_t{lv.q[threadIdx.x >> 4], lv.q[threadIdx.x & 15]};
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= n_groups) return;
+  const u32x4_t cw = *reinterpret_cast<const u32x4_t*>(codes + g * 16);
+  const float cp = block_const(qc, g >> 1);
+  u32x4_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const f32x2_t q = pair[(cw[d] >> (8 * b)) & 0xFFu];
+      o[d][b] = pack_bf16x2(q.x * cp, q.y * cp);
+    }
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + g * 32);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) dst[d] = o[d];
+}
+
+// Codebook dequant: one thread per 8 elements of a 64-block (one byte of
+// each bit-plane). Row i's levels live in levels[i*16 ...].
+__global__ __launch_bounds__(256) void k_dequant_codebook(const uint8_t* __restrict__ codes,
+                                                          QConst qc, int64_t N, int64_t K,
+                                                          const uint8_t* __restrict__ row_bits,
+                                                          const int64_t* __restrict__ row_offset,
+                                                          const float* __restrict__ levels,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 8 elements
+  const int64_t groups_per_row = K / 8;
+  if (g >= N * groups_per_row) return;
+  const int64_t row = g / groups_per_row;
+  const int64_t k8 = g - row * groups_per_row;                 // 8-element group in row
+  const int64_t blk_in_row = k8 >> 3;
+  const int byte_in_plane = (int)(k8 & 7);
+  const int nb = min(max((int)row_bits[row], 1), 4);
+  const uint8_t* src = codes + row_offset[row] + blk_in_row * 8 * nb;
+  uint32_t code[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int p = 0; p < nb; ++p) {
+    const uint32_t byte = src[8 * p + byte_in_plane];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] |= ((byte >> e) & 1u) << p;
+  }
+  const float cp = block_const(qc, row * (K / 64) + blk_in_row);
+  const float* L = levels + row * 16;
+  u32x4_t o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(L[code[2 * e]] * cp, L[code[2 * e + 1]] * cp);
+  *reinterpret_cast<u32x4_t*>(out + row * K + k8 * 8) = o;
+}
+
+// ---------------------------------------------------------------------------
+// Codebook quantize: one wave per 64-block, lane e holds element e, so each
+// bit-plane is one wave ballot. x = w / c is the IEEE quotient; the code is
+// the number of the row's thresholds strictly below x.
+// ---------------------------------------------------------------------------
+template <typename Tin> __device__ __forceinline__ float load1(const Tin* p);
+template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <> __device__ __forceinline__ float load1<_Float16>(const _Float16* p) { return (float)*p; }
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict__ W, int64_t N,
+                                                           int64_t K,
+                                                           const uint8_t* __restrict__ row_bits,
+                                                           const int64_t* __restrict__ row_offset,
+                                                           const float* __restrict__ T,
+                                                           uint8_t* __restrict__ codes,
+                                                           float* __restrict__ absmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t blocks_per_row = K / 64;
+  if (blk >= N * blocks_per_row) return;   // uniform per wave
+  const int64_t row = blk / blocks_per_row;
+  const int64_t blk_in_row = blk - row * blocks_per_row;
+  const float w = load1<Tin>(W + blk * 64 + lane);
+  const float m = wave_max(fabsf(w));
+  const float x = (m > 0.0f) ? w / m : 0.0f;
+  const int nb = min(max((int)row_bits[row], 1), 4);
+  const int nt = (1 << nb) - 1;
+  const float* Tr = T + row * 15;
+  uint32_t code = 0;
+  for (int k = 0; k < nt; ++k) code += (x > Tr[k]) ? 1u : 0u;
+  uint8_t* dst = codes + row_offset[row] + blk_in_row * 8 * nb;
+  for (int p = 0; p < nb; ++p) {
+    const uint64_t plane = __ballot((code >> p) & 1u);
+    if (lane == 0) *reinterpret_cast<uint64_t*>(dst + 8 * p) = plane;
+  }
+  if (lane == 0) absmax[blk] = m;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8_t* codes,
+                               float* absmax, hipStream_t s) {
+  const int64_t per_wg = 16 * kQuantPasses;
+  const dim3 grid((unsigned)((n_blocks + per_wg - 1) / per_wg));
+  const Nf4Lut& lut = tables().lut;
+  if (dtype == LQ_F32)
+    hipLaunchKernelGGL(k_quantize_nf4<float>, grid, dim3(256), 0, s, (const float*)W, n_blocks, codes, absmax, lut);
+  else if (dtype == LQ_BF16)
+    hipLaunchKernelGGL(k_quantize_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, codes, absmax, lut);
+  else
+    hipLaunchKernelGGL(k_quantize_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, codes, absmax, lut);
+  return hipGetLastError();
+}
+
+size_t double_quant_ws_doubles(int64_t n_blocks) {
+  const int64_t n_d = (n_blocks + 255) / 256;
+  int64_t total = n_d, level = n_d;
+  while (level > 1024) {
+    level = (level + 1023) / 1024;
+    total += level;
+  }
+  return (size_t)total + 16;
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax_q,
+                               float* dq_scale, float* dq_mean, double* ws, hipStream_t s) {
+  const int64_t n_d = (n_b + 255) / 256;
+  hipLaunchKernelGGL(k_dq_block_sums, dim3((unsigned)n_d), dim3(64), 0, s, absmax, n_b, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  double* cur = ws;
+  int64_t n = n_d;
+  while (n > 1024) {
+    const int64_t groups = (n + 1023) / 1024;
+    double* nxt = cur + n;
+    hipLaunchKernelGGL(k_tree_reduce, dim3((unsigned)groups), dim3(1024), 0, s, cur, n, nxt, n_b,
+                       (float*)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    cur = nxt;
+    n = groups;
+  }
+  hipLaunchKernelGGL(k_tree_reduce, dim3(1), dim3(1024), 0, s, cur, n, (double*)nullptr, n_b, dq_mean);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dq_encode, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b, dq_mean,
+                     absmax_q, dq_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
+  if (w.format == LQ_FMT_NF4) {
+    const int64_t n_groups = w.N * w.K / 32;
+    hipLaunchKernelGGL(k_dequant_nf4, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, s,
+                       w.codes, w.qc, n_groups, out, tables().lv);
+  } else {
+    const int64_t n_groups = w.N * w.K / 8;
+    hipLaunchKernelGGL(k_dequant_codebook, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0,
+                       s, w.codes, w.qc, w.N, w.K, w.row_bits, w.row_offset, w.levels, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
+                                    const uint8_t* row_bits, const int64_t* row_offset,
+                                    const float* T, uint8_t* codes, float* absmax, hipStream_t s) {
+  const int64_t nblk = N * K / 64;
+  const dim3 grid((unsigned)((nblk + 3) / 4));
+  if (dtype == LQ_F32)
+    hipLaunchKernelGGL(k_quantize_codebook<float>, grid, dim3(256), 0, s, (const float*)W, N, K, row_bits, row_offset, T, codes, absmax);
+  else if (dtype == LQ_BF16)
+    hipLaunchKernelGGL(k_quantize_codebook<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, N, K, row_bits, row_offset, T, codes, absmax);
+  else
+    hipLaunchKernelGGL(k_quantize_codebook<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, N, K, row_bits, row_offset, T, codes, absmax);
+  return hipGetLastError();
+}
+
+}  // namespace lq

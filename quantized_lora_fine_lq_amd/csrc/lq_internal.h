@@ -1,0 +1,90 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lq.h"
+
+namespace lq {
+
+// Block constants of a quantized weight (float32, or double quantized).
+struct QConst {
+  const float* absmax;
+  const uint8_t* absmax_q;
+  const float* dq_scale;
+  const float* dq_mean;
+};
+
+// The 16 NF4 levels (ascending).
+struct Nf4Levels {
+  float q[16];
+};
+
+// Code-search table over 33 bins of width 1/16 covering [-1, 1 + 1/16):
+// bin j holds x in [j/16 - 1, (j+1)/16 - 1]. base[j] counts thresholds below
+// the bin (with a 2^-20 margin) and T[j] is the one threshold inside the
+// widened bin (or 4.0 if there is none), so code(x) = base[j] + (x > T[j]).
+struct Nf4Lut {
+  float T[33];
+  int32_t base[33];
+};
+
+// Host-built tables (computed once, then read-only).
+struct Tables {
+  float levels[16];
+  float thresholds[15];
+  Nf4Levels lv;
+  Nf4Lut lut;
+};
+const Tables& tables();
+
+// Quantized-weight view used by the kernels.
+struct QWeight {
+  int32_t format;
+  int64_t N, K;
+  const uint8_t* codes;
+  QConst qc;
+  const uint8_t* row_bits;
+  const int64_t* row_offset;
+  const float* levels;
+};
+
+// ---- launchers (return hipError_t of the launch) ----------------------------
+hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8_t* codes,
+                               float* absmax, hipStream_t s);
+hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* absmax_q,
+                               float* dq_scale, float* dq_mean, double* ws, hipStream_t s);
+size_t double_quant_ws_doubles(int64_t n_blocks);
+hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s);
+hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
+                                    const uint8_t* row_bits, const int64_t* row_offset,
+                                    const float* thresholds, uint8_t* codes, float* absmax,
+                                    hipStream_t s);
+
+// Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R(j, c) with
+// R(j, c) = Rm[j*C + c] (r_transposed = false) or Rm[c*r + j] (true).
+size_t row_skinny_ws_floats(int64_t M, int64_t C, int r);
+hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rm,
+                             bool r_transposed, int r, float* out, float* ws, hipStream_t s);
+// Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c]; written as
+// out[j*C + c] (out_transposed = false, [r, C]) or out[c*r + j] ([C, r]).
+size_t col_skinny_ws_floats(int64_t M, int64_t C, int r);
+hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
+                             float scale, float* out, bool out_transposed, float* ws,
+                             hipStream_t s);
+
+// Dequant-GEMM with the LoRA segment.
+//  forward : out[m][n] = sum_k X[m][k] W'[n][k] + s * sum_j t[m][j] B[n][j]
+//  backward: out[m][k] = sum_n G[m][n] W'[n][k] + s * sum_j u[m][j] A[j][k]
+hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
+                           const uint16_t* B, int r, float s, void* H, int h_dtype,
+                           hipStream_t st);
+hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
+                           const uint16_t* A, int r, float s, uint16_t* gX, hipStream_t st);
+hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
+                           const uint16_t* B, int r, float s, void* H, int h_dtype,
+                           hipStream_t st);
+
+}  // namespace lq

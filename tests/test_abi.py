@@ -1,0 +1,143 @@
+"""CPU tests of the C-ABI library: it loads, exports every entry point that
+include/lq.h declares, its host tables equal the oracle's, its size queries
+follow the closed forms, and argument validation rejects bad calls before
+anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lq.h")
+
+
+@pytest.fixture(scope="module")
+def lq():
+    from quantized_lora_fine_lq_amd import build
+    if not os.path.exists(build.LIB):
+        build.build()
+    import quantized_lora_fine_lq_amd as mod
+    return mod
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s+(lq_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lq):
+    names = declared_symbols()
+    assert len(names) == 13
+    for name in names:
+        assert hasattr(lq.lib, name), name
+        assert name in lq.SIGNATURES, name
+
+
+def test_status_strings(lq):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lq.status_string(s) and lq.status_string(s) != "unknown status"
+    assert lq.status_string(42) == "unknown status"
+    assert lq.lib.lq_version() >= 100
+
+
+def test_library_nf4_table_equals_oracle(lq):
+    # the library builds its table with its own quantile routine (bisection on
+    # erfc); the oracle uses scipy's ndtri. Both must round to the same float32.
+    from oracle import nf4
+    levels, thresholds = lq.nf4_table()
+    assert np.array_equal(np.array(levels, dtype=np.float32), nf4.levels())
+    assert np.array_equal(np.array(thresholds, dtype=np.float32), nf4.thresholds())
+
+
+def test_sizes_closed_form(lq):
+    s = lq.sizes(28672, 8192, 4)
+    assert s["code_bytes"] == 117440512
+    assert s["n_blocks"] == 3670016 and s["n_dq_blocks"] == 14336
+    assert s["dq_const_bytes"] == 3670016 + 4 * 14336 + 4
+    assert abs(s["const_bits_per_param_dq"] - 0.126953125) < 1e-15
+    assert round(s["const_bits_per_param_dq"], 3) == 0.127
+    assert s["const_bits_per_param_fp32"] == 0.5
+    # LowRA-style mix: bits per weight from the code bytes
+    s1 = lq.sizes(4096, 4096, 1)
+    assert s1["code_bytes"] == 4096 * 4096 // 8
+
+
+def test_validation_errors_without_launch(lq):
+    L = lq.lib
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)   # never dereferenced: every call below fails validation
+    null = vp(None)
+    assert L.lq_sizes(10, 64, 4, None) == lq.LQ_ERR_ARG
+    assert L.lq_sizes(10, 65, 4, ctypes.byref(lq.lq_sizes_t())) == lq.LQ_ERR_SHAPE
+    assert L.lq_quantize_nf4(null, 0, 4, 64, 64, fake, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_quantize_nf4(fake, 7, 4, 64, 64, fake, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_quantize_nf4(fake, 0, 4, 96, 64, fake, fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_quantize_nf4(fake, 0, 0, 64, 64, fake, fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_quantize_nf4(fake, 0, 4, 64, 32, fake, fake, null) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_double_quant_workspace(1000, 256) >= 8 * 4
+    assert L.lq_double_quant_workspace(1000, 128) == 0
+    assert L.lq_double_quant(fake, 1000, 128, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_double_quant(fake, 1000, 256, fake, fake, fake, fake, 8, null) == lq.LQ_ERR_WORKSPACE
+    assert L.lq_double_quant(fake, 0, 256, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_double_quant(null, 10, 256, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_ARG
+
+    def qw(**kw):
+        d = dict(format=0, blocksize=64, N=128, K=256, codes=0x1000, absmax=0x1000, absmax_q=None,
+                 dq_scale=None, dq_mean=None, dq_blocksize=256, reserved0=0, row_bits=None,
+                 row_offset=None, levels=None)
+        d.update(kw)
+        return lq.lq_qweight(**d)
+
+    assert L.lq_dequant(None, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_dequant(ctypes.byref(qw(format=5)), fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_dequant(ctypes.byref(qw(blocksize=128)), fake, null) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_dequant(ctypes.byref(qw(K=100)), fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_dequant(ctypes.byref(qw(absmax=None)), fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_dequant(ctypes.byref(qw(absmax=None, absmax_q=1, dq_scale=1, dq_mean=1, dq_blocksize=64)),
+                        fake, null) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_dequant(ctypes.byref(qw(format=1)), fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_dequant(ctypes.byref(qw()), null, null) == lq.LQ_ERR_ARG
+
+    w = qw()
+    ws = L.lq_forward_workspace(ctypes.byref(w), 16, 16)
+    assert ws >= 16 * 16 * 4
+    assert L.lq_forward_workspace(ctypes.byref(w), 16, 0) == 0
+    assert L.lq_forward_workspace(ctypes.byref(w), 16, 129) == 0
+    args = (ctypes.byref(w), fake, 16, fake, fake, 16, 32.0, fake, 1, null, fake, ws, null)
+    bad_r = list(args); bad_r[5] = 0
+    assert L.lq_qlora_forward(*bad_r) == lq.LQ_ERR_SHAPE
+    bad_h = list(args); bad_h[8] = 2
+    assert L.lq_qlora_forward(*bad_h) == lq.LQ_ERR_UNSUPPORTED
+    bad_ws = list(args); bad_ws[11] = ws - 1
+    assert L.lq_qlora_forward(*bad_ws) == lq.LQ_ERR_WORKSPACE
+    bad_x = list(args); bad_x[1] = null
+    assert L.lq_qlora_forward(*bad_x) == lq.LQ_ERR_ARG
+    bad_m = list(args); bad_m[2] = 0
+    assert L.lq_qlora_forward(*bad_m) == lq.LQ_ERR_SHAPE
+
+    wsb = L.lq_backward_workspace(ctypes.byref(w), 64, 16)
+    assert wsb >= 2 * 64 * 16 * 4
+    bargs = [ctypes.byref(w), fake, fake, 64, fake, fake, 16, 32.0, null, fake, fake, fake, fake, wsb, null]
+    b1 = list(bargs); b1[1] = null      # X needed for dA and for recomputing t
+    assert L.lq_qlora_backward(*b1) == lq.LQ_ERR_ARG
+    b2 = list(bargs); b2[13] = 0
+    assert L.lq_qlora_backward(*b2) == lq.LQ_ERR_WORKSPACE
+    w_odd = qw(N=100)                   # backward needs N % 8 == 0
+    b3 = list(bargs); b3[0] = ctypes.byref(w_odd)
+    assert L.lq_qlora_backward(*b3) == lq.LQ_ERR_SHAPE
+    wc = qw(format=1, row_bits=1, row_offset=1, levels=1)
+    b4 = list(bargs); b4[0] = ctypes.byref(wc)
+    assert L.lq_qlora_backward(*b4) == lq.LQ_ERR_UNSUPPORTED
+
+    assert L.lq_quantize_codebook(fake, 0, 4, 64, 64, null, fake, fake, fake, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_quantize_codebook(fake, 0, 4, 60, 64, fake, fake, fake, fake, fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_quantize_codebook(fake, 0, 4, 64, 16, fake, fake, fake, fake, fake, null) == lq.LQ_ERR_UNSUPPORTED
+
+
+def test_workspace_queries_deterministic(lq):
+    w = lq.lq_qweight(0, 64, 4096, 4096, 1, 1, None, None, None, 256, 0, None, None, None)
+    a = [lq.lib.lq_forward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
+    b = [lq.lib.lq_backward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
+    assert len(set(a)) == 1 and len(set(b)) == 1 and a[0] > 0 and b[0] > 0

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: bit-exact for codes, packed bytes, block constants, E4M3 codes and the
+bfloat16 dequantized weight; relative Frobenius error <= 2e-3 for bfloat16
+outputs of the GEMMs (H, grad_X) and <= 1e-4 for float32 outputs (H in
+float32, t, dA, dB) against the float64 oracle.
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from oracle import nf4, dq, layer, codebook, lloyd
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-3
+F32_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def lq():
+    import quantized_lora_fine_lq_amd as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_dev(torch, bits):
+    return dev(torch, bits.view(np.int16)).view(torch.bfloat16)
+
+
+def bf16_to_f32(t):
+    import torch
+    bits = host(t.contiguous().view(torch.int16)).view(np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def oracle_qweight(W, double_quant=True):
+    packed, c = nf4.quantize(W)
+    if double_quant:
+        code8, s2, mu = dq.double_quant(c)
+        cp = dq.dq_decode(code8, s2, mu)
+        return packed, c, (code8, s2, mu), cp
+    return packed, c, None, c
+
+
+# ---------------------------------------------------------------------------
+# quantize
+# ---------------------------------------------------------------------------
+def edge_weight(rng, N, K):
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    flat = W.reshape(-1, 64)
+    nb = flat.shape[0]
+    flat[0] = 0.0                                   # all-zero block
+    flat[1, ::2] = -0.0                             # signed zeros
+    flat[2] = np.float32(3e-39) * rng.standard_normal(64).astype(np.float32)  # subnormal block
+    flat[3] = np.float32(0.0123)                    # constant block
+    flat[4, 7] = 5.0                                # one huge outlier
+    t = nf4.thresholds()
+    # exact midpoints and their neighbours for several block constants
+    for b in range(5, min(nb, 40)):
+        c = np.float32(rng.uniform(0.001, 0.2))
+        vals = []
+        for ti in t:
+            w0 = np.float32(ti * c)
+            vals += [w0, np.nextafter(w0, np.float32(1)), np.nextafter(w0, np.float32(-1))]
+        vals = np.array(vals[:63], dtype=np.float32)
+        flat[b, :63] = vals
+        flat[b, 63] = c
+    return W
+
+
+@pytest.mark.parametrize("shape", [(64, 64), (192, 320), (1000, 128), (37, 1024)])
+def test_quantize_nf4_bit_exact(lq, torch, shape):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    W = edge_weight(rng, *shape) if shape[0] * shape[1] >= 64 * 64 else \
+        (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    codes, absmax = lq.quantize_nf4(dev(torch, W))
+    packed, c = nf4.quantize(W)
+    assert np.array_equal(host(absmax), c)
+    assert np.array_equal(host(codes), packed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_quantize_nf4_half_inputs(lq, torch, dtype):
+    rng = np.random.default_rng(5)
+    W32 = (rng.standard_normal((96, 256)) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        Wt = dev(torch, W32).to(torch.bfloat16)
+    else:
+        Wt = dev(torch, W32).to(torch.float16)
+    Wexact = host(Wt.float())
+    codes, absmax = lq.quantize_nf4(Wt)
+    packed, c = nf4.quantize(Wexact)
+    assert np.array_equal(host(absmax), c) and np.array_equal(host(codes), packed)
+
+
+def test_quantize_threshold_windows(lq, torch):
+    """Every float32 within +-2^15 ulps of each threshold (and of each level),
+    in blocks that also hold 1.0 so the block constant is 1 and x = w."""
+    t = nf4.thresholds()
+    pts = []
+    for v in list(t) + list(nf4.levels()[1:-1]):
+        b = np.float32(v).view(np.int32)
+        if v > 0:
+            pts.append((b + np.arange(-32768, 32768, dtype=np.int32)).view(np.float32))
+        else:
+            mag = np.float32(-v).view(np.int32) if v < 0 else np.int32(0)
+            m = mag + np.arange(-32768, 32768, dtype=np.int32)
+            m = m[m >= 0]
+            pts.append(-(m.view(np.float32)))
+    x = np.concatenate(pts).astype(np.float32)
+    x = x[np.abs(x) <= 1.0]
+    n63 = (x.size + 62) // 63
+    blocks = np.zeros((n63, 64), dtype=np.float32)
+    flat = np.zeros(n63 * 63, dtype=np.float32)
+    flat[:x.size] = x
+    blocks[:, :63] = flat.reshape(n63, 63)
+    blocks[:, 63] = 1.0
+    blocks[1::2, 63] = -1.0
+    W = blocks.reshape(n63, 64)
+    codes, absmax = lq.quantize_nf4(dev(torch, W))
+    packed, c = nf4.quantize(W)
+    assert np.array_equal(host(absmax), c)
+    assert np.array_equal(host(codes), packed)
+
+
+# ---------------------------------------------------------------------------
+# double quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n_b", [1, 255, 256, 1000, 16384, 300000])
+def test_double_quant_bit_exact(lq, torch, n_b):
+    rng = np.random.default_rng(n_b)
+    c = np.abs(rng.standard_normal(n_b) * 0.02 + 0.05).astype(np.float32)
+    if n_b > 300:
+        c[256:512] = np.float32(0.04)               # one constant block
+    q, s2, mu = lq.double_quant(dev(torch, c))
+    oq, os2, omu = dq.double_quant(c)
+    assert host(mu)[0] == omu
+    assert np.array_equal(host(s2), os2)
+    assert np.array_equal(host(q), oq)
+
+
+# ---------------------------------------------------------------------------
+# dequant
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("double", [False, True])
+def test_dequant_bit_exact(lq, torch, double):
+    rng = np.random.default_rng(11)
+    W = edge_weight(rng, 256, 512)
+    qw = lq.QWeight.from_weight(dev(torch, W), double_quantize=double)
+    got = bf16_to_f32(lq.dequant(qw))
+    packed, c, dqp, cp = oracle_qweight(W, double)
+    want = nf4.dequant(packed, cp, W.shape)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# forward / backward
+# ---------------------------------------------------------------------------
+def make_layer(rng_seed, N, K, M, r, alpha):
+    L = syn.small_layer(N, K, M, r, alpha, rng_seed)
+    W = syn.weight(L)
+    X = syn.activations(L)
+    A = syn.lora_a(L)
+    B = syn.lora_b(L)
+    return L, W, X, A, B
+
+
+def oracle_wd(W, double=True):
+    packed, c, dqp, cp = oracle_qweight(W, double)
+    return nf4.dequant(packed, cp, W.shape)
+
+
+@pytest.mark.parametrize("N,K,M,r,alpha", [
+    (384, 640, 300, 16, 32.0),     # ragged M, several tiles
+    (1024, 1024, 16, 16, 32.0),    # the 1024x1024 workload (GEMV path)
+    (520, 256, 17, 64, 16.0),      # just above the GEMV boundary, ragged N
+    (256, 512, 1, 16, 32.0),       # single token
+    (256, 512, 4, 24, 8.0),        # r not a multiple of 16
+])
+def test_forward(lq, torch, N, K, M, r, alpha):
+    L, W, X, A, B = make_layer(100 + M, N, K, M, r, alpha)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    Xd, Ad, Bd = bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits)
+    H, t = lq.qlora_forward(qw, Xd, Ad, Bd, alpha)
+    H32, _ = lq.qlora_forward(qw, Xd, Ad, Bd, alpha, out_dtype=torch.float32)
+    Wd = oracle_wd(W)
+    Href, tref = layer.forward(Wd, X.f32, A.f32, B.f32, alpha)
+    assert layer.rel_frobenius(host(t), tref) <= 1e-5
+    assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
+    assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
+
+
+def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
+    L, W, X, A, B = make_layer(7, 512, 1024, 16, 16, 32.0)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    args = (qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), 32.0)
+    H1, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    monkeypatch.setenv("LQ_FORCE_PATH", "gemm")
+    H2, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    Href, _ = layer.forward(oracle_wd(W), X.f32, A.f32, B.f32, 32.0)
+    assert layer.rel_frobenius(host(H1), Href) <= F32_TOL
+    assert layer.rel_frobenius(host(H2), Href) <= F32_TOL
+
+
+@pytest.mark.parametrize("M", [5, 300])
+def test_unit_vector_probe_bit_exact(lq, torch, M):
+    """X rows = e_k, B = 0: H[m, :] = W'[:, k_m] exactly (float32 output)."""
+    rng = np.random.default_rng(3)
+    N, K = 384, 512
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    ks = rng.integers(0, K, M)
+    X = np.zeros((M, K), dtype=np.uint16)
+    X[np.arange(M), ks] = 0x3F80       # 1.0 in bf16
+    A = syn.to_bf16_bits(rng.standard_normal((16, K)).astype(np.float32))
+    B = np.zeros((N, 16), dtype=np.uint16)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    H, _ = lq.qlora_forward(qw, bf16_dev(torch, X), bf16_dev(torch, A), bf16_dev(torch, B), 32.0,
+                            out_dtype=torch.float32)
+    Wd = oracle_wd(W)
+    assert np.array_equal(host(H), Wd[:, ks].T)
+
+
+@pytest.mark.parametrize("N,K,M,r,alpha", [
+    (384, 640, 300, 16, 32.0),
+    (512, 256, 96, 64, 16.0),
+    (264, 320, 33, 24, 8.0),
+])
+@pytest.mark.parametrize("recompute_t", [False, True])
+def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
+    L, W, X, A, B = make_layer(200 + M, N, K, M, r, alpha)
+    G = syn.grad_out(L)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    Xd, Ad, Bd, Gd = (bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits),
+                      bf16_dev(torch, G.bits))
+    _, t = lq.qlora_forward(qw, Xd, Ad, Bd, alpha)
+    gx, dA, dB = lq.qlora_backward(qw, Xd, Gd, Ad, Bd, alpha, t=None if recompute_t else t)
+    Wd = oracle_wd(W)
+    rX, rA, rB = layer.backward(Wd, X.f32, G.f32, A.f32, B.f32, alpha)
+    assert layer.rel_frobenius(bf16_to_f32(gx), rX) <= BF16_TOL
+    assert layer.rel_frobenius(host(dA), rA) <= F32_TOL
+    assert layer.rel_frobenius(host(dB), rB) <= F32_TOL
+
+
+def test_backward_grad_x_unit_probe(lq, torch):
+    """G rows = e_n, B = 0 (so u = 0): grad_X[m, :] = W'[n_m, :] exactly."""
+    rng = np.random.default_rng(4)
+    N, K, M = 256, 384, 40
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    ns = rng.integers(0, N, M)
+    G = np.zeros((M, N), dtype=np.uint16)
+    G[np.arange(M), ns] = 0x3F80
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    A = syn.to_bf16_bits(rng.standard_normal((16, K)).astype(np.float32))
+    B = np.zeros((N, 16), dtype=np.uint16)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    gx, dA, dB = lq.qlora_backward(qw, bf16_dev(torch, X), bf16_dev(torch, G), bf16_dev(torch, A),
+                                   bf16_dev(torch, B), 32.0)
+    Wd = oracle_wd(W)
+    assert np.array_equal(bf16_to_f32(gx), Wd[ns])
+    assert np.all(host(dA) == 0)
+
+
+# ---------------------------------------------------------------------------
+# codebook path
+# ---------------------------------------------------------------------------
+def codebook_case(seed, N, K):
+    rng = np.random.default_rng(seed)
+    sig = 0.02 * np.exp(0.3 * rng.standard_normal(N))
+    W = (rng.standard_normal((N, K)) * sig[:, None]).astype(np.float32)
+    bits = rng.integers(1, 5, N).astype(np.uint8)
+    L, T = lloyd.learn_codebooks(W, bits)
+    return W, bits, L, T
+
+
+def test_codebook_quantize_bit_exact(lq, torch):
+    W, bits, L, T = codebook_case(1, 200, 384)
+    codes, absmax, row_off = lq.quantize_codebook(dev(torch, W), dev(torch, bits), dev(torch, T))
+    packed, c, _ = codebook.quantize(W, bits, T)
+    assert np.array_equal(host(absmax), c)
+    assert np.array_equal(host(row_off), codebook.row_offsets(bits, 384))
+    assert np.array_equal(host(codes)[:packed.size], packed)
+
+
+def test_codebook_nf4_cross_check(lq, torch):
+    """4 bits with the NF4 thresholds/levels: dequant equals the NF4 path's."""
+    rng = np.random.default_rng(2)
+    N, K = 128, 256
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bits = np.full(N, 4, dtype=np.uint8)
+    T = np.tile(nf4.thresholds(), (N, 1)).astype(np.float32)
+    Lv = np.tile(nf4.levels(), (N, 1)).astype(np.float32)
+    qc = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    qn = lq.QWeight.from_weight(dev(torch, W))
+    assert np.array_equal(bf16_to_f32(lq.dequant(qc)), bf16_to_f32(lq.dequant(qn)))
+
+
+@pytest.mark.parametrize("M", [64, 300])
+def test_codebook_dequant_and_forward(lq, torch, M):
+    N, K, r, alpha = 256, 512, 16, 32.0
+    W, bits, Lv, T = codebook_case(3, N, K)
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    packed, c, _ = codebook.quantize(W, bits, T)
+    code8, s2, mu = dq.double_quant(c)
+    cp = dq.dq_decode(code8, s2, mu)
+    Wd = codebook.dequant(packed, bits, Lv, cp, N, K)
+    assert np.array_equal(bf16_to_f32(lq.dequant(qw)).view(np.uint32), Wd.view(np.uint32))
+    Ls = syn.small_layer(N, K, M, r, alpha, 300 + M)
+    X, A, B = syn.activations(Ls), syn.lora_a(Ls), syn.lora_b(Ls)
+    H, t = lq.qlora_forward(qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), alpha)
+    Href, _ = layer.forward(Wd, X.f32, A.f32, B.f32, alpha)
+    assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
