@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized-LoRA hot path on one MI355X.
+
+One step = the whole path on the Llama-7B q_proj workload (W 4096x4096
+float32 ~ N(0, 0.02^2), 2048 bf16 tokens = batch 4 x seq 512, LoRA r = 16,
+alpha = 32): NF4 quantize -> double quantization -> dequant to bf16 ->
+forward (t = X A^T, fused dequant-GEMM + LoRA) -> backward (u, dB, grad_X,
+dA). Inputs are resident in HBM before timing; four input sets are rotated
+so the 256 MB Infinity Cache cannot hold the step's working set.
+
+value = algorithmic GEMM + LoRA flops of the forward and backward per step
+divided by the step time (TFLOP/s); quantize / double quant / dequant add time
+but no flops. The JSON line also carries the roofline of the dominant kernel
+(the forward dequant-GEMM), the CPU oracle timed on the host, and a
+per-kernel table (GB/s or TFLOP/s against MI355X peaks) for the other
+workloads: the MLP pair (4096 <-> 11008, 4096 tokens, r = 64) and the decode
+GEMV (28672 x 8192, 1 / 4 / 16 tokens).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "dequant-GEMM+LoRA TFLOP/s & quantize/GEMV GB/s; % of MFMA/HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
+    ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the steps")
+    return ap.parse_args()
+
+
+class Dev:
+    """Device copies of one layer's inputs and preallocated outputs."""
+
+    def __init__(self, torch, lq, layer, W, X, A, B, G, M):
+        import numpy as np
+        dev = torch.device("cuda")
+        self.layer, self.M, self.r = layer, M, layer.r
+        N, K, r = layer.N, layer.K, layer.r
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        self.W = torch.from_numpy(W).to(dev)
+        self.X = bf(X.bits)
+        self.A = bf(A.bits)
+        self.B = bf(B.bits)
+        self.G = bf(G.bits) if G is not None else None
+        n_b = N * K // 64
+        n_d = (n_b + 255) // 256
+        self.codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+        self.absmax = torch.empty(n_b, dtype=torch.float32, device=dev)
+        self.aq = torch.empty(n_b, dtype=torch.uint8, device=dev)
+        self.s2 = torch.empty(n_d, dtype=torch.float32, device=dev)
+        self.mu = torch.empty(1, dtype=torch.float32, device=dev)
+        self.dq_ws_bytes = lq.lib.lq_double_quant_workspace(n_b, 256)
+        self.dq_ws = torch.empty(self.dq_ws_bytes, dtype=torch.uint8, device=dev)
+        self.qw = lq.QWeight(N, K, self.codes, absmax_q=self.aq, dq_scale=self.s2, dq_mean=self.mu)
+        self.Wd = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        self.t = torch.empty(M, r, dtype=torch.float32, device=dev)
+        self.H = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        self.ld_ws_bytes = lq.lib.lq_lora_down_workspace(M, K, r)
+        self.ld_ws = torch.empty(max(self.ld_ws_bytes, 1), dtype=torch.uint8, device=dev)
+        if G is not None:
+            self.gX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+            self.dA = torch.empty(r, K, dtype=torch.float32, device=dev)
+            self.dB = torch.empty(N, r, dtype=torch.float32, device=dev)
+            self.u = torch.empty(M, r, dtype=torch.float32, device=dev)
+            self.bw_ws_bytes = lq.lib.lq_backward_workspace(self.qw.ref(), M, r)
+            self.bw_ws = torch.empty(self.bw_ws_bytes, dtype=torch.uint8, device=dev)
+
+
+class Calls:
+    """The library entry points bound to one Dev's buffers (raw C-ABI calls)."""
+
+    def __init__(self, torch, lq, d: Dev):
+        self.lq, self.d = lq, d
+        self.lib = lq.lib
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.P = P
+        L = d.layer
+        self.alpha = float(L.alpha)
+        self.args_q = (P(d.W), 0, L.N, L.K, 64, P(d.codes), P(d.absmax), self.stream)
+        self.args_dq = (P(d.absmax), L.N * L.K // 64, 256, P(d.aq), P(d.s2), P(d.mu), P(d.dq_ws),
+                        d.dq_ws_bytes, self.stream)
+        self.args_deq = (d.qw.ref(), P(d.Wd), self.stream)
+        self.args_ld = (P(d.X), d.M, L.K, P(d.A), d.r, P(d.t), P(d.ld_ws), d.ld_ws_bytes, self.stream)
+        self.args_fwd = (d.qw.ref(), P(d.X), d.M, P(d.t), P(d.B), d.r, self.alpha, P(d.H), 1, self.stream)
+        if d.G is not None:
+            self.args_bwd = (d.qw.ref(), P(d.X), P(d.G), d.M, P(d.A), P(d.B), d.r, self.alpha, P(d.t),
+                             P(d.gX), P(d.dA), P(d.dB), P(d.bw_ws), d.bw_ws_bytes, self.stream)
+            self.args_gx = (d.qw.ref(), P(d.G), d.M, P(d.u), P(d.A), d.r, self.alpha, P(d.gX), self.stream)
+
+    def chk(self, st, name):
+        if st != 0:
+            raise RuntimeError(f"{name} failed: {st}")
+
+    def quantize(self):
+        self.chk(self.lib.lq_quantize_nf4(*self.args_q), "quantize")
+
+    def double_quant(self):
+        self.chk(self.lib.lq_double_quant(*self.args_dq), "double_quant")
+
+    def dequant(self):
+        self.chk(self.lib.lq_dequant(*self.args_deq), "dequant")
+
+    def lora_down(self):
+        self.chk(self.lib.lq_lora_down(*self.args_ld), "lora_down")
+
+    def fwd_gemm(self):
+        self.chk(self.lib.lq_dequant_gemm(*self.args_fwd), "dequant_gemm")
+
+    def backward(self):
+        self.chk(self.lib.lq_qlora_backward(*self.args_bwd), "backward")
+
+    def grad_x(self):
+        self.chk(self.lib.lq_dequant_gemm_t(*self.args_gx), "dequant_gemm_t")
+
+    def step(self):
+        self.quantize()
+        self.double_quant()
+        self.dequant()
+        self.lora_down()
+        self.fwd_gemm()
+        self.backward()
+
+
+def make_devs(torch, lq, syn, name, n_sets, M=None, with_grad=True):
+    import numpy as np
+    L = syn.LAYERS[name]
+    M = L.M if M is None else M
+    W = syn.weight(L)
+    X = syn.activations(L, M)
+    A, B = syn.lora_a(L), syn.lora_b(L)
+    G = syn.grad_out(L, M) if with_grad else None
+    devs = [Dev(torch, lq, L, W, X, A, B, G, M)]
+    for k in range(1, n_sets):
+        # extra copies (distinct buffers, same values) defeat the Infinity Cache
+        devs.append(Dev(torch, lq, L, W, X, A, B, G, M))
+    return devs
+
+
+def time_ms(torch, fns, iters, warmup=3):
+    """Average ms per call of fns[i % len(fns)] over `iters` back-to-back
+    calls on the current stream (HIP events)."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fns[i % len(fns)]()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def layer_flops(L, M):
+    N, K, r = L.N, L.K, L.r
+    fwd_gemm = 2 * M * N * K + 2 * M * N * r
+    lora_down = 2 * M * K * r
+    bwd = 2 * M * N * K + 4 * M * r * (N + K)
+    gx = 2 * M * N * K + 2 * M * K * r
+    return {"fwd_gemm": fwd_gemm, "lora_down": lora_down, "fwd": fwd_gemm + lora_down, "bwd": bwd, "grad_x": gx}
+
+
+def codec_bytes(L, M=0):
+    n = L.N * L.K
+    n_b = n // 64
+    n_d = (n_b + 255) // 256
+    packed = n // 2 + n_b + 4 * n_d + 4
+    return {
+        "quantize": 4 * n + n // 2 + 4 * n_b,
+        "double_quant": 4 * n_b + n_b + 4 * n_d + 4,
+        "dequant": packed + 2 * n,
+        "gemv": packed + 2 * L.K * M + 2 * L.r * L.K + 2 * L.N * L.r + 2 * L.N * M + 4 * M * L.r,
+    }
+
+
+def cpu_baseline(syn):
+    """The oracle (numpy / float64 BLAS) on one full q_proj step."""
+    import numpy as np
+    from oracle import nf4, dq, layer
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    L = syn.LAYERS["q_proj"]
+    W, X, A, B, G = syn.weight(L), syn.activations(L), syn.lora_a(L), syn.lora_b(L), syn.grad_out(L)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        packed, c = nf4.quantize(W)
+        code8, s2, mu = dq.double_quant(c)
+        Wd = nf4.dequant(packed, dq.dq_decode(code8, s2, mu), W.shape)
+        H, t = layer.forward(Wd, X.f32, A.f32, B.f32, L.alpha)
+        dX, dA, dB = layer.backward(Wd, X.f32, G.f32, A.f32, B.f32, L.alpha)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[1]
+    fl = layer_flops(L, L.M)
+    return {"value": round((fl["fwd"] + fl["bwd"]) / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "one full q_proj step (quantize, double quant, dequant, float64 forward + backward) "
+                      "on the host CPU, median of 3"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantized-LoRA hot path here is a single-GPU "
+              "kernel library (multi-GPU sharding is described in DESIGN.md, not run).", flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import quantized_lora_fine_lq_amd as lq
+    import synthetic as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log("generating q_proj inputs")
+    devs = make_devs(torch, lq, syn, "q_proj", args.sets)
+    calls = [Calls(torch, lq, d) for d in devs]
+    L = syn.LAYERS["q_proj"]
+    fl = layer_flops(L, L.M)
+    step_flops = fl["fwd"] + fl["bwd"]
+
+    # ---- the timed step -------------------------------------------------
+    for i in range(args.warmup):
+        calls[i % len(calls)].step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        calls[i % len(calls)].step()
+    e1.record()
+    e1.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    log(f"step: {ms_step:.4f} ms  ({value:.1f} TFLOP/s), wall {wall:.3f} s")
+
+    # ---- dominant kernel: forward dequant-GEMM on q_proj -------------------
+    for c in calls:
+        c.lora_down()
+    fwd_ms = time_ms(torch, [c.fwd_gemm for c in calls], 50)
+    fwd_tflops = fl["fwd_gemm"] / (fwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "k_dq_gemm<ProdFwdNF4> (q_proj, M=2048)",
+                "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_us": round(fwd_ms * 1e3, 2),
+                "algorithmic_flop_per_launch": fl["fwd_gemm"]}
+
+    kernels = {}
+    if not args.no_kernels:
+        def rec(name, ms, work, unit):
+            if unit == "GB/s":
+                ach = work / (ms * 1e-3) / 1e9
+                kernels[name] = {"us": round(ms * 1e3, 2), "GB/s": round(ach, 1),
+                                 "frac_hbm": round(ach / HBM_PEAK_GBS, 4), "bytes": work}
+            else:
+                ach = work / (ms * 1e-3) / 1e12
+                kernels[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(ach, 1),
+                                 "frac_mfma": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "flop": work}
+            log(name, kernels[name])
+
+        cb = codec_bytes(L)
+        rec("q_proj.quantize_nf4", time_ms(torch, [c.quantize for c in calls], 40), cb["quantize"], "GB/s")
+        rec("q_proj.double_quant", time_ms(torch, [c.double_quant for c in calls], 40), cb["double_quant"], "GB/s")
+        rec("q_proj.dequant", time_ms(torch, [c.dequant for c in calls], 40), cb["dequant"], "GB/s")
+        rec("q_proj.lora_down", time_ms(torch, [c.lora_down for c in calls], 40), fl["lora_down"], "TFLOP/s")
+        rec("q_proj.dequant_gemm_fwd", fwd_ms, fl["fwd_gemm"], "TFLOP/s")
+        rec("q_proj.backward", time_ms(torch, [c.backward for c in calls], 30), fl["bwd"], "TFLOP/s")
+        del calls, devs
+        torch.cuda.empty_cache()
+
+        for name in ("mlp_up", "mlp_down"):
+            log(f"generating {name} inputs")
+            Lm = syn.LAYERS[name]
+            dv = make_devs(torch, lq, syn, name, 2)
+            cs = [Calls(torch, lq, d) for d in dv]
+            for c in cs:
+                c.quantize(); c.double_quant(); c.lora_down()
+            flm = layer_flops(Lm, Lm.M)
+            rec(f"{name}.quantize_nf4", time_ms(torch, [c.quantize for c in cs], 20), codec_bytes(Lm)["quantize"], "GB/s")
+            for c in cs:
+                c.double_quant()
+            rec(f"{name}.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in cs], 20), flm["fwd_gemm"], "TFLOP/s")
+            rec(f"{name}.backward", time_ms(torch, [c.backward for c in cs], 10), flm["bwd"], "TFLOP/s")
+            del cs, dv
+            torch.cuda.empty_cache()
+
+        log("generating decode inputs")
+        Ld = syn.LAYERS["decode"]
+        dv = make_devs(torch, lq, syn, "decode", 1, M=16, with_grad=False)
+        c0 = Calls(torch, lq, dv[0])
+        rec("decode.quantize_nf4", time_ms(torch, [c0.quantize], 10), codec_bytes(Ld)["quantize"], "GB/s")
+        rec("decode.double_quant", time_ms(torch, [c0.double_quant], 10), codec_bytes(Ld)["double_quant"], "GB/s")
+        rec("decode.dequant", time_ms(torch, [c0.dequant], 10), codec_bytes(Ld)["dequant"], "GB/s")
+        # 9 copies of the 121 MB quantized weight rotate through the GEMV
+        copies = [dv[0].qw]
+        keep = []
+        for k in range(8):
+            cc = dv[0].codes.clone(); aq = dv[0].aq.clone(); s2 = dv[0].s2.clone(); mu = dv[0].mu.clone()
+            keep.append((cc, aq, s2, mu))
+            copies.append(lq.QWeight(Ld.N, Ld.K, cc, absmax_q=aq, dq_scale=s2, dq_mean=mu))
+        del dv[0].W
+        torch.cuda.empty_cache()
+        for M in (1, 4, 16):
+            X = dv[0].X[:M].contiguous()
+            t = torch.zeros(M, Ld.r, dtype=torch.float32, device="cuda")
+            lq.lora_down(X, dv[0].A, t)
+            H = torch.empty(M, Ld.N, dtype=torch.bfloat16, device="cuda")
+            fns = [(lambda q=q: lq.dequant_gemm(q, X, t, dv[0].B, Ld.alpha, out=H)) for q in copies]
+            rec(f"decode.gemv_M{M}", time_ms(torch, fns, 45), codec_bytes(Ld, M)["gemv"], "GB/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "q_proj 4096x4096 NF4 + double quant, 2048 tokens (batch 4 x seq 512), "
+                               "LoRA r=16 alpha=32; step = quantize + double quant + dequant + forward + backward",
+                   "global_batch": L.M, "tokens": L.M, "N": L.N, "K": L.K, "r": L.r, "alpha": L.alpha,
+                   "input_sets_rotated": args.sets},
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one q_proj step")
+        out["cpu_baseline"] = cpu_baseline(syn)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

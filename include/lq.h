@@ -201,6 +201,39 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M,
                      void* H, int32_t h_dtype, float* t_save,
                      void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for lq_lora_down with M rows, K columns and rank r. */
+size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r);
+
+/*
+ * First stage of the forward ([QLoRA] introduction, the A x term):
+ * t = X A^T in float32.
+ *   X [M, K] bf16, A [r, K] bf16, t [M, r] float32 (written).
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (M, K <= 0, K % 8 != 0, r outside
+ * [1, 128]), LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Second stage of the forward ([QLoRA] introduction): given t = X A^T,
+ * H = X W'^T + (alpha / r) t B^T with W' dequantized inside the kernel (the
+ * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM). Needs no workspace.
+ * Arguments as lq_qlora_forward; t [M, r] float32 is read.
+ */
+int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
+                    const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
+                    void* stream);
+
+/*
+ * The transposed dequant-GEMM of the backward ([QLoRA] introduction: the
+ * gradient flows through the frozen 4-bit base): given u = G B,
+ * grad_X = G W' + (alpha / r) u A, bfloat16 output.
+ *   G [M, N] bf16, u [M, r] float32, A [r, K] bf16, grad_X [M, K] bf16.
+ * NF4 weights only (LQ_ERR_UNSUPPORTED otherwise); N % 8 == 0 (LQ_ERR_SHAPE).
+ */
+int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
+                      const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X, void* stream);
+
 /* Workspace bytes for lq_qlora_backward with M tokens and rank r. */
 size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
@@ -214,6 +247,8 @@ size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *   G [M, N] bf16; X [M, K] bf16 (needed for dA and when t_saved is NULL)
  *   t_saved [M, r] float32 from the forward, or NULL to recompute t = X A^T
  *   grad_X, dA, dB may each be NULL to skip that output.
+ * Requires N % 8 == 0 (LQ_ERR_SHAPE); grad_X needs an NF4 weight
+ * (LQ_ERR_UNSUPPORTED for a codebook weight).
  * Errors: as lq_qlora_forward.
  */
 int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,

@@ -11,7 +11,7 @@ Two layers, both argument marshalling only:
   entry points. All arithmetic runs in the library's HIP kernels.
 
 Importing fails loudly if liblq.so has not been built
-(``python -m quantized_lora_fine_lq_amd.build``).
+(``python quantized_lora_fine_lq_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -66,6 +66,10 @@ SIGNATURES = {
                                          c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_quantize_codebook": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
                                             c_vp, c_vp, c_vp]),
+    "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
+    "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "lq_dequant_gemm": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_i32, c_vp]),
+    "lq_dequant_gemm_t": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_vp]),
 }
 
 
@@ -77,7 +81,7 @@ class LqError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_lora_fine_lq_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_lora_fine_lq_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(handle, name)
@@ -248,6 +252,41 @@ def qlora_backward(qw: QWeight, X, G, A, B, alpha: float, t=None,
                                  _ptr(gx), _ptr(dA), _ptr(dB), _ptr(ws), ws_bytes, _stream(dev)),
            "lq_qlora_backward")
     return gx, dA, dB
+
+
+def lora_down(X, A, t=None):
+    """t = X A^T (float32 [M, r])."""
+    torch = _torch()
+    M, K = X.shape
+    r = A.shape[0]
+    t = torch.empty(M, r, dtype=torch.float32, device=X.device) if t is None else t
+    ws_bytes = lib.lq_lora_down_workspace(M, K, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=X.device)
+    _check(lib.lq_lora_down(_ptr(X), M, K, _ptr(A), r, _ptr(t), _ptr(ws), ws_bytes, _stream(X.device)),
+           "lq_lora_down")
+    return t
+
+
+def dequant_gemm(qw: QWeight, X, t, B, alpha: float, out=None, out_dtype=None):
+    """H = X W'^T + (alpha/r) t B^T given t."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    M, r = X.shape[0], t.shape[1]
+    H = torch.empty(M, qw.N, dtype=out_dtype, device=X.device) if out is None else out
+    h_code = LQ_F32 if H.dtype == torch.float32 else LQ_BF16
+    _check(lib.lq_dequant_gemm(qw.ref(), _ptr(X), M, _ptr(t), _ptr(B), r, float(alpha), _ptr(H), h_code,
+                               _stream(X.device)), "lq_dequant_gemm")
+    return H
+
+
+def dequant_gemm_t(qw: QWeight, G, u, A, alpha: float, out=None):
+    """grad_X = G W' + (alpha/r) u A given u = G B (bfloat16 [M, K])."""
+    torch = _torch()
+    M, r = G.shape[0], u.shape[1]
+    gx = torch.empty(M, qw.K, dtype=torch.bfloat16, device=G.device) if out is None else out
+    _check(lib.lq_dequant_gemm_t(qw.ref(), _ptr(G), M, _ptr(u), _ptr(A), r, float(alpha), _ptr(gx),
+                                 _stream(G.device)), "lq_dequant_gemm_t")
+    return gx
 
 
 def row_offsets(row_bits_host, K: int):

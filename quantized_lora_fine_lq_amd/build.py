@@ -1,6 +1,6 @@
 """Build liblq.so (the HIP library behind include/lq.h) for gfx950, in-tree.
 
-    python -m quantized_lora_fine_lq_amd.build
+    python quantized_lora_fine_lq_amd/build.py
 
 hipcc cross-compiles without a GPU. Flags: -O3, no floating-point contraction
 (the codec kernels are bit-exact and spell out every fused multiply-add),

@@ -176,6 +176,46 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   return launch_status(e);
 }
 
+size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r) {
+  if (M <= 0 || K <= 0 || r < 1 || r > 128) return 0;
+  return align_up(row_skinny_ws_floats(M, K, r) * sizeof(float));
+}
+
+int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  if (!X || !A || !t) return LQ_ERR_ARG;
+  if (M <= 0 || K <= 0 || K % 8 != 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
+  const size_t need = lq_lora_down_workspace(M, K, r);
+  if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_row_skinny(X, M, K, A, false, r, t, (float*)workspace, (hipStream_t)stream));
+}
+
+int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
+                    const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
+                    void* stream) {
+  QWeight q;
+  const int st = check_qweight(w, &q);
+  if (st != LQ_OK) return st;
+  if (!X || !t || !B || !H) return LQ_ERR_ARG;
+  if (M <= 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
+  if (h_dtype != LQ_BF16 && h_dtype != LQ_F32) return LQ_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const float scale = alpha / (float)r;
+  if (use_gemv(q, M)) return launch_status(launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s));
+  return launch_status(launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, s));
+}
+
+int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
+                      const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X, void* stream) {
+  QWeight q;
+  const int st = check_qweight(w, &q);
+  if (st != LQ_OK) return st;
+  if (q.format != LQ_FMT_NF4) return LQ_ERR_UNSUPPORTED;
+  if (!G || !u || !A || !grad_X) return LQ_ERR_ARG;
+  if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
+  return launch_status(launch_gemm_bwd(q, G, M, u, A, r, alpha / (float)r, grad_X, (hipStream_t)stream));
+}
+
 size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r) {
   QWeight q;
   if (check_qweight(w, &q) != LQ_OK || M <= 0 || r < 1 || r > 128) return 0;

@@ -77,8 +77,9 @@ def edge_weight(rng, N, K):
         for ti in t:
             w0 = np.float32(ti * c)
             vals += [w0, np.nextafter(w0, np.float32(1)), np.nextafter(w0, np.float32(-1))]
-        vals = np.array(vals[:63], dtype=np.float32)
-        flat[b, :63] = vals
+        vals = np.array(vals, dtype=np.float32)           # 45 values
+        flat[b, :vals.size] = vals
+        flat[b, vals.size:63] = (c * rng.uniform(-1, 1, 63 - vals.size)).astype(np.float32)
         flat[b, 63] = c
     return W
 
