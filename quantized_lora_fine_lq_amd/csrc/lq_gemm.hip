@@ -50,195 +50,238 @@ __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
   lo = v - hi;
 }
 
-// A-side fragments of one k-step for one wave: [2 row tiles][4 sub-steps].
-__device__ __forceinline__ void load_a_frags(const GemmParams& p, int it, int nMain, int64_t mrow0,
-                                             int li, int lh, u32x4_t (&a)[2][4]) {
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+
+// A fragments of one 64-wide step of the main segment for one wave
+// ([2 row tiles][4 sub-steps]). arow[rt] points at the lane's row (rows past
+// M were clamped to row M-1: their outputs are never stored) plus its 32h
+// column offset. An 8-column group past the end of the contraction reads
+// column 0 instead -- the Bt tile is zero there, so it adds nothing.
+template <bool TAIL>
+__device__ __forceinline__ void load_a_main(const GemmParams& p, int it, const uint16_t* const (&arow)[2],
+                                            int lh, u32x4_t (&a)[2][4]) {
+  const int64_t col0 = (int64_t)it * BK;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int64_t off = col0 + 8 * s;
+      if (TAIL) off = (col0 + 32 * lh + 8 * s + 8 <= p.Kc) ? off : -32 * lh;
+      a[rt][s] = ld16(arow[rt] + off);
+    }
+}
+
+// A fragments of the LoRA segment: columns [0, r) carry hi(s*L), [r, 2r)
+// carry lo(s*L), the rest 0 (L = t forward, u backward).
+__device__ void load_a_lora(const GemmParams& p, int jt, int64_t mrow0, int li, int lh,
+                            u32x4_t (&a)[2][4]) {
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int64_t row = mrow0 + 32 * rt + li;
-    const bool row_ok = row < p.M;
-    if (it < nMain) {
-      const uint16_t* src = p.A + row * p.Kc;
+    const int64_t row = min(mrow0 + 32 * rt + li, p.M - 1);
+    const float* src = p.la + row * p.r;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int64_t col = (int64_t)it * BK + 32 * lh + 8 * s;
-        if (row_ok && col + 8 <= p.Kc) {
-          a[rt][s] = *reinterpret_cast<const u32x4_t*>(src + col);
-        } else {
-          zero(a[rt][s]);
-          if (row_ok)
-            for (int e = 0; e < 8; e += 2) {
-              const uint32_t lo = (col + e < p.Kc) ? src[col + e] : 0u;
-              const uint32_t hi = (col + e + 1 < p.Kc) ? src[col + e + 1] : 0u;
-              a[rt][s][e / 2] = lo | (hi << 16);
-            }
+    for (int s = 0; s < 4; ++s) {
+      const int c0 = jt * BK + 32 * lh + 8 * s;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        float x = 0.0f;
+        if (c < 2 * p.r) {
+          float hi, lo;
+          split_bf16(p.s * src[c < p.r ? c : c - p.r], hi, lo);
+          x = (c < p.r) ? hi : lo;
         }
+        v[e] = x;
       }
-    } else {  // LoRA segment: columns [0, r) hi part, [r, 2r) lo part
-      const float* src = p.la + row * p.r;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c0 = (it - nMain) * BK + 32 * lh + 8 * s;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = c0 + e;
-          float x = 0.0f;
-          if (row_ok && c < 2 * p.r) {
-            float hi, lo;
-            split_bf16(p.s * src[c < p.r ? c : c - p.r], hi, lo);
-            x = (c < p.r) ? hi : lo;
-          }
-          v[e] = x;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[rt][s][e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-      }
+      for (int e = 0; e < 4; ++e) a[rt][s][e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
     }
   }
 }
 
+// 32 MFMAs of one 64-wide step: wave tile 64 x 128 = [2 row tiles] x [4 col
+// tiles]. B fragments of sub-step s+1 are read from LDS while sub-step s
+// multiplies.
+__device__ __forceinline__ void mfma_step(const uint16_t* sBt, const u32x4_t (&a)[2][4],
+                                          f32x16_t (&acc)[2][4], int li, int lh) {
+  const uint16_t* base = sBt + li * PITCH + 32 * lh;
+  u32x4_t b[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) b[0][ct] = ld16(base + 32 * ct * PITCH);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s < 3) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) b[(s + 1) & 1][ct] = ld16(base + 32 * ct * PITCH + 8 * (s + 1));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[rt][s]), as_bf16x8(b[s & 1][ct]),
+                                                              acc[rt][ct], 0, 0, 0);
+  }
+}
+
+// 32 bf16 -> LDS: thread (row tid/2, half) fills Bt[row][32 half .. +32).
+__device__ __forceinline__ void lora_fill_rows(const GemmParams& p, int jt, int64_t n0,
+                                               uint16_t* sB, bool fwd) {
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int64_t n = n0 + row;
+  const int64_t ncols = fwd ? p.w.N : p.w.K;
+  const int c0 = jt * BK + 32 * half;
+  uint32_t h[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    const int c = c0 + e;
+    uint32_t v = 0;
+    if (n < ncols && c < 2 * p.r) {
+      const int j = c < p.r ? c : c - p.r;
+      v = fwd ? p.lb[n * p.r + j] : p.lb[(int64_t)j * p.w.K + n];
+    }
+    h[e] = v;
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    u32x4_t v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
+    dst[d] = v;
+  }
+}
+
 // ---- Bt producers -----------------------------------------------------------
+// load() only issues global loads into members; store() decodes and writes
+// the dequantized bf16 tile to LDS. Keeping arithmetic out of load() lets
+// the loads stay in flight across a whole MFMA step.
+
+// Block constant from the loaded parts: float32 (DQ = false) or
+// fma(E4M3(q8), s2, mean) (DQ = true).
+template <bool DQ>
+__device__ __forceinline__ float const_of(float c0, uint32_t q8, float s2, float mean) {
+  return DQ ? __builtin_fmaf(e4m3_decode(q8), s2, mean) : c0;
+}
+
 // Forward NF4: Bt[n][k] = W'[n0 + n][64 it + k]; thread -> (row tid/2, 32 codes).
+template <bool DQ>
 struct ProdFwdNF4 {
-  __device__ void init(const GemmParams&, int64_t) {}
+  const uint8_t* crow;   // codes of the thread's row at its 32-column half
+  int64_t blk0;          // block index of step 0
   u32x4_t codes;
-  float cst;        // float32 constant, or decoded E4M3 value before the fma
-  float s2;
-  __device__ void load(const GemmParams& p, int it, int nMain, int64_t n0) {
+  float c0, s2;
+  uint32_t q8;
+  bool live;             // false for a padding step past the end: tile of zeros
+  __device__ void init(const GemmParams& p, int64_t n0) {
     const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t n = n0 + row;
-    if (it < nMain) {
-      if (n < p.w.N) {
-        const int64_t e0 = n * p.w.K + (int64_t)it * BK + 32 * half;
-        codes = *reinterpret_cast<const u32x4_t*>(p.w.codes + e0 / 2);
-        const int64_t blk = e0 >> 6;
-        if (p.w.qc.absmax) { cst = p.w.qc.absmax[blk]; s2 = 0.f; }
-        else { cst = e4m3_decode(p.w.qc.absmax_q[blk]); s2 = p.w.qc.dq_scale[blk >> 8]; }
-      } else {
-        zero(codes); cst = 0.f; s2 = 0.f;
-      }
-    } else {  // LoRA segment: Bt[n][c] = B[n][c mod r] for c < 2r
-      const int c0 = (it - nMain) * BK + 32 * half;
-      uint32_t h[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int c = c0 + e;
-        h[e] = (n < p.w.N && c < 2 * p.r) ? p.lb[n * p.r + (c < p.r ? c : c - p.r)] : 0u;
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4_t v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
-        lora[d] = v;
-      }
+    const int64_t n = min(n0 + row, p.w.N - 1);   // rows past N: outputs never stored
+    const int64_t e0 = n * p.w.K + 32 * half;
+    crow = p.w.codes + e0 / 2;
+    blk0 = e0 >> 6;
+  }
+  __device__ void load(const GemmParams& p, int step, int nMain) {
+    live = step < nMain;
+    const int it = min(step, nMain - 1);
+    codes = ld16(crow + (int64_t)it * (BK / 2));
+    const int64_t blk = blk0 + it;
+    if (DQ) {
+      q8 = p.w.qc.absmax_q[blk];
+      s2 = p.w.qc.dq_scale[blk >> 8];
+    } else {
+      c0 = p.w.qc.absmax[blk];
     }
   }
-  u32x4_t lora[4];
-  __device__ void store(const GemmParams& p, int it, int nMain, uint16_t* sB,
-                        const f32x2_t* sPair, float mean) {
+  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t* sPair, float mean) {
     const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const float cp = live ? const_of<DQ>(c0, q8, s2, mean) : 0.0f;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
-    if (it < nMain) {
-      const float cp = p.w.qc.absmax ? cst : __builtin_fmaf(cst, s2, mean);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4_t o;
+    for (int d = 0; d < 4; ++d) {
+      u32x4_t o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x2_t q = sPair[(codes[d] >> (8 * b)) & 0xFFu];
-          o[b] = pack_bf16x2(q.x * cp, q.y * cp);
-        }
-        dst[d] = o;
+      for (int b = 0; b < 4; ++b) {
+        const f32x2_t q = sPair[(codes[d] >> (8 * b)) & 0xFFu];
+        o[b] = pack_bf16x2(q.x * cp, q.y * cp);
       }
-    } else {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) dst[d] = lora[d];
+      dst[d] = o;
     }
+  }
+  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
+    lora_fill_rows(p, jt, n0, sB, true);
   }
 };
 
 // Backward NF4: Bt[c][n] = W'[64 it + n][n0 + c] (the contraction runs over
 // W's rows). Thread -> 8 rows x 4 columns: g8 = tid % 8 picks rows
-// 8*g8 .. 8*g8+7 of the 64-row step, kq = tid / 8 picks columns 4kq .. 4kq+3.
+// 8*g8 .. 8*g8+7 of the step, kq = tid / 8 picks columns 4kq .. 4kq+3.
+// Rows past N must contribute zero: their constant is forced to 0.
+template <bool DQ>
 struct ProdBwdNF4 {
-  __device__ void init(const GemmParams&, int64_t) {}
-  uint32_t code16[8];   // 4 codes (2 bytes) per row
-  float cst[8];
-  float s2[8];
-  u32x4_t lora[4];
-  __device__ void load(const GemmParams& p, int it, int nMain, int64_t n0) {
-    if (it < nMain) {
-      const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
-      const int64_t k = n0 + 4 * kq;
+  int64_t e00;           // flat element of (row 8*g8, column k) at step 0
+  uint32_t code16[8];
+  float c0[8], s2[8];
+  uint32_t q8[8];
+  int nvalid;            // rows of this step below N (0..8)
+  __device__ void init(const GemmParams& p, int64_t n0) {
+    const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
+    const int64_t k = min(n0 + 4 * kq, p.w.K - 4);   // columns past K: outputs never stored
+    e00 = (int64_t)(8 * g8) * p.w.K + k;
+  }
+  __device__ void load(const GemmParams& p, int step, int nMain) {
+    const int g8 = threadIdx.x & 7;
+    const int it = min(step, nMain - 1);
+    const int64_t nfirst = (int64_t)it * BK + 8 * g8;
+    nvalid = step < nMain ? (int)min((int64_t)8, max((int64_t)0, p.w.N - nfirst)) : 0;
+    const int64_t estep = e00 + (int64_t)it * BK * p.w.K;
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const int64_t n = (int64_t)it * BK + 8 * g8 + rr;
-        if (n < p.w.N && k < p.w.K) {
-          const int64_t e0 = n * p.w.K + k;
-          code16[rr] = *reinterpret_cast<const uint16_t*>(p.w.codes + e0 / 2);
-          const int64_t blk = e0 >> 6;
-          if (p.w.qc.absmax) { cst[rr] = p.w.qc.absmax[blk]; s2[rr] = 0.f; }
-          else { cst[rr] = e4m3_decode(p.w.qc.absmax_q[blk]); s2[rr] = p.w.qc.dq_scale[blk >> 8]; }
-        } else {
-          code16[rr] = 0; cst[rr] = 0.f; s2[rr] = 0.f;
-        }
-      }
-    } else {  // LoRA segment: Bt[c][j] = A[j mod r][n0 + c], thread -> (c = tid/2, 32 j)
-      const int cl = threadIdx.x >> 1, half = threadIdx.x & 1;
-      const int64_t kcol = n0 + cl;
-      const int j0 = (it - nMain) * BK + 32 * half;
-      uint32_t h[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int j = j0 + e;
-        h[e] = (kcol < p.w.K && j < 2 * p.r) ? p.lb[(int64_t)(j < p.r ? j : j - p.r) * p.w.K + kcol] : 0u;
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4_t v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
-        lora[d] = v;
+    for (int rr = 0; rr < 8; ++rr) {
+      const int64_t e0 = estep + (int64_t)(rr < nvalid ? rr : 0) * p.w.K;
+      code16[rr] = *reinterpret_cast<const uint16_t*>(p.w.codes + e0 / 2);
+      const int64_t blk = e0 >> 6;
+      if (DQ) {
+        q8[rr] = p.w.qc.absmax_q[blk];
+        s2[rr] = p.w.qc.dq_scale[blk >> 8];
+      } else {
+        c0[rr] = p.w.qc.absmax[blk];
       }
     }
   }
-  __device__ void store(const GemmParams& p, int it, int nMain, uint16_t* sB,
-                        const f32x2_t* sPair, float mean) {
-    if (it < nMain) {
-      const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
-      float v[8][4];
+  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t* sPair, float mean) {
+    const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
+    float v[8][4];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const float cp = p.w.qc.absmax ? cst[rr] : __builtin_fmaf(cst[rr], s2[rr], mean);
-        const f32x2_t q0 = sPair[code16[rr] & 0xFFu];         // columns 4kq, 4kq+1
-        const f32x2_t q1 = sPair[(code16[rr] >> 8) & 0xFFu];  // columns 4kq+2, 4kq+3
-        v[rr][0] = q0.x * cp; v[rr][1] = q0.y * cp;
-        v[rr][2] = q1.x * cp; v[rr][3] = q1.y * cp;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4_t o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q][kk], v[2 * q + 1][kk]);
-        *reinterpret_cast<u32x4_t*>(sB + (4 * kq + kk) * PITCH + 8 * g8) = o;
-      }
-    } else {
-      const int cl = threadIdx.x >> 1, half = threadIdx.x & 1;
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + cl * PITCH + 32 * half);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) dst[d] = lora[d];
+    for (int rr = 0; rr < 8; ++rr) {
+      float cp = const_of<DQ>(c0[rr], q8[rr], s2[rr], mean);
+      cp = (rr < nvalid) ? cp : 0.0f;
+      const f32x2_t qa = sPair[code16[rr] & 0xFFu];          // columns 4kq, 4kq+1
+      const f32x2_t qb = sPair[(code16[rr] >> 8) & 0xFFu];   // columns 4kq+2, 4kq+3
+      v[rr][0] = qa.x * cp; v[rr][1] = qa.y * cp;
+      v[rr][2] = qb.x * cp; v[rr][3] = qb.y * cp;
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q][kk], v[2 * q + 1][kk]);
+      *reinterpret_cast<u32x4_t*>(sB + (4 * kq + kk) * PITCH + 8 * g8) = o;
+    }
+  }
+  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
+    lora_fill_rows(p, jt, n0, sB, false);
   }
 };
 
 // Codebook forward: Bt[n][k] from the row's bit-planes and its 16-entry
 // mapping (staged in LDS for the workgroup's 128 rows).
+template <bool DQ>
 struct ProdFwdCodebook {
+  const uint8_t* crow;
+  int64_t blk0;
+  int nb;
   uint32_t plane[4];
-  float cst, s2;
-  u32x4_t lora[4];
+  float c0, s2;
+  uint32_t q8;
   __device__ static float* levels_lds() {
     __shared__ float sL[BN * 17];
     return sL;
@@ -247,77 +290,63 @@ struct ProdFwdCodebook {
     float* sL = levels_lds();
     for (int idx = threadIdx.x; idx < BN * 16; idx += 256) {
       const int rr = idx / 16, q = idx % 16;
-      const int64_t n = n0 + rr;
-      sL[rr * 17 + q] = (n < p.w.N) ? p.w.levels[n * 16 + q] : 0.f;
+      const int64_t n = min(n0 + rr, p.w.N - 1);
+      sL[rr * 17 + q] = p.w.levels[n * 16 + q];
     }
-  }
-  __device__ void load(const GemmParams& p, int it, int nMain, int64_t n0) {
     const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t n = n0 + row;
-    if (it < nMain) {
-      if (n < p.w.N) {
-        const int nb = min(max((int)p.w.row_bits[n], 1), 4);
-        const uint8_t* src = p.w.codes + p.w.row_offset[n] + (int64_t)it * 8 * nb + 4 * half;
+    const int64_t n = min(n0 + row, p.w.N - 1);
+    nb = min(max((int)p.w.row_bits[n], 1), 4);
+    crow = p.w.codes + p.w.row_offset[n] + 4 * half;
+    blk0 = n * (p.w.K / 64);
+  }
+  bool live;
+  __device__ void load(const GemmParams& p, int step, int nMain) {
+    live = step < nMain;
+    const int it = min(step, nMain - 1);
+    const uint8_t* src = crow + (int64_t)it * 8 * nb;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) plane[q] = (q < nb) ? *reinterpret_cast<const uint32_t*>(src + 8 * q) : 0u;
-        const int64_t blk = n * (p.w.K / 64) + it;
-        if (p.w.qc.absmax) { cst = p.w.qc.absmax[blk]; s2 = 0.f; }
-        else { cst = e4m3_decode(p.w.qc.absmax_q[blk]); s2 = p.w.qc.dq_scale[blk >> 8]; }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) plane[q] = 0u;
-        cst = 0.f; s2 = 0.f;
-      }
+    for (int q = 0; q < 4; ++q) plane[q] = *reinterpret_cast<const uint32_t*>(src + 8 * min(q, nb - 1));
+    const int64_t blk = blk0 + it;
+    if (DQ) {
+      q8 = p.w.qc.absmax_q[blk];
+      s2 = p.w.qc.dq_scale[blk >> 8];
     } else {
-      const int c0 = (it - nMain) * BK + 32 * half;
-      uint32_t h[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const int c = c0 + e;
-        h[e] = (n < p.w.N && c < 2 * p.r) ? p.lb[n * p.r + (c < p.r ? c : c - p.r)] : 0u;
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4_t v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
-        lora[d] = v;
-      }
+      c0 = p.w.qc.absmax[blk];
     }
   }
-  __device__ void store(const GemmParams& p, int it, int nMain, uint16_t* sB,
-                        const f32x2_t* /*sPair*/, float mean) {
+  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t*, float mean) {
     const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const float cp = live ? const_of<DQ>(c0, q8, s2, mean) : 0.0f;
+    const float* L = levels_lds() + row * 17;
+    uint32_t pl[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pl[q] = (q < nb) ? plane[q] : 0u;
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
-    if (it < nMain) {
-      const float cp = p.w.qc.absmax ? cst : __builtin_fmaf(cst, s2, mean);
-      const float* L = levels_lds() + row * 17;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        u32x4_t o;
+    for (int d = 0; d < 4; ++d) {
+      u32x4_t o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          float x[2];
+      for (int b = 0; b < 4; ++b) {
+        float x[2];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int e = 8 * d + 2 * b + t;
-            uint32_t code = 0;
+        for (int t = 0; t < 2; ++t) {
+          const int e = 8 * d + 2 * b + t;
+          uint32_t code = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) code |= ((plane[q] >> e) & 1u) << q;
-            x[t] = L[code] * cp;
-          }
-          o[b] = pack_bf16x2(x[0], x[1]);
+          for (int q = 0; q < 4; ++q) code |= ((pl[q] >> e) & 1u) << q;
+          x[t] = L[code] * cp;
         }
-        dst[d] = o;
+        o[b] = pack_bf16x2(x[0], x[1]);
       }
-    } else {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) dst[d] = lora[d];
+      dst[d] = o;
     }
+  }
+  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
+    lora_fill_rows(p, jt, n0, sB, true);
   }
 };
 
-template <class Prod, bool OUT_F32>
+template <class Prod, bool OUT_F32, bool TAIL>
 __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
   __shared__ f32x2_t sPair[256];
@@ -340,9 +369,11 @@ __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
   const int li = lane & 31, lh = lane >> 5;
   const int64_t mrow0 = m0 + 64 * wave;
   const float mean = p.w.qc.absmax ? 0.0f : *p.w.qc.dq_mean;
-
   const int nMain = (int)((p.Kc + BK - 1) / BK);
-  const int nIter = nMain + (2 * p.r + BK - 1) / BK;
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+    arow[rt] = p.A + min(mrow0 + 32 * rt + li, p.M - 1) * p.Kc + 32 * lh;
 
   f32x16_t acc[2][4];
 #pragma unroll
@@ -354,39 +385,42 @@ __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
 
   Prod prod;
   prod.init(p, n0);
-  u32x4_t a_cur[2][4], a_nxt[2][4];
+  u32x4_t a0[2][4], a1[2][4];
   __syncthreads();  // sPair and producer tables ready
-  prod.load(p, 0, nMain, n0);
-  load_a_frags(p, 0, nMain, mrow0, li, lh, a_cur);
-  prod.store(p, 0, nMain, sB[0], sPair, mean);
-  __syncthreads();
 
-  for (int it = 0; it < nIter; ++it) {
-    const bool has_next = it + 1 < nIter;
-    if (has_next) {
-      prod.load(p, it + 1, nMain, n0);
-      load_a_frags(p, it + 1, nMain, mrow0, li, lh, a_nxt);
-    }
-    const uint16_t* cur = sB[it & 1];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(cur + (32 * ct + li) * PITCH + 32 * lh + 8 * s);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a_cur[rt][s]), as_bf16x8(bv),
-                                                                acc[rt][ct], 0, 0, 0);
-      }
-    }
-    if (has_next) prod.store(p, it + 1, nMain, sB[(it + 1) & 1], sPair, mean);
+  // Two-stage pipeline, unrolled by two so that each A register set lives
+  // two steps: while step `it` multiplies (a0, sB[0]), the codes of it+1
+  // (already loaded) are dequantized into sB[1] and the loads of it+2 are
+  // issued. Every phase issues the same loads (tile indices are clamped and
+  // a step past the end yields a zero Bt tile), so the number of loads in
+  // flight never depends on the path and each phase is one basic block.
+  prod.load(p, 0, nMain);
+  load_a_main<TAIL>(p, 0, arow, lh, a0);
+  prod.store(p, sB[0], sPair, mean);
+  prod.load(p, 1, nMain);
+  load_a_main<TAIL>(p, min(1, nMain - 1), arow, lh, a1);
+  __syncthreads();
+  for (int it = 0; it < nMain; it += 2) {
+    mfma_step(sB[0], a0, acc, li, lh);
+    prod.store(p, sB[1], sPair, mean);
+    prod.load(p, it + 2, nMain);
+    load_a_main<TAIL>(p, min(it + 2, nMain - 1), arow, lh, a0);
     __syncthreads();
-    if (has_next) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) a_cur[rt][s] = a_nxt[rt][s];
-    }
+    mfma_step(sB[1], a1, acc, li, lh);
+    prod.store(p, sB[0], sPair, mean);
+    prod.load(p, it + 3, nMain);
+    load_a_main<TAIL>(p, min(it + 3, nMain - 1), arow, lh, a1);
+    __syncthreads();
+  }
+
+  // LoRA segment (2r columns, one or two steps)
+  const int nLora = (2 * p.r + BK - 1) / BK;
+  for (int jt = 0; jt < nLora; ++jt) {
+    prod.lora_fill(p, jt, n0, sB[0]);
+    load_a_lora(p, jt, mrow0, li, lh, a0);
+    __syncthreads();
+    mfma_step(sB[0], a0, acc, li, lh);
+    __syncthreads();
   }
 
   // epilogue: lane holds column li of each 32x32 tile, rows 8(v/4) + 4lh + v%4
@@ -771,13 +805,18 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   GemmParams p = make_params(w, X, M, w.N, w.K, t, B, r, s, H);
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
-  if (w.format == LQ_FMT_NF4) {
-    if (h_dtype == LQ_F32) hipLaunchKernelGGL((k_dq_gemm<ProdFwdNF4, true>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_dq_gemm<ProdFwdNF4, false>), grid, dim3(256), 0, st, p);
-  } else {
-    if (h_dtype == LQ_F32) hipLaunchKernelGGL((k_dq_gemm<ProdFwdCodebook, true>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_dq_gemm<ProdFwdCodebook, false>), grid, dim3(256), 0, st, p);
-  }
+  const bool dq = w.qc.absmax == nullptr;
+  const bool f32 = h_dtype == LQ_F32;
+#define LQ_LAUNCH_FWD(PROD)                                                                          \
+  do {                                                                                               \
+    if (dq && f32) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, true, false>), grid, dim3(256), 0, st, p);   \
+    else if (dq) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, false, false>), grid, dim3(256), 0, st, p);    \
+    else if (f32) hipLaunchKernelGGL((k_dq_gemm<PROD<false>, true, false>), grid, dim3(256), 0, st, p);   \
+    else hipLaunchKernelGGL((k_dq_gemm<PROD<false>, false, false>), grid, dim3(256), 0, st, p);           \
+  } while (0)
+  if (w.format == LQ_FMT_NF4) LQ_LAUNCH_FWD(ProdFwdNF4);
+  else LQ_LAUNCH_FWD(ProdFwdCodebook);
+#undef LQ_LAUNCH_FWD
   return hipGetLastError();
 }
 
@@ -786,8 +825,15 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   GemmParams p = make_params(w, G, M, w.K, w.N, u, A, r, s, gX);
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
-  if (w.format == LQ_FMT_NF4) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4, false>), grid, dim3(256), 0, st, p);
-  else return hipErrorInvalidValue;
+  if (w.format != LQ_FMT_NF4) return hipErrorInvalidValue;
+  const bool tail = w.N % BK != 0;   // contraction over N: last step partial
+  if (w.qc.absmax == nullptr) {
+    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, false>), grid, dim3(256), 0, st, p);
+  } else {
+    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, false>), grid, dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
