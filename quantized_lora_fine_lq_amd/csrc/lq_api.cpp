@@ -72,7 +72,8 @@ size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
   const size_t cands[3] = {row_skinny_ws_floats(M, w.N, r), col_skinny_ws_floats(M, w.K, r),
                            col_skinny_ws_floats(M, w.N, r)};
   for (size_t c : cands) part = c > part ? c : part;
-  return 2 * align_up((size_t)M * r * sizeof(float)) + align_up(part * sizeof(float));
+  return 2 * align_up((size_t)M * r * sizeof(float)) + align_up((size_t)w.N * r * sizeof(uint16_t)) +
+         align_up(part * sizeof(float));
 }
 
 }  // namespace
@@ -169,7 +170,7 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   float* part = cv.take<float>(row_skinny_ws_floats(M, q.K, r));
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
-  hipError_t e = launch_row_skinny(X, M, q.K, A, false, r, t, part, s);
+  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, part, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (use_gemv(q, M)) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
   else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
@@ -187,7 +188,7 @@ int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int
   if (M <= 0 || K <= 0 || K % 8 != 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
   const size_t need = lq_lora_down_workspace(M, K, r);
   if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
-  return launch_status(launch_row_skinny(X, M, K, A, false, r, t, (float*)workspace, (hipStream_t)stream));
+  return launch_status(launch_row_skinny(X, M, K, A, r, t, (float*)workspace, (hipStream_t)stream));
 }
 
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
@@ -239,16 +240,19 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   Carver cv(workspace);
   float* u = cv.take<float>((size_t)M * r);
   float* t_ws = cv.take<float>((size_t)M * r);
+  uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
   float* part = reinterpret_cast<float*>(cv.base + cv.used);
   const float scale = alpha / (float)r;
   hipError_t e = hipSuccess;
   const float* t = t_saved;
   if (!t) {
-    e = launch_row_skinny(X, M, q.K, A, false, r, t_ws, part, s);
+    e = launch_row_skinny(X, M, q.K, A, r, t_ws, part, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
     t = t_ws;
   }
-  e = launch_row_skinny(G, M, q.N, B, true, r, u, part, s);
+  e = launch_transpose_u16(B, q.N, r, Bt, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  e = launch_row_skinny(G, M, q.N, Bt, r, u, part, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (dB) {
     e = launch_col_skinny(t, G, M, q.N, r, scale, dB, true, part, s);

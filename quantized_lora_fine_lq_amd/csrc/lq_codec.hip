@@ -169,31 +169,49 @@ __global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, 
 }
 
 // ---------------------------------------------------------------------------
-// Dequant to bfloat16. One thread turns 32 codes (16 bytes) into 32 bf16.
-// NF4: a 256-entry table in LDS maps a code byte to its two float32 levels.
+// Dequant to bfloat16. A wave covers 2048 consecutive elements in 4 passes;
+// in pass d lane l handles elements 512d + 8l .. +7 (one dword of codes), so
+// each code load reads 256 contiguous bytes and each 16-byte store instruction
+// writes 1 KB contiguous. NF4: a 256-entry table in LDS maps a code byte to
+// its two float32 levels.
 // ---------------------------------------------------------------------------
+template <bool DQ>
 __global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__ codes, QConst qc,
-                                                     int64_t n_groups, uint16_t* __restrict__ out,
+                                                     int64_t n, uint16_t* __restrict__ out,
                                                      Nf4Levels lv) {
   __shared__ f32x2_t pair[256];
   pair[threadIdx.x] = f32x2_t{lv.q[threadIdx.x >> 4], lv.q[threadIdx.x & 15]};
   __syncthreads();
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= n_groups) return;
-  const u32x4_t cw = *reinterpret_cast<const u32x4_t*>(codes + g * 16);
-  const float cp = block_const(qc, g >> 1);
-  u32x4_t o[4];
+  const int lane = threadIdx.x & 63;
+  const int64_t e_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2048 + 8 * lane;
+  const float mean = DQ ? *qc.dq_mean : 0.0f;
+  uint32_t w[4];
+  float c0[4], s2[4];
+  uint32_t q8[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f32x2_t q = pair[(cw[d] >> (8 * b)) & 0xFFu];
-      o[d][b] = pack_bf16x2(q.x * cp, q.y * cp);
+    const int64_t e = min(e_base + 512 * d, n - 8);   // n % 64 == 0; clamped lanes do not store
+    w[d] = *reinterpret_cast<const uint32_t*>(codes + e / 2);
+    const int64_t blk = e >> 6;
+    if (DQ) {
+      q8[d] = qc.absmax_q[blk];
+      s2[d] = qc.dq_scale[blk >> 8];
+    } else {
+      c0[d] = qc.absmax[blk];
     }
   }
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + g * 32);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) dst[d] = o[d];
+  for (int d = 0; d < 4; ++d) {
+    const int64_t e = e_base + 512 * d;
+    const float cp = DQ ? __builtin_fmaf(e4m3_decode(q8[d]), s2[d], mean) : c0[d];
+    u32x4_t o;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const f32x2_t q = pair[(w[d] >> (8 * b)) & 0xFFu];
+      o[b] = pack_bf16x2(q.x * cp, q.y * cp);
+    }
+    if (e < n) *reinterpret_cast<u32x4_t*>(out + e) = o;
+  }
 }
 
 // Codebook dequant: one thread per 8 elements of a 64-block (one byte of
@@ -322,9 +340,10 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
 
 hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
   if (w.format == LQ_FMT_NF4) {
-    const int64_t n_groups = w.N * w.K / 32;
-    hipLaunchKernelGGL(k_dequant_nf4, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0, s,
-                       w.codes, w.qc, n_groups, out, tables().lv);
+    const int64_t n = w.N * w.K;
+    const dim3 grid((unsigned)((n + 8191) / 8192));
+    if (w.qc.absmax) hipLaunchKernelGGL(k_dequant_nf4<false>, grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+    else hipLaunchKernelGGL(k_dequant_nf4<true>, grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
   } else {
     const int64_t n_groups = w.N * w.K / 8;
     hipLaunchKernelGGL(k_dequant_codebook, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0,

@@ -60,10 +60,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---- OCP E4M3 (bias 7, max 448, subnormal step 2^-9) ------------------------
+// Placing the 7 magnitude bits at float32 bit 20 gives 2^(e-127) (1 + m/8)
+// for e > 0 and the float32 denormal m 2^-129 for e = 0; scaling by 2^120 is
+// exact and yields 2^(e-7) (1 + m/8) and m 2^-9 respectively.
 __device__ __forceinline__ float e4m3_decode(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (code & 0x80u) ? -mag : mag;
+  return __uint_as_float(((code & 0x7Fu) << 20) | ((code & 0x80u) << 24)) * 0x1p120f;
 }
 
 // v must be finite and within [-448, 448]. Round to nearest, ties to even.

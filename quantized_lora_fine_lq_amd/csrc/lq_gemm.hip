@@ -443,14 +443,20 @@ __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
 
 // ===========================================================================
 // Decode GEMV (M <= 16), NF4. MFMA 16x16x32 with tokens as the 16 A-rows
-// (rows >= M are zero) and 16 weight rows per tile. Each workgroup owns 64
-// weight rows; its 4 waves split K in 128-wide chunks; each lane streams 16
-// bytes of codes per 16-row group per chunk and dequantizes straight into
-// MFMA B-registers. Partial sums meet in LDS; the LoRA term s t B^T is added
-// in float32 before the single rounding of H.
+// (rows >= M repeat row M-1; their outputs are not stored) and 16 weight rows
+// per MFMA tile. A workgroup owns RG tiles (16*RG weight rows); its 8 waves
+// take 256-wide K chunks in turn. In a chunk, lane (li, lg) covers
+// k = 256c + 64lg + [0, 64): one whole 64-block per weight row, so one block
+// constant per 32 bytes of codes. Two register sets keep the next chunk's
+// codes and X in flight while the current one is dequantized straight into
+// MFMA B registers.
+//
+// Level lookup without LDS: every lane holds q[lane % 16]; ds_bpermute takes
+// the source lane from address bits [7:2], so shifting the code word until the
+// wanted nibble sits at bits [5:2] is the whole address computation (the
+// bits above select one of the four identical 16-lane copies). No bank
+// conflicts, one VALU op per element for the address.
 // ===========================================================================
-constexpr int GV_RG = 4;
-
 struct GemvParams {
   const uint16_t* X;   // [M, K]
   int64_t M;
@@ -463,73 +469,131 @@ struct GemvParams {
   Nf4Levels lv;
 };
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) void k_gemv_nf4(GemvParams p) {
-  __shared__ f32x2_t sPair[256];
-  __shared__ f32x4_t sRed[4][GV_RG][64];
-  sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
-  __syncthreads();
+// X slice [16 tokens][1024 k] in LDS, row pitch 1032 bf16 (2064 bytes: the
+// 16-byte fragment reads of 8 consecutive rows fall in distinct banks).
+constexpr int GV_XS = 1024 + 8;
+
+// 8 codes of one code word -> 8 bf16 (4 dwords). Element e sits at bit
+// 8*(e/2) + 4*(1 - e%2) of the word (high nibble first).
+__device__ __forceinline__ u32x4_t dequant8_bperm(uint32_t w, int qv, float cp) {
+  const int a[8] = {(int)(w >> 2),  (int)(w << 2),  (int)(w >> 10), (int)(w >> 6),
+                    (int)(w >> 18), (int)(w >> 14), (int)(w >> 26), (int)(w >> 22)};
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(a[e], qv)) * cp;
+  return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+}
+
+// Decode GEMV. A workgroup owns 16*WV weight rows (one 16-row group per wave)
+// and walks K in 1024-column iterations. Per iteration the code tile
+// [16*WV rows x 512 bytes] and the X slice [16 x 1024] are loaded with
+// contiguous 512-byte (codes) and 2 KB (X) runs per row into LDS -- reading
+// only 128 bytes per row per visit leaves HBM pages mostly unused -- and the
+// next iteration's tile is prefetched into registers meanwhile. Each wave
+// then takes its MFMA fragments from LDS: lane (li, lg) dequantizes block
+// 4s + lg of row li in step s. Iteration order is rotated by workgroup.
+constexpr int GV_CP = 512 + 16;          // code tile row pitch (bytes)
+
+template <int WV, bool DQ, bool OUT_F32>
+__global__ __launch_bounds__(64 * WV) void k_gemv_nf4(GemvParams p) {
+  constexpr int NT = 64 * WV;            // threads
+  constexpr int RW = 16 * WV;            // weight rows per workgroup
+  constexpr int CQ = RW * 32 / NT;       // 16-byte code loads per thread (= 8)
+  constexpr int XQ = 16 * 128 / NT;      // 16-byte X loads per thread
+  __shared__ __attribute__((aligned(16))) uint8_t sC[RW * GV_CP];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[16 * GV_XS];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t N = p.w.N, K = p.w.K;
-  const int64_t n0 = (int64_t)blockIdx.x * (16 * GV_RG);
-  const float mean = p.w.qc.absmax ? 0.0f : *p.w.qc.dq_mean;
-  f32x4_t acc[GV_RG];
-#pragma unroll
-  for (int g = 0; g < GV_RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t n0 = (int64_t)blockIdx.x * RW;
+  const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
+  const int qv = __float_as_int(p.lv.q[li]);
+  const int64_t nrow = min(n0 + 16 * wave + li, N - 1);   // rows past N: outputs not stored
+  const int64_t Kb = K / 2;                               // code bytes per row
 
-  const int64_t nChunks = (K + 127) / 128;
-  for (int64_t ch = wave; ch < nChunks; ch += 4) {
-    const int64_t kb = ch * 128 + 32 * lg;
-    const bool k_ok = kb < K;   // K % 64 == 0: then kb + 32 <= K
-    u32x4_t xa[4];
-    if (k_ok && li < p.M) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.X + li * K + kb);
+  // code tile loads: load q of thread t -> tile row t/32 + (NT/32) q, bytes 16 (t%32)
+  const int crr = threadIdx.x >> 5, cby = 16 * (threadIdx.x & 31);
+  // X slice loads: load q -> token t/128 + (NT/128) q, columns 8 (t%128)
+  const int xrr = threadIdx.x >> 7, xcol = 8 * (threadIdx.x & 127);
+
+  const int64_t nit = (K + 1023) / 1024;
+  const int64_t rot = blockIdx.x % nit;
+  auto col_of = [&](int64_t i) -> int64_t {
+    int64_t ii = min(i, nit - 1) + rot;
+    ii = ii >= nit ? ii - nit : ii;
+    return ii * 1024;
+  };
+
+  u32x4_t cr[CQ], xr[XQ];
+  float c0v[4], s2v[4];
+  uint32_t q8v[4];
+  bool livev[4];
+  auto issue = [&](int64_t i) {
+    const int64_t c0 = col_of(i);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xa[s] = src[s];
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) zero(xa[s]);
+    for (int q = 0; q < CQ; ++q) {
+      const int64_t row = min(n0 + crr + (NT / 32) * q, N - 1);
+      const int64_t byte = c0 / 2 + cby;
+      cr[q] = ld16(p.w.codes + row * Kb + (byte + 16 <= Kb ? byte : 0));
     }
-    u32x4_t cw[GV_RG];
-    float cp[GV_RG];
 #pragma unroll
-    for (int g = 0; g < GV_RG; ++g) {
-      const int64_t n = n0 + 16 * g + li;
-      if (k_ok && n < N) {
-        const int64_t e0 = n * K + kb;
-        cw[g] = *reinterpret_cast<const u32x4_t*>(p.w.codes + e0 / 2);
-        const int64_t blk = e0 >> 6;
-        cp[g] = p.w.qc.absmax ? p.w.qc.absmax[blk]
-                              : __builtin_fmaf(e4m3_decode(p.w.qc.absmax_q[blk]), p.w.qc.dq_scale[blk >> 8], mean);
+    for (int q = 0; q < XQ; ++q) {   // token rows >= M only feed outputs that are not stored
+      const int64_t m = xrr + (NT / 128) * q;
+      const int64_t col = c0 + xcol;
+      if (m < p.M) xr[q] = ld16(p.X + m * K + (col + 8 <= K ? col : 0));
+    }
+    // block constants of the lane's four blocks (steps s = 0..3)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int64_t kb = c0 + 256 * st + 64 * lg;
+      livev[st] = i < nit && kb < K;
+      const int64_t blk = (nrow * K + (livev[st] ? kb : 0)) >> 6;
+      if (DQ) {
+        q8v[st] = p.w.qc.absmax_q[blk];
+        s2v[st] = p.w.qc.dq_scale[blk >> 8];
       } else {
-        zero(cw[g]);
-        cp[g] = 0.f;
+        c0v[st] = p.w.qc.absmax[blk];
       }
     }
+  };
+
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  for (int64_t i = 0; i < nit; ++i) {
+    __syncthreads();                     // previous tile fully read
 #pragma unroll
-    for (int g = 0; g < GV_RG; ++g) {
+    for (int q = 0; q < CQ; ++q)
+      *reinterpret_cast<u32x4_t*>(sC + (crr + (NT / 32) * q) * GV_CP + cby) = cr[q];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4_t bv;
+    for (int q = 0; q < XQ; ++q)
+      if (xrr + (NT / 128) * q < p.M)
+        *reinterpret_cast<u32x4_t*>(sX + (xrr + (NT / 128) * q) * GV_XS + xcol) = xr[q];
+    float cp[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x2_t q = sPair[(cw[g][s] >> (8 * b)) & 0xFFu];
-          bv[b] = pack_bf16x2(q.x * cp[g], q.y * cp[g]);
-        }
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[s]), as_bf16x8(bv), acc[g], 0, 0, 0);
+    for (int st = 0; st < 4; ++st) {
+      const float c = DQ ? __builtin_fmaf(e4m3_decode(q8v[st]), s2v[st], mean) : c0v[st];
+      cp[st] = livev[st] ? c : 0.0f;
+    }
+    issue(i + 1);
+    __syncthreads();                     // tile i staged
+    const uint8_t* crow = sC + (16 * wave + li) * GV_CP;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4_t w0 = ld16(crow + 128 * st + 32 * lg);
+      const u32x4_t w1 = ld16(crow + 128 * st + 32 * lg + 16);
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const uint32_t w = s8 < 4 ? w0[s8] : w1[s8 - 4];
+        const u32x4_t bv = dequant8_bperm(w, qv, cp[st]);
+        const u32x4_t xa = ld16(sX + li * GV_XS + 256 * st + 64 * lg + 8 * s8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(bv), acc, 0, 0, 0);
       }
     }
   }
-#pragma unroll
-  for (int g = 0; g < GV_RG; ++g) sRed[wave][g][lane] = acc[g];
-  __syncthreads();
-  // thread -> (g = tid/64, lane): tokens 4*(lane/16) + v, weight row n0 + 16g + lane%16
-  const int g = threadIdx.x >> 6;
-  f32x4_t sum = sRed[0][g][lane];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) sum += sRed[w][g][lane];
-  const int64_t n = n0 + 16 * g + li;
+
+  // lane holds tokens 4*lg + v of weight row n0 + 16*wave + li
+  const int64_t n = n0 + 16 * wave + li;
   if (n >= N) return;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -537,7 +601,7 @@ __global__ __launch_bounds__(256) void k_gemv_nf4(GemvParams p) {
     if (m >= p.M) continue;
     float lora = 0.0f;
     for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(p.t[m * p.r + j], bf16_to_f32(p.B[n * p.r + j]), lora);
-    const float h = sum[v] + p.s * lora;
+    const float h = acc[v] + p.s * lora;
     if (OUT_F32) reinterpret_cast<float*>(p.out)[m * N + n] = h;
     else reinterpret_cast<uint16_t*>(p.out)[m * N + n] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
   }
@@ -546,65 +610,49 @@ __global__ __launch_bounds__(256) void k_gemv_nf4(GemvParams p) {
 // ===========================================================================
 // Skinny products (HBM-bound: they stream X or G once).
 // ===========================================================================
-// Row form: part[split][m][j] = sum_{c in split} Q[m][c] R(j, c), MFMA
-// 16x16x32 with 16 rows of Q per wave, R staged in LDS as [j][64 c].
+// Row form: part[split][m][j] = sum_{c in split} Q[m][c] R[j][c] with R
+// [r, C] row-major. MFMA 16x16x32: a wave owns 16 rows of Q, lane (li, lg)
+// reads 8 consecutive columns of Q row li and of R row 16jt + li straight
+// into MFMA registers (R is small and stays in cache); no LDS, no barriers.
 constexpr int RS_ROWS = 64;
+template <int JT>
 __global__ __launch_bounds__(256) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M,
-                                                    int64_t C, const uint16_t* __restrict__ Rm,
-                                                    int r_transposed, int r, int64_t c_per_split,
-                                                    float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint16_t sR[128 * PITCH];
+                                                    int64_t C, const uint16_t* __restrict__ R, int r,
+                                                    int64_t c_per_split, float* __restrict__ out) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t m = (int64_t)blockIdx.x * RS_ROWS + 16 * wave + li;
+  const int64_t m = min((int64_t)blockIdx.x * RS_ROWS + 16 * wave + li, M - 1);
+  const uint16_t* qrow = Q + m * C + 8 * lg;
+  const uint16_t* rrow[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C + 8 * lg;
   const int64_t c_begin = (int64_t)blockIdx.y * c_per_split;
   const int64_t c_end = min(C, c_begin + c_per_split);
-  const int jtiles = (r + 15) / 16;
-  f32x4_t acc[8];
+  f32x4_t acc[JT];
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
-    // stage R(j, c0 .. c0+63) for j < 16*jtiles (zero outside)
-    for (int idx = threadIdx.x; idx < 16 * jtiles * 64; idx += 256) {
-      const int j = idx / 64, cc = idx % 64;
-      const int64_t c = c0 + cc;
-      uint16_t v = 0;
-      if (j < r && c < c_end) v = r_transposed ? Rm[c * r + j] : Rm[(int64_t)j * C + c];
-      sR[j * PITCH + cc] = v;
-    }
-    __syncthreads();
-    u32x4_t a[2];
+  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c = c_begin; c < c_end; c += 128) {
+    u32x4_t a[4], b[4][JT];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int64_t c = c0 + 16 * lg + 8 * s;
-      if (m < M && c + 8 <= c_end) a[s] = *reinterpret_cast<const u32x4_t*>(Q + m * C + c);
-      else {
-        zero(a[s]);
-        if (m < M)
-          for (int e = 0; e < 8; e += 2) {
-            const uint32_t lo = (c + e < c_end) ? Q[m * C + c + e] : 0u;
-            const uint32_t hi = (c + e + 1 < c_end) ? Q[m * C + c + e + 1] : 0u;
-            a[s][e / 2] = lo | (hi << 16);
-          }
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int64_t cc = c + 32 * u;
+      const bool ok = cc + 8 * lg + 8 <= c_end;
+      const int64_t off = ok ? cc : c_begin;
+      a[u] = ld16(qrow + off);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) b[u][jt] = ld16(rrow[jt] + off);
+      if (!ok) zero(a[u]);
     }
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      if (jt < jtiles) {
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(sR + (16 * jt + li) * PITCH + 16 * lg + 8 * s);
-          acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[s]), as_bf16x8(bv), acc[jt], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
+      for (int jt = 0; jt < JT; ++jt)
+        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b[u][jt]), acc[jt], 0, 0, 0);
   }
   // D: lane holds column j = 16jt + li, rows 4lg + v
   float* dst = out + (int64_t)blockIdx.y * M * r;
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
-    if (jt >= jtiles) continue;
+  for (int jt = 0; jt < JT; ++jt) {
     const int j = 16 * jt + li;
     if (j >= r) continue;
 #pragma unroll
@@ -613,6 +661,15 @@ __global__ __launch_bounds__(256) void k_row_skinny(const uint16_t* __restrict__
       if (row < M) dst[row * r + j] = acc[jt][v];
     }
   }
+}
+
+// out[j][n] = in[n][j] for a small [N, r] bf16 matrix.
+__global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restrict__ in, int64_t N, int r,
+                                                       uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= N * r) return;
+  const int64_t n = i / r, j = i % r;
+  out[j * N + n] = in[i];
 }
 
 // Column form: part[split][j][c] = sum_{m in split} P[m][j] Q[m][c], MFMA
@@ -749,21 +806,31 @@ size_t row_skinny_ws_floats(int64_t M, int64_t C, int r) {
   return splits > 1 ? (size_t)splits * M * r : 0;
 }
 
-hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rm,
-                             bool r_transposed, int r, float* out, float* ws, hipStream_t s) {
+hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
+                             float* out, float* ws, hipStream_t s) {
   const int splits = row_skinny_splits(M, C);
   const int64_t chunks = (C + 63) / 64;
   const int64_t c_per_split = ((chunks + splits - 1) / splits) * 64;
   const int real_splits = (int)((C + c_per_split - 1) / c_per_split);
   float* dst = real_splits > 1 ? ws : out;
   const dim3 grid((unsigned)((M + RS_ROWS - 1) / RS_ROWS), (unsigned)real_splits);
-  hipLaunchKernelGGL(k_row_skinny, grid, dim3(256), 0, s, Q, M, C, Rm, r_transposed ? 1 : 0, r,
-                     c_per_split, dst);
+  switch ((r + 15) / 16) {
+#define LQ_RS(JT) case JT: hipLaunchKernelGGL(k_row_skinny<JT>, grid, dim3(256), 0, s, Q, M, C, R, r, c_per_split, dst); break;
+    LQ_RS(1) LQ_RS(2) LQ_RS(3) LQ_RS(4) LQ_RS(5) LQ_RS(6) LQ_RS(7) LQ_RS(8)
+#undef LQ_RS
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || real_splits == 1) return e;
   const int64_t n = M * r;
   hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws,
                      real_splits, M, (int64_t)r, 1.0f, out, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* out, hipStream_t s) {
+  const int64_t n = N * r;
+  hipLaunchKernelGGL(k_transpose_u16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, N, r, out);
   return hipGetLastError();
 }
 
@@ -837,14 +904,24 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   return hipGetLastError();
 }
 
+template <int WV>
+static void launch_gemv_wv(const GemvParams& p, bool dq, bool f32, hipStream_t st) {
+  const dim3 grid((unsigned)((p.w.N + 16 * WV - 1) / (16 * WV))), block(64 * WV);
+  if (dq && f32) hipLaunchKernelGGL((k_gemv_nf4<WV, true, true>), grid, block, 0, st, p);
+  else if (dq) hipLaunchKernelGGL((k_gemv_nf4<WV, true, false>), grid, block, 0, st, p);
+  else if (f32) hipLaunchKernelGGL((k_gemv_nf4<WV, false, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((k_gemv_nf4<WV, false, false>), grid, block, 0, st, p);
+}
+
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
                            hipStream_t st) {
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
-  const dim3 grid((unsigned)((w.N + 16 * GV_RG - 1) / (16 * GV_RG)));
-  if (h_dtype == LQ_F32) hipLaunchKernelGGL(k_gemv_nf4<true>, grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL(k_gemv_nf4<false>, grid, dim3(256), 0, st, p);
+  const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
+  // 8 waves (128 rows) when X is large enough for its re-reads to matter
+  if (M > 4) launch_gemv_wv<8>(p, dq, f32, st);
+  else launch_gemv_wv<4>(p, dq, f32, st);
   return hipGetLastError();
 }
 

@@ -63,11 +63,12 @@ hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t
                                     const float* thresholds, uint8_t* codes, float* absmax,
                                     hipStream_t s);
 
-// Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R(j, c) with
-// R(j, c) = Rm[j*C + c] (r_transposed = false) or Rm[c*r + j] (true).
+// Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R[j][c] with R
+// [r, C] row-major (C % 8 == 0).
 size_t row_skinny_ws_floats(int64_t M, int64_t C, int r);
-hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rm,
-                             bool r_transposed, int r, float* out, float* ws, hipStream_t s);
+hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
+                             float* out, float* ws, hipStream_t s);
+hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* out, hipStream_t s);
 // Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c]; written as
 // out[j*C + c] (out_transposed = false, [r, C]) or out[c*r + j] ([C, r]).
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r);
