@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the steps")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
 
 
@@ -138,12 +140,18 @@ class Calls:
     def grad_x(self):
         self.chk(self.lib.lq_dequant_gemm_t(*self.args_gx), "dequant_gemm_t")
 
-    def step(self):
+    def step(self, ev=None):
+        """One pass of the path; `ev` = (start, end) events put around the
+        forward dequant-GEMM launch on the same stream."""
         self.quantize()
         self.double_quant()
         self.dequant()
         self.lora_down()
+        if ev is not None:
+            ev[0].record()
         self.fwd_gemm()
+        if ev is not None:
+            ev[1].record()
         self.backward()
 
 
@@ -200,6 +208,38 @@ def codec_bytes(L, M=0):
     }
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dq_gemm_fwd_q_proj_traffic.md")
+TRAFFIC_SOURCES = ("quantized_lora_fine_lq_amd/csrc/lq_gemm.hip", "quantized_lora_fine_lq_amd/csrc/lq_device.h")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward dequant-GEMM, from the committed
+    FETCH_SIZE / WRITE_SIZE counter runs (calibrated on a plain copy), or
+    None if the kernel sources changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    vals = {}
+    for ln in lines:
+        if ln.startswith("traffic_bytes_per_launch:") or ln.startswith("source_digest:"):
+            k, v = ln.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("source_digest") != kernel_source_digest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(syn):
     """The oracle (numpy / float64 BLAS) on one full q_proj step."""
     import numpy as np
@@ -248,15 +288,28 @@ def main():
     fl = layer_flops(L, L.M)
     step_flops = fl["fwd"] + fl["bwd"]
 
+    if args.copy_probe:
+        # plain copy of known size: 512 MiB read + 512 MiB written per launch
+        src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- the timed step -------------------------------------------------
+    # The forward dequant-GEMM (the dominant kernel) is bracketed by its own
+    # events inside every timed step, on the stream the library launches on.
     for i in range(args.warmup):
         calls[i % len(calls)].step()
     torch.cuda.synchronize()
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        calls[i % len(calls)].step()
+        calls[i % len(calls)].step(kev[i])
     e1.record()
     e1.synchronize()
     wall = time.perf_counter() - w0
@@ -265,14 +318,13 @@ def main():
     log(f"step: {ms_step:.4f} ms  ({value:.1f} TFLOP/s), wall {wall:.3f} s")
 
     # ---- dominant kernel: forward dequant-GEMM on q_proj -------------------
-    for c in calls:
-        c.lora_down()
-    fwd_ms = time_ms(torch, [c.fwd_gemm for c in calls], 50)
+    fwd_ms = sum(a.elapsed_time(b) for a, b in kev) / len(kev)
     fwd_tflops = fl["fwd_gemm"] / (fwd_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_dq_gemm<ProdFwdNF4> (q_proj, M=2048)",
+    roofline = {"bound": "mfma", "kernel": "k_dq_gemm<ProdFwdNF4<true>> (q_proj, M=2048)",
                 "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_us": round(fwd_ms * 1e3, 2),
+                "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(),
+                "avg_us": round(fwd_ms * 1e3, 2), "launches_timed": len(kev),
                 "algorithmic_flop_per_launch": fl["fwd_gemm"]}
 
     kernels = {}
@@ -293,7 +345,9 @@ def main():
         rec("q_proj.double_quant", time_ms(torch, [c.double_quant for c in calls], 40), cb["double_quant"], "GB/s")
         rec("q_proj.dequant", time_ms(torch, [c.dequant for c in calls], 40), cb["dequant"], "GB/s")
         rec("q_proj.lora_down", time_ms(torch, [c.lora_down for c in calls], 40), fl["lora_down"], "TFLOP/s")
-        rec("q_proj.dequant_gemm_fwd", fwd_ms, fl["fwd_gemm"], "TFLOP/s")
+        for c in calls:
+            c.lora_down()
+        rec("q_proj.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in calls], 50), fl["fwd_gemm"], "TFLOP/s")
         rec("q_proj.backward", time_ms(torch, [c.backward for c in calls], 30), fl["bwd"], "TFLOP/s")
         del calls, devs
         torch.cuda.empty_cache()
