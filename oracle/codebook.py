@@ -9,7 +9,7 @@ LowRA page:
     figure 3); inside a channel, groups of 64 elements are scaled by their
     absmax, following QLoRA.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * code = number of the row's thresholds strictly below x = w / c (a value on
     a threshold goes to the lower bin), x computed as in NF4;
   * packing: each 64-block of a row with b bits is stored as b bit-planes of

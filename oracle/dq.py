@@ -8,7 +8,7 @@ QLoRA page, section "贡献二：Double Quantization":
     added back at dequantization;
   * constant overhead: 8/64 + 32/(64*256) = 0.127 bit per parameter.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * one mean per tensor -- the 0.127 closed form has exactly one 32-bit term
     per 256 constants, so there is no per-block mean;
   * the mean is the float64 sum of the constants taken as a fixed binary

@@ -12,7 +12,7 @@ LowRA page, section 5 (mapping and threshold learner):
     levels; it stops at the iteration limit or when the MSE stops decreasing,
     and outputs the last computed mapping and thresholds.
 
-Readings (listed in DESIGN.md):
+Readings where the pages are silent:
   * data = the block-normalised values x = w / c (float32), weight = c;
   * 3 bits (not on the page) start from NF3, built like NF4 with 4 + 5 - 1
     levels; NF2 uses 2 + 3 - 1; the truncation probability of NF_b is

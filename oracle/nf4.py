@@ -11,7 +11,7 @@ QLoRA page, section "贡献一：4-bit NormalFloat（NF4）":
     the positive half and dropping the duplicated 0: 8 + 9 - 1 = 16.
 Section "贡献二：Double Quantization": one FP32 constant per 64 weights.
 
-Readings where the page is silent (listed in the design doc):
+Readings where the page is silent:
   * truncation probability delta = 1 - (1/32 + 1/30)/2 (not on the page);
   * quantiles equally spaced in probability on each half;
   * ties at a midpoint go to the lower index: thresholds are the float32
