@@ -19,16 +19,19 @@ namespace {
 // Lb = B (forward) or A^T (backward). hi + lo carries L to about 2^-17, so
 // the LoRA term is computed at float32-like accuracy on the bf16 MFMA.
 //
-// Tile 256 x 128 x 64 per 256-thread workgroup; wave w owns rows
-// [64w, 64w + 64) and all 128 columns (2 x 4 MFMA 32x32x16 tiles).
-// The A operand goes straight from global memory into MFMA registers; the
-// Bt tile is dequantized cooperatively (each weight once per workgroup)
-// into a double-buffered LDS tile. Inside a 64-wide k-step, lane (i, h) of a
-// 32x32x16 MFMA takes k = 32h + 8s + e for step s -- a permutation of k that
-// both operands share, so each lane reads 64 contiguous bytes of A.
+// Tile 256 x 128 x 64 per 512-thread workgroup (8 waves, two per SIMD, so
+// one wave's MFMAs overlap the other's loads, dequantization and LDS
+// traffic). Wave w owns rows [64 (w % 4), +64) and columns [64 (w / 4), +64)
+// of the tile: 2 x 2 MFMA 32x32x16 tiles. Per 64-wide k-step the A tile
+// (rows of X or G) is staged in LDS with coalesced 16-byte loads, and the Bt
+// tile is dequantized cooperatively -- each weight once per workgroup --
+// into LDS. Both are double buffered; the global loads of step j are issued
+// two steps ahead. Inside a k-step, lane (i, h) of a 32x32x16 MFMA takes
+// k = 32h + 8s + e in sub-step s, a permutation of k that both operands share.
 // ===========================================================================
 constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int PITCH = BK + 8;  // bf16 per LDS row: 144 bytes, conflict-free b128 access
+constexpr int GEMM_THREADS = 512;
 
 struct GemmParams {
   const uint16_t* A;   // [M, Kc] bf16, row stride Kc
@@ -52,88 +55,91 @@ __device__ __forceinline__ void split_bf16(float v, float& hi, float& lo) {
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
-// A fragments of one 64-wide step of the main segment for one wave
-// ([2 row tiles][4 sub-steps]). arow[rt] points at the lane's row (rows past
-// M were clamped to row M-1: their outputs are never stored) plus its 32h
-// column offset. An 8-column group past the end of the contraction reads
-// column 0 instead -- the Bt tile is zero there, so it adds nothing.
+// ---- A tile (rows of X or G) through LDS ------------------------------------
+// Thread t stages 16-byte chunk c = t % 8 of tile rows t/8 + 64q (q = 0..3):
+// each global load instruction of a wave reads 8 whole 128-byte row segments.
+// Rows past M repeat row M-1 (their outputs are never stored); a chunk past
+// the end of the contraction reads column 0 instead (the Bt tile is zero
+// there, so it adds nothing).
 template <bool TAIL>
-__device__ __forceinline__ void load_a_main(const GemmParams& p, int it, const uint16_t* const (&arow)[2],
-                                            int lh, u32x4_t (&a)[2][4]) {
-  const int64_t col0 = (int64_t)it * BK;
+__device__ __forceinline__ void load_a_tile(const GemmParams& p, int it, const uint16_t* const (&ar)[4],
+                                            u32x4_t (&r)[4]) {
+  const int64_t col = (int64_t)it * BK + 8 * (threadIdx.x & 7);
+  const int64_t off = (TAIL && col + 8 > p.Kc) ? 0 : col;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int q = 0; q < 4; ++q) r[q] = ld16(ar[q] + off);
+}
+__device__ __forceinline__ void store_a_tile(uint16_t* sA, const u32x4_t (&r)[4]) {
+  uint16_t* dst = sA + (threadIdx.x >> 3) * PITCH + 8 * (threadIdx.x & 7);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      int64_t off = col0 + 8 * s;
-      if (TAIL) off = (col0 + 32 * lh + 8 * s + 8 <= p.Kc) ? off : -32 * lh;
-      a[rt][s] = ld16(arow[rt] + off);
-    }
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(dst + 64 * q * PITCH) = r[q];
 }
 
-// A fragments of the LoRA segment: columns [0, r) carry hi(s*L), [r, 2r)
-// carry lo(s*L), the rest 0 (L = t forward, u backward).
-__device__ void load_a_lora(const GemmParams& p, int jt, int64_t mrow0, int li, int lh,
-                            u32x4_t (&a)[2][4]) {
+// 16 MFMAs of one 64-wide step, both operands from LDS: wave tile 64 x 64 =
+// [2 row tiles] x [2 col tiles]; fragments of sub-step s+1 are read while
+// sub-step s multiplies.
+__device__ __forceinline__ void mfma_step(const uint16_t* sAt, const uint16_t* sBt, f32x16_t (&acc)[2][2],
+                                          int wr, int wc, int li, int lh) {
+  const uint16_t* abase = sAt + (64 * wr + li) * PITCH + 32 * lh;
+  const uint16_t* bbase = sBt + (64 * wc + li) * PITCH + 32 * lh;
+  u32x4_t a[2][2], b[2][2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int64_t row = min(mrow0 + 32 * rt + li, p.M - 1);
-    const float* src = p.la + row * p.r;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c0 = jt * BK + 32 * lh + 8 * s;
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        float x = 0.0f;
-        if (c < 2 * p.r) {
-          float hi, lo;
-          split_bf16(p.s * src[c < p.r ? c : c - p.r], hi, lo);
-          x = (c < p.r) ? hi : lo;
-        }
-        v[e] = x;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[rt][s][e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-    }
+  for (int t = 0; t < 2; ++t) {
+    a[0][t] = ld16(abase + 32 * t * PITCH);
+    b[0][t] = ld16(bbase + 32 * t * PITCH);
   }
-}
-
-// 32 MFMAs of one 64-wide step: wave tile 64 x 128 = [2 row tiles] x [4 col
-// tiles]. B fragments of sub-step s+1 are read from LDS while sub-step s
-// multiplies.
-__device__ __forceinline__ void mfma_step(const uint16_t* sBt, const u32x4_t (&a)[2][4],
-                                          f32x16_t (&acc)[2][4], int li, int lh) {
-  const uint16_t* base = sBt + li * PITCH + 32 * lh;
-  u32x4_t b[2][4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) b[0][ct] = ld16(base + 32 * ct * PITCH);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (s < 3) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) b[(s + 1) & 1][ct] = ld16(base + 32 * ct * PITCH + 8 * (s + 1));
+      for (int t = 0; t < 2; ++t) {
+        a[(s + 1) & 1][t] = ld16(abase + 32 * t * PITCH + 8 * (s + 1));
+        b[(s + 1) & 1][t] = ld16(bbase + 32 * t * PITCH + 8 * (s + 1));
+      }
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[rt][s]), as_bf16x8(b[s & 1][ct]),
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[s & 1][rt]), as_bf16x8(b[s & 1][ct]),
                                                               acc[rt][ct], 0, 0, 0);
   }
 }
 
-// 32 bf16 -> LDS: thread (row tid/2, half) fills Bt[row][32 half .. +32).
-__device__ __forceinline__ void lora_fill_rows(const GemmParams& p, int jt, int64_t n0,
-                                               uint16_t* sB, bool fwd) {
+// ---- LoRA segment tiles -------------------------------------------------------
+// A-side: thread (row t/2, half) fills 32 columns of [hi(s*L) | lo(s*L) | 0].
+__device__ void lora_fill_a(const GemmParams& p, int jt, int64_t m0, uint16_t* sA) {
   const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int64_t n = n0 + row;
-  const int64_t ncols = fwd ? p.w.N : p.w.K;
+  const float* src = p.la + min(m0 + row, p.M - 1) * p.r;
   const int c0 = jt * BK + 32 * half;
-  uint32_t h[32];
+  float v[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
+    const int c = c0 + e;
+    float x = 0.0f;
+    if (c < 2 * p.r) {
+      float hi, lo;
+      split_bf16(p.s * src[c < p.r ? c : c - p.r], hi, lo);
+      x = (c < p.r) ? hi : lo;
+    }
+    v[e] = x;
+  }
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sA + row * PITCH + 32 * half);
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    dst[d] = u32x4_t{pack_bf16x2(v[8 * d], v[8 * d + 1]), pack_bf16x2(v[8 * d + 2], v[8 * d + 3]),
+                     pack_bf16x2(v[8 * d + 4], v[8 * d + 5]), pack_bf16x2(v[8 * d + 6], v[8 * d + 7])};
+}
+// Bt-side: thread (row t/4, quarter) fills 16 columns of [Lb | Lb | 0] for
+// output column n0 + row (B[n][j] forward, A[j][n] backward).
+__device__ void lora_fill_b(const GemmParams& p, int jt, int64_t n0, uint16_t* sB, bool fwd) {
+  const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
+  const int64_t n = n0 + row;
+  const int64_t ncols = fwd ? p.w.N : p.w.K;
+  const int c0 = jt * BK + 16 * qq;
+  uint32_t h[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
     const int c = c0 + e;
     uint32_t v = 0;
     if (n < ncols && c < 2 * p.r) {
@@ -142,9 +148,9 @@ __device__ __forceinline__ void lora_fill_rows(const GemmParams& p, int jt, int6
     }
     h[e] = v;
   }
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < 2; ++d) {
     u32x4_t v;
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
@@ -155,7 +161,7 @@ __device__ __forceinline__ void lora_fill_rows(const GemmParams& p, int jt, int6
 // ---- Bt producers -----------------------------------------------------------
 // load() only issues global loads into members; store() decodes and writes
 // the dequantized bf16 tile to LDS. Keeping arithmetic out of load() lets
-// the loads stay in flight across a whole MFMA step.
+// the loads stay in flight for a whole step.
 
 // Block constant from the loaded parts: float32 (DQ = false) or
 // fma(E4M3(q8), s2, mean) (DQ = true).
@@ -164,26 +170,30 @@ __device__ __forceinline__ float const_of(float c0, uint32_t q8, float s2, float
   return DQ ? __builtin_fmaf(e4m3_decode(q8), s2, mean) : c0;
 }
 
-// Forward NF4: Bt[n][k] = W'[n0 + n][64 it + k]; thread -> (row tid/2, 32 codes).
+// Forward NF4: Bt[n][k] = W'[n0 + n][64 it + k]; thread -> row t/4,
+// columns 16 (t % 4) .. +16 (8 code bytes, one block constant).
 template <bool DQ>
 struct ProdFwdNF4 {
-  const uint8_t* crow;   // codes of the thread's row at its 32-column half
+  static constexpr bool kFwd = true;
+  const uint8_t* crow;   // codes of the thread's row at its 16 columns
   int64_t blk0;          // block index of step 0
-  u32x4_t codes;
+  uint32_t code[2];
   float c0, s2;
   uint32_t q8;
-  bool live;             // false for a padding step past the end: tile of zeros
+  float livef;           // 0 for a padding step past the end: tile of zeros
   __device__ void init(const GemmParams& p, int64_t n0) {
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
     const int64_t n = min(n0 + row, p.w.N - 1);   // rows past N: outputs never stored
-    const int64_t e0 = n * p.w.K + 32 * half;
+    const int64_t e0 = n * p.w.K + 16 * qq;
     crow = p.w.codes + e0 / 2;
     blk0 = e0 >> 6;
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
-    live = step < nMain;
+    livef = step < nMain ? 1.0f : 0.0f;
     const int it = min(step, nMain - 1);
-    codes = ld16(crow + (int64_t)it * (BK / 2));
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(crow + (int64_t)it * (BK / 2));
+    code[0] = src[0];
+    code[1] = src[1];
     const int64_t blk = blk0 + it;
     if (DQ) {
       q8 = p.w.qc.absmax_q[blk];
@@ -193,51 +203,48 @@ struct ProdFwdNF4 {
     }
   }
   __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t* sPair, float mean) {
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const float cp = live ? const_of<DQ>(c0, q8, s2, mean) : 0.0f;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
+    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
+    const float cp = const_of<DQ>(c0, q8, s2, mean) * livef;   // c * 0 = 0 (c is finite)
+    f32x2_t q[8];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int b = 0; b < 8; ++b) q[b] = sPair[(code[b >> 2] >> (8 * (b & 3))) & 0xFFu];
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
       u32x4_t o;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x2_t q = sPair[(codes[d] >> (8 * b)) & 0xFFu];
-        o[b] = pack_bf16x2(q.x * cp, q.y * cp);
-      }
+      for (int b = 0; b < 4; ++b) o[b] = pack_bf16x2(q[4 * d + b].x * cp, q[4 * d + b].y * cp);
       dst[d] = o;
     }
-  }
-  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
-    lora_fill_rows(p, jt, n0, sB, true);
   }
 };
 
 // Backward NF4: Bt[c][n] = W'[64 it + n][n0 + c] (the contraction runs over
-// W's rows). Thread -> 8 rows x 4 columns: g8 = tid % 8 picks rows
-// 8*g8 .. 8*g8+7 of the step, kq = tid / 8 picks columns 4kq .. 4kq+3.
-// Rows past N must contribute zero: their constant is forced to 0.
+// W's rows). Thread -> rows 2 (t % 32) + {0, 1} of the step and columns
+// 8 (t / 32) .. +8 (4 code bytes per row, one block constant per row).
+// Rows past N contribute zero: their constant is forced to 0.
 template <bool DQ>
 struct ProdBwdNF4 {
-  int64_t e00;           // flat element of (row 8*g8, column k) at step 0
-  uint32_t code16[8];
-  float c0[8], s2[8];
-  uint32_t q8[8];
-  int nvalid;            // rows of this step below N (0..8)
+  static constexpr bool kFwd = false;
+  int64_t kcol;          // first of the thread's 8 columns
+  uint32_t code[2];
+  float c0[2], s2[2];
+  uint32_t q8[2];
+  float livef[2];
   __device__ void init(const GemmParams& p, int64_t n0) {
-    const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
-    const int64_t k = min(n0 + 4 * kq, p.w.K - 4);   // columns past K: outputs never stored
-    e00 = (int64_t)(8 * g8) * p.w.K + k;
+    const int kq = threadIdx.x >> 5;
+    kcol = min(n0 + 8 * kq, p.w.K - 8);   // columns past K: outputs never stored
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
-    const int g8 = threadIdx.x & 7;
+    const int g = threadIdx.x & 31;
     const int it = min(step, nMain - 1);
-    const int64_t nfirst = (int64_t)it * BK + 8 * g8;
-    nvalid = step < nMain ? (int)min((int64_t)8, max((int64_t)0, p.w.N - nfirst)) : 0;
-    const int64_t estep = e00 + (int64_t)it * BK * p.w.K;
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      const int64_t e0 = estep + (int64_t)(rr < nvalid ? rr : 0) * p.w.K;
-      code16[rr] = *reinterpret_cast<const uint16_t*>(p.w.codes + e0 / 2);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t nrow = (int64_t)it * BK + 2 * g + rr;
+      const bool ok = step < nMain && nrow < p.w.N;
+      livef[rr] = ok ? 1.0f : 0.0f;
+      const int64_t e0 = min(nrow, p.w.N - 1) * p.w.K + kcol;   // a valid row either way
+      code[rr] = *reinterpret_cast<const uint32_t*>(p.w.codes + e0 / 2);
       const int64_t blk = e0 >> 6;
       if (DQ) {
         q8[rr] = p.w.qc.absmax_q[blk];
@@ -248,64 +255,60 @@ struct ProdBwdNF4 {
     }
   }
   __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t* sPair, float mean) {
-    const int g8 = threadIdx.x & 7, kq = threadIdx.x >> 3;
-    float v[8][4];
+    const int g = threadIdx.x & 31, kq = threadIdx.x >> 5;
+    float v[2][8];
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-      float cp = const_of<DQ>(c0[rr], q8[rr], s2[rr], mean);
-      cp = (rr < nvalid) ? cp : 0.0f;
-      const f32x2_t qa = sPair[code16[rr] & 0xFFu];          // columns 4kq, 4kq+1
-      const f32x2_t qb = sPair[(code16[rr] >> 8) & 0xFFu];   // columns 4kq+2, 4kq+3
-      v[rr][0] = qa.x * cp; v[rr][1] = qa.y * cp;
-      v[rr][2] = qb.x * cp; v[rr][3] = qb.y * cp;
+    for (int rr = 0; rr < 2; ++rr) {
+      const float cp = const_of<DQ>(c0[rr], q8[rr], s2[rr], mean) * livef[rr];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x2_t q = sPair[(code[rr] >> (8 * b)) & 0xFFu];   // columns 8kq + 2b, +1
+        v[rr][2 * b] = q.x * cp;
+        v[rr][2 * b + 1] = q.y * cp;
+      }
     }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(sB + (8 * kq) * PITCH + 2 * g);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4_t o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q][kk], v[2 * q + 1][kk]);
-      *reinterpret_cast<u32x4_t*>(sB + (4 * kq + kk) * PITCH + 8 * g8) = o;
-    }
-  }
-  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
-    lora_fill_rows(p, jt, n0, sB, false);
+    for (int cc = 0; cc < 8; ++cc) dst[cc * (PITCH / 2)] = pack_bf16x2(v[0][cc], v[1][cc]);
   }
 };
 
 // Codebook forward: Bt[n][k] from the row's bit-planes and its 16-entry
-// mapping (staged in LDS for the workgroup's 128 rows).
+// mapping (staged in LDS for the workgroup's 128 rows). Thread -> row t/4,
+// columns 16 (t % 4) .. +16 (two bytes of each bit-plane).
 template <bool DQ>
 struct ProdFwdCodebook {
+  static constexpr bool kFwd = true;
   const uint8_t* crow;
   int64_t blk0;
   int nb;
   uint32_t plane[4];
   float c0, s2;
   uint32_t q8;
+  float livef;
   __device__ static float* levels_lds() {
     __shared__ float sL[BN * 17];
     return sL;
   }
   __device__ void init(const GemmParams& p, int64_t n0) {
     float* sL = levels_lds();
-    for (int idx = threadIdx.x; idx < BN * 16; idx += 256) {
+    for (int idx = threadIdx.x; idx < BN * 16; idx += GEMM_THREADS) {
       const int rr = idx / 16, q = idx % 16;
       const int64_t n = min(n0 + rr, p.w.N - 1);
       sL[rr * 17 + q] = p.w.levels[n * 16 + q];
     }
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
     const int64_t n = min(n0 + row, p.w.N - 1);
     nb = min(max((int)p.w.row_bits[n], 1), 4);
-    crow = p.w.codes + p.w.row_offset[n] + 4 * half;
+    crow = p.w.codes + p.w.row_offset[n] + 2 * qq;
     blk0 = n * (p.w.K / 64);
   }
-  bool live;
   __device__ void load(const GemmParams& p, int step, int nMain) {
-    live = step < nMain;
+    livef = step < nMain ? 1.0f : 0.0f;
     const int it = min(step, nMain - 1);
     const uint8_t* src = crow + (int64_t)it * 8 * nb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) plane[q] = *reinterpret_cast<const uint32_t*>(src + 8 * min(q, nb - 1));
+    for (int q = 0; q < 4; ++q) plane[q] = *reinterpret_cast<const uint16_t*>(src + 8 * min(q, nb - 1));
     const int64_t blk = blk0 + it;
     if (DQ) {
       q8 = p.w.qc.absmax_q[blk];
@@ -315,15 +318,15 @@ struct ProdFwdCodebook {
     }
   }
   __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t*, float mean) {
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const float cp = live ? const_of<DQ>(c0, q8, s2, mean) : 0.0f;
+    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
+    const float cp = const_of<DQ>(c0, q8, s2, mean) * livef;
     const float* L = levels_lds() + row * 17;
     uint32_t pl[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pl[q] = (q < nb) ? plane[q] : 0u;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 32 * half);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < 2; ++d) {
       u32x4_t o;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -341,16 +344,14 @@ struct ProdFwdCodebook {
       dst[d] = o;
     }
   }
-  __device__ void lora_fill(const GemmParams& p, int jt, int64_t n0, uint16_t* sB) {
-    lora_fill_rows(p, jt, n0, sB, true);
-  }
 };
 
 template <class Prod, bool OUT_F32, bool TAIL>
-__global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
+__global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
   __shared__ f32x2_t sPair[256];
-  sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
+  if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
 
   // XCD-aware tile order: the 8 XCDs take workgroups round robin, so give
   // each XCD a contiguous range of tiles, M-tiles fastest (they share the
@@ -366,60 +367,63 @@ __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wr = wave & 3, wc = wave >> 2;
   const int li = lane & 31, lh = lane >> 5;
-  const int64_t mrow0 = m0 + 64 * wave;
   const float mean = p.w.qc.absmax ? 0.0f : *p.w.qc.dq_mean;
   const int nMain = (int)((p.Kc + BK - 1) / BK);
-  const uint16_t* arow[2];
+  const uint16_t* ar[4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    arow[rt] = p.A + min(mrow0 + 32 * rt + li, p.M - 1) * p.Kc + 32 * lh;
+  for (int q = 0; q < 4; ++q)
+    ar[q] = p.A + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.Kc;
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[2][2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
-  Prod prod;
-  prod.init(p, n0);
-  u32x4_t a0[2][4], a1[2][4];
+  // Two register sets (producer state + A chunks) alternate: the data of
+  // step j is loaded during step j-2, written to LDS buffer j%2 at the end of
+  // step j-1, and multiplied in step j. One barrier per step. Every step
+  // issues the same loads (indices are clamped; a step past the end yields a
+  // zero Bt tile), so each step is one basic block.
+  Prod pa, pb;
+  pa.init(p, n0);
+  pb.init(p, n0);
+  u32x4_t ra[4], rb[4];
   __syncthreads();  // sPair and producer tables ready
 
-  // Two-stage pipeline, unrolled by two so that each A register set lives
-  // two steps: while step `it` multiplies (a0, sB[0]), the codes of it+1
-  // (already loaded) are dequantized into sB[1] and the loads of it+2 are
-  // issued. Every phase issues the same loads (tile indices are clamped and
-  // a step past the end yields a zero Bt tile), so the number of loads in
-  // flight never depends on the path and each phase is one basic block.
-  prod.load(p, 0, nMain);
-  load_a_main<TAIL>(p, 0, arow, lh, a0);
-  prod.store(p, sB[0], sPair, mean);
-  prod.load(p, 1, nMain);
-  load_a_main<TAIL>(p, min(1, nMain - 1), arow, lh, a1);
+  pa.load(p, 0, nMain);
+  load_a_tile<TAIL>(p, 0, ar, ra);
+  pb.load(p, 1, nMain);
+  load_a_tile<TAIL>(p, min(1, nMain - 1), ar, rb);
+  pa.store(p, sB[0], sPair, mean);
+  store_a_tile(sA[0], ra);
   __syncthreads();
   for (int it = 0; it < nMain; it += 2) {
-    mfma_step(sB[0], a0, acc, li, lh);
-    prod.store(p, sB[1], sPair, mean);
-    prod.load(p, it + 2, nMain);
-    load_a_main<TAIL>(p, min(it + 2, nMain - 1), arow, lh, a0);
+    pa.load(p, it + 2, nMain);
+    load_a_tile<TAIL>(p, min(it + 2, nMain - 1), ar, ra);
+    mfma_step(sA[0], sB[0], acc, wr, wc, li, lh);
+    pb.store(p, sB[1], sPair, mean);
+    store_a_tile(sA[1], rb);
     __syncthreads();
-    mfma_step(sB[1], a1, acc, li, lh);
-    prod.store(p, sB[0], sPair, mean);
-    prod.load(p, it + 3, nMain);
-    load_a_main<TAIL>(p, min(it + 3, nMain - 1), arow, lh, a1);
+    pb.load(p, it + 3, nMain);
+    load_a_tile<TAIL>(p, min(it + 3, nMain - 1), ar, rb);
+    mfma_step(sA[1], sB[1], acc, wr, wc, li, lh);
+    pa.store(p, sB[0], sPair, mean);
+    store_a_tile(sA[0], ra);
     __syncthreads();
   }
 
-  // LoRA segment (2r columns, one or two steps)
+  // LoRA segment (2r columns, one or two steps) through the same LDS tiles
   const int nLora = (2 * p.r + BK - 1) / BK;
   for (int jt = 0; jt < nLora; ++jt) {
-    prod.lora_fill(p, jt, n0, sB[0]);
-    load_a_lora(p, jt, mrow0, li, lh, a0);
+    lora_fill_a(p, jt, m0, sA[0]);
+    lora_fill_b(p, jt, n0, sB[0], Prod::kFwd);
     __syncthreads();
-    mfma_step(sB[0], a0, acc, li, lh);
+    mfma_step(sA[0], sB[0], acc, wr, wc, li, lh);
     __syncthreads();
   }
 
@@ -427,12 +431,12 @@ __global__ __launch_bounds__(256) void k_dq_gemm(GemmParams p) {
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int64_t col = n0 + 32 * ct + li;
+    for (int ct = 0; ct < 2; ++ct) {
+      const int64_t col = n0 + 64 * wc + 32 * ct + li;
       if (col >= p.Ncols) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = mrow0 + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3);
+        const int64_t row = m0 + 64 * wr + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (row < p.M) {
           if (OUT_F32) reinterpret_cast<float*>(p.out)[row * p.Ncols + col] = acc[rt][ct][v];
           else reinterpret_cast<uint16_t*>(p.out)[row * p.Ncols + col] = (uint16_t)(pack_bf16x2(acc[rt][ct][v], 0.f) & 0xFFFFu);
@@ -876,10 +880,10 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   const bool f32 = h_dtype == LQ_F32;
 #define LQ_LAUNCH_FWD(PROD)                                                                          \
   do {                                                                                               \
-    if (dq && f32) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, true, false>), grid, dim3(256), 0, st, p);   \
-    else if (dq) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, false, false>), grid, dim3(256), 0, st, p);    \
-    else if (f32) hipLaunchKernelGGL((k_dq_gemm<PROD<false>, true, false>), grid, dim3(256), 0, st, p);   \
-    else hipLaunchKernelGGL((k_dq_gemm<PROD<false>, false, false>), grid, dim3(256), 0, st, p);           \
+    if (dq && f32) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, true, false>), grid, dim3(GEMM_THREADS), 0, st, p);   \
+    else if (dq) hipLaunchKernelGGL((k_dq_gemm<PROD<true>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);    \
+    else if (f32) hipLaunchKernelGGL((k_dq_gemm<PROD<false>, true, false>), grid, dim3(GEMM_THREADS), 0, st, p);   \
+    else hipLaunchKernelGGL((k_dq_gemm<PROD<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);           \
   } while (0)
   if (w.format == LQ_FMT_NF4) LQ_LAUNCH_FWD(ProdFwdNF4);
   else LQ_LAUNCH_FWD(ProdFwdCodebook);
@@ -895,11 +899,11 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   if (w.format != LQ_FMT_NF4) return hipErrorInvalidValue;
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
   if (w.qc.absmax == nullptr) {
-    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, true>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, false>), grid, dim3(256), 0, st, p);
+    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
   } else {
-    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, true>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, false>), grid, dim3(256), 0, st, p);
+    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
   }
   return hipGetLastError();
 }
