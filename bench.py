@@ -84,6 +84,8 @@ class Dev:
         self.H = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         self.ld_ws_bytes = lq.lib.lq_lora_down_workspace(M, K, r)
         self.ld_ws = torch.empty(max(self.ld_ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.fw_ws_bytes = lq.lib.lq_dequant_gemm_workspace(self.qw.ref(), M, r)
+        self.fw_ws = torch.empty(max(self.fw_ws_bytes, 1), dtype=torch.uint8, device=dev)
         if G is not None:
             self.gX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
             self.dA = torch.empty(r, K, dtype=torch.float32, device=dev)
@@ -91,6 +93,8 @@ class Dev:
             self.u = torch.empty(M, r, dtype=torch.float32, device=dev)
             self.bw_ws_bytes = lq.lib.lq_backward_workspace(self.qw.ref(), M, r)
             self.bw_ws = torch.empty(self.bw_ws_bytes, dtype=torch.uint8, device=dev)
+            self.gx_ws_bytes = lq.lib.lq_dequant_gemm_t_workspace(self.qw.ref(), M, r)
+            self.gx_ws = torch.empty(max(self.gx_ws_bytes, 1), dtype=torch.uint8, device=dev)
 
 
 class Calls:
@@ -109,11 +113,13 @@ class Calls:
                         d.dq_ws_bytes, self.stream)
         self.args_deq = (d.qw.ref(), P(d.Wd), self.stream)
         self.args_ld = (P(d.X), d.M, L.K, P(d.A), d.r, P(d.t), P(d.ld_ws), d.ld_ws_bytes, self.stream)
-        self.args_fwd = (d.qw.ref(), P(d.X), d.M, P(d.t), P(d.B), d.r, self.alpha, P(d.H), 1, self.stream)
+        self.args_fwd = (d.qw.ref(), P(d.X), d.M, P(d.t), P(d.B), d.r, self.alpha, P(d.H), 1,
+                         P(d.fw_ws), d.fw_ws_bytes, self.stream)
         if d.G is not None:
             self.args_bwd = (d.qw.ref(), P(d.X), P(d.G), d.M, P(d.A), P(d.B), d.r, self.alpha, P(d.t),
                              P(d.gX), P(d.dA), P(d.dB), P(d.bw_ws), d.bw_ws_bytes, self.stream)
-            self.args_gx = (d.qw.ref(), P(d.G), d.M, P(d.u), P(d.A), d.r, self.alpha, P(d.gX), self.stream)
+            self.args_gx = (d.qw.ref(), P(d.G), d.M, P(d.u), P(d.A), d.r, self.alpha, P(d.gX),
+                            P(d.gx_ws), d.gx_ws_bytes, self.stream)
 
     def chk(self, st, name):
         if st != 0:

@@ -214,25 +214,37 @@ size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r);
 int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
                  void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for lq_dequant_gemm with M tokens and rank r: the bf16
+ * LoRA-segment operands of the MFMA path, (M + N) * 64 * ceil(2r / 64) * 2
+ * bytes, or 0 when the GEMV path is taken (M <= 16, NF4). */
+size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
+
 /*
  * Second stage of the forward ([QLoRA] introduction): given t = X A^T,
  * H = X W'^T + (alpha / r) t B^T with W' dequantized inside the kernel (the
- * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM). Needs no workspace.
- * Arguments as lq_qlora_forward; t [M, r] float32 is read.
+ * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM). Arguments as
+ * lq_qlora_forward; t [M, r] float32 is read. The workspace (caller-owned,
+ * lq_dequant_gemm_workspace bytes) receives the LoRA operands of the MFMA
+ * path; it may be NULL when the GEMV path is taken (M <= 16, NF4).
  */
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
                     const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
-                    void* stream);
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for lq_dequant_gemm_t ((M + K) * 64 * ceil(2r / 64) * 2). */
+size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
  * The transposed dequant-GEMM of the backward ([QLoRA] introduction: the
  * gradient flows through the frozen 4-bit base): given u = G B,
  * grad_X = G W' + (alpha / r) u A, bfloat16 output.
  *   G [M, N] bf16, u [M, r] float32, A [r, K] bf16, grad_X [M, K] bf16.
- * NF4 weights only (LQ_ERR_UNSUPPORTED otherwise); N % 8 == 0 (LQ_ERR_SHAPE).
+ * NF4 weights only (LQ_ERR_UNSUPPORTED otherwise); N % 8 == 0 (LQ_ERR_SHAPE);
+ * workspace of lq_dequant_gemm_t_workspace bytes (LQ_ERR_WORKSPACE).
  */
 int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
-                      const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X, void* stream);
+                      const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X,
+                      void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for lq_qlora_backward with M tokens and rank r. */
 size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);

@@ -68,8 +68,12 @@ SIGNATURES = {
                                             c_vp, c_vp, c_vp]),
     "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
-    "lq_dequant_gemm": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_i32, c_vp]),
-    "lq_dequant_gemm_t": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_vp]),
+    "lq_dequant_gemm_workspace": (c_sz, [QW_P, c_i64, c_i32]),
+    "lq_dequant_gemm": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_i32,
+                                       c_vp, c_sz, c_vp]),
+    "lq_dequant_gemm_t_workspace": (c_sz, [QW_P, c_i64, c_i32]),
+    "lq_dequant_gemm_t": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp,
+                                         c_vp, c_sz, c_vp]),
 }
 
 
@@ -274,8 +278,10 @@ def dequant_gemm(qw: QWeight, X, t, B, alpha: float, out=None, out_dtype=None):
     M, r = X.shape[0], t.shape[1]
     H = torch.empty(M, qw.N, dtype=out_dtype, device=X.device) if out is None else out
     h_code = LQ_F32 if H.dtype == torch.float32 else LQ_BF16
+    ws_bytes = lib.lq_dequant_gemm_workspace(qw.ref(), M, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=X.device)
     _check(lib.lq_dequant_gemm(qw.ref(), _ptr(X), M, _ptr(t), _ptr(B), r, float(alpha), _ptr(H), h_code,
-                               _stream(X.device)), "lq_dequant_gemm")
+                               _ptr(ws), ws_bytes, _stream(X.device)), "lq_dequant_gemm")
     return H
 
 
@@ -284,8 +290,10 @@ def dequant_gemm_t(qw: QWeight, G, u, A, alpha: float, out=None):
     torch = _torch()
     M, r = G.shape[0], u.shape[1]
     gx = torch.empty(M, qw.K, dtype=torch.bfloat16, device=G.device) if out is None else out
+    ws_bytes = lib.lq_dequant_gemm_t_workspace(qw.ref(), M, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=G.device)
     _check(lib.lq_dequant_gemm_t(qw.ref(), _ptr(G), M, _ptr(u), _ptr(A), r, float(alpha), _ptr(gx),
-                                 _stream(G.device)), "lq_dequant_gemm_t")
+                                 _ptr(ws), ws_bytes, _stream(G.device)), "lq_dequant_gemm_t")
     return gx
 
 

@@ -4,6 +4,8 @@
 //
 // QLoRA (Heng's Blog), introduction: h = dequant(W0_NF4) x + (alpha/r) B A x,
 // W0 dequantized to BFloat16 when used; the optimizer updates only A and B.
+#include <algorithm>
+
 #include "lq_device.h"
 
 namespace lq {
@@ -36,10 +38,9 @@ constexpr int GEMM_THREADS = 512;
 struct GemmParams {
   const uint16_t* A;   // [M, Kc] bf16, row stride Kc
   int64_t M, Ncols, Kc;
-  const float* la;     // [M, r] float32 (t or u)
-  const uint16_t* lb;  // forward: B [N, r]; backward: A [r, K]
-  int r;
-  float s;
+  const uint16_t* t2;  // LoRA segment, A-side [M, R2] bf16: [hi(s L) | lo(s L) | 0]
+  const uint16_t* lb2; // LoRA segment, Bt-side [Ncols, R2] bf16: [Lb | Lb | 0]
+  int R2;              // 64 * ceil(2r / 64)
   void* out;           // [M, Ncols]
   QWeight w;
   Nf4Levels lv;
@@ -107,54 +108,67 @@ __device__ __forceinline__ void mfma_step(const uint16_t* sAt, const uint16_t* s
 }
 
 // ---- LoRA segment tiles -------------------------------------------------------
-// A-side: thread (row t/2, half) fills 32 columns of [hi(s*L) | lo(s*L) | 0].
-__device__ void lora_fill_a(const GemmParams& p, int jt, int64_t m0, uint16_t* sA) {
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const float* src = p.la + min(m0 + row, p.M - 1) * p.r;
-  const int c0 = jt * BK + 32 * half;
-  float v[32];
+// Step jt of the LoRA segment: the A-side tile from t2 (same thread mapping
+// and row clamping as the main A tiles) and the Bt-side tile from lb2
+// (thread -> row t/4, columns 16 (t % 4) .. +16).
+__device__ __forceinline__ void lora_tiles(const GemmParams& p, int jt, int64_t m0, int64_t n0,
+                                           uint16_t* sA, uint16_t* sB) {
+  u32x4_t ra[4];
+  const uint16_t* abase = p.t2 + (int64_t)jt * BK + 8 * (threadIdx.x & 7);
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const int c = c0 + e;
-    float x = 0.0f;
-    if (c < 2 * p.r) {
-      float hi, lo;
-      split_bf16(p.s * src[c < p.r ? c : c - p.r], hi, lo);
-      x = (c < p.r) ? hi : lo;
-    }
-    v[e] = x;
-  }
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sA + row * PITCH + 32 * half);
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    dst[d] = u32x4_t{pack_bf16x2(v[8 * d], v[8 * d + 1]), pack_bf16x2(v[8 * d + 2], v[8 * d + 3]),
-                     pack_bf16x2(v[8 * d + 4], v[8 * d + 5]), pack_bf16x2(v[8 * d + 6], v[8 * d + 7])};
-}
-// Bt-side: thread (row t/4, quarter) fills 16 columns of [Lb | Lb | 0] for
-// output column n0 + row (B[n][j] forward, A[j][n] backward).
-__device__ void lora_fill_b(const GemmParams& p, int jt, int64_t n0, uint16_t* sB, bool fwd) {
+  for (int q = 0; q < 4; ++q) ra[q] = ld16(abase + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.R2);
   const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
-  const int64_t n = n0 + row;
-  const int64_t ncols = fwd ? p.w.N : p.w.K;
-  const int c0 = jt * BK + 16 * qq;
-  uint32_t h[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int c = c0 + e;
-    uint32_t v = 0;
-    if (n < ncols && c < 2 * p.r) {
-      const int j = c < p.r ? c : c - p.r;
-      v = fwd ? p.lb[n * p.r + j] : p.lb[(int64_t)j * p.w.K + n];
-    }
-    h[e] = v;
-  }
+  const uint16_t* bsrc = p.lb2 + min(n0 + row, p.Ncols - 1) * p.R2 + (int64_t)jt * BK + 16 * qq;
+  const u32x4_t b0 = ld16(bsrc), b1 = ld16(bsrc + 8);
+  store_a_tile(sA, ra);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
+  dst[0] = b0;
+  dst[1] = b1;
+}
+
+// LoRA segment operands, one 16-byte chunk per thread and grid-stride step:
+// rows [0, M) of the A-side t2 from L (t or u), then rows [0, Ncols) of the
+// Bt-side lb2 from Lb (B[n][j] forward, A[j][n] backward).
+__global__ __launch_bounds__(256) void k_lora_operands(const float* L, int64_t M, const uint16_t* lb,
+                                                       int64_t Ncols, int64_t K, int r, int R2, float s,
+                                                       int fwd, uint16_t* t2, uint16_t* lb2) {
+  const int64_t per_row = R2 / 8;
+  const int64_t total = (M + Ncols) * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / per_row;
+    const int c0 = (int)(i % per_row) * 8;
+    float v[8];
+    uint32_t h[8];
+    if (row < M) {
+      const float* src = L + row * r;
 #pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    u32x4_t v;
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        float x = 0.0f;
+        if (c < 2 * r) {
+          float hi, lo;
+          split_bf16(s * src[c < r ? c : c - r], hi, lo);
+          x = (c < r) ? hi : lo;
+        }
+        v[e] = x;
+      }
+      *reinterpret_cast<u32x4_t*>(t2 + row * R2 + c0) =
+          u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+      const int64_t n = row - M;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = h[8 * d + 2 * q] | (h[8 * d + 2 * q + 1] << 16);
-    dst[d] = v;
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        uint32_t x = 0;
+        if (c < 2 * r) {
+          const int j = c < r ? c : c - r;
+          x = fwd ? lb[n * r + j] : lb[(int64_t)j * K + n];
+        }
+        h[e] = x;
+      }
+      *reinterpret_cast<u32x4_t*>(lb2 + n * R2 + c0) =
+          u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    }
   }
 }
 
@@ -174,7 +188,6 @@ __device__ __forceinline__ float const_of(float c0, uint32_t q8, float s2, float
 // columns 16 (t % 4) .. +16 (8 code bytes, one block constant).
 template <bool DQ>
 struct ProdFwdNF4 {
-  static constexpr bool kFwd = true;
   const uint8_t* crow;   // codes of the thread's row at its 16 columns
   int64_t blk0;          // block index of step 0
   uint32_t code[2];
@@ -225,7 +238,6 @@ struct ProdFwdNF4 {
 // Rows past N contribute zero: their constant is forced to 0.
 template <bool DQ>
 struct ProdBwdNF4 {
-  static constexpr bool kFwd = false;
   int64_t kcol;          // first of the thread's 8 columns
   uint32_t code[2];
   float c0[2], s2[2];
@@ -278,7 +290,6 @@ struct ProdBwdNF4 {
 // columns 16 (t % 4) .. +16 (two bytes of each bit-plane).
 template <bool DQ>
 struct ProdFwdCodebook {
-  static constexpr bool kFwd = true;
   const uint8_t* crow;
   int64_t blk0;
   int nb;
@@ -417,11 +428,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
     __syncthreads();
   }
 
-  // LoRA segment (2r columns, one or two steps) through the same LDS tiles
-  const int nLora = (2 * p.r + BK - 1) / BK;
+  // LoRA segment (R2 = 64 ceil(2r / 64) columns) through the same LDS tiles
+  const int nLora = p.R2 / BK;
   for (int jt = 0; jt < nLora; ++jt) {
-    lora_fill_a(p, jt, m0, sA[0]);
-    lora_fill_b(p, jt, n0, sB[0], Prod::kFwd);
+    lora_tiles(p, jt, m0, n0, sA[0], sB[0]);
     __syncthreads();
     mfma_step(sA[0], sB[0], acc, wr, wc, li, lh);
     __syncthreads();
@@ -859,21 +869,43 @@ hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64
   return hipGetLastError();
 }
 
-static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, int64_t Ncols,
-                              int64_t Kc, const float* la, const uint16_t* lb, int r, float s,
+int lora_seg_cols(int r) { return BK * ((2 * r + BK - 1) / BK); }
+
+size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r) {
+  return (size_t)(M + Ncols) * lora_seg_cols(r) * sizeof(uint16_t);
+}
+
+// Writes the LoRA operands into ws (t2 first, then lb2) and fills p.
+static hipError_t prepare_lora(GemmParams& p, const float* L, const uint16_t* lb, int r, float s, bool fwd,
+                               uint16_t* ws, hipStream_t st) {
+  p.R2 = lora_seg_cols(r);
+  uint16_t* t2 = ws;
+  uint16_t* lb2 = ws + p.M * p.R2;
+  p.t2 = t2;
+  p.lb2 = lb2;
+  const int64_t chunks = (p.M + p.Ncols) * (p.R2 / 8);
+  const unsigned blocks = (unsigned)std::min<int64_t>((chunks + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_lora_operands, dim3(blocks), dim3(256), 0, st, L, p.M, lb, p.Ncols, p.w.K, r, p.R2, s,
+                     fwd ? 1 : 0, t2, lb2);
+  return hipGetLastError();
+}
+
+static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, int64_t Ncols, int64_t Kc,
                               void* out) {
   GemmParams p;
-  p.A = A; p.M = M; p.Ncols = Ncols; p.Kc = Kc;
-  p.la = la; p.lb = lb; p.r = r; p.s = s; p.out = out;
+  p.A = A; p.M = M; p.Ncols = Ncols; p.Kc = Kc; p.out = out;
+  p.t2 = nullptr; p.lb2 = nullptr; p.R2 = 0;
   p.w = w;
   p.lv = tables().lv;
   return p;
 }
 
 hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
-                           const uint16_t* B, int r, float s, void* H, int h_dtype,
+                           const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,
                            hipStream_t st) {
-  GemmParams p = make_params(w, X, M, w.N, w.K, t, B, r, s, H);
+  GemmParams p = make_params(w, X, M, w.N, w.K, H);
+  hipError_t e = prepare_lora(p, t, B, r, s, true, ws, st);
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool dq = w.qc.absmax == nullptr;
@@ -892,11 +924,13 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
 }
 
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
-                           const uint16_t* A, int r, float s, uint16_t* gX, hipStream_t st) {
-  GemmParams p = make_params(w, G, M, w.K, w.N, u, A, r, s, gX);
+                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st) {
+  if (w.format != LQ_FMT_NF4) return hipErrorInvalidValue;
+  GemmParams p = make_params(w, G, M, w.K, w.N, gX);
+  hipError_t e = prepare_lora(p, u, A, r, s, false, ws, st);
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
-  if (w.format != LQ_FMT_NF4) return hipErrorInvalidValue;
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
   if (w.qc.absmax == nullptr) {
     if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);

@@ -79,11 +79,15 @@ hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64
 // Dequant-GEMM with the LoRA segment.
 //  forward : out[m][n] = sum_k X[m][k] W'[n][k] + s * sum_j t[m][j] B[n][j]
 //  backward: out[m][k] = sum_n G[m][n] W'[n][k] + s * sum_j u[m][j] A[j][k]
+// ws receives the bf16 LoRA segment operands: lora_operands_ws_bytes(M,
+// output columns, r) bytes (output columns = N forward, K backward).
+int lora_seg_cols(int r);
+size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r);
 hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
-                           const uint16_t* B, int r, float s, void* H, int h_dtype,
+                           const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,
                            hipStream_t st);
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
-                           const uint16_t* A, int r, float s, uint16_t* gX, hipStream_t st);
+                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st);
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
                            hipStream_t st);
