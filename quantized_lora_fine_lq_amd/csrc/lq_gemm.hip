@@ -41,6 +41,7 @@ struct GemmParams {
   const uint16_t* t2;  // LoRA segment, A-side [M, R2] bf16: [hi(s L) | lo(s L) | 0]
   const uint16_t* lb2; // LoRA segment, Bt-side [Ncols, R2] bf16: [Lb | Lb | 0]
   int R2;              // 64 * ceil(2r / 64)
+  int gm;              // M-tiles per group of the tile order
   void* out;           // [M, Ncols]
   QWeight w;
   Nf4Levels lv;
@@ -364,9 +365,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   __shared__ f32x2_t sPair[256];
   if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
 
-  // XCD-aware tile order: the 8 XCDs take workgroups round robin, so give
-  // each XCD a contiguous range of tiles, M-tiles fastest (they share the
-  // same weight columns).
+  // XCD-aware tile order: the 8 XCDs take workgroups round robin, so each
+  // XCD gets a contiguous range of logical tiles. Logical tiles run over
+  // groups of p.gm M-tiles with the N-tiles outer inside a group, so the
+  // workgroups resident on one XCD at a time share p.gm A row-tiles and a
+  // run of consecutive weight tiles in that XCD's L2.
   const int64_t tiles_m = (p.M + BM - 1) / BM;
   const int64_t tiles_n = (p.Ncols + BN - 1) / BN;
   const int64_t total = tiles_m * tiles_n;
@@ -374,7 +377,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   const int64_t per = total / 8, rem = total % 8;
   const int64_t xcd = b % 8, local = b / 8;
   const int64_t logical = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int64_t tm = logical % tiles_m, tn = logical / tiles_m;
+  const int64_t group = (int64_t)p.gm * tiles_n;
+  const int64_t first_m = (logical / group) * p.gm;
+  const int64_t gm = min((int64_t)p.gm, tiles_m - first_m);
+  const int64_t within = logical % group;
+  const int64_t tm = first_m + within % gm, tn = within / gm;
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -437,7 +444,40 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
     __syncthreads();
   }
 
-  // epilogue: lane holds column li of each 32x32 tile, rows 8(v/4) + 4lh + v%4
+  // epilogue: lane holds column li of each 32x32 tile, rows 8(v/4) + 4lh + v%4.
+  // bfloat16 output with Ncols % 8 == 0: adjacent lanes swap one value so
+  // each holds a column pair of one row, the tile goes through LDS (the A
+  // buffers are free now), and each thread stores whole 16-byte row chunks.
+  if (!OUT_F32 && p.Ncols % 8 == 0) {
+    constexpr int CP = BN + 8;                 // 136 bf16 per staged row
+    uint16_t* sC = &sA[0][0];                  // 256 x 136 x 2 B fits in sA
+    const bool odd = li & 1;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float send = odd ? acc[rt][ct][v] : acc[rt][ct][v + 1];
+          const float recv = dpp_f32<DPP_QUAD_XOR1>(send);
+          const int row = 64 * wr + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3) + (odd ? 1 : 0);
+          const int col = 64 * wc + 32 * ct + (li & ~1);
+          const uint32_t pair = odd ? pack_bf16x2(recv, acc[rt][ct][v + 1]) : pack_bf16x2(acc[rt][ct][v], recv);
+          *reinterpret_cast<uint32_t*>(sC + row * CP + col) = pair;
+        }
+    __syncthreads();
+    const int c = threadIdx.x & 15;
+    const int64_t gcol = n0 + 8 * c;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = (threadIdx.x >> 4) + 32 * q;
+      const int64_t grow = m0 + row;
+      if (grow < p.M && gcol < p.Ncols)
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p.out) + grow * p.Ncols + gcol) =
+            *reinterpret_cast<const u32x4_t*>(sC + row * CP + 8 * c);
+    }
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -895,6 +935,9 @@ static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, in
   GemmParams p;
   p.A = A; p.M = M; p.Ncols = Ncols; p.Kc = Kc; p.out = out;
   p.t2 = nullptr; p.lb2 = nullptr; p.R2 = 0;
+  // 32 workgroups are resident per XCD: 2 A row-tiles x 16 weight tiles
+  // minimise the bytes they pull into the XCD's L2.
+  p.gm = (int)std::min<int64_t>(2, (M + BM - 1) / BM);
   p.w = w;
   p.lv = tables().lv;
   return p;

@@ -192,6 +192,8 @@ def oracle_wd(W, double=True):
     (520, 256, 17, 64, 16.0),      # just above the GEMV boundary, ragged N
     (256, 512, 1, 16, 32.0),       # single token
     (256, 512, 4, 24, 8.0),        # r not a multiple of 16
+    (100, 256, 40, 16, 32.0),      # N % 8 != 0: element-wise epilogue
+    (136, 192, 600, 40, 16.0),     # three M tiles, two LoRA steps (2r = 80)
 ])
 def test_forward(lq, torch, N, K, M, r, alpha):
     L, W, X, A, B = make_layer(100 + M, N, K, M, r, alpha)
