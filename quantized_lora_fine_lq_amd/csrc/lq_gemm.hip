@@ -23,8 +23,10 @@ namespace {
 //
 // Tile 256 x 128 x 64 per 512-thread workgroup (8 waves, two per SIMD, so
 // one wave's MFMAs overlap the other's loads, dequantization and LDS
-// traffic). Wave w owns rows [64 (w % 4), +64) and columns [64 (w / 4), +64)
-// of the tile: 2 x 2 MFMA 32x32x16 tiles. Per 64-wide k-step the A tile
+// traffic). Wave w owns rows [64 (w % 4), +64) and all 128 columns of the
+// tile (2 x 4 MFMA 32x32x16 tiles) over one half of every 64-wide k-step
+// (kh = w / 4); the two halves are summed at the end. Fragment traffic from
+// LDS is 0.75 KB per MFMA. Per 64-wide k-step the A tile
 // (rows of X or G) is staged in LDS with coalesced 16-byte loads, and the Bt
 // tile is dequantized cooperatively -- each weight once per workgroup --
 // into LDS. Both are double buffered; the global loads of step j are issued
@@ -77,35 +79,30 @@ __device__ __forceinline__ void store_a_tile(uint16_t* sA, const u32x4_t (&r)[4]
   for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(dst + 64 * q * PITCH) = r[q];
 }
 
-// 16 MFMAs of one 64-wide step, both operands from LDS: wave tile 64 x 64 =
-// [2 row tiles] x [2 col tiles]; fragments of sub-step s+1 are read while
-// sub-step s multiplies.
-__device__ __forceinline__ void mfma_step(const uint16_t* sAt, const uint16_t* sBt, f32x16_t (&acc)[2][2],
-                                          int wr, int wc, int li, int lh) {
-  const uint16_t* abase = sAt + (64 * wr + li) * PITCH + 32 * lh;
-  const uint16_t* bbase = sBt + (64 * wc + li) * PITCH + 32 * lh;
-  u32x4_t a[2][2], b[2][2];
+// 16 MFMAs of one half of a 64-wide step, both operands from LDS: wave tile
+// 64 x 128 = [2 row tiles] x [4 col tiles] over sub-steps 2 kh and 2 kh + 1
+// (the other wave of the pair takes the other half); all fragments of the
+// half are read up front.
+__device__ __forceinline__ void mfma_half(const uint16_t* sAt, const uint16_t* sBt, f32x16_t (&acc)[2][4],
+                                          int wr, int kh, int li, int lh) {
+  const uint16_t* abase = sAt + (64 * wr + li) * PITCH + 32 * lh + 16 * kh;
+  const uint16_t* bbase = sBt + li * PITCH + 32 * lh + 16 * kh;
+  u32x4_t a[2][2], b[2][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    a[0][t] = ld16(abase + 32 * t * PITCH);
-    b[0][t] = ld16(bbase + 32 * t * PITCH);
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) a[u][rt] = ld16(abase + 32 * rt * PITCH + 8 * u);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) b[u][ct] = ld16(bbase + 32 * ct * PITCH + 8 * u);
   }
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s < 3) {
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[(s + 1) & 1][t] = ld16(abase + 32 * t * PITCH + 8 * (s + 1));
-        b[(s + 1) & 1][t] = ld16(bbase + 32 * t * PITCH + 8 * (s + 1));
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[s & 1][rt]), as_bf16x8(b[s & 1][ct]),
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[u][rt]), as_bf16x8(b[u][ct]),
                                                               acc[rt][ct], 0, 0, 0);
-  }
 }
 
 // ---- LoRA segment tiles -------------------------------------------------------
@@ -385,7 +382,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   const int64_t m0 = tm * BM, n0 = tn * BN;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wr = wave & 3, wc = wave >> 2;
+  const int wr = wave & 3, kh = wave >> 2;
   const int li = lane & 31, lh = lane >> 5;
   const float mean = p.w.qc.absmax ? 0.0f : *p.w.qc.dq_mean;
   const int nMain = (int)((p.Kc + BK - 1) / BK);
@@ -394,11 +391,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   for (int q = 0; q < 4; ++q)
     ar[q] = p.A + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.Kc;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
@@ -423,13 +420,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   for (int it = 0; it < nMain; it += 2) {
     pa.load(p, it + 2, nMain);
     load_a_tile<TAIL>(p, min(it + 2, nMain - 1), ar, ra);
-    mfma_step(sA[0], sB[0], acc, wr, wc, li, lh);
+    mfma_half(sA[0], sB[0], acc, wr, kh, li, lh);
     pb.store(p, sB[1], sPair, mean);
     store_a_tile(sA[1], rb);
     __syncthreads();
     pb.load(p, it + 3, nMain);
     load_a_tile<TAIL>(p, min(it + 3, nMain - 1), ar, rb);
-    mfma_step(sA[1], sB[1], acc, wr, wc, li, lh);
+    mfma_half(sA[1], sB[1], acc, wr, kh, li, lh);
     pa.store(p, sB[0], sPair, mean);
     store_a_tile(sA[0], ra);
     __syncthreads();
@@ -440,31 +437,62 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   for (int jt = 0; jt < nLora; ++jt) {
     lora_tiles(p, jt, m0, n0, sA[0], sB[0]);
     __syncthreads();
-    mfma_step(sA[0], sB[0], acc, wr, wc, li, lh);
+    mfma_half(sA[0], sB[0], acc, wr, kh, li, lh);
     __syncthreads();
   }
 
-  // epilogue: lane holds column li of each 32x32 tile, rows 8(v/4) + 4lh + v%4.
-  // bfloat16 output with Ncols % 8 == 0: adjacent lanes swap one value so
-  // each holds a column pair of one row, the tile goes through LDS (the A
-  // buffers are free now), and each thread stores whole 16-byte row chunks.
+  // The two waves of a pair hold partial sums over the two k halves: the
+  // kh = 1 wave hands its accumulators over through LDS (the A buffers are
+  // free now), one 32-row tile at a time, in the lane order it holds them
+  // (four consecutive values per 16-byte access).
+  float* sR = reinterpret_cast<float*>(&sA[0][0]);   // 4 waves x 64 floats x 64 lanes = 64 KB
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    if (kh == 1) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          *reinterpret_cast<f32x4_t*>(sR + (((wr * 4 + ct) * 4 + v4) * 64 + lane) * 4) =
+              f32x4_t{acc[rt][ct][4 * v4], acc[rt][ct][4 * v4 + 1], acc[rt][ct][4 * v4 + 2], acc[rt][ct][4 * v4 + 3]};
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4_t o = *reinterpret_cast<const f32x4_t*>(sR + (((wr * 4 + ct) * 4 + v4) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rt][ct][4 * v4 + e] += o[e];
+        }
+    }
+    __syncthreads();
+  }
+
+  // epilogue (kh = 0 waves): lane holds column li of each 32x32 tile, rows
+  // 8(v/4) + 4lh + v%4. bfloat16 output with Ncols % 8 == 0: adjacent lanes
+  // swap one value so each holds a column pair of one row, the tile goes
+  // through LDS, and all threads store whole 16-byte row chunks.
   if (!OUT_F32 && p.Ncols % 8 == 0) {
     constexpr int CP = BN + 8;                 // 136 bf16 per staged row
     uint16_t* sC = &sA[0][0];                  // 256 x 136 x 2 B fits in sA
-    const bool odd = li & 1;
+    if (kh == 0) {
+      const bool odd = li & 1;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const float send = odd ? acc[rt][ct][v] : acc[rt][ct][v + 1];
-          const float recv = dpp_f32<DPP_QUAD_XOR1>(send);
-          const int row = 64 * wr + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3) + (odd ? 1 : 0);
-          const int col = 64 * wc + 32 * ct + (li & ~1);
-          const uint32_t pair = odd ? pack_bf16x2(recv, acc[rt][ct][v + 1]) : pack_bf16x2(acc[rt][ct][v], recv);
-          *reinterpret_cast<uint32_t*>(sC + row * CP + col) = pair;
-        }
+          for (int v = 0; v < 16; v += 2) {
+            const float send = odd ? acc[rt][ct][v] : acc[rt][ct][v + 1];
+            const float recv = dpp_f32<DPP_QUAD_XOR1>(send);
+            const int row = 64 * wr + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3) + (odd ? 1 : 0);
+            const int col = 32 * ct + (li & ~1);
+            const uint32_t pair = odd ? pack_bf16x2(recv, acc[rt][ct][v + 1]) : pack_bf16x2(acc[rt][ct][v], recv);
+            *reinterpret_cast<uint32_t*>(sC + row * CP + col) = pair;
+          }
+    }
     __syncthreads();
     const int c = threadIdx.x & 15;
     const int64_t gcol = n0 + 8 * c;
@@ -478,11 +506,12 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
     }
     return;
   }
+  if (kh != 0) return;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int64_t col = n0 + 64 * wc + 32 * ct + li;
+    for (int ct = 0; ct < 4; ++ct) {
+      const int64_t col = n0 + 32 * ct + li;
       if (col >= p.Ncols) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
