@@ -525,20 +525,22 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
 }
 
 // ===========================================================================
-// Decode GEMV (M <= 16), NF4. MFMA 16x16x32 with tokens as the 16 A-rows
+// Decode GEMV (M <= 16), NF4. MFMA 16x16x32 with the tokens as the 16 A-rows
 // (rows >= M repeat row M-1; their outputs are not stored) and 16 weight rows
-// per MFMA tile. A workgroup owns RG tiles (16*RG weight rows); its 8 waves
-// take 256-wide K chunks in turn. In a chunk, lane (li, lg) covers
-// k = 256c + 64lg + [0, 64): one whole 64-block per weight row, so one block
-// constant per 32 bytes of codes. Two register sets keep the next chunk's
-// codes and X in flight while the current one is dequantized straight into
-// MFMA B registers.
+// per MFMA tile. A workgroup owns 64 weight rows (4 row groups) and its 8
+// waves split K: wave w takes 64-blocks [w nb / 8, (w+1) nb / 8). For one
+// 64-block, lane (li, lg) of row group g takes k = 16 lg + [0, 16) of weight
+// row 16 g + li (8 code bytes, one load) and the same k of token li (from
+// global memory, L2-resident; one X fragment serves all 4 row groups). Codes
+// are dequantized straight into MFMA B registers; nothing goes through LDS
+// until the 8 partial sums are reduced at the end, where the LoRA term is
+// added. Three register stages keep two blocks of loads in flight.
 //
-// Level lookup without LDS: every lane holds q[lane % 16]; ds_bpermute takes
-// the source lane from address bits [7:2], so shifting the code word until the
-// wanted nibble sits at bits [5:2] is the whole address computation (the
-// bits above select one of the four identical 16-lane copies). No bank
-// conflicts, one VALU op per element for the address.
+// Level lookup without LDS memory: every lane holds q[lane % 16]; ds_bpermute
+// takes the source lane from address bits [7:2], so shifting the code word
+// until the wanted nibble sits at bits [5:2] is the whole address
+// computation (the bits above select one of the four identical 16-lane
+// copies). No bank conflicts, one VALU op per element for the address.
 // ===========================================================================
 struct GemvParams {
   const uint16_t* X;   // [M, K]
@@ -552,10 +554,6 @@ struct GemvParams {
   Nf4Levels lv;
 };
 
-// X slice [16 tokens][1024 k] in LDS, row pitch 1032 bf16 (2064 bytes: the
-// 16-byte fragment reads of 8 consecutive rows fall in distinct banks).
-constexpr int GV_XS = 1024 + 8;
-
 // 8 codes of one code word -> 8 bf16 (4 dwords). Element e sits at bit
 // 8*(e/2) + 4*(1 - e%2) of the word (high nibble first).
 __device__ __forceinline__ u32x4_t dequant8_bperm(uint32_t w, int qv, float cp) {
@@ -568,125 +566,121 @@ __device__ __forceinline__ u32x4_t dequant8_bperm(uint32_t w, int qv, float cp) 
                  pack_bf16x2(v[6], v[7])};
 }
 
-// Decode GEMV. A workgroup owns 16*WV weight rows (one 16-row group per wave)
-// and walks K in 1024-column iterations. Per iteration the code tile
-// [16*WV rows x 512 bytes] and the X slice [16 x 1024] are loaded with
-// contiguous 512-byte (codes) and 2 KB (X) runs per row into LDS -- reading
-// only 128 bytes per row per visit leaves HBM pages mostly unused -- and the
-// next iteration's tile is prefetched into registers meanwhile. Each wave
-// then takes its MFMA fragments from LDS: lane (li, lg) dequantizes block
-// 4s + lg of row li in step s. Iteration order is rotated by workgroup.
-constexpr int GV_CP = 512 + 16;          // code tile row pitch (bytes)
+constexpr int GV_WAVES = 8;      // K splits per workgroup
 
-template <int WV, bool DQ, bool OUT_F32>
-__global__ __launch_bounds__(64 * WV) void k_gemv_nf4(GemvParams p) {
-  constexpr int NT = 64 * WV;            // threads
-  constexpr int RW = 16 * WV;            // weight rows per workgroup
-  constexpr int CQ = RW * 32 / NT;       // 16-byte code loads per thread (= 8)
-  constexpr int XQ = 16 * 128 / NT;      // 16-byte X loads per thread
-  __shared__ __attribute__((aligned(16))) uint8_t sC[RW * GV_CP];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[16 * GV_XS];
+// One pipeline stage: two 64-blocks (128 k) of RG row groups.
+template <int RG, bool DQ>
+struct GvStage {
+  u32x4_t code[RG];      // 32 codes: k = 32 lg + [0, 32) of the stage
+  uint32_t q8[RG];
+  float c[RG];           // float32 constant, or dq scale s2
+  u32x4_t x[4];          // X fragments, k = 32 lg + 8 u + [0, 8)
+  float live;
+};
+
+template <int RG, bool DQ>
+__device__ __forceinline__ void gv_load(const GemvParams& p, const uint8_t* const (&crow)[RG],
+                                        const int64_t (&blkrow)[RG], const uint16_t* xrow, int lg,
+                                        int st2, int e1, int ns, int nb, GvStage<RG, DQ>& st) {
+  // the lane's block: 2 ss + lg / 2 (past the row when K/64 is odd and this
+  // is the last stage); its loads use a valid block either way and add 0
+  const int ss = min(st2, ns - 1);
+  const int bl = 2 * ss + (lg >> 1);
+  st.live = (st2 < e1 && bl < nb) ? 1.0f : 0.0f;
+  const int bb = min(bl, nb - 1);
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    st.code[g] = ld16(crow[g] + (int64_t)bb * 32 + 16 * (lg & 1));
+    const int64_t blk = blkrow[g] + bb;
+    if (DQ) {
+      st.q8[g] = p.w.qc.absmax_q[blk];
+      st.c[g] = p.w.qc.dq_scale[blk >> 8];
+    } else {
+      st.c[g] = p.w.qc.absmax[blk];
+    }
+  }
+  const uint16_t* xs = xrow + (int64_t)bb * 64 + 32 * (lg & 1);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.x[u] = ld16(xs + 8 * u);
+}
+
+template <int RG, bool DQ>
+__device__ __forceinline__ void gv_compute(const GvStage<RG, DQ>& st, int qv, float mean, f32x4_t (&acc)[RG]) {
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const float c = DQ ? __builtin_fmaf(e4m3_decode(st.q8[g]), st.c[g], mean) : st.c[g];
+    const float cp = c * st.live;   // c * 0 = 0 for a stage past the wave's range (c is finite)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4_t bv = dequant8_bperm(st.code[g][u], qv, cp);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc[g], 0, 0, 0);
+    }
+  }
+}
+
+// RG row groups (16 RG weight rows) per workgroup; the 8 waves split the
+// K/128 stages evenly. Lane (li, lg) of row group g takes, in each stage,
+// the 32 codes k = 32 lg + [0, 32) of row 16 g + li (one 16-byte load, all
+// inside one 64-block) and the same k of token li.
+template <int RG, bool DQ, bool OUT_F32>
+__global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
+  __shared__ __attribute__((aligned(16))) float sR[GV_WAVES][RG][4][64];   // [wave][group][v][lane]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t N = p.w.N, K = p.w.K;
-  const int64_t n0 = (int64_t)blockIdx.x * RW;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
+  const int nb = (int)(K / 64);
+  const int ns = (int)((K + 127) / 128);   // stages; the last one is half empty when nb is odd
+  const int e0 = (int)((int64_t)wave * ns / GV_WAVES), e1 = (int)((int64_t)(wave + 1) * ns / GV_WAVES);
   const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
   const int qv = __float_as_int(p.lv.q[li]);
-  const int64_t nrow = min(n0 + 16 * wave + li, N - 1);   // rows past N: outputs not stored
-  const int64_t Kb = K / 2;                               // code bytes per row
 
-  // code tile loads: load q of thread t -> tile row t/32 + (NT/32) q, bytes 16 (t%32)
-  const int crr = threadIdx.x >> 5, cby = 16 * (threadIdx.x & 31);
-  // X slice loads: load q -> token t/128 + (NT/128) q, columns 8 (t%128)
-  const int xrr = threadIdx.x >> 7, xcol = 8 * (threadIdx.x & 127);
+  const uint8_t* crow[RG];
+  int64_t blkrow[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int64_t n = min(n0 + 16 * g + li, N - 1);   // rows past N: outputs not stored
+    crow[g] = p.w.codes + n * (K / 2);
+    blkrow[g] = n * nb;
+  }
+  const uint16_t* xrow = p.X + min((int64_t)li, p.M - 1) * K;
 
-  const int64_t nit = (K + 1023) / 1024;
-  const int64_t rot = blockIdx.x % nit;
-  auto col_of = [&](int64_t i) -> int64_t {
-    int64_t ii = min(i, nit - 1) + rot;
-    ii = ii >= nit ? ii - nit : ii;
-    return ii * 1024;
-  };
+  f32x4_t acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t cr[CQ], xr[XQ];
-  float c0v[4], s2v[4];
-  uint32_t q8v[4];
-  bool livev[4];
-  auto issue = [&](int64_t i) {
-    const int64_t c0 = col_of(i);
-#pragma unroll
-    for (int q = 0; q < CQ; ++q) {
-      const int64_t row = min(n0 + crr + (NT / 32) * q, N - 1);
-      const int64_t byte = c0 / 2 + cby;
-      cr[q] = ld16(p.w.codes + row * Kb + (byte + 16 <= Kb ? byte : 0));
-    }
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {   // token rows >= M only feed outputs that are not stored
-      const int64_t m = xrr + (NT / 128) * q;
-      const int64_t col = c0 + xcol;
-      if (m < p.M) xr[q] = ld16(p.X + m * K + (col + 8 <= K ? col : 0));
-    }
-    // block constants of the lane's four blocks (steps s = 0..3)
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int64_t kb = c0 + 256 * st + 64 * lg;
-      livev[st] = i < nit && kb < K;
-      const int64_t blk = (nrow * K + (livev[st] ? kb : 0)) >> 6;
-      if (DQ) {
-        q8v[st] = p.w.qc.absmax_q[blk];
-        s2v[st] = p.w.qc.dq_scale[blk >> 8];
-      } else {
-        c0v[st] = p.w.qc.absmax[blk];
-      }
-    }
-  };
-
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  for (int64_t i = 0; i < nit; ++i) {
-    __syncthreads();                     // previous tile fully read
-#pragma unroll
-    for (int q = 0; q < CQ; ++q)
-      *reinterpret_cast<u32x4_t*>(sC + (crr + (NT / 32) * q) * GV_CP + cby) = cr[q];
-#pragma unroll
-    for (int q = 0; q < XQ; ++q)
-      if (xrr + (NT / 128) * q < p.M)
-        *reinterpret_cast<u32x4_t*>(sX + (xrr + (NT / 128) * q) * GV_XS + xcol) = xr[q];
-    float cp[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const float c = DQ ? __builtin_fmaf(e4m3_decode(q8v[st]), s2v[st], mean) : c0v[st];
-      cp[st] = livev[st] ? c : 0.0f;
-    }
-    issue(i + 1);
-    __syncthreads();                     // tile i staged
-    const uint8_t* crow = sC + (16 * wave + li) * GV_CP;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const u32x4_t w0 = ld16(crow + 128 * st + 32 * lg);
-      const u32x4_t w1 = ld16(crow + 128 * st + 32 * lg + 16);
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        const uint32_t w = s8 < 4 ? w0[s8] : w1[s8 - 4];
-        const u32x4_t bv = dequant8_bperm(w, qv, cp[st]);
-        const u32x4_t xa = ld16(sX + li * GV_XS + 256 * st + 64 * lg + 8 * s8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(bv), acc, 0, 0, 0);
-      }
-    }
+  GvStage<RG, DQ> s0, s1;
+  gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, e0, e1, ns, nb, s0);
+  for (int st = e0; st < e1; st += 2) {
+    gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, st + 1, e1, ns, nb, s1);
+    gv_compute<RG, DQ>(s0, qv, mean, acc);
+    gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, st + 2, e1, ns, nb, s0);
+    gv_compute<RG, DQ>(s1, qv, mean, acc);
   }
 
-  // lane holds tokens 4*lg + v of weight row n0 + 16*wave + li
-  const int64_t n = n0 + 16 * wave + li;
-  if (n >= N) return;
+  // reduce the 8 K-splits; lane (li, lg) holds tokens 4 lg + v of row 16 g + li
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t m = 4 * lg + v;
-    if (m >= p.M) continue;
-    float lora = 0.0f;
-    for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(p.t[m * p.r + j], bf16_to_f32(p.B[n * p.r + j]), lora);
-    const float h = acc[v] + p.s * lora;
-    if (OUT_F32) reinterpret_cast<float*>(p.out)[m * N + n] = h;
-    else reinterpret_cast<uint16_t*>(p.out)[m * N + n] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sR[wave][g][v][lane] = acc[g][v];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < RG * 64; idx += 64 * GV_WAVES) {
+    const int g = idx >> 6, ln = idx & 63;
+    const int64_t n = n0 + 16 * g + (ln & 15);
+    if (n >= N) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = 4 * (ln >> 4) + v;
+      if (m >= p.M) continue;
+      float h = 0.0f;
+#pragma unroll
+      for (int w = 0; w < GV_WAVES; ++w) h += sR[w][g][v][ln];
+      float lora = 0.0f;
+      for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(p.t[m * p.r + j], bf16_to_f32(p.B[n * p.r + j]), lora);
+      h += p.s * lora;
+      if (OUT_F32) reinterpret_cast<float*>(p.out)[m * N + n] = h;
+      else reinterpret_cast<uint16_t*>(p.out)[m * N + n] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+    }
   }
 }
 
@@ -1014,13 +1008,13 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   return hipGetLastError();
 }
 
-template <int WV>
-static void launch_gemv_wv(const GemvParams& p, bool dq, bool f32, hipStream_t st) {
-  const dim3 grid((unsigned)((p.w.N + 16 * WV - 1) / (16 * WV))), block(64 * WV);
-  if (dq && f32) hipLaunchKernelGGL((k_gemv_nf4<WV, true, true>), grid, block, 0, st, p);
-  else if (dq) hipLaunchKernelGGL((k_gemv_nf4<WV, true, false>), grid, block, 0, st, p);
-  else if (f32) hipLaunchKernelGGL((k_gemv_nf4<WV, false, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((k_gemv_nf4<WV, false, false>), grid, block, 0, st, p);
+template <int RG>
+static void launch_gemv_rg(const GemvParams& p, bool dq, bool f32, hipStream_t st) {
+  const dim3 grid((unsigned)((p.w.N + 16 * RG - 1) / (16 * RG))), block(64 * GV_WAVES);
+  if (dq && f32) hipLaunchKernelGGL((k_gemv_nf4<RG, true, true>), grid, block, 0, st, p);
+  else if (dq) hipLaunchKernelGGL((k_gemv_nf4<RG, true, false>), grid, block, 0, st, p);
+  else if (f32) hipLaunchKernelGGL((k_gemv_nf4<RG, false, true>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((k_gemv_nf4<RG, false, false>), grid, block, 0, st, p);
 }
 
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
@@ -1029,9 +1023,14 @@ hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
-  // 8 waves (128 rows) when X is large enough for its re-reads to matter
-  if (M > 4) launch_gemv_wv<8>(p, dq, f32, st);
-  else launch_gemv_wv<4>(p, dq, f32, st);
+  // 4 or 7 row groups per workgroup, whichever fills the last round of 256
+  // CUs better (7 gives exactly 256 workgroups for 28672 rows).
+  auto fill = [&](int rg) {
+    const int64_t wgs = (w.N + 16 * rg - 1) / (16 * rg);
+    return (double)wgs / (double)(((wgs + 255) / 256) * 256);
+  };
+  if (fill(7) > fill(4) + 0.01) launch_gemv_rg<7>(p, dq, f32, st);
+  else launch_gemv_rg<4>(p, dq, f32, st);
   return hipGetLastError();
 }
 
