@@ -46,7 +46,7 @@ int check_qweight(const lq_qweight* w, QWeight* out) {
 // Forward path choice: the GEMV kernel for decode-sized M (NF4 only), else
 // the MFMA GEMM. LQ_FORCE_PATH=gemm|gemv overrides (for tests).
 bool use_gemv(const QWeight& w, int64_t M) {
-  if (w.format != LQ_FMT_NF4 || M > 16) return false;
+  if (M > 16 || !gemv_supported(w)) return false;
   const char* f = std::getenv("LQ_FORCE_PATH");
   if (f && std::strcmp(f, "gemm") == 0) return false;
   return true;

@@ -527,20 +527,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
 // ===========================================================================
 // Decode GEMV (M <= 16), NF4. MFMA 16x16x32 with the tokens as the 16 A-rows
 // (rows >= M repeat row M-1; their outputs are not stored) and 16 weight rows
-// per MFMA tile. A workgroup owns 64 weight rows (4 row groups) and its 8
-// waves split K: wave w takes 64-blocks [w nb / 8, (w+1) nb / 8). For one
-// 64-block, lane (li, lg) of row group g takes k = 16 lg + [0, 16) of weight
-// row 16 g + li (8 code bytes, one load) and the same k of token li (from
-// global memory, L2-resident; one X fragment serves all 4 row groups). Codes
-// are dequantized straight into MFMA B registers; nothing goes through LDS
-// until the 8 partial sums are reduced at the end, where the LoRA term is
-// added. Three register stages keep two blocks of loads in flight.
-//
-// Level lookup without LDS memory: every lane holds q[lane % 16]; ds_bpermute
-// takes the source lane from address bits [7:2], so shifting the code word
-// until the wanted nibble sits at bits [5:2] is the whole address
-// computation (the bits above select one of the four identical 16-lane
-// copies). No bank conflicts, one VALU op per element for the address.
+// per MFMA tile. A workgroup owns RG row groups (16 RG weight rows); its 8
+// waves split the K/128 stages evenly. In a stage, lane (li, lg) of row group
+// g takes the 32 codes k = 32 lg + [0, 32) of row 16 g + li (one 16-byte
+// load, inside one 64-block) and the same k of token li (from global
+// memory, L2-resident; one X fragment serves all row groups). Codes are
+// dequantized straight into MFMA B registers through a 256-entry LDS table
+// of level pairs (one 8-byte lookup per code byte). The block constants of
+// the workgroup's rows are decoded once into LDS at the start, so the main
+// loop loads nothing but codes and X. The 8 partial sums are reduced in LDS
+// at the end, where the LoRA term is added.
 // ===========================================================================
 struct GemvParams {
   const uint16_t* X;   // [M, K]
@@ -554,115 +550,122 @@ struct GemvParams {
   Nf4Levels lv;
 };
 
-// 8 codes of one code word -> 8 bf16 (4 dwords). Element e sits at bit
-// 8*(e/2) + 4*(1 - e%2) of the word (high nibble first).
-__device__ __forceinline__ u32x4_t dequant8_bperm(uint32_t w, int qv, float cp) {
-  const int a[8] = {(int)(w >> 2),  (int)(w << 2),  (int)(w >> 10), (int)(w >> 6),
-                    (int)(w >> 18), (int)(w >> 14), (int)(w >> 26), (int)(w >> 22)};
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = __int_as_float(__builtin_amdgcn_ds_bpermute(a[e], qv)) * cp;
-  return u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                 pack_bf16x2(v[6], v[7])};
-}
-
-constexpr int GV_WAVES = 8;      // K splits per workgroup
+constexpr int GV_WAVES = 8;        // K splits per workgroup
+constexpr int GV_CTAB = 24576;     // floats of LDS for the constant table (96 KB)
 
 // One pipeline stage: two 64-blocks (128 k) of RG row groups.
-template <int RG, bool DQ>
+template <int RG>
 struct GvStage {
   u32x4_t code[RG];      // 32 codes: k = 32 lg + [0, 32) of the stage
-  uint32_t q8[RG];
-  float c[RG];           // float32 constant, or dq scale s2
   u32x4_t x[4];          // X fragments, k = 32 lg + 8 u + [0, 8)
+  int bl;                // the lane's block within the row
   float live;
 };
 
-template <int RG, bool DQ>
-__device__ __forceinline__ void gv_load(const GemvParams& p, const uint8_t* const (&crow)[RG],
-                                        const int64_t (&blkrow)[RG], const uint16_t* xrow, int lg,
-                                        int st2, int e1, int ns, int nb, GvStage<RG, DQ>& st) {
+template <int RG>
+__device__ __forceinline__ void gv_load(const uint8_t* const (&crow)[RG], const uint16_t* xrow, int lg,
+                                        int st2, int e1, int ns, int nb, GvStage<RG>& st) {
   // the lane's block: 2 ss + lg / 2 (past the row when K/64 is odd and this
   // is the last stage); its loads use a valid block either way and add 0
   const int ss = min(st2, ns - 1);
   const int bl = 2 * ss + (lg >> 1);
   st.live = (st2 < e1 && bl < nb) ? 1.0f : 0.0f;
-  const int bb = min(bl, nb - 1);
+  st.bl = min(bl, nb - 1);
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    st.code[g] = ld16(crow[g] + (int64_t)bb * 32 + 16 * (lg & 1));
-    const int64_t blk = blkrow[g] + bb;
-    if (DQ) {
-      st.q8[g] = p.w.qc.absmax_q[blk];
-      st.c[g] = p.w.qc.dq_scale[blk >> 8];
-    } else {
-      st.c[g] = p.w.qc.absmax[blk];
-    }
-  }
-  const uint16_t* xs = xrow + (int64_t)bb * 64 + 32 * (lg & 1);
+  for (int g = 0; g < RG; ++g) st.code[g] = ld16(crow[g] + (int64_t)st.bl * 32 + 16 * (lg & 1));
+  const uint16_t* xs = xrow + (int64_t)st.bl * 64 + 32 * (lg & 1);
 #pragma unroll
   for (int u = 0; u < 4; ++u) st.x[u] = ld16(xs + 8 * u);
 }
 
-template <int RG, bool DQ>
-__device__ __forceinline__ void gv_compute(const GvStage<RG, DQ>& st, int qv, float mean, f32x4_t (&acc)[RG]) {
+// 8 codes of one code word -> 8 bf16 through the LDS table of level pairs
+// (high nibble = first level).
+__device__ __forceinline__ u32x4_t dequant8_pair(uint32_t w, const f32x2_t* sPair, float cp) {
+  u32x4_t o;
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const float c = DQ ? __builtin_fmaf(e4m3_decode(st.q8[g]), st.c[g], mean) : st.c[g];
-    const float cp = c * st.live;   // c * 0 = 0 for a stage past the wave's range (c is finite)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4_t bv = dequant8_bperm(st.code[g][u], qv, cp);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc[g], 0, 0, 0);
-    }
+  for (int b = 0; b < 4; ++b) {
+    const f32x2_t q = sPair[(w >> (8 * b)) & 0xFFu];
+    o[b] = pack_bf16x2(q.x * cp, q.y * cp);
   }
+  return o;
 }
 
-// RG row groups (16 RG weight rows) per workgroup; the 8 waves split the
-// K/128 stages evenly. Lane (li, lg) of row group g takes, in each stage,
-// the 32 codes k = 32 lg + [0, 32) of row 16 g + li (one 16-byte load, all
-// inside one 64-block) and the same k of token li.
+// Sub-step outer, row group inner: consecutive MFMAs go to different
+// accumulators, so none waits for the previous one.
+template <int RG>
+__device__ __forceinline__ void gv_compute(const GvStage<RG>& st, const f32x2_t* sPair, const float* sC,
+                                           int pitch, int li, f32x4_t (&acc)[RG]) {
+  float cp[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) cp[g] = sC[(16 * g + li) * pitch + st.bl] * st.live;   // c * 0 = 0
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const u32x4_t bv = dequant8_pair(st.code[g][u], sPair, cp[g]);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc[g], 0, 0, 0);
+    }
+}
+
 template <int RG, bool DQ, bool OUT_F32>
 __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
-  __shared__ __attribute__((aligned(16))) float sR[GV_WAVES][RG][4][64];   // [wave][group][v][lane]
+  __shared__ __attribute__((aligned(16))) float sC[GV_CTAB];   // constants [16 RG rows][nb + 1]; then partial sums
+  __shared__ f32x2_t sPair[256];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t N = p.w.N, K = p.w.K;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * RG;
   const int nb = (int)(K / 64);
+  const int pitch = nb + 1;                // odd pitch: the 16 rows of a lookup hit distinct banks
   const int ns = (int)((K + 127) / 128);   // stages; the last one is half empty when nb is odd
   const int e0 = (int)((int64_t)wave * ns / GV_WAVES), e1 = (int)((int64_t)(wave + 1) * ns / GV_WAVES);
-  const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
-  const int qv = __float_as_int(p.lv.q[li]);
 
   const uint8_t* crow[RG];
-  int64_t blkrow[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int64_t n = min(n0 + 16 * g + li, N - 1);   // rows past N: outputs not stored
-    crow[g] = p.w.codes + n * (K / 2);
-    blkrow[g] = n * nb;
-  }
+  for (int g = 0; g < RG; ++g) crow[g] = p.w.codes + min(n0 + 16 * g + li, N - 1) * (K / 2);   // rows past N: not stored
   const uint16_t* xrow = p.X + min((int64_t)li, p.M - 1) * K;
+
+  // first stage's loads go out before the constant table is built
+  GvStage<RG> s0, s1;
+  gv_load<RG>(crow, xrow, lg, e0, e1, ns, nb, s0);
+
+  if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
+  const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
+  const int ncon = 16 * RG * nb;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < ncon; i += 64 * GV_WAVES) {
+    const int rr = i / nb, bl = i - rr * nb;
+    const int64_t blk = min(n0 + rr, N - 1) * nb + bl;
+    const float c = DQ ? __builtin_fmaf(e4m3_decode(p.w.qc.absmax_q[blk]), p.w.qc.dq_scale[blk >> 8], mean)
+                       : p.w.qc.absmax[blk];
+    sC[rr * pitch + bl] = c;
+  }
+  __syncthreads();
 
   f32x4_t acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  GvStage<RG, DQ> s0, s1;
-  gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, e0, e1, ns, nb, s0);
+  // The scheduling barriers keep each stage's loads where they are issued
+  // (left alone, the compiler sinks them next to their first use and the
+  // wave then waits for them).
   for (int st = e0; st < e1; st += 2) {
-    gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, st + 1, e1, ns, nb, s1);
-    gv_compute<RG, DQ>(s0, qv, mean, acc);
-    gv_load<RG, DQ>(p, crow, blkrow, xrow, lg, st + 2, e1, ns, nb, s0);
-    gv_compute<RG, DQ>(s1, qv, mean, acc);
+    gv_load<RG>(crow, xrow, lg, st + 1, e1, ns, nb, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    gv_compute<RG>(s0, sPair, sC, pitch, li, acc);
+    gv_load<RG>(crow, xrow, lg, st + 2, e1, ns, nb, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    gv_compute<RG>(s1, sPair, sC, pitch, li, acc);
   }
 
-  // reduce the 8 K-splits; lane (li, lg) holds tokens 4 lg + v of row 16 g + li
+  // reduce the 8 K-splits (the constant table is free now); lane (li, lg)
+  // holds tokens 4 lg + v of row 16 g + li
+  __syncthreads();
+  float* sR = sC;   // [wave][group][v][lane]
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sR[wave][g][v][lane] = acc[g][v];
+    for (int v = 0; v < 4; ++v) sR[((wave * RG + g) * 4 + v) * 64 + lane] = acc[g][v];
   __syncthreads();
   for (int idx = threadIdx.x; idx < RG * 64; idx += 64 * GV_WAVES) {
     const int g = idx >> 6, ln = idx & 63;
@@ -674,7 +677,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
       if (m >= p.M) continue;
       float h = 0.0f;
 #pragma unroll
-      for (int w = 0; w < GV_WAVES; ++w) h += sR[w][g][v][ln];
+      for (int w = 0; w < GV_WAVES; ++w) h += sR[((w * RG + g) * 4 + v) * 64 + ln];
       float lora = 0.0f;
       for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(p.t[m * p.r + j], bf16_to_f32(p.B[n * p.r + j]), lora);
       h += p.s * lora;
@@ -1008,6 +1011,20 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   return hipGetLastError();
 }
 
+// 4 or 7 row groups per workgroup, whichever fills the last round of 256
+// CUs better (7 gives exactly 256 workgroups for 28672 rows).
+static int gemv_rg(int64_t N) {
+  auto fill = [&](int rg) {
+    const int64_t wgs = (N + 16 * rg - 1) / (16 * rg);
+    return (double)wgs / (double)(((wgs + 255) / 256) * 256);
+  };
+  return fill(7) > fill(4) + 0.01 ? 7 : 4;
+}
+
+bool gemv_supported(const QWeight& w) {
+  return w.format == LQ_FMT_NF4 && (int64_t)16 * gemv_rg(w.N) * (w.K / 64 + 1) <= GV_CTAB;
+}
+
 template <int RG>
 static void launch_gemv_rg(const GemvParams& p, bool dq, bool f32, hipStream_t st) {
   const dim3 grid((unsigned)((p.w.N + 16 * RG - 1) / (16 * RG))), block(64 * GV_WAVES);
@@ -1020,16 +1037,11 @@ static void launch_gemv_rg(const GemvParams& p, bool dq, bool f32, hipStream_t s
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
                            hipStream_t st) {
+  if (!gemv_supported(w)) return hipErrorInvalidValue;
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
-  // 4 or 7 row groups per workgroup, whichever fills the last round of 256
-  // CUs better (7 gives exactly 256 workgroups for 28672 rows).
-  auto fill = [&](int rg) {
-    const int64_t wgs = (w.N + 16 * rg - 1) / (16 * rg);
-    return (double)wgs / (double)(((wgs + 255) / 256) * 256);
-  };
-  if (fill(7) > fill(4) + 0.01) launch_gemv_rg<7>(p, dq, f32, st);
+  if (gemv_rg(w.N) == 7) launch_gemv_rg<7>(p, dq, f32, st);
   else launch_gemv_rg<4>(p, dq, f32, st);
   return hipGetLastError();
 }

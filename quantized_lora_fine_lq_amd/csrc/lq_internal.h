@@ -88,6 +88,9 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
                            hipStream_t st);
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
                            const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st);
+// The decode GEMV handles NF4 weights whose per-workgroup constant table
+// fits in LDS (K up to about 14000 for wide N); others use the GEMM.
+bool gemv_supported(const QWeight& w);
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
                            hipStream_t st);
