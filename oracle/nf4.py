@@ -173,3 +173,19 @@ def roundtrip_error(W: np.ndarray, block: int = BLOCK) -> float:
     rec = (q[codes] * c[:, None]).astype(np.float64)
     diff = np.asarray(W, dtype=np.float64).reshape(-1, block) - rec
     return float(np.sum(diff * diff) / diff.size)
+
+
+TAU = 0.01   # AQLoRA page, section 3.1: threshold of the small-weight fraction
+
+
+def small_fraction(W: np.ndarray, tau: float = TAU) -> float:
+    """AQLoRA page, section 3.1: s = Pr[|w| < tau] over the layer's weights.
+    The comparison is exact: |w| (a float32 value) against tau in float64."""
+    a = np.abs(np.asarray(W, dtype=np.float32).astype(np.float64))
+    return float(np.count_nonzero(a < tau)) / a.size
+
+
+def profile(W: np.ndarray, tau: float = TAU, block: int = BLOCK):
+    """The AQLoRA profiling pass of one layer (section 3.1): returns
+    (eps, s) = (mean squared NF4 round-trip error, small-weight fraction)."""
+    return roundtrip_error(W, block), small_fraction(W, tau)

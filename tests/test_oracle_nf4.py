@@ -170,3 +170,54 @@ def test_aqlora_error_of_exact_levels_is_zero():
     q = nf4.levels()
     W = np.tile(q * np.float32(0.5), 4).reshape(1, 64).astype(np.float32)
     assert nf4.roundtrip_error(W) == 0.0
+
+
+def test_profile_error_matches_bruteforce_nearest():
+    """eps from the threshold-count quantizer equals the error of a brute-force
+    nearest-level reconstruction (independent code path, ties never hit by
+    random data)."""
+    rng = np.random.default_rng(21)
+    W = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    blocks = W.reshape(-1, 64)
+    c = np.abs(blocks).max(axis=1)
+    q = nf4.levels()
+    total = 0.0
+    for b, cb in zip(blocks, c):
+        x = (b / cb).astype(np.float32)
+        k = nf4.nearest_code_bruteforce(x, q)
+        rec = (q[k] * cb).astype(np.float32).astype(np.float64)
+        total += float(np.sum((b.astype(np.float64) - rec) ** 2))
+    eps, s = nf4.profile(W)
+    assert eps == pytest.approx(total / W.size, rel=1e-12)
+
+
+def test_profile_power_of_two_scaling_is_exact():
+    """Every step of the round trip commutes with a power-of-two scale, so
+    eps(2^k W) = 4^k eps(W) exactly (no subnormals involved)."""
+    rng = np.random.default_rng(22)
+    W = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    e1, _ = nf4.profile(W)
+    e2, _ = nf4.profile((W * np.float32(8.0)).astype(np.float32))
+    assert e2 == 64.0 * e1
+
+
+def test_profile_small_fraction_threshold():
+    """s counts |w| < 0.01: the float32 nearest 0.01 lies just below it and
+    counts; the next float32 up does not; signs do not matter."""
+    t32 = np.float32(0.01)
+    assert float(t32) < 0.01
+    up = np.nextafter(t32, np.float32(1.0))
+    W = np.array([t32, -t32, up, -up, 0.0, -0.0, 0.005, 0.5] + [1.0] * 56, dtype=np.float32).reshape(1, 64)
+    _, s = nf4.profile(W)
+    assert s == 5 / 64      # +-t32, +-0, 0.005
+
+
+def test_profile_single_spike_blocks_have_zero_error():
+    """A block with one nonzero weight maps it to +-1 (exact) and the zeros to
+    the zero level, so its round trip is exact."""
+    W = np.zeros((2, 64), dtype=np.float32)
+    W[0, 5] = 0.037
+    W[1, 60] = -3.5
+    eps, s = nf4.profile(W)
+    assert eps == 0.0
+    assert s == 126 / 128
