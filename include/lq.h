@@ -148,6 +148,26 @@ int lq_sizes(int64_t N, int64_t K, int32_t bits, lq_sizes_t* out);
 int lq_quantize_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
                     uint8_t* codes, float* absmax, void* stream);
 
+/* Workspace bytes for lq_profile_nf4: 16 bytes per 64 weight blocks. */
+size_t lq_profile_workspace(int64_t N, int64_t K, int32_t blocksize);
+
+/*
+ * AQLoRA profiling pass ([AQLoRA] section 3.1): for one layer's weight
+ * W [N, K] (dtype LQ_F32 / LQ_BF16 / LQ_F16, bf16 and f16 converted exactly),
+ * flattened into 64-blocks as in lq_quantize_nf4,
+ *   stats[0] = eps = (1/|W|) * sum over blocks of ||b - NF4^-1(NF4(b))||_2^2
+ *   stats[1] = s   = fraction of weights with |w| < tau (exact comparison)
+ * The round trip uses the float32 block constant and the float32 product
+ * level * constant; each squared error is formed in float64 and the sum is
+ * reduced in a fixed order (the result is reproducible run to run).
+ *   stats  device double [2], written
+ *   workspace  device memory of lq_profile_workspace(N, K, 64) bytes
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (K % 64 != 0, sizes <= 0),
+ * LQ_ERR_UNSUPPORTED (blocksize != 64), LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_profile_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize, double tau,
+                   double* stats, void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for lq_double_quant (float64 partial sums). */
 size_t lq_double_quant_workspace(int64_t n_blocks, int32_t dq_blocksize);
 

@@ -55,6 +55,8 @@ SIGNATURES = {
     "lq_nf4_table": (ctypes.c_int, [c_vp, c_vp]),
     "lq_sizes": (ctypes.c_int, [c_i64, c_i64, c_i32, ctypes.POINTER(lq_sizes_t)]),
     "lq_quantize_nf4": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
+    "lq_profile_workspace": (c_sz, [c_i64, c_i64, c_i32]),
+    "lq_profile_nf4": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, ctypes.c_double, c_vp, c_vp, c_sz, c_vp]),
     "lq_double_quant_workspace": (c_sz, [c_i64, c_i32]),
     "lq_double_quant": (ctypes.c_int, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_dequant": (ctypes.c_int, [QW_P, c_vp, c_vp]),
@@ -158,6 +160,20 @@ def quantize_nf4(W, blocksize: int = 64):
     _check(lib.lq_quantize_nf4(_ptr(W), _dtype_code(W), N, K, blocksize, _ptr(codes), _ptr(absmax),
                                _stream(W.device)), "lq_quantize_nf4")
     return codes, absmax
+
+
+def profile_nf4(W, tau: float = 0.01, blocksize: int = 64):
+    """AQLoRA profiling pass of one layer: device float64 tensor
+    [eps, fraction of |w| < tau]."""
+    torch = _torch()
+    _contig_cuda(W, "W")
+    N, K = W.shape
+    stats = torch.empty(2, dtype=torch.float64, device=W.device)
+    ws_bytes = lib.lq_profile_workspace(N, K, blocksize)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=W.device)
+    _check(lib.lq_profile_nf4(_ptr(W), _dtype_code(W), N, K, blocksize, float(tau), _ptr(stats), _ptr(ws),
+                              ws_bytes, _stream(W.device)), "lq_profile_nf4")
+    return stats
 
 
 def double_quant(absmax, dq_blocksize: int = 256):

@@ -124,6 +124,21 @@ int lq_quantize_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t 
   return launch_status(launch_quantize_nf4(W, dtype, N * K / 64, codes, absmax, (hipStream_t)stream));
 }
 
+size_t lq_profile_workspace(int64_t N, int64_t K, int32_t blocksize) {
+  if (N <= 0 || K <= 0 || K % 64 != 0 || blocksize != 64) return 0;
+  return align_up(profile_ws_doubles(N * K / 64) * sizeof(double));
+}
+
+int lq_profile_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize, double tau,
+                   double* stats, void* workspace, size_t ws_bytes, void* stream) {
+  if (!W || !stats || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
+  if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < lq_profile_workspace(N, K, blocksize)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_profile_nf4(W, dtype, N * K / 64, tau, stats, (double*)workspace,
+                                          (hipStream_t)stream));
+}
+
 size_t lq_double_quant_workspace(int64_t n_blocks, int32_t dq_blocksize) {
   if (n_blocks <= 0 || dq_blocksize != 256) return 0;
   return align_up(double_quant_ws_doubles(n_blocks) * sizeof(double));

@@ -102,6 +102,100 @@ __global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W,
 }
 
 // ---------------------------------------------------------------------------
+// AQLoRA profiling pass (AQLoRA page, section 3.1): per layer, the mean
+// squared error of the absmax-NF4 round trip and the fraction of weights with
+// |w| < tau. Same block layout and code search as the quantizer; the
+// reconstruction is the float32 product level * absmax, the error of each
+// weight is squared in float64. Per workgroup: the error sum and the small
+// count (both exact to float64 rounding of the sum), written to part[2 wg],
+// then summed in a fixed order by k_profile_finish.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ __launch_bounds__(256) void k_profile_nf4(const Tin* __restrict__ W, int64_t n_blocks, Nf4Lut lut,
+                                                     Nf4Levels lv, double tau, double* __restrict__ part) {
+  __shared__ float sT[33];
+  __shared__ int32_t sB[33];
+  __shared__ float sQ[16];
+  __shared__ double sW[2][4];
+  if (threadIdx.x < 33) {
+    sT[threadIdx.x] = lut.T[threadIdx.x];
+    sB[threadIdx.x] = lut.base[threadIdx.x];
+  }
+  if (threadIdx.x < 16) sQ[threadIdx.x] = lv.q[threadIdx.x];
+  __syncthreads();
+  const int i16 = threadIdx.x & 15;
+  const int64_t blk0 = (int64_t)blockIdx.x * (16 * kQuantPasses) + (threadIdx.x >> 4);
+  f32x4_t v[kQuantPasses];
+#pragma unroll
+  for (int p = 0; p < kQuantPasses; ++p) {
+    const int64_t blk = blk0 + 16 * p;
+    v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  double err = 0.0, cnt = 0.0;
+#pragma unroll
+  for (int p = 0; p < kQuantPasses; ++p) {
+    const int64_t blk = blk0 + 16 * p;
+    float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+    m = row16_max(m);
+    const bool fast_ok = (m >= FLT_MIN) && (m <= 0x1p125f);
+    const float r = fast_ok ? 1.0f / m : 0.0f;
+    if (blk < n_blocks) {
+      const float w4[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t code = nf4_code(w4[e], m, r, fast_ok, sT, sB);
+        const float rec = sQ[code] * m;
+        const double d = (double)w4[e] - (double)rec;
+        err = __builtin_fma(d, d, err);
+        cnt += (fabs((double)w4[e]) < tau) ? 1.0 : 0.0;
+      }
+    }
+  }
+  // fixed-order reductions: butterfly inside the wave, then the 4 waves in order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    err += __shfl_xor(err, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sW[0][wave] = err;
+    sW[1][wave] = cnt;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = ((sW[0][0] + sW[0][1]) + sW[0][2]) + sW[0][3];
+    part[2 * blockIdx.x + 1] = ((sW[1][0] + sW[1][1]) + sW[1][2]) + sW[1][3];
+  }
+}
+
+// One workgroup: thread t sums parts t, t + 1024, ... in order, then a
+// pairwise tree over the 1024 thread sums. out = {err / n, count / n}.
+__global__ __launch_bounds__(1024) void k_profile_finish(const double* __restrict__ part, int64_t nparts,
+                                                         double n, double* __restrict__ out) {
+  __shared__ double sE[1024], sC[1024];
+  double e = 0.0, c = 0.0;
+  for (int64_t i = threadIdx.x; i < nparts; i += 1024) {
+    e += part[2 * i];
+    c += part[2 * i + 1];
+  }
+  sE[threadIdx.x] = e;
+  sC[threadIdx.x] = c;
+  __syncthreads();
+  for (int h = 512; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      sE[threadIdx.x] += sE[threadIdx.x + h];
+      sC[threadIdx.x] += sC[threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = sE[0] / n;
+    out[1] = sC[0] / n;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Double quantization. (1) per 256-constant block: float64 pairwise tree sum
 // (4 leaves per lane, then a butterfly over the 64 lanes, which pairs
 // neighbouring subtrees level by level). (2) pairwise tree over the block
@@ -301,6 +395,28 @@ hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8
     hipLaunchKernelGGL(k_quantize_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, codes, absmax, lut);
   else
     hipLaunchKernelGGL(k_quantize_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, codes, absmax, lut);
+  return hipGetLastError();
+}
+
+size_t profile_ws_doubles(int64_t n_blocks) {
+  const int64_t per_wg = 16 * kQuantPasses;
+  return (size_t)(2 * ((n_blocks + per_wg - 1) / per_wg));
+}
+
+hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double tau, double* stats,
+                              double* ws, hipStream_t s) {
+  const int64_t per_wg = 16 * kQuantPasses;
+  const int64_t nwg = (n_blocks + per_wg - 1) / per_wg;
+  const dim3 grid((unsigned)nwg);
+  const Nf4Lut& lut = tables().lut;
+  const Nf4Levels& lv = tables().lv;
+  if (dtype == LQ_F32)
+    hipLaunchKernelGGL(k_profile_nf4<float>, grid, dim3(256), 0, s, (const float*)W, n_blocks, lut, lv, tau, ws);
+  else if (dtype == LQ_BF16)
+    hipLaunchKernelGGL(k_profile_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, lut, lv, tau, ws);
+  else
+    hipLaunchKernelGGL(k_profile_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, lut, lv, tau, ws);
+  hipLaunchKernelGGL(k_profile_finish, dim3(1), dim3(1024), 0, s, ws, nwg, (double)n_blocks * 64.0, stats);
   return hipGetLastError();
 }
 

@@ -58,6 +58,9 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* a
                                float* dq_scale, float* dq_mean, double* ws, hipStream_t s);
 size_t double_quant_ws_doubles(int64_t n_blocks);
 hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s);
+size_t profile_ws_doubles(int64_t n_blocks);
+hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double tau, double* stats,
+                              double* ws, hipStream_t s);
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* thresholds, uint8_t* codes, float* absmax,

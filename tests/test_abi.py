@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 21
     for name in names:
         assert hasattr(lq.lib, name), name
         assert name in lq.SIGNATURES, name
@@ -80,6 +80,14 @@ def test_validation_errors_without_launch(lq):
     assert L.lq_quantize_nf4(fake, 0, 4, 96, 64, fake, fake, null) == lq.LQ_ERR_SHAPE
     assert L.lq_quantize_nf4(fake, 0, 0, 64, 64, fake, fake, null) == lq.LQ_ERR_SHAPE
     assert L.lq_quantize_nf4(fake, 0, 4, 64, 32, fake, fake, null) == lq.LQ_ERR_UNSUPPORTED
+    # AQLoRA profiling pass: 2 doubles per 64 blocks of workspace
+    assert L.lq_profile_workspace(64, 4096, 64) == 2 * 64 * 8   # 4096 blocks = 64 workgroups
+    assert L.lq_profile_workspace(4, 96, 64) == 0
+    assert L.lq_profile_nf4(fake, 0, 4, 4096, 64, 0.01, fake, fake, 63, null) == lq.LQ_ERR_WORKSPACE
+    assert L.lq_profile_nf4(fake, 0, 4, 4096, 32, 0.01, fake, fake, 64, null) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_profile_nf4(fake, 0, 4, 100, 64, 0.01, fake, fake, 64, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_profile_nf4(fake, 0, 4, 4096, 64, 0.01, null, fake, 64, null) == lq.LQ_ERR_ARG
+    assert L.lq_profile_nf4(fake, 7, 4, 4096, 64, 0.01, fake, fake, 64, null) == lq.LQ_ERR_ARG
     assert L.lq_double_quant_workspace(1000, 256) >= 8 * 4
     assert L.lq_double_quant_workspace(1000, 128) == 0
     assert L.lq_double_quant(fake, 1000, 128, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_UNSUPPORTED

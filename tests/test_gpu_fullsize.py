@@ -90,6 +90,14 @@ def oracle_col_blocks(W, blocks, cp):
     return cols, nf4.dequant(packed, cpc, (N, cols.size))
 
 
+def check_profile(lq, torch, W):
+    """AQLoRA profiling pass over the whole layer against the oracle."""
+    stats = host(lq.profile_nf4(dev(torch, W)))
+    eps, s = nf4.profile(W)
+    assert stats[0] == pytest.approx(eps, rel=1e-9)
+    assert round(stats[1] * W.size) == round(s * W.size)
+
+
 def check_codec(lq, torch, W, qw, rows, cp_ref, dqp_ref, c_ref):
     N, K = W.shape
     code8, s2, mu = dqp_ref
@@ -129,6 +137,7 @@ def test_prefill_layer_full_size(lq, torch, name):
     assert np.array_equal(host(absmax).view(np.uint32), c_ref.view(np.uint32))
     rows = sample(rng, N, 192)
     wd_rows = check_codec(lq, torch, W, qw, rows, cp, dqp, c_ref)
+    check_profile(lq, torch, W)
 
     X, A, B, G = syn.activations(L), syn.lora_a(L), syn.lora_b(L), syn.grad_out(L)
     Xd, Ad, Bd, Gd = (bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits),
@@ -172,6 +181,7 @@ def test_decode_codec_full_size(lq, torch, decode_case):
     L, W, c_ref, dqp, cp, absmax, qw, rows = decode_case
     assert np.array_equal(host(absmax).view(np.uint32), c_ref.view(np.uint32))
     check_codec(lq, torch, W, qw, rows, cp, dqp, c_ref)
+    check_profile(lq, torch, W)
 
 
 @pytest.mark.parametrize("M", list(syn.DECODE_TOKENS))

@@ -327,3 +327,30 @@ def test_codebook_dequant_and_forward(lq, torch, M):
     H, t = lq.qlora_forward(qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), alpha)
     Href, _ = layer.forward(Wd, X.f32, A.f32, B.f32, alpha)
     assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# AQLoRA profiling pass
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(64, 64), (192, 320), (1000, 128), (37, 1024)])
+def test_profile_matches_oracle(lq, torch, shape):
+    """eps to float64 summation-order rounding; the small-weight count exactly."""
+    rng = np.random.default_rng(shape[0] + 3 * shape[1])
+    W = edge_weight(rng, *shape) if shape[0] * shape[1] >= 64 * 64 else \
+        (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    stats = host(lq.profile_nf4(dev(torch, W)))
+    eps, s = nf4.profile(W)
+    assert stats[0] == pytest.approx(eps, rel=1e-10, abs=1e-300)
+    assert round(stats[1] * W.size) == round(s * W.size)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_profile_half_inputs(lq, torch, dtype):
+    rng = np.random.default_rng(8)
+    W32 = (rng.standard_normal((96, 256)) * 0.02).astype(np.float32)
+    t = torch.from_numpy(W32).to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    Wexact = t.float().numpy()
+    stats = host(lq.profile_nf4(t.cuda()))
+    eps, s = nf4.profile(Wexact)
+    assert stats[0] == pytest.approx(eps, rel=1e-10)
+    assert round(stats[1] * W32.size) == round(s * W32.size)
