@@ -76,6 +76,9 @@ class Dev:
         self.aq = torch.empty(n_b, dtype=torch.uint8, device=dev)
         self.s2 = torch.empty(n_d, dtype=torch.float32, device=dev)
         self.mu = torch.empty(1, dtype=torch.float32, device=dev)
+        self.stats = torch.empty(2, dtype=torch.float64, device=dev)
+        self.prof_ws_bytes = lq.lib.lq_profile_workspace(N, K, 64)
+        self.prof_ws = torch.empty(self.prof_ws_bytes, dtype=torch.uint8, device=dev)
         self.dq_ws_bytes = lq.lib.lq_double_quant_workspace(n_b, 256)
         self.dq_ws = torch.empty(self.dq_ws_bytes, dtype=torch.uint8, device=dev)
         self.qw = lq.QWeight(N, K, self.codes, absmax_q=self.aq, dq_scale=self.s2, dq_mean=self.mu)
@@ -109,6 +112,8 @@ class Calls:
         L = d.layer
         self.alpha = float(L.alpha)
         self.args_q = (P(d.W), 0, L.N, L.K, 64, P(d.codes), P(d.absmax), self.stream)
+        self.args_prof = (P(d.W), 0, L.N, L.K, 64, ctypes.c_double(0.01), P(d.stats), P(d.prof_ws),
+                          d.prof_ws_bytes, self.stream)
         self.args_dq = (P(d.absmax), L.N * L.K // 64, 256, P(d.aq), P(d.s2), P(d.mu), P(d.dq_ws),
                         d.dq_ws_bytes, self.stream)
         self.args_deq = (d.qw.ref(), P(d.Wd), self.stream)
@@ -124,6 +129,9 @@ class Calls:
     def chk(self, st, name):
         if st != 0:
             raise RuntimeError(f"{name} failed: {st}")
+
+    def profile(self):
+        self.chk(self.lib.lq_profile_nf4(*self.args_prof), "profile")
 
     def quantize(self):
         self.chk(self.lib.lq_quantize_nf4(*self.args_q), "quantize")
@@ -208,6 +216,7 @@ def codec_bytes(L, M=0):
     packed = n // 2 + n_b + 4 * n_d + 4
     return {
         "quantize": 4 * n + n // 2 + 4 * n_b,
+        "profile": 4 * n,
         "double_quant": 4 * n_b + n_b + 4 * n_d + 4,
         "dequant": packed + 2 * n,
         "gemv": packed + 2 * L.K * M + 2 * L.r * L.K + 2 * L.N * L.r + 2 * L.N * M + 4 * M * L.r,
@@ -348,6 +357,7 @@ def main():
 
         cb = codec_bytes(L)
         rec("q_proj.quantize_nf4", time_ms(torch, [c.quantize for c in calls], 40), cb["quantize"], "GB/s")
+        rec("q_proj.profile_nf4", time_ms(torch, [c.profile for c in calls], 40), cb["profile"], "GB/s")
         rec("q_proj.double_quant", time_ms(torch, [c.double_quant for c in calls], 40), cb["double_quant"], "GB/s")
         rec("q_proj.dequant", time_ms(torch, [c.dequant for c in calls], 40), cb["dequant"], "GB/s")
         rec("q_proj.lora_down", time_ms(torch, [c.lora_down for c in calls], 40), fl["lora_down"], "TFLOP/s")
@@ -379,6 +389,7 @@ def main():
         dv = make_devs(torch, lq, syn, "decode", 1, M=16, with_grad=False)
         c0 = Calls(torch, lq, dv[0])
         rec("decode.quantize_nf4", time_ms(torch, [c0.quantize], 10), codec_bytes(Ld)["quantize"], "GB/s")
+        rec("decode.profile_nf4", time_ms(torch, [c0.profile], 10), codec_bytes(Ld)["profile"], "GB/s")
         rec("decode.double_quant", time_ms(torch, [c0.double_quant], 10), codec_bytes(Ld)["double_quant"], "GB/s")
         rec("decode.dequant", time_ms(torch, [c0.dequant], 10), codec_bytes(Ld)["dequant"], "GB/s")
         # 9 copies of the 121 MB quantized weight rotate through the GEMV

@@ -752,26 +752,49 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
   out[j * N + n] = in[i];
 }
 
-// Column form: part[split][j][c] = sum_{m in split} P[m][j] Q[m][c], MFMA
-// 32x32x16 with A = P^T (hi/lo bf16 split of float32 P) and B = Q, both
-// gathered along m from LDS. Workgroup: 128 columns, wave: 32 columns.
-__global__ __launch_bounds__(256) void k_col_skinny(const float* __restrict__ P,
-                                                    const uint16_t* __restrict__ Q, int64_t M,
-                                                    int64_t C, int r, int64_t m_per_split,
-                                                    float* __restrict__ out) {
+// Column form: out(j, c) = sum_m P[m][j] Q[m][c] for j < r, P float32 [M, r]
+// small, Q bfloat16 [M, C] streamed once. P enters as pt2 = [hi(P)^T ;
+// lo(P)^T] (bfloat16 [2r, Mp], Mp = M rounded up to 32, zero padded; hi + lo
+// carries P to about 2^-17), so an MFMA A fragment is one 16-byte load. The
+// Q tile [32 m x 128 c] goes through LDS and is gathered along m for the B
+// fragments. Workgroup: 128 columns x one m-split, wave: 32 columns,
+// MFMA 32x32x16 over the 2r product rows; hi and lo rows are added in
+// registers when r % 32 == 0 or r == 16 (partner row in the same lane),
+// otherwise both are written and the reduction adds them.
+__global__ __launch_bounds__(256) void k_split_t(const float* __restrict__ P, int64_t M, int r, int64_t Mp,
+                                                uint16_t* __restrict__ pt2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over [r][Mp]
+  if (i >= (int64_t)r * Mp) return;
+  const int64_t j = i / Mp, m = i % Mp;
+  float hi = 0.0f, lo = 0.0f;
+  if (m < M) split_bf16(P[m * r + j], hi, lo);
+  pt2[j * Mp + m] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+  pt2[(j + r) * Mp + m] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
+}
+
+template <int JT2>
+__global__ __launch_bounds__(256) void k_col_skinny(const uint16_t* __restrict__ pt2, int64_t Mp,
+                                                    const uint16_t* __restrict__ Q, int64_t M, int64_t C, int r,
+                                                    int64_t m_per_split, int combine, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * (128 + 8)];
-  __shared__ float sP[32 * (128 + 1)];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int64_t c0 = (int64_t)blockIdx.x * 128;
   const int64_t m_begin = (int64_t)blockIdx.y * m_per_split;
   const int64_t m_end = min(M, m_begin + m_per_split);
-  const int jtiles = (r + 31) / 32;
-  f32x16_t acc[4];
+  const int rows2 = 2 * r;
+  f32x16_t acc[JT2];
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
+  for (int jt = 0; jt < JT2; ++jt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jt][v] = 0.f;
+  // A-fragment rows (rows past 2r read row 0: their products are not used)
+  const uint16_t* arow[JT2];
+#pragma unroll
+  for (int jt = 0; jt < JT2; ++jt) {
+    const int j = 32 * jt + li;
+    arow[jt] = pt2 + (int64_t)(j < rows2 ? j : 0) * Mp + 8 * lh;
+  }
   for (int64_t mb = m_begin; mb < m_end; mb += 32) {
     for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
       const int row = idx / 16, cc = (idx % 16) * 8;
@@ -789,11 +812,12 @@ __global__ __launch_bounds__(256) void k_col_skinny(const float* __restrict__ P,
       }
       *reinterpret_cast<u32x4_t*>(sQ + row * (128 + 8) + cc) = v;
     }
-    for (int idx = threadIdx.x; idx < 32 * r; idx += 256) {
-      const int row = idx / r, j = idx % r;
-      const int64_t m = mb + row;
-      sP[row * (128 + 1) + j] = (m < m_end) ? P[m * r + j] : 0.f;
-    }
+    // pt2 is zero past M (padding) and rows of Q past m_end are zero in LDS
+    u32x4_t af[2][JT2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int jt = 0; jt < JT2; ++jt) af[s][jt] = ld16(arow[jt] + mb + 16 * s);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -806,52 +830,57 @@ __global__ __launch_bounds__(256) void k_col_skinny(const float* __restrict__ P,
         bv[e] = lo | (hi << 16);
       }
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt < jtiles) {
-          const int j = 32 * jt + li;
-          float vh[8], vl[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = (j < r) ? sP[(16 * s + 8 * lh + e) * (128 + 1) + j] : 0.f;
-            split_bf16(x, vh[e], vl[e]);
-          }
-          u32x4_t ah, al;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ah[e] = pack_bf16x2(vh[2 * e], vh[2 * e + 1]);
-            al[e] = pack_bf16x2(vl[2 * e], vl[2 * e + 1]);
-          }
-          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ah), as_bf16x8(bv), acc[jt], 0, 0, 0);
-          acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al), as_bf16x8(bv), acc[jt], 0, 0, 0);
-        }
-      }
+      for (int jt = 0; jt < JT2; ++jt)
+        acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[s][jt]), as_bf16x8(bv), acc[jt], 0, 0, 0);
     }
     __syncthreads();
   }
-  float* dst = out + (int64_t)blockIdx.y * r * C;
   const int64_t c = c0 + 32 * wave + li;
   if (c >= C) return;
+  if (combine) {
+    // partner row j + r: tile jt + r/32 (r % 32 == 0) or v + 8 of the same tile (r == 16)
+    float* dst = out + (int64_t)blockIdx.y * r * C;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    if (jt >= jtiles) continue;
+    for (int jt = 0; jt < JT2; ++jt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
-      if (j < r) dst[(int64_t)j * C + c] = acc[jt][v];
-    }
+      for (int v = 0; v < 16; ++v) {
+        const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (j >= r) continue;
+        float partner = 0.0f;
+        if (r == 16) partner = acc[jt][(v + 8) & 15];
+#pragma unroll
+        for (int pt = 0; pt < JT2; ++pt)
+          if (r % 32 == 0 && pt == jt + r / 32) partner = acc[pt][v];
+        dst[(int64_t)j * C + c] = acc[jt][v] + partner;
+      }
+  } else {
+    float* dst = out + (int64_t)blockIdx.y * rows2 * C;
+#pragma unroll
+    for (int jt = 0; jt < JT2; ++jt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
+        if (j < rows2) dst[(int64_t)j * C + c] = acc[jt][v];
+      }
   }
 }
 
-// out[i] = scale * sum_{s < splits} part[s][i] (fixed order); optional
-// transposed write for [rows, cols] -> [cols, rows].
+// out[i] = scale * sum_{s < splits} (part[s][i] + part[s][i + pair]) in a
+// fixed order, where part[s] holds `srows` rows of `cols` and pair is 0 or
+// the offset of a partner row block (hi + lo halves); optional transposed
+// write for [rows, cols] -> [cols, rows].
 __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int splits,
                                                        int64_t rows, int64_t cols, float scale,
-                                                       float* __restrict__ out, int transposed) {
+                                                       float* __restrict__ out, int transposed,
+                                                       int64_t srows, int64_t pair) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = rows * cols;
+  const int64_t n = rows * cols, sn = srows * cols;
   if (i >= n) return;
-  float acc = part[i];
-  for (int s = 1; s < splits; ++s) acc += part[(int64_t)s * n + i];
+  float acc = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = part + (int64_t)s * sn + i;
+    acc += pair ? ps[0] + ps[pair] : ps[0];
+  }
   acc *= scale;
   if (transposed) {
     const int64_t rr = i / cols, cc = i % cols;
@@ -904,7 +933,7 @@ hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint
   if (e != hipSuccess || real_splits == 1) return e;
   const int64_t n = M * r;
   hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws,
-                     real_splits, M, (int64_t)r, 1.0f, out, 0);
+                     real_splits, M, (int64_t)r, 1.0f, out, 0, M, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -914,8 +943,10 @@ hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* 
   return hipGetLastError();
 }
 
+// workspace: partial sums [splits][2r][C] floats, then pt2 [2r][Mp] bf16
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r) {
-  return (size_t)col_skinny_splits(M, C) * r * C;
+  const int64_t Mp = (M + 31) / 32 * 32;
+  return (size_t)col_skinny_splits(M, C) * 2 * r * C + (size_t)(2 * r * Mp + 1) / 2;
 }
 
 hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
@@ -925,13 +956,26 @@ hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64
   const int64_t mchunks = (M + 31) / 32;
   const int64_t m_per_split = ((mchunks + splits - 1) / splits) * 32;
   const int real_splits = (int)((M + m_per_split - 1) / m_per_split);
+  const int64_t Mp = mchunks * 32;
+  float* part = ws;
+  uint16_t* pt2 = reinterpret_cast<uint16_t*>(ws + (size_t)splits * 2 * r * C);
+  hipLaunchKernelGGL(k_split_t, dim3((unsigned)(((int64_t)r * Mp + 255) / 256)), dim3(256), 0, s, P, M, r, Mp,
+                     pt2);
+  const int combine = (r % 32 == 0 || r == 16) ? 1 : 0;
   const dim3 grid((unsigned)((C + 127) / 128), (unsigned)real_splits);
-  hipLaunchKernelGGL(k_col_skinny, grid, dim3(256), 0, s, P, Q, M, C, r, m_per_split, ws);
+  switch ((2 * r + 31) / 32) {
+#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, pt2, Mp, Q, M, C, r, m_per_split, combine, part); break;
+    LQ_CS(1) LQ_CS(2) LQ_CS(3) LQ_CS(4) LQ_CS(5) LQ_CS(6) LQ_CS(7) LQ_CS(8)
+#undef LQ_CS
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)r * C;
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws,
-                     real_splits, (int64_t)r, C, scale, out, out_transposed ? 1 : 0);
+  const int64_t srows = combine ? r : 2 * r;
+  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
+                     real_splits, (int64_t)r, C, scale, out, out_transposed ? 1 : 0, srows,
+                     combine ? (int64_t)0 : (int64_t)r * C);
   return hipGetLastError();
 }
 
