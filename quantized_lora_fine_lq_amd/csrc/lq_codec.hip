@@ -11,6 +11,9 @@
 // groups of 64 scaled by absmax.
 #include <float.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "lq_device.h"
 
 namespace lq {
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W,
 // ---------------------------------------------------------------------------
 template <typename Tin>
 __global__ __launch_bounds__(256) void k_profile_nf4(const Tin* __restrict__ W, int64_t n_blocks, Nf4Lut lut,
-                                                     Nf4Levels lv, double tau, double* __restrict__ part) {
+                                                     Nf4Levels lv, float tau_le, double* __restrict__ part) {
   __shared__ float sT[33];
   __shared__ int32_t sB[33];
   __shared__ float sQ[16];
@@ -124,43 +127,50 @@ __global__ __launch_bounds__(256) void k_profile_nf4(const Tin* __restrict__ W, 
   if (threadIdx.x < 16) sQ[threadIdx.x] = lv.q[threadIdx.x];
   __syncthreads();
   const int i16 = threadIdx.x & 15;
-  const int64_t blk0 = (int64_t)blockIdx.x * (16 * kQuantPasses) + (threadIdx.x >> 4);
-  f32x4_t v[kQuantPasses];
+  const int64_t per_tile = 16 * kQuantPasses;
+  const int64_t n_tiles = (n_blocks + per_tile - 1) / per_tile;
+  double err = 0.0;
+  uint32_t cnt = 0;
+  // grid-stride over tiles of 64 blocks (fixed order for a given shape)
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int64_t blk0 = tile * per_tile + (threadIdx.x >> 4);
+    f32x4_t v[kQuantPasses];
 #pragma unroll
-  for (int p = 0; p < kQuantPasses; ++p) {
-    const int64_t blk = blk0 + 16 * p;
-    v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  double err = 0.0, cnt = 0.0;
+    for (int p = 0; p < kQuantPasses; ++p) {
+      const int64_t blk = blk0 + 16 * p;
+      v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-  for (int p = 0; p < kQuantPasses; ++p) {
-    const int64_t blk = blk0 + 16 * p;
-    float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
-    m = row16_max(m);
-    const bool fast_ok = (m >= FLT_MIN) && (m <= 0x1p125f);
-    const float r = fast_ok ? 1.0f / m : 0.0f;
-    if (blk < n_blocks) {
-      const float w4[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+    for (int p = 0; p < kQuantPasses; ++p) {
+      const int64_t blk = blk0 + 16 * p;
+      float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+      m = row16_max(m);
+      const bool fast_ok = (m >= FLT_MIN) && (m <= 0x1p125f);
+      const float r = fast_ok ? 1.0f / m : 0.0f;
+      if (blk < n_blocks) {
+        const float w4[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t code = nf4_code(w4[e], m, r, fast_ok, sT, sB);
-        const float rec = sQ[code] * m;
-        const double d = (double)w4[e] - (double)rec;
-        err = __builtin_fma(d, d, err);
-        cnt += (fabs((double)w4[e]) < tau) ? 1.0 : 0.0;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t code = nf4_code(w4[e], m, r, fast_ok, sT, sB);
+          const float rec = sQ[code] * m;
+          const double d = (double)w4[e] - (double)rec;   // exact
+          err = __builtin_fma(d, d, err);
+          cnt += (fabsf(w4[e]) <= tau_le) ? 1u : 0u;
+        }
       }
     }
   }
   // fixed-order reductions: butterfly inside the wave, then the 4 waves in order
+  double c = (double)cnt;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     err += __shfl_xor(err, off);
-    cnt += __shfl_xor(cnt, off);
+    c += __shfl_xor(c, off);
   }
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sW[0][wave] = err;
-    sW[1][wave] = cnt;
+    sW[1][wave] = c;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -398,24 +408,29 @@ hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8
   return hipGetLastError();
 }
 
-size_t profile_ws_doubles(int64_t n_blocks) {
-  const int64_t per_wg = 16 * kQuantPasses;
-  return (size_t)(2 * ((n_blocks + per_wg - 1) / per_wg));
+static int64_t profile_grid(int64_t n_blocks) {
+  const int64_t per_tile = 16 * kQuantPasses;
+  const int64_t n_tiles = (n_blocks + per_tile - 1) / per_tile;
+  return std::min<int64_t>(n_tiles, 2048);   // 8 workgroups of 4 waves per CU
 }
+
+size_t profile_ws_doubles(int64_t n_blocks) { return (size_t)(2 * profile_grid(n_blocks)); }
 
 hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double tau, double* stats,
                               double* ws, hipStream_t s) {
-  const int64_t per_wg = 16 * kQuantPasses;
-  const int64_t nwg = (n_blocks + per_wg - 1) / per_wg;
+  const int64_t nwg = profile_grid(n_blocks);
   const dim3 grid((unsigned)nwg);
   const Nf4Lut& lut = tables().lut;
   const Nf4Levels& lv = tables().lv;
+  // |w| < tau for a float32 |w|  <=>  |w| <= the largest float32 below tau
+  float tau_le = (float)tau;
+  if ((double)tau_le >= tau) tau_le = std::nextafter(tau_le, 0.0f);
   if (dtype == LQ_F32)
-    hipLaunchKernelGGL(k_profile_nf4<float>, grid, dim3(256), 0, s, (const float*)W, n_blocks, lut, lv, tau, ws);
+    hipLaunchKernelGGL(k_profile_nf4<float>, grid, dim3(256), 0, s, (const float*)W, n_blocks, lut, lv, tau_le, ws);
   else if (dtype == LQ_BF16)
-    hipLaunchKernelGGL(k_profile_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, lut, lv, tau, ws);
+    hipLaunchKernelGGL(k_profile_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, lut, lv, tau_le, ws);
   else
-    hipLaunchKernelGGL(k_profile_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, lut, lv, tau, ws);
+    hipLaunchKernelGGL(k_profile_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, lut, lv, tau_le, ws);
   hipLaunchKernelGGL(k_profile_finish, dim3(1), dim3(1024), 0, s, ws, nwg, (double)n_blocks * 64.0, stats);
   return hipGetLastError();
 }
