@@ -223,6 +223,21 @@ def codec_bytes(L, M=0):
     }
 
 
+def lowra_bytes(syn, L):
+    """Algorithmic bytes of the per-channel codebook kernels: the learner reads
+    W and writes levels, thresholds and iteration counts; the quantizer reads
+    W, the widths, offsets and thresholds and writes the bit planes and the
+    block constants."""
+    import numpy as np
+    n = L.N * L.K
+    bits = syn.lowra_row_bits(L).astype(np.int64)
+    planes = int(np.sum(L.K * bits // 8))
+    return {
+        "lloyd": 4 * n + L.N + L.N * (16 + 15 + 1) * 4,
+        "quantize": 4 * n + L.N + 8 * (L.N + 1) + L.N * 15 * 4 + planes + 4 * (n // 64),
+    }
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "dq_gemm_fwd_q_proj_traffic.md")
 TRAFFIC_SOURCES = ("quantized_lora_fine_lq_amd/csrc/lq_gemm.hip", "quantized_lora_fine_lq_amd/csrc/lq_device.h")
 
@@ -383,6 +398,47 @@ def main():
             rec(f"{name}.backward", time_ms(torch, [c.backward for c in cs], 10), flm["bwd"], "TFLOP/s")
             del cs, dv
             torch.cuda.empty_cache()
+
+        # ---- per-channel codebook layer (LowRA): learner, quantizer, GEMM ----
+        log("generating lowra inputs")
+        Ll = syn.LAYERS["lowra"]
+        lb = lowra_bytes(syn, Ll)
+        Wl = torch.from_numpy(syn.weight(Ll)).cuda()
+        bits_h = syn.lowra_row_bits(Ll)
+        bl = torch.from_numpy(bits_h).cuda()
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        lv = torch.empty(Ll.N, 16, dtype=torch.float32, device="cuda")
+        th = torch.empty(Ll.N, 15, dtype=torch.float32, device="cuda")
+        its = torch.empty(Ll.N, dtype=torch.int32, device="cuda")
+
+        def lloyd():
+            if lq.lib.lq_lloyd_codebooks(P(Wl), 0, Ll.N, Ll.K, 64, P(bl), 100, P(lv), P(th), P(its), st) != 0:
+                raise RuntimeError("lq_lloyd_codebooks failed")
+        rec("lowra.lloyd_codebooks", time_ms(torch, [lloyd], 5, warmup=1), lb["lloyd"], "GB/s")
+        kernels["lowra.lloyd_codebooks"]["iterations_mean"] = round(its.float().mean().item(), 2)
+        kernels["lowra.lloyd_codebooks"]["iterations_max"] = int(its.max().item())
+        offs = lq.row_offsets(bits_h.tolist(), Ll.K)
+        roff = torch.tensor(offs, dtype=torch.int64, device="cuda")
+        cc = torch.empty(offs[-1], dtype=torch.uint8, device="cuda")
+        am = torch.empty(Ll.N * Ll.K // 64, dtype=torch.float32, device="cuda")
+
+        def cb_quant():
+            if lq.lib.lq_quantize_codebook(P(Wl), 0, Ll.N, Ll.K, 64, P(bl), P(roff), P(th), P(cc), P(am), st) != 0:
+                raise RuntimeError("lq_quantize_codebook failed")
+        rec("lowra.quantize_codebook", time_ms(torch, [cb_quant], 20), lb["quantize"], "GB/s")
+        qwl = lq.QWeight.from_codebook(Wl, bl, th, lv)
+        Xl, Al, Bl = syn.activations(Ll), syn.lora_a(Ll), syn.lora_b(Ll)
+        bfd = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+        Xd, Ad, Bd = bfd(Xl.bits), bfd(Al.bits), bfd(Bl.bits)
+        tl = torch.empty(Ll.M, Ll.r, dtype=torch.float32, device="cuda")
+        lq.lora_down(Xd, Ad, tl)
+        Hl = torch.empty(Ll.M, Ll.N, dtype=torch.bfloat16, device="cuda")
+        flw = layer_flops(Ll, Ll.M)
+        rec("lowra.dequant_gemm_fwd", time_ms(torch, [lambda: lq.dequant_gemm(qwl, Xd, tl, Bd, Ll.alpha, out=Hl)], 20),
+            flw["fwd_gemm"], "TFLOP/s")
+        del Wl, qwl, Xd, Hl, cc
+        torch.cuda.empty_cache()
 
         log("generating decode inputs")
         Ld = syn.LAYERS["decode"]

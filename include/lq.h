@@ -307,6 +307,47 @@ int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int
                          const uint8_t* row_bits, const int64_t* row_offset,
                          const float* thresholds, uint8_t* codes, float* absmax, void* stream);
 
+/* Limits of lq_lloyd_codebooks: row length (one row is sorted in the LDS of
+ * one workgroup) and iteration count. */
+#define LQ_LLOYD_MAX_K 16384
+#define LQ_LLOYD_MAX_ITERS_LIMIT 100000
+
+/*
+ * Weighted Lloyd-Max learner for per-output-channel codebooks ([LowRA]
+ * section 5, mapping and threshold learner), for use with
+ * lq_quantize_codebook. For each row i of W [N, K] with b = row_bits[i] in
+ * {1, 2, 3, 4} (values outside are clamped into that range):
+ *   data x = w / c (float32, exactly as lq_quantize_nf4 normalises), weight c
+ *   (the absmax of the element's 64-block);
+ *   start: thresholds = midpoints of the NormalFloat levels of width b (2^(b-1)
+ *   + 1 normal quantiles on the positive half, 2^(b-1) on the negative half,
+ *   equal probability steps up to delta_b = 1 - (1/(2 * 2^b) + 1/(2 (2^b - 1)))/2,
+ *   the shared 0 once; {-1, +1} at b = 1), levels = those NormalFloat levels;
+ *   iteration: code = number of thresholds below x; level j = sum(c x)/sum(c)
+ *   over code j (an empty code keeps its level); error = sum(c (x - level)^2)
+ *   / sum(c); thresholds = midpoints of adjacent levels;
+ *   stop after max_iters iterations or after the first iteration whose error
+ *   is not below the previous one; the last computed levels are the result.
+ * All learner arithmetic is float64; the interval sums are formed in a fixed
+ * order, so results repeat exactly run to run.
+ *   W           [N, K] of dtype (LQ_F32, LQ_BF16, LQ_F16; widened exactly)
+ *   row_bits    [N] uint8, device
+ *   max_iters   1 .. LQ_LLOYD_MAX_ITERS_LIMIT (100 in the method)
+ *   levels      [N, 16] float32, written: the first 2^b are the levels rounded
+ *               to nearest float32, the rest repeat the last one
+ *   thresholds  [N, 15] float32, written: the first 2^b - 1 are the largest
+ *               float32 not above the midpoint of adjacent float32 levels
+ *               (so lq_quantize_codebook maps x to its nearest level, ties
+ *               to the lower one), the rest 3.0
+ *   iterations  [N] int32, written (may be NULL): iterations computed per row
+ * Errors: LQ_ERR_ARG (null pointer, bad dtype, max_iters out of range),
+ * LQ_ERR_SHAPE (N, K <= 0, K % 64 != 0, N > 2^31 - 1), LQ_ERR_UNSUPPORTED
+ * (blocksize != 64, K > LQ_LLOYD_MAX_K), LQ_ERR_LAUNCH.
+ */
+int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                       const uint8_t* row_bits, int32_t max_iters, float* levels,
+                       float* thresholds, int32_t* iterations, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

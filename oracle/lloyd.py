@@ -72,7 +72,8 @@ def centroids(x, w, code, L_prev):
 
 def weighted_mse(x, w, code, L):
     rec = np.take_along_axis(L, code, axis=1)
-    return np.sum(w * (x - rec) ** 2, axis=1) / np.sum(w, axis=1)
+    with np.errstate(invalid="ignore"):   # a row of zero weights gives 0/0 = NaN
+        return np.sum(w * (x - rec) ** 2, axis=1) / np.sum(w, axis=1)
 
 
 def lloyd_step(x, w, T, L_prev):
@@ -113,11 +114,12 @@ def learn(x, w, bits: int, max_iters: int = MAX_ITERS, history: list = None):
 
 
 def learn_codebooks(W: np.ndarray, row_bits: np.ndarray, block: int = 64,
-                    max_iters: int = MAX_ITERS):
+                    max_iters: int = MAX_ITERS, return_iters: bool = False):
     """Per-row codebooks for W [N, K]. Returns (levels float32 [N, 16],
-    thresholds float32 [N, 15]). A row with b bits uses the first 2^b levels
-    and 2^b - 1 thresholds; the unused level slots repeat the last level and
-    the unused threshold slots hold 3.0 (above every normalised value)."""
+    thresholds float32 [N, 15]), plus the iterations computed per row when
+    return_iters is set. A row with b bits uses the first 2^b levels and
+    2^b - 1 thresholds; the unused level slots repeat the last level and the
+    unused threshold slots hold 3.0 (above every normalised value)."""
     W = np.asarray(W, dtype=np.float32)
     N, K = W.shape
     c = block_absmax(W, block)
@@ -125,15 +127,19 @@ def learn_codebooks(W: np.ndarray, row_bits: np.ndarray, block: int = 64,
     wgt = np.repeat(c.astype(np.float64), block).reshape(N, K)
     levels = np.zeros((N, 16), dtype=np.float32)
     thresh = np.full((N, 15), 3.0, dtype=np.float32)
+    iters = np.zeros(N, dtype=np.int64)
     row_bits = np.asarray(row_bits)
     for b in np.unique(row_bits):
         b = int(b)
         rows = np.nonzero(row_bits == b)[0]
-        L, _, _ = learn(x[rows], wgt[rows], b, max_iters)
+        L, _, it = learn(x[rows], wgt[rows], b, max_iters)
+        iters[rows] = it
         L32 = L.astype(np.float32)
         n = 1 << b
         levels[rows, :n] = L32
         levels[rows, n:] = L32[:, -1:]
         for j, i in enumerate(rows):
             thresh[i, :n - 1] = midpoint_thresholds(L32[j])
+    if return_iters:
+        return levels, thresh, iters
     return levels, thresh

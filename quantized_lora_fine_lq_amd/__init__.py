@@ -68,6 +68,8 @@ SIGNATURES = {
                                          c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_quantize_codebook": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
                                             c_vp, c_vp, c_vp]),
+    "lq_lloyd_codebooks": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
+                                          c_vp, c_vp]),
     "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "lq_dequant_gemm_workspace": (c_sz, [QW_P, c_i64, c_i32]),
@@ -319,6 +321,21 @@ def row_offsets(row_bits_host, K: int):
     for b in row_bits_host:
         off.append(off[-1] + K * int(b) // 8)
     return off
+
+
+def lloyd_codebooks(W, row_bits, max_iters: int = 100, blocksize: int = 64):
+    """Per-row weighted Lloyd-Max codebooks for W [N, K] (device) with
+    row_bits uint8 [N] (device) -> (levels f32 [N, 16], thresholds f32 [N, 15],
+    iterations int32 [N]), ready for quantize_codebook / QWeight.from_codebook."""
+    torch = _torch()
+    N, K = W.shape
+    levels = torch.empty(N, 16, dtype=torch.float32, device=W.device)
+    thresholds = torch.empty(N, 15, dtype=torch.float32, device=W.device)
+    iters = torch.empty(N, dtype=torch.int32, device=W.device)
+    _check(lib.lq_lloyd_codebooks(_ptr(W), _dtype_code(W), N, K, blocksize, _ptr(row_bits), int(max_iters),
+                                  _ptr(levels), _ptr(thresholds), _ptr(iters), _stream(W.device)),
+           "lq_lloyd_codebooks")
+    return levels, thresholds, iters
 
 
 def quantize_codebook(W, row_bits, thresholds, blocksize: int = 64):

@@ -315,4 +315,15 @@ int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int
                                                 codes, absmax, (hipStream_t)stream));
 }
 
+int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
+                       const uint8_t* row_bits, int32_t max_iters, float* levels,
+                       float* thresholds, int32_t* iterations, void* stream) {
+  if (!W || !row_bits || !levels || !thresholds || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (max_iters < 1 || max_iters > LQ_LLOYD_MAX_ITERS_LIMIT) return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N > INT32_MAX) return LQ_ERR_SHAPE;
+  if (blocksize != 64 || K > LQ_LLOYD_MAX_K) return LQ_ERR_UNSUPPORTED;
+  return launch_status(launch_lloyd(W, dtype, N, K, row_bits, max_iters, levels, thresholds,
+                                    iterations, (hipStream_t)stream));
+}
+
 }  // extern "C"

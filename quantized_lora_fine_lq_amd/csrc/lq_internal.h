@@ -40,6 +40,16 @@ struct Tables {
 };
 const Tables& tables();
 
+// Starting point of the weighted Lloyd-Max learner for widths b = 1..4
+// (index b - 1), float64: the NormalFloat levels of width b (2^(b-1) + 1
+// quantiles on the positive half, 2^(b-1) on the negative half, the shared 0
+// once; {-1, +1} at b = 1) and the midpoints of adjacent levels.
+struct LloydInit {
+  double L[4][16];
+  double T[4][15];
+};
+const LloydInit& lloyd_init();
+
 // Quantized-weight view used by the kernels.
 struct QWeight {
   int32_t format;
@@ -61,6 +71,9 @@ hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s);
 size_t profile_ws_doubles(int64_t n_blocks);
 hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double tau, double* stats,
                               double* ws, hipStream_t s);
+hipError_t launch_lloyd(const void* W, int dtype, int64_t N, int64_t K, const uint8_t* row_bits,
+                        int max_iters, float* levels, float* thresholds, int32_t* iterations,
+                        hipStream_t s);
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* thresholds, uint8_t* codes, float* absmax,

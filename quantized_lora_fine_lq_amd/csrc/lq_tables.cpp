@@ -91,7 +91,52 @@ Tables build() {
   return t;
 }
 
+// NormalFloat levels of width b in float64, ascending in [-1, 1]: with
+// h = 2^(b-1) and delta_b = 1 - (1/(2 * 2^b) + 1/(2 * (2^b - 1)))/2 (delta_4 is
+// NF4's), h + 1 quantiles at probabilities 1/2 .. delta_b in equal steps on the
+// positive half and h on the negative half, divided by Phi^-1(delta_b), the
+// shared 0 kept once. Width 1 is {-1, +1}. These start the per-channel
+// learner (LowRA, section 5: NormalFloat thresholds at 2 and 4 bits, 0 at 1
+// bit; width 3 and delta_b for widths below 4 are not given there).
+void nf_levels_f64(int bits, double* out) {
+  if (bits == 1) {
+    out[0] = -1.0;
+    out[1] = 1.0;
+    return;
+  }
+  const int n = 1 << bits, half = n / 2;
+  const double delta = 1.0 - 0.5 * (1.0 / (2.0 * n) + 1.0 / (2.0 * (n - 1)));
+  const double scale = normal_quantile_upper(delta);
+  int c = 0;
+  out[c++] = 0.0;
+  for (int j = 1; j <= half; ++j)
+    out[c++] = normal_quantile_upper(0.5 + (delta - 0.5) * ((double)j / (double)half)) / scale;
+  for (int j = 1; j <= half - 1; ++j)
+    out[c++] = -normal_quantile_upper(0.5 + (delta - 0.5) * ((double)j / (double)(half - 1))) / scale;
+  for (int i = 1; i < n; ++i)
+    for (int k = i; k > 0 && out[k] < out[k - 1]; --k) {
+      const double tmp = out[k]; out[k] = out[k - 1]; out[k - 1] = tmp;
+    }
+}
+
+LloydInit build_lloyd_init() {
+  LloydInit li{};
+  for (int b = 1; b <= 4; ++b) {
+    const int n = 1 << b;
+    nf_levels_f64(b, li.L[b - 1]);
+    for (int i = 0; i + 1 < n; ++i) li.T[b - 1][i] = (li.L[b - 1][i] + li.L[b - 1][i + 1]) / 2.0;
+  }
+  return li;
+}
+
 }  // namespace
+
+const LloydInit& lloyd_init() {
+  static LloydInit li;
+  static std::once_flag once;
+  std::call_once(once, [] { li = build_lloyd_init(); });
+  return li;
+}
 
 const Tables& tables() {
   static Tables t;

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 21
+    assert len(names) == 22
     for name in names:
         assert hasattr(lq.lib, name), name
         assert name in lq.SIGNATURES, name
@@ -167,6 +167,23 @@ def test_validation_errors_without_launch(lq):
     assert L.lq_quantize_codebook(fake, 0, 4, 64, 64, null, fake, fake, fake, fake, null) == lq.LQ_ERR_ARG
     assert L.lq_quantize_codebook(fake, 0, 4, 60, 64, fake, fake, fake, fake, fake, null) == lq.LQ_ERR_SHAPE
     assert L.lq_quantize_codebook(fake, 0, 4, 64, 16, fake, fake, fake, fake, fake, null) == lq.LQ_ERR_UNSUPPORTED
+
+    largs = [fake, 0, 4, 64, 64, fake, 100, fake, fake, null, null]   # iterations may be NULL
+    for pos in (0, 5, 7, 8):
+        a = list(largs); a[pos] = null
+        assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_ARG
+    for it in (0, -1, 100001):
+        a = list(largs); a[6] = it
+        assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_ARG
+    a = list(largs); a[1] = 7
+    assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_ARG
+    for n, k in ((0, 64), (4, 0), (4, 96), (1 << 31, 64)):
+        a = list(largs); a[2] = n; a[3] = k
+        assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_SHAPE
+    a = list(largs); a[4] = 32
+    assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_UNSUPPORTED
+    a = list(largs); a[3] = 16384 + 64
+    assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_UNSUPPORTED
 
 
 def test_workspace_queries_deterministic(lq):

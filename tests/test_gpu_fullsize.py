@@ -200,26 +200,33 @@ def test_decode_gemv_full_size(lq, torch, decode_case, M):
 
 
 def test_codebook_layer_full_size(lq, torch):
-    """1.75-bit per-channel layer: NF-initial tables per row width (any valid
-    strictly increasing tables exercise the same kernels)."""
+    """1.75-bit per-channel layer with its tables learned on the GPU by the
+    weighted Lloyd-Max learner (checked against the oracle's learner on
+    sampled rows), then quantized, dequantized and run forward."""
     L = syn.LAYERS["lowra"]
     N, K, M, r, alpha = L.N, L.K, L.M, L.r, L.alpha
     W = syn.weight(L)
     bits = syn.lowra_row_bits(L)
-    T = np.full((N, 15), 0, dtype=np.float32)
-    Lv = np.zeros((N, 16), dtype=np.float32)
-    for b in (1, 2, 3, 4):
-        sel = bits == b
-        nb = 1 << b
-        T[sel, :nb - 1] = lloyd.init_thresholds(b).astype(np.float32)
-        Lv[sel, :nb] = lloyd.init_levels(b).astype(np.float32)
-    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    Wdev = dev(torch, W)
+    Lg, Tg, itg = lq.lloyd_codebooks(Wdev, dev(torch, bits))
+    Lv, T, it = host(Lg), host(Tg), host(itg)
+    rng = np.random.default_rng(5)
+    rows = sample(rng, N, 192)
+    Lr, Tr, itr = lloyd.learn_codebooks(W[rows], bits[rows], return_iters=True)
+    assert np.array_equal(it[rows], itr)
+    Lo = Lv[rows]
+    assert np.all((Lo == Lr) | (Lo == np.nextafter(Lr, np.float32(np.inf)))
+                  | (Lo == np.nextafter(Lr, np.float32(-np.inf))))
+    assert np.mean(np.all(Lo == Lr, axis=1)) >= 0.99
+    for i in rows:
+        n = 1 << int(bits[i])
+        assert np.array_equal(T[i, :n - 1].view(np.uint32),
+                              nf4.midpoint_thresholds(Lv[i, :n]).view(np.uint32))
+    qw = lq.QWeight.from_codebook(Wdev, dev(torch, bits), Tg, Lg)
     c_ref, (code8, s2, mu), cp = oracle_constants(W)
     assert np.array_equal(host(qw.absmax_q), code8)
     assert np.array_equal(host(qw.dq_scale).view(np.uint32), s2.view(np.uint32))
 
-    rng = np.random.default_rng(5)
-    rows = sample(rng, N, 192)
     packed, _, _ = codebook.quantize(W[rows], bits[rows], T[rows])
     off_full = codebook.row_offsets(bits, K)
     off_sub = codebook.row_offsets(bits[rows], K)
