@@ -46,6 +46,11 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float((s & 0x80000000u) ? (s & 0x7FFFFFFFu) : ~s);
 }
 
+// LDS slot of sorted position p: the low 4 bits are XORed with bits 4..7, so
+// that 64 lanes reading 16 consecutive keys each (lane stride 128 bytes) hit
+// distinct banks; the slot stays inside p's aligned group of 16.
+__device__ __forceinline__ int kslot(int p) { return p ^ ((p >> 4) & 15); }
+
 __device__ __forceinline__ void cmp_swap(uint64_t& a, uint64_t& b, bool ascending) {
   const uint64_t lo = a < b ? a : b;
   const uint64_t hi = a < b ? b : a;
@@ -55,7 +60,8 @@ __device__ __forceinline__ void cmp_swap(uint64_t& a, uint64_t& b, bool ascendin
 
 // G consecutive substages (strides j, j/2, ..., j >> (G-1), all >= 16) of the
 // bitonic stage `size`, on sets of 2^G keys that these substages only ever
-// compare among themselves; each thread takes 16 keys (16 >> G sets).
+// compare among themselves; each thread takes 16 keys (16 >> G sets). Keys
+// of sorted position p live in LDS slot kslot(p).
 template <int G, int NT>
 __device__ __forceinline__ void bitonic_group(uint64_t* s, int lj, int size, int t) {
   constexpr int E = 1 << G;
@@ -68,40 +74,47 @@ __device__ __forceinline__ void bitonic_group(uint64_t* s, int lj, int size, int
     const bool asc = (base & size) == 0;
     uint64_t v[E];
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = s[base + (m << lb)];
+    for (int m = 0; m < E; ++m) v[m] = s[kslot(base + (m << lb))];
 #pragma unroll
     for (int st = G - 1; st >= 0; --st)
 #pragma unroll
       for (int m = 0; m < E; ++m)
         if (!(m & (1 << st))) cmp_swap(v[m], v[m | (1 << st)], asc);
 #pragma unroll
-    for (int m = 0; m < E; ++m) s[base + (m << lb)] = v[m];
+    for (int m = 0; m < E; ++m) s[kslot(base + (m << lb))] = v[m];
   }
 }
 
-// Number of sorted values <= T, for the 16 lanes of one row group (e = lane
-// within the group, gmask = the group's lanes). Every lane of the group must
-// be active; the result is uniform over the group.
+// Numbers of sorted values <= Ta and <= Tb, for the 16 lanes of one row group
+// (e = lane within the group, gmask = the group's lanes); every lane of the
+// group must be active and the results are uniform over the group. A 16-ary
+// search over the segment maxima (rounds fixed by NT, the two searches side
+// by side), then a vote inside the segment found.
+// Invariant per search: segments below lo end <= T; segments from lo + len
+// on end > T or do not exist.
 template <int NT>
-__device__ __forceinline__ int sorted_position(float T, const float* sLast, const uint64_t* sKey,
-                                               int e, uint64_t gmask) {
-  // invariant: segments below lo end <= T; segments from lo + len on end > T
-  int lo = 0, len = NT;
-  while (true) {
+__device__ __forceinline__ void sorted_positions(float Ta, float Tb, const float* sLast,
+                                                 const uint64_t* sKey, int e, uint64_t gmask,
+                                                 int& pa, int& pb) {
+  int la = 0, lb = 0;
+#pragma unroll
+  for (int len = NT; len > 1;) {
     const int n = len < 16 ? len : 16;
     const int sub = len / n;
-    const bool pred = (e < n) && (sLast[lo + (e + 1) * sub - 1] <= T);
-    const int c = __popcll(__ballot(pred) & gmask);
-    lo += c * sub;
-    if (sub == 1 || c == n) break;
+    const int ia = la + (e + 1) * sub - 1;
+    const int ib = lb + (e + 1) * sub - 1;
+    const float va = sLast[ia < NT ? ia : NT - 1];
+    const float vb = sLast[ib < NT ? ib : NT - 1];
+    const bool qa = (e < n) && (ia < NT) && (va <= Ta);
+    const bool qb = (e < n) && (ib < NT) && (vb <= Tb);
+    la += __popcll(__ballot(qa) & gmask) * sub;
+    lb += __popcll(__ballot(qb) & gmask) * sub;
     len = sub;
   }
-  int p = lo * 16;
-  if (lo < NT) {
-    const float x = key_value(sKey[lo * 16 + e]);
-    p += __popcll(__ballot(x <= T) & gmask);
-  }
-  return p;
+  const float xa = key_value(sKey[kslot(min(la, NT - 1) * 16 + e)]);
+  const float xb = key_value(sKey[kslot(min(lb, NT - 1) * 16 + e)]);
+  pa = la * 16 + ((la < NT) ? __popcll(__ballot(xa <= Ta) & gmask) : 0);
+  pb = lb * 16 + ((lb < NT) ? __popcll(__ballot(xb <= Tb) & gmask) : 0);
 }
 
 template <typename Tin> __device__ __forceinline__ float load_w(const Tin* p);
@@ -109,11 +122,20 @@ template <> __device__ __forceinline__ float load_w<float>(const float* p) { ret
 template <> __device__ __forceinline__ float load_w<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 template <> __device__ __forceinline__ float load_w<_Float16>(const _Float16* p) { return (float)*p; }
 
-__device__ __forceinline__ double xor16_sum(double v) {
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 1);
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+// Sum over the 16 lanes of a DPP row; every lane of the row ends with the
+// same bits (each step adds two operands that its partner adds in the other
+// order).
+__device__ __forceinline__ double row16_sum(double v) {
+  v = v + dpp_f64<DPP_QUAD_XOR1>(v);
+  v = v + dpp_f64<DPP_QUAD_XOR2>(v);
+  v = v + dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+  v = v + dpp_f64<DPP_ROW_MIRROR>(v);
   return v;
 }
 
@@ -137,20 +159,28 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
   const int nb = 1 << nbits, nT = nb - 1;
   const int Ki = (int)K;
 
-  // ---- load, block absmax, x = w / c, keys (slot i*NT + t) ----------------
+  // ---- load, block absmax, x = w / c, keys --------------------------------
+  // thread t takes elements 16t .. 16t+15 (four threads per 64-block) into
+  // sorted slots 16t .. 16t+15 (any start order serves the sort)
   uint64_t k[16];
-  const Tin* Wr = W + row * K;
+  {
+    const int e0 = t * 16;
+    const Tin* Wr = W + row * K + e0;
+    float w[16];
+    float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = i * NT + t;   // 64 | NT: a wave covers one 64-block
-    if (e < Ki) {
-      const float w = load_w<Tin>(Wr + e);
-      const float m = wave_max(fabsf(w));
-      const float x = (m > 0.0f) ? w / m : 0.0f;
-      if (lane == 0) sAbs[e >> 6] = m;
-      k[i] = ((uint64_t)f32_order_bits(x) << 32) | (uint32_t)e;
-    } else {
-      k[i] = ((uint64_t)kPadHi << 32) | (uint32_t)e;
+    for (int i = 0; i < 16; ++i) {
+      w[i] = (e0 < Ki) ? load_w<Tin>(Wr + i) : 0.0f;
+      m = fmaxf(m, fabsf(w[i]));
+    }
+    m = fmaxf(m, dpp_f32<DPP_QUAD_XOR1>(m));
+    m = fmaxf(m, dpp_f32<DPP_QUAD_XOR2>(m));
+    if (e0 < Ki && (t & 3) == 0) sAbs[t >> 2] = m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = (m > 0.0f) ? w[i] / m : 0.0f;
+      k[i] = (e0 < Ki) ? (((uint64_t)f32_order_bits(x) << 32) | (uint32_t)(e0 + i))
+                       : (((uint64_t)kPadHi << 32) | (uint32_t)(e0 + i));
     }
   }
 
@@ -163,9 +193,10 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if ((i ^ j) > i) cmp_swap(k[i], k[i ^ j], (((t * 16 + i) & size) == 0));
+  const int sw = t & 15;   // kslot(16t + i) = 16t + (i ^ sw)
   for (int size = 32; size <= KP; size <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sKey[t * 16 + i] = k[i];
+    for (int i = 0; i < 16; ++i) sKey[t * 16 + (i ^ sw)] = k[i];
     __syncthreads();
     int lj = 31 - __builtin_clz((unsigned)size) - 1;   // log2 of the first stride
     while (lj >= 4) {
@@ -179,7 +210,7 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
     }
     // strides 8 .. 1 inside the thread's own 16 slots
 #pragma unroll
-    for (int i = 0; i < 16; ++i) k[i] = sKey[t * 16 + i];
+    for (int i = 0; i < 16; ++i) k[i] = sKey[t * 16 + (i ^ sw)];
     const bool asc = ((t * 16) & size) == 0;
 #pragma unroll
     for (int j = 8; j > 0; j >>= 1)
@@ -188,33 +219,33 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
         if ((i ^ j) > i) cmp_swap(k[i], k[i ^ j], asc);
   }
 
-  // ---- segment sums (thread t owns sorted slots 16t .. 16t+15) -----------
+  // ---- segment sums (thread t owns sorted positions 16t .. 16t+15) -------
   {
-    double sw = 0.0, swx = 0.0, swx2 = 0.0;
+    double sw0 = 0.0, swx = 0.0, swx2 = 0.0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sKey[t * 16 + i] = k[i];
+      sKey[t * 16 + (i ^ sw)] = k[i];
       if ((uint32_t)(k[i] >> 32) != kPadHi) {
         const double x = (double)key_value(k[i]);
         const double w = (double)sAbs[(uint32_t)k[i] >> 6];
         const double wx = w * x;
-        sw += w;
+        sw0 += w;
         swx += wx;
         swx2 += wx * x;
       }
     }
-    sSeg[0][t] = sw;
+    sSeg[0][t] = sw0;
     sSeg[1][t] = swx;
     sSeg[2][t] = swx2;
     sLast[t] = key_value(k[15]);
   }
+  __syncthreads();
   // total weight, the same in every wave: sum of 64 c over the blocks
   double wtot = 0.0;
   for (int b = lane; b < Ki / 64; b += 64) wtot += 64.0 * (double)sAbs[b];
   wtot += __shfl_xor(wtot, 32);
   wtot += __shfl_xor(wtot, 16);
-  wtot = xor16_sum(wtot);
-  __syncthreads();
+  wtot = row16_sum(wtot);
 
   // ---- iterations ---------------------------------------------------------
   // Every wave keeps the whole state in lanes kk = lane & 15 (each 16-lane
@@ -228,63 +259,68 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
   int it = 0, par = 0;
   const int g = t >> 4, e = t & 15;   // interval group, lane within it
   const uint64_t gmask = 0xFFFFull << (lane & 48);
+  const int rowbase = lane & 48;
   bool go = max_iters > 0;
   while (go) {
     // thresholds in ascending order (a code counts thresholds below x, so
-    // interval k lies between the k-th and (k+1)-th smallest threshold)
+    // interval k lies between the k-th and (k+1)-th smallest threshold);
+    // midpoints of increasing levels already are, else rank them
     const float T32 = __double2float_rd(Tc);
-    int rank = 0;
-    for (int j = 0; j < nT; ++j) {
-      const float v = __shfl(T32, j);
-      rank += (v < T32 || (v == T32 && j < kk)) ? 1 : 0;
-    }
-    float Ts = 0.0f;
-    for (int j = 0; j < nT; ++j) {
-      const int rj = __shfl(rank, j);
-      const float vj = __shfl(T32, j);
-      if (rj == kk) Ts = vj;
+    float Ts = T32;
+    const float Tup = __shfl(T32, rowbase | ((kk + 1) & 15));
+    if (__ballot(kk + 1 < nT && !(T32 <= Tup)) != 0) {
+      int rank = 0;
+      for (int j = 0; j < nT; ++j) {
+        const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(T32), j));
+        rank += (v < T32 || (v == T32 && j < kk)) ? 1 : 0;
+      }
+      for (int j = 0; j < nT; ++j) {
+        const int rj = __builtin_amdgcn_readlane(rank, j);
+        const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(T32), j));
+        if (rj == kk) Ts = vj;
+      }
     }
     const float tlo = __shfl(Ts, (g - 1) & 15);
     const float thi = __shfl(Ts, g & 15);
 
     // interval g = positions [a, b)
-    int a = sorted_position<NT>(tlo, sLast, sKey, e, gmask);
-    int b = sorted_position<NT>(thi, sLast, sKey, e, gmask);
+    int a, b;
+    sorted_positions<NT>(tlo, thi, sLast, sKey, e, gmask, a, b);
     if (g == 0) a = 0;
     if (g >= nT) b = Ki;
     if (g >= nb) { a = 0; b = 0; }
-    double sw = 0.0, swx = 0.0, swx2 = 0.0;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
     if (a < b) {
       const int sa = (a + 15) >> 4, sb = b >> 4;
       const int head_end = (sa <= sb) ? sa * 16 : b;
       const int tail_start = (sa <= sb) ? sb * 16 : b;
       const int p0 = a + e;
       if (p0 < head_end) {
-        const uint64_t key = sKey[p0];
+        const uint64_t key = sKey[kslot(p0)];
         const double x = (double)key_value(key);
         const double w = (double)sAbs[(uint32_t)key >> 6];
         const double wx = w * x;
-        sw += w; swx += wx; swx2 += wx * x;
+        s0 += w; s1 += wx; s2 += wx * x;
       }
-      for (int s = sa + e; s < sb; s += 16) {
-        sw += sSeg[0][s]; swx += sSeg[1][s]; swx2 += sSeg[2][s];
+      for (int q = sa + e; q < sb; q += 16) {
+        s0 += sSeg[0][q]; s1 += sSeg[1][q]; s2 += sSeg[2][q];
       }
       const int p1 = tail_start + e;
       if (p1 < b) {
-        const uint64_t key = sKey[p1];
+        const uint64_t key = sKey[kslot(p1)];
         const double x = (double)key_value(key);
         const double w = (double)sAbs[(uint32_t)key >> 6];
         const double wx = w * x;
-        sw += w; swx += wx; swx2 += wx * x;
+        s0 += w; s1 += wx; s2 += wx * x;
       }
     }
-    sw = xor16_sum(sw);
-    swx = xor16_sum(swx);
-    swx2 = xor16_sum(swx2);
+    s0 = row16_sum(s0);
+    s1 = row16_sum(s1);
+    s2 = row16_sum(s2);
     if (g < nb && e == 0) {
-      sBin[par][g][0] = sw;
-      sBin[par][g][1] = swx;
-      sBin[par][g][2] = swx2;
+      sBin[par][g][0] = s0;
+      sBin[par][g][1] = s1;
+      sBin[par][g][2] = s2;
     }
     __syncthreads();
 
@@ -297,10 +333,10 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
     }
     const double Ln = (bw > 0.0) ? bwx / bw : Lc;
     double sse = (kk < nb) ? (bwx2 - 2.0 * Ln * bwx + Ln * Ln * bw) : 0.0;
-    sse = xor16_sum(sse);
+    sse = row16_sum(sse);
     const double mse = sse / wtot;
     Lc = Ln;
-    const double Lup = __shfl(Lc, (lane & 48) | ((kk + 1) & 15));
+    const double Lup = __shfl(Lc, rowbase | ((kk + 1) & 15));
     Tc = (kk < nT) ? (Lc + Lup) / 2.0 : 0.0;
     ++it;
     const bool stop = mse >= prev;   // false while either is NaN, as in IEEE
