@@ -208,8 +208,11 @@ size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * weight and s = alpha / r,
  *     t = X A^T            (float32, [M, r])
  *     H = X W'^T + s t B^T (float32 accumulation, stored as h_dtype)
- * W' is never materialised in memory: packed codes are dequantized inside the
- * GEMM. M <= 16 uses the memory-bound GEMV kernel, larger M the MFMA GEMM.
+ * For an NF4 weight W' is never materialised in memory: packed codes are
+ * dequantized inside the GEMM (M <= 16 uses the memory-bound GEMV kernel,
+ * larger M the MFMA GEMM). A codebook weight is first dequantized into the
+ * workspace by its per-channel dequantization kernel ([LowRA] section 3),
+ * then multiplied by the MFMA GEMM.
  *   X  [M, K] bf16;  A [r, K] bf16;  B [N, r] bf16
  *   H  [M, N] of h_dtype (LQ_BF16 or LQ_F32), written
  *   t_save [M, r] float32, written if not NULL (for the backward)
@@ -236,22 +239,26 @@ int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int
 
 /* Workspace bytes for lq_dequant_gemm with M tokens and rank r: the bf16
  * LoRA-segment operands of the MFMA path, (M + N) * 64 * ceil(2r / 64) * 2
- * bytes, or 0 when the GEMV path is taken (M <= 16, NF4). */
+ * bytes (rounded up to 256), plus N * K * 2 bytes for the dequantized weight
+ * of a codebook weight; 0 when the GEMV path is taken (M <= 16, NF4). */
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
  * Second stage of the forward ([QLoRA] introduction): given t = X A^T,
  * H = X W'^T + (alpha / r) t B^T with W' dequantized inside the kernel (the
- * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM). Arguments as
- * lq_qlora_forward; t [M, r] float32 is read. The workspace (caller-owned,
+ * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM; a codebook weight is
+ * dequantized into the workspace first). Arguments as lq_qlora_forward;
+ * t [M, r] float32 is read. The workspace (caller-owned,
  * lq_dequant_gemm_workspace bytes) receives the LoRA operands of the MFMA
- * path; it may be NULL when the GEMV path is taken (M <= 16, NF4).
+ * path (and the dequantized codebook weight); it may be NULL when the GEMV
+ * path is taken (M <= 16, NF4).
  */
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
                     const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
                     void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for lq_dequant_gemm_t ((M + K) * 64 * ceil(2r / 64) * 2). */
+/* Workspace bytes for lq_dequant_gemm_t: (M + K) * 64 * ceil(2r / 64) * 2
+ * (rounded up to 256), plus N * K * 2 for a codebook weight. */
 size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
@@ -259,8 +266,9 @@ size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * gradient flows through the frozen 4-bit base): given u = G B,
  * grad_X = G W' + (alpha / r) u A, bfloat16 output.
  *   G [M, N] bf16, u [M, r] float32, A [r, K] bf16, grad_X [M, K] bf16.
- * NF4 weights only (LQ_ERR_UNSUPPORTED otherwise); N % 8 == 0 (LQ_ERR_SHAPE);
- * workspace of lq_dequant_gemm_t_workspace bytes (LQ_ERR_WORKSPACE).
+ * NF4 weights are dequantized inside the GEMM, codebook weights into the
+ * workspace first. N % 8 == 0 (LQ_ERR_SHAPE); workspace of
+ * lq_dequant_gemm_t_workspace bytes (LQ_ERR_WORKSPACE).
  */
 int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
                       const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X,
@@ -279,8 +287,8 @@ size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *   G [M, N] bf16; X [M, K] bf16 (needed for dA and when t_saved is NULL)
  *   t_saved [M, r] float32 from the forward, or NULL to recompute t = X A^T
  *   grad_X, dA, dB may each be NULL to skip that output.
- * Requires N % 8 == 0 (LQ_ERR_SHAPE); grad_X needs an NF4 weight
- * (LQ_ERR_UNSUPPORTED for a codebook weight).
+ * Requires N % 8 == 0 (LQ_ERR_SHAPE). For a codebook weight, grad_X
+ * dequantizes it into the workspace first.
  * Errors: as lq_qlora_forward.
  */
 int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,

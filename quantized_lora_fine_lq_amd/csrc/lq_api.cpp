@@ -65,7 +65,7 @@ struct Carver {
 
 size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
   return align_up((size_t)M * r * sizeof(float)) + align_up(row_skinny_ws_floats(M, w.K, r) * sizeof(float)) +
-         align_up(lora_operands_ws_bytes(M, w.N, r));
+         align_up(gemm_ws_bytes(w, M, r, true));
 }
 
 size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
@@ -74,7 +74,7 @@ size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
                            col_skinny_ws_floats(M, w.N, r)};
   for (size_t c : cands) part = c > part ? c : part;
   return 2 * align_up((size_t)M * r * sizeof(float)) + align_up((size_t)w.N * r * sizeof(uint16_t)) +
-         align_up(part * sizeof(float)) + align_up(lora_operands_ws_bytes(M, w.K, r));
+         align_up(part * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
 }
 
 }  // namespace
@@ -184,7 +184,7 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   Carver cv(workspace);
   float* t_ws = cv.take<float>((size_t)M * r);
   float* part = cv.take<float>(row_skinny_ws_floats(M, q.K, r));
-  uint16_t* lora = cv.take<uint16_t>(lora_operands_ws_bytes(M, q.N, r) / sizeof(uint16_t));
+  uint16_t* lora = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
   hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, part, s);
@@ -212,7 +212,7 @@ size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r) {
   QWeight q;
   if (check_qweight(w, &q) != LQ_OK || M <= 0 || r < 1 || r > 128) return 0;
   if (use_gemv(q, M)) return 0;   // the GEMV kernel reads t and B directly
-  return align_up(lora_operands_ws_bytes(M, q.N, r));
+  return align_up(gemm_ws_bytes(q, M, r, true));
 }
 
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
@@ -227,14 +227,14 @@ int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const flo
   hipStream_t s = (hipStream_t)stream;
   const float scale = alpha / (float)r;
   if (use_gemv(q, M)) return launch_status(launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s));
-  if (!workspace || ws_bytes < lora_operands_ws_bytes(M, q.N, r)) return LQ_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < gemm_ws_bytes(q, M, r, true)) return LQ_ERR_WORKSPACE;
   return launch_status(launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, (uint16_t*)workspace, s));
 }
 
 size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r) {
   QWeight q;
   if (check_qweight(w, &q) != LQ_OK || M <= 0 || r < 1 || r > 128) return 0;
-  return align_up(lora_operands_ws_bytes(M, q.K, r));
+  return align_up(gemm_ws_bytes(q, M, r, false));
 }
 
 int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
@@ -243,10 +243,9 @@ int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const f
   QWeight q;
   const int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
-  if (q.format != LQ_FMT_NF4) return LQ_ERR_UNSUPPORTED;
   if (!G || !u || !A || !grad_X) return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
-  if (!workspace || ws_bytes < lora_operands_ws_bytes(M, q.K, r)) return LQ_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < gemm_ws_bytes(q, M, r, false)) return LQ_ERR_WORKSPACE;
   return launch_status(launch_gemm_bwd(q, G, M, u, A, r, alpha / (float)r, grad_X, (uint16_t*)workspace,
                                        (hipStream_t)stream));
 }
@@ -264,7 +263,6 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   QWeight q;
   int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
-  if (q.format != LQ_FMT_NF4 && grad_X) return LQ_ERR_UNSUPPORTED;
   if (!G || !A || !B) return LQ_ERR_ARG;
   if ((dA || !t_saved) && !X) return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
@@ -275,7 +273,7 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   float* u = cv.take<float>((size_t)M * r);
   float* t_ws = cv.take<float>((size_t)M * r);
   uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
-  uint16_t* lora = cv.take<uint16_t>(lora_operands_ws_bytes(M, q.K, r) / sizeof(uint16_t));
+  uint16_t* lora = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
   float* part = reinterpret_cast<float*>(cv.base + cv.used);
   const float scale = alpha / (float)r;
   hipError_t e = hipSuccess;

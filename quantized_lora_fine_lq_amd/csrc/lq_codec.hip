@@ -350,43 +350,117 @@ __global__ __launch_bounds__(256) void k_dequant_codebook(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Codebook quantize: one wave per 64-block, lane e holds element e, so each
-// bit-plane is one wave ballot. x = w / c is the IEEE quotient; the code is
-// the number of the row's thresholds strictly below x.
+// Codebook quantize: one workgroup per row. Each wave takes 256-element
+// chunks of the row (four 64-blocks); lane l holds elements 4(l & 15) ..
+// 4(l & 15) + 3 of block l >> 4, so a block is one 16-lane DPP row and its
+// absmax is a row maximum. x = w / c is the IEEE quotient; the code is the
+// number of the row's thresholds strictly below x. Bit-plane p of a block is
+// assembled as two 32-bit words, each the OR over 8 lanes of their 4-bit
+// slices.
 // ---------------------------------------------------------------------------
-template <typename Tin> __device__ __forceinline__ float load1(const Tin* p);
-template <> __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
-template <> __device__ __forceinline__ float load1<_Float16>(const _Float16* p) { return (float)*p; }
+template <typename Tin, bool VEC>
+__device__ __forceinline__ void load4(const Tin* p, float (&w)[4]);
+template <> __device__ __forceinline__ void load4<float, true>(const float* p, float (&w)[4]) {
+  const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p);
+  w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+}
+template <> __device__ __forceinline__ void load4<float, false>(const float* p, float (&w)[4]) {
+  w[0] = p[0]; w[1] = p[1]; w[2] = p[2]; w[3] = p[3];
+}
+template <> __device__ __forceinline__ void load4<uint16_t, true>(const uint16_t* p, float (&w)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  w[0] = bf16lo_to_f32(v.x); w[1] = bf16hi_to_f32(v.x); w[2] = bf16lo_to_f32(v.y); w[3] = bf16hi_to_f32(v.y);
+}
+template <> __device__ __forceinline__ void load4<uint16_t, false>(const uint16_t* p, float (&w)[4]) {
+  for (int j = 0; j < 4; ++j) w[j] = bf16_to_f32(p[j]);
+}
+template <> __device__ __forceinline__ void load4<_Float16, true>(const _Float16* p, float (&w)[4]) {
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  const h4_t v = *reinterpret_cast<const h4_t*>(p);
+  w[0] = (float)v[0]; w[1] = (float)v[1]; w[2] = (float)v[2]; w[3] = (float)v[3];
+}
+template <> __device__ __forceinline__ void load4<_Float16, false>(const _Float16* p, float (&w)[4]) {
+  for (int j = 0; j < 4; ++j) w[j] = (float)p[j];
+}
 
-template <typename Tin>
-__global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict__ W, int64_t N,
-                                                           int64_t K,
+__device__ __forceinline__ uint32_t row8_or(uint32_t v) {
+  v |= dpp_u32<DPP_QUAD_XOR1>(v);
+  v |= dpp_u32<DPP_QUAD_XOR2>(v);
+  v |= dpp_u32<DPP_ROW_HALF_MIRROR>(v);
+  return v;
+}
+
+// One row at a compile-time width: thresholds in registers, the wave's
+// chunks of the row loaded together before any is processed.
+template <int NBITS, typename Tin, bool VEC>
+__device__ __forceinline__ void codebook_row(const Tin* __restrict__ Wr, int64_t blocks,
+                                             const float* __restrict__ Tr, uint8_t* __restrict__ dst,
+                                             float* __restrict__ absmax_row, int wave, int lane) {
+  constexpr int NT = (1 << NBITS) - 1;
+  constexpr int BATCH = 4;
+  float tr[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) tr[k] = Tr[k];
+  const int g = lane >> 4, m = lane & 15;
+  for (int64_t c0 = wave; c0 * 4 < blocks; c0 += 4 * BATCH) {
+    float w[BATCH][4];
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int64_t blk = (c0 + 4 * b) * 4 + g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[b][j] = 0.0f;
+      if (blk < blocks) load4<Tin, VEC>(Wr + blk * 64 + 4 * m, w[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int64_t blk = (c0 + 4 * b) * 4 + g;
+      const bool live = blk < blocks;   // uniform over the 16-lane row
+      float mx = fmaxf(fmaxf(fabsf(w[b][0]), fabsf(w[b][1])), fmaxf(fabsf(w[b][2]), fabsf(w[b][3])));
+      mx = row16_max(mx);
+      uint32_t code[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = (mx > 0.0f) ? w[b][j] / mx : 0.0f;
+        uint32_t cj = 0;
+#pragma unroll
+        for (int k = 0; k < NT; ++k) cj += (x > tr[k]) ? 1u : 0u;
+        code[j] = cj;
+      }
+#pragma unroll
+      for (int p = 0; p < NBITS; ++p) {
+        uint32_t nib = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nib |= ((code[j] >> p) & 1u) << j;
+        const uint32_t word = row8_or(nib << (4 * (m & 7)));
+        if (live && (m & 7) == 0)
+          *reinterpret_cast<uint32_t*>(dst + blk * 8 * NBITS + 8 * p + 4 * (m >> 3)) = word;
+      }
+      if (live && m == 0) absmax_row[blk] = mx;
+    }
+  }
+}
+
+template <typename Tin, bool VEC>
+__global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict__ W, int64_t K,
                                                            const uint8_t* __restrict__ row_bits,
                                                            const int64_t* __restrict__ row_offset,
                                                            const float* __restrict__ T,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t blocks_per_row = K / 64;
-  if (blk >= N * blocks_per_row) return;   // uniform per wave
-  const int64_t row = blk / blocks_per_row;
-  const int64_t blk_in_row = blk - row * blocks_per_row;
-  const float w = load1<Tin>(W + blk * 64 + lane);
-  const float m = wave_max(fabsf(w));
-  const float x = (m > 0.0f) ? w / m : 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
   const int nb = min(max((int)row_bits[row], 1), 4);
-  const int nt = (1 << nb) - 1;
+  const int64_t blocks = K / 64;
+  const Tin* Wr = W + row * K;
   const float* Tr = T + row * 15;
-  uint32_t code = 0;
-  for (int k = 0; k < nt; ++k) code += (x > Tr[k]) ? 1u : 0u;
-  uint8_t* dst = codes + row_offset[row] + blk_in_row * 8 * nb;
-  for (int p = 0; p < nb; ++p) {
-    const uint64_t plane = __ballot((code >> p) & 1u);
-    if (lane == 0) *reinterpret_cast<uint64_t*>(dst + 8 * p) = plane;
+  uint8_t* dst = codes + row_offset[row];
+  float* am = absmax + row * blocks;
+  switch (nb) {
+    case 1: codebook_row<1, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
+    case 2: codebook_row<2, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
+    case 3: codebook_row<3, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
+    default: codebook_row<4, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
   }
-  if (lane == 0) absmax[blk] = m;
 }
 
 }  // namespace
@@ -486,14 +560,24 @@ hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* T, uint8_t* codes, float* absmax, hipStream_t s) {
-  const int64_t nblk = N * K / 64;
-  const dim3 grid((unsigned)((nblk + 3) / 4));
-  if (dtype == LQ_F32)
-    hipLaunchKernelGGL(k_quantize_codebook<float>, grid, dim3(256), 0, s, (const float*)W, N, K, row_bits, row_offset, T, codes, absmax);
-  else if (dtype == LQ_BF16)
-    hipLaunchKernelGGL(k_quantize_codebook<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, N, K, row_bits, row_offset, T, codes, absmax);
-  else
-    hipLaunchKernelGGL(k_quantize_codebook<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, N, K, row_bits, row_offset, T, codes, absmax);
+  const dim3 grid((unsigned)N), block(256);
+  const uintptr_t a = (uintptr_t)W;
+  if (dtype == LQ_F32) {
+    if (a % 16 == 0)
+      hipLaunchKernelGGL((k_quantize_codebook<float, true>), grid, block, 0, s, (const float*)W, K, row_bits, row_offset, T, codes, absmax);
+    else
+      hipLaunchKernelGGL((k_quantize_codebook<float, false>), grid, block, 0, s, (const float*)W, K, row_bits, row_offset, T, codes, absmax);
+  } else if (dtype == LQ_BF16) {
+    if (a % 8 == 0)
+      hipLaunchKernelGGL((k_quantize_codebook<uint16_t, true>), grid, block, 0, s, (const uint16_t*)W, K, row_bits, row_offset, T, codes, absmax);
+    else
+      hipLaunchKernelGGL((k_quantize_codebook<uint16_t, false>), grid, block, 0, s, (const uint16_t*)W, K, row_bits, row_offset, T, codes, absmax);
+  } else {
+    if (a % 8 == 0)
+      hipLaunchKernelGGL((k_quantize_codebook<_Float16, true>), grid, block, 0, s, (const _Float16*)W, K, row_bits, row_offset, T, codes, absmax);
+    else
+      hipLaunchKernelGGL((k_quantize_codebook<_Float16, false>), grid, block, 0, s, (const _Float16*)W, K, row_bits, row_offset, T, codes, absmax);
+  }
   return hipGetLastError();
 }
 

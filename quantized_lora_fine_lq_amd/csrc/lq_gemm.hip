@@ -15,7 +15,8 @@ namespace {
 // Fused dequant-GEMM.
 //
 // out[m][c] = sum_k A[m][k] * Bt[c][k] over a main segment (Bt = W' forward,
-// Bt = W'^T backward, both produced from packed codes) followed by a LoRA
+// Bt = W'^T backward; produced from the packed NF4 codes, or copied from the
+// bf16 weight that the codebook format's dequantization writes first) followed by a LoRA
 // segment of 2r columns: A-side [hi(s*L) | lo(s*L)] with L = t (forward) or
 // u (backward) split into two bfloat16 terms, Bt-side [Lb | Lb] with
 // Lb = B (forward) or A^T (backward). hi + lo carries L to about 2^-17, so
@@ -47,6 +48,7 @@ struct GemmParams {
   void* out;           // [M, Ncols]
   QWeight w;
   Nf4Levels lv;
+  const uint16_t* wbf; // dequantized weight [N, K] bf16 (codebook format), else null
 };
 
 __device__ __forceinline__ void zero(u32x4_t& v) { v = u32x4_t{0u, 0u, 0u, 0u}; }
@@ -283,74 +285,67 @@ struct ProdBwdNF4 {
   }
 };
 
-// Codebook forward: Bt[n][k] from the row's bit-planes and its 16-entry
-// mapping (staged in LDS for the workgroup's 128 rows). Thread -> row t/4,
-// columns 16 (t % 4) .. +16 (two bytes of each bit-plane).
+// Dequantized bfloat16 weight (the codebook format: its per-channel
+// dequantization kernel writes W' first). Forward: Bt[n][k] = W'[n0 + n][64 it
+// + k]; thread -> row t/4, columns 16 (t % 4) .. +16 (two 16-byte loads).
 template <bool DQ>
-struct ProdFwdCodebook {
-  const uint8_t* crow;
-  int64_t blk0;
-  int nb;
-  uint32_t plane[4];
-  float c0, s2;
-  uint32_t q8;
-  float livef;
-  __device__ static float* levels_lds() {
-    __shared__ float sL[BN * 17];
-    return sL;
-  }
+struct ProdFwdBF16 {
+  const uint16_t* src;
+  u32x4_t v[2];
+  bool live;
   __device__ void init(const GemmParams& p, int64_t n0) {
-    float* sL = levels_lds();
-    for (int idx = threadIdx.x; idx < BN * 16; idx += GEMM_THREADS) {
-      const int rr = idx / 16, q = idx % 16;
-      const int64_t n = min(n0 + rr, p.w.N - 1);
-      sL[rr * 17 + q] = p.w.levels[n * 16 + q];
-    }
     const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
-    const int64_t n = min(n0 + row, p.w.N - 1);
-    nb = min(max((int)p.w.row_bits[n], 1), 4);
-    crow = p.w.codes + p.w.row_offset[n] + 2 * qq;
-    blk0 = n * (p.w.K / 64);
+    const int64_t n = min(n0 + row, p.w.N - 1);   // rows past N: outputs never stored
+    src = p.wbf + n * p.w.K + 16 * qq;
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
-    livef = step < nMain ? 1.0f : 0.0f;
+    live = step < nMain;
     const int it = min(step, nMain - 1);
-    const uint8_t* src = crow + (int64_t)it * 8 * nb;
+    const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src + (int64_t)it * BK);
+    v[0] = s[0];
+    v[1] = s[1];
+  }
+  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t*, float) {
+    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    dst[0] = live ? v[0] : z;
+    dst[1] = live ? v[1] : z;
+  }
+};
+
+// Backward over a dequantized bfloat16 weight: Bt[c][n] = W'[64 it + n][n0 + c].
+// Thread -> rows 2 (t % 32) + {0, 1} of the step, columns 8 (t / 32) .. +8
+// (one 16-byte load per row); each LDS word pairs the two rows of a column.
+// Rows past N contribute zero.
+template <bool DQ>
+struct ProdBwdBF16 {
+  int64_t kcol;
+  u32x4_t v[2];
+  bool ok[2];
+  __device__ void init(const GemmParams& p, int64_t n0) {
+    const int kq = threadIdx.x >> 5;
+    kcol = min(n0 + 8 * kq, p.w.K - 8);   // columns past K: outputs never stored
+  }
+  __device__ void load(const GemmParams& p, int step, int nMain) {
+    const int g = threadIdx.x & 31;
+    const int it = min(step, nMain - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) plane[q] = *reinterpret_cast<const uint16_t*>(src + 8 * min(q, nb - 1));
-    const int64_t blk = blk0 + it;
-    if (DQ) {
-      q8 = p.w.qc.absmax_q[blk];
-      s2 = p.w.qc.dq_scale[blk >> 8];
-    } else {
-      c0 = p.w.qc.absmax[blk];
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t nrow = (int64_t)it * BK + 2 * g + rr;
+      ok[rr] = step < nMain && nrow < p.w.N;
+      v[rr] = *reinterpret_cast<const u32x4_t*>(p.wbf + min(nrow, p.w.N - 1) * p.w.K + kcol);
     }
   }
-  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t*, float mean) {
-    const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
-    const float cp = const_of<DQ>(c0, q8, s2, mean) * livef;
-    const float* L = levels_lds() + row * 17;
-    uint32_t pl[4];
+  __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t*, float) {
+    const int g = threadIdx.x & 31, kq = threadIdx.x >> 5;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const u32x4_t a = ok[0] ? v[0] : z, b = ok[1] ? v[1] : z;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(sB + (8 * kq) * PITCH + 2 * g);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pl[q] = (q < nb) ? plane[q] : 0u;
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      u32x4_t o;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float x[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int e = 8 * d + 2 * b + t;
-          uint32_t code = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) code |= ((pl[q] >> e) & 1u) << q;
-          x[t] = L[code] * cp;
-        }
-        o[b] = pack_bf16x2(x[0], x[1]);
-      }
-      dst[d] = o;
+    for (int j = 0; j < 4; ++j) {
+      dst[(2 * j) * (PITCH / 2)] = (a[j] & 0xFFFFu) | (b[j] << 16);
+      dst[(2 * j + 1) * (PITCH / 2)] = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
     }
   }
 };
@@ -985,6 +980,20 @@ size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r) {
   return (size_t)(M + Ncols) * lora_seg_cols(r) * sizeof(uint16_t);
 }
 
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of the forward / backward GEMM: the LoRA operands, then (codebook
+// format) the dequantized bf16 weight.
+size_t gemm_ws_bytes(const QWeight& w, int64_t M, int r, bool fwd) {
+  size_t b = align256(lora_operands_ws_bytes(M, fwd ? w.N : w.K, r));
+  if (w.format == LQ_FMT_CODEBOOK) b += align256((size_t)w.N * w.K * sizeof(uint16_t));
+  return b;
+}
+
+static uint16_t* weight_ws(const QWeight& w, int64_t M, int r, bool fwd, uint16_t* ws) {
+  return ws + align256(lora_operands_ws_bytes(M, fwd ? w.N : w.K, r)) / sizeof(uint16_t);
+}
+
 // Writes the LoRA operands into ws (t2 first, then lb2) and fills p.
 static hipError_t prepare_lora(GemmParams& p, const float* L, const uint16_t* lb, int r, float s, bool fwd,
                                uint16_t* ws, hipStream_t st) {
@@ -1010,6 +1019,7 @@ static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, in
   p.gm = (int)std::min<int64_t>(2, (M + BM - 1) / BM);
   p.w = w;
   p.lv = tables().lv;
+  p.wbf = nullptr;
   return p;
 }
 
@@ -1030,22 +1040,36 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
     else if (f32) hipLaunchKernelGGL((k_dq_gemm<PROD<false>, true, false>), grid, dim3(GEMM_THREADS), 0, st, p);   \
     else hipLaunchKernelGGL((k_dq_gemm<PROD<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);           \
   } while (0)
-  if (w.format == LQ_FMT_NF4) LQ_LAUNCH_FWD(ProdFwdNF4);
-  else LQ_LAUNCH_FWD(ProdFwdCodebook);
+  if (w.format == LQ_FMT_NF4) {
+    LQ_LAUNCH_FWD(ProdFwdNF4);
+  } else {
+    uint16_t* wbf = weight_ws(w, M, r, true, ws);
+    e = launch_dequant(w, wbf, st);
+    if (e != hipSuccess) return e;
+    p.wbf = wbf;
+    if (f32) hipLaunchKernelGGL((k_dq_gemm<ProdFwdBF16<false>, true, false>), grid, dim3(GEMM_THREADS), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdFwdBF16<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
+  }
 #undef LQ_LAUNCH_FWD
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
                            const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st) {
-  if (w.format != LQ_FMT_NF4) return hipErrorInvalidValue;
   GemmParams p = make_params(w, G, M, w.K, w.N, gX);
   hipError_t e = prepare_lora(p, u, A, r, s, false, ws, st);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
-  if (w.qc.absmax == nullptr) {
+  if (w.format == LQ_FMT_CODEBOOK) {
+    uint16_t* wbf = weight_ws(w, M, r, false, ws);
+    e = launch_dequant(w, wbf, st);
+    if (e != hipSuccess) return e;
+    p.wbf = wbf;
+    if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdBF16<false>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);
+    else hipLaunchKernelGGL((k_dq_gemm<ProdBwdBF16<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
+  } else if (w.qc.absmax == nullptr) {
     if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);
     else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<true>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
   } else {

@@ -99,6 +99,9 @@ hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64
 // output columns, r) bytes (output columns = N forward, K backward).
 int lora_seg_cols(int r);
 size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r);
+// Workspace of launch_gemm_fwd (fwd) / launch_gemm_bwd: LoRA operands, plus
+// the dequantized bf16 weight for the codebook format.
+size_t gemm_ws_bytes(const QWeight& w, int64_t M, int r, bool fwd);
 hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,
                            hipStream_t st);

@@ -139,9 +139,15 @@ def test_validation_errors_without_launch(lq):
     w_odd = qw(N=100)                   # backward needs N % 8 == 0
     b3 = list(bargs); b3[0] = ctypes.byref(w_odd)
     assert L.lq_qlora_backward(*b3) == lq.LQ_ERR_SHAPE
+    # a codebook weight is dequantized into the workspace: N * K * 2 more bytes
     wc = qw(format=1, row_bits=1, row_offset=1, levels=1)
+    wsc = L.lq_backward_workspace(ctypes.byref(wc), 64, 16)
+    assert wsc == wsb + 128 * 256 * 2
     b4 = list(bargs); b4[0] = ctypes.byref(wc)
-    assert L.lq_qlora_backward(*b4) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_qlora_backward(*b4) == lq.LQ_ERR_WORKSPACE
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 300, 16) == (300 + 128) * 64 * 2 + 128 * 256 * 2
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 16, 16) == (16 + 128) * 64 * 2 + 128 * 256 * 2
+    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(wc), 300, 16) == (300 + 256) * 64 * 2 + 128 * 256 * 2
 
     # split forward stages: the MFMA path (M > 16) needs the LoRA-operand workspace,
     # (M + N) * 64 * ceil(2r / 64) * 2 bytes; the GEMV path (M <= 16, NF4) needs none

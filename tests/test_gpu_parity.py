@@ -299,6 +299,22 @@ def test_codebook_quantize_bit_exact(lq, torch):
     assert np.array_equal(host(codes)[:packed.size], packed)
 
 
+@pytest.mark.parametrize("dtype,offset", [("f32", 1), ("bf16", 0), ("bf16", 1), ("f16", 0), ("f16", 3)])
+def test_codebook_quantize_half_and_unaligned(lq, torch, dtype, offset):
+    """bf16 / f16 inputs (widened exactly) and base pointers off the vector
+    alignment (element offset into a larger buffer); K not a multiple of 256."""
+    W, bits, L, T = codebook_case(4, 72, 320)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    buf = torch.zeros(W.size + 8, dtype=tdt, device="cuda")
+    Wd = buf[offset:offset + W.size].view(W.shape)
+    Wd.copy_(dev(torch, W).to(tdt))
+    W32 = host(Wd.float())
+    codes, absmax, row_off = lq.quantize_codebook(Wd, dev(torch, bits), dev(torch, T))
+    packed, c, _ = codebook.quantize(W32, bits, T)
+    assert np.array_equal(host(absmax), c)
+    assert np.array_equal(host(codes)[:packed.size], packed)
+
+
 def test_codebook_nf4_cross_check(lq, torch):
     """4 bits with the NF4 thresholds/levels: dequant equals the NF4 path's."""
     rng = np.random.default_rng(2)
@@ -327,6 +343,56 @@ def test_codebook_dequant_and_forward(lq, torch, M):
     H, t = lq.qlora_forward(qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), alpha)
     Href, _ = layer.forward(Wd, X.f32, A.f32, B.f32, alpha)
     assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
+
+
+def codebook_oracle_wd(W, bits, Lv, T):
+    N, K = W.shape
+    packed, c, _ = codebook.quantize(W, bits, T)
+    code8, s2, mu = dq.double_quant(c)
+    return codebook.dequant(packed, bits, Lv, dq.dq_decode(code8, s2, mu), N, K)
+
+
+@pytest.mark.parametrize("N,K,M,r,alpha", [(256, 512, 300, 16, 32.0), (200, 320, 70, 64, 16.0)])
+def test_codebook_forward_f32_and_backward(lq, torch, N, K, M, r, alpha):
+    """Codebook weights through the full layer: forward (bf16 and float32 H)
+    and backward (grad_X through the dequantized weight, dA, dB); N = 200
+    leaves a partial last step of the backward's contraction."""
+    W, bits, Lv, T = codebook_case(7 + M, N, K)
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    Wd = codebook_oracle_wd(W, bits, Lv, T)
+    Ls = syn.small_layer(N, K, M, r, alpha, 400 + M)
+    X, A, B, G = syn.activations(Ls), syn.lora_a(Ls), syn.lora_b(Ls), syn.grad_out(Ls)
+    Xd, Ad, Bd, Gd = (bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits),
+                      bf16_dev(torch, G.bits))
+    H, t = lq.qlora_forward(qw, Xd, Ad, Bd, alpha)
+    H32, _ = lq.qlora_forward(qw, Xd, Ad, Bd, alpha, out_dtype=torch.float32)
+    Href, tref = layer.forward(Wd, X.f32, A.f32, B.f32, alpha)
+    assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
+    assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
+    gx, dA, dB = lq.qlora_backward(qw, Xd, Gd, Ad, Bd, alpha, t=t)
+    rX, rA, rB = layer.backward(Wd, X.f32, G.f32, A.f32, B.f32, alpha)
+    assert layer.rel_frobenius(bf16_to_f32(gx), rX) <= BF16_TOL
+    assert layer.rel_frobenius(host(dA), rA) <= F32_TOL
+    assert layer.rel_frobenius(host(dB), rB) <= F32_TOL
+
+
+def test_codebook_grad_x_unit_probe(lq, torch):
+    """G rows = e_n, B = 0: grad_X[m, :] = W'[n_m, :] exactly (the
+    transposed copy of the dequantized codebook weight)."""
+    rng = np.random.default_rng(6)
+    N, K, M = 136, 384, 40
+    W, bits, Lv, T = codebook_case(9, N, K)
+    ns = rng.integers(0, N, M)
+    G = np.zeros((M, N), dtype=np.uint16)
+    G[np.arange(M), ns] = 0x3F80
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    A = syn.to_bf16_bits(rng.standard_normal((16, K)).astype(np.float32))
+    B = np.zeros((N, 16), dtype=np.uint16)
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    gx, dA, dB = lq.qlora_backward(qw, bf16_dev(torch, X), bf16_dev(torch, G), bf16_dev(torch, A),
+                                   bf16_dev(torch, B), 32.0)
+    Wd = codebook_oracle_wd(W, bits, Lv, T)
+    assert np.array_equal(bf16_to_f32(gx), Wd[ns])
 
 
 # ---------------------------------------------------------------------------
