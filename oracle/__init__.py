@@ -15,6 +15,8 @@ It is written to be checked by eye against the pages it follows:
   quantization with custom thresholds (section 3, workflow), groups of 64
   scaled by absmax (section 4.1), mappings and thresholds (section 4.1,
   figure 3) and the weighted Lloyd-Max learner (section 5).
+* LowRA page, sections 3 and 5: the LoftQ-style low-rank initialiser (five
+  alternating quantize / rank-r SVD steps).
 * AQLoRA page -- bittide.aicompass.dev translation of AQLoRA, section 3.1
   (profiling pass): the per-layer NF4 round-trip error.
 
@@ -26,4 +28,4 @@ Functions without an independent pin say "parity unpinned" in their
 docstring; at present there are none.
 """
 
-from . import bf16, fp8, nf4, dq, layer, codebook, lloyd, sizes  # noqa: F401
+from . import bf16, fp8, nf4, dq, layer, codebook, lloyd, loftq, sizes  # noqa: F401
