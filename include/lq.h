@@ -356,6 +356,80 @@ int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32
                        const uint8_t* row_bits, int32_t max_iters, float* levels,
                        float* thresholds, int32_t* iterations, void* stream);
 
+/*
+ * Low-rank initialisation of the adapter ([LowRA] sections 3 and 5: LoftQ,
+ * five alternating steps in which the weight minus the current adapter is
+ * quantized and the adapter is refit to what quantization leaves).
+ *
+ * lq_lowrank_sub: out = float32(W - B A), the rank-r product summed in
+ * float64 in order j = 0 .. r-1 (each product of two float32 values is exact
+ * there) and subtracted from W in float64 before the single rounding.
+ *   W, out [N, K] float32 (out may alias W); B [N, r], A [r, K] float32;
+ *   16-byte aligned, K % 4 == 0. r = 0 copies W.
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (sizes <= 0, K % 4 != 0, r outside [0, 128]),
+ * LQ_ERR_LAUNCH.
+ */
+int lq_lowrank_sub(const float* W, int64_t N, int64_t K, const float* B, const float* A, int32_t r,
+                   float* out, void* stream);
+
+/*
+ * lq_residual: R = float32(W - W') elementwise, W' a bfloat16 weight (for
+ * example lq_dequant's output): what the quantized base misses.
+ *   W, R [n] float32 (16-byte aligned), Wd [n] bfloat16 (8-byte aligned), n % 4 == 0.
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_LAUNCH.
+ */
+int lq_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, void* stream);
+
+/* Workspace bytes for lq_svd_lowrank (0 for an invalid shape). */
+size_t lq_svd_lowrank_workspace(int64_t N, int64_t K, int32_t r, int32_t l);
+
+/*
+ * Rank-r SVD of R [N, K] (float32, row-major), split evenly between the
+ * factors: B = U_r S_r^(1/2) [N, r], A = S_r^(1/2) V_r^T [r, K], sigma = the r
+ * largest singular values [r], so that B A approximates the best rank-r
+ * approximation of R. Computed by randomized subspace iteration on l >= r
+ * columns: Y = R omega, then power_iters steps of Z = R^T Y, Y = R Z, every
+ * block orthonormalised (Cholesky QR applied twice, float64 Gram); then the
+ * Rayleigh-Ritz step on Z = R^T Y (eigenvectors of Z^T Z by cyclic Jacobi in
+ * float64). The result approaches the truncated SVD as power_iters grows; its
+ * error is the part of the spectrum the iteration has not separated (see the
+ * tests for the measured gap to the exact SVD). Deterministic for a given
+ * omega (all reductions in a fixed order).
+ *   omega  [K, l] float32, caller-drawn (standard normal is the usual choice)
+ *   l      even, r <= l <= min(N, K, 96) (LQ_ERR_SHAPE; above 96 LQ_ERR_UNSUPPORTED)
+ *   power_iters 0 .. 1000 (LQ_ERR_ARG)
+ *   B [N, r], A [r, K], sigma [r] float32, written
+ * A numerically rank-deficient R gives zero factors and sigma = 0 past its rank.
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_svd_lowrank(const float* R, int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters,
+                   const float* omega, float* B, float* A, float* sigma, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* Workspace bytes for lq_loftq_init (0 for an invalid shape). */
+size_t lq_loftq_workspace(int64_t N, int64_t K, int32_t r, int32_t l, int32_t double_quant);
+
+/*
+ * LoftQ-style initialisation ([LowRA] sections 3 and 5). Starting from
+ * B = 0, A = 0, each of `steps` alternations
+ *   Q   = NF4 quantization of W - B A (lq_lowrank_sub, then lq_quantize_nf4 and,
+ *         if double_quant, lq_double_quant),
+ *   R   = W - W' with W' the bf16 dequantized Q (lq_dequant, lq_residual),
+ *   B,A = rank-r SVD of R (lq_svd_lowrank with l, power_iters, omega),
+ * and optionally objectives[t] = ||R - B A||_F^2 (float64, fixed-order sum):
+ * the error the adapter leaves after step t.
+ * The outputs are the last step's quantized weight (codes, absmax and, with
+ * double_quant, absmax_q / dq_scale / dq_mean, laid out as lq_quantize_nf4 and
+ * lq_double_quant write them) and the float32 factors B [N, r], A [r, K].
+ *   W  [N, K] float32, K % 64 == 0; blocksize 64; steps 1 .. 100 (5 in the method)
+ *   objectives [steps] device float64, may be NULL
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32_t double_quant, int32_t r,
+                  int32_t l, int32_t steps, int32_t power_iters, const float* omega, uint8_t* codes,
+                  float* absmax, uint8_t* absmax_q, float* dq_scale, float* dq_mean, float* B, float* A,
+                  float* sigma, double* objectives, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

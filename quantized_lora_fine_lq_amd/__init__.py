@@ -70,6 +70,14 @@ SIGNATURES = {
                                             c_vp, c_vp, c_vp]),
     "lq_lloyd_codebooks": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp,
                                           c_vp, c_vp]),
+    "lq_lowrank_sub": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp]),
+    "lq_residual": (ctypes.c_int, [c_vp, c_vp, c_i64, c_vp, c_vp]),
+    "lq_svd_lowrank_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32]),
+    "lq_svd_lowrank": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                      c_sz, c_vp]),
+    "lq_loftq_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32, c_i32]),
+    "lq_loftq_init": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "lq_dequant_gemm_workspace": (c_sz, [QW_P, c_i64, c_i32]),
@@ -336,6 +344,73 @@ def lloyd_codebooks(W, row_bits, max_iters: int = 100, blocksize: int = 64):
                                   _ptr(levels), _ptr(thresholds), _ptr(iters), _stream(W.device)),
            "lq_lloyd_codebooks")
     return levels, thresholds, iters
+
+
+def lowrank_sub(W, B, A):
+    """float32(W - B A) with the rank-r product summed in float64."""
+    torch = _torch()
+    N, K = W.shape
+    r = B.shape[1]
+    out = torch.empty_like(W)
+    _check(lib.lq_lowrank_sub(_ptr(W), N, K, _ptr(B) if r else None, _ptr(A) if r else None, r, _ptr(out),
+                              _stream(W.device)), "lq_lowrank_sub")
+    return out
+
+
+def residual(W, Wd):
+    """R = W - W' for a float32 W and a bfloat16 W'."""
+    torch = _torch()
+    R = torch.empty_like(W)
+    _check(lib.lq_residual(_ptr(W), _ptr(Wd), W.numel(), _ptr(R), _stream(W.device)), "lq_residual")
+    return R
+
+
+def svd_lowrank(R, r: int, omega, power_iters: int = 8):
+    """Rank-r SVD of R [N, K] (float32) by randomized subspace iteration from
+    omega [K, l] -> (B [N, r], A [r, K], sigma [r]) with B A ~ the truncated SVD."""
+    torch = _torch()
+    N, K = R.shape
+    l = omega.shape[1]
+    B = torch.empty(N, r, dtype=torch.float32, device=R.device)
+    A = torch.empty(r, K, dtype=torch.float32, device=R.device)
+    sigma = torch.empty(r, dtype=torch.float32, device=R.device)
+    ws_bytes = lib.lq_svd_lowrank_workspace(N, K, r, l)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=R.device)
+    _check(lib.lq_svd_lowrank(_ptr(R), N, K, r, l, int(power_iters), _ptr(omega), _ptr(B), _ptr(A), _ptr(sigma),
+                              _ptr(ws), ws_bytes, _stream(R.device)), "lq_svd_lowrank")
+    return B, A, sigma
+
+
+def loftq_init(W, r: int, omega, steps: int = 5, power_iters: int = 8, double_quant: bool = True,
+               blocksize: int = 64):
+    """LoftQ-style initialisation of W [N, K] (float32): returns (QWeight,
+    B [N, r] f32, A [r, K] f32, sigma [r], objectives [steps] f64)."""
+    torch = _torch()
+    N, K = W.shape
+    l = omega.shape[1]
+    dev = W.device
+    n_b = N * K // blocksize
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n_b, dtype=torch.float32, device=dev)
+    aq = torch.empty(n_b, dtype=torch.uint8, device=dev) if double_quant else None
+    s2 = torch.empty((n_b + 255) // 256, dtype=torch.float32, device=dev) if double_quant else None
+    mu = torch.empty(1, dtype=torch.float32, device=dev) if double_quant else None
+    B = torch.empty(N, r, dtype=torch.float32, device=dev)
+    A = torch.empty(r, K, dtype=torch.float32, device=dev)
+    sigma = torch.empty(r, dtype=torch.float32, device=dev)
+    objectives = torch.empty(steps, dtype=torch.float64, device=dev)
+    ws_bytes = lib.lq_loftq_workspace(N, K, r, l, int(double_quant))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    P = lambda t: _ptr(t) if t is not None else None
+    _check(lib.lq_loftq_init(_ptr(W), N, K, blocksize, int(double_quant), r, l, int(steps), int(power_iters),
+                             _ptr(omega), _ptr(codes), _ptr(absmax), P(aq), P(s2), P(mu), _ptr(B), _ptr(A),
+                             _ptr(sigma), _ptr(objectives), _ptr(ws), ws_bytes, _stream(dev)), "lq_loftq_init")
+    if double_quant:
+        qw = QWeight(N, K, codes, absmax_q=aq, dq_scale=s2, dq_mean=mu)
+    else:
+        qw = QWeight(N, K, codes, absmax=absmax)
+    qw.absmax_f32 = absmax
+    return qw, B, A, sigma, objectives
 
 
 def quantize_codebook(W, row_bits, thresholds, blocksize: int = 64):

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "liblq.so")
-SOURCES = ["lq_tables.cpp", "lq_api.cpp", "lq_codec.hip", "lq_gemm.hip", "lq_lloyd.hip"]
+SOURCES = ["lq_tables.cpp", "lq_api.cpp", "lq_codec.hip", "lq_gemm.hip", "lq_lloyd.hip", "lq_lowrank.hip"]
 ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 
 

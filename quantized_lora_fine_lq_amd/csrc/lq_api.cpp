@@ -324,4 +324,62 @@ int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32
                                     iterations, (hipStream_t)stream));
 }
 
+int lq_lowrank_sub(const float* W, int64_t N, int64_t K, const float* B, const float* A, int32_t r,
+                   float* out, void* stream) {
+  if (!W || !out || (r > 0 && (!B || !A))) return LQ_ERR_ARG;
+  if (N <= 0 || K <= 0 || K % 4 != 0 || r < 0 || r > 128) return LQ_ERR_SHAPE;
+  return launch_status(launch_lowrank_sub(W, N, K, B, A, r, out, (hipStream_t)stream));
+}
+
+int lq_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, void* stream) {
+  if (!W || !Wd || !R) return LQ_ERR_ARG;
+  if (n <= 0 || n % 4 != 0) return LQ_ERR_SHAPE;
+  return launch_status(launch_residual(W, Wd, n, R, (hipStream_t)stream));
+}
+
+static int check_svd_shape(int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters) {
+  if (N <= 0 || K <= 0 || r < 1 || l < r || l % 2 != 0 || l > N || l > K) return LQ_ERR_SHAPE;
+  if (l > lowrank_max_l()) return LQ_ERR_UNSUPPORTED;
+  if (power_iters < 0 || power_iters > 1000) return LQ_ERR_ARG;
+  return LQ_OK;
+}
+
+size_t lq_svd_lowrank_workspace(int64_t N, int64_t K, int32_t r, int32_t l) {
+  if (check_svd_shape(N, K, r, l, 0) != LQ_OK) return 0;
+  return align_up(svd_ws_bytes(N, K, l, r));
+}
+
+int lq_svd_lowrank(const float* R, int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters,
+                   const float* omega, float* B, float* A, float* sigma, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  if (!R || !omega || !B || !A || !sigma) return LQ_ERR_ARG;
+  const int st = check_svd_shape(N, K, r, l, power_iters);
+  if (st != LQ_OK) return st;
+  if (!workspace || ws_bytes < svd_ws_bytes(N, K, l, r)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_svd_lowrank(R, N, K, r, l, power_iters, omega, B, A, sigma, workspace,
+                                          (hipStream_t)stream));
+}
+
+size_t lq_loftq_workspace(int64_t N, int64_t K, int32_t r, int32_t l, int32_t double_quant) {
+  if (K % 64 != 0 || check_svd_shape(N, K, r, l, 0) != LQ_OK) return 0;
+  return align_up(loftq_ws_bytes(N, K, r, l, double_quant != 0));
+}
+
+int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32_t double_quant, int32_t r,
+                  int32_t l, int32_t steps, int32_t power_iters, const float* omega, uint8_t* codes,
+                  float* absmax, uint8_t* absmax_q, float* dq_scale, float* dq_mean, float* B, float* A,
+                  float* sigma, double* objectives, void* workspace, size_t ws_bytes, void* stream) {
+  const bool dq = double_quant != 0;
+  if (!W || !omega || !codes || !absmax || !B || !A || !sigma) return LQ_ERR_ARG;
+  if (dq && (!absmax_q || !dq_scale || !dq_mean)) return LQ_ERR_ARG;
+  if (steps < 1 || steps > 100) return LQ_ERR_ARG;
+  if (K % 64 != 0) return LQ_ERR_SHAPE;
+  const int st = check_svd_shape(N, K, r, l, power_iters);
+  if (st != LQ_OK) return st;
+  if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < loftq_ws_bytes(N, K, r, l, dq)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_loftq(W, N, K, dq, r, l, steps, power_iters, omega, codes, absmax, absmax_q,
+                                    dq_scale, dq_mean, B, A, sigma, objectives, workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -74,6 +74,22 @@ hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double
 hipError_t launch_lloyd(const void* W, int dtype, int64_t N, int64_t K, const uint8_t* row_bits,
                         int max_iters, float* levels, float* thresholds, int32_t* iterations,
                         hipStream_t s);
+// Low-rank initialisation (LoftQ-style): building blocks and the alternation.
+int lowrank_max_l();
+hipError_t launch_lowrank_sub(const float* W, int64_t N, int64_t K, const float* B, const float* A, int r,
+                              float* out, hipStream_t s);
+hipError_t launch_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, hipStream_t s);
+size_t svd_ws_bytes(int64_t N, int64_t K, int l, int r);
+hipError_t launch_svd_lowrank(const float* R, int64_t N, int64_t K, int r, int l, int power_iters,
+                              const float* omega, float* B, float* A, float* sigma, void* ws, hipStream_t s);
+size_t sqerr_ws_bytes();
+hipError_t launch_lowrank_sqerr(const float* R, int64_t N, int64_t K, const float* B, const float* A, int r,
+                                double* out, void* ws, hipStream_t s);
+size_t loftq_ws_bytes(int64_t N, int64_t K, int r, int l, bool dq);
+hipError_t launch_loftq(const float* W, int64_t N, int64_t K, bool dq, int r, int l, int steps, int power_iters,
+                        const float* omega, uint8_t* codes, float* absmax, uint8_t* absmax_q, float* dq_scale,
+                        float* dq_mean, float* B, float* A, float* sigma, double* objectives, void* ws,
+                        hipStream_t s);
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* thresholds, uint8_t* codes, float* absmax,

@@ -1,0 +1,628 @@
+// Low-rank initialisation of the adapter (LowRA, sections 3 and 5: the
+// quantization error is turned into the starting adapter by LoftQ, five
+// alternating steps of quantizing W - B A and a rank-r SVD of the residual).
+//
+// Kernels:
+//   * W - B A with the rank-r product summed in float64 in order of j;
+//   * R = W - W' (W' the layer's bf16 weight);
+//   * the rank-r SVD of R by randomized subspace iteration: Y = R Omega, then
+//     power steps Z = R^T Y, Y = R Z, each block orthonormalised by CholQR2
+//     (float64 Gram, Cholesky and the inverse of its factor in one workgroup,
+//     then a right multiply); a final Rayleigh-Ritz step takes the
+//     eigenvectors of the l x l Gram of R^T Y by cyclic Jacobi in float64 in
+//     one workgroup;
+//   * ||R - B A||_F^2 with a fixed-order float64 reduction.
+// Tall-skinny products keep R row-major and stream it once per product.
+#include <algorithm>
+#include <cmath>
+
+#include "lq_device.h"
+
+namespace lq {
+namespace {
+
+constexpr int LR_MAXL = 96;    // l = r + oversampling, one Jacobi workgroup holds two l x l float64 matrices
+
+// ---- out = float32(W - sum_j B[n][j] A[j][k]), float64 sum in order of j ----
+__global__ __launch_bounds__(256) void k_lowrank_sub(const float* __restrict__ W, int64_t N, int64_t K,
+                                                     const float* __restrict__ B, const float* __restrict__ A,
+                                                     int r, float* __restrict__ out) {
+  const int64_t quads = N * K / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+    const int64_t e = 4 * i;
+    const int64_t n = e / K, k = e - n * K;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < r; ++j) {
+      const double b = (double)B[n * r + j];
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(A + (int64_t)j * K + k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += b * (double)a[q];   // products exact in float64
+    }
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(W + e);
+    f32x4_t o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (float)((double)w[q] - acc[q]);
+    *reinterpret_cast<f32x4_t*>(out + e) = o;
+  }
+}
+
+// ---- R = W - W' (one float32 subtraction) ---------------------------------
+__global__ __launch_bounds__(256) void k_residual(const float* __restrict__ W, const uint16_t* __restrict__ Wd,
+                                                  int64_t n, float* __restrict__ R) {
+  const int64_t quads = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(W + 4 * i);
+    const uint2 d = *reinterpret_cast<const uint2*>(Wd + 4 * i);
+    f32x4_t o;
+    o[0] = w[0] - bf16lo_to_f32(d.x);
+    o[1] = w[1] - bf16hi_to_f32(d.x);
+    o[2] = w[2] - bf16lo_to_f32(d.y);
+    o[3] = w[3] - bf16hi_to_f32(d.y);
+    *reinterpret_cast<f32x4_t*>(R + 4 * i) = o;
+  }
+}
+
+// ---- Y[M, l] = X[M, C] V[C, l] (float32; X row-major, V row-major) --------
+// Workgroup: 16 rows of X and all l columns; the contraction in chunks of 64
+// staged in LDS. Thread t: row t % 16, columns (t / 16) + 16 c.
+__global__ __launch_bounds__(256) void k_tall_skinny(const float* __restrict__ X, int64_t M, int64_t C,
+                                                     const float* __restrict__ V, int l, float* __restrict__ Y) {
+  __shared__ float sX[16][65];
+  __shared__ float sV[64][LR_MAXL];
+  const int t = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int row = t & 15, cg = t >> 4;
+  float acc[LR_MAXL / 16];
+#pragma unroll
+  for (int c = 0; c < LR_MAXL / 16; ++c) acc[c] = 0.0f;
+  for (int64_t c0 = 0; c0 < C; c0 += 64) {
+    for (int i = t; i < 16 * 64; i += 256) {
+      const int rr = i >> 6, cc = i & 63;
+      const int64_t m = m0 + rr, col = c0 + cc;
+      sX[rr][cc] = (m < M && col < C) ? X[m * C + col] : 0.0f;
+    }
+    for (int i = t; i < 64 * l; i += 256) {
+      const int rr = i / l, cc = i - rr * l;
+      const int64_t col = c0 + rr;
+      sV[rr][cc] = (col < C) ? V[col * l + cc] : 0.0f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 64; ++kk) {
+      const float x = sX[row][kk];
+#pragma unroll
+      for (int c = 0; c < LR_MAXL / 16; ++c) {
+        const int col = cg + 16 * c;
+        if (col < l) acc[c] = __builtin_fmaf(x, sV[kk][col], acc[c]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t m = m0 + row;
+  if (m < M) {
+#pragma unroll
+    for (int c = 0; c < LR_MAXL / 16; ++c) {
+      const int col = cg + 16 * c;
+      if (col < l) Y[m * l + col] = acc[c];
+    }
+  }
+}
+
+// ---- part[s][C, l] = sum over rows m of split s of X[m][c] Q[m][:] ---------
+// (Z = X^T Q with X [M, C] row-major.) Workgroup: 16 columns c of X, rows of
+// one split in chunks of 64. Thread t: column t % 16, outputs (t / 16) + 16 j.
+__global__ __launch_bounds__(256) void k_skinny_t(const float* __restrict__ X, int64_t M, int64_t C,
+                                                  const float* __restrict__ Q, int l, int64_t rows_per_split,
+                                                  float* __restrict__ part) {
+  __shared__ float sX[64][17];
+  __shared__ float sQ[64][LR_MAXL];
+  const int t = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 16;
+  const int s = blockIdx.y;
+  const int64_t mb = (int64_t)s * rows_per_split, me = std::min<int64_t>(M, mb + rows_per_split);
+  const int col = t & 15, cg = t >> 4;
+  float acc[LR_MAXL / 16];
+#pragma unroll
+  for (int j = 0; j < LR_MAXL / 16; ++j) acc[j] = 0.0f;
+  for (int64_t m0 = mb; m0 < me; m0 += 64) {
+    for (int i = t; i < 64 * 16; i += 256) {
+      const int rr = i >> 4, cc = i & 15;
+      const int64_t m = m0 + rr, c = c0 + cc;
+      sX[rr][cc] = (m < me && c < C) ? X[m * C + c] : 0.0f;
+    }
+    for (int i = t; i < 64 * l; i += 256) {
+      const int rr = i / l, cc = i - rr * l;
+      const int64_t m = m0 + rr;
+      sQ[rr][cc] = (m < me) ? Q[m * l + cc] : 0.0f;
+    }
+    __syncthreads();
+    for (int mm = 0; mm < 64; ++mm) {
+      const float x = sX[mm][col];
+#pragma unroll
+      for (int j = 0; j < LR_MAXL / 16; ++j) {
+        const int q = cg + 16 * j;
+        if (q < l) acc[j] = __builtin_fmaf(x, sQ[mm][q], acc[j]);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t c = c0 + col;
+  if (c < C) {
+#pragma unroll
+    for (int j = 0; j < LR_MAXL / 16; ++j) {
+      const int q = cg + 16 * j;
+      if (q < l) part[((int64_t)s * C + c) * l + q] = acc[j];
+    }
+  }
+}
+
+// out[i] = sum_s part[s][i] in order of s
+__global__ __launch_bounds__(256) void k_sum_splits(const float* __restrict__ part, int splits, int64_t n,
+                                                    float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float v = 0.0f;
+    for (int s = 0; s < splits; ++s) v += part[(int64_t)s * n + i];
+    out[i] = v;
+  }
+}
+
+// ---- Gram G = Y^T Y in float64: per-workgroup partials, fixed-order sum -----
+__global__ __launch_bounds__(256) void k_gram_partial(const float* __restrict__ Y, int64_t M, int l,
+                                                      int64_t rows_per_wg, double* __restrict__ part) {
+  __shared__ float sY[32][LR_MAXL];
+  const int t = threadIdx.x;
+  const int64_t mb = (int64_t)blockIdx.x * rows_per_wg, me = std::min<int64_t>(M, mb + rows_per_wg);
+  constexpr int PER = (LR_MAXL * LR_MAXL + 255) / 256;
+  double acc[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) acc[q] = 0.0;
+  const int ll = l * l;
+  for (int64_t m0 = mb; m0 < me; m0 += 32) {
+    for (int i = t; i < 32 * l; i += 256) {
+      const int rr = i / l, cc = i - rr * l;
+      const int64_t m = m0 + rr;
+      sY[rr][cc] = (m < me) ? Y[m * l + cc] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = t + 256 * q;
+      if (e < ll) {
+        const int i = e / l, j = e - i * l;
+        double a = acc[q];
+        for (int rr = 0; rr < 32; ++rr) a += (double)sY[rr][i] * (double)sY[rr][j];
+        acc[q] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int e = t + 256 * q;
+    if (e < ll) part[(int64_t)blockIdx.x * ll + e] = acc[q];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gram_finish(const double* __restrict__ part, int parts, int ll,
+                                                     double* __restrict__ G) {
+  for (int e = blockIdx.x * 256 + threadIdx.x; e < ll; e += gridDim.x * 256) {
+    double v = 0.0;
+    for (int s = 0; s < parts; ++s) v += part[(int64_t)s * ll + e];
+    G[e] = v;
+  }
+}
+
+// ---- Cholesky G = L L^T and T = L^{-T} in one workgroup (float64) ----------
+// Q = Y T then has orthonormal columns (up to rounding). A pivot at or below
+// 1e-28 of the largest diagonal marks a column that depends on the earlier
+// ones: its column of L and its row of L^{-1} are set to zero, so that Q gets
+// a zero column there.
+__global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__ G, int l, double* __restrict__ T) {
+  __shared__ double sA[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sI[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sRed[4];
+  const int t = threadIdx.x;
+  double m = 0.0;
+  for (int e = t; e < l * l; e += 256) {
+    const int i = e / l, k = e % l;
+    const double v = G[e];
+    sA[i][k] = v;
+    if (i == k) m = fmax(m, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) sRed[t >> 6] = m;
+  __syncthreads();
+  const double tol = 1e-28 * fmax(fmax(sRed[0], sRed[1]), fmax(sRed[2], sRed[3]));
+  for (int j = 0; j < l; ++j) {
+    const double d = sA[j][j];
+    const bool ok = d > tol && d > 0.0;
+    const double piv = ok ? sqrt(d) : 0.0;
+    __syncthreads();
+    for (int i = j + 1 + t; i < l; i += 256) sA[i][j] = ok ? sA[i][j] / piv : 0.0;
+    if (t == 0) sA[j][j] = piv;
+    __syncthreads();
+    const int n = l - j - 1;
+    for (int e = t; e < n * n; e += 256) {
+      const int i = j + 1 + e / n, k = j + 1 + e % n;
+      if (k <= i) sA[i][k] -= sA[i][j] * sA[k][j];
+    }
+    __syncthreads();
+  }
+  // L^{-1} by forward substitution, row i at a time, all columns c <= i at once
+  for (int i = 0; i < l; ++i) {
+    const double d = sA[i][i];
+    for (int c = t; c <= i; c += 256) {
+      double v = (c == i) ? 1.0 : 0.0;
+      for (int k = c; k < i; ++k) v -= sA[i][k] * sI[k][c];
+      sI[i][c] = (d > 0.0) ? v / d : 0.0;
+    }
+    __syncthreads();
+  }
+  // T[k][j] = L^{-1}[j][k] (upper triangular)
+  for (int e = t; e < l * l; e += 256) {
+    const int k = e / l, j = e % l;
+    T[e] = (k <= j) ? sI[j][k] : 0.0;
+  }
+}
+
+// ---- symmetric eigen-decomposition by cyclic Jacobi (one workgroup) ---------
+// Round-robin pairing: in each of the l - 1 rounds of a sweep every index is
+// in exactly one pair, so the rotations of a round commute; G <- J^T G J is
+// applied as a column pass then a row pass. Sweeps stop when the squared
+// off-diagonal mass is below 1e-30 of the total or after 30 sweeps. Then
+// the top r eigenpairs (descending, ties by index) give
+//   M1[:, i] = u_i sqrt(sigma_i), M2[:, i] = u_i / sqrt(sigma_i) (0 if sigma_i = 0),
+// with sigma_i = sqrt(max(lambda_i, 0)).
+__global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ Gin, int l, int r,
+                                                     double* __restrict__ M1, double* __restrict__ M2,
+                                                     float* __restrict__ sigma) {
+  __shared__ double sG[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sV[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sC[LR_MAXL / 2], sS[LR_MAXL / 2];
+  __shared__ int sP[LR_MAXL / 2], sQ[LR_MAXL / 2];
+  __shared__ int sOrder[LR_MAXL];
+  __shared__ double sOff, sTot, sRedO[16], sRedT[16];
+  const int t = threadIdx.x;
+  const int n = l;   // even (l % 8 == 0)
+  for (int e = t; e < n * n; e += 1024) {
+    const int i = e / n, j = e % n;
+    sG[i][j] = Gin[e];
+    sV[i][j] = (i == j) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    {
+      double off = 0.0, tot = 0.0;
+      for (int e = t; e < n * n; e += 1024) {
+        const int i = e / n, j = e % n;
+        const double v = sG[i][j] * sG[i][j];
+        tot += v;
+        if (i != j) off += v;
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        off += __shfl_xor(off, o);
+        tot += __shfl_xor(tot, o);
+      }
+      if ((t & 63) == 0) { sRedO[t >> 6] = off; sRedT[t >> 6] = tot; }
+      __syncthreads();
+      if (t == 0) {
+        double a = 0.0, b = 0.0;
+        for (int w = 0; w < 16; ++w) { a += sRedO[w]; b += sRedT[w]; }
+        sOff = a;
+        sTot = b;
+      }
+      __syncthreads();
+    }
+    if (!(sOff > 1e-30 * sTot)) break;
+    for (int round = 0; round < n - 1; ++round) {
+      // pairs of the round-robin schedule: slot 0 fixed, the rest rotate
+      if (t < n / 2) {
+        auto slot = [&](int s) { return s == 0 ? 0 : 1 + (s - 1 + round) % (n - 1); };
+        int p = slot(t), q = slot(n - 1 - t);
+        if (p > q) { const int tmp = p; p = q; q = tmp; }
+        const double apq = sG[p][q], app = sG[p][p], aqq = sG[q][q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double theta = (aqq - app) / (2.0 * apq);
+          const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+          c = 1.0 / sqrt(tt * tt + 1.0);
+          s = tt * c;
+        }
+        sP[t] = p; sQ[t] = q; sC[t] = c; sS[t] = s;
+      }
+      __syncthreads();
+      // columns: G <- G J, V <- V J
+      for (int e = t; e < (n / 2) * n; e += 1024) {
+        const int pi = e / n, i = e % n;
+        const int p = sP[pi], q = sQ[pi];
+        const double c = sC[pi], s = sS[pi];
+        const double gp = sG[i][p], gq = sG[i][q];
+        sG[i][p] = c * gp - s * gq;
+        sG[i][q] = s * gp + c * gq;
+        const double vp = sV[i][p], vq = sV[i][q];
+        sV[i][p] = c * vp - s * vq;
+        sV[i][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+      // rows: G <- J^T G
+      for (int e = t; e < (n / 2) * n; e += 1024) {
+        const int pi = e / n, j = e % n;
+        const int p = sP[pi], q = sQ[pi];
+        const double c = sC[pi], s = sS[pi];
+        const double gp = sG[p][j], gq = sG[q][j];
+        sG[p][j] = c * gp - s * gq;
+        sG[q][j] = s * gp + c * gq;
+      }
+      __syncthreads();
+    }
+  }
+  // rank of each eigenvalue (descending, ties by index)
+  if (t < n) {
+    const double lt = sG[t][t];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double lj = sG[j][j];
+      rank += (lj > lt || (lj == lt && j < t)) ? 1 : 0;
+    }
+    sOrder[rank] = t;
+  }
+  __syncthreads();
+  for (int e = t; e < n * r; e += 1024) {
+    const int i = e / r, k = e % r;
+    const int col = sOrder[k];
+    const double sg = sqrt(fmax(sG[col][col], 0.0));
+    const double h = sqrt(sg);
+    M1[e] = sV[i][col] * h;
+    M2[e] = (h > 0.0) ? sV[i][col] / h : 0.0;
+    if (i == 0) sigma[k] = (float)sg;
+  }
+}
+
+// ---- out = X S (X [M, l] float32, S [l, c] float64), or its transpose --------
+// Workgroup: 16 rows of X staged in LDS; thread -> (row, column) pairs. The
+// rows are read into LDS before any output is written, so out may alias X
+// when c == l and the output is not transposed.
+__global__ __launch_bounds__(256) void k_right_mul(const float* X, int64_t M, int l,
+                                                   const double* __restrict__ S, int c,
+                                                   float* out, int transposed) {
+  __shared__ double sS[LR_MAXL * LR_MAXL];
+  __shared__ float sX[16][LR_MAXL + 1];
+  const int t = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  for (int e = t; e < l * c; e += 256) sS[e] = S[e];
+  for (int e = t; e < 16 * l; e += 256) {
+    const int rr = e / l, i = e % l;
+    const int64_t m = m0 + rr;
+    sX[rr][i] = (m < M) ? X[m * l + i] : 0.0f;
+  }
+  __syncthreads();
+  for (int e = t; e < 16 * c; e += 256) {
+    const int rr = e / c, j = e % c;
+    const int64_t m = m0 + rr;
+    if (m >= M) continue;
+    double v = 0.0;
+    for (int i = 0; i < l; ++i) v += (double)sX[rr][i] * sS[i * c + j];
+    if (transposed) out[(int64_t)j * M + m] = (float)v;
+    else out[m * c + j] = (float)v;
+  }
+}
+
+// ---- ||R - B A||_F^2: float64 partials per workgroup, fixed-order finish -----
+__global__ __launch_bounds__(256) void k_lowrank_sqerr(const float* __restrict__ R, int64_t N, int64_t K,
+                                                       const float* __restrict__ B, const float* __restrict__ A,
+                                                       int r, double* __restrict__ part) {
+  __shared__ double sW[4];
+  const int64_t quads = N * K / 4;
+  double acc = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (int64_t)gridDim.x * 256) {
+    const int64_t e = 4 * i;
+    const int64_t n = e / K, k = e - n * K;
+    double d[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int j = 0; j < r; ++j) {
+      const double b = (double)B[n * r + j];
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(A + (int64_t)j * K + k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] += b * (double)a[q];
+    }
+    const f32x4_t x = *reinterpret_cast<const f32x4_t*>(R + e);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double v = (double)x[q] - d[q];
+      acc += v * v;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) sW[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = ((sW[0] + sW[1]) + sW[2]) + sW[3];
+}
+
+__global__ __launch_bounds__(64) void k_sum_doubles(const double* __restrict__ part, int n, double* __restrict__ out) {
+  if (threadIdx.x == 0) {
+    double v = 0.0;
+    for (int i = 0; i < n; ++i) v += part[i];
+    *out = v;
+  }
+}
+
+static unsigned grid_for(int64_t items, int64_t per_wg, int64_t cap) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cap, (items + per_wg - 1) / per_wg));
+}
+
+constexpr int SKINNY_SPLITS = 8;
+constexpr int GRAM_PARTS = 64;
+constexpr int SQERR_WGS = 1024;
+
+}  // namespace
+
+int lowrank_max_l() { return LR_MAXL; }
+
+hipError_t launch_lowrank_sub(const float* W, int64_t N, int64_t K, const float* B, const float* A, int r,
+                              float* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_lowrank_sub, dim3(grid_for(N * K / 4, 256, 8192)), dim3(256), 0, s, W, N, K, B, A, r, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, hipStream_t s) {
+  hipLaunchKernelGGL(k_residual, dim3(grid_for(n / 4, 256, 8192)), dim3(256), 0, s, W, Wd, n, R);
+  return hipGetLastError();
+}
+
+// Workspace of the rank-r SVD, in floats: Y [N, l], Z [K, l], split partials
+// [S, max(N, K), l]; then float64: Gram partials, G, L, M1, M2.
+size_t svd_ws_bytes(int64_t N, int64_t K, int l, int r) {
+  const int64_t mx = std::max(N, K);
+  size_t f = (size_t)(N * l + K * l + (int64_t)SKINNY_SPLITS * mx * l);
+  f = (f + 1) & ~(size_t)1;   // float64 alignment
+  const size_t d = (size_t)GRAM_PARTS * l * l + 2 * (size_t)l * l + 2 * (size_t)l * r + SQERR_WGS;
+  return f * sizeof(float) + d * sizeof(double);
+}
+
+namespace {
+struct SvdWs {
+  float *Y, *Z, *part;
+  double *gpart, *G, *L, *M1, *M2, *sq;
+};
+SvdWs carve(void* ws, int64_t N, int64_t K, int l, int r) {
+  SvdWs w;
+  float* f = (float*)ws;
+  const int64_t mx = std::max(N, K);
+  w.Y = f; f += N * l;
+  w.Z = f; f += K * l;
+  w.part = f; f += (int64_t)SKINNY_SPLITS * mx * l;
+  size_t used = (size_t)(f - (float*)ws);
+  used = (used + 1) & ~(size_t)1;
+  double* d = (double*)((float*)ws + used);
+  w.gpart = d; d += (size_t)GRAM_PARTS * l * l;
+  w.G = d; d += (size_t)l * l;
+  w.L = d; d += (size_t)l * l;
+  w.M1 = d; d += (size_t)l * r;
+  w.M2 = d; d += (size_t)l * r;
+  w.sq = d;
+  return w;
+}
+
+#define LR_CHECK() do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
+
+// Y [M, l] <- orthonormal basis of its columns (CholQR twice)
+hipError_t orthonormalise(float* Y, int64_t M, int l, const SvdWs& w, hipStream_t s) {
+  const int parts = (int)std::min<int64_t>(GRAM_PARTS, (M + 31) / 32);
+  const int64_t rows = (M + parts - 1) / parts;
+  for (int pass = 0; pass < 2; ++pass) {
+    hipLaunchKernelGGL(k_gram_partial, dim3(parts), dim3(256), 0, s, Y, M, l, rows, w.gpart);
+    hipLaunchKernelGGL(k_gram_finish, dim3(grid_for(l * l, 256, 64)), dim3(256), 0, s, w.gpart, parts, l * l, w.G);
+    hipLaunchKernelGGL(k_cholesky_inv, dim3(1), dim3(256), 0, s, w.G, l, w.L);
+    hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, s, Y, M, l, w.L, l, Y, 0);
+    LR_CHECK();
+  }
+  return hipSuccess;
+}
+
+// Z [C, l] = X^T Q for X [M, C]
+hipError_t skinny_t(const float* X, int64_t M, int64_t C, const float* Q, int l, float* Z, const SvdWs& w,
+                    hipStream_t s) {
+  const int64_t rows = (M + SKINNY_SPLITS - 1) / SKINNY_SPLITS;
+  hipLaunchKernelGGL(k_skinny_t, dim3((unsigned)((C + 15) / 16), SKINNY_SPLITS), dim3(256), 0, s, X, M, C, Q, l,
+                     rows, w.part);
+  hipLaunchKernelGGL(k_sum_splits, dim3(grid_for(C * l, 256, 4096)), dim3(256), 0, s, w.part, SKINNY_SPLITS,
+                     C * l, Z);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_svd_lowrank(const float* R, int64_t N, int64_t K, int r, int l, int power_iters,
+                              const float* omega, float* B, float* A, float* sigma, void* ws, hipStream_t s) {
+  const SvdWs w = carve(ws, N, K, l, r);
+  hipError_t e;
+  hipLaunchKernelGGL(k_tall_skinny, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, R, N, K, omega, l, w.Y);
+  LR_CHECK();
+  if ((e = orthonormalise(w.Y, N, l, w, s)) != hipSuccess) return e;
+  for (int it = 0; it < power_iters; ++it) {
+    if ((e = skinny_t(R, N, K, w.Y, l, w.Z, w, s)) != hipSuccess) return e;
+    if ((e = orthonormalise(w.Z, K, l, w, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tall_skinny, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, R, N, K, w.Z, l, w.Y);
+    LR_CHECK();
+    if ((e = orthonormalise(w.Y, N, l, w, s)) != hipSuccess) return e;
+  }
+  // Rayleigh-Ritz: Z = R^T Y, eigen-decomposition of Z^T Z
+  if ((e = skinny_t(R, N, K, w.Y, l, w.Z, w, s)) != hipSuccess) return e;
+  const int parts = (int)std::min<int64_t>(GRAM_PARTS, (K + 31) / 32);
+  hipLaunchKernelGGL(k_gram_partial, dim3(parts), dim3(256), 0, s, w.Z, K, l, (K + parts - 1) / parts, w.gpart);
+  hipLaunchKernelGGL(k_gram_finish, dim3(grid_for(l * l, 256, 64)), dim3(256), 0, s, w.gpart, parts, l * l, w.G);
+  hipLaunchKernelGGL(k_jacobi_eig, dim3(1), dim3(1024), 0, s, w.G, l, r, w.M1, w.M2, sigma);
+  hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, w.Y, N, l, w.M1, r, B, 0);
+  hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((K + 15) / 16)), dim3(256), 0, s, w.Z, K, l, w.M2, r, A, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_sqerr(const float* R, int64_t N, int64_t K, const float* B, const float* A, int r,
+                                double* out, void* ws, hipStream_t s) {
+  double* part = (double*)ws;
+  const unsigned g = grid_for(N * K / 4, 256, SQERR_WGS);
+  hipLaunchKernelGGL(k_lowrank_sqerr, dim3(g), dim3(256), 0, s, R, N, K, B, A, r, part);
+  hipLaunchKernelGGL(k_sum_doubles, dim3(1), dim3(64), 0, s, part, (int)g, out);
+  return hipGetLastError();
+}
+
+size_t sqerr_ws_bytes() { return SQERR_WGS * sizeof(double); }
+
+namespace {
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+}  // namespace
+
+size_t loftq_ws_bytes(int64_t N, int64_t K, int r, int l, bool dq) {
+  const int64_t n = N * K;
+  size_t b = align256((size_t)n * sizeof(float)) + align256((size_t)n * sizeof(uint16_t));
+  if (dq) b += align256(double_quant_ws_doubles(n / 64) * sizeof(double));
+  b += align256(svd_ws_bytes(N, K, l, r)) + align256(sqerr_ws_bytes());
+  return b;
+}
+
+hipError_t launch_loftq(const float* W, int64_t N, int64_t K, bool dq, int r, int l, int steps, int power_iters,
+                        const float* omega, uint8_t* codes, float* absmax, uint8_t* absmax_q, float* dq_scale,
+                        float* dq_mean, float* B, float* A, float* sigma, double* objectives, void* ws,
+                        hipStream_t s) {
+  const int64_t n = N * K, n_blocks = n / 64;
+  char* p = (char*)ws;
+  float* Wt = (float*)p;               // W - B A, then the residual R
+  p += align256((size_t)n * sizeof(float));
+  uint16_t* Wd = (uint16_t*)p;         // the layer's bf16 weight
+  p += align256((size_t)n * sizeof(uint16_t));
+  double* dq_ws = (double*)p;
+  if (dq) p += align256(double_quant_ws_doubles(n_blocks) * sizeof(double));
+  void* svd_ws = p;
+  p += align256(svd_ws_bytes(N, K, l, r));
+  void* sq_ws = p;
+
+  hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(N * r, 256, 1024)), dim3(256), 0, s, B, N * (int64_t)r);
+  hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(K * r, 256, 1024)), dim3(256), 0, s, A, K * (int64_t)r);
+  LR_CHECK();
+  QWeight q{};
+  q.format = LQ_FMT_NF4;
+  q.N = N;
+  q.K = K;
+  q.codes = codes;
+  if (dq) q.qc = QConst{nullptr, absmax_q, dq_scale, dq_mean};
+  else q.qc = QConst{absmax, nullptr, nullptr, nullptr};
+  hipError_t e;
+  for (int t = 0; t < steps; ++t) {
+    const float* src = W;              // the adapter starts at zero
+    if (t > 0) {
+      if ((e = launch_lowrank_sub(W, N, K, B, A, r, Wt, s)) != hipSuccess) return e;
+      src = Wt;
+    }
+    if ((e = launch_quantize_nf4(src, LQ_F32, n_blocks, codes, absmax, s)) != hipSuccess) return e;
+    if (dq && (e = launch_double_quant(absmax, n_blocks, absmax_q, dq_scale, dq_mean, dq_ws, s)) != hipSuccess)
+      return e;
+    if ((e = launch_dequant(q, Wd, s)) != hipSuccess) return e;
+    if ((e = launch_residual(W, Wd, n, Wt, s)) != hipSuccess) return e;
+    if ((e = launch_svd_lowrank(Wt, N, K, r, l, power_iters, omega, B, A, sigma, svd_ws, s)) != hipSuccess) return e;
+    if (objectives && (e = launch_lowrank_sqerr(Wt, N, K, B, A, r, objectives + t, sq_ws, s)) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace lq

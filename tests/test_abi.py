@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 22
+    assert len(names) == 28
     for name in names:
         assert hasattr(lq.lib, name), name
         assert name in lq.SIGNATURES, name
@@ -190,6 +190,54 @@ def test_validation_errors_without_launch(lq):
     assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_UNSUPPORTED
     a = list(largs); a[3] = 16384 + 64
     assert L.lq_lloyd_codebooks(*a) == lq.LQ_ERR_UNSUPPORTED
+
+
+def test_lowrank_validation(lq):
+    """Low-rank initialisation entry points: argument checks before any launch."""
+    L = lq.lib
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(None)
+    assert L.lq_lowrank_sub(null, 4, 64, fake, fake, 2, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_lowrank_sub(fake, 4, 64, null, fake, 2, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_lowrank_sub(fake, 4, 66, fake, fake, 2, fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_lowrank_sub(fake, 4, 64, fake, fake, 129, fake, null) == lq.LQ_ERR_SHAPE
+    assert L.lq_residual(fake, null, 64, fake, null) == lq.LQ_ERR_ARG
+    assert L.lq_residual(fake, fake, 62, fake, null) == lq.LQ_ERR_SHAPE
+
+    # l even, r <= l <= min(N, K, 96)
+    assert L.lq_svd_lowrank_workspace(256, 512, 16, 32) > 0
+    for (N, K, r, l) in ((256, 512, 16, 15), (256, 512, 16, 33), (256, 512, 0, 32), (16, 512, 8, 32),
+                         (256, 24, 8, 32)):
+        assert L.lq_svd_lowrank_workspace(N, K, r, l) == 0
+    ws = L.lq_svd_lowrank_workspace(256, 512, 16, 32)
+    sargs = [fake, 256, 512, 16, 32, 8, fake, fake, fake, fake, fake, ws, null]
+    s1 = list(sargs); s1[6] = null
+    assert L.lq_svd_lowrank(*s1) == lq.LQ_ERR_ARG
+    s2 = list(sargs); s2[4] = 98
+    assert L.lq_svd_lowrank(*s2) == lq.LQ_ERR_UNSUPPORTED
+    s3 = list(sargs); s3[4] = 8
+    assert L.lq_svd_lowrank(*s3) == lq.LQ_ERR_SHAPE        # l < r
+    s4 = list(sargs); s4[5] = -1
+    assert L.lq_svd_lowrank(*s4) == lq.LQ_ERR_ARG
+    s5 = list(sargs); s5[11] = ws - 1
+    assert L.lq_svd_lowrank(*s5) == lq.LQ_ERR_WORKSPACE
+
+    wl = L.lq_loftq_workspace(256, 512, 16, 32, 1)
+    assert wl > ws + 256 * 512 * 6
+    assert L.lq_loftq_workspace(256, 500, 16, 32, 1) == 0   # K % 64
+    largs = [fake, 256, 512, 64, 1, 16, 32, 5, 8, fake, fake, fake, fake, fake, fake, fake, fake, fake, null,
+             fake, wl, null]
+    l1 = list(largs); l1[12] = null                         # double quant needs its outputs
+    assert L.lq_loftq_init(*l1) == lq.LQ_ERR_ARG
+    # without double quant the DQ outputs may be NULL (then only the workspace check is left)
+    l2 = list(largs); l2[4] = 0; l2[12] = null; l2[13] = null; l2[14] = null; l2[20] = 1
+    assert L.lq_loftq_init(*l2) == lq.LQ_ERR_WORKSPACE
+    l3 = list(largs); l3[7] = 0
+    assert L.lq_loftq_init(*l3) == lq.LQ_ERR_ARG
+    l4 = list(largs); l4[3] = 32
+    assert L.lq_loftq_init(*l4) == lq.LQ_ERR_UNSUPPORTED
+    l5 = list(largs); l5[20] = wl - 1
+    assert L.lq_loftq_init(*l5) == lq.LQ_ERR_WORKSPACE
 
 
 def test_workspace_queries_deterministic(lq):
