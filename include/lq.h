@@ -384,7 +384,7 @@ int lq_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, void* s
 size_t lq_svd_lowrank_workspace(int64_t N, int64_t K, int32_t r, int32_t l);
 
 /*
- * Rank-r SVD of R [N, K] (float32, row-major), split evenly between the
+ * Rank-r SVD of R [N, K] (float32, row-major, 16-byte aligned, K % 4 == 0), split evenly between the
  * factors: B = U_r S_r^(1/2) [N, r], A = S_r^(1/2) V_r^T [r, K], sigma = the r
  * largest singular values [r], so that B A approximates the best rank-r
  * approximation of R. Computed by randomized subspace iteration on l >= r

@@ -338,7 +338,7 @@ int lq_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, void* s
 }
 
 static int check_svd_shape(int64_t N, int64_t K, int32_t r, int32_t l, int32_t power_iters) {
-  if (N <= 0 || K <= 0 || r < 1 || l < r || l % 2 != 0 || l > N || l > K) return LQ_ERR_SHAPE;
+  if (N <= 0 || K <= 0 || K % 4 != 0 || r < 1 || l < r || l % 2 != 0 || l > N || l > K) return LQ_ERR_SHAPE;
   if (l > lowrank_max_l()) return LQ_ERR_UNSUPPORTED;
   if (power_iters < 0 || power_iters > 1000) return LQ_ERR_ARG;
   return LQ_OK;

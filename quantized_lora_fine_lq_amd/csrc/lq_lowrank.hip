@@ -6,7 +6,7 @@
 //   * W - B A with the rank-r product summed in float64 in order of j;
 //   * R = W - W' (W' the layer's bf16 weight);
 //   * the rank-r SVD of R by randomized subspace iteration: Y = R Omega, then
-//     power steps Z = R^T Y, Y = R Z, each block orthonormalised by CholQR2
+//     power steps Y = R (R^T Y), each new Y orthonormalised by CholQR2
 //     (float64 Gram, Cholesky and the inverse of its factor in one workgroup,
 //     then a right multiply); a final Rayleigh-Ritz step takes the
 //     eigenvectors of the l x l Gram of R^T Y by cyclic Jacobi in float64 in
@@ -62,95 +62,91 @@ __global__ __launch_bounds__(256) void k_residual(const float* __restrict__ W, c
   }
 }
 
-// ---- Y[M, l] = X[M, C] V[C, l] (float32; X row-major, V row-major) --------
-// Workgroup: 16 rows of X and all l columns; the contraction in chunks of 64
-// staged in LDS. Thread t: row t % 16, columns (t / 16) + 16 c.
-__global__ __launch_bounds__(256) void k_tall_skinny(const float* __restrict__ X, int64_t M, int64_t C,
-                                                     const float* __restrict__ V, int l, float* __restrict__ Y) {
-  __shared__ float sX[16][65];
-  __shared__ float sV[64][LR_MAXL];
+// ---- tall-skinny products, split over the contraction -----------------------
+// TRANS = false: Y[M, l] = X[M, C] V[C, l]   (contraction over C)
+// TRANS = true:  Z[C, l] = X[M, C]^T V[M, l] (contraction over M)
+// X row-major [M, C] with C % 4 == 0. Workgroup: 128 output rows x all l
+// columns over one slice of the contraction (partials [slices, rows_out, l]).
+// Tiles are k-major in LDS (32 x 128 of X, 32 x LP of V, LP = l rounded up
+// to 32); thread t computes rows 4 (t % 32) .. +3 and TN = LP / 8 columns
+// TN (t / 32) .. +TN - 1, reading both operands as 16-byte LDS words.
+template <bool TRANS, int TN>
+__global__ __launch_bounds__(256) void k_skinny_gemm(const float* __restrict__ X, int64_t M, int64_t C,
+                                                     const float* __restrict__ V, int l, int64_t kslice,
+                                                     float* __restrict__ part) {
+  constexpr int BM = 128, BK = 32, LP = 8 * TN;
+  __shared__ __attribute__((aligned(16))) float sA[BK][BM + 4];
+  __shared__ __attribute__((aligned(16))) float sV[BK][LP + 4];
   const int t = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int row = t & 15, cg = t >> 4;
-  float acc[LR_MAXL / 16];
+  const int64_t rows_out = TRANS ? C : M, kc = TRANS ? M : C;
+  const int64_t o0 = (int64_t)blockIdx.x * BM;
+  const int64_t kb = (int64_t)blockIdx.y * kslice, ke = std::min<int64_t>(kc, kb + kslice);
+  const int rg = t & 31, cg = t >> 5;
+  float acc[4][TN];
 #pragma unroll
-  for (int c = 0; c < LR_MAXL / 16; ++c) acc[c] = 0.0f;
-  for (int64_t c0 = 0; c0 < C; c0 += 64) {
-    for (int i = t; i < 16 * 64; i += 256) {
-      const int rr = i >> 6, cc = i & 63;
-      const int64_t m = m0 + rr, col = c0 + cc;
-      sX[rr][cc] = (m < M && col < C) ? X[m * C + col] : 0.0f;
-    }
-    for (int i = t; i < 64 * l; i += 256) {
-      const int rr = i / l, cc = i - rr * l;
-      const int64_t col = c0 + rr;
-      sV[rr][cc] = (col < C) ? V[col * l + cc] : 0.0f;
-    }
-    __syncthreads();
-    for (int kk = 0; kk < 64; ++kk) {
-      const float x = sX[row][kk];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < LR_MAXL / 16; ++c) {
-        const int col = cg + 16 * c;
-        if (col < l) acc[c] = __builtin_fmaf(x, sV[kk][col], acc[c]);
+    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+  for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+    if (!TRANS) {
+      // rows o0 + t/2, contraction k0 + 16 (t % 2) .. +15, stored transposed
+      const int o = t >> 1, kq = (t & 1) * 16;
+      const int64_t row = o0 + o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t k = k0 + kq + 4 * q;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (row < M && k + 4 <= ke) v = *reinterpret_cast<const f32x4_t*>(X + row * C + k);
+        else if (row < M)
+          for (int e = 0; e < 4; ++e) v[e] = (k + e < ke) ? X[row * C + k + e] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sA[kq + 4 * q + e][o] = v[e];
+      }
+    } else {
+      // contraction rows k0 + t/8, output columns o0 + 16 (t % 8) .. +15
+      const int kk = t >> 3, oq = (t & 7) * 16;
+      const int64_t krow = k0 + kk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t o = o0 + oq + 4 * q;
+        f32x4_t v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (krow < ke && o + 4 <= C) v = *reinterpret_cast<const f32x4_t*>(X + krow * C + o);
+        else if (krow < ke)
+          for (int e = 0; e < 4; ++e) v[e] = (o + e < C) ? X[krow * C + o + e] : 0.0f;
+        *reinterpret_cast<f32x4_t*>(&sA[kk][oq + 4 * q]) = v;
       }
     }
-    __syncthreads();
-  }
-  const int64_t m = m0 + row;
-  if (m < M) {
-#pragma unroll
-    for (int c = 0; c < LR_MAXL / 16; ++c) {
-      const int col = cg + 16 * c;
-      if (col < l) Y[m * l + col] = acc[c];
-    }
-  }
-}
-
-// ---- part[s][C, l] = sum over rows m of split s of X[m][c] Q[m][:] ---------
-// (Z = X^T Q with X [M, C] row-major.) Workgroup: 16 columns c of X, rows of
-// one split in chunks of 64. Thread t: column t % 16, outputs (t / 16) + 16 j.
-__global__ __launch_bounds__(256) void k_skinny_t(const float* __restrict__ X, int64_t M, int64_t C,
-                                                  const float* __restrict__ Q, int l, int64_t rows_per_split,
-                                                  float* __restrict__ part) {
-  __shared__ float sX[64][17];
-  __shared__ float sQ[64][LR_MAXL];
-  const int t = threadIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.x * 16;
-  const int s = blockIdx.y;
-  const int64_t mb = (int64_t)s * rows_per_split, me = std::min<int64_t>(M, mb + rows_per_split);
-  const int col = t & 15, cg = t >> 4;
-  float acc[LR_MAXL / 16];
-#pragma unroll
-  for (int j = 0; j < LR_MAXL / 16; ++j) acc[j] = 0.0f;
-  for (int64_t m0 = mb; m0 < me; m0 += 64) {
-    for (int i = t; i < 64 * 16; i += 256) {
-      const int rr = i >> 4, cc = i & 15;
-      const int64_t m = m0 + rr, c = c0 + cc;
-      sX[rr][cc] = (m < me && c < C) ? X[m * C + c] : 0.0f;
-    }
-    for (int i = t; i < 64 * l; i += 256) {
-      const int rr = i / l, cc = i - rr * l;
-      const int64_t m = m0 + rr;
-      sQ[rr][cc] = (m < me) ? Q[m * l + cc] : 0.0f;
+    for (int i = t; i < BK * LP; i += 256) {
+      const int kk = i / LP, c = i % LP;   // LP is a compile-time constant
+      const int64_t k = k0 + kk;
+      sV[kk][c] = (k < ke && c < l) ? V[k * l + c] : 0.0f;
     }
     __syncthreads();
-    for (int mm = 0; mm < 64; ++mm) {
-      const float x = sX[mm][col];
+#pragma unroll 4
+    for (int kk = 0; kk < BK; ++kk) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&sA[kk][4 * rg]);
+      float v[TN];
 #pragma unroll
-      for (int j = 0; j < LR_MAXL / 16; ++j) {
-        const int q = cg + 16 * j;
-        if (q < l) acc[j] = __builtin_fmaf(x, sQ[mm][q], acc[j]);
+      for (int j4 = 0; j4 < TN / 4; ++j4) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t*>(&sV[kk][TN * cg + 4 * j4]);
+        v[4 * j4] = w[0]; v[4 * j4 + 1] = w[1]; v[4 * j4 + 2] = w[2]; v[4 * j4 + 3] = w[3];
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], v[j], acc[i][j]);
     }
     __syncthreads();
   }
-  const int64_t c = c0 + col;
-  if (c < C) {
+  float* dst = part + (int64_t)blockIdx.y * rows_out * l;
 #pragma unroll
-    for (int j = 0; j < LR_MAXL / 16; ++j) {
-      const int q = cg + 16 * j;
-      if (q < l) part[((int64_t)s * C + c) * l + q] = acc[j];
+  for (int i = 0; i < 4; ++i) {
+    const int64_t o = o0 + 4 * rg + i;
+    if (o >= rows_out) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = TN * cg + j;
+      if (c < l) dst[o * l + c] = acc[i][j];
     }
   }
 }
@@ -206,28 +202,39 @@ __global__ __launch_bounds__(256) void k_gram_finish(const double* __restrict__ 
                                                      double* __restrict__ G) {
   for (int e = blockIdx.x * 256 + threadIdx.x; e < ll; e += gridDim.x * 256) {
     double v = 0.0;
-    for (int s = 0; s < parts; ++s) v += part[(int64_t)s * ll + e];
+    for (int s0 = 0; s0 < parts; s0 += 16) {   // 16 loads in flight, summed in order
+      double x[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x[u] = (s0 + u < parts) ? part[(int64_t)(s0 + u) * ll + e] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v += x[u];
+    }
     G[e] = v;
   }
 }
 
 // ---- Cholesky G = L L^T and T = L^{-T} in one workgroup (float64) ----------
-// Q = Y T then has orthonormal columns (up to rounding). A pivot at or below
+// Q = Y T then has orthonormal columns (up to rounding). Column step j: every
+// thread forms the pivot d = A[j][j] itself; the trailing update uses the
+// unscaled column, A[i][k] -= A[i][j] A[k][j] / d, and L's column j goes to a
+// separate array, so one barrier per step suffices. A pivot at or below
 // 1e-28 of the largest diagonal marks a column that depends on the earlier
-// ones: its column of L and its row of L^{-1} are set to zero, so that Q gets
-// a zero column there.
+// ones: its column of L and its row of L^{-1} are zero, so that Q gets a
+// zero column there. L^{-1} by forward substitution, one row at a time, each
+// column's dot product split over TPC threads.
 __global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__ G, int l, double* __restrict__ T) {
   __shared__ double sA[LR_MAXL][LR_MAXL + 1];
-  __shared__ double sI[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sL[LR_MAXL][LR_MAXL + 1];
   __shared__ double sRed[4];
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   double m = 0.0;
-  for (int e = t; e < l * l; e += 256) {
-    const int i = e / l, k = e % l;
-    const double v = G[e];
-    sA[i][k] = v;
-    if (i == k) m = fmax(m, v);
-  }
+  for (int i = ty; i < l; i += 16)
+    for (int k = tx; k < l; k += 16) {
+      const double v = G[i * l + k];
+      sA[i][k] = v;
+      sL[i][k] = 0.0;
+      if (i == k) m = fmax(m, v);
+    }
   for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if ((t & 63) == 0) sRed[t >> 6] = m;
   __syncthreads();
@@ -236,43 +243,50 @@ __global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__
     const double d = sA[j][j];
     const bool ok = d > tol && d > 0.0;
     const double piv = ok ? sqrt(d) : 0.0;
-    __syncthreads();
-    for (int i = j + 1 + t; i < l; i += 256) sA[i][j] = ok ? sA[i][j] / piv : 0.0;
-    if (t == 0) sA[j][j] = piv;
-    __syncthreads();
-    const int n = l - j - 1;
-    for (int e = t; e < n * n; e += 256) {
-      const int i = j + 1 + e / n, k = j + 1 + e % n;
-      if (k <= i) sA[i][k] -= sA[i][j] * sA[k][j];
+    const double inv_d = ok ? 1.0 / d : 0.0;
+    // L's column j (from the unchanged column of A)
+    if (ty == 0)
+      for (int i = j + tx; i < l; i += 16) sL[i][j] = ok ? ((i == j) ? piv : sA[i][j] / piv) : 0.0;
+    // trailing update of the lower triangle
+    for (int i = j + 1 + ty; i < l; i += 16) {
+      const double aij = sA[i][j] * inv_d;
+      for (int k = j + 1 + tx; k <= i; k += 16) sA[i][k] -= aij * sA[k][j];
     }
     __syncthreads();
   }
-  // L^{-1} by forward substitution, row i at a time, all columns c <= i at once
+  // L^{-1}: row i from rows < i; column c's dot product over k in [c, i)
+  // split over the 16 threads of a row group (tx), reduced by shuffles
+  double* sI = &sA[0][0];   // reuse: sI[i * (LR_MAXL + 1) + c]
+  constexpr int P = LR_MAXL + 1;
+  for (int e = t; e < LR_MAXL * P; e += 256) sI[e] = 0.0;
+  __syncthreads();
   for (int i = 0; i < l; ++i) {
-    const double d = sA[i][i];
-    for (int c = t; c <= i; c += 256) {
-      double v = (c == i) ? 1.0 : 0.0;
-      for (int k = c; k < i; ++k) v -= sA[i][k] * sI[k][c];
-      sI[i][c] = (d > 0.0) ? v / d : 0.0;
+    const double d = sL[i][i];
+    for (int c = ty; c <= i; c += 16) {
+      double v = 0.0;
+      for (int k = c + tx; k < i; k += 16) v += sL[i][k] * sI[k * P + c];
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      if (tx == 0) sI[i * P + c] = (d > 0.0) ? (((c == i) ? 1.0 : 0.0) - v) / d : 0.0;
     }
     __syncthreads();
   }
   // T[k][j] = L^{-1}[j][k] (upper triangular)
-  for (int e = t; e < l * l; e += 256) {
-    const int k = e / l, j = e % l;
-    T[e] = (k <= j) ? sI[j][k] : 0.0;
-  }
+  for (int k = ty; k < l; k += 16)
+    for (int j = tx; j < l; j += 16) T[k * l + j] = (k <= j) ? sI[j * P + k] : 0.0;
 }
 
 // ---- symmetric eigen-decomposition by cyclic Jacobi (one workgroup) ---------
 // Round-robin pairing: in each of the l - 1 rounds of a sweep every index is
 // in exactly one pair, so the rotations of a round commute; G <- J^T G J is
 // applied as a column pass then a row pass. Sweeps stop when the squared
-// off-diagonal mass is below 1e-30 of the total or after 30 sweeps. Then
+// off-diagonal mass is below 1e-26 of the total (1e-13 in norm) or after 30 sweeps. Then
 // the top r eigenpairs (descending, ties by index) give
 //   M1[:, i] = u_i sqrt(sigma_i), M2[:, i] = u_i / sqrt(sigma_i) (0 if sigma_i = 0),
 // with sigma_i = sqrt(max(lambda_i, 0)).
-__global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ Gin, int l, int r,
+__global__ __launch_bounds__(256) void k_jacobi_eig(const double* __restrict__ Gin, int l, int r,
                                                      double* __restrict__ M1, double* __restrict__ M2,
                                                      float* __restrict__ sigma) {
   __shared__ double sG[LR_MAXL][LR_MAXL + 1];
@@ -280,10 +294,10 @@ __global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ 
   __shared__ double sC[LR_MAXL / 2], sS[LR_MAXL / 2];
   __shared__ int sP[LR_MAXL / 2], sQ[LR_MAXL / 2];
   __shared__ int sOrder[LR_MAXL];
-  __shared__ double sOff, sTot, sRedO[16], sRedT[16];
+  __shared__ double sOff, sTot, sRedO[4], sRedT[4];
   const int t = threadIdx.x;
   const int n = l;   // even (l % 8 == 0)
-  for (int e = t; e < n * n; e += 1024) {
+  for (int e = t; e < n * n; e += 256) {
     const int i = e / n, j = e % n;
     sG[i][j] = Gin[e];
     sV[i][j] = (i == j) ? 1.0 : 0.0;
@@ -292,12 +306,12 @@ __global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ 
   for (int sweep = 0; sweep < 30; ++sweep) {
     {
       double off = 0.0, tot = 0.0;
-      for (int e = t; e < n * n; e += 1024) {
-        const int i = e / n, j = e % n;
-        const double v = sG[i][j] * sG[i][j];
-        tot += v;
-        if (i != j) off += v;
-      }
+      for (int i = t >> 4; i < n; i += 16)
+        for (int j = t & 15; j < n; j += 16) {
+          const double v = sG[i][j] * sG[i][j];
+          tot += v;
+          if (i != j) off += v;
+        }
       for (int o = 32; o > 0; o >>= 1) {
         off += __shfl_xor(off, o);
         tot += __shfl_xor(tot, o);
@@ -305,19 +319,17 @@ __global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ 
       if ((t & 63) == 0) { sRedO[t >> 6] = off; sRedT[t >> 6] = tot; }
       __syncthreads();
       if (t == 0) {
-        double a = 0.0, b = 0.0;
-        for (int w = 0; w < 16; ++w) { a += sRedO[w]; b += sRedT[w]; }
-        sOff = a;
-        sTot = b;
+        sOff = ((sRedO[0] + sRedO[1]) + sRedO[2]) + sRedO[3];
+        sTot = ((sRedT[0] + sRedT[1]) + sRedT[2]) + sRedT[3];
       }
       __syncthreads();
     }
-    if (!(sOff > 1e-30 * sTot)) break;
+    if (!(sOff > 1e-26 * sTot)) break;
     for (int round = 0; round < n - 1; ++round) {
       // pairs of the round-robin schedule: slot 0 fixed, the rest rotate
-      if (t < n / 2) {
+      for (int pi = t; pi < n / 2; pi += 256) {
         auto slot = [&](int s) { return s == 0 ? 0 : 1 + (s - 1 + round) % (n - 1); };
-        int p = slot(t), q = slot(n - 1 - t);
+        int p = slot(pi), q = slot(n - 1 - pi);
         if (p > q) { const int tmp = p; p = q; q = tmp; }
         const double apq = sG[p][q], app = sG[p][p], aqq = sG[q][q];
         double c = 1.0, s = 0.0;
@@ -327,46 +339,48 @@ __global__ __launch_bounds__(1024) void k_jacobi_eig(const double* __restrict__ 
           c = 1.0 / sqrt(tt * tt + 1.0);
           s = tt * c;
         }
-        sP[t] = p; sQ[t] = q; sC[t] = c; sS[t] = s;
+        sP[pi] = p; sQ[pi] = q; sC[pi] = c; sS[pi] = s;
       }
       __syncthreads();
       // columns: G <- G J, V <- V J
-      for (int e = t; e < (n / 2) * n; e += 1024) {
-        const int pi = e / n, i = e % n;
+      for (int pi = t >> 4; pi < n / 2; pi += 16) {
         const int p = sP[pi], q = sQ[pi];
         const double c = sC[pi], s = sS[pi];
+        for (int i = t & 15; i < n; i += 16) {
         const double gp = sG[i][p], gq = sG[i][q];
         sG[i][p] = c * gp - s * gq;
         sG[i][q] = s * gp + c * gq;
         const double vp = sV[i][p], vq = sV[i][q];
         sV[i][p] = c * vp - s * vq;
         sV[i][q] = s * vp + c * vq;
+        }
       }
       __syncthreads();
       // rows: G <- J^T G
-      for (int e = t; e < (n / 2) * n; e += 1024) {
-        const int pi = e / n, j = e % n;
+      for (int pi = t >> 4; pi < n / 2; pi += 16) {
         const int p = sP[pi], q = sQ[pi];
         const double c = sC[pi], s = sS[pi];
-        const double gp = sG[p][j], gq = sG[q][j];
-        sG[p][j] = c * gp - s * gq;
-        sG[q][j] = s * gp + c * gq;
+        for (int j = t & 15; j < n; j += 16) {
+          const double gp = sG[p][j], gq = sG[q][j];
+          sG[p][j] = c * gp - s * gq;
+          sG[q][j] = s * gp + c * gq;
+        }
       }
       __syncthreads();
     }
   }
   // rank of each eigenvalue (descending, ties by index)
-  if (t < n) {
-    const double lt = sG[t][t];
+  for (int i = t; i < n; i += 256) {
+    const double lt = sG[i][i];
     int rank = 0;
     for (int j = 0; j < n; ++j) {
       const double lj = sG[j][j];
-      rank += (lj > lt || (lj == lt && j < t)) ? 1 : 0;
+      rank += (lj > lt || (lj == lt && j < i)) ? 1 : 0;
     }
-    sOrder[rank] = t;
+    sOrder[rank] = i;
   }
   __syncthreads();
-  for (int e = t; e < n * r; e += 1024) {
+  for (int e = t; e < n * r; e += 256) {
     const int i = e / r, k = e % r;
     const int col = sOrder[k];
     const double sg = sqrt(fmax(sG[col][col], 0.0));
@@ -448,7 +462,7 @@ static unsigned grid_for(int64_t items, int64_t per_wg, int64_t cap) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(cap, (items + per_wg - 1) / per_wg));
 }
 
-constexpr int SKINNY_SPLITS = 8;
+constexpr int SKINNY_SPLITS = 16;   // most contraction slices of a tall-skinny product
 constexpr int GRAM_PARTS = 64;
 constexpr int SQERR_WGS = 1024;
 
@@ -517,14 +531,36 @@ hipError_t orthonormalise(float* Y, int64_t M, int l, const SvdWs& w, hipStream_
   return hipSuccess;
 }
 
-// Z [C, l] = X^T Q for X [M, C]
-hipError_t skinny_t(const float* X, int64_t M, int64_t C, const float* Q, int l, float* Z, const SvdWs& w,
-                    hipStream_t s) {
-  const int64_t rows = (M + SKINNY_SPLITS - 1) / SKINNY_SPLITS;
-  hipLaunchKernelGGL(k_skinny_t, dim3((unsigned)((C + 15) / 16), SKINNY_SPLITS), dim3(256), 0, s, X, M, C, Q, l,
-                     rows, w.part);
-  hipLaunchKernelGGL(k_sum_splits, dim3(grid_for(C * l, 256, 4096)), dim3(256), 0, s, w.part, SKINNY_SPLITS,
-                     C * l, Z);
+template <bool TRANS, int TN>
+void launch_skinny_tn(const float* X, int64_t M, int64_t C, const float* V, int l, int64_t kslice, int slices,
+                      float* part, hipStream_t s) {
+  const int64_t rows_out = TRANS ? C : M;
+  const dim3 grid((unsigned)((rows_out + 127) / 128), (unsigned)slices);
+  hipLaunchKernelGGL((k_skinny_gemm<TRANS, TN>), grid, dim3(256), 0, s, X, M, C, V, l, kslice, part);
+}
+
+// out = X V (trans = false, [M, l]) or X^T V (trans = true, [C, l]) for X [M, C]:
+// enough contraction slices for about 512 workgroups, summed in a fixed order.
+hipError_t skinny(const float* X, int64_t M, int64_t C, const float* V, int l, bool trans, float* out,
+                  const SvdWs& w, hipStream_t s) {
+  const int64_t rows_out = trans ? C : M, kc = trans ? M : C;
+  const int64_t tiles = (rows_out + 127) / 128;
+  int slices = (int)std::min<int64_t>(SKINNY_SPLITS, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+  int64_t kslice = (kc + slices - 1) / slices;
+  kslice = (kslice + 31) / 32 * 32;
+  slices = (int)((kc + kslice - 1) / kslice);
+  const int tn = ((l + 31) / 32) * 4;
+  if (trans) {
+    if (tn == 4) launch_skinny_tn<true, 4>(X, M, C, V, l, kslice, slices, w.part, s);
+    else if (tn == 8) launch_skinny_tn<true, 8>(X, M, C, V, l, kslice, slices, w.part, s);
+    else launch_skinny_tn<true, 12>(X, M, C, V, l, kslice, slices, w.part, s);
+  } else {
+    if (tn == 4) launch_skinny_tn<false, 4>(X, M, C, V, l, kslice, slices, w.part, s);
+    else if (tn == 8) launch_skinny_tn<false, 8>(X, M, C, V, l, kslice, slices, w.part, s);
+    else launch_skinny_tn<false, 12>(X, M, C, V, l, kslice, slices, w.part, s);
+  }
+  hipLaunchKernelGGL(k_sum_splits, dim3(grid_for(rows_out * l, 256, 4096)), dim3(256), 0, s, w.part, slices,
+                     rows_out * l, out);
   return hipGetLastError();
 }
 }  // namespace
@@ -533,22 +569,21 @@ hipError_t launch_svd_lowrank(const float* R, int64_t N, int64_t K, int r, int l
                               const float* omega, float* B, float* A, float* sigma, void* ws, hipStream_t s) {
   const SvdWs w = carve(ws, N, K, l, r);
   hipError_t e;
-  hipLaunchKernelGGL(k_tall_skinny, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, R, N, K, omega, l, w.Y);
-  LR_CHECK();
+  if ((e = skinny(R, N, K, omega, l, false, w.Y, w, s)) != hipSuccess) return e;
   if ((e = orthonormalise(w.Y, N, l, w, s)) != hipSuccess) return e;
   for (int it = 0; it < power_iters; ++it) {
-    if ((e = skinny_t(R, N, K, w.Y, l, w.Z, w, s)) != hipSuccess) return e;
-    if ((e = orthonormalise(w.Z, K, l, w, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_tall_skinny, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, R, N, K, w.Z, l, w.Y);
-    LR_CHECK();
+    // Y <- orth(R R^T Y): the float64 Gram of CholQR (applied twice) takes the
+    // squared condition number of R R^T Y
+    if ((e = skinny(R, N, K, w.Y, l, true, w.Z, w, s)) != hipSuccess) return e;
+    if ((e = skinny(R, N, K, w.Z, l, false, w.Y, w, s)) != hipSuccess) return e;
     if ((e = orthonormalise(w.Y, N, l, w, s)) != hipSuccess) return e;
   }
   // Rayleigh-Ritz: Z = R^T Y, eigen-decomposition of Z^T Z
-  if ((e = skinny_t(R, N, K, w.Y, l, w.Z, w, s)) != hipSuccess) return e;
+  if ((e = skinny(R, N, K, w.Y, l, true, w.Z, w, s)) != hipSuccess) return e;
   const int parts = (int)std::min<int64_t>(GRAM_PARTS, (K + 31) / 32);
   hipLaunchKernelGGL(k_gram_partial, dim3(parts), dim3(256), 0, s, w.Z, K, l, (K + parts - 1) / parts, w.gpart);
   hipLaunchKernelGGL(k_gram_finish, dim3(grid_for(l * l, 256, 64)), dim3(256), 0, s, w.gpart, parts, l * l, w.G);
-  hipLaunchKernelGGL(k_jacobi_eig, dim3(1), dim3(1024), 0, s, w.G, l, r, w.M1, w.M2, sigma);
+  hipLaunchKernelGGL(k_jacobi_eig, dim3(1), dim3(256), 0, s, w.G, l, r, w.M1, w.M2, sigma);
   hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((N + 15) / 16)), dim3(256), 0, s, w.Y, N, l, w.M1, r, B, 0);
   hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((K + 15) / 16)), dim3(256), 0, s, w.Z, K, l, w.M2, r, A, 1);
   return hipGetLastError();
