@@ -223,6 +223,24 @@ def codec_bytes(L, M=0):
     }
 
 
+def loftq_bytes(L, r, q, steps):
+    """Algorithmic bytes of the LoftQ-style initialisation: per alternation,
+    W - B A (read W, write it; skipped in the first), NF4 quantize + double
+    quant + dequant, the residual (read W and W', write R), the rank-r SVD
+    (2 q + 3 passes over R for the tall-skinny products) and the error sum
+    (one more pass); the small l x l work is not counted."""
+    n = L.N * L.K
+    n_b = n // 64
+    quant = 4 * n + n // 2 + 4 * n_b
+    dqb = 4 * n_b + n_b + 4 * ((n_b + 255) // 256) + 4
+    deq = n // 2 + n_b + 2 * n
+    resid = 4 * n + 2 * n + 4 * n
+    svd = (2 * q + 3) * 4 * n
+    sq = 4 * n
+    per = quant + dqb + deq + resid + svd + sq
+    return steps * per + (steps - 1) * 8 * n
+
+
 def lowra_bytes(syn, L):
     """Algorithmic bytes of the per-channel codebook kernels: the learner reads
     W and writes levels, thresholds and iteration counts; the quantizer reads
@@ -380,6 +398,27 @@ def main():
             c.lora_down()
         rec("q_proj.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in calls], 50), fl["fwd_gemm"], "TFLOP/s")
         rec("q_proj.backward", time_ms(torch, [c.backward for c in calls], 30), fl["bwd"], "TFLOP/s")
+
+        # LoftQ-style initialisation of the q_proj adapter (r = 16, l = 32, 8 power steps, 5 alternations)
+        r_lq, l_lq, q_lq, t_lq = L.r, 2 * L.r, 8, 5
+        d0 = devs[0]
+        om = torch.from_numpy(np.random.default_rng(1).standard_normal((L.K, l_lq)).astype(np.float32)).cuda()
+        Bq = torch.empty(L.N, r_lq, dtype=torch.float32, device="cuda")
+        Aq = torch.empty(r_lq, L.K, dtype=torch.float32, device="cuda")
+        sg = torch.empty(r_lq, dtype=torch.float32, device="cuda")
+        ob = torch.empty(t_lq, dtype=torch.float64, device="cuda")
+        lws_b = lq.lib.lq_loftq_workspace(L.N, L.K, r_lq, l_lq, 1)
+        lws = torch.empty(lws_b, dtype=torch.uint8, device="cuda")
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+        def loftq():
+            if lq.lib.lq_loftq_init(P(d0.W), L.N, L.K, 64, 1, r_lq, l_lq, t_lq, q_lq, P(om), P(d0.codes), P(d0.absmax),
+                                    P(d0.aq), P(d0.s2), P(d0.mu), P(Bq), P(Aq), P(sg), P(ob), P(lws), lws_b, st) != 0:
+                raise RuntimeError("lq_loftq_init failed")
+        rec("q_proj.loftq_init", time_ms(torch, [loftq], 3, warmup=1), loftq_bytes(L, r_lq, q_lq, t_lq), "GB/s")
+        kernels["q_proj.loftq_init"]["objectives"] = [round(x, 4) for x in ob.cpu().tolist()]
+        del lws
         del calls, devs
         torch.cuda.empty_cache()
 
