@@ -19,6 +19,9 @@ It is written to be checked by eye against the pages it follows:
   alternating quantize / rank-r SVD steps).
 * AQLoRA page -- bittide.aicompass.dev translation of AQLoRA, section 3.1
   (profiling pass): the per-layer NF4 round-trip error.
+* LoRAQuant page -- "LoRAQuant: Mixed-Precision Quantization of LoRA to
+  Ultra-Low Bits", method overview and key design: SVD reparameterization of
+  the adapter and mixed-precision quantization of its components.
 
 Floating point follows IEEE binary32/binary64 with round to nearest even and
 subnormals kept. numpy's float32 operators are single correctly rounded
@@ -28,4 +31,4 @@ Functions without an independent pin say "parity unpinned" in their
 docstring; at present there are none.
 """
 
-from . import bf16, fp8, nf4, dq, layer, codebook, lloyd, loftq, sizes  # noqa: F401
+from . import bf16, fp8, nf4, dq, layer, codebook, lloyd, loftq, loraquant, sizes  # noqa: F401
