@@ -430,6 +430,56 @@ int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32
                   float* absmax, uint8_t* absmax_q, float* dq_scale, float* dq_mean, float* B, float* A,
                   float* sigma, double* objectives, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for lq_loraquant (0 for an invalid shape). */
+size_t lq_loraquant_workspace(int64_t N, int64_t K, int32_t r);
+
+/*
+ * LoRAQuant-style mixed-precision quantization of a LoRA adapter ([LoRAQuant]
+ * method overview and key design). For B [N, r] and A [r, K] (float32,
+ * row-major):
+ *   reparameterization by the SVD of B A, split evenly: B' = U S^(1/2),
+ *   A' = S^(1/2) V^T (computed from the r x r Grams B^T B and A A^T in float64,
+ *   so that B' A' = B A and B'^T B' = A' A'^T = diag(sigma)); component i =
+ *   row i of A' and column i of B', signed so that the largest-magnitude
+ *   entry of row i of A' (the first on ties) is positive;
+ *   h = the given h if h >= 0, else the smallest count whose squared float32
+ *   singular values, summed in order, reach rho times their total (0 for a
+ *   zero adapter);
+ *   components i < h quantized at bits_hi, the rest at bits_lo, each vector
+ *   (row of A', row of B'^T) in the codebook format of lq_quantize_codebook
+ *   with the NormalFloat levels of its width (NF_b; {-1, +1} at 1 bit).
+ * Outputs (device, caller-owned):
+ *   codes_a  bytes of A' [r, K]: up to r K bits_max / 8; absmax_a [r K / 64]
+ *   codes_b  bytes of B'^T [r, N]: up to r N bits_max / 8; absmax_b [r N / 64]
+ *   row_bits [r] uint8; offsets_a, offsets_b [r + 1] int64 (byte offsets)
+ *   levels [r, 16], thresholds [r, 15] float32 (the tables used)
+ *   sigma [r] float32 (descending), h_out [1] int32
+ *   Ap [r, K], Bpt [r, N] float32 reparameterized factors (may be NULL)
+ * Requires N % 64 == 0, K % 64 == 0 (LQ_ERR_SHAPE), r <= 64 (LQ_ERR_UNSUPPORTED),
+ * widths 1..4 and h <= r (LQ_ERR_ARG).
+ * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_loraquant(const float* B, const float* A, int64_t N, int64_t K, int32_t r, double rho, int32_t h,
+                 int32_t bits_hi, int32_t bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
+                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels,
+                 float* thresholds, float* sigma, int32_t* h_out, float* Ap, float* Bpt, void* workspace,
+                 size_t ws_bytes, void* stream);
+
+/* Workspace bytes for lq_loraquant_dequant (N * r * 2). */
+size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r);
+
+/*
+ * The quantized adapter back in bfloat16 for the layer: A_bf16 [r, K] and
+ * B_bf16 [N, r] (row-major), each value bfloat16(level * absmax) as
+ * lq_dequant computes it for a codebook weight. Arguments as written by
+ * lq_loraquant. Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED,
+ * LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ */
+int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const uint8_t* codes_b,
+                         const float* absmax_b, const uint8_t* row_bits, const int64_t* offsets_a,
+                         const int64_t* offsets_b, const float* levels, int64_t N, int64_t K, int32_t r,
+                         uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,10 +56,10 @@ def choose_h(sigma: np.ndarray, rho: float) -> int:
     """Smallest h with sum_{i<h} sigma_i^2 >= rho * sum sigma_i^2 (0 for a
     zero adapter)."""
     e = np.asarray(sigma, np.float64) ** 2
-    tot = float(np.sum(e))
+    c = np.cumsum(e)            # in order; the total is its last entry
+    tot = float(c[-1]) if len(c) else 0.0
     if tot == 0.0:
         return 0
-    c = np.cumsum(e)
     return int(min(len(e), max(1, int(np.searchsorted(c, rho * tot, side="left")) + 1)))
 
 

@@ -78,6 +78,13 @@ SIGNATURES = {
     "lq_loftq_workspace": (c_sz, [c_i64, c_i64, c_i32, c_i32, c_i32]),
     "lq_loftq_init": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lq_loraquant_workspace": (c_sz, [c_i64, c_i64, c_i32]),
+    "lq_loraquant": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, ctypes.c_double, c_i32, c_i32, c_i32,
+                                    c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                    c_vp, c_sz, c_vp]),
+    "lq_loraquant_dequant_workspace": (c_sz, [c_i64, c_i64, c_i32]),
+    "lq_loraquant_dequant": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
+                                            c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "lq_dequant_gemm_workspace": (c_sz, [QW_P, c_i64, c_i32]),
@@ -411,6 +418,59 @@ def loftq_init(W, r: int, omega, steps: int = 5, power_iters: int = 8, double_qu
         qw = QWeight(N, K, codes, absmax=absmax)
     qw.absmax_f32 = absmax
     return qw, B, A, sigma, objectives
+
+
+class QuantAdapter:
+    """A LoRAQuant-quantized adapter: device tensors written by lq_loraquant."""
+
+    def __init__(self, N, K, r, bits_max, device):
+        torch = _torch()
+        self.N, self.K, self.r = N, K, r
+        z = lambda n, dt: torch.empty(n, dtype=dt, device=device)
+        self.codes_a = z(r * K * bits_max // 8, torch.uint8)
+        self.absmax_a = z(r * K // 64, torch.float32)
+        self.codes_b = z(r * N * bits_max // 8, torch.uint8)
+        self.absmax_b = z(r * N // 64, torch.float32)
+        self.row_bits = z(r, torch.uint8)
+        self.offsets_a = z(r + 1, torch.int64)
+        self.offsets_b = z(r + 1, torch.int64)
+        self.levels = z(r * 16, torch.float32)
+        self.thresholds = z(r * 15, torch.float32)
+        self.sigma = z(r, torch.float32)
+        self.h = z(1, torch.int32)
+        self.Ap = z(r * K, torch.float32)
+        self.Bpt = z(r * N, torch.float32)
+
+
+def loraquant(B, A, rho: float = 0.9, bits_hi: int = 3, bits_lo: int = 1, h: int = -1) -> QuantAdapter:
+    """LoRAQuant-style quantization of B [N, r], A [r, K] (float32, device)."""
+    torch = _torch()
+    N, r = B.shape
+    K = A.shape[1]
+    q = QuantAdapter(N, K, r, max(bits_hi, bits_lo), B.device)
+    ws_bytes = lib.lq_loraquant_workspace(N, K, r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=B.device)
+    _check(lib.lq_loraquant(_ptr(B), _ptr(A), N, K, r, float(rho), int(h), int(bits_hi), int(bits_lo),
+                            _ptr(q.codes_a), _ptr(q.absmax_a), _ptr(q.codes_b), _ptr(q.absmax_b), _ptr(q.row_bits),
+                            _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels), _ptr(q.thresholds), _ptr(q.sigma),
+                            _ptr(q.h), _ptr(q.Ap), _ptr(q.Bpt), _ptr(ws), ws_bytes, _stream(B.device)),
+           "lq_loraquant")
+    return q
+
+
+def loraquant_dequant(q: QuantAdapter):
+    """-> (A bf16 [r, K], B bf16 [N, r]) of a quantized adapter."""
+    torch = _torch()
+    dev = q.codes_a.device
+    A = torch.empty(q.r, q.K, dtype=torch.bfloat16, device=dev)
+    B = torch.empty(q.N, q.r, dtype=torch.bfloat16, device=dev)
+    ws_bytes = lib.lq_loraquant_dequant_workspace(q.N, q.K, q.r)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.lq_loraquant_dequant(_ptr(q.codes_a), _ptr(q.absmax_a), _ptr(q.codes_b), _ptr(q.absmax_b),
+                                    _ptr(q.row_bits), _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels),
+                                    q.N, q.K, q.r, _ptr(A), _ptr(B), _ptr(ws), ws_bytes, _stream(dev)),
+           "lq_loraquant_dequant")
+    return A, B
 
 
 def quantize_codebook(W, row_bits, thresholds, blocksize: int = 64):

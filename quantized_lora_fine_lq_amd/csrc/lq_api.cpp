@@ -382,4 +382,70 @@ int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32
                                     dq_scale, dq_mean, B, A, sigma, objectives, workspace, (hipStream_t)stream));
 }
 
+static int check_loraquant_shape(int64_t N, int64_t K, int32_t r) {
+  if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || r < 1) return LQ_ERR_SHAPE;
+  if (r > LQ_LORAQUANT_MAX_R) return LQ_ERR_UNSUPPORTED;
+  return LQ_OK;
+}
+
+size_t lq_loraquant_workspace(int64_t N, int64_t K, int32_t r) {
+  if (check_loraquant_shape(N, K, r) != LQ_OK) return 0;
+  return align_up(loraquant_ws_bytes(N, K, r));
+}
+
+int lq_loraquant(const float* B, const float* A, int64_t N, int64_t K, int32_t r, double rho, int32_t h,
+                 int32_t bits_hi, int32_t bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
+                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels,
+                 float* thresholds, float* sigma, int32_t* h_out, float* Ap, float* Bpt, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  if (!B || !A || !codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b ||
+      !levels || !thresholds || !sigma || !h_out)
+    return LQ_ERR_ARG;
+  if (bits_hi < 1 || bits_hi > 4 || bits_lo < 1 || bits_lo > 4 || h > r) return LQ_ERR_ARG;
+  const int st = check_loraquant_shape(N, K, r);
+  if (st != LQ_OK) return st;
+  if (!workspace || ws_bytes < loraquant_ws_bytes(N, K, r)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_loraquant(B, A, N, K, r, rho, h, bits_hi, bits_lo, codes_a, absmax_a, codes_b,
+                                        absmax_b, row_bits, offsets_a, offsets_b, levels, thresholds, sigma, h_out,
+                                        Ap, Bpt, workspace, (hipStream_t)stream));
+}
+
+size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r) {
+  if (check_loraquant_shape(N, K, r) != LQ_OK) return 0;
+  return align_up((size_t)N * r * sizeof(uint16_t));
+}
+
+int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const uint8_t* codes_b,
+                         const float* absmax_b, const uint8_t* row_bits, const int64_t* offsets_a,
+                         const int64_t* offsets_b, const float* levels, int64_t N, int64_t K, int32_t r,
+                         uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes, void* stream) {
+  if (!codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b || !levels ||
+      !A_bf16 || !B_bf16)
+    return LQ_ERR_ARG;
+  const int st = check_loraquant_shape(N, K, r);
+  if (st != LQ_OK) return st;
+  if (!workspace || ws_bytes < (size_t)N * r * sizeof(uint16_t)) return LQ_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  QWeight qa{};
+  qa.format = LQ_FMT_CODEBOOK;
+  qa.N = r;
+  qa.K = K;
+  qa.codes = codes_a;
+  qa.qc = QConst{absmax_a, nullptr, nullptr, nullptr};
+  qa.row_bits = row_bits;
+  qa.row_offset = offsets_a;
+  qa.levels = levels;
+  QWeight qb = qa;
+  qb.K = N;
+  qb.codes = codes_b;
+  qb.qc = QConst{absmax_b, nullptr, nullptr, nullptr};
+  qb.row_offset = offsets_b;
+  hipError_t e = launch_dequant(qa, A_bf16, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  uint16_t* bt = (uint16_t*)workspace;   // B'^T [r, N]
+  e = launch_dequant(qb, bt, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  return launch_status(launch_transpose_u16(bt, r, (int)N, B_bf16, s));
+}
+
 }  // extern "C"

@@ -213,15 +213,165 @@ __global__ __launch_bounds__(256) void k_gram_finish(const double* __restrict__ 
   }
 }
 
-// ---- Cholesky G = L L^T and T = L^{-T} in one workgroup (float64) ----------
-// Q = Y T then has orthonormal columns (up to rounding). Column step j: every
-// thread forms the pivot d = A[j][j] itself; the trailing update uses the
-// unscaled column, A[i][k] -= A[i][j] A[k][j] / d, and L's column j goes to a
-// separate array, so one barrier per step suffices. A pivot at or below
-// 1e-28 of the largest diagonal marks a column that depends on the earlier
-// ones: its column of L and its row of L^{-1} are zero, so that Q gets a
-// zero column there. L^{-1} by forward substitution, one row at a time, each
-// column's dot product split over TPC threads.
+// ---- small dense float64 kernels on LDS matrices (one 256-thread workgroup) ---
+// Matrices are [D][D + 1] arrays (padded rows); every thread calls each
+// routine, which ends with a barrier.
+
+// Cholesky: sL = L with A = L L^T from the lower triangle of sA (destroyed).
+// Column step j: every thread forms the pivot d = A[j][j] itself; the
+// trailing update uses the unscaled column, A[i][k] -= A[i][j] A[k][j] / d,
+// and L's column j goes to sL, so one barrier per step suffices. A pivot at
+// or below tol marks a column that depends on the earlier ones: its column
+// of L is zero.
+template <int D>
+__device__ void lds_cholesky(double (*sA)[D + 1], double (*sL)[D + 1], int l, double tol) {
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  for (int i = ty; i < l; i += 16)
+    for (int k = tx; k < l; k += 16) sL[i][k] = 0.0;
+  __syncthreads();
+  for (int j = 0; j < l; ++j) {
+    const double d = sA[j][j];
+    const bool ok = d > tol && d > 0.0;
+    const double piv = ok ? sqrt(d) : 0.0;
+    const double inv_d = ok ? 1.0 / d : 0.0;
+    if (ty == 0)
+      for (int i = j + tx; i < l; i += 16) sL[i][j] = ok ? ((i == j) ? piv : sA[i][j] / piv) : 0.0;
+    for (int i = j + 1 + ty; i < l; i += 16) {
+      const double aij = sA[i][j] * inv_d;
+      for (int k = j + 1 + tx; k <= i; k += 16) sA[i][k] -= aij * sA[k][j];
+    }
+    __syncthreads();
+  }
+}
+
+// sI = L^{-1} (lower triangular; a zero pivot gives a zero row) by forward
+// substitution one row at a time, each column's dot product split over the
+// 16 threads of a row group and reduced by shuffles.
+template <int D>
+__device__ void lds_tri_inverse(const double (*sL)[D + 1], double (*sI)[D + 1], int l) {
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  for (int i = ty; i < l; i += 16)
+    for (int k = tx; k < l; k += 16) sI[i][k] = 0.0;
+  __syncthreads();
+  for (int i = 0; i < l; ++i) {
+    const double d = sL[i][i];
+    for (int c = ty; c <= i; c += 16) {
+      double v = 0.0;
+      for (int k = c + tx; k < i; k += 16) v += sL[i][k] * sI[k][c];
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      if (tx == 0) sI[i][c] = (d > 0.0) ? (((c == i) ? 1.0 : 0.0) - v) / d : 0.0;
+    }
+    __syncthreads();
+  }
+}
+
+// Cyclic Jacobi on the symmetric sG (n x n): sG ends diagonal (the
+// eigenvalues), sV holds the eigenvectors as columns. Round-robin pairing
+// over n rounded up to even (the extra slot idles): in each round every index
+// is in at most one pair, so the rotations of a round commute and
+// G <- J^T G J is applied as a column pass then a row pass. Sweeps stop when
+// the squared off-diagonal mass is below 1e-26 of the total (1e-13 in norm)
+// or after 30 sweeps.
+template <int D>
+__device__ void lds_jacobi(double (*sG)[D + 1], double (*sV)[D + 1], int n) {
+  __shared__ double sC[D / 2 + 1], sS[D / 2 + 1];
+  __shared__ int sP[D / 2 + 1], sQ[D / 2 + 1];
+  __shared__ double sOff, sTot, sRedO[4], sRedT[4];
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  const int ne = n + (n & 1), np = ne / 2;
+  for (int i = ty; i < n; i += 16)
+    for (int j = tx; j < n; j += 16) sV[i][j] = (i == j) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    double off = 0.0, tot = 0.0;
+    for (int i = ty; i < n; i += 16)
+      for (int j = tx; j < n; j += 16) {
+        const double v = sG[i][j] * sG[i][j];
+        tot += v;
+        if (i != j) off += v;
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      tot += __shfl_xor(tot, o);
+    }
+    if ((t & 63) == 0) { sRedO[t >> 6] = off; sRedT[t >> 6] = tot; }
+    __syncthreads();
+    if (t == 0) {
+      sOff = ((sRedO[0] + sRedO[1]) + sRedO[2]) + sRedO[3];
+      sTot = ((sRedT[0] + sRedT[1]) + sRedT[2]) + sRedT[3];
+    }
+    __syncthreads();
+    if (!(sOff > 1e-26 * sTot)) break;
+    for (int round = 0; round < ne - 1; ++round) {
+      for (int pi = t; pi < np; pi += 256) {
+        auto slot = [&](int x) { return x == 0 ? 0 : 1 + (x - 1 + round) % (ne - 1); };
+        int p = slot(pi), q = slot(ne - 1 - pi);
+        if (p > q) { const int tmp = p; p = q; q = tmp; }
+        double c = 1.0, sn = 0.0;
+        if (q < n) {
+          const double apq = sG[p][q], app = sG[p][p], aqq = sG[q][q];
+          if (apq != 0.0) {
+            const double theta = (aqq - app) / (2.0 * apq);
+            const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(tt * tt + 1.0);
+            sn = tt * c;
+          }
+        } else {
+          q = -1;   // the idle slot
+        }
+        sP[pi] = p; sQ[pi] = q; sC[pi] = c; sS[pi] = sn;
+      }
+      __syncthreads();
+      for (int pi = ty; pi < np; pi += 16) {   // columns: G <- G J, V <- V J
+        const int p = sP[pi], q = sQ[pi];
+        if (q < 0) continue;
+        const double c = sC[pi], sn = sS[pi];
+        for (int i = tx; i < n; i += 16) {
+          const double gp = sG[i][p], gq = sG[i][q];
+          sG[i][p] = c * gp - sn * gq;
+          sG[i][q] = sn * gp + c * gq;
+          const double vp = sV[i][p], vq = sV[i][q];
+          sV[i][p] = c * vp - sn * vq;
+          sV[i][q] = sn * vp + c * vq;
+        }
+      }
+      __syncthreads();
+      for (int pi = ty; pi < np; pi += 16) {   // rows: G <- J^T G
+        const int p = sP[pi], q = sQ[pi];
+        if (q < 0) continue;
+        const double c = sC[pi], sn = sS[pi];
+        for (int j = tx; j < n; j += 16) {
+          const double gp = sG[p][j], gq = sG[q][j];
+          sG[p][j] = c * gp - sn * gq;
+          sG[q][j] = sn * gp + c * gq;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// sOrder[k] = index of the k-th largest diagonal entry of sG (ties by index)
+template <int D>
+__device__ void lds_eig_order(const double (*sG)[D + 1], int n, int* sOrder) {
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const double lt = sG[i][i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double lj = sG[j][j];
+      rank += (lj > lt || (lj == lt && j < i)) ? 1 : 0;
+    }
+    sOrder[rank] = i;
+  }
+  __syncthreads();
+}
+
+// ---- Cholesky G = L L^T and T = L^{-T} (one workgroup) -----------------------
+// Q = Y T then has orthonormal columns (up to rounding); a dependent column
+// (pivot at or below 1e-28 of the largest diagonal) gets a zero column of Q.
 __global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__ G, int l, double* __restrict__ T) {
   __shared__ double sA[LR_MAXL][LR_MAXL + 1];
   __shared__ double sL[LR_MAXL][LR_MAXL + 1];
@@ -232,163 +382,42 @@ __global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__
     for (int k = tx; k < l; k += 16) {
       const double v = G[i * l + k];
       sA[i][k] = v;
-      sL[i][k] = 0.0;
       if (i == k) m = fmax(m, v);
     }
   for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if ((t & 63) == 0) sRed[t >> 6] = m;
   __syncthreads();
   const double tol = 1e-28 * fmax(fmax(sRed[0], sRed[1]), fmax(sRed[2], sRed[3]));
-  for (int j = 0; j < l; ++j) {
-    const double d = sA[j][j];
-    const bool ok = d > tol && d > 0.0;
-    const double piv = ok ? sqrt(d) : 0.0;
-    const double inv_d = ok ? 1.0 / d : 0.0;
-    // L's column j (from the unchanged column of A)
-    if (ty == 0)
-      for (int i = j + tx; i < l; i += 16) sL[i][j] = ok ? ((i == j) ? piv : sA[i][j] / piv) : 0.0;
-    // trailing update of the lower triangle
-    for (int i = j + 1 + ty; i < l; i += 16) {
-      const double aij = sA[i][j] * inv_d;
-      for (int k = j + 1 + tx; k <= i; k += 16) sA[i][k] -= aij * sA[k][j];
-    }
-    __syncthreads();
-  }
-  // L^{-1}: row i from rows < i; column c's dot product over k in [c, i)
-  // split over the 16 threads of a row group (tx), reduced by shuffles
-  double* sI = &sA[0][0];   // reuse: sI[i * (LR_MAXL + 1) + c]
-  constexpr int P = LR_MAXL + 1;
-  for (int e = t; e < LR_MAXL * P; e += 256) sI[e] = 0.0;
-  __syncthreads();
-  for (int i = 0; i < l; ++i) {
-    const double d = sL[i][i];
-    for (int c = ty; c <= i; c += 16) {
-      double v = 0.0;
-      for (int k = c + tx; k < i; k += 16) v += sL[i][k] * sI[k * P + c];
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 2);
-      v += __shfl_xor(v, 1);
-      if (tx == 0) sI[i * P + c] = (d > 0.0) ? (((c == i) ? 1.0 : 0.0) - v) / d : 0.0;
-    }
-    __syncthreads();
-  }
-  // T[k][j] = L^{-1}[j][k] (upper triangular)
+  lds_cholesky<LR_MAXL>(sA, sL, l, tol);
+  lds_tri_inverse<LR_MAXL>(sL, sA, l);   // sA now holds L^{-1}
   for (int k = ty; k < l; k += 16)
-    for (int j = tx; j < l; j += 16) T[k * l + j] = (k <= j) ? sI[j * P + k] : 0.0;
+    for (int j = tx; j < l; j += 16) T[k * l + j] = (k <= j) ? sA[j][k] : 0.0;   // T = L^{-T}
 }
 
-// ---- symmetric eigen-decomposition by cyclic Jacobi (one workgroup) ---------
-// Round-robin pairing: in each of the l - 1 rounds of a sweep every index is
-// in exactly one pair, so the rotations of a round commute; G <- J^T G J is
-// applied as a column pass then a row pass. Sweeps stop when the squared
-// off-diagonal mass is below 1e-26 of the total (1e-13 in norm) or after 30 sweeps. Then
-// the top r eigenpairs (descending, ties by index) give
-//   M1[:, i] = u_i sqrt(sigma_i), M2[:, i] = u_i / sqrt(sigma_i) (0 if sigma_i = 0),
-// with sigma_i = sqrt(max(lambda_i, 0)).
+// ---- eigen-decomposition of the Rayleigh-Ritz Gram (one workgroup) ----------
+// The top r eigenpairs (descending) give M1[:, i] = u_i sqrt(sigma_i),
+// M2[:, i] = u_i / sqrt(sigma_i) (0 if sigma_i = 0), sigma_i = sqrt(max(lambda_i, 0)).
 __global__ __launch_bounds__(256) void k_jacobi_eig(const double* __restrict__ Gin, int l, int r,
                                                      double* __restrict__ M1, double* __restrict__ M2,
                                                      float* __restrict__ sigma) {
   __shared__ double sG[LR_MAXL][LR_MAXL + 1];
   __shared__ double sV[LR_MAXL][LR_MAXL + 1];
-  __shared__ double sC[LR_MAXL / 2], sS[LR_MAXL / 2];
-  __shared__ int sP[LR_MAXL / 2], sQ[LR_MAXL / 2];
   __shared__ int sOrder[LR_MAXL];
-  __shared__ double sOff, sTot, sRedO[4], sRedT[4];
-  const int t = threadIdx.x;
-  const int n = l;   // even (l % 8 == 0)
-  for (int e = t; e < n * n; e += 256) {
-    const int i = e / n, j = e % n;
-    sG[i][j] = Gin[e];
-    sV[i][j] = (i == j) ? 1.0 : 0.0;
-  }
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  for (int i = ty; i < l; i += 16)
+    for (int j = tx; j < l; j += 16) sG[i][j] = Gin[i * l + j];
   __syncthreads();
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    {
-      double off = 0.0, tot = 0.0;
-      for (int i = t >> 4; i < n; i += 16)
-        for (int j = t & 15; j < n; j += 16) {
-          const double v = sG[i][j] * sG[i][j];
-          tot += v;
-          if (i != j) off += v;
-        }
-      for (int o = 32; o > 0; o >>= 1) {
-        off += __shfl_xor(off, o);
-        tot += __shfl_xor(tot, o);
-      }
-      if ((t & 63) == 0) { sRedO[t >> 6] = off; sRedT[t >> 6] = tot; }
-      __syncthreads();
-      if (t == 0) {
-        sOff = ((sRedO[0] + sRedO[1]) + sRedO[2]) + sRedO[3];
-        sTot = ((sRedT[0] + sRedT[1]) + sRedT[2]) + sRedT[3];
-      }
-      __syncthreads();
+  lds_jacobi<LR_MAXL>(sG, sV, l);
+  lds_eig_order<LR_MAXL>(sG, l, sOrder);
+  for (int i = ty; i < l; i += 16)
+    for (int k = tx; k < r; k += 16) {
+      const int col = sOrder[k];
+      const double sg = sqrt(fmax(sG[col][col], 0.0));
+      const double h = sqrt(sg);
+      M1[i * r + k] = sV[i][col] * h;
+      M2[i * r + k] = (h > 0.0) ? sV[i][col] / h : 0.0;
+      if (i == 0) sigma[k] = (float)sg;
     }
-    if (!(sOff > 1e-26 * sTot)) break;
-    for (int round = 0; round < n - 1; ++round) {
-      // pairs of the round-robin schedule: slot 0 fixed, the rest rotate
-      for (int pi = t; pi < n / 2; pi += 256) {
-        auto slot = [&](int s) { return s == 0 ? 0 : 1 + (s - 1 + round) % (n - 1); };
-        int p = slot(pi), q = slot(n - 1 - pi);
-        if (p > q) { const int tmp = p; p = q; q = tmp; }
-        const double apq = sG[p][q], app = sG[p][p], aqq = sG[q][q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0) {
-          const double theta = (aqq - app) / (2.0 * apq);
-          const double tt = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-          c = 1.0 / sqrt(tt * tt + 1.0);
-          s = tt * c;
-        }
-        sP[pi] = p; sQ[pi] = q; sC[pi] = c; sS[pi] = s;
-      }
-      __syncthreads();
-      // columns: G <- G J, V <- V J
-      for (int pi = t >> 4; pi < n / 2; pi += 16) {
-        const int p = sP[pi], q = sQ[pi];
-        const double c = sC[pi], s = sS[pi];
-        for (int i = t & 15; i < n; i += 16) {
-        const double gp = sG[i][p], gq = sG[i][q];
-        sG[i][p] = c * gp - s * gq;
-        sG[i][q] = s * gp + c * gq;
-        const double vp = sV[i][p], vq = sV[i][q];
-        sV[i][p] = c * vp - s * vq;
-        sV[i][q] = s * vp + c * vq;
-        }
-      }
-      __syncthreads();
-      // rows: G <- J^T G
-      for (int pi = t >> 4; pi < n / 2; pi += 16) {
-        const int p = sP[pi], q = sQ[pi];
-        const double c = sC[pi], s = sS[pi];
-        for (int j = t & 15; j < n; j += 16) {
-          const double gp = sG[p][j], gq = sG[q][j];
-          sG[p][j] = c * gp - s * gq;
-          sG[q][j] = s * gp + c * gq;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // rank of each eigenvalue (descending, ties by index)
-  for (int i = t; i < n; i += 256) {
-    const double lt = sG[i][i];
-    int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      const double lj = sG[j][j];
-      rank += (lj > lt || (lj == lt && j < i)) ? 1 : 0;
-    }
-    sOrder[rank] = i;
-  }
-  __syncthreads();
-  for (int e = t; e < n * r; e += 256) {
-    const int i = e / r, k = e % r;
-    const int col = sOrder[k];
-    const double sg = sqrt(fmax(sG[col][col], 0.0));
-    const double h = sqrt(sg);
-    M1[e] = sV[i][col] * h;
-    M2[e] = (h > 0.0) ? sV[i][col] / h : 0.0;
-    if (i == 0) sigma[k] = (float)sg;
-  }
 }
 
 // ---- out = X S (X [M, l] float32, S [l, c] float64), or its transpose --------
@@ -658,6 +687,259 @@ hipError_t launch_loftq(const float* W, int64_t N, int64_t K, bool dq, int r, in
       return e;
   }
   return hipSuccess;
+}
+
+// ===========================================================================
+// LoRAQuant-style quantization of an adapter (LoRAQuant page, method overview
+// and key design): SVD reparameterization B A = B' A' with B' = U S^(1/2),
+// A' = S^(1/2) V^T, the important components (by singular value) at a higher
+// width, the rest at an ultra-low width, each component vector quantized in
+// the codebook format with the NormalFloat tables of its width.
+//
+// The SVD needs only r x r work: with G_B = B^T B, G_A = A A^T = L_A L_A^T
+// and S = L_A^T G_B L_A = W diag(sigma^2) W^T,
+//   B' = B (L_A W sigma^(-1/2)),  A' = (sigma^(1/2) W^T L_A^(-1)) A,
+// so that B' A' = B A, B'^T B' = A' A'^T = diag(sigma).
+// ===========================================================================
+namespace {
+
+constexpr int LQ_D = LQ_LORAQUANT_MAX_R;
+
+__global__ __launch_bounds__(256) void k_adapter_core(const double* __restrict__ GB, const double* __restrict__ GA,
+                                                      int r, double rho, int h_fixed, int bits_hi, int bits_lo,
+                                                      NfCodebooks tabs, double* __restrict__ MBt,
+                                                      double* __restrict__ MA, float* __restrict__ sigma,
+                                                      int32_t* __restrict__ h_out, uint8_t* __restrict__ row_bits,
+                                                      float* __restrict__ levels, float* __restrict__ thresholds) {
+  __shared__ double sA[LQ_D][LQ_D + 1];   // G_A (destroyed), then G_B L_A, then W
+  __shared__ double sL[LQ_D][LQ_D + 1];   // L_A
+  __shared__ double sI[LQ_D][LQ_D + 1];   // L_A^{-1}
+  __shared__ double sS[LQ_D][LQ_D + 1];   // G_B, then S (diagonalised)
+  __shared__ int sOrder[LQ_D];
+  __shared__ double sSig[LQ_D];
+  __shared__ double sRed[4];
+  __shared__ int sH;
+  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
+  double m = 0.0;
+  for (int i = ty; i < r; i += 16)
+    for (int k = tx; k < r; k += 16) {
+      const double a = GA[i * r + k];
+      sA[i][k] = a;
+      sS[i][k] = GB[i * r + k];
+      if (i == k) m = fmax(m, a);
+    }
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  if ((t & 63) == 0) sRed[t >> 6] = m;
+  __syncthreads();
+  const double tol = 1e-28 * fmax(fmax(sRed[0], sRed[1]), fmax(sRed[2], sRed[3]));
+  lds_cholesky<LQ_D>(sA, sL, r, tol);
+  lds_tri_inverse<LQ_D>(sL, sI, r);
+  for (int i = ty; i < r; i += 16)          // sA = G_B L_A
+    for (int j = tx; j < r; j += 16) {
+      double v = 0.0;
+      for (int k = j; k < r; ++k) v += sS[i][k] * sL[k][j];
+      sA[i][j] = v;
+    }
+  __syncthreads();
+  for (int i = ty; i < r; i += 16)          // sS = L_A^T (G_B L_A)
+    for (int j = tx; j < r; j += 16) {
+      double v = 0.0;
+      for (int k = i; k < r; ++k) v += sL[k][i] * sA[k][j];
+      sS[i][j] = v;
+    }
+  __syncthreads();
+  for (int i = ty; i < r; i += 16)          // symmetrise
+    for (int j = tx; j < i; j += 16) {
+      const double v = 0.5 * (sS[i][j] + sS[j][i]);
+      sS[i][j] = v;
+      sS[j][i] = v;
+    }
+  __syncthreads();
+  lds_jacobi<LQ_D>(sS, sA, r);              // sA = W
+  lds_eig_order<LQ_D>(sS, r, sOrder);
+  for (int k = t; k < r; k += 256) {
+    const double sg = sqrt(fmax(sS[sOrder[k]][sOrder[k]], 0.0));
+    sSig[k] = sg;
+    sigma[k] = (float)sg;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int h;
+    if (h_fixed >= 0) {
+      h = min(h_fixed, r);
+    } else {
+      // energies of the float32 singular values, summed in order
+      double tot = 0.0;
+      for (int k = 0; k < r; ++k) { const double f = (double)(float)sSig[k]; tot += f * f; }
+      if (tot == 0.0) {
+        h = 0;
+      } else {
+        double c = 0.0;
+        h = r;
+        for (int k = 0; k < r; ++k) {
+          const double f = (double)(float)sSig[k];
+          c += f * f;
+          if (c >= rho * tot) { h = k + 1; break; }
+        }
+      }
+    }
+    sH = h;
+    *h_out = h;
+  }
+  __syncthreads();
+  const int h = sH;
+  for (int k = ty; k < r; k += 16)
+    for (int j = tx; j < r; j += 16) {
+      const int col = sOrder[k];
+      const double sg = sSig[k];
+      const double rs = sqrt(sg);
+      double b = 0.0;
+      for (int q = 0; q <= j; ++q) b += sL[j][q] * sA[q][col];       // (L_A W)[j][col]
+      double a = 0.0;
+      for (int q = j; q < r; ++q) a += sA[q][col] * sI[q][j];        // (W^T L_A^{-1})[col][j]
+      MBt[k * r + j] = (rs > 0.0) ? b / rs : 0.0;                    // M_B^T[k][j]
+      MA[k * r + j] = rs * a;                                         // M_A[k][j]
+    }
+  for (int k = t; k < r; k += 256) {
+    const int bits = (k < h) ? bits_hi : bits_lo;
+    row_bits[k] = (uint8_t)bits;
+    for (int q = 0; q < 16; ++q) levels[k * 16 + q] = tabs.L[bits - 1][q];
+    for (int q = 0; q < 15; ++q) thresholds[k * 15 + q] = tabs.T[bits - 1][q];
+  }
+}
+
+// out[i][c] = sum_j M[i][j] X(j, c) for i < r, c < C, summed in float64;
+// X(j, c) = X[j C + c] (X [r, C]) or X[c r + j] (transposed: X [C, r]).
+__global__ __launch_bounds__(256) void k_small_left(const double* __restrict__ M, int r,
+                                                    const float* __restrict__ X, int64_t C, int trans,
+                                                    float* __restrict__ out) {
+  __shared__ double sM[LQ_D * LQ_D];
+  __shared__ float sX[LQ_D][257];
+  const int t = threadIdx.x;
+  const int64_t c = (int64_t)blockIdx.x * 256 + t;
+  for (int e = t; e < r * r; e += 256) sM[e] = M[e];
+  for (int j = 0; j < r; ++j) sX[j][t] = (c < C) ? (trans ? X[c * r + j] : X[(int64_t)j * C + c]) : 0.0f;
+  __syncthreads();
+  if (c >= C) return;
+  for (int i = 0; i < r; ++i) {
+    double v = 0.0;
+    for (int j = 0; j < r; ++j) v += sM[i * r + j] * (double)sX[j][t];
+    out[(int64_t)i * C + c] = (float)v;
+  }
+}
+
+// Component i: the entry of largest magnitude in row i of A' (the first on
+// ties) is made positive; row i of B'^T flips with it.
+__global__ __launch_bounds__(256) void k_sign_fix(float* __restrict__ Ap, int64_t K, float* __restrict__ Bpt,
+                                                  int64_t N) {
+  __shared__ float sV[4];
+  __shared__ int64_t sK[4];
+  __shared__ int sFlip;
+  const int t = threadIdx.x;
+  const int64_t i = blockIdx.x;
+  float best = -1.0f;
+  int64_t bk = 0;
+  for (int64_t k = t; k < K; k += 256) {
+    const float v = fabsf(Ap[i * K + k]);
+    if (v > best) { best = v; bk = k; }   // k increases per thread: the first maximum stays
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o);
+    const int64_t ok = __shfl_xor(bk, o);
+    if (ov > best || (ov == best && ok < bk)) { best = ov; bk = ok; }
+  }
+  if ((t & 63) == 0) { sV[t >> 6] = best; sK[t >> 6] = bk; }
+  __syncthreads();
+  if (t == 0) {
+    float b = sV[0];
+    int64_t kk = sK[0];
+    for (int w = 1; w < 4; ++w)
+      if (sV[w] > b || (sV[w] == b && sK[w] < kk)) { b = sV[w]; kk = sK[w]; }
+    sFlip = Ap[i * K + kk] < 0.0f;
+  }
+  __syncthreads();
+  if (!sFlip) return;
+  for (int64_t k = t; k < K; k += 256) Ap[i * K + k] = -Ap[i * K + k];
+  for (int64_t n = t; n < N; n += 256) Bpt[i * N + n] = -Bpt[i * N + n];
+}
+
+__global__ void k_row_offsets(const uint8_t* __restrict__ row_bits, int r, int64_t K, int64_t N,
+                              int64_t* __restrict__ offA, int64_t* __restrict__ offB) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t a = 0, b = 0;
+  for (int i = 0; i < r; ++i) {
+    offA[i] = a;
+    offB[i] = b;
+    a += K * row_bits[i] / 8;
+    b += N * row_bits[i] / 8;
+  }
+  offA[r] = a;
+  offB[r] = b;
+}
+
+__global__ __launch_bounds__(256) void k_transpose_f32(const float* __restrict__ in, int rows, int64_t cols,
+                                                       float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over in [rows, cols]
+  if (e >= (int64_t)rows * cols) return;
+  const int64_t i = e / cols, c = e % cols;
+  out[c * rows + i] = in[e];
+}
+
+struct LqWs {
+  float *At, *Ap, *Bpt;
+  double *gpart, *GB, *GA, *MBt, *MA;
+};
+LqWs carve_lq(void* ws, int64_t N, int64_t K, int r) {
+  LqWs w;
+  char* p = (char*)ws;
+  w.At = (float*)p; p += align256((size_t)K * r * sizeof(float));
+  w.Ap = (float*)p; p += align256((size_t)K * r * sizeof(float));
+  w.Bpt = (float*)p; p += align256((size_t)N * r * sizeof(float));
+  w.gpart = (double*)p; p += align256((size_t)GRAM_PARTS * r * r * sizeof(double));
+  w.GB = (double*)p; p += align256((size_t)r * r * sizeof(double));
+  w.GA = (double*)p; p += align256((size_t)r * r * sizeof(double));
+  w.MBt = (double*)p; p += align256((size_t)r * r * sizeof(double));
+  w.MA = (double*)p;
+  return w;
+}
+
+hipError_t gram(const float* Y, int64_t M, int l, double* part, double* G, hipStream_t s) {
+  const int parts = (int)std::min<int64_t>(GRAM_PARTS, (M + 31) / 32);
+  hipLaunchKernelGGL(k_gram_partial, dim3(parts), dim3(256), 0, s, Y, M, l, (M + parts - 1) / parts, part);
+  hipLaunchKernelGGL(k_gram_finish, dim3(grid_for(l * l, 256, 64)), dim3(256), 0, s, part, parts, l * l, G);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t loraquant_ws_bytes(int64_t N, int64_t K, int r) {
+  return 2 * align256((size_t)K * r * sizeof(float)) + align256((size_t)N * r * sizeof(float)) +
+         align256((size_t)GRAM_PARTS * r * r * sizeof(double)) + 4 * align256((size_t)r * r * sizeof(double));
+}
+
+hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K, int r, double rho, int h_fixed,
+                            int bits_hi, int bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
+                            float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b,
+                            float* levels, float* thresholds, float* sigma, int32_t* h_out, float* Ap_out,
+                            float* Bpt_out, void* ws, hipStream_t s) {
+  LqWs w = carve_lq(ws, N, K, r);
+  float* Ap = Ap_out ? Ap_out : w.Ap;
+  float* Bpt = Bpt_out ? Bpt_out : w.Bpt;
+  hipError_t e;
+  if ((e = gram(B, N, r, w.gpart, w.GB, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_transpose_f32, dim3((unsigned)((K * r + 255) / 256)), dim3(256), 0, s, A, r, K, w.At);
+  if ((e = gram(w.At, K, r, w.gpart, w.GA, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_adapter_core, dim3(1), dim3(256), 0, s, w.GB, w.GA, r, rho, h_fixed, bits_hi, bits_lo,
+                     nf_codebooks(), w.MBt, w.MA, sigma, h_out, row_bits, levels, thresholds);
+  hipLaunchKernelGGL(k_small_left, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, w.MA, r, A, K, 0, Ap);
+  hipLaunchKernelGGL(k_small_left, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, w.MBt, r, B, N, 1, Bpt);
+  hipLaunchKernelGGL(k_sign_fix, dim3((unsigned)r), dim3(256), 0, s, Ap, K, Bpt, N);
+  hipLaunchKernelGGL(k_row_offsets, dim3(1), dim3(64), 0, s, row_bits, r, K, N, offsets_a, offsets_b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_quantize_codebook(Ap, LQ_F32, r, K, row_bits, offsets_a, thresholds, codes_a, absmax_a, s)) !=
+      hipSuccess)
+    return e;
+  return launch_quantize_codebook(Bpt, LQ_F32, r, N, row_bits, offsets_b, thresholds, codes_b, absmax_b, s);
 }
 
 }  // namespace lq

@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 28
+    assert len(names) == 32
     for name in names:
         assert hasattr(lq.lib, name), name
         assert name in lq.SIGNATURES, name
@@ -245,3 +245,33 @@ def test_workspace_queries_deterministic(lq):
     a = [lq.lib.lq_forward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
     b = [lq.lib.lq_backward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
     assert len(set(a)) == 1 and len(set(b)) == 1 and a[0] > 0 and b[0] > 0
+
+
+def test_loraquant_validation(lq):
+    L = lq.lib
+    fake = ctypes.c_void_p(0x1000)
+    null = ctypes.c_void_p(None)
+    assert L.lq_loraquant_workspace(256, 512, 16) > 0
+    assert L.lq_loraquant_workspace(250, 512, 16) == 0     # N % 64
+    assert L.lq_loraquant_workspace(256, 512, 65) == 0     # r > 64
+    ws = L.lq_loraquant_workspace(256, 512, 16)
+    args = [fake, fake, 256, 512, 16, 0.9, -1, 3, 1] + [fake] * 13 + [fake, ws, null]
+    a = list(args); a[9] = null
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_ARG
+    a = list(args); a[7] = 5
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_ARG
+    a = list(args); a[6] = 17                              # h > r
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_ARG
+    a = list(args); a[3] = 500
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_SHAPE
+    a = list(args); a[4] = 65
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_UNSUPPORTED
+    a = list(args); a[23] = ws - 1
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_WORKSPACE
+    dws = L.lq_loraquant_dequant_workspace(256, 512, 16)
+    assert dws == 256 * 16 * 2
+    dargs = [fake] * 8 + [256, 512, 16, fake, fake, fake, dws, null]
+    d = list(dargs); d[11] = null
+    assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_ARG
+    d = list(dargs); d[14] = dws - 1
+    assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_WORKSPACE
