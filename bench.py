@@ -223,6 +223,36 @@ def codec_bytes(L, M=0):
     }
 
 
+def rec_loraquant(torch, lq, name, d, rec, kernels, rho=0.9, bits_hi=3, bits_lo=1):
+    """LoRAQuant-style quantization of the layer's adapter (float32 copies of
+    its bf16 B [N, r] and A [r, K]): time per call and the adapter's error."""
+    import numpy as np
+    N, r = d.B.shape
+    K = d.A.shape[1]
+    B32, A32 = d.B.float().contiguous(), d.A.float().contiguous()
+    q = lq.QuantAdapter(N, K, r, max(bits_hi, bits_lo), B32.device)
+    wsb = lq.lib.lq_loraquant_workspace(N, K, r)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        if lq.lib.lq_loraquant(P(B32), P(A32), N, K, r, rho, -1, bits_hi, bits_lo, P(q.codes_a), P(q.absmax_a),
+                               P(q.codes_b), P(q.absmax_b), P(q.row_bits), P(q.offsets_a), P(q.offsets_b),
+                               P(q.levels_a), P(q.thresholds_a), P(q.levels_b), P(q.thresholds_b), P(q.sigma),
+                               P(q.h), P(q.Ap), P(q.Bpt), P(ws), wsb, st) != 0:
+            raise RuntimeError("lq_loraquant failed")
+    # reads B and A, writes the float32 reparameterized factors and reads them
+    # twice (codebook learner, quantizer), writes codes and constants
+    byts = 4 * r * (N + K) + 12 * r * (N + K) + r * (N + K) * bits_hi // 8 + 4 * r * (N + K) // 64
+    rec(f"{name}.loraquant", time_ms(torch, [run], 20), byts, "GB/s")
+    Ad, Bd = lq.loraquant_dequant(q)
+    ref = B32.double() @ A32.double()
+    err = ((Bd.double() @ Ad.double() - ref).norm() / ref.norm()).item()
+    kernels[f"{name}.loraquant"].update({"h": int(q.h.item()), "rel_error": round(err, 4), "r": r,
+                                         "bits_hi": bits_hi, "bits_lo": bits_lo, "rho": rho})
+
+
 def loftq_bytes(L, r, q, steps):
     """Algorithmic bytes of the LoftQ-style initialisation: per alternation,
     W - B A (read W, write it; skipped in the first), NF4 quantize + double
@@ -419,6 +449,7 @@ def main():
         rec("q_proj.loftq_init", time_ms(torch, [loftq], 3, warmup=1), loftq_bytes(L, r_lq, q_lq, t_lq), "GB/s")
         kernels["q_proj.loftq_init"]["objectives"] = [round(x, 4) for x in ob.cpu().tolist()]
         del lws
+        rec_loraquant(torch, lq, "q_proj", d0, rec, kernels)
         del calls, devs
         torch.cuda.empty_cache()
 
@@ -435,6 +466,8 @@ def main():
                 c.double_quant()
             rec(f"{name}.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in cs], 20), flm["fwd_gemm"], "TFLOP/s")
             rec(f"{name}.backward", time_ms(torch, [c.backward for c in cs], 10), flm["bwd"], "TFLOP/s")
+            if name == "mlp_up":
+                rec_loraquant(torch, lq, name, dv[0], rec, kernels)
             del cs, dv
             torch.cuda.empty_cache()
 

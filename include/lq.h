@@ -447,23 +447,25 @@ size_t lq_loraquant_workspace(int64_t N, int64_t K, int32_t r);
  *   zero adapter);
  *   components i < h quantized at bits_hi, the rest at bits_lo, each vector
  *   (row of A', row of B'^T) in the codebook format of lq_quantize_codebook
- *   with the NormalFloat levels of its width (NF_b; {-1, +1} at 1 bit).
+ *   with its own codebook from the weighted Lloyd-Max learner
+ *   (lq_lloyd_codebooks, 100 iterations at most) at its width.
  * Outputs (device, caller-owned):
  *   codes_a  bytes of A' [r, K]: up to r K bits_max / 8; absmax_a [r K / 64]
  *   codes_b  bytes of B'^T [r, N]: up to r N bits_max / 8; absmax_b [r N / 64]
  *   row_bits [r] uint8; offsets_a, offsets_b [r + 1] int64 (byte offsets)
- *   levels [r, 16], thresholds [r, 15] float32 (the tables used)
+ *   levels_a, levels_b [r, 16], thresholds_a, thresholds_b [r, 15] float32
+ *               (the learned tables of A' rows and B'^T rows)
  *   sigma [r] float32 (descending), h_out [1] int32
  *   Ap [r, K], Bpt [r, N] float32 reparameterized factors (may be NULL)
- * Requires N % 64 == 0, K % 64 == 0 (LQ_ERR_SHAPE), r <= 64 (LQ_ERR_UNSUPPORTED),
- * widths 1..4 and h <= r (LQ_ERR_ARG).
+ * Requires N % 64 == 0, K % 64 == 0 (LQ_ERR_SHAPE), r <= 64 and N, K <=
+ * LQ_LLOYD_MAX_K (LQ_ERR_UNSUPPORTED), widths 1..4 and h <= r (LQ_ERR_ARG).
  * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
  */
 int lq_loraquant(const float* B, const float* A, int64_t N, int64_t K, int32_t r, double rho, int32_t h,
                  int32_t bits_hi, int32_t bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
-                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels,
-                 float* thresholds, float* sigma, int32_t* h_out, float* Ap, float* Bpt, void* workspace,
-                 size_t ws_bytes, void* stream);
+                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels_a,
+                 float* thresholds_a, float* levels_b, float* thresholds_b, float* sigma, int32_t* h_out, float* Ap,
+                 float* Bpt, void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for lq_loraquant_dequant (N * r * 2). */
 size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r);
@@ -477,8 +479,9 @@ size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r);
  */
 int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const uint8_t* codes_b,
                          const float* absmax_b, const uint8_t* row_bits, const int64_t* offsets_a,
-                         const int64_t* offsets_b, const float* levels, int64_t N, int64_t K, int32_t r,
-                         uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes, void* stream);
+                         const int64_t* offsets_b, const float* levels_a, const float* levels_b, int64_t N,
+                         int64_t K, int32_t r, uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,12 +17,14 @@ Readings where the page is silent:
   * importance: the h largest components, h the smallest count whose squared
     singular values reach a fraction rho of the total (at least 1 when the
     adapter is nonzero), unless h is given;
-  * quantizer: each component vector (row of A', column of B') is quantized
-    like a codebook row of this framework: 64-element groups scaled by their
-    absmax, codes = number of thresholds below x, with the NormalFloat levels
-    of its width (NF_b; {-1, +1} at 1 bit) and thresholds = largest float32 not
-    above the midpoints of the float32 levels; b_hi bits for the h important
-    components, b_lo bits for the rest;
+  * quantizer: each component vector (row of A', column of B') is a
+    codebook row of this framework: 64-element groups scaled by their absmax,
+    codes = number of thresholds below x, with its own levels and thresholds
+    learned by the weighted Lloyd-Max learner at its width (started from the
+    NormalFloat tables of that width); b_hi bits for the h important
+    components, b_lo bits for the rest. (With fixed NormalFloat tables a
+    1-bit vector would become +-absmax everywhere, about 2.5 times its RMS for
+    Gaussian-like data; the learned 1-bit levels sit near the mean |x|.)
   * arithmetic: the reparameterized factors are formed in float64 and stored
     as float32, which is what gets quantized.
 """
@@ -31,7 +33,6 @@ from __future__ import annotations
 import numpy as np
 
 from . import codebook, lloyd
-from .nf4 import midpoint_thresholds
 
 
 def reparam(B: np.ndarray, A: np.ndarray):
@@ -63,32 +64,17 @@ def choose_h(sigma: np.ndarray, rho: float) -> int:
     return int(min(len(e), max(1, int(np.searchsorted(c, rho * tot, side="left")) + 1)))
 
 
-def nf_tables(bits: int):
-    """float32 levels [16] (the 2^b NF_b levels, the rest repeating the last)
-    and thresholds [15] (round-down midpoints, the rest 3.0)."""
-    L = lloyd.init_levels(bits).astype(np.float32)
-    n = 1 << bits
-    lv = np.full(16, L[-1], np.float32)
-    lv[:n] = L
-    th = np.full(15, 3.0, np.float32)
-    th[:n - 1] = midpoint_thresholds(L)
-    return lv, th
-
-
 def component_bits(r: int, h: int, bits_hi: int, bits_lo: int) -> np.ndarray:
     return np.array([bits_hi if i < h else bits_lo for i in range(r)], np.uint8)
 
 
 def quantize(Bp32: np.ndarray, Ap32: np.ndarray, bits: np.ndarray):
-    """Codebook quantization of A' rows and B'^T rows with per-row NF tables.
-    Returns dicts for A and B: packed, absmax, offsets, levels, thresholds."""
-    r = len(bits)
-    lv = np.zeros((r, 16), np.float32)
-    th = np.zeros((r, 15), np.float32)
-    for i, b in enumerate(bits):
-        lv[i], th[i] = nf_tables(int(b))
+    """Per-component learned codebooks for A' rows and B'^T rows, then their
+    codebook quantization. Returns dicts for A and B: packed, absmax,
+    offsets, levels [r, 16], thresholds [r, 15], shape."""
     out = {}
     for name, X in (("A", np.asarray(Ap32, np.float32)), ("B", np.ascontiguousarray(np.asarray(Bp32, np.float32).T))):
+        lv, th = lloyd.learn_codebooks(X, bits)
         packed, c, _ = codebook.quantize(X, bits, th)
         out[name] = {"packed": packed, "absmax": c, "offsets": codebook.row_offsets(bits, X.shape[1]),
                      "levels": lv, "thresholds": th, "shape": X.shape}

@@ -81,10 +81,10 @@ SIGNATURES = {
     "lq_loraquant_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_loraquant": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_i32, ctypes.c_double, c_i32, c_i32, c_i32,
                                     c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                    c_vp, c_sz, c_vp]),
+                                    c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_loraquant_dequant_workspace": (c_sz, [c_i64, c_i64, c_i32]),
-    "lq_loraquant_dequant": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32,
-                                            c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lq_loraquant_dequant": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                            c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "lq_lora_down_workspace": (c_sz, [c_i64, c_i64, c_i32]),
     "lq_lora_down": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "lq_dequant_gemm_workspace": (c_sz, [QW_P, c_i64, c_i32]),
@@ -434,8 +434,10 @@ class QuantAdapter:
         self.row_bits = z(r, torch.uint8)
         self.offsets_a = z(r + 1, torch.int64)
         self.offsets_b = z(r + 1, torch.int64)
-        self.levels = z(r * 16, torch.float32)
-        self.thresholds = z(r * 15, torch.float32)
+        self.levels_a = z(r * 16, torch.float32)
+        self.thresholds_a = z(r * 15, torch.float32)
+        self.levels_b = z(r * 16, torch.float32)
+        self.thresholds_b = z(r * 15, torch.float32)
         self.sigma = z(r, torch.float32)
         self.h = z(1, torch.int32)
         self.Ap = z(r * K, torch.float32)
@@ -452,8 +454,9 @@ def loraquant(B, A, rho: float = 0.9, bits_hi: int = 3, bits_lo: int = 1, h: int
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=B.device)
     _check(lib.lq_loraquant(_ptr(B), _ptr(A), N, K, r, float(rho), int(h), int(bits_hi), int(bits_lo),
                             _ptr(q.codes_a), _ptr(q.absmax_a), _ptr(q.codes_b), _ptr(q.absmax_b), _ptr(q.row_bits),
-                            _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels), _ptr(q.thresholds), _ptr(q.sigma),
-                            _ptr(q.h), _ptr(q.Ap), _ptr(q.Bpt), _ptr(ws), ws_bytes, _stream(B.device)),
+                            _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels_a), _ptr(q.thresholds_a),
+                            _ptr(q.levels_b), _ptr(q.thresholds_b), _ptr(q.sigma), _ptr(q.h), _ptr(q.Ap),
+                            _ptr(q.Bpt), _ptr(ws), ws_bytes, _stream(B.device)),
            "lq_loraquant")
     return q
 
@@ -467,8 +470,9 @@ def loraquant_dequant(q: QuantAdapter):
     ws_bytes = lib.lq_loraquant_dequant_workspace(q.N, q.K, q.r)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _check(lib.lq_loraquant_dequant(_ptr(q.codes_a), _ptr(q.absmax_a), _ptr(q.codes_b), _ptr(q.absmax_b),
-                                    _ptr(q.row_bits), _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels),
-                                    q.N, q.K, q.r, _ptr(A), _ptr(B), _ptr(ws), ws_bytes, _stream(dev)),
+                                    _ptr(q.row_bits), _ptr(q.offsets_a), _ptr(q.offsets_b), _ptr(q.levels_a),
+                                    _ptr(q.levels_b), q.N, q.K, q.r, _ptr(A), _ptr(B), _ptr(ws), ws_bytes,
+                                    _stream(dev)),
            "lq_loraquant_dequant")
     return A, B
 

@@ -384,7 +384,7 @@ int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32
 
 static int check_loraquant_shape(int64_t N, int64_t K, int32_t r) {
   if (N <= 0 || K <= 0 || N % 64 != 0 || K % 64 != 0 || r < 1) return LQ_ERR_SHAPE;
-  if (r > LQ_LORAQUANT_MAX_R) return LQ_ERR_UNSUPPORTED;
+  if (r > LQ_LORAQUANT_MAX_R || N > LQ_LLOYD_MAX_K || K > LQ_LLOYD_MAX_K) return LQ_ERR_UNSUPPORTED;
   return LQ_OK;
 }
 
@@ -395,19 +395,19 @@ size_t lq_loraquant_workspace(int64_t N, int64_t K, int32_t r) {
 
 int lq_loraquant(const float* B, const float* A, int64_t N, int64_t K, int32_t r, double rho, int32_t h,
                  int32_t bits_hi, int32_t bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
-                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels,
-                 float* thresholds, float* sigma, int32_t* h_out, float* Ap, float* Bpt, void* workspace,
-                 size_t ws_bytes, void* stream) {
+                 float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b, float* levels_a,
+                 float* thresholds_a, float* levels_b, float* thresholds_b, float* sigma, int32_t* h_out, float* Ap,
+                 float* Bpt, void* workspace, size_t ws_bytes, void* stream) {
   if (!B || !A || !codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b ||
-      !levels || !thresholds || !sigma || !h_out)
+      !levels_a || !thresholds_a || !levels_b || !thresholds_b || !sigma || !h_out)
     return LQ_ERR_ARG;
   if (bits_hi < 1 || bits_hi > 4 || bits_lo < 1 || bits_lo > 4 || h > r) return LQ_ERR_ARG;
   const int st = check_loraquant_shape(N, K, r);
   if (st != LQ_OK) return st;
   if (!workspace || ws_bytes < loraquant_ws_bytes(N, K, r)) return LQ_ERR_WORKSPACE;
   return launch_status(launch_loraquant(B, A, N, K, r, rho, h, bits_hi, bits_lo, codes_a, absmax_a, codes_b,
-                                        absmax_b, row_bits, offsets_a, offsets_b, levels, thresholds, sigma, h_out,
-                                        Ap, Bpt, workspace, (hipStream_t)stream));
+                                        absmax_b, row_bits, offsets_a, offsets_b, levels_a, thresholds_a, levels_b,
+                                        thresholds_b, sigma, h_out, Ap, Bpt, workspace, (hipStream_t)stream));
 }
 
 size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r) {
@@ -417,10 +417,11 @@ size_t lq_loraquant_dequant_workspace(int64_t N, int64_t K, int32_t r) {
 
 int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const uint8_t* codes_b,
                          const float* absmax_b, const uint8_t* row_bits, const int64_t* offsets_a,
-                         const int64_t* offsets_b, const float* levels, int64_t N, int64_t K, int32_t r,
-                         uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes, void* stream) {
-  if (!codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b || !levels ||
-      !A_bf16 || !B_bf16)
+                         const int64_t* offsets_b, const float* levels_a, const float* levels_b, int64_t N,
+                         int64_t K, int32_t r, uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  if (!codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b || !levels_a ||
+      !levels_b || !A_bf16 || !B_bf16)
     return LQ_ERR_ARG;
   const int st = check_loraquant_shape(N, K, r);
   if (st != LQ_OK) return st;
@@ -434,12 +435,13 @@ int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const ui
   qa.qc = QConst{absmax_a, nullptr, nullptr, nullptr};
   qa.row_bits = row_bits;
   qa.row_offset = offsets_a;
-  qa.levels = levels;
+  qa.levels = levels_a;
   QWeight qb = qa;
   qb.K = N;
   qb.codes = codes_b;
   qb.qc = QConst{absmax_b, nullptr, nullptr, nullptr};
   qb.row_offset = offsets_b;
+  qb.levels = levels_b;
   hipError_t e = launch_dequant(qa, A_bf16, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   uint16_t* bt = (uint16_t*)workspace;   // B'^T [r, N]

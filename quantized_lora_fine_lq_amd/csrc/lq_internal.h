@@ -50,15 +50,6 @@ struct LloydInit {
 };
 const LloydInit& lloyd_init();
 
-// NormalFloat codebooks of widths 1..4 (index b - 1) in the codebook format:
-// float32 levels (the 2^b NF_b levels rounded to nearest, the rest repeating
-// the last) and thresholds (largest float32 not above the midpoints of
-// adjacent float32 levels, the rest 3.0).
-struct NfCodebooks {
-  float L[4][16];
-  float T[4][15];
-};
-const NfCodebooks& nf_codebooks();
 
 // Quantized-weight view used by the kernels.
 struct QWeight {
@@ -106,8 +97,8 @@ size_t loraquant_ws_bytes(int64_t N, int64_t K, int r);
 hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K, int r, double rho, int h_fixed,
                             int bits_hi, int bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
                             float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b,
-                            float* levels, float* thresholds, float* sigma, int32_t* h_out, float* Ap_out,
-                            float* Bpt_out, void* ws, hipStream_t s);
+                            float* levels_a, float* thresholds_a, float* levels_b, float* thresholds_b,
+                            float* sigma, int32_t* h_out, float* Ap_out, float* Bpt_out, void* ws, hipStream_t s);
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* thresholds, uint8_t* codes, float* absmax,

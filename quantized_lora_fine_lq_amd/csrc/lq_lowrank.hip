@@ -694,7 +694,7 @@ hipError_t launch_loftq(const float* W, int64_t N, int64_t K, bool dq, int r, in
 // and key design): SVD reparameterization B A = B' A' with B' = U S^(1/2),
 // A' = S^(1/2) V^T, the important components (by singular value) at a higher
 // width, the rest at an ultra-low width, each component vector quantized in
-// the codebook format with the NormalFloat tables of its width.
+// the codebook format with its own weighted Lloyd-Max codebook of its width.
 //
 // The SVD needs only r x r work: with G_B = B^T B, G_A = A A^T = L_A L_A^T
 // and S = L_A^T G_B L_A = W diag(sigma^2) W^T,
@@ -707,10 +707,9 @@ constexpr int LQ_D = LQ_LORAQUANT_MAX_R;
 
 __global__ __launch_bounds__(256) void k_adapter_core(const double* __restrict__ GB, const double* __restrict__ GA,
                                                       int r, double rho, int h_fixed, int bits_hi, int bits_lo,
-                                                      NfCodebooks tabs, double* __restrict__ MBt,
-                                                      double* __restrict__ MA, float* __restrict__ sigma,
-                                                      int32_t* __restrict__ h_out, uint8_t* __restrict__ row_bits,
-                                                      float* __restrict__ levels, float* __restrict__ thresholds) {
+                                                      double* __restrict__ MBt, double* __restrict__ MA,
+                                                      float* __restrict__ sigma, int32_t* __restrict__ h_out,
+                                                      uint8_t* __restrict__ row_bits) {
   __shared__ double sA[LQ_D][LQ_D + 1];   // G_A (destroyed), then G_B L_A, then W
   __shared__ double sL[LQ_D][LQ_D + 1];   // L_A
   __shared__ double sI[LQ_D][LQ_D + 1];   // L_A^{-1}
@@ -800,12 +799,7 @@ __global__ __launch_bounds__(256) void k_adapter_core(const double* __restrict__
       MBt[k * r + j] = (rs > 0.0) ? b / rs : 0.0;                    // M_B^T[k][j]
       MA[k * r + j] = rs * a;                                         // M_A[k][j]
     }
-  for (int k = t; k < r; k += 256) {
-    const int bits = (k < h) ? bits_hi : bits_lo;
-    row_bits[k] = (uint8_t)bits;
-    for (int q = 0; q < 16; ++q) levels[k * 16 + q] = tabs.L[bits - 1][q];
-    for (int q = 0; q < 15; ++q) thresholds[k * 15 + q] = tabs.T[bits - 1][q];
-  }
+  for (int k = t; k < r; k += 256) row_bits[k] = (uint8_t)((k < h) ? bits_hi : bits_lo);
 }
 
 // out[i][c] = sum_j M[i][j] X(j, c) for i < r, c < C, summed in float64;
@@ -920,8 +914,8 @@ size_t loraquant_ws_bytes(int64_t N, int64_t K, int r) {
 hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K, int r, double rho, int h_fixed,
                             int bits_hi, int bits_lo, uint8_t* codes_a, float* absmax_a, uint8_t* codes_b,
                             float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b,
-                            float* levels, float* thresholds, float* sigma, int32_t* h_out, float* Ap_out,
-                            float* Bpt_out, void* ws, hipStream_t s) {
+                            float* levels_a, float* thresholds_a, float* levels_b, float* thresholds_b,
+                            float* sigma, int32_t* h_out, float* Ap_out, float* Bpt_out, void* ws, hipStream_t s) {
   LqWs w = carve_lq(ws, N, K, r);
   float* Ap = Ap_out ? Ap_out : w.Ap;
   float* Bpt = Bpt_out ? Bpt_out : w.Bpt;
@@ -930,16 +924,19 @@ hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K
   hipLaunchKernelGGL(k_transpose_f32, dim3((unsigned)((K * r + 255) / 256)), dim3(256), 0, s, A, r, K, w.At);
   if ((e = gram(w.At, K, r, w.gpart, w.GA, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_adapter_core, dim3(1), dim3(256), 0, s, w.GB, w.GA, r, rho, h_fixed, bits_hi, bits_lo,
-                     nf_codebooks(), w.MBt, w.MA, sigma, h_out, row_bits, levels, thresholds);
+                     w.MBt, w.MA, sigma, h_out, row_bits);
   hipLaunchKernelGGL(k_small_left, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, w.MA, r, A, K, 0, Ap);
   hipLaunchKernelGGL(k_small_left, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, w.MBt, r, B, N, 1, Bpt);
   hipLaunchKernelGGL(k_sign_fix, dim3((unsigned)r), dim3(256), 0, s, Ap, K, Bpt, N);
   hipLaunchKernelGGL(k_row_offsets, dim3(1), dim3(64), 0, s, row_bits, r, K, N, offsets_a, offsets_b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_quantize_codebook(Ap, LQ_F32, r, K, row_bits, offsets_a, thresholds, codes_a, absmax_a, s)) !=
+  // per-component codebooks (weighted Lloyd-Max, 100 iterations at most), then quantization
+  if ((e = launch_lloyd(Ap, LQ_F32, r, K, row_bits, 100, levels_a, thresholds_a, nullptr, s)) != hipSuccess) return e;
+  if ((e = launch_lloyd(Bpt, LQ_F32, r, N, row_bits, 100, levels_b, thresholds_b, nullptr, s)) != hipSuccess) return e;
+  if ((e = launch_quantize_codebook(Ap, LQ_F32, r, K, row_bits, offsets_a, thresholds_a, codes_a, absmax_a, s)) !=
       hipSuccess)
     return e;
-  return launch_quantize_codebook(Bpt, LQ_F32, r, N, row_bits, offsets_b, thresholds, codes_b, absmax_b, s);
+  return launch_quantize_codebook(Bpt, LQ_F32, r, N, row_bits, offsets_b, thresholds_b, codes_b, absmax_b, s);
 }
 
 }  // namespace lq

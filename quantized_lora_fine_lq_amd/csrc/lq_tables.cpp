@@ -131,23 +131,6 @@ LloydInit build_lloyd_init() {
 
 }  // namespace
 
-const NfCodebooks& nf_codebooks() {
-  static NfCodebooks nc;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    const LloydInit& li = lloyd_init();
-    for (int b = 1; b <= 4; ++b) {
-      const int n = 1 << b;
-      for (int i = 0; i < 16; ++i) nc.L[b - 1][i] = (float)li.L[b - 1][i < n ? i : n - 1];
-      for (int i = 0; i < 15; ++i)
-        nc.T[b - 1][i] = (i < n - 1)
-                             ? largest_f32_not_above(((double)nc.L[b - 1][i] + (double)nc.L[b - 1][i + 1]) / 2.0)
-                             : 3.0f;
-    }
-  });
-  return nc;
-}
-
 const LloydInit& lloyd_init() {
   static LloydInit li;
   static std::once_flag once;

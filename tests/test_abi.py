@@ -255,7 +255,7 @@ def test_loraquant_validation(lq):
     assert L.lq_loraquant_workspace(250, 512, 16) == 0     # N % 64
     assert L.lq_loraquant_workspace(256, 512, 65) == 0     # r > 64
     ws = L.lq_loraquant_workspace(256, 512, 16)
-    args = [fake, fake, 256, 512, 16, 0.9, -1, 3, 1] + [fake] * 13 + [fake, ws, null]
+    args = [fake, fake, 256, 512, 16, 0.9, -1, 3, 1] + [fake] * 15 + [fake, ws, null]
     a = list(args); a[9] = null
     assert L.lq_loraquant(*a) == lq.LQ_ERR_ARG
     a = list(args); a[7] = 5
@@ -266,12 +266,17 @@ def test_loraquant_validation(lq):
     assert L.lq_loraquant(*a) == lq.LQ_ERR_SHAPE
     a = list(args); a[4] = 65
     assert L.lq_loraquant(*a) == lq.LQ_ERR_UNSUPPORTED
-    a = list(args); a[23] = ws - 1
+    a = list(args); a[2] = 16448                           # beyond the codebook learner's row length
+    assert L.lq_loraquant(*a) == lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_loraquant_workspace(16448, 512, 16) == 0
+    a = list(args); a[25] = ws - 1
     assert L.lq_loraquant(*a) == lq.LQ_ERR_WORKSPACE
     dws = L.lq_loraquant_dequant_workspace(256, 512, 16)
     assert dws == 256 * 16 * 2
-    dargs = [fake] * 8 + [256, 512, 16, fake, fake, fake, dws, null]
-    d = list(dargs); d[11] = null
+    dargs = [fake] * 9 + [256, 512, 16, fake, fake, fake, dws, null]
+    d = list(dargs); d[12] = null
     assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_ARG
-    d = list(dargs); d[14] = dws - 1
+    d = list(dargs); d[8] = null
+    assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_ARG
+    d = list(dargs); d[15] = dws - 1
     assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_WORKSPACE

@@ -279,3 +279,38 @@ def test_loftq_full_size(lq, torch):
     o5 = host(ob5)
     assert o5[0] == host(ob1)[0]
     assert o5[-1] < o5[0]
+
+
+def test_loraquant_full_size(lq, torch):
+    """LoRAQuant-style quantization of the MLP-up adapter (B 11008 x 64,
+    A 64 x 4096, bf16 values), as bench.py times it: factors and singular
+    values against the oracle's SVD of B A, the component count from the same
+    float32 singular values, each component's learned codebook within one
+    float32 ulp of the oracle learner's on the GPU's factors, and the codes
+    bit-exact given the GPU's tables."""
+    from oracle import loraquant
+    L = syn.LAYERS["mlp_up"]
+    A = syn.lora_a(L).f32
+    B = syn.lora_b(L).f32
+    q = lq.loraquant(dev(torch, B), dev(torch, A), rho=0.9, bits_hi=3, bits_lo=1)
+    r, N, K = L.r, L.N, L.K
+    Ap = host(q.Ap).reshape(r, K)
+    Bp = host(q.Bpt).reshape(r, N).T
+    sig = host(q.sigma)
+    Bo, Ao, so = loraquant.reparam(B, A)
+    assert np.max(np.abs(sig - so) / so) <= 1e-5
+    assert np.max(np.abs(Ap - Ao)) <= 1e-4 * np.max(np.abs(Ao))
+    h = int(host(q.h)[0])
+    assert h == loraquant.choose_h(sig, 0.9)
+    bits = loraquant.component_bits(r, h, 3, 1)
+    qo = loraquant.quantize(Bp, Ap, bits)
+    for side, X, codes, absmax, lv, th in (
+            ("A", Ap, q.codes_a, q.absmax_a, q.levels_a, q.thresholds_a),
+            ("B", np.ascontiguousarray(Bp.T), q.codes_b, q.absmax_b, q.levels_b, q.thresholds_b)):
+        Lg, T = host(lv).reshape(r, 16), host(th).reshape(r, 15)
+        Lr = qo[side]["levels"]
+        near = (Lg == Lr) | (Lg == np.nextafter(Lr, np.float32(np.inf))) | (Lg == np.nextafter(Lr, np.float32(-np.inf)))
+        assert np.all(near), side
+        packed, c, _ = codebook.quantize(X, bits, T)
+        assert np.array_equal(host(absmax), c)
+        assert np.array_equal(host(codes)[:packed.size], packed)

@@ -55,25 +55,31 @@ def test_choose_h_by_hand():
     assert loraquant.choose_h(np.zeros(4), 0.9) == 0
 
 
-def test_nf_tables():
-    lv, th = loraquant.nf_tables(4)
-    assert np.array_equal(lv, nf4.levels()) and np.array_equal(th, nf4.thresholds())
-    lv, th = loraquant.nf_tables(1)
-    assert np.array_equal(lv[:2], [-1.0, 1.0]) and np.all(lv[2:] == 1.0)
-    assert th[0] == 0.0 and np.all(th[1:] == 3.0)
-
-
-def test_four_bit_components_are_nf4_rows():
-    """With 4 bits everywhere each component vector is NF4-quantized: the
-    dequantized A' equals NF4's dequantization of A' with float32 constants."""
+def test_components_use_their_learned_nearest_levels():
+    """Each component vector's codes pick its nearest learned level (ties to
+    the lower), and the learned 1-bit levels leave less error than the fixed
+    {-1, +1} start would (the learner never raises a row's error)."""
     rng = np.random.default_rng(2)
     B = (rng.standard_normal((128, 8)) * 0.02).astype(np.float32)
     A = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
-    out = loraquant.loraquant(B, A, bits_hi=4, bits_lo=4, h=3)
-    packed, c = nf4.quantize(out["Ap"])
-    assert np.array_equal(out["A_deq"].astype(np.float32), nf4.dequant(packed, c, out["Ap"].shape))
-    packed, c = nf4.quantize(np.ascontiguousarray(out["Bp"].T))
-    assert np.array_equal(out["B_deq"].T.astype(np.float32), nf4.dequant(packed, c, (8, 128)))
+    out = loraquant.loraquant(B, A, bits_hi=3, bits_lo=1, h=3)
+    bits = out["bits"]
+    qa = out["q"]["A"]
+    X = out["Ap"]
+    c = nf4.block_absmax(X)
+    x = nf4.normalise(X, c).reshape(X.shape).astype(np.float64)
+    got = (out["A_deq"] / np.repeat(c, 64).reshape(X.shape)).astype(np.float64)   # level per element
+    for i, b in enumerate(bits):
+        n = 1 << int(b)
+        lv = qa["levels"][i, :n].astype(np.float64)
+        near = lv[np.argmin(np.abs(x[i][:, None] - lv[None, :]), axis=1)]
+        assert np.allclose(got[i], near, rtol=2 ** -8, atol=0)       # bf16 of level * absmax
+    # 1-bit rows: learned levels beat the {-1, +1} start
+    for i in np.nonzero(bits == 1)[0]:
+        lv = qa["levels"][i, :2].astype(np.float64)
+        err_learned = np.sum((x[i] - lv[(x[i] > qa["thresholds"][i, 0]).astype(int)]) ** 2)
+        err_start = np.sum((x[i] - np.where(x[i] > 0, 1.0, -1.0)) ** 2)
+        assert err_learned < err_start
 
 
 def test_more_bits_less_error_and_zero_adapter():
