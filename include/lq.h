@@ -224,7 +224,8 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M,
                      void* H, int32_t h_dtype, float* t_save,
                      void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for lq_lora_down with M rows, K columns and rank r. */
+/* Workspace bytes for lq_lora_down: 0 (no workspace is needed; the
+ * workspace arguments of lq_lora_down are ignored and may be NULL / 0). */
 size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r);
 
 /*
@@ -232,15 +233,14 @@ size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r);
  * t = X A^T in float32.
  *   X [M, K] bf16, A [r, K] bf16, t [M, r] float32 (written).
  * Errors: LQ_ERR_ARG, LQ_ERR_SHAPE (M, K <= 0, K % 8 != 0, r outside
- * [1, 128]), LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH.
+ * [1, 128]), LQ_ERR_LAUNCH.
  */
 int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
                  void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for lq_dequant_gemm with M tokens and rank r: the bf16
- * LoRA-segment operands of the MFMA path, (M + N) * 64 * ceil(2r / 64) * 2
- * bytes (rounded up to 256), plus N * K * 2 bytes for the dequantized weight
- * of a codebook weight; 0 when the GEMV path is taken (M <= 16, NF4). */
+/* Workspace bytes for lq_dequant_gemm with M tokens and rank r: N * K * 2
+ * bytes (rounded up to 256) for the dequantized weight of a codebook weight;
+ * 0 for NF4 weights (the kernels form the LoRA-segment operands themselves). */
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
@@ -249,16 +249,15 @@ size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM; a codebook weight is
  * dequantized into the workspace first). Arguments as lq_qlora_forward;
  * t [M, r] float32 is read. The workspace (caller-owned,
- * lq_dequant_gemm_workspace bytes) receives the LoRA operands of the MFMA
- * path (and the dequantized codebook weight); it may be NULL when the GEMV
- * path is taken (M <= 16, NF4).
+ * lq_dequant_gemm_workspace bytes) receives the dequantized codebook weight;
+ * it may be NULL when that size is 0.
  */
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
                     const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
                     void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for lq_dequant_gemm_t: (M + K) * 64 * ceil(2r / 64) * 2
- * (rounded up to 256), plus N * K * 2 for a codebook weight. */
+/* Workspace bytes for lq_dequant_gemm_t: N * K * 2 (rounded up to 256) for a
+ * codebook weight, 0 for NF4. */
 size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
@@ -268,7 +267,7 @@ size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *   G [M, N] bf16, u [M, r] float32, A [r, K] bf16, grad_X [M, K] bf16.
  * NF4 weights are dequantized inside the GEMM, codebook weights into the
  * workspace first. N % 8 == 0 (LQ_ERR_SHAPE); workspace of
- * lq_dequant_gemm_t_workspace bytes (LQ_ERR_WORKSPACE).
+ * lq_dequant_gemm_t_workspace bytes (LQ_ERR_WORKSPACE; NULL allowed when 0).
  */
 int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const float* u,
                       const uint16_t* A, int32_t r, float alpha, uint16_t* grad_X,
@@ -288,7 +287,9 @@ size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *   t_saved [M, r] float32 from the forward, or NULL to recompute t = X A^T
  *   grad_X, dA, dB may each be NULL to skip that output.
  * Requires N % 8 == 0 (LQ_ERR_SHAPE). For a codebook weight, grad_X
- * dequantizes it into the workspace first.
+ * dequantizes it into the workspace first. The workspace
+ * (lq_backward_workspace bytes) holds u, B^T and partial sums; the
+ * call sets up whatever it needs, so its contents on entry do not matter.
  * Errors: as lq_qlora_forward.
  */
 int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,

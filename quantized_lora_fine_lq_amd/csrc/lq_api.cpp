@@ -64,17 +64,16 @@ struct Carver {
 };
 
 size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
-  return align_up((size_t)M * r * sizeof(float)) + align_up(row_skinny_ws_floats(M, w.K, r) * sizeof(float)) +
-         align_up(gemm_ws_bytes(w, M, r, true));
+  return align_up((size_t)M * r * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, true));
 }
 
+// u, recomputed t, B^T, split t and u, partial sums of dB and of dA, GEMM
+// workspace
 size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
-  size_t part = row_skinny_ws_floats(M, w.K, r);
-  const size_t cands[3] = {row_skinny_ws_floats(M, w.N, r), col_skinny_ws_floats(M, w.K, r),
-                           col_skinny_ws_floats(M, w.N, r)};
-  for (size_t c : cands) part = c > part ? c : part;
   return 2 * align_up((size_t)M * r * sizeof(float)) + align_up((size_t)w.N * r * sizeof(uint16_t)) +
-         align_up(part * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
+         2 * align_up((size_t)2 * r * split_rows(M) * sizeof(uint16_t)) +
+         align_up(col_skinny_ws_floats(M, w.N, r) * sizeof(float)) +
+         align_up(col_skinny_ws_floats(M, w.K, r) * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
 }
 
 }  // namespace
@@ -183,29 +182,25 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   hipStream_t s = (hipStream_t)stream;
   Carver cv(workspace);
   float* t_ws = cv.take<float>((size_t)M * r);
-  float* part = cv.take<float>(row_skinny_ws_floats(M, q.K, r));
-  uint16_t* lora = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
+  uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
-  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, part, s);
+  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, nullptr, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (use_gemv(q, M)) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
-  else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, lora, s);
+  else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, gws, s);
   return launch_status(e);
 }
 
-size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r) {
-  if (M <= 0 || K <= 0 || r < 1 || r > 128) return 0;
-  return align_up(row_skinny_ws_floats(M, K, r) * sizeof(float));
-}
+size_t lq_lora_down_workspace(int64_t, int64_t, int32_t) { return 0; }
 
 int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
                  void* workspace, size_t ws_bytes, void* stream) {
   if (!X || !A || !t) return LQ_ERR_ARG;
   if (M <= 0 || K <= 0 || K % 8 != 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
-  const size_t need = lq_lora_down_workspace(M, K, r);
-  if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
-  return launch_status(launch_row_skinny(X, M, K, A, r, t, (float*)workspace, (hipStream_t)stream));
+  (void)workspace;
+  (void)ws_bytes;
+  return launch_status(launch_row_skinny(X, M, K, A, r, t, nullptr, (hipStream_t)stream));
 }
 
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r) {
@@ -227,7 +222,8 @@ int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const flo
   hipStream_t s = (hipStream_t)stream;
   const float scale = alpha / (float)r;
   if (use_gemv(q, M)) return launch_status(launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s));
-  if (!workspace || ws_bytes < gemm_ws_bytes(q, M, r, true)) return LQ_ERR_WORKSPACE;
+  const size_t need = gemm_ws_bytes(q, M, r, true);
+  if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
   return launch_status(launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, (uint16_t*)workspace, s));
 }
 
@@ -245,7 +241,8 @@ int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const f
   if (st != LQ_OK) return st;
   if (!G || !u || !A || !grad_X) return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
-  if (!workspace || ws_bytes < gemm_ws_bytes(q, M, r, false)) return LQ_ERR_WORKSPACE;
+  const size_t need = gemm_ws_bytes(q, M, r, false);
+  if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
   return launch_status(launch_gemm_bwd(q, G, M, u, A, r, alpha / (float)r, grad_X, (uint16_t*)workspace,
                                        (hipStream_t)stream));
 }
@@ -273,33 +270,37 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   float* u = cv.take<float>((size_t)M * r);
   float* t_ws = cv.take<float>((size_t)M * r);
   uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
-  uint16_t* lora = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
-  float* part = reinterpret_cast<float*>(cv.base + cv.used);
+  uint16_t* pt2_t = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
+  uint16_t* pt2_u = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
+  float* part_b = cv.take<float>(col_skinny_ws_floats(M, q.N, r));
+  float* part_a = cv.take<float>(col_skinny_ws_floats(M, q.K, r));
+  uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
   const float scale = alpha / (float)r;
   hipError_t e = hipSuccess;
   const float* t = t_saved;
   if (!t) {
-    e = launch_row_skinny(X, M, q.K, A, r, t_ws, part, s);
+    e = launch_row_skinny(X, M, q.K, A, r, t_ws, nullptr, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
     t = t_ws;
   }
-  e = launch_transpose_u16(B, q.N, r, Bt, s);
+  e = launch_bwd_prep(B, q.N, r, Bt, t, M, pt2_t, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  e = launch_row_skinny(G, M, q.N, Bt, r, u, part, s);
+  e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  SplitJobDesc job_b, job_a;
   if (dB) {
-    e = launch_col_skinny(t, G, M, q.N, r, scale, dB, true, part, s);
+    e = launch_col_skinny(pt2_t, G, M, q.N, r, scale, dB, true, part_b, &job_b, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
   }
   if (grad_X) {
-    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, lora, s);
+    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
   }
   if (dA) {
-    e = launch_col_skinny(u, X, M, q.K, r, scale, dA, false, part, s);
+    e = launch_col_skinny(pt2_u, X, M, q.K, r, scale, dA, false, part_a, &job_a, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
   }
-  return LQ_OK;
+  return launch_status(launch_reduce_splits2(job_b, job_a, s));
 }
 
 int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,

@@ -19,8 +19,9 @@ namespace {
 // bf16 weight that the codebook format's dequantization writes first) followed by a LoRA
 // segment of 2r columns: A-side [hi(s*L) | lo(s*L)] with L = t (forward) or
 // u (backward) split into two bfloat16 terms, Bt-side [Lb | Lb] with
-// Lb = B (forward) or A^T (backward). hi + lo carries L to about 2^-17, so
-// the LoRA term is computed at float32-like accuracy on the bf16 MFMA.
+// Lb = B (forward) or A^T (backward), both formed in the kernel from the
+// float32 L and the bf16 adapter. hi + lo carries L to about 2^-17, so the
+// LoRA term is computed at float32-like accuracy on the bf16 MFMA.
 //
 // Tile 256 x 128 x 64 per 512-thread workgroup (8 waves, two per SIMD, so
 // one wave's MFMAs overlap the other's loads, dequantization and LDS
@@ -41,9 +42,12 @@ constexpr int GEMM_THREADS = 512;
 struct GemmParams {
   const uint16_t* A;   // [M, Kc] bf16, row stride Kc
   int64_t M, Ncols, Kc;
-  const uint16_t* t2;  // LoRA segment, A-side [M, R2] bf16: [hi(s L) | lo(s L) | 0]
-  const uint16_t* lb2; // LoRA segment, Bt-side [Ncols, R2] bf16: [Lb | Lb | 0]
-  int R2;              // 64 * ceil(2r / 64)
+  const float* L;      // LoRA segment source, A-side: t (forward) or u (backward), float32 [M, r]
+  const uint16_t* lb;  // Bt-side source: B [Ncols, r] (forward) or A [r, Ncols] (backward), bf16
+  int r;
+  float s;             // alpha / r
+  int fwd;             // 1: Lb(n, j) = B[n][j]; 0: Lb(n, j) = A[j][n]
+  int R2;              // 64 * ceil(2r / 64) columns of the LoRA segment
   int gm;              // M-tiles per group of the tile order
   void* out;           // [M, Ncols]
   QWeight w;
@@ -108,68 +112,50 @@ __device__ __forceinline__ void mfma_half(const uint16_t* sAt, const uint16_t* s
 }
 
 // ---- LoRA segment tiles -------------------------------------------------------
-// Step jt of the LoRA segment: the A-side tile from t2 (same thread mapping
-// and row clamping as the main A tiles) and the Bt-side tile from lb2
-// (thread -> row t/4, columns 16 (t % 4) .. +16).
+// Step jt covers segment columns c = 64 jt + [0, 64): column c < r holds
+// hi(s L[m][c]) on the A side and Lb(n, c) on the Bt side, column r <= c < 2r
+// holds lo(s L[m][c - r]) and Lb(n, c - r), the rest are zero. The A-side tile
+// uses the main A tiles' thread mapping and row clamping; the Bt-side tile
+// maps thread -> row t/4, columns 16 (t % 4) .. +16 (rows past Ncols repeat
+// the last one: their outputs are never stored).
 __device__ __forceinline__ void lora_tiles(const GemmParams& p, int jt, int64_t m0, int64_t n0,
                                            uint16_t* sA, uint16_t* sB) {
+  const int cA = BK * jt + 8 * (threadIdx.x & 7);
   u32x4_t ra[4];
-  const uint16_t* abase = p.t2 + (int64_t)jt * BK + 8 * (threadIdx.x & 7);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ra[q] = ld16(abase + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.R2);
+  for (int q = 0; q < 4; ++q) {
+    const float* lrow = p.L + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.r;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = cA + e;
+      float x = 0.0f;
+      if (c < 2 * p.r) {
+        float hi, lo;
+        split_bf16(p.s * lrow[c < p.r ? c : c - p.r], hi, lo);
+        x = (c < p.r) ? hi : lo;
+      }
+      v[e] = x;
+    }
+    ra[q] = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
   const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
-  const uint16_t* bsrc = p.lb2 + min(n0 + row, p.Ncols - 1) * p.R2 + (int64_t)jt * BK + 16 * qq;
-  const u32x4_t b0 = ld16(bsrc), b1 = ld16(bsrc + 8);
+  const int64_t n = min(n0 + row, p.Ncols - 1);
+  uint32_t h[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int c = BK * jt + 16 * qq + e;
+    uint32_t x = 0;
+    if (c < 2 * p.r) {
+      const int j = c < p.r ? c : c - p.r;
+      x = p.fwd ? p.lb[n * p.r + j] : p.lb[(int64_t)j * p.Ncols + n];
+    }
+    h[e] = x;
+  }
   store_a_tile(sA, ra);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
-  dst[0] = b0;
-  dst[1] = b1;
-}
-
-// LoRA segment operands, one 16-byte chunk per thread and grid-stride step:
-// rows [0, M) of the A-side t2 from L (t or u), then rows [0, Ncols) of the
-// Bt-side lb2 from Lb (B[n][j] forward, A[j][n] backward).
-__global__ __launch_bounds__(256) void k_lora_operands(const float* L, int64_t M, const uint16_t* lb,
-                                                       int64_t Ncols, int64_t K, int r, int R2, float s,
-                                                       int fwd, uint16_t* t2, uint16_t* lb2) {
-  const int64_t per_row = R2 / 8;
-  const int64_t total = (M + Ncols) * per_row;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t row = i / per_row;
-    const int c0 = (int)(i % per_row) * 8;
-    float v[8];
-    uint32_t h[8];
-    if (row < M) {
-      const float* src = L + row * r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        float x = 0.0f;
-        if (c < 2 * r) {
-          float hi, lo;
-          split_bf16(s * src[c < r ? c : c - r], hi, lo);
-          x = (c < r) ? hi : lo;
-        }
-        v[e] = x;
-      }
-      *reinterpret_cast<u32x4_t*>(t2 + row * R2 + c0) =
-          u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-    } else {
-      const int64_t n = row - M;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = c0 + e;
-        uint32_t x = 0;
-        if (c < 2 * r) {
-          const int j = c < r ? c : c - r;
-          x = fwd ? lb[n * r + j] : lb[(int64_t)j * K + n];
-        }
-        h[e] = x;
-      }
-      *reinterpret_cast<u32x4_t*>(lb2 + n * R2 + c0) =
-          u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    }
-  }
+  dst[0] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  dst[1] = u32x4_t{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16), h[14] | (h[15] << 16)};
 }
 
 // ---- Bt producers -----------------------------------------------------------
@@ -685,55 +671,117 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
 // ===========================================================================
 // Skinny products (HBM-bound: they stream X or G once).
 // ===========================================================================
-// Row form: part[split][m][j] = sum_{c in split} Q[m][c] R[j][c] with R
-// [r, C] row-major. MFMA 16x16x32: a wave owns 16 rows of Q, lane (li, lg)
-// reads 8 consecutive columns of Q row li and of R row 16jt + li straight
-// into MFMA registers (R is small and stays in cache); no LDS, no barriers.
-constexpr int RS_ROWS = 64;
-template <int JT>
-__global__ __launch_bounds__(256) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M,
-                                                    int64_t C, const uint16_t* __restrict__ R, int r,
-                                                    int64_t c_per_split, float* __restrict__ out) {
+// Row form: out[m][j] = sum_c Q[m][c] R[j][c] with R [r, C] row-major (C a
+// multiple of 8). One workgroup per 16 G rows of Q (G row groups, more for
+// larger r so that the R fragments, re-read by every workgroup, are shared
+// by more rows); its 8 waves take contiguous runs of 32-column steps. MFMA
+// 16x16x32: lane (li, lg) reads 8 consecutive columns of Q row 16g + li and
+// of R row 16jt + li straight into MFMA registers (R is small and stays in
+// cache). The 8 partial sums meet in LDS, one row group at a time, and are
+// added in wave order, so no second pass is needed. When pt2 is given, the
+// result is also written split and transposed for the column form: pt2
+// [2r][Mp] bf16 = [hi(out)^T ; lo(out)^T], zero for rows M..Mp-1 (the grid
+// then covers Mp rows).
+constexpr int RW_WAVES = 8;
+template <int JT, int G>
+__global__ __launch_bounds__(64 * RW_WAVES) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M,
+                                                              int64_t C, const uint16_t* __restrict__ R, int r,
+                                                              float* __restrict__ out, uint16_t* __restrict__ pt2,
+                                                              int64_t Mp) {
+  __shared__ f32x4_t sPart[RW_WAVES][JT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t m = min((int64_t)blockIdx.x * RS_ROWS + 16 * wave + li, M - 1);
-  const uint16_t* qrow = Q + m * C + 8 * lg;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * G;
+  const uint16_t* qrow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qrow[g] = Q + min(row0 + 16 * g + li, M - 1) * C;   // rows past M: not stored
   const uint16_t* rrow[JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C + 8 * lg;
-  const int64_t c_begin = (int64_t)blockIdx.y * c_per_split;
-  const int64_t c_end = min(C, c_begin + c_per_split);
-  f32x4_t acc[JT];
+  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C;
+  const int64_t steps = (C + 31) / 32;
+  const int64_t per = (steps + RW_WAVES - 1) / RW_WAVES;
+  const int64_t s_begin = min(steps, wave * per), s_end = min(steps, s_begin + per);
+  f32x4_t acc[G][JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t c = c_begin; c < c_end; c += 128) {
-    u32x4_t a[4], b[4][JT];
+  for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t cc = c + 32 * u;
-      const bool ok = cc + 8 * lg + 8 <= c_end;
-      const int64_t off = ok ? cc : c_begin;
-      a[u] = ld16(qrow + off);
+    for (int jt = 0; jt < JT; ++jt) acc[g][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = (G + JT) <= 2 ? 8 : ((G + JT) <= 4 ? 4 : 2);   // steps with loads in flight together
+  for (int64_t st = s_begin; st < s_end; st += U) {
+    u32x4_t a[U][G], b[U][JT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t cc = 32 * (st + u) + 8 * lg;
+      const bool ok = st + u < s_end && cc + 8 <= C;
+      const int64_t off = ok ? cc : 0;   // a lane past the end reads columns 0..7 and adds 0
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        a[u][g] = ld16(qrow[g] + off);
+        if (!ok) zero(a[u][g]);
+      }
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) b[u][jt] = ld16(rrow[jt] + off);
-      if (!ok) zero(a[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt)
-        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b[u][jt]), acc[jt], 0, 0, 0);
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          acc[g][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][g]), as_bf16x8(b[u][jt]), acc[g][jt],
+                                                               0, 0, 0);
   }
-  // D: lane holds column j = 16jt + li, rows 4lg + v
-  float* dst = out + (int64_t)blockIdx.y * M * r;
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) {
-    const int j = 16 * jt + li;
-    if (j >= r) continue;
+  for (int g = 0; g < G; ++g) {
+    if (g > 0) __syncthreads();   // the previous group's sums have been read
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = (int64_t)blockIdx.x * RS_ROWS + 16 * wave + 4 * lg + v;
-      if (row < M) dst[row * r + j] = acc[jt][v];
+    for (int jt = 0; jt < JT; ++jt) sPart[wave][jt][lane] = acc[g][jt];
+    __syncthreads();
+    // thread -> (jt, lane) of the 16 x 16JT output: column j = 16jt + li,
+    // rows 4lg + v of row group g
+    for (int idx = threadIdx.x; idx < JT * 64; idx += 64 * RW_WAVES) {
+      const int jt = idx >> 6, ln = idx & 63;
+      const int j = 16 * jt + (ln & 15);
+      if (j >= r) continue;
+      f32x4_t sum = sPart[0][jt][ln];
+#pragma unroll
+      for (int w = 1; w < RW_WAVES; ++w) {
+        const f32x4_t o = sPart[w][jt][ln];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum[v] += o[v];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + 16 * g + 4 * (ln >> 4) + v;
+        if (row < M) out[row * r + j] = sum[v];
+        if (pt2 && row < Mp) {
+          float hi = 0.0f, lo = 0.0f;
+          if (row < M) split_bf16(sum[v], hi, lo);
+          pt2[(int64_t)j * Mp + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+          pt2[(int64_t)(j + r) * Mp + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
+        }
+      }
+    }
+  }
+}
+
+// Set-up of the backward in one launch: Bt = B^T ([N, r] -> [r, N]) for the
+// row form u = G B, and pt2 = [hi(t)^T ; lo(t)^T] ([2r][Mp] bf16, zero for
+// rows M..Mp-1) for the column form dB = s G^T t.
+__global__ __launch_bounds__(256) void k_bwd_prep(const uint16_t* __restrict__ B, int64_t N, int r,
+                                                  uint16_t* __restrict__ Bt, const float* __restrict__ t, int64_t M,
+                                                  int64_t Mp, uint16_t* __restrict__ pt2) {
+  const int64_t nb = N * r, nt = (int64_t)r * Mp;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nb + nt; i += (int64_t)gridDim.x * 256) {
+    if (i < nb) {
+      const int64_t n = i / r, j = i % r;
+      Bt[j * N + n] = B[i];
+    } else {
+      const int64_t k = i - nb, j = k / Mp, m = k % Mp;
+      float hi = 0.0f, lo = 0.0f;
+      if (m < M) split_bf16(t[m * r + j], hi, lo);
+      pt2[j * Mp + m] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+      pt2[(j + r) * Mp + m] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
     }
   }
 }
@@ -747,30 +795,20 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
   out[j * N + n] = in[i];
 }
 
-// Column form: out(j, c) = sum_m P[m][j] Q[m][c] for j < r, P float32 [M, r]
-// small, Q bfloat16 [M, C] streamed once. P enters as pt2 = [hi(P)^T ;
+// Column form: out(j, c) = scale * sum_m P[m][j] Q[m][c] for j < r, P float32
+// [M, r] small, Q bfloat16 [M, C] streamed once. P enters as pt2 = [hi(P)^T ;
 // lo(P)^T] (bfloat16 [2r, Mp], Mp = M rounded up to 32, zero padded; hi + lo
 // carries P to about 2^-17), so an MFMA A fragment is one 16-byte load. The
 // Q tile [32 m x 128 c] goes through LDS and is gathered along m for the B
-// fragments. Workgroup: 128 columns x one m-split, wave: 32 columns,
-// MFMA 32x32x16 over the 2r product rows; hi and lo rows are added in
-// registers when r % 32 == 0 or r == 16 (partner row in the same lane),
-// otherwise both are written and the reduction adds them.
-__global__ __launch_bounds__(256) void k_split_t(const float* __restrict__ P, int64_t M, int r, int64_t Mp,
-                                                uint16_t* __restrict__ pt2) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // over [r][Mp]
-  if (i >= (int64_t)r * Mp) return;
-  const int64_t j = i / Mp, m = i % Mp;
-  float hi = 0.0f, lo = 0.0f;
-  if (m < M) split_bf16(P[m * r + j], hi, lo);
-  pt2[j * Mp + m] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
-  pt2[(j + r) * Mp + m] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
-}
-
+// fragments. Workgroup: 128 columns x one m-split, wave: 32 columns, MFMA
+// 32x32x16 over the 2r product rows; hi and lo rows are added in registers
+// when r % 32 == 0 or r == 16 (partner row in the same lane), otherwise both
+// are kept. Each workgroup writes the partial sums of its m-split;
+// k_reduce_splits2 adds them.
 template <int JT2>
 __global__ __launch_bounds__(256) void k_col_skinny(const uint16_t* __restrict__ pt2, int64_t Mp,
                                                     const uint16_t* __restrict__ Q, int64_t M, int64_t C, int r,
-                                                    int64_t m_per_split, int combine, float* __restrict__ out) {
+                                                    int64_t m_per_split, int combine, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * (128 + 8)];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 31, lh = lane >> 5;
@@ -831,67 +869,83 @@ __global__ __launch_bounds__(256) void k_col_skinny(const uint16_t* __restrict__
     __syncthreads();
   }
   const int64_t c = c0 + 32 * wave + li;
-  if (c >= C) return;
-  if (combine) {
-    // partner row j + r: tile jt + r/32 (r % 32 == 0) or v + 8 of the same tile (r == 16)
-    float* dst = out + (int64_t)blockIdx.y * r * C;
+  const int srows = combine ? r : rows2;
+  if (c < C) {
+    float* dst = part + (int64_t)blockIdx.y * srows * C;
+    if (combine) {
+      // partner row j + r: tile jt + r/32 (r % 32 == 0) or v + 8 of the same tile (r == 16)
 #pragma unroll
-    for (int jt = 0; jt < JT2; ++jt)
+      for (int jt = 0; jt < JT2; ++jt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (j >= r) continue;
-        float partner = 0.0f;
-        if (r == 16) partner = acc[jt][(v + 8) & 15];
+        for (int v = 0; v < 16; ++v) {
+          const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
+          if (j >= r) continue;
+          float partner = 0.0f;
+          if (r == 16) partner = acc[jt][(v + 8) & 15];
 #pragma unroll
-        for (int pt = 0; pt < JT2; ++pt)
-          if (r % 32 == 0 && pt == jt + r / 32) partner = acc[pt][v];
-        dst[(int64_t)j * C + c] = acc[jt][v] + partner;
-      }
-  } else {
-    float* dst = out + (int64_t)blockIdx.y * rows2 * C;
+          for (int pt = 0; pt < JT2; ++pt)
+            if (r % 32 == 0 && pt == jt + r / 32) partner = acc[pt][v];
+          dst[(int64_t)j * C + c] = acc[jt][v] + partner;
+        }
+    } else {
 #pragma unroll
-    for (int jt = 0; jt < JT2; ++jt)
+      for (int jt = 0; jt < JT2; ++jt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (j < rows2) dst[(int64_t)j * C + c] = acc[jt][v];
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int j = 32 * jt + 8 * (v >> 2) + 4 * lh + (v & 3);
+          if (j < rows2) dst[(int64_t)j * C + c] = acc[jt][v];
+        }
+    }
   }
 }
 
-// out[i] = scale * sum_{s < splits} (part[s][i] + part[s][i + pair]) in a
-// fixed order, where part[s] holds `srows` rows of `cols` and pair is 0 or
-// the offset of a partner row block (hi + lo halves); optional transposed
-// write for [rows, cols] -> [cols, rows].
-__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int splits,
-                                                       int64_t rows, int64_t cols, float scale,
-                                                       float* __restrict__ out, int transposed,
-                                                       int64_t srows, int64_t pair) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = rows * cols, sn = srows * cols;
-  if (i >= n) return;
+// Two split reductions in one launch (dB and dA of the backward): for each
+// i < n1 + n2, out = scale * sum_s (part[s][i] + part[s][i + pair]) in split
+// order, rows x cols per job, optionally written transposed ([cols, rows]).
+struct SplitJob {
+  const float* part;
+  int splits;
+  int64_t rows, cols, srows, pair;
+  float scale;
+  float* out;
+  int transposed;
+};
+
+__device__ __forceinline__ void reduce_one(const SplitJob& jb, int64_t i) {
+  const int64_t sn = jb.srows * jb.cols;
+  const float* ps = jb.part + i;
   float acc = 0.0f;
-  for (int s = 0; s < splits; ++s) {
-    const float* ps = part + (int64_t)s * sn + i;
-    acc += pair ? ps[0] + ps[pair] : ps[0];
+  int s = 0;
+  for (; s + 4 <= jb.splits; s += 4) {   // four loads in flight, added in order
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* q = ps + (int64_t)(s + u) * sn;
+      v[u] = jb.pair ? q[0] + q[jb.pair] : q[0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += v[u];
   }
-  acc *= scale;
-  if (transposed) {
-    const int64_t rr = i / cols, cc = i % cols;
-    out[cc * rows + rr] = acc;
+  for (; s < jb.splits; ++s) {
+    const float* q = ps + (int64_t)s * sn;
+    acc += jb.pair ? q[0] + q[jb.pair] : q[0];
+  }
+  acc *= jb.scale;
+  if (jb.transposed) {
+    const int64_t rr = i / jb.cols, cc = i % jb.cols;
+    jb.out[cc * jb.rows + rr] = acc;
   } else {
-    out[i] = acc;
+    jb.out[i] = acc;
   }
 }
 
-int row_skinny_splits(int64_t M, int64_t C) {
-  const int64_t row_tiles = (M + RS_ROWS - 1) / RS_ROWS;
-  const int64_t chunks = (C + 63) / 64;
-  int64_t splits = (512 + row_tiles - 1) / row_tiles;
-  if (splits > chunks) splits = chunks;
-  if (splits < 1) splits = 1;
-  return (int)splits;
+__global__ __launch_bounds__(256) void k_reduce_splits2(SplitJob j1, SplitJob j2) {
+  const int64_t n1 = j1.out ? j1.rows * j1.cols : 0;
+  const int64_t n2 = j2.out ? j2.rows * j2.cols : 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n1 + n2; i += (int64_t)gridDim.x * 256) {
+    if (i < n1) reduce_one(j1, i);
+    else reduce_one(j2, i - n1);
+  }
 }
 
 int col_skinny_splits(int64_t M, int64_t C) {
@@ -905,30 +959,30 @@ int col_skinny_splits(int64_t M, int64_t C) {
 
 }  // namespace
 
-size_t row_skinny_ws_floats(int64_t M, int64_t C, int r) {
-  const int splits = row_skinny_splits(M, C);
-  return splits > 1 ? (size_t)splits * M * r : 0;
-}
+int64_t split_rows(int64_t M) { return (M + 31) / 32 * 32; }
 
 hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
-                             float* out, float* ws, hipStream_t s) {
-  const int splits = row_skinny_splits(M, C);
-  const int64_t chunks = (C + 63) / 64;
-  const int64_t c_per_split = ((chunks + splits - 1) / splits) * 64;
-  const int real_splits = (int)((C + c_per_split - 1) / c_per_split);
-  float* dst = real_splits > 1 ? ws : out;
-  const dim3 grid((unsigned)((M + RS_ROWS - 1) / RS_ROWS), (unsigned)real_splits);
-  switch ((r + 15) / 16) {
-#define LQ_RS(JT) case JT: hipLaunchKernelGGL(k_row_skinny<JT>, grid, dim3(256), 0, s, Q, M, C, R, r, c_per_split, dst); break;
-    LQ_RS(1) LQ_RS(2) LQ_RS(3) LQ_RS(4) LQ_RS(5) LQ_RS(6) LQ_RS(7) LQ_RS(8)
+                             float* out, uint16_t* pt2, hipStream_t s) {
+  const int64_t Mp = split_rows(M);
+  const int64_t rows = pt2 ? Mp : M;
+  // row groups per workgroup: 1 for r <= 16, 2 for r <= 32, else 4
+  const int jt = (r + 15) / 16;
+  const int g = jt <= 1 ? 1 : (jt <= 2 ? 2 : 4);
+  const dim3 grid((unsigned)((rows + 16 * g - 1) / (16 * g)));
+  switch (jt) {
+#define LQ_RS(JT, G) case JT: hipLaunchKernelGGL((k_row_skinny<JT, G>), grid, dim3(64 * RW_WAVES), 0, s, Q, M, C, R, r, out, pt2, Mp); break;
+    LQ_RS(1, 1) LQ_RS(2, 2) LQ_RS(3, 4) LQ_RS(4, 4) LQ_RS(5, 4) LQ_RS(6, 4) LQ_RS(7, 4) LQ_RS(8, 4)
 #undef LQ_RS
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || real_splits == 1) return e;
-  const int64_t n = M * r;
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ws,
-                     real_splits, M, (int64_t)r, 1.0f, out, 0, M, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* Bt, const float* t, int64_t M,
+                           uint16_t* pt2, hipStream_t s) {
+  const int64_t n = N * r + (int64_t)r * split_rows(M);
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(k_bwd_prep, dim3(blocks), dim3(256), 0, s, B, N, r, Bt, t, M, split_rows(M), pt2);
   return hipGetLastError();
 }
 
@@ -938,82 +992,79 @@ hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* 
   return hipGetLastError();
 }
 
-// workspace: partial sums [splits][2r][C] floats, then pt2 [2r][Mp] bf16
+// workspace: partial sums [splits][2r][C] floats
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r) {
-  const int64_t Mp = (M + 31) / 32 * 32;
-  return (size_t)col_skinny_splits(M, C) * 2 * r * C + (size_t)(2 * r * Mp + 1) / 2;
+  return (size_t)col_skinny_splits(M, C) * 2 * r * C;
 }
 
-hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                             float scale, float* out, bool out_transposed, float* ws,
-                             hipStream_t s) {
+// Partial sums of the column form into ws ([splits][srows][C]); returns the
+// reduction job that finishes it (run by launch_reduce_splits2).
+hipError_t launch_col_skinny(const uint16_t* pt2, const uint16_t* Q, int64_t M, int64_t C, int r, float scale,
+                             float* out, bool out_transposed, float* ws, SplitJobDesc* job, hipStream_t s) {
   const int splits = col_skinny_splits(M, C);
   const int64_t mchunks = (M + 31) / 32;
   const int64_t m_per_split = ((mchunks + splits - 1) / splits) * 32;
   const int real_splits = (int)((M + m_per_split - 1) / m_per_split);
-  const int64_t Mp = mchunks * 32;
-  float* part = ws;
-  uint16_t* pt2 = reinterpret_cast<uint16_t*>(ws + (size_t)splits * 2 * r * C);
-  hipLaunchKernelGGL(k_split_t, dim3((unsigned)(((int64_t)r * Mp + 255) / 256)), dim3(256), 0, s, P, M, r, Mp,
-                     pt2);
   const int combine = (r % 32 == 0 || r == 16) ? 1 : 0;
   const dim3 grid((unsigned)((C + 127) / 128), (unsigned)real_splits);
   switch ((2 * r + 31) / 32) {
-#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, pt2, Mp, Q, M, C, r, m_per_split, combine, part); break;
+#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, pt2, split_rows(M), Q, M, C, r, m_per_split, combine, ws); break;
     LQ_CS(1) LQ_CS(2) LQ_CS(3) LQ_CS(4) LQ_CS(5) LQ_CS(6) LQ_CS(7) LQ_CS(8)
 #undef LQ_CS
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = (int64_t)r * C;
-  const int64_t srows = combine ? r : 2 * r;
-  hipLaunchKernelGGL(k_reduce_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
-                     real_splits, (int64_t)r, C, scale, out, out_transposed ? 1 : 0, srows,
-                     combine ? (int64_t)0 : (int64_t)r * C);
+  job->part = ws;
+  job->splits = real_splits;
+  job->rows = r;
+  job->cols = C;
+  job->srows = combine ? r : 2 * r;
+  job->pair = combine ? 0 : (int64_t)r * C;
+  job->scale = scale;
+  job->out = out;
+  job->transposed = out_transposed ? 1 : 0;
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_splits2(const SplitJobDesc& a, const SplitJobDesc& b, hipStream_t s) {
+  SplitJob j[2];
+  const SplitJobDesc* d[2] = {&a, &b};
+  int64_t n = 0;
+  for (int i = 0; i < 2; ++i) {
+    j[i] = SplitJob{d[i]->part, d[i]->splits, d[i]->rows, d[i]->cols, d[i]->srows, d[i]->pair, d[i]->scale,
+                    d[i]->out, d[i]->transposed};
+    if (d[i]->out) n += d[i]->rows * d[i]->cols;
+  }
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(k_reduce_splits2, dim3(blocks), dim3(256), 0, s, j[0], j[1]);
   return hipGetLastError();
 }
 
 int lora_seg_cols(int r) { return BK * ((2 * r + BK - 1) / BK); }
 
-size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r) {
-  return (size_t)(M + Ncols) * lora_seg_cols(r) * sizeof(uint16_t);
-}
-
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Workspace of the forward / backward GEMM: the LoRA operands, then (codebook
-// format) the dequantized bf16 weight.
-size_t gemm_ws_bytes(const QWeight& w, int64_t M, int r, bool fwd) {
-  size_t b = align256(lora_operands_ws_bytes(M, fwd ? w.N : w.K, r));
-  if (w.format == LQ_FMT_CODEBOOK) b += align256((size_t)w.N * w.K * sizeof(uint16_t));
-  return b;
+// Workspace of the forward / backward GEMM: (codebook format) the dequantized
+// bf16 weight; none for NF4.
+size_t gemm_ws_bytes(const QWeight& w, int64_t, int, bool) {
+  return w.format == LQ_FMT_CODEBOOK ? align256((size_t)w.N * w.K * sizeof(uint16_t)) : 0;
 }
 
-static uint16_t* weight_ws(const QWeight& w, int64_t M, int r, bool fwd, uint16_t* ws) {
-  return ws + align256(lora_operands_ws_bytes(M, fwd ? w.N : w.K, r)) / sizeof(uint16_t);
-}
-
-// Writes the LoRA operands into ws (t2 first, then lb2) and fills p.
-static hipError_t prepare_lora(GemmParams& p, const float* L, const uint16_t* lb, int r, float s, bool fwd,
-                               uint16_t* ws, hipStream_t st) {
+// The LoRA segment's sources (read by the GEMM itself).
+static void set_lora(GemmParams& p, const float* L, const uint16_t* lb, int r, float s, bool fwd) {
+  p.L = L;
+  p.lb = lb;
+  p.r = r;
+  p.s = s;
+  p.fwd = fwd ? 1 : 0;
   p.R2 = lora_seg_cols(r);
-  uint16_t* t2 = ws;
-  uint16_t* lb2 = ws + p.M * p.R2;
-  p.t2 = t2;
-  p.lb2 = lb2;
-  const int64_t chunks = (p.M + p.Ncols) * (p.R2 / 8);
-  const unsigned blocks = (unsigned)std::min<int64_t>((chunks + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_lora_operands, dim3(blocks), dim3(256), 0, st, L, p.M, lb, p.Ncols, p.w.K, r, p.R2, s,
-                     fwd ? 1 : 0, t2, lb2);
-  return hipGetLastError();
 }
 
 static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, int64_t Ncols, int64_t Kc,
                               void* out) {
   GemmParams p;
   p.A = A; p.M = M; p.Ncols = Ncols; p.Kc = Kc; p.out = out;
-  p.t2 = nullptr; p.lb2 = nullptr; p.R2 = 0;
+  p.L = nullptr; p.lb = nullptr; p.r = 0; p.s = 0.0f; p.fwd = 1; p.R2 = 0;
   // 32 workgroups are resident per XCD: 2 A row-tiles x 16 weight tiles
   // minimise the bytes they pull into the XCD's L2.
   p.gm = (int)std::min<int64_t>(2, (M + BM - 1) / BM);
@@ -1027,8 +1078,8 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
                            const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,
                            hipStream_t st) {
   GemmParams p = make_params(w, X, M, w.N, w.K, H);
-  hipError_t e = prepare_lora(p, t, B, r, s, true, ws, st);
-  if (e != hipSuccess) return e;
+  set_lora(p, t, B, r, s, true);
+  hipError_t e = hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool dq = w.qc.absmax == nullptr;
@@ -1043,7 +1094,7 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   if (w.format == LQ_FMT_NF4) {
     LQ_LAUNCH_FWD(ProdFwdNF4);
   } else {
-    uint16_t* wbf = weight_ws(w, M, r, true, ws);
+    uint16_t* wbf = ws;
     e = launch_dequant(w, wbf, st);
     if (e != hipSuccess) return e;
     p.wbf = wbf;
@@ -1057,13 +1108,13 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
                            const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st) {
   GemmParams p = make_params(w, G, M, w.K, w.N, gX);
-  hipError_t e = prepare_lora(p, u, A, r, s, false, ws, st);
-  if (e != hipSuccess) return e;
+  set_lora(p, u, A, r, s, false);
+  hipError_t e = hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
   const dim3 grid((unsigned)tiles);
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
   if (w.format == LQ_FMT_CODEBOOK) {
-    uint16_t* wbf = weight_ws(w, M, r, false, ws);
+    uint16_t* wbf = ws;
     e = launch_dequant(w, wbf, st);
     if (e != hipSuccess) return e;
     p.wbf = wbf;

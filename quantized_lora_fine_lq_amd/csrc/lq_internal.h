@@ -105,27 +105,44 @@ hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t
                                     hipStream_t s);
 
 // Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R[j][c] with R
-// [r, C] row-major (C % 8 == 0).
-size_t row_skinny_ws_floats(int64_t M, int64_t C, int r);
+// [r, C] row-major (C % 8 == 0); one launch, no workspace. If pt2 is not
+// null the result is also written as the column form's P operand
+// ([2r][split_rows(M)] bf16: hi and lo halves, transposed, zero padded).
+int64_t split_rows(int64_t M);
 hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
-                             float* out, float* ws, hipStream_t s);
+                             float* out, uint16_t* pt2, hipStream_t s);
+// Backward set-up: Bt = B^T ([N, r] -> [r, N]) and pt2 = the column form's P
+// operand from t (as launch_row_skinny writes it).
+hipError_t launch_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* Bt, const float* t, int64_t M,
+                           uint16_t* pt2, hipStream_t s);
 hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* out, hipStream_t s);
-// Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c]; written as
+// Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c] with P given as
+// pt2 (see launch_row_skinny); written as
 // out[j*C + c] (out_transposed = false, [r, C]) or out[c*r + j] ([C, r]).
+// launch_col_skinny writes partial sums into ws (col_skinny_ws_floats) and
+// describes the reduction that finishes it in *job; launch_reduce_splits2
+// runs up to two such reductions in one launch (a job with out == nullptr is
+// skipped).
+struct SplitJobDesc {
+  const float* part = nullptr;
+  int splits = 0;
+  int64_t rows = 0, cols = 0, srows = 0, pair = 0;
+  float scale = 0.0f;
+  float* out = nullptr;
+  int transposed = 0;
+};
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r);
-hipError_t launch_col_skinny(const float* P, const uint16_t* Q, int64_t M, int64_t C, int r,
-                             float scale, float* out, bool out_transposed, float* ws,
-                             hipStream_t s);
+hipError_t launch_col_skinny(const uint16_t* pt2, const uint16_t* Q, int64_t M, int64_t C, int r, float scale,
+                             float* out, bool out_transposed, float* ws, SplitJobDesc* job, hipStream_t s);
+hipError_t launch_reduce_splits2(const SplitJobDesc& a, const SplitJobDesc& b, hipStream_t s);
 
-// Dequant-GEMM with the LoRA segment.
+// Dequant-GEMM with the LoRA segment (formed in the kernel from t or u and
+// B or A).
 //  forward : out[m][n] = sum_k X[m][k] W'[n][k] + s * sum_j t[m][j] B[n][j]
 //  backward: out[m][k] = sum_n G[m][n] W'[n][k] + s * sum_j u[m][j] A[j][k]
-// ws receives the bf16 LoRA segment operands: lora_operands_ws_bytes(M,
-// output columns, r) bytes (output columns = N forward, K backward).
 int lora_seg_cols(int r);
-size_t lora_operands_ws_bytes(int64_t M, int64_t Ncols, int r);
-// Workspace of launch_gemm_fwd (fwd) / launch_gemm_bwd: LoRA operands, plus
-// the dequantized bf16 weight for the codebook format.
+// Workspace of launch_gemm_fwd (fwd) / launch_gemm_bwd: the dequantized bf16
+// weight for the codebook format, none for NF4.
 size_t gemm_ws_bytes(const QWeight& w, int64_t M, int r, bool fwd);
 hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,

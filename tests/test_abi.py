@@ -145,26 +145,25 @@ def test_validation_errors_without_launch(lq):
     assert wsc == wsb + 128 * 256 * 2
     b4 = list(bargs); b4[0] = ctypes.byref(wc)
     assert L.lq_qlora_backward(*b4) == lq.LQ_ERR_WORKSPACE
-    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 300, 16) == (300 + 128) * 64 * 2 + 128 * 256 * 2
-    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 16, 16) == (16 + 128) * 64 * 2 + 128 * 256 * 2
-    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(wc), 300, 16) == (300 + 256) * 64 * 2 + 128 * 256 * 2
-
-    # split forward stages: the MFMA path (M > 16) needs the LoRA-operand workspace,
-    # (M + N) * 64 * ceil(2r / 64) * 2 bytes; the GEMV path (M <= 16, NF4) needs none
-    wg = L.lq_dequant_gemm_workspace(ctypes.byref(w), 300, 16)
-    assert wg == (300 + 128) * 64 * 2          # N = 128
-    assert L.lq_dequant_gemm_workspace(ctypes.byref(w), 300, 40) == (300 + 128) * 128 * 2
+    # split forward stages: NF4 needs no workspace (the GEMM forms its LoRA
+    # operands itself); a codebook weight is dequantized into N * K * 2 bytes
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 300, 16) == 128 * 256 * 2
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 16, 16) == 128 * 256 * 2
+    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(wc), 300, 16) == 128 * 256 * 2
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(w), 300, 16) == 0
     assert L.lq_dequant_gemm_workspace(ctypes.byref(w), 16, 16) == 0
-    gargs = [ctypes.byref(w), fake, 300, fake, fake, 16, 32.0, fake, 1, fake, wg, null]
+    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(w), 300, 16) == 0
+    assert L.lq_lora_down_workspace(300, 256, 16) == 0
+    wg = L.lq_dequant_gemm_workspace(ctypes.byref(wc), 300, 16)
+    gargs = [ctypes.byref(wc), fake, 300, fake, fake, 16, 32.0, fake, 1, fake, wg, null]
     g1 = list(gargs); g1[10] = wg - 1
     assert L.lq_dequant_gemm(*g1) == lq.LQ_ERR_WORKSPACE
     g2 = list(gargs); g2[9] = null
     assert L.lq_dequant_gemm(*g2) == lq.LQ_ERR_WORKSPACE
     g3 = list(gargs); g3[5] = 129
     assert L.lq_dequant_gemm(*g3) == lq.LQ_ERR_SHAPE
-    wt = L.lq_dequant_gemm_t_workspace(ctypes.byref(w), 300, 16)
-    assert wt == (300 + 256) * 64 * 2          # K = 256
-    targs = [ctypes.byref(w), fake, 300, fake, fake, 16, 32.0, fake, fake, wt, null]
+    wt = L.lq_dequant_gemm_t_workspace(ctypes.byref(wc), 300, 16)
+    targs = [ctypes.byref(wc), fake, 300, fake, fake, 16, 32.0, fake, fake, wt, null]
     t1 = list(targs); t1[9] = wt - 1
     assert L.lq_dequant_gemm_t(*t1) == lq.LQ_ERR_WORKSPACE
     t2 = list(targs); t2[0] = ctypes.byref(w_odd)
