@@ -672,94 +672,84 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
 // Skinny products (HBM-bound: they stream X or G once).
 // ===========================================================================
 // Row form: out[m][j] = sum_c Q[m][c] R[j][c] with R [r, C] row-major (C a
-// multiple of 8). One workgroup per 16 G rows of Q (G row groups, more for
-// larger r so that the R fragments, re-read by every workgroup, are shared
-// by more rows); its 8 waves take contiguous runs of 32-column steps. MFMA
-// 16x16x32: lane (li, lg) reads 8 consecutive columns of Q row 16g + li and
-// of R row 16jt + li straight into MFMA registers (R is small and stays in
-// cache). The 8 partial sums meet in LDS, one row group at a time, and are
-// added in wave order, so no second pass is needed. When pt2 is given, the
-// result is also written split and transposed for the column form: pt2
-// [2r][Mp] bf16 = [hi(out)^T ; lo(out)^T], zero for rows M..Mp-1 (the grid
-// then covers Mp rows).
-constexpr int RW_WAVES = 8;
-template <int JT, int G>
-__global__ __launch_bounds__(64 * RW_WAVES) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M,
-                                                              int64_t C, const uint16_t* __restrict__ R, int r,
-                                                              float* __restrict__ out, uint16_t* __restrict__ pt2,
-                                                              int64_t Mp) {
-  __shared__ f32x4_t sPart[RW_WAVES][JT][64];
+// multiple of 8). One workgroup per 16 rows of Q; its W waves (16 for r <= 64,
+// else 8) take contiguous runs of 64-column blocks. MFMA 16x16x32 with the
+// contraction order permuted inside each 64-column block: in its two steps
+// lane (li, lg) takes columns 16 lg + [0, 8) and 16 lg + [8, 16) of Q row li
+// and of R row 16jt + li, straight into MFMA registers, so the four lanes of
+// a row read whole 128-byte lines (R is small and stays in cache). The W
+// partial sums meet in LDS and are added in wave order, so no second pass is
+// needed. When pt2 is given, the result is also written split and
+// transposed for the column form: pt2 [2r][Mp] bf16 = [hi(out)^T ;
+// lo(out)^T], zero for rows M..Mp-1 (the grid then covers Mp rows).
+template <int JT, int W>
+__global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M, int64_t C,
+                                                       const uint16_t* __restrict__ R, int r,
+                                                       float* __restrict__ out, uint16_t* __restrict__ pt2,
+                                                       int64_t Mp) {
+  __shared__ f32x4_t sPart[W][JT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 16 * G;
-  const uint16_t* qrow[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qrow[g] = Q + min(row0 + 16 * g + li, M - 1) * C;   // rows past M: not stored
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const uint16_t* qrow = Q + min(row0 + li, M - 1) * C + 16 * lg;   // rows past M: not stored
   const uint16_t* rrow[JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C;
-  const int64_t steps = (C + 31) / 32;
-  const int64_t per = (steps + RW_WAVES - 1) / RW_WAVES;
-  const int64_t s_begin = min(steps, wave * per), s_end = min(steps, s_begin + per);
-  f32x4_t acc[G][JT];
+  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C + 16 * lg;
+  const int64_t blocks = (C + 63) / 64;
+  const int64_t per = (blocks + W - 1) / W;
+  const int64_t b_begin = min(blocks, wave * per), b_end = min(blocks, b_begin + per);
+  f32x4_t acc[JT];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) acc[g][jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = (G + JT) <= 2 ? 8 : ((G + JT) <= 4 ? 4 : 2);   // steps with loads in flight together
-  for (int64_t st = s_begin; st < s_end; st += U) {
-    u32x4_t a[U][G], b[U][JT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t cc = 32 * (st + u) + 8 * lg;
-      const bool ok = st + u < s_end && cc + 8 <= C;
-      const int64_t off = ok ? cc : 0;   // a lane past the end reads columns 0..7 and adds 0
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        a[u][g] = ld16(qrow[g] + off);
-        if (!ok) zero(a[u][g]);
-      }
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) b[u][jt] = ld16(rrow[jt] + off);
-    }
+  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = JT <= 2 ? 4 : (JT <= 4 ? 2 : 1);   // 64-column blocks with loads in flight together
+  for (int64_t bk = b_begin; bk < b_end; bk += U) {
+    u32x4_t a[U][2], b[U][2][JT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int h = 0; h < 2; ++h) {
+        const int64_t cc = 64 * (bk + u) + 8 * h;   // + 16 lg in the row pointers
+        const bool ok = bk + u < b_end && cc + 16 * lg + 8 <= C;
+        const int64_t off = ok ? cc : -16 * lg;     // a lane past the end reads columns 0..7 and adds 0
+        a[u][h] = ld16(qrow + off);
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt)
-          acc[g][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][g]), as_bf16x8(b[u][jt]), acc[g][jt],
-                                                               0, 0, 0);
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (g > 0) __syncthreads();   // the previous group's sums have been read
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) sPart[wave][jt][lane] = acc[g][jt];
-    __syncthreads();
-    // thread -> (jt, lane) of the 16 x 16JT output: column j = 16jt + li,
-    // rows 4lg + v of row group g
-    for (int idx = threadIdx.x; idx < JT * 64; idx += 64 * RW_WAVES) {
-      const int jt = idx >> 6, ln = idx & 63;
-      const int j = 16 * jt + (ln & 15);
-      if (j >= r) continue;
-      f32x4_t sum = sPart[0][jt][ln];
-#pragma unroll
-      for (int w = 1; w < RW_WAVES; ++w) {
-        const f32x4_t o = sPart[w][jt][ln];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) sum[v] += o[v];
+        for (int jt = 0; jt < JT; ++jt) b[u][h][jt] = ld16(rrow[jt] + off);
+        if (!ok) zero(a[u][h]);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = row0 + 16 * g + 4 * (ln >> 4) + v;
-        if (row < M) out[row * r + j] = sum[v];
-        if (pt2 && row < Mp) {
-          float hi = 0.0f, lo = 0.0f;
-          if (row < M) split_bf16(sum[v], hi, lo);
-          pt2[(int64_t)j * Mp + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
-          pt2[(int64_t)(j + r) * Mp + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
-        }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][h]), as_bf16x8(b[u][h][jt]), acc[jt], 0,
+                                                            0, 0);
+  }
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) sPart[wave][jt][lane] = acc[jt];
+  __syncthreads();
+  // thread -> (jt, lane) of the 16 x 16JT output: column j = 16jt + li,
+  // rows 4lg + v
+  for (int idx = threadIdx.x; idx < JT * 64; idx += 64 * W) {
+    const int jt = idx >> 6, ln = idx & 63;
+    const int j = 16 * jt + (ln & 15);
+    if (j >= r) continue;
+    f32x4_t sum = sPart[0][jt][ln];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+      const f32x4_t o = sPart[w][jt][ln];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sum[v] += o[v];
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t row = row0 + 4 * (ln >> 4) + v;
+      if (row < M) out[row * r + j] = sum[v];
+      if (pt2 && row < Mp) {
+        float hi = 0.0f, lo = 0.0f;
+        if (row < M) split_bf16(sum[v], hi, lo);
+        pt2[(int64_t)j * Mp + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+        pt2[(int64_t)(j + r) * Mp + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
       }
     }
   }
@@ -965,13 +955,10 @@ hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint
                              float* out, uint16_t* pt2, hipStream_t s) {
   const int64_t Mp = split_rows(M);
   const int64_t rows = pt2 ? Mp : M;
-  // row groups per workgroup: 1 for r <= 16, 2 for r <= 32, else 4
-  const int jt = (r + 15) / 16;
-  const int g = jt <= 1 ? 1 : (jt <= 2 ? 2 : 4);
-  const dim3 grid((unsigned)((rows + 16 * g - 1) / (16 * g)));
-  switch (jt) {
-#define LQ_RS(JT, G) case JT: hipLaunchKernelGGL((k_row_skinny<JT, G>), grid, dim3(64 * RW_WAVES), 0, s, Q, M, C, R, r, out, pt2, Mp); break;
-    LQ_RS(1, 1) LQ_RS(2, 2) LQ_RS(3, 4) LQ_RS(4, 4) LQ_RS(5, 4) LQ_RS(6, 4) LQ_RS(7, 4) LQ_RS(8, 4)
+  const dim3 grid((unsigned)((rows + 15) / 16));
+  switch ((r + 15) / 16) {
+#define LQ_RS(JT, W) case JT: hipLaunchKernelGGL((k_row_skinny<JT, W>), grid, dim3(64 * W), 0, s, Q, M, C, R, r, out, pt2, Mp); break;
+    LQ_RS(1, 16) LQ_RS(2, 16) LQ_RS(3, 16) LQ_RS(4, 16) LQ_RS(5, 8) LQ_RS(6, 8) LQ_RS(7, 8) LQ_RS(8, 8)
 #undef LQ_RS
     default: return hipErrorInvalidValue;
   }
