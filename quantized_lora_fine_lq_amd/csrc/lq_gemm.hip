@@ -338,9 +338,17 @@ struct ProdBwdBF16 {
 
 template <class Prod, bool OUT_F32, bool TAIL>
 __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * PITCH];
-  __shared__ f32x2_t sPair[256];
+  // one LDS object with the pair table first: at LDS address 0 a lookup
+  // address is one shift of the code byte
+  struct __attribute__((aligned(16))) Lds {
+    f32x2_t pair[256];
+    uint16_t a[2][BM * PITCH];
+    uint16_t b[2][BN * PITCH];
+  };
+  __shared__ Lds lds;
+  f32x2_t* sPair = lds.pair;
+  uint16_t (*sA)[BM * PITCH] = lds.a;
+  uint16_t (*sB)[BN * PITCH] = lds.b;
   if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
 
   // XCD-aware tile order: the 8 XCDs take workgroups round robin, so each
@@ -590,8 +598,15 @@ __device__ __forceinline__ void gv_compute(const GvStage<RG>& st, const f32x2_t*
 
 template <int RG, bool DQ, bool OUT_F32>
 __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
-  __shared__ __attribute__((aligned(16))) float sC[GV_CTAB];   // constants [16 RG rows][nb + 1]; then partial sums
-  __shared__ f32x2_t sPair[256];
+  // one LDS object with the pair table first: at LDS address 0 a lookup
+  // address is one shift of the code byte
+  struct __attribute__((aligned(16))) Lds {
+    f32x2_t pair[256];
+    float c[GV_CTAB];   // constants [16 RG rows][nb + 1]; then partial sums
+  };
+  __shared__ Lds lds;
+  f32x2_t* sPair = lds.pair;
+  float* sC = lds.c;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int64_t N = p.w.N, K = p.w.K;
@@ -612,14 +627,42 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
 
   if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
   const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
-  const int ncon = 16 * RG * nb;
+  if (DQ && nb % 16 == 0) {
+    // 16 constants per thread and chunk: one 16-byte load of E4M3 codes and
+    // one second-level scale (16 aligned blocks never straddle a 256-block),
+    // all chunks of a thread in flight together
+    const int cpr = nb / 16, nchunks = 16 * RG * cpr;
+    constexpr int CH = (16 * RG * (GV_CTAB / (16 * RG) / 16) + 64 * GV_WAVES - 1) / (64 * GV_WAVES);
+    u32x4_t q8[CH];
+    float s2[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = min((int)threadIdx.x + u * 64 * GV_WAVES, nchunks - 1);
+      const int rr = i / cpr, cb = i - rr * cpr;
+      const int64_t blk = min(n0 + rr, N - 1) * nb + 16 * cb;
+      q8[u] = ld16(p.w.qc.absmax_q + blk);
+      s2[u] = p.w.qc.dq_scale[blk >> 8];
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int i = (int)threadIdx.x + u * 64 * GV_WAVES;
+      if (i >= nchunks) continue;
+      const int rr = i / cpr, cb = i - rr * cpr;
+      float* dst = sC + rr * pitch + 16 * cb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        dst[e] = __builtin_fmaf(e4m3_decode((q8[u][e >> 2] >> (8 * (e & 3))) & 0xFFu), s2[u], mean);
+    }
+  } else {
+    const int ncon = 16 * RG * nb;
 #pragma unroll 4
-  for (int i = threadIdx.x; i < ncon; i += 64 * GV_WAVES) {
-    const int rr = i / nb, bl = i - rr * nb;
-    const int64_t blk = min(n0 + rr, N - 1) * nb + bl;
-    const float c = DQ ? __builtin_fmaf(e4m3_decode(p.w.qc.absmax_q[blk]), p.w.qc.dq_scale[blk >> 8], mean)
-                       : p.w.qc.absmax[blk];
-    sC[rr * pitch + bl] = c;
+    for (int i = threadIdx.x; i < ncon; i += 64 * GV_WAVES) {
+      const int rr = i / nb, bl = i - rr * nb;
+      const int64_t blk = min(n0 + rr, N - 1) * nb + bl;
+      const float c = DQ ? __builtin_fmaf(e4m3_decode(p.w.qc.absmax_q[blk]), p.w.qc.dq_scale[blk >> 8], mean)
+                         : p.w.qc.absmax[blk];
+      sC[rr * pitch + bl] = c;
+    }
   }
   __syncthreads();
 
