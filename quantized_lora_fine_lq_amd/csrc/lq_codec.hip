@@ -206,13 +206,12 @@ __global__ __launch_bounds__(1024) void k_profile_finish(const double* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Double quantization, two launches. (1) per 256-constant block: float64
-// pairwise tree sum (4 leaves per lane, then a butterfly over the 64 lanes,
-// which pairs neighbouring subtrees level by level). (2) every workgroup of
-// the encoder first forms the mean itself from the block sums by the same
-// pairwise tree (zero padding to a power of two does not change the sum, so
-// all workgroups get the bit-identical mean), then encodes its blocks: d = c -
-// mean, scale = max|d| / 448, code = E4M3(clamp(d / scale)).
+// Double quantization. (1) per 256-constant block: float64 pairwise tree sum
+// (4 leaves per lane, then a butterfly over the 64 lanes, which pairs
+// neighbouring subtrees level by level). (2) pairwise tree over the block
+// sums, 1024 leaves per workgroup, repeated until one value is left; zero
+// padding to a power of two does not change the sum. (3) per block:
+// d = c - mean, scale = max|d| / 448, code = E4M3(clamp(d / scale)).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_dq_block_sums(const float* __restrict__ c, int64_t n_b,
                                                       double* __restrict__ sums) {
@@ -227,58 +226,50 @@ __global__ __launch_bounds__(64) void k_dq_block_sums(const float* __restrict__ 
   if (l == 0) sums[blockIdx.x] = s;
 }
 
-// Pairwise float64 sum of sums[0 .. n) padded with zeros to P = 256 L leaves
-// (L a power of two): thread t sums leaves [tL, tL + L) pairwise (a binary
-// counter of partial subtrees), then the 256 thread sums are paired by a
-// butterfly inside each wave and the 4 wave sums as (w0 + w1) + (w2 + w3).
-__device__ double dq_tree_mean_sum(const double* __restrict__ sums, int64_t n, int64_t L, double* sW) {
+__global__ __launch_bounds__(1024) void k_tree_reduce(const double* __restrict__ in, int64_t n_in,
+                                                      double* __restrict__ out, int64_t n_b,
+                                                      float* __restrict__ mean_out) {
+  __shared__ double wsum[16];
   const int t = threadIdx.x;
-  double stack[24];
-  int depth = 0;
-  for (int64_t i = 0; i < L; ++i) {
-    const int64_t k = (int64_t)t * L + i;
-    double v = k < n ? sums[k] : 0.0;
-    // merge while the count of leaves taken so far has trailing ones
-    for (int64_t c = i + 1; (c & 1) == 0; c >>= 1) v = stack[--depth] + v;
-    stack[depth++] = v;
-  }
-  double s = stack[0];   // L is a power of two: one subtree left
+  const int64_t i = (int64_t)blockIdx.x * 1024 + t;
+  double s = (i < n_in) ? in[i] : 0.0;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) s = s + __shfl_xor(s, m);
-  if ((t & 63) == 0) sW[t >> 6] = s;
+  if ((t & 63) == 0) wsum[t >> 6] = s;
   __syncthreads();
-  return (sW[0] + sW[1]) + (sW[2] + sW[3]);
+  if (t < 64) {
+    double w = (t < 16) ? wsum[t] : 0.0;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) w = w + __shfl_xor(w, m);
+    if (t == 0) {
+      if (mean_out) *mean_out = (float)(w / (double)n_b);
+      else out[blockIdx.x] = w;
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void k_dq_encode_mean(const float* __restrict__ c, int64_t n_b,
-                                                        const double* __restrict__ sums, int64_t L,
-                                                        float* __restrict__ mean_out,
-                                                        uint8_t* __restrict__ absmax_q,
-                                                        float* __restrict__ dq_scale) {
-  __shared__ double sW[4];
-  __shared__ float wmax[2][4];
+__global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, int64_t n_b,
+                                                   const float* __restrict__ mean,
+                                                   uint8_t* __restrict__ absmax_q,
+                                                   float* __restrict__ dq_scale) {
+  __shared__ float wmax[4];
   const int t = threadIdx.x;
-  const int64_t n_d = (n_b + 255) / 256;
-  const float mu = (float)(dq_tree_mean_sum(sums, n_d, L, sW) / (double)n_b);
-  if (blockIdx.x == 0 && t == 0) *mean_out = mu;
-  int buf = 0;
-  for (int64_t blk = blockIdx.x; blk < n_d; blk += gridDim.x, buf ^= 1) {
-    const int64_t j = blk * 256 + t;
-    const float d = (j < n_b) ? c[j] - mu : 0.0f;
-    float a = wave_max(fabsf(d));
-    if ((t & 63) == 0) wmax[buf][t >> 6] = a;
-    __syncthreads();   // (alternating buffers: the next block's writes cannot overtake these reads)
-    a = fmaxf(fmaxf(wmax[buf][0], wmax[buf][1]), fmaxf(wmax[buf][2], wmax[buf][3]));
-    const float s2 = a / 448.0f;
-    if (t == 0) dq_scale[blk] = s2;
-    uint32_t code = 0;
-    if (s2 > 0.0f) {
-      float v = d / s2;
-      v = fminf(fmaxf(v, -448.0f), 448.0f);
-      code = e4m3_encode(v);
-    }
-    if (j < n_b) absmax_q[j] = (uint8_t)code;
+  const int64_t j = (int64_t)blockIdx.x * 256 + t;
+  const float mu = *mean;
+  const float d = (j < n_b) ? c[j] - mu : 0.0f;
+  float a = wave_max(fabsf(d));
+  if ((t & 63) == 0) wmax[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s2 = a / 448.0f;
+  if (t == 0) dq_scale[blockIdx.x] = s2;
+  uint32_t code = 0;
+  if (s2 > 0.0f) {
+    float v = d / s2;
+    v = fminf(fmaxf(v, -448.0f), 448.0f);
+    code = e4m3_encode(v);
   }
+  if (j < n_b) absmax_q[j] = (uint8_t)code;
 }
 
 // ---------------------------------------------------------------------------
@@ -518,7 +509,15 @@ hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double
   return hipGetLastError();
 }
 
-size_t double_quant_ws_doubles(int64_t n_blocks) { return (size_t)((n_blocks + 255) / 256); }
+size_t double_quant_ws_doubles(int64_t n_blocks) {
+  const int64_t n_d = (n_blocks + 255) / 256;
+  int64_t total = n_d, level = n_d;
+  while (level > 1024) {
+    level = (level + 1023) / 1024;
+    total += level;
+  }
+  return (size_t)total + 16;
+}
 
 hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax_q,
                                float* dq_scale, float* dq_mean, double* ws, hipStream_t s) {
@@ -526,11 +525,21 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
   hipLaunchKernelGGL(k_dq_block_sums, dim3((unsigned)n_d), dim3(64), 0, s, absmax, n_b, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t L = 1;   // leaves per thread: 256 L >= n_d
-  while (256 * L < n_d) L <<= 1;
-  const unsigned grid = (unsigned)std::min<int64_t>(n_d, 256);
-  hipLaunchKernelGGL(k_dq_encode_mean, dim3(grid), dim3(256), 0, s, absmax, n_b, ws, L, dq_mean, absmax_q,
-                     dq_scale);
+  double* cur = ws;
+  int64_t n = n_d;
+  while (n > 1024) {
+    const int64_t groups = (n + 1023) / 1024;
+    double* nxt = cur + n;
+    hipLaunchKernelGGL(k_tree_reduce, dim3((unsigned)groups), dim3(1024), 0, s, cur, n, nxt, n_b,
+                       (float*)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    cur = nxt;
+    n = groups;
+  }
+  hipLaunchKernelGGL(k_tree_reduce, dim3(1), dim3(1024), 0, s, cur, n, (double*)nullptr, n_b, dq_mean);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dq_encode, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b, dq_mean,
+                     absmax_q, dq_scale);
   return hipGetLastError();
 }
 
