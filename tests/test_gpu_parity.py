@@ -208,6 +208,21 @@ def test_forward(lq, torch, N, K, M, r, alpha):
     assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
 
 
+@pytest.mark.parametrize("M,K,r", [(1, 8, 16), (17, 24, 5), (33, 40, 128), (300, 72, 64), (64, 4096, 16),
+                                   (16, 8256, 32)])
+def test_lora_down_shapes(lq, torch, M, K, r):
+    """t = X A^T for short and ragged contractions (K a multiple of 8 only,
+    fewer columns than one 64-column block, K past a whole number of blocks)."""
+    rng = np.random.default_rng(M * 7 + K + r)
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    A = syn.to_bf16_bits((rng.standard_normal((r, K)) * 0.02).astype(np.float32))
+    t = lq.lora_down(bf16_dev(torch, X), bf16_dev(torch, A))
+    B = np.zeros((8, r), np.float32)
+    _, tref = layer.forward(np.zeros((8, K), np.float32), syn.bf16_bits_to_f32(X), syn.bf16_bits_to_f32(A), B,
+                            float(r))
+    assert layer.rel_frobenius(host(t), tref) <= 1e-5
+
+
 def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
     L, W, X, A, B = make_layer(7, 512, 1024, 16, 16, 32.0)
     qw = lq.QWeight.from_weight(dev(torch, W))
@@ -241,7 +256,9 @@ def test_unit_vector_probe_bit_exact(lq, torch, M):
 @pytest.mark.parametrize("N,K,M,r,alpha", [
     (384, 640, 300, 16, 32.0),
     (512, 256, 96, 64, 16.0),
-    (264, 320, 33, 24, 8.0),
+    (264, 320, 33, 24, 8.0),       # N % 64 != 0, M % 32 != 0, hi/lo rows kept apart
+    (192, 256, 50, 128, 16.0),     # largest rank: eight 16-wide tiles of t and u
+    (136, 192, 77, 40, 16.0),      # 2r = 80: three 32-row product tiles
 ])
 @pytest.mark.parametrize("recompute_t", [False, True])
 def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
