@@ -325,25 +325,39 @@ __device__ void lds_jacobi(double (*sG)[D + 1], double (*sV)[D + 1], int n) {
         sP[pi] = p; sQ[pi] = q; sC[pi] = c; sS[pi] = sn;
       }
       __syncthreads();
-      for (int pi = ty; pi < np; pi += 16) {   // columns: G <- G J, V <- V J
+      // (loops over compile-time bounds with guards, so the LDS reads of a
+      // thread are issued together)
+#pragma unroll
+      for (int k = 0; k < (D / 2 + 15) / 16; ++k) {   // columns: G <- G J, V <- V J
+        const int pi = ty + 16 * k;
+        if (pi >= np) break;
         const int p = sP[pi], q = sQ[pi];
         if (q < 0) continue;
         const double c = sC[pi], sn = sS[pi];
-        for (int i = tx; i < n; i += 16) {
+#pragma unroll
+        for (int m = 0; m < (D + 15) / 16; ++m) {
+          const int i = tx + 16 * m;
+          if (i >= n) break;
           const double gp = sG[i][p], gq = sG[i][q];
+          const double vp = sV[i][p], vq = sV[i][q];
           sG[i][p] = c * gp - sn * gq;
           sG[i][q] = sn * gp + c * gq;
-          const double vp = sV[i][p], vq = sV[i][q];
           sV[i][p] = c * vp - sn * vq;
           sV[i][q] = sn * vp + c * vq;
         }
       }
       __syncthreads();
-      for (int pi = ty; pi < np; pi += 16) {   // rows: G <- J^T G
+#pragma unroll
+      for (int k = 0; k < (D / 2 + 15) / 16; ++k) {   // rows: G <- J^T G
+        const int pi = ty + 16 * k;
+        if (pi >= np) break;
         const int p = sP[pi], q = sQ[pi];
         if (q < 0) continue;
         const double c = sC[pi], sn = sS[pi];
-        for (int j = tx; j < n; j += 16) {
+#pragma unroll
+        for (int m = 0; m < (D + 15) / 16; ++m) {
+          const int j = tx + 16 * m;
+          if (j >= n) break;
           const double gp = sG[p][j], gq = sG[q][j];
           sG[p][j] = c * gp - sn * gq;
           sG[q][j] = sn * gp + c * gq;
