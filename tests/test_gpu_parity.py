@@ -139,6 +139,32 @@ def test_quantize_threshold_windows(lq, torch):
     assert np.array_equal(host(codes), packed)
 
 
+@pytest.mark.parametrize("scaled", [False, True])
+def test_quantize_strided_sweep(lq, torch, scaled):
+    """Every 61st float32 bit pattern of [-1, 1] (about 35 M values: every
+    exponent, mantissas at a prime stride), 63 per block with the block's
+    absmax in the last slot. Unscaled: absmax 1, so x = w exactly. Scaled:
+    each block multiplied by its own constant in [0.01, 0.05] (rounded to
+    float32), so the kernel's reciprocal shortcut and its exact-quotient
+    fallback both decide codes; the oracle divides."""
+    one = np.float32(1.0).view(np.int32)
+    pos = np.arange(0, one + 1, 61, dtype=np.int32).view(np.float32)
+    x = np.concatenate([pos, -pos[1:]])
+    n63 = (x.size + 62) // 63
+    flat = np.zeros(n63 * 63, dtype=np.float32)
+    flat[:x.size] = x
+    W = np.empty((n63, 64), dtype=np.float32)
+    W[:, :63] = flat.reshape(n63, 63)
+    W[:, 63] = 1.0
+    if scaled:
+        c = np.random.default_rng(11).uniform(0.01, 0.05, n63).astype(np.float32)
+        W = (W.astype(np.float64) * c[:, None]).astype(np.float32)
+    codes, absmax = lq.quantize_nf4(dev(torch, W))
+    packed, cref = nf4.quantize(W)
+    assert np.array_equal(host(absmax), cref)
+    assert np.array_equal(host(codes), packed)
+
+
 # ---------------------------------------------------------------------------
 # double quantization
 # ---------------------------------------------------------------------------
