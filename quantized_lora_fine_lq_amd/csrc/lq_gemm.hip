@@ -540,7 +540,8 @@ struct GemvParams {
 };
 
 constexpr int GV_WAVES = 8;        // K splits per workgroup
-constexpr int GV_CTAB = 24576;     // floats of LDS for the constant table (96 KB)
+constexpr int GV_CTAB = 8448;      // floats of LDS for the constant table (33 KB: two workgroups per CU)
+static_assert(GV_WAVES * 4 * 4 * 64 <= GV_CTAB, "the epilogue's partial sums of 4 row groups reuse the table");
 
 // One pipeline stage: two 64-blocks (128 k) of RG row groups.
 template <int RG>
@@ -597,7 +598,7 @@ __device__ __forceinline__ void gv_compute(const GvStage<RG>& st, const f32x2_t*
 }
 
 template <int RG, bool DQ, bool OUT_F32>
-__global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_nf4(GemvParams p) {
+__global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
   // one LDS object with the pair table first: at LDS address 0 a lookup
   // address is one shift of the code byte
   struct __attribute__((aligned(16))) Lds {
@@ -1160,18 +1161,24 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   return hipGetLastError();
 }
 
-// 4 or 7 row groups per workgroup, whichever fills the last round of 256
-// CUs better (7 gives exactly 256 workgroups for 28672 rows).
-static int gemv_rg(int64_t N) {
-  auto fill = [&](int rg) {
-    const int64_t wgs = (N + 16 * rg - 1) / (16 * rg);
-    return (double)wgs / (double)(((wgs + 255) / 256) * 256);
-  };
-  return fill(7) > fill(4) + 0.01 ? 7 : 4;
+// Row groups per workgroup: 4, 2 or 1, the largest whose constant table
+// (16 RG rows of K/64 + 1 floats) fits in LDS and that still gives at least
+// 1.5 workgroups per CU for M <= 4 (few loads per workgroup: latency wants
+// more of them) or 1 per CU for larger M (more row groups per X fragment);
+// 0 when not even one row group fits.
+static int gemv_rg(int64_t N, int64_t K, int64_t M) {
+  auto fits = [&](int rg) { return (int64_t)16 * rg * (K / 64 + 1) <= GV_CTAB; };
+  const int64_t min_wgs = M <= 4 ? 384 : 256;
+  int best = 0;
+  for (int rg = 1; rg <= 4; rg *= 2) {
+    if (!fits(rg)) break;
+    if (best == 0 || (N + 16 * rg - 1) / (16 * rg) >= min_wgs) best = rg;
+  }
+  return best;
 }
 
 bool gemv_supported(const QWeight& w) {
-  return w.format == LQ_FMT_NF4 && (int64_t)16 * gemv_rg(w.N) * (w.K / 64 + 1) <= GV_CTAB;
+  return w.format == LQ_FMT_NF4 && gemv_rg(w.N, w.K, 1) > 0;
 }
 
 template <int RG>
@@ -1190,8 +1197,10 @@ hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
-  if (gemv_rg(w.N) == 7) launch_gemv_rg<7>(p, dq, f32, st);
-  else launch_gemv_rg<4>(p, dq, f32, st);
+  const int rg = gemv_rg(w.N, w.K, M);
+  if (rg == 4) launch_gemv_rg<4>(p, dq, f32, st);
+  else if (rg == 2) launch_gemv_rg<2>(p, dq, f32, st);
+  else launch_gemv_rg<1>(p, dq, f32, st);
   return hipGetLastError();
 }
 

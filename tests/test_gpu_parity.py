@@ -261,6 +261,36 @@ def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
     assert layer.rel_frobenius(host(H2), Href) <= F32_TOL
 
 
+@pytest.mark.parametrize("N,K,M,r,double", [
+    (16384, 256, 16, 16, True),    # 4 row groups per workgroup, K/64 not a multiple of 16
+    (24576, 1024, 2, 16, True),    # 4 row groups at M <= 4
+    (8200, 2048, 16, 24, True),    # 2 row groups, the last workgroup half past N
+    (12288, 640, 1, 16, False),    # 2 row groups, float32 constants, odd K/64
+    (4100, 8192, 16, 64, True),    # 1 row group, 16 + 4 rows past a whole workgroup
+    (64, 20480, 3, 16, True),      # K past two row groups' constant table
+    (40, 17024, 5, 8, False),      # same, K/64 not a multiple of 16, ragged N
+])
+def test_decode_gemv_row_groups(lq, torch, monkeypatch, N, K, M, r, double):
+    """The decode kernel at every row-group count it launches with, against
+    the oracle and against the GEMM path on the same inputs."""
+    rng = np.random.default_rng(N + K + M)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    A = syn.to_bf16_bits((rng.standard_normal((r, K)) * 0.02).astype(np.float32))
+    B = syn.to_bf16_bits((rng.standard_normal((N, r)) * 0.02).astype(np.float32))
+    qw = lq.QWeight.from_weight(dev(torch, W), double_quantize=double)
+    args = (qw, bf16_dev(torch, X), bf16_dev(torch, A), bf16_dev(torch, B), 32.0)
+    H, _ = lq.qlora_forward(*args)
+    H32, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    Href, _ = layer.forward(oracle_wd(W, double), syn.bf16_bits_to_f32(X), syn.bf16_bits_to_f32(A),
+                            syn.bf16_bits_to_f32(B), 32.0)
+    assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
+    assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
+    monkeypatch.setenv("LQ_FORCE_PATH", "gemm")
+    Hg, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    assert layer.rel_frobenius(host(Hg), Href) <= F32_TOL
+
+
 @pytest.mark.parametrize("M", [5, 300])
 def test_unit_vector_probe_bit_exact(lq, torch, M):
     """X rows = e_k, B = 0: H[m, :] = W'[:, k_m] exactly (float32 output)."""
