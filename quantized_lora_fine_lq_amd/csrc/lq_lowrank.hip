@@ -383,12 +383,19 @@ __device__ void lds_eig_order(const double (*sG)[D + 1], int n, int* sOrder) {
   __syncthreads();
 }
 
-// ---- Cholesky G = L L^T and T = L^{-T} (one workgroup) -----------------------
-// Q = Y T then has orthonormal columns (up to rounding); a dependent column
-// (pivot at or below 1e-28 of the largest diagonal) gets a zero column of Q.
-__global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__ G, int l, double* __restrict__ T) {
+// ---- T = L^{-T} for G = L L^T (one workgroup) -------------------------------
+// Gaussian elimination without pivoting on [G | I] (G is symmetric positive
+// semi-definite): after step j every row i > j has had f = G[i][j] / G[j][j]
+// times row j subtracted, so E G = U with E = L1^{-1} for G = L1 D L1^T
+// (L1 unit lower triangular). The Cholesky factor is L = L1 D^{1/2}, hence
+// L^{-1} = D^{-1/2} E and T[k][j] = E[j][k] / sqrt(D[j]) for k <= j. A
+// dependent column (pivot at or below 1e-28 of the largest diagonal entry)
+// eliminates nothing and gets a zero column of T, so Q = Y T has a zero
+// column there. One barrier per pivot.
+__global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, int l, double* __restrict__ T) {
   __shared__ double sA[LR_MAXL][LR_MAXL + 1];
-  __shared__ double sL[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sE[LR_MAXL][LR_MAXL + 1];
+  __shared__ double sR[LR_MAXL];   // D[j]^{-1/2}, 0 for a dependent column
   __shared__ double sRed[4];
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
   double m = 0.0;
@@ -396,16 +403,27 @@ __global__ __launch_bounds__(256) void k_cholesky_inv(const double* __restrict__
     for (int k = tx; k < l; k += 16) {
       const double v = G[i * l + k];
       sA[i][k] = v;
+      sE[i][k] = (i == k) ? 1.0 : 0.0;
       if (i == k) m = fmax(m, v);
     }
   for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
   if ((t & 63) == 0) sRed[t >> 6] = m;
   __syncthreads();
   const double tol = 1e-28 * fmax(fmax(sRed[0], sRed[1]), fmax(sRed[2], sRed[3]));
-  lds_cholesky<LR_MAXL>(sA, sL, l, tol);
-  lds_tri_inverse<LR_MAXL>(sL, sA, l);   // sA now holds L^{-1}
+  for (int j = 0; j < l; ++j) {
+    const double d = sA[j][j];
+    const bool ok = d > tol && d > 0.0;
+    const double inv = ok ? 1.0 / d : 0.0;
+    for (int i = j + 1 + ty; i < l; i += 16) {
+      const double f = sA[i][j] * inv;
+      for (int k = j + 1 + tx; k < l; k += 16) sA[i][k] -= f * sA[j][k];
+      for (int k = tx; k <= j; k += 16) sE[i][k] -= f * sE[j][k];
+    }
+    if (t == 0) sR[j] = ok ? 1.0 / sqrt(d) : 0.0;
+    __syncthreads();
+  }
   for (int k = ty; k < l; k += 16)
-    for (int j = tx; j < l; j += 16) T[k * l + j] = (k <= j) ? sA[j][k] : 0.0;   // T = L^{-T}
+    for (int j = tx; j < l; j += 16) T[k * l + j] = (k <= j) ? sE[j][k] * sR[j] : 0.0;
 }
 
 // ---- eigen-decomposition of the Rayleigh-Ritz Gram (one workgroup) ----------
@@ -567,7 +585,7 @@ hipError_t orthonormalise(float* Y, int64_t M, int l, const SvdWs& w, hipStream_
   for (int pass = 0; pass < 2; ++pass) {
     hipLaunchKernelGGL(k_gram_partial, dim3(parts), dim3(256), 0, s, Y, M, l, rows, w.gpart);
     hipLaunchKernelGGL(k_gram_finish, dim3(grid_for(l * l, 256, 64)), dim3(256), 0, s, w.gpart, parts, l * l, w.G);
-    hipLaunchKernelGGL(k_cholesky_inv, dim3(1), dim3(256), 0, s, w.G, l, w.L);
+    hipLaunchKernelGGL(k_chol_inv, dim3(1), dim3(256), 0, s, w.G, l, w.L);
     hipLaunchKernelGGL(k_right_mul, dim3((unsigned)((M + 15) / 16)), dim3(256), 0, s, Y, M, l, w.L, l, Y, 0);
     LR_CHECK();
   }
