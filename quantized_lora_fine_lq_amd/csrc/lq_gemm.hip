@@ -85,21 +85,31 @@ __device__ __forceinline__ void store_a_tile(uint16_t* sA, const u32x4_t (&r)[4]
   for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t*>(dst + 64 * q * PITCH) = r[q];
 }
 
+// Bt tiles written by the backward NF4 producer keep 16-byte chunk q of
+// row c at chunk q ^ bsw(c) (its LDS writes then hit 64 distinct banks);
+// the other producers store chunks in place.
+template <bool SWZ>
+__device__ __forceinline__ int bsw(int c) { return SWZ ? (c >> 4) & 7 : 0; }
+
 // 16 MFMAs of one half of a 64-wide step, both operands from LDS: wave tile
 // 64 x 128 = [2 row tiles] x [4 col tiles] over sub-steps 2 kh and 2 kh + 1
 // (the other wave of the pair takes the other half); all fragments of the
 // half are read up front.
+template <bool SWZ>
 __device__ __forceinline__ void mfma_half(const uint16_t* sAt, const uint16_t* sBt, f32x16_t (&acc)[2][4],
                                           int wr, int kh, int li, int lh) {
   const uint16_t* abase = sAt + (64 * wr + li) * PITCH + 32 * lh + 16 * kh;
-  const uint16_t* bbase = sBt + li * PITCH + 32 * lh + 16 * kh;
+  const int q0 = 4 * lh + 2 * kh;   // the lane's chunk in sub-step 2 kh
   u32x4_t a[2][2], b[2][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) a[u][rt] = ld16(abase + 32 * rt * PITCH + 8 * u);
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) b[u][ct] = ld16(bbase + 32 * ct * PITCH + 8 * u);
+    for (int ct = 0; ct < 4; ++ct) {
+      const int c = 32 * ct + li;
+      b[u][ct] = ld16(sBt + c * PITCH + 8 * ((q0 + u) ^ bsw<SWZ>(c)));
+    }
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -118,6 +128,7 @@ __device__ __forceinline__ void mfma_half(const uint16_t* sAt, const uint16_t* s
 // uses the main A tiles' thread mapping and row clamping; the Bt-side tile
 // maps thread -> row t/4, columns 16 (t % 4) .. +16 (rows past Ncols repeat
 // the last one: their outputs are never stored).
+template <bool SWZ>
 __device__ __forceinline__ void lora_tiles(const GemmParams& p, int jt, int64_t m0, int64_t n0,
                                            uint16_t* sA, uint16_t* sB) {
   const int cA = BK * jt + 8 * (threadIdx.x & 7);
@@ -153,9 +164,10 @@ __device__ __forceinline__ void lora_tiles(const GemmParams& p, int jt, int64_t 
     h[e] = x;
   }
   store_a_tile(sA, ra);
-  u32x4_t* dst = reinterpret_cast<u32x4_t*>(sB + row * PITCH + 16 * qq);
-  dst[0] = u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  dst[1] = u32x4_t{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16), h[14] | (h[15] << 16)};
+  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq) ^ bsw<SWZ>(row))) =
+      u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq + 1) ^ bsw<SWZ>(row))) =
+      u32x4_t{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16), h[14] | (h[15] << 16)};
 }
 
 // ---- Bt producers -----------------------------------------------------------
@@ -174,6 +186,7 @@ __device__ __forceinline__ float const_of(float c0, uint32_t q8, float s2, float
 // columns 16 (t % 4) .. +16 (8 code bytes, one block constant).
 template <bool DQ>
 struct ProdFwdNF4 {
+  static constexpr bool kSwz = false;
   const uint8_t* crow;   // codes of the thread's row at its 16 columns
   int64_t blk0;          // block index of step 0
   uint32_t code[2];
@@ -219,26 +232,31 @@ struct ProdFwdNF4 {
 };
 
 // Backward NF4: Bt[c][n] = W'[64 it + n][n0 + c] (the contraction runs over
-// W's rows). Thread -> rows 2 (t % 32) + {0, 1} of the step and columns
-// 8 (t / 32) .. +8 (4 code bytes per row, one block constant per row).
-// Rows past N contribute zero: their constant is forced to 0.
+// W's rows). Thread t of wave w -> rows 8 w + 2 (t % 4) + {0, 1} of the step
+// and columns 8 cg .. +8 with cg = (t % 64) / 4 (4 code bytes per row, one
+// block constant per row): a load instruction reads 4 whole 64-byte row
+// segments and 8 block constants. Each LDS word pairs the two rows of a
+// column; with the chunk swizzle bsw() the 64 words of a write instruction
+// fall in 64 distinct banks. Rows past N contribute zero: their constant is
+// forced to 0.
 template <bool DQ>
 struct ProdBwdNF4 {
+  static constexpr bool kSwz = true;
   int64_t kcol;          // first of the thread's 8 columns
   uint32_t code[2];
   float c0[2], s2[2];
   uint32_t q8[2];
   float livef[2];
   __device__ void init(const GemmParams& p, int64_t n0) {
-    const int kq = threadIdx.x >> 5;
-    kcol = min(n0 + 8 * kq, p.w.K - 8);   // columns past K: outputs never stored
+    const int cg = (threadIdx.x & 63) >> 2;
+    kcol = min(n0 + 8 * cg, p.w.K - 8);   // columns past K: outputs never stored
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
-    const int g = threadIdx.x & 31;
+    const int rp = 8 * (threadIdx.x >> 6) + 2 * (threadIdx.x & 3);   // first row of the pair in the step
     const int it = min(step, nMain - 1);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-      const int64_t nrow = (int64_t)it * BK + 2 * g + rr;
+      const int64_t nrow = (int64_t)it * BK + rp + rr;
       const bool ok = step < nMain && nrow < p.w.N;
       livef[rr] = ok ? 1.0f : 0.0f;
       const int64_t e0 = min(nrow, p.w.N - 1) * p.w.K + kcol;   // a valid row either way
@@ -253,21 +271,24 @@ struct ProdBwdNF4 {
     }
   }
   __device__ void store(const GemmParams& p, uint16_t* sB, const f32x2_t* sPair, float mean) {
-    const int g = threadIdx.x & 31, kq = threadIdx.x >> 5;
+    const int w = threadIdx.x >> 6, pr = threadIdx.x & 3, cg = (threadIdx.x & 63) >> 2;
     float v[2][8];
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const float cp = const_of<DQ>(c0[rr], q8[rr], s2[rr], mean) * livef[rr];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const f32x2_t q = sPair[(code[rr] >> (8 * b)) & 0xFFu];   // columns 8kq + 2b, +1
+        const f32x2_t q = sPair[(code[rr] >> (8 * b)) & 0xFFu];   // columns 8cg + 2b, +1
         v[rr][2 * b] = q.x * cp;
         v[rr][2 * b + 1] = q.y * cp;
       }
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(sB + (8 * kq) * PITCH + 2 * g);
+    // word of column c at rows 8w + 2pr, +1: chunk w of row c
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) dst[cc * (PITCH / 2)] = pack_bf16x2(v[0][cc], v[1][cc]);
+    for (int cc = 0; cc < 8; ++cc) {
+      const int c = 8 * cg + cc;
+      *reinterpret_cast<uint32_t*>(sB + c * PITCH + 8 * (w ^ bsw<true>(c)) + 2 * pr) = pack_bf16x2(v[0][cc], v[1][cc]);
+    }
   }
 };
 
@@ -276,6 +297,7 @@ struct ProdBwdNF4 {
 // + k]; thread -> row t/4, columns 16 (t % 4) .. +16 (two 16-byte loads).
 template <bool DQ>
 struct ProdFwdBF16 {
+  static constexpr bool kSwz = false;
   const uint16_t* src;
   u32x4_t v[2];
   bool live;
@@ -306,6 +328,7 @@ struct ProdFwdBF16 {
 // Rows past N contribute zero.
 template <bool DQ>
 struct ProdBwdBF16 {
+  static constexpr bool kSwz = false;
   int64_t kcol;
   u32x4_t v[2];
   bool ok[2];
@@ -409,13 +432,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   for (int it = 0; it < nMain; it += 2) {
     pa.load(p, it + 2, nMain);
     load_a_tile<TAIL>(p, min(it + 2, nMain - 1), ar, ra);
-    mfma_half(sA[0], sB[0], acc, wr, kh, li, lh);
+    mfma_half<Prod::kSwz>(sA[0], sB[0], acc, wr, kh, li, lh);
     pb.store(p, sB[1], sPair, mean);
     store_a_tile(sA[1], rb);
     __syncthreads();
     pb.load(p, it + 3, nMain);
     load_a_tile<TAIL>(p, min(it + 3, nMain - 1), ar, rb);
-    mfma_half(sA[1], sB[1], acc, wr, kh, li, lh);
+    mfma_half<Prod::kSwz>(sA[1], sB[1], acc, wr, kh, li, lh);
     pa.store(p, sB[0], sPair, mean);
     store_a_tile(sA[0], ra);
     __syncthreads();
@@ -424,9 +447,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   // LoRA segment (R2 = 64 ceil(2r / 64) columns) through the same LDS tiles
   const int nLora = p.R2 / BK;
   for (int jt = 0; jt < nLora; ++jt) {
-    lora_tiles(p, jt, m0, n0, sA[0], sB[0]);
+    lora_tiles<Prod::kSwz>(p, jt, m0, n0, sA[0], sB[0]);
     __syncthreads();
-    mfma_half(sA[0], sB[0], acc, wr, kh, li, lh);
+    mfma_half<Prod::kSwz>(sA[0], sB[0], acc, wr, kh, li, lh);
     __syncthreads();
   }
 
