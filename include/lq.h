@@ -209,8 +209,10 @@ size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *     t = X A^T            (float32, [M, r])
  *     H = X W'^T + s t B^T (float32 accumulation, stored as h_dtype)
  * For an NF4 weight W' is never materialised in memory: packed codes are
- * dequantized inside the GEMM (M <= 16 uses the memory-bound GEMV kernel,
- * larger M the MFMA GEMM). A codebook weight is first dequantized into the
+ * dequantized inside the GEMM (M <= 16 and K <= 33728 use the memory-bound
+ * GEMV kernel, other shapes the MFMA GEMM; the environment variable
+ * LQ_FORCE_PATH=gemm selects the GEMM at any M, a testing aid). A codebook
+ * weight is first dequantized into the
  * workspace by its per-channel dequantization kernel ([LowRA] section 3),
  * then multiplied by the MFMA GEMM.
  *   X  [M, K] bf16;  A [r, K] bf16;  B [N, r] bf16
@@ -246,7 +248,8 @@ size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
 /*
  * Second stage of the forward ([QLoRA] introduction): given t = X A^T,
  * H = X W'^T + (alpha / r) t B^T with W' dequantized inside the kernel (the
- * GEMV kernel for M <= 16 with NF4, else the MFMA GEMM; a codebook weight is
+ * GEMV kernel for M <= 16 and K <= 33728 with NF4, else the MFMA GEMM, as for
+ * lq_qlora_forward; a codebook weight is
  * dequantized into the workspace first). Arguments as lq_qlora_forward;
  * t [M, r] float32 is read. The workspace (caller-owned,
  * lq_dequant_gemm_workspace bytes) receives the dequantized codebook weight;

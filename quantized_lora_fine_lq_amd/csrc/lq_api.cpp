@@ -44,7 +44,7 @@ int check_qweight(const lq_qweight* w, QWeight* out) {
 }
 
 // Forward path choice: the GEMV kernel for decode-sized M (NF4 only), else
-// the MFMA GEMM. LQ_FORCE_PATH=gemm|gemv overrides (for tests).
+// the MFMA GEMM. LQ_FORCE_PATH=gemm forces the GEMM at any M (for tests).
 bool use_gemv(const QWeight& w, int64_t M) {
   if (M > 16 || !gemv_supported(w)) return false;
   const char* f = std::getenv("LQ_FORCE_PATH");
