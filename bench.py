@@ -14,7 +14,9 @@ but no flops. The JSON line also carries the roofline of the dominant kernel
 (the forward dequant-GEMM), the CPU oracle timed on the host, and a
 per-kernel table (GB/s or TFLOP/s against MI355X peaks) for the other
 workloads: the MLP pair (4096 <-> 11008, 4096 tokens, r = 64) and the decode
-GEMV (28672 x 8192, 1 / 4 / 16 tokens).
+GEMV (28672 x 8192, 1 / 4 / 16 tokens). With the table come two measured
+ceilings: the bandwidth of a plain 1 GiB device copy (each memory-bound row
+also gives its fraction of it) and the shader clock under the step's load.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -346,6 +348,51 @@ def cpu_baseline(syn):
                       "on the host CPU, median of 3"}
 
 
+def copy_ceiling_gbs(torch) -> float:
+    """Measured memory ceiling: torch's own device copy of 1 GiB (1 GiB read
+    + 1 GiB written per copy), HIP events around 5 copies after 2 warm-ups."""
+    src = torch.ones(256 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbs = 5 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def sclk_under_load(torch, step) -> dict | None:
+    """The shader clock while the step runs: about a second of steps is
+    queued, then rocm-smi (a separate process reading the driver's clock
+    report) samples the current sclk. None when the tool is missing or its
+    output has no sclk line."""
+    import re
+    import shutil
+    import subprocess
+    tool = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if tool is None:
+        return None
+    for _ in range(3000):
+        step()
+    try:
+        r = subprocess.run([tool, "--showclocks"], capture_output=True, text=True, timeout=30)
+        txt = r.stdout
+    except Exception:
+        txt = ""
+    torch.cuda.synchronize()
+    m = re.search(r"sclk[^\n]*?\((\d+)\s*Mhz\)", txt, re.IGNORECASE)
+    if not m:
+        return None
+    return {"MHz": int(m.group(1)), "how": "rocm-smi --showclocks while ~1 s of q_proj steps was queued"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -406,12 +453,21 @@ def main():
                 "algorithmic_flop_per_launch": fl["fwd_gemm"]}
 
     kernels = {}
+    ceilings = None
     if not args.no_kernels:
+        copy_gbs = copy_ceiling_gbs(torch)
+        ceilings = {"copy_GB/s": round(copy_gbs, 1),
+                    "copy": "torch device copy, 1 GiB read + 1 GiB written; frac_copy in the kernel table is "
+                            "relative to it",
+                    "sclk": sclk_under_load(torch, calls[0].step)}
+        log("ceilings", ceilings)
+
         def rec(name, ms, work, unit):
             if unit == "GB/s":
                 ach = work / (ms * 1e-3) / 1e9
                 kernels[name] = {"us": round(ms * 1e3, 2), "GB/s": round(ach, 1),
-                                 "frac_hbm": round(ach / HBM_PEAK_GBS, 4), "bytes": work}
+                                 "frac_hbm": round(ach / HBM_PEAK_GBS, 4),
+                                 "frac_copy": round(ach / copy_gbs, 4), "bytes": work}
             else:
                 ach = work / (ms * 1e-3) / 1e12
                 kernels[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(ach, 1),
@@ -556,6 +612,7 @@ def main():
                    "input_sets_rotated": args.sets},
         "roofline": roofline,
         "cpu_baseline": None,
+        "ceilings": ceilings,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
