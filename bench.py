@@ -397,7 +397,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the quantized-LoRA hot path here is a single-GPU "
-              "kernel library; sharding across GPUs is a design note, not a run).", flush=True)
+              "kernel library, and sharding across GPUs is a design note, not a run.", flush=True)
         sys.exit(2)
     import numpy as np
     import torch

@@ -1,0 +1,71 @@
+"""Host-side checks of bench.py: the algorithmic work it divides by, and its
+one-GPU guard (runs without a GPU).
+
+The byte counts follow from the storage format alone: a weight is read as
+float32 (4 B) and written as packed NF4 (1/2 B), one float32 absmax per
+64-block (QLoRA page, NF4 section), and with double quantization one 8-bit
+code per block, one float32 scale per 256 blocks and one float32 mean
+(QLoRA page, double-quantization section); the dequantized weight is bf16.
+"""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+class Layer:
+    def __init__(self, N, K, r, M):
+        self.N, self.K, self.r, self.M = N, K, r, M
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (11008, 4096), (28672, 8192)])
+def test_codec_bytes_follow_the_format(bench, N, K):
+    n = N * K
+    b = bench.codec_bytes(Layer(N, K, 16, 1), 1)
+    # quantize: 4 B read + 1/2 B written per weight, 4 B per 64 weights
+    assert b["quantize"] * 64 == n * (4 * 64 + 32 + 4)
+    # profiling pass: the float32 weight once
+    assert b["profile"] == 4 * n
+    consts = n // 64 + 4 * ((n // 64 + 255) // 256) + 4
+    assert b["dequant"] == n // 2 + consts + 2 * n
+    assert b["double_quant"] == 4 * (n // 64) + consts
+    # decode GEMV at M tokens: packed weight + X + A + B + H + t
+    for M in (1, 4, 16):
+        g = bench.codec_bytes(Layer(N, K, 16, M), M)["gemv"]
+        assert g == n // 2 + consts + 2 * K * M + 2 * 16 * K + 2 * N * 16 + 2 * N * M + 4 * M * 16
+
+
+def test_q_proj_decode_figures(bench):
+    # the 4096^2 and 28672 x 8192 layers in whole bytes
+    q = bench.codec_bytes(Layer(4096, 4096, 16, 2048))
+    assert q["quantize"] == 76_546_048 and q["dequant"] == 42_209_284
+    d = bench.codec_bytes(Layer(28672, 8192, 16, 1), 1)
+    assert d["gemv"] - (2 * 8192 + 2 * 16 * 8192 + 2 * 28672 * 16 + 2 * 28672 + 4 * 16) == 121_167_876
+
+
+def test_layer_flops(bench):
+    M, N, K, r = 2048, 4096, 4096, 16
+    f = bench.layer_flops(Layer(N, K, r, M), M)
+    assert f["fwd_gemm"] == 2 * M * N * K + 2 * M * N * r     # X W'^T + (s t) B^T in one GEMM
+    assert f["lora_down"] == 2 * M * K * r                     # t = X A^T
+    # backward: grad_X = G W' + s u A, u = G B, dB = s G^T t, dA = s u^T X
+    assert f["bwd"] == 2 * M * N * K + 2 * M * K * r + 2 * M * N * r + 2 * M * N * r + 2 * M * K * r
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
