@@ -287,17 +287,14 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  // dB = s G^T t and dA = s u^T X in one launch, then grad_X
   SplitJobDesc job_b, job_a;
-  if (dB) {
-    e = launch_col_skinny(pt2_t, G, M, q.N, r, scale, dB, true, part_b, &job_b, s);
-    if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  }
+  const ColSkinnyReq req_b{pt2_t, G, q.N, scale, dB, true, part_b};
+  const ColSkinnyReq req_a{pt2_u, X, q.K, scale, dA, false, part_a};
+  e = launch_col_skinny(dB ? &req_b : nullptr, dA ? &req_a : nullptr, M, r, &job_b, &job_a, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (grad_X) {
     e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s);
-    if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  }
-  if (dA) {
-    e = launch_col_skinny(pt2_u, X, M, q.K, r, scale, dA, false, part_a, &job_a, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
   }
   return launch_status(launch_reduce_splits2(job_b, job_a, s));

@@ -862,14 +862,34 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
 // when r % 32 == 0 or r == 16 (partner row in the same lane), otherwise both
 // are kept. Each workgroup writes the partial sums of its m-split;
 // k_reduce_splits2 adds them.
+// One job of the column form: product pt2^T-by-Q over its m-splits, in
+// `tiles` column tiles of 128.
+struct ColJob {
+  const uint16_t* pt2;
+  const uint16_t* Q;
+  int64_t C;
+  int64_t m_per_split;
+  int splits;
+  unsigned tiles;
+  float* part;
+};
+
+// Two jobs share one launch (same M and r): workgroups x < j0.tiles take
+// job 0, the rest job 1; split rows y past a job's own split count exit.
 template <int JT2>
-__global__ __launch_bounds__(256) void k_col_skinny(const uint16_t* __restrict__ pt2, int64_t Mp,
-                                                    const uint16_t* __restrict__ Q, int64_t M, int64_t C, int r,
-                                                    int64_t m_per_split, int combine, float* __restrict__ part) {
+__global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_t Mp, int64_t M, int r,
+                                                    int combine) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * (128 + 8)];
+  const bool second = blockIdx.x >= j0.tiles;
+  const ColJob jb = second ? j1 : j0;
+  if ((int)blockIdx.y >= jb.splits) return;   // the whole workgroup
+  const uint16_t* __restrict__ pt2 = jb.pt2;
+  const uint16_t* __restrict__ Q = jb.Q;
+  const int64_t C = jb.C, m_per_split = jb.m_per_split;
+  float* __restrict__ part = jb.part;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 31, lh = lane >> 5;
-  const int64_t c0 = (int64_t)blockIdx.x * 128;
+  const int64_t c0 = (int64_t)(second ? blockIdx.x - j0.tiles : blockIdx.x) * 128;
   const int64_t m_begin = (int64_t)blockIdx.y * m_per_split;
   const int64_t m_end = min(M, m_begin + m_per_split);
   const int rows2 = 2 * r;
@@ -1053,29 +1073,42 @@ size_t col_skinny_ws_floats(int64_t M, int64_t C, int r) {
 
 // Partial sums of the column form into ws ([splits][srows][C]); returns the
 // reduction job that finishes it (run by launch_reduce_splits2).
-hipError_t launch_col_skinny(const uint16_t* pt2, const uint16_t* Q, int64_t M, int64_t C, int r, float scale,
-                             float* out, bool out_transposed, float* ws, SplitJobDesc* job, hipStream_t s) {
-  const int splits = col_skinny_splits(M, C);
-  const int64_t mchunks = (M + 31) / 32;
-  const int64_t m_per_split = ((mchunks + splits - 1) / splits) * 32;
-  const int real_splits = (int)((M + m_per_split - 1) / m_per_split);
+hipError_t launch_col_skinny(const ColSkinnyReq* a, const ColSkinnyReq* b, int64_t M, int r, SplitJobDesc* ja,
+                             SplitJobDesc* jb, hipStream_t s) {
+  const ColSkinnyReq* req[2] = {a, b};
+  SplitJobDesc* desc[2] = {ja, jb};
+  ColJob job[2] = {};
+  int njobs = 0, ymax = 1;
   const int combine = (r % 32 == 0 || r == 16) ? 1 : 0;
-  const dim3 grid((unsigned)((C + 127) / 128), (unsigned)real_splits);
+  for (int i = 0; i < 2; ++i) {
+    if (!req[i]) continue;
+    const ColSkinnyReq& q = *req[i];
+    const int splits = col_skinny_splits(M, q.C);
+    const int64_t mchunks = (M + 31) / 32;
+    const int64_t m_per_split = ((mchunks + splits - 1) / splits) * 32;
+    const int real_splits = (int)((M + m_per_split - 1) / m_per_split);
+    job[njobs] = ColJob{q.pt2, q.Q, q.C, m_per_split, real_splits, (unsigned)((q.C + 127) / 128), q.ws};
+    ymax = std::max(ymax, real_splits);
+    ++njobs;
+    SplitJobDesc* d = desc[i];
+    d->part = q.ws;
+    d->splits = real_splits;
+    d->rows = r;
+    d->cols = q.C;
+    d->srows = combine ? r : 2 * r;
+    d->pair = combine ? 0 : (int64_t)r * q.C;
+    d->scale = q.scale;
+    d->out = q.out;
+    d->transposed = q.out_transposed ? 1 : 0;
+  }
+  if (njobs == 0) return hipSuccess;
+  const dim3 grid(job[0].tiles + (njobs > 1 ? job[1].tiles : 0u), (unsigned)ymax);
   switch ((2 * r + 31) / 32) {
-#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, pt2, split_rows(M), Q, M, C, r, m_per_split, combine, ws); break;
+#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, job[0], job[1], split_rows(M), M, r, combine); break;
     LQ_CS(1) LQ_CS(2) LQ_CS(3) LQ_CS(4) LQ_CS(5) LQ_CS(6) LQ_CS(7) LQ_CS(8)
 #undef LQ_CS
     default: return hipErrorInvalidValue;
   }
-  job->part = ws;
-  job->splits = real_splits;
-  job->rows = r;
-  job->cols = C;
-  job->srows = combine ? r : 2 * r;
-  job->pair = combine ? 0 : (int64_t)r * C;
-  job->scale = scale;
-  job->out = out;
-  job->transposed = out_transposed ? 1 : 0;
   return hipGetLastError();
 }
 

@@ -132,8 +132,21 @@ struct SplitJobDesc {
   int transposed = 0;
 };
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r);
-hipError_t launch_col_skinny(const uint16_t* pt2, const uint16_t* Q, int64_t M, int64_t C, int r, float scale,
-                             float* out, bool out_transposed, float* ws, SplitJobDesc* job, hipStream_t s);
+// One column-form product: pt2 ([2r][Mp] split operand), Q [M, C], its
+// output and partial-sum workspace (col_skinny_ws_floats(M, C, r) floats).
+struct ColSkinnyReq {
+  const uint16_t* pt2;
+  const uint16_t* Q;
+  int64_t C;
+  float scale;
+  float* out;
+  bool out_transposed;
+  float* ws;
+};
+// Up to two column-form products with the same M and r in one launch
+// (either request may be null); fills the reduction job of each.
+hipError_t launch_col_skinny(const ColSkinnyReq* a, const ColSkinnyReq* b, int64_t M, int r, SplitJobDesc* ja,
+                             SplitJobDesc* jb, hipStream_t s);
 hipError_t launch_reduce_splits2(const SplitJobDesc& a, const SplitJobDesc& b, hipStream_t s);
 
 // Dequant-GEMM with the LoRA segment (formed in the kernel from t or u and
