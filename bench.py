@@ -14,7 +14,9 @@ but no flops. The JSON line also carries the roofline of the dominant kernel
 (the forward dequant-GEMM), the CPU oracle timed on the host, and a
 per-kernel table (GB/s or TFLOP/s against MI355X peaks) for the other
 workloads: the MLP pair (4096 <-> 11008, 4096 tokens, r = 64) and the decode
-GEMV (28672 x 8192, 1 / 4 / 16 tokens). With the table come two measured
+GEMV (28672 x 8192, 1 / 4 / 16 tokens). After the headline window, further
+windows of the same steps give the run-to-run spread (step_spread). With the
+table come two measured
 ceilings: the bandwidth of a plain 1 GiB device copy (each memory-bound row
 also gives its fraction of it) and the shader clock under the step's load.
 
@@ -44,11 +46,13 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the steps")
+    ap.add_argument("--noise-windows", type=int, default=5,
+                    help="further timed windows of K steps for the run-to-run spread (0: none)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -186,6 +190,12 @@ def make_devs(torch, lq, syn, name, n_sets, M=None, with_grad=True):
     return devs
 
 
+def kernel_event_stride(steps):
+    """Steps between the timed steps whose forward dequant-GEMM gets its own
+    event pair: every 4th, or closer so that at least 5 launches are timed."""
+    return max(1, min(4, steps // 5))
+
+
 def time_ms(torch, fns, iters, warmup=3):
     """Average ms per call of fns[i % len(fns)] over `iters` back-to-back
     calls on the current stream (HIP events)."""
@@ -321,7 +331,8 @@ def measured_traffic():
 
 
 def cpu_baseline(syn):
-    """The oracle (numpy / float64 BLAS) on one full q_proj step."""
+    """The oracle (numpy / float64 BLAS) on whole q_proj steps, repeated
+    until about 10 s of CPU work."""
     import numpy as np
     from oracle import nf4, dq, layer
     try:
@@ -332,7 +343,8 @@ def cpu_baseline(syn):
     L = syn.LAYERS["q_proj"]
     W, X, A, B, G = syn.weight(L), syn.activations(L), syn.lora_a(L), syn.lora_b(L), syn.grad_out(L)
     times = []
-    for _ in range(3):
+    # whole q_proj steps until about 10 s of CPU work (at least 3 steps)
+    while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
         t0 = time.perf_counter()
         packed, c = nf4.quantize(W)
         code8, s2, mu = dq.double_quant(c)
@@ -340,12 +352,13 @@ def cpu_baseline(syn):
         H, t = layer.forward(Wd, X.f32, A.f32, B.f32, L.alpha)
         dX, dA, dB = layer.backward(Wd, X.f32, G.f32, A.f32, B.f32, L.alpha)
         times.append(time.perf_counter() - t0)
-    dt = sorted(times)[1]
+    total = sum(times)
     fl = layer_flops(L, L.M)
-    return {"value": round((fl["fwd"] + fl["bwd"]) / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "one full q_proj step (quantize, double quant, dequant, float64 forward + backward) "
-                      "on the host CPU, median of 3"}
+    return {"value": round(len(times) * (fl["fwd"] + fl["bwd"]) / total / 1e12, 4), "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle", "seconds": round(total, 2),
+            "seconds_per_step_median": round(sorted(times)[len(times) // 2], 3),
+            "sample": f"{len(times)} full q_proj steps (quantize, double quant, dequant, float64 forward + "
+                      f"backward) on the host CPU, {total:.1f} s in all; value = their flops / that time"}
 
 
 def copy_ceiling_gbs(torch) -> float:
@@ -424,17 +437,20 @@ def main():
 
     # ---- the timed step -------------------------------------------------
     # The forward dequant-GEMM (the dominant kernel) is bracketed by its own
-    # events inside every timed step, on the stream the library launches on.
+    # events inside the timed steps, on the stream the library launches on:
+    # every `ev_stride`-th step (at least 5 launches), since each pair of
+    # event records adds a few microseconds to the step it sits in.
     for i in range(args.warmup):
         calls[i % len(calls)].step()
     torch.cuda.synchronize()
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    ev_stride = kernel_event_stride(args.steps)
+    kev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in range(0, args.steps, ev_stride)}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        calls[i % len(calls)].step(kev[i])
+        calls[i % len(calls)].step(kev.get(i))
     e1.record()
     e1.synchronize()
     wall = time.perf_counter() - w0
@@ -442,8 +458,27 @@ def main():
     value = step_flops / (ms_step * 1e-3) / 1e12
     log(f"step: {ms_step:.4f} ms  ({value:.1f} TFLOP/s), wall {wall:.3f} s")
 
+    # run-to-run spread: further windows of the same K steps, after the
+    # headline window (which alone gives value and ms_per_step)
+    windows = []
+    for w in range(args.noise_windows):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for i in range(args.steps):
+            calls[(i + w) % len(calls)].step()
+        a1.record()
+        a1.synchronize()
+        windows.append(a0.elapsed_time(a1) / args.steps)
+    spread = None
+    if windows:
+        ws = sorted(windows)
+        pick = lambda q: ws[min(len(ws) - 1, int(round(q * (len(ws) - 1))))]
+        spread = {"windows": len(ws), "steps_each": args.steps, "ms_per_step_p10": round(pick(0.1), 5),
+                  "ms_per_step_p50": round(pick(0.5), 5), "ms_per_step_p90": round(pick(0.9), 5)}
+        log("spread", spread)
+
     # ---- dominant kernel: forward dequant-GEMM on q_proj -------------------
-    fwd_ms = sum(a.elapsed_time(b) for a, b in kev) / len(kev)
+    fwd_ms = sum(a.elapsed_time(b) for a, b in kev.values()) / len(kev)
     fwd_tflops = fl["fwd_gemm"] / (fwd_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "k_dq_gemm<ProdFwdNF4<true>> (q_proj, M=2048)",
                 "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -611,6 +646,7 @@ def main():
                    "global_batch": L.M, "tokens": L.M, "N": L.N, "K": L.K, "r": L.r, "alpha": L.alpha,
                    "input_sets_rotated": args.sets},
         "roofline": roofline,
+        "step_spread": spread,
         "cpu_baseline": None,
         "ceilings": ceilings,
         "kernels": kernels,

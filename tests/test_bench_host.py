@@ -69,3 +69,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+@pytest.mark.parametrize("steps", [1, 4, 5, 9, 20, 21, 200, 1000])
+def test_kernel_event_stride_times_enough_launches(bench, steps):
+    s = bench.kernel_event_stride(steps)
+    timed = len(range(0, steps, s))
+    assert 1 <= s <= 4
+    # at least 5 launches are timed whenever the window has 5 steps
+    assert timed >= min(5, steps)
