@@ -249,6 +249,25 @@ def test_lora_down_shapes(lq, torch, M, K, r):
     assert layer.rel_frobenius(host(t), tref) <= 1e-5
 
 
+@pytest.mark.parametrize("M,K,r", [(2050, 512, 16), (2048, 4096, 16), (4100, 256, 16), (1030, 1024, 64),
+                                   (3000, 512, 128)])
+def test_lora_down_many_rows(lq, torch, M, K, r):
+    """t = X A^T with many 16-row groups and ragged M: every row is written
+    once and matches the oracle, and repeated calls give the same bits."""
+    rng = np.random.default_rng(M + 3 * K + r)
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    A = syn.to_bf16_bits((rng.standard_normal((r, K)) * 0.02).astype(np.float32))
+    Xd, Ad = bf16_dev(torch, X), bf16_dev(torch, A)
+    t1 = torch.full((M, r), float("nan"), dtype=torch.float32, device="cuda")
+    t2 = torch.full((M, r), float("nan"), dtype=torch.float32, device="cuda")
+    lq.lora_down(Xd, Ad, t1)
+    lq.lora_down(Xd, Ad, t2)
+    assert torch.equal(t1, t2)
+    _, tref = layer.forward(np.zeros((8, K), np.float32), syn.bf16_bits_to_f32(X), syn.bf16_bits_to_f32(A),
+                            np.zeros((8, r), np.float32), float(r))
+    assert layer.rel_frobenius(host(t1), tref) <= 1e-5
+
+
 def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
     L, W, X, A, B = make_layer(7, 512, 1024, 16, 16, 32.0)
     qw = lq.QWeight.from_weight(dev(torch, W))
@@ -315,6 +334,10 @@ def test_unit_vector_probe_bit_exact(lq, torch, M):
     (264, 320, 33, 24, 8.0),       # N % 64 != 0, M % 32 != 0, hi/lo rows kept apart
     (192, 256, 50, 128, 16.0),     # largest rank: eight 16-wide tiles of t and u
     (136, 192, 77, 40, 16.0),      # 2r = 80: three 32-row product tiles
+    (2056, 2048, 70, 16, 32.0),    # wide N, K with few rows: u's contraction ragged past 32 blocks
+    (2048, 2048, 40, 64, 16.0),    # four 16-wide tiles over 32 column blocks
+    (1024, 1024, 48, 128, 16.0),   # eight tiles (8 waves per workgroup)
+    (264, 256, 2050, 16, 32.0),    # many row groups, ragged M (split rows padded to 2080)
 ])
 @pytest.mark.parametrize("recompute_t", [False, True])
 def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
