@@ -248,15 +248,40 @@ __global__ __launch_bounds__(1024) void k_tree_reduce(const double* __restrict__
   }
 }
 
+// With SUMS, the block sums (at most 1024 of them) are passed instead of the
+// mean, and every workgroup forms the mean itself by the same tree as
+// k_tree_reduce: 1024 zero-padded leaves in order, 4 per lane summed in
+// pairs, a butterfly over the 64 lanes, then the 4 wave sums in pairs, which
+// is the same perfect binary tree, so every workgroup gets the same value;
+// workgroup 0 stores it. This saves the launch of k_tree_reduce.
+template <bool SUMS>
 __global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, int64_t n_b,
-                                                   const float* __restrict__ mean,
+                                                   const double* __restrict__ sums, int64_t n_sums,
+                                                   float* __restrict__ mean,
                                                    uint8_t* __restrict__ absmax_q,
                                                    float* __restrict__ dq_scale) {
   __shared__ float wmax[4];
+  __shared__ double wsum[4];
   const int t = threadIdx.x;
   const int64_t j = (int64_t)blockIdx.x * 256 + t;
-  const float mu = *mean;
-  const float d = (j < n_b) ? c[j] - mu : 0.0f;
+  const float cj = (j < n_b) ? c[j] : 0.0f;
+  float mu;
+  if constexpr (SUMS) {
+    double v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (4 * t + i < n_sums) ? sums[4 * t + i] : 0.0;
+    double w = (v[0] + v[1]) + (v[2] + v[3]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) w = w + __shfl_xor(w, m);
+    if ((t & 63) == 0) wsum[t >> 6] = w;
+    __syncthreads();
+    const double total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    mu = (float)(total / (double)n_b);
+    if (blockIdx.x == 0 && t == 0) *mean = mu;
+  } else {
+    mu = *mean;
+  }
+  const float d = (j < n_b) ? cj - mu : 0.0f;
   float a = wave_max(fabsf(d));
   if ((t & 63) == 0) wmax[t >> 6] = a;
   __syncthreads();
@@ -525,6 +550,11 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
   hipLaunchKernelGGL(k_dq_block_sums, dim3((unsigned)n_d), dim3(64), 0, s, absmax, n_b, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (n_d <= 1024) {   // one level of the tree: the encoder forms the mean itself
+    hipLaunchKernelGGL(k_dq_encode<true>, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b,
+                       (const double*)ws, n_d, dq_mean, absmax_q, dq_scale);
+    return hipGetLastError();
+  }
   double* cur = ws;
   int64_t n = n_d;
   while (n > 1024) {
@@ -538,8 +568,8 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
   }
   hipLaunchKernelGGL(k_tree_reduce, dim3(1), dim3(1024), 0, s, cur, n, (double*)nullptr, n_b, dq_mean);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_dq_encode, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b, dq_mean,
-                     absmax_q, dq_scale);
+  hipLaunchKernelGGL(k_dq_encode<false>, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b,
+                     (const double*)nullptr, (int64_t)0, dq_mean, absmax_q, dq_scale);
   return hipGetLastError();
 }
 

@@ -168,8 +168,11 @@ def test_quantize_strided_sweep(lq, torch, scaled):
 # ---------------------------------------------------------------------------
 # double quantization
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("n_b", [1, 255, 256, 1000, 16384, 300000])
+@pytest.mark.parametrize("n_b", [1, 255, 256, 1000, 16384, 262144, 262145, 300000])
 def test_double_quant_bit_exact(lq, torch, n_b):
+    """Codes, scales and the mean bit for bit. Up to 1024 blocks of 256
+    (n_b <= 262144) the encoder forms the mean from the block sums itself;
+    past that a separate tree reduction does (262145: 1025 block sums)."""
     rng = np.random.default_rng(n_b)
     c = np.abs(rng.standard_normal(n_b) * 0.02 + 0.05).astype(np.float32)
     if n_b > 300:
