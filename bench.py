@@ -10,15 +10,22 @@ so the 256 MB Infinity Cache cannot hold the step's working set.
 
 value = algorithmic GEMM + LoRA flops of the forward and backward per step
 divided by the step time (TFLOP/s); quantize / double quant / dequant add time
-but no flops. The JSON line also carries the roofline of the dominant kernel
-(the forward dequant-GEMM), the CPU oracle timed on the host, and a
-per-kernel table (GB/s or TFLOP/s against MI355X peaks) for the other
-workloads: the MLP pair (4096 <-> 11008, 4096 tokens, r = 64) and the decode
-GEMV (28672 x 8192, 1 / 4 / 16 tokens). After the headline window, further
-windows of the same steps give the run-to-run spread (step_spread). With the
-table come two measured
-ceilings: the bandwidth of a plain 1 GiB device copy (each memory-bound row
-also gives its fraction of it) and the shader clock under the step's load.
+but no flops. Before the timed window the GPU runs steps for a fixed wall
+time (clock settling), then the W warm-up steps.
+
+The JSON line also carries:
+  * roofline -- the dominant kernel (the forward dequant-GEMM) timed by HIP
+    events around back-to-back launches on rotated inputs (the same kernel
+    duration a kernel trace reports), against the bf16 MFMA peak, with its
+    HBM traffic from the committed counter profile;
+  * kernels -- every kernel of the path on the five workloads (1024^2 latency
+    rows, q_proj, the MLP pair, the 1.75-bit codebook layer, decode GEMV),
+    each arm run for a fixed wall time after 20 warm-up launches, the median
+    of its batches with p10 / p90; memory-bound arms rotate at least 1 GiB
+    of distinct buffers so every launch streams from HBM; the forward GEMM
+    arm is run twice (replicated arm) and their gap is the noise floor;
+  * sessions -- the headline step measured again in fresh processes;
+  * cpu_baseline -- the CPU oracle on the host (all BLAS threads, and one).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -48,8 +55,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-seconds", type=float, default=2.0,
+                    help="wall time of untimed steps before the warm-up (clock settling)")
+    ap.add_argument("--arm-seconds", type=float, default=0.4, help="wall time of each kernel-table arm")
+    ap.add_argument("--sessions", type=int, default=3,
+                    help="whole sessions (this process + fresh child processes) of the headline step")
+    ap.add_argument("--session-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel table")
+    ap.add_argument("--only", default="",
+                    help="comma list of kernel-table groups to run (linear1k, q_proj, mlp, lowra, decode); "
+                         "default all")
     ap.add_argument("--sets", type=int, default=4, help="input sets rotated through the steps")
     ap.add_argument("--noise-windows", type=int, default=5,
                     help="further timed windows of K steps for the run-to-run spread (0: none)")
@@ -196,20 +212,48 @@ def kernel_event_stride(steps):
     return max(1, min(4, steps // 5))
 
 
-def time_ms(torch, fns, iters, warmup=3):
-    """Average ms per call of fns[i % len(fns)] over `iters` back-to-back
-    calls on the current stream (HIP events)."""
+ARM_WARMUP = 20
+
+
+def time_arm(torch, fns, seconds, warmup=ARM_WARMUP):
+    """One fixed-duration arm: `warmup` untimed launches, then batches of
+    back-to-back launches of fns[i % len(fns)] (each batch about 20 ms,
+    bracketed by HIP events on the current stream, which is the stream the
+    library launches on) until `seconds` of wall time have passed (at least
+    3 batches). Returns (median, p10, p90) ms per launch over the batches and
+    the number of timed launches."""
+    n = len(fns)
     for i in range(warmup):
-        fns[i % len(fns)]()
+        fns[i % n]()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # calibration batch: one pass over the rotation (at least 4 launches)
+    cal = n * max(1, -(-4 // n))
     e0.record()
-    for i in range(iters):
-        fns[i % len(fns)]()
+    for i in range(cal):
+        fns[i % n]()
     e1.record()
     e1.synchronize()
-    return e0.elapsed_time(e1) / iters
+    est = max(e0.elapsed_time(e1) / cal, 1e-3)
+    batch = max(1, int(round(20.0 / est / n))) * n
+    per, k, launches = [], 0, 0
+    t0 = time.perf_counter()
+    while len(per) < 3 or time.perf_counter() - t0 < seconds:
+        e0.record()
+        for i in range(batch):
+            fns[(k + i) % n]()
+        e1.record()
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) / batch)
+        k += batch
+        launches += batch
+    per.sort()
+    pick = lambda q: per[min(len(per) - 1, int(round(q * (len(per) - 1))))]
+    return pick(0.5), pick(0.1), pick(0.9), launches
+
+
+def time_ms(torch, fns, seconds):
+    return time_arm(torch, fns, seconds)[0]
 
 
 def layer_flops(L, M):
@@ -235,7 +279,7 @@ def codec_bytes(L, M=0):
     }
 
 
-def rec_loraquant(torch, lq, name, d, rec, kernels, rho=0.9, bits_hi=3, bits_lo=1):
+def rec_loraquant(torch, lq, name, d, rec, kernels, arm_s, rho=0.9, bits_hi=3, bits_lo=1):
     """LoRAQuant-style quantization of the layer's adapter (float32 copies of
     its bf16 B [N, r] and A [r, K]): time per call and the adapter's error."""
     import numpy as np
@@ -257,7 +301,7 @@ def rec_loraquant(torch, lq, name, d, rec, kernels, rho=0.9, bits_hi=3, bits_lo=
     # reads B and A, writes the float32 reparameterized factors and reads them
     # twice (codebook learner, quantizer), writes codes and constants
     byts = 4 * r * (N + K) + 12 * r * (N + K) + r * (N + K) * bits_hi // 8 + 4 * r * (N + K) // 64
-    rec(f"{name}.loraquant", time_ms(torch, [run], 20), byts, "GB/s")
+    rec(f"{name}.loraquant", time_arm(torch, [run], arm_s), byts, "GB/s")
     Ad, Bd = lq.loraquant_dequant(q)
     ref = B32.double() @ A32.double()
     err = ((Bd.double() @ Ad.double() - ref).norm() / ref.norm()).item()
@@ -332,13 +376,15 @@ def measured_traffic():
 
 def cpu_baseline(syn):
     """The oracle (numpy / float64 BLAS) on whole q_proj steps, repeated
-    until about 10 s of CPU work."""
+    until about 10 s of CPU work, on all the BLAS threads; then its forward +
+    backward on a 512-token slice of the same step on one thread."""
     import numpy as np
     from oracle import nf4, dq, layer
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
+        threadpool_limits = None
         cores = os.cpu_count() or 1
     L = syn.LAYERS["q_proj"]
     W, X, A, B, G = syn.weight(L), syn.activations(L), syn.lora_a(L), syn.lora_b(L), syn.grad_out(L)
@@ -354,11 +400,27 @@ def cpu_baseline(syn):
         times.append(time.perf_counter() - t0)
     total = sum(times)
     fl = layer_flops(L, L.M)
-    return {"value": round(len(times) * (fl["fwd"] + fl["bwd"]) / total / 1e12, 4), "unit": "TFLOP/s",
-            "cores": int(cores), "kind": "oracle", "seconds": round(total, 2),
-            "seconds_per_step_median": round(sorted(times)[len(times) // 2], 3),
-            "sample": f"{len(times)} full q_proj steps (quantize, double quant, dequant, float64 forward + "
-                      f"backward) on the host CPU, {total:.1f} s in all; value = their flops / that time"}
+    out = {"value": round(len(times) * (fl["fwd"] + fl["bwd"]) / total / 1e12, 4), "unit": "TFLOP/s",
+           "cores": int(cores), "kind": "oracle", "seconds": round(total, 2),
+           "seconds_per_step_median": round(sorted(times)[len(times) // 2], 3),
+           "sample": f"{len(times)} full q_proj steps (quantize, double quant, dequant, float64 forward + "
+                     f"backward) on the host CPU, {total:.1f} s in all; value = their flops / that time"}
+    if threadpool_limits is not None:
+        Ms = 512
+        Xs, Gs = X.f32[:Ms], G.f32[:Ms]
+        with threadpool_limits(limits=1):
+            reps = []
+            while len(reps) < 2 or (sum(reps) < 3.0 and len(reps) < 20):
+                t0 = time.perf_counter()
+                layer.forward(Wd, Xs, A.f32, B.f32, L.alpha)
+                layer.backward(Wd, Xs, Gs, A.f32, B.f32, L.alpha)
+                reps.append(time.perf_counter() - t0)
+        fls = layer_flops(L, Ms)
+        out["single_thread"] = {
+            "value": round(len(reps) * (fls["fwd"] + fls["bwd"]) / sum(reps) / 1e12, 4), "unit": "TFLOP/s",
+            "cores": 1, "sample": f"{len(reps)} float64 forward + backward passes over the first {Ms} of the "
+                                  f"step's {L.M} tokens, one BLAS thread, {sum(reps):.1f} s"}
+    return out
 
 
 def copy_ceiling_gbs(torch) -> float:
@@ -406,12 +468,87 @@ def sclk_under_load(torch, step) -> dict | None:
     return {"MHz": int(m.group(1)), "how": "rocm-smi --showclocks while ~1 s of q_proj steps was queued"}
 
 
+class CodecSet:
+    """Distinct buffers for the memory-bound codec arms of one layer: a copy
+    of W and every output of quantize, the profiling pass, double quant and
+    dequant."""
+
+    def __init__(self, torch, lq, L, W_dev):
+        dev = torch.device("cuda")
+        N, K = L.N, L.K
+        n_b = N * K // 64
+        n_d = (n_b + 255) // 256
+        self.N, self.K = N, K
+        self.W = W_dev.clone()
+        self.codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+        self.absmax = torch.empty(n_b, dtype=torch.float32, device=dev)
+        self.aq = torch.empty(n_b, dtype=torch.uint8, device=dev)
+        self.s2 = torch.empty(n_d, dtype=torch.float32, device=dev)
+        self.mu = torch.empty(1, dtype=torch.float32, device=dev)
+        self.stats = torch.empty(2, dtype=torch.float64, device=dev)
+        self.prof_b = lq.lib.lq_profile_workspace(N, K, 64)
+        self.prof_ws = torch.empty(self.prof_b, dtype=torch.uint8, device=dev)
+        self.dq_b = lq.lib.lq_double_quant_workspace(n_b, 256)
+        self.dq_ws = torch.empty(self.dq_b, dtype=torch.uint8, device=dev)
+        self.Wd = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        self.qw = lq.QWeight(N, K, self.codes, absmax_q=self.aq, dq_scale=self.s2, dq_mean=self.mu)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        lib = lq.lib
+        n = N * K
+
+        def chk(v, name):
+            if v != 0:
+                raise RuntimeError(f"{name} failed: {v}")
+        self.quantize = lambda: chk(lib.lq_quantize_nf4(P(self.W), 0, N, K, 64, P(self.codes), P(self.absmax), st),
+                                    "quantize")
+        self.profile = lambda: chk(lib.lq_profile_nf4(P(self.W), 0, N, K, 64, ctypes.c_double(0.01), P(self.stats),
+                                                      P(self.prof_ws), self.prof_b, st), "profile")
+        self.double_quant = lambda: chk(lib.lq_double_quant(P(self.absmax), n // 64, 256, P(self.aq), P(self.s2),
+                                                            P(self.mu), P(self.dq_ws), self.dq_b, st), "double_quant")
+        self.dequant = lambda: chk(lib.lq_dequant(self.qw.ref(), P(self.Wd), st), "dequant")
+
+
+def rotation_count(n_weights, min_bytes=1 << 30):
+    """Copies such that one pass over them moves at least `min_bytes` in the
+    smallest of the rotated codec arms (dequant: 2.5 B per weight)."""
+    return max(1, -(-min_bytes // (5 * n_weights // 2)))
+
+
+def codec_sets(torch, lq, L, W_dev, min_bytes=1 << 30):
+    """rotation_count(N K) CodecSets of one layer, quantized once."""
+    sets = [CodecSet(torch, lq, L, W_dev) for _ in range(rotation_count(L.N * L.K, min_bytes))]
+    for c in sets:
+        c.quantize()
+        c.double_quant()
+    torch.cuda.synchronize()
+    return sets
+
+
+def run_sessions(args):
+    """The headline step again in fresh processes (started before this
+    process touches the GPU); returns their ms per step."""
+    import subprocess
+    out = []
+    for _ in range(max(0, args.sessions - 1)):
+        cmd = [sys.executable, os.path.abspath(__file__), "--session-child", "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--settle-seconds", str(args.settle_seconds), "--sets", str(args.sets)]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        if r.returncode != 0:
+            raise RuntimeError(f"session child failed ({r.returncode}): {r.stderr[-2000:]}")
+        line = [ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1]
+        out.append(json.loads(line)["ms_per_step"])
+        log(f"session child: {out[-1]:.5f} ms/step")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the quantized-LoRA hot path here is a single-GPU "
               "kernel library, and sharding across GPUs is a design note, not a run.", flush=True)
         sys.exit(2)
+    child_ms = [] if args.session_child else run_sessions(args)
     import numpy as np
     import torch
     import quantized_lora_fine_lq_amd as lq
@@ -425,6 +562,7 @@ def main():
     L = syn.LAYERS["q_proj"]
     fl = layer_flops(L, L.M)
     step_flops = fl["fwd"] + fl["bwd"]
+    arm_s = args.arm_seconds
 
     if args.copy_probe:
         # plain copy of known size: 512 MiB read + 512 MiB written per launch
@@ -435,14 +573,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the timed step -------------------------------------------------
-    # The forward dequant-GEMM (the dominant kernel) is bracketed by its own
-    # events inside the timed steps, on the stream the library launches on:
-    # every `ev_stride`-th step (at least 5 launches), since each pair of
-    # event records adds a few microseconds to the step it sits in.
+    # ---- clock settling, warm-up, the timed step --------------------------
+    # Steps for a fixed wall time first: the shader clock rises over the
+    # first second or so of load, and a count-only warm-up can end before it
+    # has (the first window then runs slower than the later ones).
+    settle_steps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_seconds:
+        for i in range(50):
+            calls[(settle_steps + i) % len(calls)].step()
+        settle_steps += 50
+        torch.cuda.synchronize()
+    settle = {"seconds": round(time.perf_counter() - t0, 3), "steps": settle_steps}
     for i in range(args.warmup):
         calls[i % len(calls)].step()
     torch.cuda.synchronize()
+    # the forward dequant-GEMM inside the timed steps also gets event pairs
+    # (every ev_stride-th step: each pair adds a few microseconds to its step)
     ev_stride = kernel_event_stride(args.steps)
     kev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for i in range(0, args.steps, ev_stride)}
@@ -456,7 +602,10 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
     value = step_flops / (ms_step * 1e-3) / 1e12
-    log(f"step: {ms_step:.4f} ms  ({value:.1f} TFLOP/s), wall {wall:.3f} s")
+    log(f"step: {ms_step:.4f} ms  ({value:.1f} TFLOP/s), wall {wall:.3f} s, settle {settle}")
+    if args.session_child:
+        print(json.dumps({"ms_per_step": ms_step}), flush=True)
+        return
 
     # run-to-run spread: further windows of the same K steps, after the
     # headline window (which alone gives value and ms_per_step)
@@ -470,25 +619,44 @@ def main():
         a1.synchronize()
         windows.append(a0.elapsed_time(a1) / args.steps)
     spread = None
+    pick = lambda v, q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
     if windows:
         ws = sorted(windows)
-        pick = lambda q: ws[min(len(ws) - 1, int(round(q * (len(ws) - 1))))]
-        spread = {"windows": len(ws), "steps_each": args.steps, "ms_per_step_p10": round(pick(0.1), 5),
-                  "ms_per_step_p50": round(pick(0.5), 5), "ms_per_step_p90": round(pick(0.9), 5)}
+        spread = {"windows": len(ws), "steps_each": args.steps, "ms_per_step_p10": round(pick(ws, 0.1), 5),
+                  "ms_per_step_p50": round(pick(ws, 0.5), 5), "ms_per_step_p90": round(pick(ws, 0.9), 5)}
         log("spread", spread)
+    sess = sorted([ms_step] + child_ms)
+    sessions = {"count": len(sess), "ms_per_step": [round(x, 5) for x in [ms_step] + child_ms],
+                "median": round(pick(sess, 0.5), 5),
+                "spread_frac": round((sess[-1] - sess[0]) / pick(sess, 0.5), 4),
+                "how": "headline window of this process and of fresh child processes (same arguments)"}
 
     # ---- dominant kernel: forward dequant-GEMM on q_proj -------------------
-    fwd_ms = sum(a.elapsed_time(b) for a, b in kev.values()) / len(kev)
+    # Two arms of back-to-back launches over the rotated input sets: the
+    # first gives the roofline, the replicated second the noise floor.
+    f1 = time_arm(torch, [c.fwd_gemm for c in calls], arm_s)
+    f2 = time_arm(torch, [c.fwd_gemm for c in calls], arm_s)
+    fwd_ms = f1[0]
     fwd_tflops = fl["fwd_gemm"] / (fwd_ms * 1e-3) / 1e12
+    in_step_ms = sum(a.elapsed_time(b) for a, b in kev.values()) / len(kev)
     roofline = {"bound": "mfma", "kernel": "k_dq_gemm<ProdFwdNF4<true>> (q_proj, M=2048)",
                 "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(),
-                "avg_us": round(fwd_ms * 1e3, 2), "launches_timed": len(kev),
+                "avg_us": round(fwd_ms * 1e3, 2), "p10_us": round(f1[1] * 1e3, 2), "p90_us": round(f1[2] * 1e3, 2),
+                "launches_timed": f1[3],
+                "how": "HIP events around batches of back-to-back launches on the library's stream, "
+                       f"{len(calls)} input sets rotated, {ARM_WARMUP} warm-up launches, median batch",
+                "replicated_arm_us": round(f2[0] * 1e3, 2),
+                "noise_floor": round(abs(f1[0] - f2[0]) / (0.5 * (f1[0] + f2[0])), 4),
+                "in_step_avg_us": round(in_step_ms * 1e3, 2), "in_step_launches": len(kev),
                 "algorithmic_flop_per_launch": fl["fwd_gemm"]}
+    log("roofline", roofline)
 
     kernels = {}
     ceilings = None
+    only = set(x for x in args.only.split(",") if x)
+    want = lambda g: not only or g in only
     if not args.no_kernels:
         copy_gbs = copy_ceiling_gbs(torch)
         ceilings = {"copy_GB/s": round(copy_gbs, 1),
@@ -497,136 +665,196 @@ def main():
                     "sclk": sclk_under_load(torch, calls[0].step)}
         log("ceilings", ceilings)
 
-        def rec(name, ms, work, unit):
+        def rec(name, arm, work, unit, rotated=None):
+            ms, p10, p90, n = arm
+            k = {"us": round(ms * 1e3, 2), "p10_us": round(p10 * 1e3, 2), "p90_us": round(p90 * 1e3, 2),
+                 "launches": n}
             if unit == "GB/s":
                 ach = work / (ms * 1e-3) / 1e9
-                kernels[name] = {"us": round(ms * 1e3, 2), "GB/s": round(ach, 1),
-                                 "frac_hbm": round(ach / HBM_PEAK_GBS, 4),
-                                 "frac_copy": round(ach / copy_gbs, 4), "bytes": work}
-            else:
+                k.update({"GB/s": round(ach, 1), "frac_hbm": round(ach / HBM_PEAK_GBS, 4),
+                          "frac_copy": round(ach / copy_gbs, 4), "bytes": work})
+            elif unit == "TFLOP/s":
                 ach = work / (ms * 1e-3) / 1e12
-                kernels[name] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(ach, 1),
-                                 "frac_mfma": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "flop": work}
-            log(name, kernels[name])
+                k.update({"TFLOP/s": round(ach, 1), "frac_mfma": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "flop": work})
+            else:
+                k["bound"] = "latency (time only)"
+            if rotated is not None:
+                k["rotated_bytes"] = int(rotated)
+            kernels[name] = k
+            log(name, k)
 
-        cb = codec_bytes(L)
-        rec("q_proj.quantize_nf4", time_ms(torch, [c.quantize for c in calls], 40), cb["quantize"], "GB/s")
-        rec("q_proj.profile_nf4", time_ms(torch, [c.profile for c in calls], 40), cb["profile"], "GB/s")
-        rec("q_proj.double_quant", time_ms(torch, [c.double_quant for c in calls], 40), cb["double_quant"], "GB/s")
-        rec("q_proj.dequant", time_ms(torch, [c.dequant for c in calls], 40), cb["dequant"], "GB/s")
-        rec("q_proj.lora_down", time_ms(torch, [c.lora_down for c in calls], 40), fl["lora_down"], "TFLOP/s")
-        for c in calls:
-            c.lora_down()
-        rec("q_proj.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in calls], 50), fl["fwd_gemm"], "TFLOP/s")
-        rec("q_proj.backward", time_ms(torch, [c.backward for c in calls], 30), fl["bwd"], "TFLOP/s")
+        rec("q_proj.dequant_gemm_fwd", f1, fl["fwd_gemm"], "TFLOP/s")
+        rec("q_proj.dequant_gemm_fwd#replicate", f2, fl["fwd_gemm"], "TFLOP/s")
 
-        # LoftQ-style initialisation of the q_proj adapter (r = 16, l = 32, 8 power steps, 5 alternations)
-        r_lq, l_lq, q_lq, t_lq = L.r, 2 * L.r, 8, 5
-        d0 = devs[0]
-        om = torch.from_numpy(np.random.default_rng(1).standard_normal((L.K, l_lq)).astype(np.float32)).cuda()
-        Bq = torch.empty(L.N, r_lq, dtype=torch.float32, device="cuda")
-        Aq = torch.empty(r_lq, L.K, dtype=torch.float32, device="cuda")
-        sg = torch.empty(r_lq, dtype=torch.float32, device="cuda")
-        ob = torch.empty(t_lq, dtype=torch.float64, device="cuda")
-        lws_b = lq.lib.lq_loftq_workspace(L.N, L.K, r_lq, l_lq, 1)
-        lws = torch.empty(lws_b, dtype=torch.uint8, device="cuda")
-        P = lambda t: ctypes.c_void_p(t.data_ptr())
-        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if want("linear1k"):
+            # BASELINE's first workload: 1024 x 1024, 16 tokens -- latency rows
+            L1 = syn.LAYERS["linear1k"]
+            d1 = make_devs(torch, lq, syn, "linear1k", 1, with_grad=False)
+            c1 = Calls(torch, lq, d1[0])
+            c1.quantize(); c1.double_quant(); c1.lora_down()
+            rec("linear1k.quantize_nf4", time_arm(torch, [c1.quantize], arm_s), None, "us")
+            rec("linear1k.double_quant", time_arm(torch, [c1.double_quant], arm_s), None, "us")
+            rec("linear1k.dequant", time_arm(torch, [c1.dequant], arm_s), None, "us")
+            rec("linear1k.lora_down", time_arm(torch, [c1.lora_down], arm_s), None, "us")
+            rec("linear1k.dequant_gemm_fwd", time_arm(torch, [c1.fwd_gemm], arm_s), None, "us")
 
-        def loftq():
-            if lq.lib.lq_loftq_init(P(d0.W), L.N, L.K, 64, 1, r_lq, l_lq, t_lq, q_lq, P(om), P(d0.codes), P(d0.absmax),
-                                    P(d0.aq), P(d0.s2), P(d0.mu), P(Bq), P(Aq), P(sg), P(ob), P(lws), lws_b, st) != 0:
-                raise RuntimeError("lq_loftq_init failed")
-        rec("q_proj.loftq_init", time_ms(torch, [loftq], 3, warmup=1), loftq_bytes(L, r_lq, q_lq, t_lq), "GB/s")
-        kernels["q_proj.loftq_init"]["objectives"] = [round(x, 4) for x in ob.cpu().tolist()]
-        del lws
-        rec_loraquant(torch, lq, "q_proj", d0, rec, kernels)
+            def fwd1():
+                c1.lora_down()
+                c1.fwd_gemm()
+            rec("linear1k.qlora_forward", time_arm(torch, [fwd1], arm_s), None, "us")
+            del c1, d1
+
+        if want("q_proj"):
+            cb = codec_bytes(L)
+            cs = codec_sets(torch, lq, L, devs[0].W)
+            rot = lambda b: b * len(cs)
+            rec("q_proj.quantize_nf4", time_arm(torch, [c.quantize for c in cs], arm_s), cb["quantize"], "GB/s",
+                rot(cb["quantize"]))
+            rec("q_proj.profile_nf4", time_arm(torch, [c.profile for c in cs], arm_s), cb["profile"], "GB/s",
+                rot(cb["profile"]))
+            rec("q_proj.double_quant", time_arm(torch, [c.double_quant for c in cs], arm_s), cb["double_quant"], "GB/s",
+                rot(cb["double_quant"]))
+            rec("q_proj.dequant", time_arm(torch, [c.dequant for c in cs], arm_s), cb["dequant"], "GB/s",
+                rot(cb["dequant"]))
+            del cs
+            torch.cuda.empty_cache()
+            rec("q_proj.lora_down", time_arm(torch, [c.lora_down for c in calls], arm_s), fl["lora_down"], "TFLOP/s")
+            for c in calls:
+                c.lora_down()
+            rec("q_proj.backward", time_arm(torch, [c.backward for c in calls], arm_s), fl["bwd"], "TFLOP/s")
+
+            # LoftQ-style initialisation of the q_proj adapter (r = 16, l = 32, 8 power steps, 5 alternations)
+            r_lq, l_lq, q_lq, t_lq = L.r, 2 * L.r, 8, 5
+            d0 = devs[0]
+            om = torch.from_numpy(np.random.default_rng(1).standard_normal((L.K, l_lq)).astype(np.float32)).cuda()
+            Bq = torch.empty(L.N, r_lq, dtype=torch.float32, device="cuda")
+            Aq = torch.empty(r_lq, L.K, dtype=torch.float32, device="cuda")
+            sg = torch.empty(r_lq, dtype=torch.float32, device="cuda")
+            ob = torch.empty(t_lq, dtype=torch.float64, device="cuda")
+            lws_b = lq.lib.lq_loftq_workspace(L.N, L.K, r_lq, l_lq, 1)
+            lws = torch.empty(lws_b, dtype=torch.uint8, device="cuda")
+            P = lambda t: ctypes.c_void_p(t.data_ptr())
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+            def loftq():
+                if lq.lib.lq_loftq_init(P(d0.W), L.N, L.K, 64, 1, r_lq, l_lq, t_lq, q_lq, P(om), P(d0.codes),
+                                        P(d0.absmax), P(d0.aq), P(d0.s2), P(d0.mu), P(Bq), P(Aq), P(sg), P(ob),
+                                        P(lws), lws_b, st) != 0:
+                    raise RuntimeError("lq_loftq_init failed")
+            rec("q_proj.loftq_init", time_arm(torch, [loftq], arm_s, warmup=2), loftq_bytes(L, r_lq, q_lq, t_lq),
+                "GB/s")
+            kernels["q_proj.loftq_init"]["objectives"] = [round(x, 4) for x in ob.cpu().tolist()]
+            del lws
+            rec_loraquant(torch, lq, "q_proj", d0, rec, kernels, arm_s)
         del calls, devs
         torch.cuda.empty_cache()
 
-        for name in ("mlp_up", "mlp_down"):
-            log(f"generating {name} inputs")
-            Lm = syn.LAYERS[name]
-            dv = make_devs(torch, lq, syn, name, 2)
-            cs = [Calls(torch, lq, d) for d in dv]
-            for c in cs:
-                c.quantize(); c.double_quant(); c.lora_down()
-            flm = layer_flops(Lm, Lm.M)
-            rec(f"{name}.quantize_nf4", time_ms(torch, [c.quantize for c in cs], 20), codec_bytes(Lm)["quantize"], "GB/s")
-            for c in cs:
-                c.double_quant()
-            rec(f"{name}.dequant_gemm_fwd", time_ms(torch, [c.fwd_gemm for c in cs], 20), flm["fwd_gemm"], "TFLOP/s")
-            rec(f"{name}.backward", time_ms(torch, [c.backward for c in cs], 10), flm["bwd"], "TFLOP/s")
-            if name == "mlp_up":
-                rec_loraquant(torch, lq, name, dv[0], rec, kernels)
-            del cs, dv
+        if want("mlp"):
+            for name in ("mlp_up", "mlp_down"):
+                log(f"generating {name} inputs")
+                Lm = syn.LAYERS[name]
+                dv = make_devs(torch, lq, syn, name, 2)
+                cs = [Calls(torch, lq, d) for d in dv]
+                for c in cs:
+                    c.quantize(); c.double_quant(); c.lora_down()
+                flm = layer_flops(Lm, Lm.M)
+                qs = codec_sets(torch, lq, Lm, dv[0].W)
+                cbm = codec_bytes(Lm)
+                rec(f"{name}.quantize_nf4", time_arm(torch, [c.quantize for c in qs], arm_s), cbm["quantize"], "GB/s",
+                    cbm["quantize"] * len(qs))
+                rec(f"{name}.dequant", time_arm(torch, [c.dequant for c in qs], arm_s), cbm["dequant"], "GB/s",
+                    cbm["dequant"] * len(qs))
+                del qs
+                torch.cuda.empty_cache()
+                rec(f"{name}.dequant_gemm_fwd", time_arm(torch, [c.fwd_gemm for c in cs], arm_s), flm["fwd_gemm"],
+                    "TFLOP/s")
+                rec(f"{name}.backward", time_arm(torch, [c.backward for c in cs], arm_s), flm["bwd"], "TFLOP/s")
+                if name == "mlp_up":
+                    rec_loraquant(torch, lq, name, dv[0], rec, kernels, arm_s)
+                del cs, dv
+                torch.cuda.empty_cache()
+
+        if want("lowra"):
+            # ---- per-channel codebook layer (LowRA): learner, quantizer, GEMM ----
+            log("generating lowra inputs")
+            Ll = syn.LAYERS["lowra"]
+            lb = lowra_bytes(syn, Ll)
+            Wl = torch.from_numpy(syn.weight(Ll)).cuda()
+            bits_h = syn.lowra_row_bits(Ll)
+            bl = torch.from_numpy(bits_h).cuda()
+            P = lambda t: ctypes.c_void_p(t.data_ptr())
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            lv = torch.empty(Ll.N, 16, dtype=torch.float32, device="cuda")
+            th = torch.empty(Ll.N, 15, dtype=torch.float32, device="cuda")
+            its = torch.empty(Ll.N, dtype=torch.int32, device="cuda")
+
+            def lloyd():
+                if lq.lib.lq_lloyd_codebooks(P(Wl), 0, Ll.N, Ll.K, 64, P(bl), 100, P(lv), P(th), P(its), st) != 0:
+                    raise RuntimeError("lq_lloyd_codebooks failed")
+            rec("lowra.lloyd_codebooks", time_arm(torch, [lloyd], arm_s, warmup=2), lb["lloyd"], "GB/s")
+            kernels["lowra.lloyd_codebooks"]["iterations_mean"] = round(its.float().mean().item(), 2)
+            kernels["lowra.lloyd_codebooks"]["iterations_max"] = int(its.max().item())
+            offs = lq.row_offsets(bits_h.tolist(), Ll.K)
+            roff = torch.tensor(offs, dtype=torch.int64, device="cuda")
+            n_rot = max(1, -(-(1 << 30) // lb["quantize"]))
+            rot_sets = [(Wl.clone(), torch.empty(offs[-1], dtype=torch.uint8, device="cuda"),
+                         torch.empty(Ll.N * Ll.K // 64, dtype=torch.float32, device="cuda")) for _ in range(n_rot)]
+
+            def cb_quant(ws):
+                Wc, cc, am = ws
+                if lq.lib.lq_quantize_codebook(P(Wc), 0, Ll.N, Ll.K, 64, P(bl), P(roff), P(th), P(cc), P(am), st) != 0:
+                    raise RuntimeError("lq_quantize_codebook failed")
+            rec("lowra.quantize_codebook", time_arm(torch, [(lambda ws=ws: cb_quant(ws)) for ws in rot_sets], arm_s),
+                lb["quantize"], "GB/s", lb["quantize"] * n_rot)
+            del rot_sets
+            qwl = lq.QWeight.from_codebook(Wl, bl, th, lv)
+            Xl, Al, Bl = syn.activations(Ll), syn.lora_a(Ll), syn.lora_b(Ll)
+            bfd = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+            Xd, Ad, Bd = bfd(Xl.bits), bfd(Al.bits), bfd(Bl.bits)
+            tl = torch.empty(Ll.M, Ll.r, dtype=torch.float32, device="cuda")
+            lq.lora_down(Xd, Ad, tl)
+            Hl = torch.empty(Ll.M, Ll.N, dtype=torch.bfloat16, device="cuda")
+            flw = layer_flops(Ll, Ll.M)
+            rec("lowra.dequant_gemm_fwd",
+                time_arm(torch, [lambda: lq.dequant_gemm(qwl, Xd, tl, Bd, Ll.alpha, out=Hl)], arm_s),
+                flw["fwd_gemm"], "TFLOP/s")
+            del Wl, qwl, Xd, Hl
             torch.cuda.empty_cache()
 
-        # ---- per-channel codebook layer (LowRA): learner, quantizer, GEMM ----
-        log("generating lowra inputs")
-        Ll = syn.LAYERS["lowra"]
-        lb = lowra_bytes(syn, Ll)
-        Wl = torch.from_numpy(syn.weight(Ll)).cuda()
-        bits_h = syn.lowra_row_bits(Ll)
-        bl = torch.from_numpy(bits_h).cuda()
-        P = lambda t: ctypes.c_void_p(t.data_ptr())
-        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        lv = torch.empty(Ll.N, 16, dtype=torch.float32, device="cuda")
-        th = torch.empty(Ll.N, 15, dtype=torch.float32, device="cuda")
-        its = torch.empty(Ll.N, dtype=torch.int32, device="cuda")
-
-        def lloyd():
-            if lq.lib.lq_lloyd_codebooks(P(Wl), 0, Ll.N, Ll.K, 64, P(bl), 100, P(lv), P(th), P(its), st) != 0:
-                raise RuntimeError("lq_lloyd_codebooks failed")
-        rec("lowra.lloyd_codebooks", time_ms(torch, [lloyd], 5, warmup=1), lb["lloyd"], "GB/s")
-        kernels["lowra.lloyd_codebooks"]["iterations_mean"] = round(its.float().mean().item(), 2)
-        kernels["lowra.lloyd_codebooks"]["iterations_max"] = int(its.max().item())
-        offs = lq.row_offsets(bits_h.tolist(), Ll.K)
-        roff = torch.tensor(offs, dtype=torch.int64, device="cuda")
-        cc = torch.empty(offs[-1], dtype=torch.uint8, device="cuda")
-        am = torch.empty(Ll.N * Ll.K // 64, dtype=torch.float32, device="cuda")
-
-        def cb_quant():
-            if lq.lib.lq_quantize_codebook(P(Wl), 0, Ll.N, Ll.K, 64, P(bl), P(roff), P(th), P(cc), P(am), st) != 0:
-                raise RuntimeError("lq_quantize_codebook failed")
-        rec("lowra.quantize_codebook", time_ms(torch, [cb_quant], 20), lb["quantize"], "GB/s")
-        qwl = lq.QWeight.from_codebook(Wl, bl, th, lv)
-        Xl, Al, Bl = syn.activations(Ll), syn.lora_a(Ll), syn.lora_b(Ll)
-        bfd = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
-        Xd, Ad, Bd = bfd(Xl.bits), bfd(Al.bits), bfd(Bl.bits)
-        tl = torch.empty(Ll.M, Ll.r, dtype=torch.float32, device="cuda")
-        lq.lora_down(Xd, Ad, tl)
-        Hl = torch.empty(Ll.M, Ll.N, dtype=torch.bfloat16, device="cuda")
-        flw = layer_flops(Ll, Ll.M)
-        rec("lowra.dequant_gemm_fwd", time_ms(torch, [lambda: lq.dequant_gemm(qwl, Xd, tl, Bd, Ll.alpha, out=Hl)], 20),
-            flw["fwd_gemm"], "TFLOP/s")
-        del Wl, qwl, Xd, Hl, cc
-        torch.cuda.empty_cache()
-
-        log("generating decode inputs")
-        Ld = syn.LAYERS["decode"]
-        dv = make_devs(torch, lq, syn, "decode", 1, M=16, with_grad=False)
-        c0 = Calls(torch, lq, dv[0])
-        rec("decode.quantize_nf4", time_ms(torch, [c0.quantize], 10), codec_bytes(Ld)["quantize"], "GB/s")
-        rec("decode.profile_nf4", time_ms(torch, [c0.profile], 10), codec_bytes(Ld)["profile"], "GB/s")
-        rec("decode.double_quant", time_ms(torch, [c0.double_quant], 10), codec_bytes(Ld)["double_quant"], "GB/s")
-        rec("decode.dequant", time_ms(torch, [c0.dequant], 10), codec_bytes(Ld)["dequant"], "GB/s")
-        # 9 copies of the 121 MB quantized weight rotate through the GEMV
-        copies = [dv[0].qw]
-        keep = []
-        for k in range(8):
-            cc = dv[0].codes.clone(); aq = dv[0].aq.clone(); s2 = dv[0].s2.clone(); mu = dv[0].mu.clone()
-            keep.append((cc, aq, s2, mu))
-            copies.append(lq.QWeight(Ld.N, Ld.K, cc, absmax_q=aq, dq_scale=s2, dq_mean=mu))
-        del dv[0].W
-        torch.cuda.empty_cache()
-        for M in (1, 4, 16):
-            X = dv[0].X[:M].contiguous()
-            t = torch.zeros(M, Ld.r, dtype=torch.float32, device="cuda")
-            lq.lora_down(X, dv[0].A, t)
-            H = torch.empty(M, Ld.N, dtype=torch.bfloat16, device="cuda")
-            fns = [(lambda q=q: lq.dequant_gemm(q, X, t, dv[0].B, Ld.alpha, out=H)) for q in copies]
-            rec(f"decode.gemv_M{M}", time_ms(torch, fns, 45), codec_bytes(Ld, M)["gemv"], "GB/s")
+        if want("decode"):
+            log("generating decode inputs")
+            Ld = syn.LAYERS["decode"]
+            dv = make_devs(torch, lq, syn, "decode", 1, M=16, with_grad=False)
+            c0 = Calls(torch, lq, dv[0])
+            cbd = codec_bytes(Ld)
+            ds = codec_sets(torch, lq, Ld, dv[0].W)
+            rec("decode.quantize_nf4", time_arm(torch, [c.quantize for c in ds], arm_s), cbd["quantize"], "GB/s",
+                cbd["quantize"] * len(ds))
+            rec("decode.profile_nf4", time_arm(torch, [c.profile for c in ds], arm_s), cbd["profile"], "GB/s",
+                cbd["profile"] * len(ds))
+            rec("decode.double_quant", time_arm(torch, [c.double_quant for c in ds], arm_s), cbd["double_quant"],
+                "GB/s", cbd["double_quant"] * len(ds))
+            rec("decode.dequant", time_arm(torch, [c.dequant for c in ds], arm_s), cbd["dequant"], "GB/s",
+                cbd["dequant"] * len(ds))
+            del ds
+            c0.quantize(); c0.double_quant()
+            # 9 copies of the 121 MB quantized weight rotate through the GEMV
+            copies = [dv[0].qw]
+            keep = []
+            for k in range(8):
+                cc = dv[0].codes.clone(); aq = dv[0].aq.clone(); s2 = dv[0].s2.clone(); mu = dv[0].mu.clone()
+                keep.append((cc, aq, s2, mu))
+                copies.append(lq.QWeight(Ld.N, Ld.K, cc, absmax_q=aq, dq_scale=s2, dq_mean=mu))
+            del dv[0].W
+            torch.cuda.empty_cache()
+            for M in (1, 4, 16):
+                X = dv[0].X[:M].contiguous()
+                t = torch.zeros(M, Ld.r, dtype=torch.float32, device="cuda")
+                lq.lora_down(X, dv[0].A, t)
+                H = torch.empty(M, Ld.N, dtype=torch.bfloat16, device="cuda")
+                fns = [(lambda q=q: lq.dequant_gemm(q, X, t, dv[0].B, Ld.alpha, out=H)) for q in copies]
+                gb = codec_bytes(Ld, M)["gemv"]
+                rec(f"decode.gemv_M{M}", time_arm(torch, fns, arm_s), gb, "GB/s", gb * len(copies))
 
     out = {
         "metric": METRIC,
@@ -646,13 +874,15 @@ def main():
                    "global_batch": L.M, "tokens": L.M, "N": L.N, "K": L.K, "r": L.r, "alpha": L.alpha,
                    "input_sets_rotated": args.sets},
         "roofline": roofline,
+        "settle": settle,
         "step_spread": spread,
+        "sessions": sessions,
         "cpu_baseline": None,
         "ceilings": ceilings,
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one q_proj step")
+        log("timing the CPU oracle on q_proj steps")
         out["cpu_baseline"] = cpu_baseline(syn)
     print(json.dumps(out), flush=True)
 

@@ -24,9 +24,28 @@
  *   - Every call returns an lq_status. Arguments are validated before anything
  *     is launched; on an error nothing is launched and outputs are untouched.
  *     No C++ exception crosses this boundary.
- *   - Preconditions not checked: inputs are finite; codebook thresholds are
- *     strictly increasing per row; device pointers are valid and large enough
- *     for the stated sizes. Violations give undefined results.
+ *   - Alignment (checked: a misaligned pointer returns LQ_ERR_ARG before any
+ *     launch). Bulk tensors are moved with 16-byte vector accesses and must be
+ *     16-byte aligned: codes (NF4 and codebook) and absmax_q of a weight
+ *     descriptor, X, G, A, B, a bfloat16 H, grad_X, the lq_dequant output,
+ *     every workspace, and the float32 matrices of the low-rank entry points
+ *     (W, out, R, omega, B, A, Ap, Bpt). W of lq_quantize_nf4 and
+ *     lq_profile_nf4 needs 16 bytes for float32 and 8 for bfloat16 / float16;
+ *     the codes output of lq_quantize_nf4 needs 8. Arrays accessed element by
+ *     element need only their natural alignment: absmax, dq_scale, dq_mean,
+ *     t, u, dA, dB, a float32 H, stats, levels, thresholds, sigma,
+ *     objectives (4 or 8 bytes), row_offset (8). lq_quantize_codebook and
+ *     lq_lloyd_codebooks read W element by element where it is not 16-byte
+ *     aligned, so any element-aligned W is accepted there. Rows stay aligned
+ *     because K % 64 == 0 (K % 8 == 0 for lq_lora_down).
+ *   - Preconditions not checked in the release build: inputs are finite;
+ *     codebook thresholds are strictly increasing per row; row_offset holds
+ *     the prefix sums of K*b/8; device pointers are valid and large enough for
+ *     the stated sizes. Violations give undefined results. The LQ_DEBUG build
+ *     (liblq_debug.so, same entry points) checks the codebook tables on the
+ *     host before launching and records non-finite weights and non-increasing
+ *     thresholds seen by the quantizers in a device flag word
+ *     (lq_debug_flags below).
  */
 #ifndef LQ_H
 #define LQ_H
@@ -41,7 +60,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 enum lq_status {
   LQ_OK = 0,
-  LQ_ERR_ARG = -1,          /* null pointer, bad enum value */
+  LQ_ERR_ARG = -1,          /* null or misaligned pointer, bad enum value */
   LQ_ERR_SHAPE = -2,        /* K % 64 != 0, r outside [1, 128], sizes <= 0 */
   LQ_ERR_UNSUPPORTED = -3,  /* blocksize != 64, dq blocksize != 256, dtype */
   LQ_ERR_WORKSPACE = -4,    /* workspace missing or too small */
@@ -486,6 +505,46 @@ int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const ui
                          const int64_t* offsets_b, const float* levels_a, const float* levels_b, int64_t N,
                          int64_t K, int32_t r, uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes,
                          void* stream);
+
+/* ---- checks and the LQ_DEBUG build ---------------------------------------- */
+
+/*
+ * Host check of a codebook weight's layout and tables ([LowRA] section 3:
+ * per-output-channel precision and thresholds), on HOST arrays:
+ *   row_bits   [N] uint8, each in {1, 2, 3, 4}
+ *   row_offset [N + 1] int64, row_offset[0] = 0 and
+ *              row_offset[i+1] - row_offset[i] = K * row_bits[i] / 8
+ *   thresholds [N, 15] float32 or NULL: the first 2^b - 1 of row i finite and
+ *              strictly increasing
+ * Returns LQ_OK, LQ_ERR_SHAPE (N <= 0, K <= 0, K % 64 != 0) or LQ_ERR_ARG
+ * (a null array or the first violation found). Pure host function.
+ */
+int lq_check_codebook_tables(int64_t N, int64_t K, const uint8_t* row_bits, const int64_t* row_offset,
+                             const float* thresholds);
+
+/* 1 in the LQ_DEBUG build (liblq_debug.so), 0 in the release build. */
+int lq_debug_build(void);
+
+/* Bits of the debug build's device flag word. */
+#define LQ_DBG_NONFINITE 1u   /* a quantizer read a NaN or infinite weight */
+#define LQ_DBG_THRESHOLDS 2u  /* a codebook row's thresholds are not strictly increasing */
+#define LQ_DBG_ROW_BITS 4u    /* a codebook row width outside 1..4 (clamped into it) */
+
+/*
+ * Debug build only: the flag word of the current device (LQ_DBG_* bits set by
+ * the quantizers since it was last cleared), read after synchronising the
+ * device; cleared to 0 afterwards if `clear` is non-zero. The debug build
+ * also checks, before launching, the row layout of codebook weights passed to
+ * lq_quantize_codebook, lq_dequant, lq_qlora_forward, lq_dequant_gemm,
+ * lq_dequant_gemm_t and lq_qlora_backward (it copies row_bits and row_offset
+ * to the host on the caller's stream and synchronises it; LQ_ERR_ARG on a
+ * violation), and asserts its launch-shape assumptions on the host
+ * (LQ_ERR_LAUNCH if one fails, with a message on stderr).
+ *   flags  host uint32, written
+ * Errors: LQ_ERR_ARG (flags NULL), LQ_ERR_UNSUPPORTED (release build),
+ * LQ_ERR_LAUNCH (runtime error).
+ */
+int lq_debug_flags(uint32_t* flags, int clear);
 
 #ifdef __cplusplus
 }

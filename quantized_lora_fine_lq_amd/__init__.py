@@ -21,6 +21,8 @@ from typing import Optional, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "liblq.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "lib", "liblq_debug.so")
+LQ_DBG_NONFINITE, LQ_DBG_THRESHOLDS, LQ_DBG_ROW_BITS = 1, 2, 4
 
 LQ_OK, LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 LQ_F32, LQ_BF16, LQ_F16 = 0, 1, 2
@@ -93,6 +95,9 @@ SIGNATURES = {
     "lq_dequant_gemm_t_workspace": (c_sz, [QW_P, c_i64, c_i32]),
     "lq_dequant_gemm_t": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp,
                                          c_vp, c_sz, c_vp]),
+    "lq_check_codebook_tables": (ctypes.c_int, [c_i64, c_i64, c_vp, c_vp, c_vp]),
+    "lq_debug_build": (ctypes.c_int, []),
+    "lq_debug_flags": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]),
 }
 
 
@@ -102,10 +107,10 @@ class LqError(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python quantized_lora_fine_lq_amd/build.py`")
-    handle = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python quantized_lora_fine_lq_amd/build.py`")
+    handle = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(handle, name)
         fn.restype = res
@@ -114,6 +119,11 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
+
+
+def load_debug_library() -> ctypes.CDLL:
+    """The LQ_DEBUG build (same entry points and signatures as ``lib``)."""
+    return _load(DEBUG_LIB_PATH)
 
 
 def status_string(status: int) -> str:

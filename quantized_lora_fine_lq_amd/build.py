@@ -1,4 +1,5 @@
-"""Build liblq.so (the HIP library behind include/lq.h) for gfx950, in-tree.
+"""Build liblq.so (the HIP library behind include/lq.h) and its LQ_DEBUG
+variant liblq_debug.so for gfx950, in-tree.
 
     python quantized_lora_fine_lq_amd/build.py
 
@@ -17,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "liblq.so")
+LIB_DEBUG = os.path.join(LIB_DIR, "liblq_debug.so")
 SOURCES = ["lq_tables.cpp", "lq_api.cpp", "lq_codec.hip", "lq_gemm.hip", "lq_lloyd.hip", "lq_lowrank.hip"]
 ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 
@@ -28,37 +30,59 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    objs = []
-    obj_dir = os.path.join(HERE, "_build")
-    os.makedirs(obj_dir, exist_ok=True)
-    common = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function"]
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(obj_dir, src + ".o")
-        if src.endswith(".hip"):
-            cmd = [hipcc(), f"--offload-arch={ARCH}", "-x", "hip", *common,
-                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                   "-c", path, "-o", obj]
-        else:
-            cmd = [hipcc(), *common, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        errs = "\n".join(l for l in res.stderr.splitlines()
-                         if "packed-fp32-ops" not in l)
-        if res.returncode != 0:
-            raise RuntimeError(f"compile failed: {src}\n{errs}")
-        if verbose and errs.strip():
-            print(errs, file=sys.stderr)
-        objs.append(obj)
-    tmp = LIB + ".tmp"
+def _compile(src: str, obj: str, defines: list, verbose: bool) -> str:
+    path = os.path.join(CSRC, src)
+    common = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function", *defines]
+    if src.endswith(".hip"):
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-x", "hip", *common,
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-c", path, "-o", obj]
+    else:
+        cmd = [hipcc(), *common, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{errs}")
+    if verbose and errs.strip():
+        print(errs, file=sys.stderr)
+    return obj
+
+
+def _link(objs: list, lib: str) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed\n" + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile the release library (liblq.so) and, unless debug=False, the
+    LQ_DEBUG variant (liblq_debug.so: device flag word for precondition
+    violations, host checks of codebook layouts, launch-shape asserts)."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(LIB_DIR, exist_ok=True)
+    variants = [("release", [], LIB)]
+    if debug:
+        variants.append(("debug", ["-DLQ_DEBUG=1"], LIB_DEBUG))
+    jobs = []
+    for name, defs, _ in variants:
+        obj_dir = os.path.join(HERE, "_build", name)
+        os.makedirs(obj_dir, exist_ok=True)
+        for src in SOURCES:
+            jobs.append((name, src, os.path.join(obj_dir, src + ".o"), defs))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [(name, ex.submit(_compile, src, obj, defs, verbose)) for name, src, obj, defs in jobs]
+        objs = {}
+        for name, f in futs:
+            objs.setdefault(name, []).append(f.result())
+    for name, _, lib in variants:
+        _link(objs[name], lib)
     return LIB
 
 

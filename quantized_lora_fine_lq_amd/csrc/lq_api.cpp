@@ -1,8 +1,10 @@
 // The C ABI of include/lq.h: argument validation, workspace carving and
 // kernel dispatch. No device memory is allocated here; every launch goes on
 // the caller's stream.
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "lq_internal.h"
 
@@ -17,6 +19,14 @@ bool valid_dtype(int32_t d) { return d == LQ_F32 || d == LQ_BF16 || d == LQ_F16;
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LQ_OK : LQ_ERR_LAUNCH; }
 
+// Alignment of a device pointer (a null pointer passes; nullness is checked
+// separately). Bulk tensors are read and written with 16-byte vector
+// accesses; per-element arrays need their natural alignment.
+constexpr uintptr_t kVec = 16;
+bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+// W of the NF4 quantizer and the profiling pass: four elements per access
+uintptr_t w_align(int32_t dtype) { return dtype == LQ_F32 ? 16 : 8; }
+
 // Validate a weight descriptor and turn it into the kernels' view.
 int check_qweight(const lq_qweight* w, QWeight* out) {
   if (!w) return LQ_ERR_ARG;
@@ -29,6 +39,9 @@ int check_qweight(const lq_qweight* w, QWeight* out) {
     if (w->dq_blocksize != 256) return LQ_ERR_UNSUPPORTED;
   }
   if (w->format == LQ_FMT_CODEBOOK && (!w->row_bits || !w->row_offset || !w->levels)) return LQ_ERR_ARG;
+  if (!al(w->codes, kVec) || !al(w->absmax, 4) || !al(w->absmax_q, kVec) || !al(w->dq_scale, 4) ||
+      !al(w->dq_mean, 4) || !al(w->row_offset, 8) || !al(w->levels, 4))
+    return LQ_ERR_ARG;
   out->format = w->format;
   out->N = w->N;
   out->K = w->K;
@@ -52,16 +65,60 @@ bool use_gemv(const QWeight& w, int64_t M) {
   return true;
 }
 
+// Carves a caller workspace into aligned pieces; ok() is false if the pieces
+// ran past its size (the entry points size the workspace first, so this is a
+// bounds assert on that arithmetic).
 struct Carver {
   char* base;
+  size_t cap;
   size_t used = 0;
-  explicit Carver(void* p) : base((char*)p) {}
+  Carver(void* p, size_t bytes) : base((char*)p), cap(bytes) {}
   template <class T> T* take(size_t count) {
     T* p = reinterpret_cast<T*>(base + used);
     used += align_up(count * sizeof(T));
     return p;
   }
+  bool ok() const { return used <= cap; }
 };
+
+// Row layout of a codebook weight (host arrays): widths in 1..4, offsets the
+// prefix sums of K*b/8; thresholds (optional) finite and strictly increasing.
+int check_codebook_host(int64_t N, int64_t K, const uint8_t* bits, const int64_t* off, const float* T) {
+  if (off[0] != 0) return LQ_ERR_ARG;
+  for (int64_t i = 0; i < N; ++i) {
+    const int b = bits[i];
+    if (b < 1 || b > 4) return LQ_ERR_ARG;
+    if (off[i + 1] - off[i] != K * b / 8) return LQ_ERR_ARG;
+    if (T) {
+      const float* t = T + i * 15;
+      for (int k = 0; k < (1 << b) - 1; ++k) {
+        if (!std::isfinite(t[k])) return LQ_ERR_ARG;
+        if (k > 0 && !(t[k] > t[k - 1])) return LQ_ERR_ARG;
+      }
+    }
+  }
+  return LQ_OK;
+}
+
+// Debug build: copy a codebook weight's row_bits and row_offset to the host
+// (in order on the caller's stream) and check the layout before launching.
+int debug_check_rows(int64_t N, int64_t K, const uint8_t* bits_d, const int64_t* off_d, hipStream_t s) {
+#ifdef LQ_DEBUG
+  std::vector<uint8_t> bits((size_t)N);
+  std::vector<int64_t> off((size_t)N + 1);
+  if (hipMemcpyAsync(bits.data(), bits_d, (size_t)N, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(off.data(), off_d, ((size_t)N + 1) * sizeof(int64_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return LQ_ERR_LAUNCH;
+  return check_codebook_host(N, K, bits.data(), off.data(), nullptr);
+#else
+  (void)N; (void)K; (void)bits_d; (void)off_d; (void)s;
+  return LQ_OK;
+#endif
+}
+int debug_check_weight(const QWeight& q, hipStream_t s) {
+  return q.format == LQ_FMT_CODEBOOK ? debug_check_rows(q.N, q.K, q.row_bits, q.row_offset, s) : LQ_OK;
+}
 
 size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
   return align_up((size_t)M * r * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, true));
@@ -83,7 +140,7 @@ extern "C" {
 const char* lq_status_string(int status) {
   switch (status) {
     case LQ_OK: return "ok";
-    case LQ_ERR_ARG: return "invalid argument (null pointer or bad enum value)";
+    case LQ_ERR_ARG: return "invalid argument (null pointer, misaligned pointer or bad enum value)";
     case LQ_ERR_SHAPE: return "invalid shape (sizes must be positive, K % 64 == 0, r in [1, 128])";
     case LQ_ERR_UNSUPPORTED: return "unsupported option (blocksize, double-quant blocksize or dtype)";
     case LQ_ERR_WORKSPACE: return "workspace missing or too small";
@@ -118,6 +175,7 @@ int lq_sizes(int64_t N, int64_t K, int32_t bits, lq_sizes_t* out) {
 int lq_quantize_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,
                     uint8_t* codes, float* absmax, void* stream) {
   if (!W || !codes || !absmax || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (!al(W, w_align(dtype)) || !al(codes, 8) || !al(absmax, 4)) return LQ_ERR_ARG;
   if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
   if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
   return launch_status(launch_quantize_nf4(W, dtype, N * K / 64, codes, absmax, (hipStream_t)stream));
@@ -131,6 +189,7 @@ size_t lq_profile_workspace(int64_t N, int64_t K, int32_t blocksize) {
 int lq_profile_nf4(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize, double tau,
                    double* stats, void* workspace, size_t ws_bytes, void* stream) {
   if (!W || !stats || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (!al(W, w_align(dtype)) || !al(stats, 8) || !al(workspace, kVec)) return LQ_ERR_ARG;
   if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
   if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < lq_profile_workspace(N, K, blocksize)) return LQ_ERR_WORKSPACE;
@@ -147,6 +206,7 @@ int lq_double_quant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
                     uint8_t* absmax_q, float* dq_scale, float* dq_mean, void* workspace,
                     size_t ws_bytes, void* stream) {
   if (!absmax || !absmax_q || !dq_scale || !dq_mean) return LQ_ERR_ARG;
+  if (!al(absmax, 4) || !al(dq_scale, 4) || !al(dq_mean, 4) || !al(workspace, kVec)) return LQ_ERR_ARG;
   if (n_blocks <= 0) return LQ_ERR_SHAPE;
   if (dq_blocksize != 256) return LQ_ERR_UNSUPPORTED;
   if (!workspace || ws_bytes < lq_double_quant_workspace(n_blocks, dq_blocksize)) return LQ_ERR_WORKSPACE;
@@ -158,7 +218,9 @@ int lq_dequant(const lq_qweight* w, uint16_t* out, void* stream) {
   QWeight q;
   const int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
-  if (!out) return LQ_ERR_ARG;
+  if (!out || !al(out, kVec)) return LQ_ERR_ARG;
+  const int dc = debug_check_weight(q, (hipStream_t)stream);
+  if (dc != LQ_OK) return dc;
   return launch_status(launch_dequant(q, out, (hipStream_t)stream));
 }
 
@@ -175,14 +237,19 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
   if (!X || !A || !B || !H) return LQ_ERR_ARG;
+  if (!al(X, kVec) || !al(A, kVec) || !al(B, kVec) || !al(H, h_dtype == LQ_F32 ? 4 : kVec) || !al(t_save, 4) ||
+      !al(workspace, kVec))
+    return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
   if (h_dtype != LQ_BF16 && h_dtype != LQ_F32) return LQ_ERR_UNSUPPORTED;
   const size_t need = forward_ws(q, M, r);
   if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  Carver cv(workspace);
+  Carver cv(workspace, ws_bytes);
   float* t_ws = cv.take<float>((size_t)M * r);
   uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
+  if (!cv.ok()) return LQ_ERR_WORKSPACE;
+  if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
   hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, nullptr, s);
@@ -197,6 +264,7 @@ size_t lq_lora_down_workspace(int64_t, int64_t, int32_t) { return 0; }
 int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
                  void* workspace, size_t ws_bytes, void* stream) {
   if (!X || !A || !t) return LQ_ERR_ARG;
+  if (!al(X, kVec) || !al(A, kVec) || !al(t, 4)) return LQ_ERR_ARG;
   if (M <= 0 || K <= 0 || K % 8 != 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
   (void)workspace;
   (void)ws_bytes;
@@ -217,10 +285,14 @@ int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const flo
   const int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
   if (!X || !t || !B || !H) return LQ_ERR_ARG;
+  if (!al(X, kVec) || !al(t, 4) || !al(B, kVec) || !al(H, h_dtype == LQ_F32 ? 4 : kVec) || !al(workspace, kVec))
+    return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
   if (h_dtype != LQ_BF16 && h_dtype != LQ_F32) return LQ_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const float scale = alpha / (float)r;
+  const int dc = debug_check_weight(q, s);
+  if (dc != LQ_OK) return dc;
   if (use_gemv(q, M)) return launch_status(launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s));
   const size_t need = gemm_ws_bytes(q, M, r, true);
   if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
@@ -240,9 +312,12 @@ int lq_dequant_gemm_t(const lq_qweight* w, const uint16_t* G, int64_t M, const f
   const int st = check_qweight(w, &q);
   if (st != LQ_OK) return st;
   if (!G || !u || !A || !grad_X) return LQ_ERR_ARG;
+  if (!al(G, kVec) || !al(u, 4) || !al(A, kVec) || !al(grad_X, kVec) || !al(workspace, kVec)) return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
   const size_t need = gemm_ws_bytes(q, M, r, false);
   if (need && (!workspace || ws_bytes < need)) return LQ_ERR_WORKSPACE;
+  const int dc = debug_check_weight(q, (hipStream_t)stream);
+  if (dc != LQ_OK) return dc;
   return launch_status(launch_gemm_bwd(q, G, M, u, A, r, alpha / (float)r, grad_X, (uint16_t*)workspace,
                                        (hipStream_t)stream));
 }
@@ -262,11 +337,14 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   if (st != LQ_OK) return st;
   if (!G || !A || !B) return LQ_ERR_ARG;
   if ((dA || !t_saved) && !X) return LQ_ERR_ARG;
+  if (!al(X, kVec) || !al(G, kVec) || !al(A, kVec) || !al(B, kVec) || !al(t_saved, 4) || !al(grad_X, kVec) ||
+      !al(dA, 4) || !al(dB, 4) || !al(workspace, kVec))
+    return LQ_ERR_ARG;
   if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
   const size_t need = backward_ws(q, M, r);
   if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  Carver cv(workspace);
+  Carver cv(workspace, ws_bytes);
   float* u = cv.take<float>((size_t)M * r);
   float* t_ws = cv.take<float>((size_t)M * r);
   uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
@@ -275,6 +353,8 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
   float* part_b = cv.take<float>(col_skinny_ws_floats(M, q.N, r));
   float* part_a = cv.take<float>(col_skinny_ws_floats(M, q.K, r));
   uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
+  if (!cv.ok()) return LQ_ERR_WORKSPACE;
+  if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
   const float scale = alpha / (float)r;
   hipError_t e = hipSuccess;
   const float* t = t_saved;
@@ -305,8 +385,13 @@ int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int
                          const float* thresholds, uint8_t* codes, float* absmax, void* stream) {
   if (!W || !row_bits || !row_offset || !thresholds || !codes || !absmax || !valid_dtype(dtype))
     return LQ_ERR_ARG;
+  if (!al(W, dtype == LQ_F32 ? 4 : 2) || !al(row_offset, 8) || !al(thresholds, 4) || !al(codes, 4) ||
+      !al(absmax, 4))
+    return LQ_ERR_ARG;
   if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
   if (blocksize != 64) return LQ_ERR_UNSUPPORTED;
+  const int dc = debug_check_rows(N, K, row_bits, row_offset, (hipStream_t)stream);
+  if (dc != LQ_OK) return dc;
   return launch_status(launch_quantize_codebook(W, dtype, N, K, row_bits, row_offset, thresholds,
                                                 codes, absmax, (hipStream_t)stream));
 }
@@ -315,6 +400,8 @@ int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32
                        const uint8_t* row_bits, int32_t max_iters, float* levels,
                        float* thresholds, int32_t* iterations, void* stream) {
   if (!W || !row_bits || !levels || !thresholds || !valid_dtype(dtype)) return LQ_ERR_ARG;
+  if (!al(W, dtype == LQ_F32 ? 4 : 2) || !al(levels, 4) || !al(thresholds, 4) || !al(iterations, 4))
+    return LQ_ERR_ARG;
   if (max_iters < 1 || max_iters > LQ_LLOYD_MAX_ITERS_LIMIT) return LQ_ERR_ARG;
   if (N <= 0 || K <= 0 || K % 64 != 0 || N > INT32_MAX) return LQ_ERR_SHAPE;
   if (blocksize != 64 || K > LQ_LLOYD_MAX_K) return LQ_ERR_UNSUPPORTED;
@@ -325,12 +412,14 @@ int lq_lloyd_codebooks(const void* W, int32_t dtype, int64_t N, int64_t K, int32
 int lq_lowrank_sub(const float* W, int64_t N, int64_t K, const float* B, const float* A, int32_t r,
                    float* out, void* stream) {
   if (!W || !out || (r > 0 && (!B || !A))) return LQ_ERR_ARG;
+  if (!al(W, kVec) || !al(out, kVec) || !al(A, kVec) || !al(B, 4)) return LQ_ERR_ARG;
   if (N <= 0 || K <= 0 || K % 4 != 0 || r < 0 || r > 128) return LQ_ERR_SHAPE;
   return launch_status(launch_lowrank_sub(W, N, K, B, A, r, out, (hipStream_t)stream));
 }
 
 int lq_residual(const float* W, const uint16_t* Wd, int64_t n, float* R, void* stream) {
   if (!W || !Wd || !R) return LQ_ERR_ARG;
+  if (!al(W, kVec) || !al(Wd, 8) || !al(R, kVec)) return LQ_ERR_ARG;
   if (n <= 0 || n % 4 != 0) return LQ_ERR_SHAPE;
   return launch_status(launch_residual(W, Wd, n, R, (hipStream_t)stream));
 }
@@ -351,6 +440,8 @@ int lq_svd_lowrank(const float* R, int64_t N, int64_t K, int32_t r, int32_t l, i
                    const float* omega, float* B, float* A, float* sigma, void* workspace, size_t ws_bytes,
                    void* stream) {
   if (!R || !omega || !B || !A || !sigma) return LQ_ERR_ARG;
+  if (!al(R, kVec) || !al(omega, kVec) || !al(B, kVec) || !al(A, kVec) || !al(sigma, 4) || !al(workspace, kVec))
+    return LQ_ERR_ARG;
   const int st = check_svd_shape(N, K, r, l, power_iters);
   if (st != LQ_OK) return st;
   if (!workspace || ws_bytes < svd_ws_bytes(N, K, l, r)) return LQ_ERR_WORKSPACE;
@@ -370,6 +461,10 @@ int lq_loftq_init(const float* W, int64_t N, int64_t K, int32_t blocksize, int32
   const bool dq = double_quant != 0;
   if (!W || !omega || !codes || !absmax || !B || !A || !sigma) return LQ_ERR_ARG;
   if (dq && (!absmax_q || !dq_scale || !dq_mean)) return LQ_ERR_ARG;
+  if (!al(W, kVec) || !al(omega, kVec) || !al(codes, kVec) || !al(absmax, 4) || !al(absmax_q, kVec) ||
+      !al(dq_scale, 4) || !al(dq_mean, 4) || !al(B, kVec) || !al(A, kVec) || !al(sigma, 4) || !al(objectives, 8) ||
+      !al(workspace, kVec))
+    return LQ_ERR_ARG;
   if (steps < 1 || steps > 100) return LQ_ERR_ARG;
   if (K % 64 != 0) return LQ_ERR_SHAPE;
   const int st = check_svd_shape(N, K, r, l, power_iters);
@@ -400,6 +495,11 @@ int lq_loraquant(const float* B, const float* A, int64_t N, int64_t K, int32_t r
       !levels_a || !thresholds_a || !levels_b || !thresholds_b || !sigma || !h_out)
     return LQ_ERR_ARG;
   if (bits_hi < 1 || bits_hi > 4 || bits_lo < 1 || bits_lo > 4 || h > r) return LQ_ERR_ARG;
+  if (!al(B, kVec) || !al(A, kVec) || !al(codes_a, kVec) || !al(codes_b, kVec) || !al(absmax_a, 4) ||
+      !al(absmax_b, 4) || !al(offsets_a, 8) || !al(offsets_b, 8) || !al(levels_a, 4) || !al(levels_b, 4) ||
+      !al(thresholds_a, 4) || !al(thresholds_b, 4) || !al(sigma, 4) || !al(h_out, 4) || !al(Ap, kVec) ||
+      !al(Bpt, kVec) || !al(workspace, kVec))
+    return LQ_ERR_ARG;
   const int st = check_loraquant_shape(N, K, r);
   if (st != LQ_OK) return st;
   if (!workspace || ws_bytes < loraquant_ws_bytes(N, K, r)) return LQ_ERR_WORKSPACE;
@@ -420,6 +520,10 @@ int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const ui
                          void* stream) {
   if (!codes_a || !absmax_a || !codes_b || !absmax_b || !row_bits || !offsets_a || !offsets_b || !levels_a ||
       !levels_b || !A_bf16 || !B_bf16)
+    return LQ_ERR_ARG;
+  if (!al(codes_a, kVec) || !al(codes_b, kVec) || !al(absmax_a, 4) || !al(absmax_b, 4) || !al(offsets_a, 8) ||
+      !al(offsets_b, 8) || !al(levels_a, 4) || !al(levels_b, 4) || !al(A_bf16, kVec) || !al(B_bf16, kVec) ||
+      !al(workspace, kVec))
     return LQ_ERR_ARG;
   const int st = check_loraquant_shape(N, K, r);
   if (st != LQ_OK) return st;
@@ -446,6 +550,30 @@ int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const ui
   e = launch_dequant(qb, bt, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   return launch_status(launch_transpose_u16(bt, r, (int)N, B_bf16, s));
+}
+
+int lq_check_codebook_tables(int64_t N, int64_t K, const uint8_t* row_bits, const int64_t* row_offset,
+                             const float* thresholds) {
+  if (N <= 0 || K <= 0 || K % 64 != 0) return LQ_ERR_SHAPE;
+  if (!row_bits || !row_offset) return LQ_ERR_ARG;
+  return check_codebook_host(N, K, row_bits, row_offset, thresholds);
+}
+
+int lq_debug_build(void) {
+#ifdef LQ_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+int lq_debug_flags(uint32_t* flags, int clear) {
+  if (!flags) return LQ_ERR_ARG;
+  if (!lq_debug_build()) return LQ_ERR_UNSUPPORTED;
+  unsigned int v = 0;
+  if (debug_flags(&v, clear != 0) != hipSuccess) return LQ_ERR_LAUNCH;
+  *flags = v;
+  return LQ_OK;
 }
 
 }  // extern "C"

@@ -17,6 +17,15 @@
 #include "lq_device.h"
 
 namespace lq {
+
+// Debug build: a per-device flag word (LQ_DBG_* bits) that the quantizers
+// set when they see input that violates the documented preconditions. The
+// release build compiles the checks away.
+#ifdef LQ_DEBUG
+__device__ unsigned int g_lq_debug_flags;
+__device__ __forceinline__ void dbg_flag(unsigned int bits) { atomicOr(&g_lq_debug_flags, bits); }
+#endif
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -81,6 +90,13 @@ __global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W,
     const int64_t blk = blk0 + 16 * p;
     v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+#ifdef LQ_DEBUG
+#pragma unroll
+  for (int p = 0; p < kQuantPasses; ++p)
+    if (!(__builtin_isfinite(v[p].x) && __builtin_isfinite(v[p].y) && __builtin_isfinite(v[p].z) &&
+          __builtin_isfinite(v[p].w)))
+      dbg_flag(LQ_DBG_NONFINITE);
+#endif
 #pragma unroll
   for (int p = 0; p < kQuantPasses; ++p) {
     const int64_t blk = blk0 + 16 * p;
@@ -426,6 +442,14 @@ __device__ __forceinline__ void codebook_row(const Tin* __restrict__ Wr, int64_t
   float tr[NT];
 #pragma unroll
   for (int k = 0; k < NT; ++k) tr[k] = Tr[k];
+#ifdef LQ_DEBUG
+  if (wave == 0 && lane == 0) {
+    bool inc = true;
+#pragma unroll
+    for (int k = 1; k < NT; ++k) inc = inc && (tr[k] > tr[k - 1]);
+    if (!inc) dbg_flag(LQ_DBG_THRESHOLDS);
+  }
+#endif
   const int g = lane >> 4, m = lane & 15;
   for (int64_t c0 = wave; c0 * 4 < blocks; c0 += 4 * BATCH) {
     float w[BATCH][4];
@@ -435,6 +459,11 @@ __device__ __forceinline__ void codebook_row(const Tin* __restrict__ Wr, int64_t
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[b][j] = 0.0f;
       if (blk < blocks) load4<Tin, VEC>(Wr + blk * 64 + 4 * m, w[b]);
+#ifdef LQ_DEBUG
+      if (!(__builtin_isfinite(w[b][0]) && __builtin_isfinite(w[b][1]) && __builtin_isfinite(w[b][2]) &&
+            __builtin_isfinite(w[b][3])))
+        dbg_flag(LQ_DBG_NONFINITE);
+#endif
     }
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
@@ -475,6 +504,9 @@ __global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
   const int nb = min(max((int)row_bits[row], 1), 4);
+#ifdef LQ_DEBUG
+  if (threadIdx.x == 0 && nb != (int)row_bits[row]) dbg_flag(LQ_DBG_ROW_BITS);
+#endif
   const int64_t blocks = K / 64;
   const Tin* Wr = W + row * K;
   const float* Tr = T + row * 15;
@@ -496,6 +528,7 @@ __global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict
 hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8_t* codes,
                                float* absmax, hipStream_t s) {
   const int64_t per_wg = 16 * kQuantPasses;
+  LQ_DASSERT(n_blocks > 0 && (n_blocks + per_wg - 1) / per_wg < (int64_t(1) << 31));
   const dim3 grid((unsigned)((n_blocks + per_wg - 1) / per_wg));
   const Nf4Lut& lut = tables().lut;
   if (dtype == LQ_F32)
@@ -574,6 +607,7 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
 }
 
 hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
+  LQ_DASSERT(w.N > 0 && w.K % 64 == 0 && (w.N * w.K + 8191) / 8192 < (int64_t(1) << 31));
   if (w.format == LQ_FMT_NF4) {
     const int64_t n = w.N * w.K;
     const dim3 grid((unsigned)((n + 8191) / 8192));
@@ -609,6 +643,23 @@ hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t
       hipLaunchKernelGGL((k_quantize_codebook<_Float16, false>), grid, block, 0, s, (const _Float16*)W, K, row_bits, row_offset, T, codes, absmax);
   }
   return hipGetLastError();
+}
+
+hipError_t debug_flags(unsigned int* out, bool clear) {
+#ifdef LQ_DEBUG
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  if ((e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_lq_debug_flags), sizeof(unsigned int))) != hipSuccess) return e;
+  if (clear) {
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_lq_debug_flags), &zero, sizeof(unsigned int));
+  }
+  return e;
+#else
+  (void)out;
+  (void)clear;
+  return hipErrorNotSupported;
+#endif
 }
 
 }  // namespace lq

@@ -1168,6 +1168,8 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   set_lora(p, t, B, r, s, true);
   hipError_t e = hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
+  LQ_DASSERT(M > 0 && w.K % 64 == 0 && tiles > 0 && tiles < (int64_t(1) << 31));
+  LQ_DASSERT(r >= 1 && r <= 128 && p.R2 % BK == 0);
   const dim3 grid((unsigned)tiles);
   const bool dq = w.qc.absmax == nullptr;
   const bool f32 = h_dtype == LQ_F32;
@@ -1198,6 +1200,8 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
   set_lora(p, u, A, r, s, false);
   hipError_t e = hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
+  LQ_DASSERT(M > 0 && w.N % 8 == 0 && w.K % 64 == 0 && tiles > 0 && tiles < (int64_t(1) << 31));
+  LQ_DASSERT(r >= 1 && r <= 128 && p.R2 % BK == 0);
   const dim3 grid((unsigned)tiles);
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
   if (w.format == LQ_FMT_CODEBOOK) {
@@ -1254,6 +1258,7 @@ hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
   const int rg = gemv_rg(w.N, w.K, M);
+  LQ_DASSERT(M >= 1 && M <= 16 && w.K % 64 == 0 && (int64_t)16 * rg * (w.K / 64 + 1) <= GV_CTAB);
   if (rg == 4) launch_gemv_rg<4>(p, dq, f32, st);
   else if (rg == 2) launch_gemv_rg<2>(p, dq, f32, st);
   else launch_gemv_rg<1>(p, dq, f32, st);

@@ -7,6 +7,21 @@
 
 #include "../../include/lq.h"
 
+// Host-side bounds asserts of the debug build: a failed check reports to
+// stderr and the launcher returns hipErrorInvalidValue instead of launching.
+#ifdef LQ_DEBUG
+#include <cstdio>
+#define LQ_DASSERT(cond)                                                                  \
+  do {                                                                                    \
+    if (!(cond)) {                                                                        \
+      std::fprintf(stderr, "lq debug: check failed: %s (%s:%d)\n", #cond, __FILE__, __LINE__); \
+      return hipErrorInvalidValue;                                                        \
+    }                                                                                     \
+  } while (0)
+#else
+#define LQ_DASSERT(cond) ((void)0)
+#endif
+
 namespace lq {
 
 // Block constants of a quantized weight (float32, or double quantized).
@@ -99,6 +114,9 @@ hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K
                             float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b,
                             float* levels_a, float* thresholds_a, float* levels_b, float* thresholds_b,
                             float* sigma, int32_t* h_out, float* Ap_out, float* Bpt_out, void* ws, hipStream_t s);
+// Debug build: read (and optionally clear) the device flag word after a
+// device synchronisation; hipErrorNotSupported in the release build.
+hipError_t debug_flags(unsigned int* out, bool clear);
 hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t K,
                                     const uint8_t* row_bits, const int64_t* row_offset,
                                     const float* thresholds, uint8_t* codes, float* absmax,
@@ -163,7 +181,7 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
                            const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st);
 // The decode GEMV handles NF4 weights whose per-workgroup constant table
-// fits in LDS (K up to about 14000 for wide N); others use the GEMM.
+// fits in LDS (K <= 33728: one row group of 16 rows); others use the GEMM.
 bool gemv_supported(const QWeight& w);
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,

@@ -33,9 +33,11 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 32
+    assert len(names) == 35
+    dbg = lq.load_debug_library()
     for name in names:
         assert hasattr(lq.lib, name), name
+        assert hasattr(dbg, name), name
         assert name in lq.SIGNATURES, name
 
 
@@ -140,7 +142,7 @@ def test_validation_errors_without_launch(lq):
     b3 = list(bargs); b3[0] = ctypes.byref(w_odd)
     assert L.lq_qlora_backward(*b3) == lq.LQ_ERR_SHAPE
     # a codebook weight is dequantized into the workspace: N * K * 2 more bytes
-    wc = qw(format=1, row_bits=1, row_offset=1, levels=1)
+    wc = qw(format=1, row_bits=1, row_offset=0x1000, levels=0x1000)
     wsc = L.lq_backward_workspace(ctypes.byref(wc), 64, 16)
     assert wsc == wsb + 128 * 256 * 2
     b4 = list(bargs); b4[0] = ctypes.byref(wc)
@@ -240,7 +242,7 @@ def test_lowrank_validation(lq):
 
 
 def test_workspace_queries_deterministic(lq):
-    w = lq.lq_qweight(0, 64, 4096, 4096, 1, 1, None, None, None, 256, 0, None, None, None)
+    w = lq.lq_qweight(0, 64, 4096, 4096, 0x1000, 0x1000, None, None, None, 256, 0, None, None, None)
     a = [lq.lib.lq_forward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
     b = [lq.lib.lq_backward_workspace(ctypes.byref(w), 2048, 16) for _ in range(3)]
     assert len(set(a)) == 1 and len(set(b)) == 1 and a[0] > 0 and b[0] > 0
@@ -279,3 +281,109 @@ def test_loraquant_validation(lq):
     assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_ARG
     d = list(dargs); d[15] = dws - 1
     assert L.lq_loraquant_dequant(*d) == lq.LQ_ERR_WORKSPACE
+
+
+# ---- alignment, the host table check and the LQ_DEBUG build ----------------
+
+def _libs(lq):
+    return [("release", lq.lib), ("debug", lq.load_debug_library())]
+
+
+def test_debug_build_flag(lq):
+    assert lq.lib.lq_debug_build() == 0
+    assert lq.load_debug_library().lq_debug_build() == 1
+    v = ctypes.c_uint32(0)
+    # the release build has no flag word; neither build accepts a null output
+    assert lq.lib.lq_debug_flags(ctypes.byref(v), 0) == lq.LQ_ERR_UNSUPPORTED
+    assert lq.load_debug_library().lq_debug_flags(None, 0) == lq.LQ_ERR_ARG
+
+
+@pytest.mark.parametrize("which", ["release", "debug"])
+def test_misaligned_pointers_rejected_before_launch(lq, which):
+    L = dict(_libs(lq))[which]
+    vp = ctypes.c_void_p
+    a = 0x10000            # 16-byte aligned fake device address (never dereferenced)
+    null = vp(None)
+    ARG = lq.LQ_ERR_ARG
+    # quantizer: float32 W needs 16 bytes, bf16 W 8, the codes 8
+    assert L.lq_quantize_nf4(vp(a + 8), 0, 4, 64, 64, vp(a), vp(a), null) == ARG
+    assert L.lq_quantize_nf4(vp(a + 4), 1, 4, 64, 64, vp(a), vp(a), null) == ARG
+    assert L.lq_quantize_nf4(vp(a), 0, 4, 64, 64, vp(a + 4), vp(a), null) == ARG
+    assert L.lq_quantize_nf4(vp(a), 0, 4, 64, 64, vp(a), vp(a + 2), null) == ARG
+    assert L.lq_profile_nf4(vp(a + 4), 0, 4, 4096, 64, 0.01, vp(a), vp(a), 1 << 20, null) == ARG
+    assert L.lq_double_quant(vp(a + 2), 1000, 256, vp(a), vp(a), vp(a), vp(a), 1 << 20, null) == ARG
+
+    def qw(**kw):
+        d = dict(format=0, blocksize=64, N=128, K=256, codes=a, absmax=a, absmax_q=None,
+                 dq_scale=None, dq_mean=None, dq_blocksize=256, reserved0=0, row_bits=None,
+                 row_offset=None, levels=None)
+        d.update(kw)
+        return lq.lq_qweight(**d)
+
+    assert L.lq_dequant(ctypes.byref(qw(codes=a + 4)), vp(a), null) == ARG
+    assert L.lq_dequant(ctypes.byref(qw(absmax=a + 2)), vp(a), null) == ARG
+    assert L.lq_dequant(ctypes.byref(qw(absmax=None, absmax_q=a + 1, dq_scale=a, dq_mean=a)), vp(a), null) == ARG
+    assert L.lq_dequant(ctypes.byref(qw()), vp(a + 8), null) == ARG
+    w = qw()
+    ws = L.lq_forward_workspace(ctypes.byref(w), 16, 16)
+    good = dict(X=a, A=a, B=a, H=a, t=a, ws=a)
+    for bad in ("X", "A", "B", "H", "t", "ws"):
+        p = dict(good)
+        p[bad] = a + 2
+        assert L.lq_qlora_forward(ctypes.byref(w), vp(p["X"]), 16, vp(p["A"]), vp(p["B"]), 16, 32.0, vp(p["H"]), 1,
+                                  vp(p["t"]), vp(p["ws"]), ws, null) == ARG, bad
+        if bad != "A":
+            assert L.lq_dequant_gemm(ctypes.byref(w), vp(p["X"]), 16, vp(p["t"]), vp(p["B"]), 16, 32.0, vp(p["H"]),
+                                     1, vp(p["ws"]), 1 << 20, null) == ARG, bad
+    # a float32 H needs only 4 bytes: that call gets past the alignment checks
+    # and stops at the next one (a workspace one byte short); nothing launches
+    st = L.lq_qlora_forward(ctypes.byref(w), vp(a), 16, vp(a), vp(a), 16, 32.0, vp(a + 4), 0, null, vp(a), ws - 1,
+                            null)
+    assert st == lq.LQ_ERR_WORKSPACE
+    bws = L.lq_backward_workspace(ctypes.byref(w), 64, 16)
+    for bad in range(9):
+        p = [a] * 9
+        p[bad] += 2
+        X, G, A, B, t, gx, dA, dB, wsp = p
+        assert L.lq_qlora_backward(ctypes.byref(w), vp(X), vp(G), 64, vp(A), vp(B), 16, 32.0, vp(t), vp(gx),
+                                   vp(dA), vp(dB), vp(wsp), bws, null) == ARG, bad
+    assert L.lq_dequant_gemm_t(ctypes.byref(w), vp(a + 8), 64, vp(a), vp(a), 16, 32.0, vp(a), vp(a), 0, null) == ARG
+    assert L.lq_lora_down(vp(a), 16, 256, vp(a + 8), 16, vp(a), null, 0, null) == ARG
+    # the codebook quantizer takes W at any element alignment (this call stops
+    # at the blocksize check, after the alignment checks), codes at 4 bytes
+    assert L.lq_quantize_codebook(vp(a + 4), 0, 4, 64, 32, vp(a), vp(a), vp(a), vp(a), vp(a), null) == \
+        lq.LQ_ERR_UNSUPPORTED
+    assert L.lq_quantize_codebook(vp(a + 2), 0, 4, 64, 64, vp(a), vp(a), vp(a), vp(a), vp(a), null) == ARG
+    assert L.lq_quantize_codebook(vp(a), 0, 4, 64, 64, vp(a), vp(a + 4), vp(a), vp(a), vp(a), null) == ARG
+    assert L.lq_quantize_codebook(vp(a), 0, 4, 64, 64, vp(a), vp(a), vp(a), vp(a + 2), vp(a), null) == ARG
+    assert L.lq_lowrank_sub(vp(a + 4), 4, 64, vp(a), vp(a), 2, vp(a), null) == ARG
+    assert L.lq_residual(vp(a), vp(a + 4), 64, vp(a), null) == ARG
+
+
+def test_host_codebook_table_check(lq):
+    L = lq.lib
+    N, K = 4, 128
+    bits = np.array([1, 4, 3, 2], dtype=np.uint8)
+    off = np.concatenate([[0], np.cumsum(K * bits.astype(np.int64) // 8)]).astype(np.int64)
+    T = np.full((N, 15), 3.0, dtype=np.float32)
+    for i, b in enumerate(bits):
+        T[i, :(1 << b) - 1] = np.linspace(-0.9, 0.9, (1 << b) - 1)
+    P = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T)) == lq.LQ_OK
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(off), None) == lq.LQ_OK
+    assert L.lq_check_codebook_tables(N, 100, P(bits), P(off), None) == lq.LQ_ERR_SHAPE
+    assert L.lq_check_codebook_tables(N, K, None, P(off), None) == lq.LQ_ERR_ARG
+    b2 = bits.copy(); b2[2] = 5
+    assert L.lq_check_codebook_tables(N, K, P(b2), P(off), None) == lq.LQ_ERR_ARG
+    b2[2] = 0
+    assert L.lq_check_codebook_tables(N, K, P(b2), P(off), None) == lq.LQ_ERR_ARG
+    o2 = off.copy(); o2[2] += 8
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(o2), None) == lq.LQ_ERR_ARG
+    o2 = off.copy(); o2[0] = 8; o2[1:] += 8
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(o2), None) == lq.LQ_ERR_ARG
+    T2 = T.copy(); T2[1, 5] = T2[1, 4]          # a tie is not strictly increasing
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T2)) == lq.LQ_ERR_ARG
+    T2 = T.copy(); T2[2, 3] = np.nan
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T2)) == lq.LQ_ERR_ARG
+    T2 = T.copy(); T2[0, 1:] = -5.0             # unused slots of a 1-bit row are not checked
+    assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T2)) == lq.LQ_OK

@@ -78,3 +78,15 @@ def test_kernel_event_stride_times_enough_launches(bench, steps):
     assert 1 <= s <= 4
     # at least 5 launches are timed whenever the window has 5 steps
     assert timed >= min(5, steps)
+
+
+@pytest.mark.parametrize("N,K", [(1024, 1024), (4096, 4096), (11008, 4096), (28672, 8192)])
+def test_codec_rotation_defeats_the_infinity_cache(bench, N, K):
+    # every rotated codec arm moves at least 1 GiB per pass over its copies
+    # (four times the 256 MB cache), the dequant arm (2.5 B per weight) being
+    # the smallest
+    k = bench.rotation_count(N * K)
+    b = bench.codec_bytes(Layer(N, K, 16, 1))
+    for arm in ("quantize", "profile", "dequant"):
+        assert k * b[arm] >= 1 << 30
+    assert (k - 1) * (5 * N * K // 2) < 1 << 30   # and no more copies than that needs

@@ -358,6 +358,32 @@ def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
     assert layer.rel_frobenius(host(dB), rB) <= F32_TOL
 
 
+@pytest.mark.parametrize("need", [(True, False, False), (False, True, False), (False, False, True),
+                                  (True, True, False), (False, True, True), (True, False, True)])
+def test_backward_output_subsets(lq, torch, need):
+    """Any subset of (grad_X, dA, dB): each requested output matches the
+    oracle and the others come back as None (dA alone moves the column-form
+    job into the first slot of the merged launch)."""
+    need_gx, need_dA, need_dB = need
+    N, K, M, r, alpha = 264, 320, 70, 24, 8.0
+    L, W, X, A, B = make_layer(900, N, K, M, r, alpha)
+    G = syn.grad_out(L)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    Xd, Ad, Bd, Gd = (bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits),
+                      bf16_dev(torch, G.bits))
+    _, t = lq.qlora_forward(qw, Xd, Ad, Bd, alpha)
+    gx, dA, dB = lq.qlora_backward(qw, Xd, Gd, Ad, Bd, alpha, t=t, need_grad_x=need_gx, need_dA=need_dA,
+                                   need_dB=need_dB)
+    rX, rA, rB = layer.backward(oracle_wd(W), X.f32, G.f32, A.f32, B.f32, alpha)
+    assert (gx is not None) == need_gx and (dA is not None) == need_dA and (dB is not None) == need_dB
+    if need_gx:
+        assert layer.rel_frobenius(bf16_to_f32(gx), rX) <= BF16_TOL
+    if need_dA:
+        assert layer.rel_frobenius(host(dA), rA) <= F32_TOL
+    if need_dB:
+        assert layer.rel_frobenius(host(dB), rB) <= F32_TOL
+
+
 def test_backward_grad_x_unit_probe(lq, torch):
     """G rows = e_n, B = 0 (so u = 0): grad_X[m, :] = W'[n_m, :] exactly."""
     rng = np.random.default_rng(4)
