@@ -506,6 +506,29 @@ int lq_loraquant_dequant(const uint8_t* codes_a, const float* absmax_a, const ui
                          int64_t K, int32_t r, uint16_t* A_bf16, uint16_t* B_bf16, void* workspace, size_t ws_bytes,
                          void* stream);
 
+/*
+ * lq_qlora_backward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * lq_qlora_backward minus the workspace; its scratch is a library-owned
+ * device array of LQ_NOALLOC_SCRATCH_BYTES per GPU (reserved on every GPU
+ * the library runs on until the process ends). Shapes whose backward
+ * workspace (lq_qlora_backward_noalloc_bytes, equal to lq_backward_workspace)
+ * exceeds that size are refused with LQ_ERR_WORKSPACE before anything runs:
+ * the NF4 layers of the 4096 x 4096 / 2048-token and 4096 <-> 11008 /
+ * 4096-token (r = 64) workloads fit. The call allocates nothing and never
+ * synchronizes (the LQ_DEBUG build's layout check of codebook weights
+ * aside). All calls on one GPU share its array, which keeps the last call's
+ * contents (the call writes every piece before reading it): calls that may
+ * overlap on one GPU -- on different streams, or from several host threads
+ * -- race on it and must be serialised by the caller.
+ */
+#define LQ_NOALLOC_SCRATCH_BYTES (96u << 20)
+size_t lq_qlora_backward_noalloc_bytes(const lq_qweight* w, int64_t M, int32_t r);
+int lq_qlora_backward_noalloc(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                              const float* t_saved, uint16_t* grad_X, float* dA, float* dB, void* stream);
+
 /* ---- checks and the LQ_DEBUG build ---------------------------------------- */
 
 /*

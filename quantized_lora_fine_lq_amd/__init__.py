@@ -23,6 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "lib", "liblq.so")
 DEBUG_LIB_PATH = os.path.join(HERE, "lib", "liblq_debug.so")
 LQ_DBG_NONFINITE, LQ_DBG_THRESHOLDS, LQ_DBG_ROW_BITS = 1, 2, 4
+LQ_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 LQ_OK, LQ_ERR_ARG, LQ_ERR_SHAPE, LQ_ERR_UNSUPPORTED, LQ_ERR_WORKSPACE, LQ_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 LQ_F32, LQ_BF16, LQ_F16 = 0, 1, 2
@@ -95,6 +96,9 @@ SIGNATURES = {
     "lq_dequant_gemm_t_workspace": (c_sz, [QW_P, c_i64, c_i32]),
     "lq_dequant_gemm_t": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp,
                                          c_vp, c_sz, c_vp]),
+    "lq_qlora_backward_noalloc_bytes": (c_sz, [QW_P, c_i64, c_i32]),
+    "lq_qlora_backward_noalloc": (ctypes.c_int, [QW_P, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp,
+                                                 c_vp, c_vp, c_vp, c_vp]),
     "lq_check_codebook_tables": (ctypes.c_int, [c_i64, c_i64, c_vp, c_vp, c_vp]),
     "lq_debug_build": (ctypes.c_int, []),
     "lq_debug_flags": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]),

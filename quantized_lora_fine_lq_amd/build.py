@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "liblq.so")
 LIB_DEBUG = os.path.join(LIB_DIR, "liblq_debug.so")
-SOURCES = ["lq_tables.cpp", "lq_api.cpp", "lq_codec.hip", "lq_gemm.hip", "lq_lloyd.hip", "lq_lowrank.hip"]
+SOURCES = ["lq_tables.cpp", "lq_api.cpp", "lq_codec.hip", "lq_gemm.hip", "lq_lloyd.hip", "lq_lowrank.hip",
+           "lq_noalloc.hip"]
 ARCH = os.environ.get("LQ_OFFLOAD_ARCH", "gfx950")
 
 

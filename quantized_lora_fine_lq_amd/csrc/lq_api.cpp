@@ -133,6 +133,64 @@ size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
          align_up(col_skinny_ws_floats(M, w.K, r) * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
 }
 
+// Arguments of the backward entry points, validated before anything runs.
+int check_backward(const lq_qweight* w, QWeight* q, const uint16_t* X, const uint16_t* G, int64_t M,
+                   const uint16_t* A, const uint16_t* B, int32_t r, const float* t_saved, const uint16_t* grad_X,
+                   const float* dA, const float* dB) {
+  const int st = check_qweight(w, q);
+  if (st != LQ_OK) return st;
+  if (!G || !A || !B) return LQ_ERR_ARG;
+  if ((dA || !t_saved) && !X) return LQ_ERR_ARG;
+  if (!al(X, kVec) || !al(G, kVec) || !al(A, kVec) || !al(B, kVec) || !al(t_saved, 4) || !al(grad_X, kVec) ||
+      !al(dA, 4) || !al(dB, 4))
+    return LQ_ERR_ARG;
+  if (M <= 0 || r < 1 || r > 128 || q->N % 8 != 0) return LQ_ERR_SHAPE;
+  return LQ_OK;
+}
+
+// The backward's launches over a workspace of at least backward_ws bytes
+// (whose contents on entry do not matter: every piece is written before it
+// is read).
+int run_backward(const QWeight& q, const uint16_t* X, const uint16_t* G, int64_t M, const uint16_t* A,
+                 const uint16_t* B, int32_t r, float alpha, const float* t_saved, uint16_t* grad_X, float* dA,
+                 float* dB, void* workspace, size_t ws_bytes, hipStream_t s) {
+  Carver cv(workspace, ws_bytes);
+  float* u = cv.take<float>((size_t)M * r);
+  float* t_ws = cv.take<float>((size_t)M * r);
+  uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
+  uint16_t* pt2_t = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
+  uint16_t* pt2_u = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
+  float* part_b = cv.take<float>(col_skinny_ws_floats(M, q.N, r));
+  float* part_a = cv.take<float>(col_skinny_ws_floats(M, q.K, r));
+  uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
+  if (!cv.ok()) return LQ_ERR_WORKSPACE;
+  int st = debug_check_weight(q, s);
+  if (st != LQ_OK) return st;
+  const float scale = alpha / (float)r;
+  hipError_t e = hipSuccess;
+  const float* t = t_saved;
+  if (!t) {
+    e = launch_row_skinny(X, M, q.K, A, r, t_ws, nullptr, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+    t = t_ws;
+  }
+  e = launch_bwd_prep(B, q.N, r, Bt, t, M, pt2_t, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  // dB = s G^T t and dA = s u^T X in one launch, then grad_X
+  SplitJobDesc job_b, job_a;
+  const ColSkinnyReq req_b{pt2_t, G, q.N, scale, dB, true, part_b};
+  const ColSkinnyReq req_a{pt2_u, X, q.K, scale, dA, false, part_a};
+  e = launch_col_skinny(dB ? &req_b : nullptr, dA ? &req_a : nullptr, M, r, &job_b, &job_a, s);
+  if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  if (grad_X) {
+    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s);
+    if (e != hipSuccess) return LQ_ERR_LAUNCH;
+  }
+  return launch_status(launch_reduce_splits2(job_b, job_a, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,51 +391,29 @@ int lq_qlora_backward(const lq_qweight* w, const uint16_t* X, const uint16_t* G,
                       const float* t_saved, uint16_t* grad_X, float* dA, float* dB,
                       void* workspace, size_t ws_bytes, void* stream) {
   QWeight q;
-  int st = check_qweight(w, &q);
+  const int st = check_backward(w, &q, X, G, M, A, B, r, t_saved, grad_X, dA, dB);
   if (st != LQ_OK) return st;
-  if (!G || !A || !B) return LQ_ERR_ARG;
-  if ((dA || !t_saved) && !X) return LQ_ERR_ARG;
-  if (!al(X, kVec) || !al(G, kVec) || !al(A, kVec) || !al(B, kVec) || !al(t_saved, 4) || !al(grad_X, kVec) ||
-      !al(dA, 4) || !al(dB, 4) || !al(workspace, kVec))
-    return LQ_ERR_ARG;
-  if (M <= 0 || r < 1 || r > 128 || q.N % 8 != 0) return LQ_ERR_SHAPE;
-  const size_t need = backward_ws(q, M, r);
-  if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  Carver cv(workspace, ws_bytes);
-  float* u = cv.take<float>((size_t)M * r);
-  float* t_ws = cv.take<float>((size_t)M * r);
-  uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
-  uint16_t* pt2_t = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
-  uint16_t* pt2_u = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
-  float* part_b = cv.take<float>(col_skinny_ws_floats(M, q.N, r));
-  float* part_a = cv.take<float>(col_skinny_ws_floats(M, q.K, r));
-  uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
-  if (!cv.ok()) return LQ_ERR_WORKSPACE;
-  if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
-  const float scale = alpha / (float)r;
-  hipError_t e = hipSuccess;
-  const float* t = t_saved;
-  if (!t) {
-    e = launch_row_skinny(X, M, q.K, A, r, t_ws, nullptr, s);
-    if (e != hipSuccess) return LQ_ERR_LAUNCH;
-    t = t_ws;
-  }
-  e = launch_bwd_prep(B, q.N, r, Bt, t, M, pt2_t, s);
-  if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
-  if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  // dB = s G^T t and dA = s u^T X in one launch, then grad_X
-  SplitJobDesc job_b, job_a;
-  const ColSkinnyReq req_b{pt2_t, G, q.N, scale, dB, true, part_b};
-  const ColSkinnyReq req_a{pt2_u, X, q.K, scale, dA, false, part_a};
-  e = launch_col_skinny(dB ? &req_b : nullptr, dA ? &req_a : nullptr, M, r, &job_b, &job_a, s);
-  if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  if (grad_X) {
-    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s);
-    if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  }
-  return launch_status(launch_reduce_splits2(job_b, job_a, s));
+  if (!al(workspace, kVec)) return LQ_ERR_ARG;
+  if (!workspace || ws_bytes < backward_ws(q, M, r)) return LQ_ERR_WORKSPACE;
+  return run_backward(q, X, G, M, A, B, r, alpha, t_saved, grad_X, dA, dB, workspace, ws_bytes,
+                      (hipStream_t)stream);
+}
+
+size_t lq_qlora_backward_noalloc_bytes(const lq_qweight* w, int64_t M, int32_t r) {
+  return lq_backward_workspace(w, M, r);
+}
+
+int lq_qlora_backward_noalloc(const lq_qweight* w, const uint16_t* X, const uint16_t* G, int64_t M,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                              const float* t_saved, uint16_t* grad_X, float* dA, float* dB, void* stream) {
+  QWeight q;
+  const int st = check_backward(w, &q, X, G, M, A, B, r, t_saved, grad_X, dA, dB);
+  if (st != LQ_OK) return st;
+  if (backward_ws(q, M, r) > (size_t)LQ_NOALLOC_SCRATCH_BYTES) return LQ_ERR_WORKSPACE;
+  void* scratch = nullptr;   // this device's copy of the library's scratch array
+  if (noalloc_scratch(&scratch) != hipSuccess) return LQ_ERR_LAUNCH;
+  return run_backward(q, X, G, M, A, B, r, alpha, t_saved, grad_X, dA, dB, scratch,
+                      (size_t)LQ_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 int lq_quantize_codebook(const void* W, int32_t dtype, int64_t N, int64_t K, int32_t blocksize,

@@ -114,6 +114,9 @@ hipError_t launch_loraquant(const float* B, const float* A, int64_t N, int64_t K
                             float* absmax_b, uint8_t* row_bits, int64_t* offsets_a, int64_t* offsets_b,
                             float* levels_a, float* thresholds_a, float* levels_b, float* thresholds_b,
                             float* sigma, int32_t* h_out, float* Ap_out, float* Bpt_out, void* ws, hipStream_t s);
+// Device address of this device's copy of the library's no-allocation
+// scratch array (LQ_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t noalloc_scratch(void** out);
 // Debug build: read (and optionally clear) the device flag word after a
 // device synchronisation; hipErrorNotSupported in the release build.
 hipError_t debug_flags(unsigned int* out, bool clear);

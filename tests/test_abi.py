@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 35
+    assert len(names) == 37
     dbg = lq.load_debug_library()
     for name in names:
         assert hasattr(lq.lib, name), name
@@ -387,3 +387,40 @@ def test_host_codebook_table_check(lq):
     assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T2)) == lq.LQ_ERR_ARG
     T2 = T.copy(); T2[0, 1:] = -5.0             # unused slots of a 1-bit row are not checked
     assert L.lq_check_codebook_tables(N, K, P(bits), P(off), P(T2)) == lq.LQ_OK
+
+
+def test_noalloc_backward_refuses_shapes_beyond_its_scratch(lq):
+    """The no-allocation backward checks its workspace need against the
+    library's fixed scratch before touching the device (fake pointers: no
+    call below gets past validation)."""
+    L = lq.lib
+    vp = ctypes.c_void_p
+    a = vp(0x10000)
+    null = vp(None)
+
+    def qw(N, K, fmt=0):
+        return lq.lq_qweight(format=fmt, blocksize=64, N=N, K=K, codes=0x10000, absmax=None, absmax_q=0x10000,
+                             dq_scale=0x10000, dq_mean=0x10000, dq_blocksize=256, reserved0=0,
+                             row_bits=0x10000 if fmt else None, row_offset=0x10000 if fmt else None,
+                             levels=0x10000 if fmt else None)
+    limit = lq.LQ_NOALLOC_SCRATCH_BYTES
+    fits = [(4096, 4096, 2048, 16), (11008, 4096, 4096, 64), (4096, 11008, 4096, 64)]
+    for N, K, M, r in fits:
+        w = qw(N, K)
+        need = L.lq_qlora_backward_noalloc_bytes(ctypes.byref(w), M, r)
+        assert need == L.lq_backward_workspace(ctypes.byref(w), M, r)
+        assert 0 < need <= limit
+    big = qw(16384, 16384)
+    assert L.lq_qlora_backward_noalloc_bytes(ctypes.byref(big), 8192, 128) > limit
+    assert L.lq_qlora_backward_noalloc(ctypes.byref(big), a, a, 8192, a, a, 128, 16.0, a, a, a, a, null) == \
+        lq.LQ_ERR_WORKSPACE
+    # the codebook format also holds the dequantized weight (N K 2 bytes)
+    cb = qw(11008, 4096, fmt=1)
+    assert L.lq_qlora_backward_noalloc(ctypes.byref(cb), a, a, 4096, a, a, 64, 16.0, a, a, a, a, null) == \
+        lq.LQ_ERR_WORKSPACE
+    # argument errors come first, as in lq_qlora_backward
+    assert L.lq_qlora_backward_noalloc(None, a, a, 64, a, a, 16, 32.0, a, a, a, a, null) == lq.LQ_ERR_ARG
+    assert L.lq_qlora_backward_noalloc(ctypes.byref(big), a, vp(0x10002), 64, a, a, 16, 32.0, a, a, a, a, null) == \
+        lq.LQ_ERR_ARG
+    assert L.lq_qlora_backward_noalloc(ctypes.byref(big), a, a, 64, a, a, 0, 32.0, a, a, a, a, null) == \
+        lq.LQ_ERR_SHAPE
