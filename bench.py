@@ -71,7 +71,14 @@ def parse():
                     help="further timed windows of K steps for the run-to-run spread (0: none)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy 5 times (counter calibration)")
-    return ap.parse_args()
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for counter collection: no clock settling, spread windows, sessions, "
+                         "ceilings or CPU baseline; each kernel arm is 2 warm-up launches and one pass over its "
+                         "rotation")
+    args = ap.parse_args()
+    if args.profile:
+        args.settle_seconds, args.noise_windows, args.sessions, args.no_cpu_baseline = 0.0, 0, 1, True
+    return args
 
 
 class Dev:
@@ -213,6 +220,7 @@ def kernel_event_stride(steps):
 
 
 ARM_WARMUP = 20
+PROFILE_ARMS = False   # set by --profile: arms of 2 warm-ups and one pass over the rotation
 
 
 def time_arm(torch, fns, seconds, warmup=ARM_WARMUP):
@@ -223,6 +231,19 @@ def time_arm(torch, fns, seconds, warmup=ARM_WARMUP):
     3 batches). Returns (median, p10, p90) ms per launch over the batches and
     the number of timed launches."""
     n = len(fns)
+    if PROFILE_ARMS:
+        for i in range(2):
+            fns[i % n]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k = max(n, 3)
+        e0.record()
+        for i in range(k):
+            fns[i % n]()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / k
+        return ms, ms, ms, k
     for i in range(warmup):
         fns[i % n]()
     torch.cuda.synchronize()
@@ -549,6 +570,8 @@ def main():
               "kernel library, and sharding across GPUs is a design note, not a run.", flush=True)
         sys.exit(2)
     child_ms = [] if args.session_child else run_sessions(args)
+    global PROFILE_ARMS
+    PROFILE_ARMS = args.profile
     import numpy as np
     import torch
     import quantized_lora_fine_lq_amd as lq
@@ -658,12 +681,13 @@ def main():
     only = set(x for x in args.only.split(",") if x)
     want = lambda g: not only or g in only
     if not args.no_kernels:
-        copy_gbs = copy_ceiling_gbs(torch)
-        ceilings = {"copy_GB/s": round(copy_gbs, 1),
-                    "copy": "torch device copy, 1 GiB read + 1 GiB written; frac_copy in the kernel table is "
-                            "relative to it",
-                    "sclk": sclk_under_load(torch, calls[0].step)}
-        log("ceilings", ceilings)
+        copy_gbs = 5000.0 if args.profile else copy_ceiling_gbs(torch)
+        if not args.profile:
+            ceilings = {"copy_GB/s": round(copy_gbs, 1),
+                        "copy": "torch device copy, 1 GiB read + 1 GiB written; frac_copy in the kernel table is "
+                                "relative to it",
+                        "sclk": sclk_under_load(torch, calls[0].step)}
+            log("ceilings", ceilings)
 
         def rec(name, arm, work, unit, rotated=None):
             ms, p10, p90, n = arm

@@ -604,19 +604,36 @@ __device__ __forceinline__ u32x4_t dequant8_pair(uint32_t w, const f32x2_t* sPai
 }
 
 // Sub-step outer, row group inner: consecutive MFMAs go to different
-// accumulators, so none waits for the previous one.
+// accumulators, so none waits for the previous one. The pair lookups of two
+// row groups (8 LDS reads) are issued together, ahead of their first use
+// (the scheduling barriers keep them there): with the register budget of
+// four waves per SIMD the compiler otherwise waits for each lookup before
+// issuing the next, exposing the LDS latency once per code byte.
 template <int RG>
 __device__ __forceinline__ void gv_compute(const GvStage<RG>& st, const f32x2_t* sPair, const float* sC,
                                            int pitch, int li, f32x4_t (&acc)[RG]) {
+  constexpr int GB = RG < 2 ? RG : 2;   // row groups per lookup batch
   float cp[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) cp[g] = sC[(16 * g + li) * pitch + st.bl] * st.live;   // c * 0 = 0
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      const u32x4_t bv = dequant8_pair(st.code[g][u], sPair, cp[g]);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc[g], 0, 0, 0);
+    for (int g0 = 0; g0 < RG; g0 += GB) {
+      f32x2_t q[GB][4];
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) q[gg][b] = sPair[(st.code[g0 + gg][u] >> (8 * b)) & 0xFFu];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gg = 0; gg < GB; ++gg) {
+        const int g = g0 + gg;
+        u32x4_t bv;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bv[b] = pack_bf16x2(q[gg][b].x * cp[g], q[gg][b].y * cp[g]);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc[g], 0, 0, 0);
+      }
     }
 }
 
