@@ -296,7 +296,7 @@ def codec_bytes(L, M=0):
         "profile": 4 * n,
         "double_quant": 4 * n_b + n_b + 4 * n_d + 4,
         "dequant": packed + 2 * n,
-        "gemv": packed + 2 * L.K * M + 2 * L.r * L.K + 2 * L.N * L.r + 2 * L.N * M + 4 * M * L.r,
+        "gemv": packed + 2 * L.K * M + 2 * L.N * L.r + 2 * L.N * M + 4 * M * L.r,
     }
 
 
@@ -357,9 +357,15 @@ def lowra_bytes(syn, L):
     n = L.N * L.K
     bits = syn.lowra_row_bits(L).astype(np.int64)
     planes = int(np.sum(L.K * bits // 8))
+    n_b = n // 64
+    weight = planes + n_b + 4 * ((n_b + 255) // 256) + 4 + L.N + 8 * (L.N + 1) + L.N * 16 * 4
     return {
         "lloyd": 4 * n + L.N + L.N * (16 + 15 + 1) * 4,
         "quantize": 4 * n + L.N + 8 * (L.N + 1) + L.N * 15 * 4 + planes + 4 * (n // 64),
+        # decode GEMV: the double-quantized codebook weight (planes, E4M3
+        # constants, scales, mean, widths, offsets, levels) + X, t, B in, H out
+        "gemv": lambda M: weight + 2 * L.K * M + 4 * M * L.r + 2 * L.N * L.r + 2 * L.N * M,
+        "weight": weight,
     }
 
 
@@ -842,6 +848,19 @@ def main():
             rec("lowra.dequant_gemm_fwd",
                 time_arm(torch, [lambda: lq.dequant_gemm(qwl, Xd, tl, Bd, Ll.alpha, out=Hl)], arm_s),
                 flw["fwd_gemm"], "TFLOP/s")
+            # decode GEMV over copies of the codebook weight (>= 1 GiB per pass)
+            n_cp = max(1, -(-(1 << 30) // lb["weight"]))
+            cb_copies = [qwl] + [lq.QWeight(Ll.N, Ll.K, qwl.codes.clone(), absmax_q=qwl.absmax_q.clone(),
+                                            dq_scale=qwl.dq_scale.clone(), dq_mean=qwl.dq_mean.clone(),
+                                            fmt=lq.LQ_FMT_CODEBOOK, row_bits=bl, row_offset=qwl.row_offset,
+                                            levels=lv) for _ in range(n_cp - 1)]
+            for M in (1, 16):
+                Hm = torch.empty(M, Ll.N, dtype=torch.bfloat16, device="cuda")
+                Xm, tm = Xd[:M].contiguous(), tl[:M].contiguous()
+                fns = [(lambda q=q: lq.dequant_gemm(q, Xm, tm, Bd, Ll.alpha, out=Hm)) for q in cb_copies]
+                gb = lb["gemv"](M)
+                rec(f"lowra.gemv_M{M}", time_arm(torch, fns, arm_s), gb, "GB/s", gb * len(cb_copies))
+            del cb_copies
             del Wl, qwl, Xd, Hl
             torch.cuda.empty_cache()
 

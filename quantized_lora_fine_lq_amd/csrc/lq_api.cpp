@@ -56,8 +56,8 @@ int check_qweight(const lq_qweight* w, QWeight* out) {
   return LQ_OK;
 }
 
-// Forward path choice: the GEMV kernel for decode-sized M (NF4 only), else
-// the MFMA GEMM. LQ_FORCE_PATH=gemm forces the GEMM at any M (for tests).
+// Forward path choice: the GEMV kernel for decode-sized M, else the MFMA
+// GEMM. LQ_FORCE_PATH=gemm forces the GEMM at any M (for tests).
 bool use_gemv(const QWeight& w, int64_t M) {
   if (M > 16 || !gemv_supported(w)) return false;
   const char* f = std::getenv("LQ_FORCE_PATH");
@@ -121,7 +121,7 @@ int debug_check_weight(const QWeight& q, hipStream_t s) {
 }
 
 size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
-  return align_up((size_t)M * r * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, true));
+  return align_up((size_t)M * r * sizeof(float)) + (use_gemv(w, M) ? 0 : align_up(gemm_ws_bytes(w, M, r, true)));
 }
 
 // u, recomputed t, B^T, split t and u, partial sums of dB and of dA, GEMM
@@ -305,14 +305,15 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   hipStream_t s = (hipStream_t)stream;
   Carver cv(workspace, ws_bytes);
   float* t_ws = cv.take<float>((size_t)M * r);
-  uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
+  const bool gemv = use_gemv(q, M);
+  uint16_t* gws = gemv ? nullptr : cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
   if (!cv.ok()) return LQ_ERR_WORKSPACE;
   if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
   hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, nullptr, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  if (use_gemv(q, M)) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
+  if (gemv) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
   else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, gws, s);
   return launch_status(e);
 }

@@ -547,8 +547,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
 // dequantized straight into MFMA B registers through a 256-entry LDS table
 // of level pairs (one 8-byte lookup per code byte). The block constants of
 // the workgroup's rows are decoded once into LDS at the start, so the main
-// loop loads nothing but codes and X. The 8 partial sums are reduced in LDS
-// at the end, where the LoRA term is added.
+// loop loads nothing but codes and X. The LoRA term enters the accumulators
+// as one more MFMA step per wave before the main loop, so the 8 partial sums
+// reduced in LDS at the end are the whole result.
 // ===========================================================================
 struct GemvParams {
   const uint16_t* X;   // [M, K]
@@ -601,6 +602,45 @@ __device__ __forceinline__ u32x4_t dequant8_pair(uint32_t w, const f32x2_t* sPai
     o[b] = pack_bf16x2(q.x * cp, q.y * cp);
   }
   return o;
+}
+
+// The LoRA term of a GEMV tile on the matrix cores: s t B^T is the product of
+// the segment [hi(s t) | lo(s t)] (2r columns, bfloat16 hi + lo ~= s t) with
+// [B | B], taken in 32-column chunks, chunk w by wave w (r <= 128: at most 8
+// chunks). Lane (li, lg) supplies token li (rows past M repeat row M - 1)
+// and weight row `row` at columns 32 w + 8 lg + [0, 8); columns past 2r
+// are zero (waves past the last chunk add an all-zero product: no branch,
+// which keeps the kernels within the register budget of two workgroups per
+// CU). gv_lora_mfma adds the chunk to the wave's accumulator.
+struct GvLora {
+  u32x4_t a, b;
+};
+__device__ __forceinline__ GvLora gv_lora_load(const float* t, const uint16_t* B, int64_t M, int r, float s,
+                                               int wave, int li, int lg, int64_t row) {
+  const float* trow = t + min((int64_t)li, M - 1) * r;
+  const uint16_t* brow = B + row * r;
+  GvLora o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float av[2];
+    uint32_t bv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 32 * wave + 8 * lg + 2 * q + e;
+      const bool in = c < 2 * r;
+      const int j = !in ? 0 : (c < r ? c : c - r);
+      float hi, lo;
+      split_bf16(s * trow[j], hi, lo);
+      av[e] = !in ? 0.0f : (c < r ? hi : lo);
+      bv[e] = in ? (uint32_t)brow[j] : 0u;
+    }
+    o.a[q] = pack_bf16x2(av[0], av[1]);
+    o.b[q] = bv[0] | (bv[1] << 16);
+  }
+  return o;
+}
+__device__ __forceinline__ f32x4_t gv_lora_mfma(const GvLora& l, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(l.a), as_bf16x8(l.b), acc, 0, 0, 0);
 }
 
 // Sub-step outer, row group inner: consecutive MFMAs go to different
@@ -707,9 +747,15 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
   }
   __syncthreads();
 
+  // the LoRA operands are loaded only now, one row group at a time: held
+  // through the table build they would cost registers
   f32x4_t acc[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RG; ++g) {
+    acc[g] = gv_lora_mfma(gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
+                          f32x4_t{0.f, 0.f, 0.f, 0.f});
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // The scheduling barriers keep each stage's loads where they are issued
   // (left alone, the compiler sinks them next to their first use and the
@@ -743,11 +789,178 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
       float h = 0.0f;
 #pragma unroll
       for (int w = 0; w < GV_WAVES; ++w) h += sR[((w * RG + g) * 4 + v) * 64 + ln];
-      float lora = 0.0f;
-      for (int j = 0; j < p.r; ++j) lora = __builtin_fmaf(p.t[m * p.r + j], bf16_to_f32(p.B[n * p.r + j]), lora);
-      h += p.s * lora;
       if (OUT_F32) reinterpret_cast<float*>(p.out)[m * N + n] = h;
       else reinterpret_cast<uint16_t*>(p.out)[m * N + n] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+    }
+  }
+}
+
+// ===========================================================================
+// Decode GEMV (M <= 16), per-channel codebook weight. The NF4 kernel's tiling
+// with one row group per workgroup (16 weight rows, shared by all 8 waves).
+// Lane (li, lg) takes codes 32 (lg & 1) + [0, 32) of block 2 ss + (lg >> 1)
+// of row n0 + li: bit-plane p of those codes is one 32-bit word, at byte
+// 8 b (block) + 8 p + 4 (lg & 1) of the row (b its width), read as 0 for
+// p >= b. Two adjacent codes become one MFMA B word through a per-row LDS
+// table of level pairs whose index interleaves the two codes' bits (bit 2p:
+// bit p of the first code, bit 2p + 1: bit p of the second), so an index is
+// the 2-bit fields of the plane words at the pair's position, one field per
+// plane. The number of planes handled is the largest width among the
+// workgroup's 16 rows (a template parameter chosen per workgroup).
+// ===========================================================================
+constexpr int CB_TAB = 257;   // level pairs per row: 256 + 1 of padding (rows start on different banks)
+
+size_t cb_gemv_lds_bytes(int64_t K) {
+  const size_t rest = std::max<size_t>(16 * (size_t)(K / 64 + 1), (size_t)GV_WAVES * 4 * 64);
+  return (size_t)16 * CB_TAB * 8 + 16 * 16 * 4 + rest * 4;
+}
+
+struct CbStage {
+  uint32_t pl[4];   // bit-planes of the lane's 32 codes (bit j: code j)
+  u32x4_t x[4];     // X fragments, k = 32 (lg & 1) + 8 u + [0, 8) of the block
+  int bl;
+  float live;
+};
+
+template <int PB>
+__device__ __forceinline__ void cb_load(const uint8_t* rowp, int bw, const uint16_t* xrow, int lg, int st2,
+                                        int e1, int ns, int nb, CbStage& st) {
+  const int ss = min(st2, ns - 1);
+  const int bl = 2 * ss + (lg >> 1);
+  st.live = (st2 < e1 && bl < nb) ? 1.0f : 0.0f;
+  st.bl = min(bl, nb - 1);
+  const uint8_t* src = rowp + (int64_t)st.bl * 8 * bw + 4 * (lg & 1);
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    // planes past the row's width re-read its last plane (in bounds) and drop it
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(src + 8 * min(p, bw - 1));
+    st.pl[p] = p < bw ? v : 0u;
+  }
+  const uint16_t* xs = xrow + (int64_t)st.bl * 64 + 32 * (lg & 1);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.x[u] = ld16(xs + 8 * u);
+}
+
+template <int PB>
+__device__ __forceinline__ void cb_compute(const CbStage& st, const f32x2_t* tab, const float* sC, int pitch,
+                                           int li, f32x4_t& acc) {
+  const float cp = sC[li * pitch + st.bl] * st.live;   // c * 0 = 0
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f32x2_t q[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int j = 8 * u + 2 * h;
+      uint32_t idx = (st.pl[0] >> j) & 3u;
+#pragma unroll
+      for (int p = 1; p < PB; ++p) idx |= ((st.pl[p] >> j) & 3u) << (2 * p);
+      q[h] = tab[idx];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t bv;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) bv[h] = pack_bf16x2(q[h].x * cp, q[h].y * cp);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(st.x[u]), as_bf16x8(bv), acc, 0, 0, 0);
+  }
+}
+
+template <int PB, bool DQ>
+__device__ __forceinline__ f32x4_t cb_body(const GemvParams& p, unsigned char* lds, int64_t n0, const uint8_t* rowp,
+                                           int bw, const uint16_t* xrow) {
+  f32x2_t* sTab = reinterpret_cast<f32x2_t*>(lds);                  // [16][CB_TAB]
+  float* sLv = reinterpret_cast<float*>(lds + 16 * CB_TAB * 8);      // [16][16] levels
+  float* sC = sLv + 256;                                              // [16][nb + 1]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int nb = (int)(K / 64), pitch = nb + 1;
+  const int ns = (int)((K + 127) / 128);
+  const int e0 = (int)((int64_t)wave * ns / GV_WAVES), e1 = (int)((int64_t)(wave + 1) * ns / GV_WAVES);
+
+  CbStage s0, s1;
+  cb_load<PB>(rowp, bw, xrow, lg, e0, e1, ns, nb, s0);   // out before the tables are built
+  const GvLora lr = gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + li, N - 1));
+
+  if (threadIdx.x < 256) sLv[threadIdx.x] = p.w.levels[min(n0 + (threadIdx.x >> 4), N - 1) * 16 + (threadIdx.x & 15)];
+  const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
+  const int ncon = 16 * nb;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < ncon; i += 64 * GV_WAVES) {
+    const int rr = i / nb, bl = i - rr * nb;
+    const int64_t blk = min(n0 + rr, N - 1) * nb + bl;
+    sC[rr * pitch + bl] = DQ ? __builtin_fmaf(e4m3_decode(p.w.qc.absmax_q[blk]), p.w.qc.dq_scale[blk >> 8], mean)
+                             : p.w.qc.absmax[blk];
+  }
+  __syncthreads();
+  {
+    // 32 threads per row, 8 entries each: entry idx = (first level, second
+    // level) with the codes read from the even and the odd bits of idx
+    const int rr = threadIdx.x >> 5;
+    const float* L = sLv + 16 * rr;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t idx = (threadIdx.x & 31) + 32 * k;
+      const uint32_t c0 = (idx & 1u) | ((idx >> 1) & 2u) | ((idx >> 2) & 4u) | ((idx >> 3) & 8u);
+      const uint32_t c1 = ((idx >> 1) & 1u) | ((idx >> 2) & 2u) | ((idx >> 3) & 4u) | ((idx >> 4) & 8u);
+      sTab[rr * CB_TAB + idx] = f32x2_t{L[c0], L[c1]};
+    }
+  }
+  __syncthreads();
+
+  const f32x2_t* tab = sTab + li * CB_TAB;
+  f32x4_t acc = gv_lora_mfma(lr, f32x4_t{0.f, 0.f, 0.f, 0.f});
+  for (int st = e0; st < e1; st += 2) {
+    cb_load<PB>(rowp, bw, xrow, lg, st + 1, e1, ns, nb, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    cb_compute<PB>(s0, tab, sC, pitch, li, acc);
+    cb_load<PB>(rowp, bw, xrow, lg, st + 2, e1, ns, nb, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    cb_compute<PB>(s1, tab, sC, pitch, li, acc);
+  }
+  return acc;
+}
+
+template <bool DQ, bool OUT_F32>
+__global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_codebook(GemvParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char cb_lds[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t row = min(n0 + li, N - 1);   // rows past N: not stored
+  const int bw = min(max((int)p.w.row_bits[row], 1), 4);
+  const uint8_t* rowp = p.w.codes + p.w.row_offset[row];
+  const uint16_t* xrow = p.X + min((int64_t)li, p.M - 1) * K;
+  const int pb = (int)row16_max((float)bw);   // the 16 rows' widest, the same in every wave
+
+  f32x4_t acc;
+  switch (pb) {
+    case 1: acc = cb_body<1, DQ>(p, cb_lds, n0, rowp, bw, xrow); break;
+    case 2: acc = cb_body<2, DQ>(p, cb_lds, n0, rowp, bw, xrow); break;
+    case 3: acc = cb_body<3, DQ>(p, cb_lds, n0, rowp, bw, xrow); break;
+    default: acc = cb_body<4, DQ>(p, cb_lds, n0, rowp, bw, xrow); break;
+  }
+
+  // reduce the 8 K-splits in the constant region (free now)
+  __syncthreads();
+  float* sR = reinterpret_cast<float*>(cb_lds + 16 * CB_TAB * 8) + 256;   // [wave][v][lane]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) sR[(wave * 4 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int ln = threadIdx.x;
+    const int64_t n = n0 + (ln & 15);
+    if (n < N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = 4 * (ln >> 4) + v;
+        if (m >= p.M) continue;
+        float h = 0.0f;
+#pragma unroll
+        for (int w = 0; w < GV_WAVES; ++w) h += sR[(w * 4 + v) * 64 + ln];
+        if (OUT_F32) reinterpret_cast<float*>(p.out)[m * N + n] = h;
+        else reinterpret_cast<uint16_t*>(p.out)[m * N + n] = (uint16_t)(pack_bf16x2(h, 0.f) & 0xFFFFu);
+      }
     }
   }
 }
@@ -1254,7 +1467,10 @@ static int gemv_rg(int64_t N, int64_t K, int64_t M) {
   return best;
 }
 
+// Codebook weights: while the kernel's LDS (pair tables, levels, constants)
+// stays within 64 KB, i.e. K <= 32576.
 bool gemv_supported(const QWeight& w) {
+  if (w.format == LQ_FMT_CODEBOOK) return cb_gemv_lds_bytes(w.K) <= 65536;
   return w.format == LQ_FMT_NF4 && gemv_rg(w.N, w.K, 1) > 0;
 }
 
@@ -1274,6 +1490,16 @@ hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
+  if (w.format == LQ_FMT_CODEBOOK) {
+    const size_t lds = cb_gemv_lds_bytes(w.K);
+    const dim3 grid((unsigned)((w.N + 15) / 16)), block(64 * GV_WAVES);
+    LQ_DASSERT(M >= 1 && M <= 16 && w.K % 64 == 0 && lds <= 65536);
+    if (dq && f32) hipLaunchKernelGGL((k_gemv_codebook<true, true>), grid, block, lds, st, p);
+    else if (dq) hipLaunchKernelGGL((k_gemv_codebook<true, false>), grid, block, lds, st, p);
+    else if (f32) hipLaunchKernelGGL((k_gemv_codebook<false, true>), grid, block, lds, st, p);
+    else hipLaunchKernelGGL((k_gemv_codebook<false, false>), grid, block, lds, st, p);
+    return hipGetLastError();
+  }
   const int rg = gemv_rg(w.N, w.K, M);
   LQ_DASSERT(M >= 1 && M <= 16 && w.K % 64 == 0 && (int64_t)16 * rg * (w.K / 64 + 1) <= GV_CTAB);
   if (rg == 4) launch_gemv_rg<4>(p, dq, f32, st);

@@ -150,7 +150,7 @@ def test_validation_errors_without_launch(lq):
     # split forward stages: NF4 needs no workspace (the GEMM forms its LoRA
     # operands itself); a codebook weight is dequantized into N * K * 2 bytes
     assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 300, 16) == 128 * 256 * 2
-    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 16, 16) == 128 * 256 * 2
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(wc), 16, 16) == 0   # decode GEMV: no weight copy
     assert L.lq_dequant_gemm_t_workspace(ctypes.byref(wc), 300, 16) == 128 * 256 * 2
     assert L.lq_dequant_gemm_workspace(ctypes.byref(w), 300, 16) == 0
     assert L.lq_dequant_gemm_workspace(ctypes.byref(w), 16, 16) == 0
@@ -424,3 +424,22 @@ def test_noalloc_backward_refuses_shapes_beyond_its_scratch(lq):
         lq.LQ_ERR_ARG
     assert L.lq_qlora_backward_noalloc(ctypes.byref(big), a, a, 64, a, a, 0, 32.0, a, a, a, a, null) == \
         lq.LQ_ERR_SHAPE
+
+
+def test_codebook_forward_workspace_by_path(lq, monkeypatch):
+    """A codebook weight at decode sizes (M <= 16) goes through the GEMV,
+    which needs no bfloat16 copy of the weight; larger M (or the GEMM
+    forced) sizes the workspace for the dequantized weight."""
+    monkeypatch.delenv("LQ_FORCE_PATH", raising=False)
+    N, K = 512, 1024
+    w = lq.lq_qweight(1, 64, N, K, 0x1000, 0x1000, None, None, None, 256, 0, 0x1000, 0x1000, 0x1000)
+    small = lq.lib.lq_forward_workspace(ctypes.byref(w), 16, 16)
+    assert 16 * 16 * 4 <= small < N * K * 2
+    assert lq.lib.lq_dequant_gemm_workspace(ctypes.byref(w), 16, 16) == 0
+    assert lq.lib.lq_forward_workspace(ctypes.byref(w), 17, 16) >= N * K * 2
+    monkeypatch.setenv("LQ_FORCE_PATH", "gemm")
+    assert lq.lib.lq_forward_workspace(ctypes.byref(w), 16, 16) >= N * K * 2
+    # K past the GEMV's LDS budget: the GEMM path at every M
+    monkeypatch.delenv("LQ_FORCE_PATH")
+    wide = lq.lq_qweight(1, 64, 16, 32768, 0x1000, 0x1000, None, None, None, 256, 0, 0x1000, 0x1000, 0x1000)
+    assert lq.lib.lq_forward_workspace(ctypes.byref(wide), 1, 16) >= 16 * 32768 * 2

@@ -41,10 +41,10 @@ def test_codec_bytes_follow_the_format(bench, N, K):
     consts = n // 64 + 4 * ((n // 64 + 255) // 256) + 4
     assert b["dequant"] == n // 2 + consts + 2 * n
     assert b["double_quant"] == 4 * (n // 64) + consts
-    # decode GEMV at M tokens: packed weight + X + A + B + H + t
+    # decode GEMV at M tokens (t given): packed weight + X + B + H + t
     for M in (1, 4, 16):
         g = bench.codec_bytes(Layer(N, K, 16, M), M)["gemv"]
-        assert g == n // 2 + consts + 2 * K * M + 2 * 16 * K + 2 * N * 16 + 2 * N * M + 4 * M * 16
+        assert g == n // 2 + consts + 2 * K * M + 2 * N * 16 + 2 * N * M + 4 * M * 16
 
 
 def test_q_proj_decode_figures(bench):
@@ -52,7 +52,7 @@ def test_q_proj_decode_figures(bench):
     q = bench.codec_bytes(Layer(4096, 4096, 16, 2048))
     assert q["quantize"] == 76_546_048 and q["dequant"] == 42_209_284
     d = bench.codec_bytes(Layer(28672, 8192, 16, 1), 1)
-    assert d["gemv"] - (2 * 8192 + 2 * 16 * 8192 + 2 * 28672 * 16 + 2 * 28672 + 4 * 16) == 121_167_876
+    assert d["gemv"] - (2 * 8192 + 2 * 28672 * 16 + 2 * 28672 + 4 * 16) == 121_167_876
 
 
 def test_layer_flops(bench):
@@ -90,3 +90,22 @@ def test_codec_rotation_defeats_the_infinity_cache(bench, N, K):
     for arm in ("quantize", "profile", "dequant"):
         assert k * b[arm] >= 1 << 30
     assert (k - 1) * (5 * N * K // 2) < 1 << 30   # and no more copies than that needs
+
+
+def test_lowra_decode_bytes(bench):
+    """Codebook decode GEMV: the bit-planes (K b / 8 bytes per row), one E4M3
+    code per 64-block, one float32 scale per 256 blocks and the mean, the
+    widths (1 B per row), offsets (8 B per row + 1) and levels (16 float32 per
+    row), then X, t, B in and H out (LowRA page, section 4.1: per-channel
+    widths and mappings)."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import synthetic as syn
+    L = syn.LAYERS["lowra"]
+    lb = bench.lowra_bytes(syn, L)
+    n_b = L.N * L.K // 64
+    planes = L.K * (256 * 4 + 512 * 3 + 1280 * 2 + 2048 * 1) // 8     # 1.75 bits per weight
+    assert planes == L.N * L.K * 7 // 32
+    w = planes + n_b + 4 * (n_b // 256) + 4 + L.N + 8 * (L.N + 1) + 64 * L.N
+    assert lb["weight"] == w
+    assert lb["gemv"](16) == w + 2 * L.K * 16 + 4 * 16 * L.r + 2 * L.N * L.r + 2 * L.N * 16

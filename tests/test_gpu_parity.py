@@ -501,6 +501,75 @@ def test_codebook_forward_f32_and_backward(lq, torch, N, K, M, r, alpha):
     assert layer.rel_frobenius(host(dB), rB) <= F32_TOL
 
 
+def codebook_case_widths(seed, N, K, widths):
+    """Like codebook_case with the widths given: an int (every row), or
+    "mixed" (random rows of 1..4 bits, the widest differing between row
+    groups)."""
+    rng = np.random.default_rng(seed)
+    sig = 0.02 * np.exp(0.3 * rng.standard_normal(N))
+    W = (rng.standard_normal((N, K)) * sig[:, None]).astype(np.float32)
+    if widths == "mixed":
+        bits = rng.integers(1, 5, N).astype(np.uint8)
+        bits[:16] = rng.integers(1, 3, 16)          # a row group of 1- and 2-bit rows
+        bits[16:32] = rng.integers(1, 4, 16)        # one of at most 3 bits
+    else:
+        bits = np.full(N, widths, dtype=np.uint8)
+    L, T = lloyd.learn_codebooks(W, bits)
+    return W, bits, L, T
+
+
+@pytest.mark.parametrize("N,K,M,widths,double", [
+    (256, 512, 1, "mixed", True),
+    (200, 1344, 4, "mixed", True),     # ragged N, K/64 = 21 (a half-empty last stage)
+    (96, 4096, 16, "mixed", False),    # float32 constants
+    (64, 256, 16, 1, True),
+    (64, 320, 7, 2, True),
+    (48, 640, 16, 3, False),
+    (33, 2048, 3, 4, True),            # one row past two whole row groups
+])
+def test_codebook_decode_gemv(lq, torch, monkeypatch, N, K, M, widths, double):
+    """The codebook decode kernel (M <= 16) against the oracle, in float32 and
+    bfloat16 H, and against the GEMM path on the same inputs."""
+    W, bits, Lv, T = codebook_case_widths(N + K + M, N, K, widths)
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv),
+                                  double_quantize=double)
+    packed, c, _ = codebook.quantize(W, bits, T)
+    cp = dq.dq_decode(*dq.double_quant(c)) if double else c
+    Wd = codebook.dequant(packed, bits, Lv, cp, N, K)
+    Ls = syn.small_layer(N, K, M, 16, 32.0, 500 + N)
+    X, A, B = syn.activations(Ls), syn.lora_a(Ls), syn.lora_b(Ls)
+    args = (qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), 32.0)
+    H32, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    H16, _ = lq.qlora_forward(*args)
+    Href, _ = layer.forward(Wd, X.f32, A.f32, B.f32, 32.0)
+    assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
+    assert layer.rel_frobenius(bf16_to_f32(H16), Href) <= BF16_TOL
+    monkeypatch.setenv("LQ_FORCE_PATH", "gemm")
+    Hg, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
+    assert layer.rel_frobenius(host(H32), host(Hg)) <= F32_TOL
+
+
+def test_codebook_decode_gemv_unit_columns(lq, torch):
+    """X rows = unit vectors e_k, B = 0: H[m, n] = W'[n, k_m] exactly, so every
+    code the decode kernel reads (each bit-plane, both halves of a block,
+    every row width, rows past a whole row group) is checked bit for bit."""
+    N, K, M = 80, 1408, 16
+    W, bits, Lv, T = codebook_case_widths(77, N, K, "mixed")
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    Wd = codebook_oracle_wd(W, bits, Lv, T)
+    rng = np.random.default_rng(78)
+    A = syn.to_bf16_bits((rng.standard_normal((16, K)) * 0.02).astype(np.float32))
+    B = np.zeros((N, 16), dtype=np.uint16)
+    ks = np.concatenate([np.arange(0, 64, 4), rng.permutation(K)[:48]])
+    for c0 in range(0, ks.size, M):
+        kk = ks[c0:c0 + M]
+        X = np.zeros((M, K), dtype=np.uint16)
+        X[np.arange(M), kk] = 0x3F80
+        H, _ = lq.qlora_forward(qw, bf16_dev(torch, X), bf16_dev(torch, A), bf16_dev(torch, B), 32.0,
+                                out_dtype=torch.float32)
+        assert np.array_equal(host(H), Wd[:, kk].T)
+
+
 def test_codebook_grad_x_unit_probe(lq, torch):
     """G rows = e_n, B = 0: grad_X[m, :] = W'[n_m, :] exactly (the
     transposed copy of the dequantized codebook weight)."""
