@@ -431,69 +431,150 @@ __device__ __forceinline__ uint32_t row8_or(uint32_t v) {
   return v;
 }
 
-// One row at a compile-time width: thresholds in registers, the wave's
-// chunks of the row loaded together before any is processed.
-template <int NBITS, typename Tin, bool VEC>
-__device__ __forceinline__ void codebook_row(const Tin* __restrict__ Wr, int64_t blocks,
-                                             const float* __restrict__ Tr, uint8_t* __restrict__ dst,
-                                             float* __restrict__ absmax_row, int wave, int lane) {
+// Code search through a per-row bin table. x in [-1, 1] falls in bin
+// j = floor((x + 1) 64) (x = 1 in the last bin); widened by 2^-20 on both
+// sides, a bin holds at most one of the row's thresholds when they are more
+// than 1/64 + 2^-19 apart. Entry j: that threshold (or 4 if there is none)
+// and the codes just below and above it, each stored spread out as one bit
+// per byte (bit p of the code at bit 8p), so four codes combine into the
+// per-plane nibbles with shifts and ORs. The bin of the fast quotient
+// xp = w * (1/m) is used when |xp - T| > 2^-21 (|xp - x| <= 2^-22 for the
+// IEEE quotient x = w / m when m is normal and below 2^125); otherwise the
+// IEEE quotient is formed and its own bin decides, which is exact. Rows with
+// two thresholds in one widened bin count thresholds directly.
+constexpr int CB_BINS = 128;
+
+__device__ __forceinline__ uint32_t spread_bits(uint32_t c) {
+  return (c & 1u) | ((c & 2u) << 7) | ((c & 4u) << 14) | ((c & 8u) << 21);
+}
+
+__device__ __forceinline__ int cb_bin(float x) {
+  const int j = (int)__builtin_fmaf(x, 64.0f, 64.0f);   // truncation: x slightly below -1 -> 0
+  return min(max(j, 0), CB_BINS - 1);
+}
+
+// Builds the row's table (thread j < CB_BINS fills entry j); returns, in
+// *bad, whether some widened bin holds two thresholds.
+__device__ __forceinline__ void cb_build_bins(const float* tr, int nt, u32x4_t* lut, int* bad) {
+  const int j = threadIdx.x;
+  if (j < CB_BINS) {
+    const float lo = -1.0f + (float)j * (1.0f / 64.0f) - 0x1p-20f;        // exact in float32
+    const float hi = -1.0f + (float)(j + 1) * (1.0f / 64.0f) + 0x1p-20f;
+    uint32_t base = 0, inside = 0;
+    float t_in = 4.0f;
+    for (int k = 0; k < nt; ++k) {
+      const float t = tr[k];
+      if (t < lo) ++base;
+      else if (t <= hi) { ++inside; t_in = t; }
+    }
+    if (inside > 1) *bad = 1;   // benign race: every writer stores 1
+    lut[j] = u32x4_t{__float_as_uint(t_in), spread_bits(base), spread_bits(base + (inside ? 1u : 0u)), 0u};
+  }
+}
+
+// Code of w (block constant m, r = 1/m when fast_ok) through the bin table,
+// as spread bits.
+__device__ __forceinline__ uint32_t cb_code_spread(float w, float m, float r, bool fast_ok, const u32x4_t* lut) {
+  const float xp = w * r;
+  const u32x4_t e = lut[cb_bin(xp)];
+  const float T = __uint_as_float(e[0]);
+  if (fast_ok && fabsf(xp - T) > 0x1p-21f) return xp > T ? e[2] : e[1];
+  const float x = (m > 0.0f) ? w / m : 0.0f;   // IEEE quotient
+  const u32x4_t f = lut[cb_bin(x)];
+  return x > __uint_as_float(f[0]) ? f[2] : f[1];
+}
+
+// A batch of a wave: 4 chunks of 4 blocks (256 weights each), lane (g, m)
+// holding weights 4m .. 4m + 3 of block g of each chunk. Blocks past the
+// row load the row's last block (no branch around the loads, so the wait
+// for an earlier load need not wait for these) and are zeroed; they are
+// not stored.
+constexpr int CB_BATCH = 4;
+template <typename Tin, bool VEC>
+__device__ __forceinline__ void cb_load_batch(const Tin* __restrict__ Wr, int64_t blocks, int64_t c0, int lane,
+                                              float (&w)[CB_BATCH][4]) {
+  const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+  for (int b = 0; b < CB_BATCH; ++b) {
+    const int64_t blk = (c0 + 4 * b) * 4 + g;
+    load4<Tin, VEC>(Wr + min(blk, blocks - 1) * 64 + 4 * m, w[b]);
+  }
+#pragma unroll
+  for (int b = 0; b < CB_BATCH; ++b) {
+    const bool live = (c0 + 4 * b) * 4 + g < blocks;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[b][j] = live ? w[b][j] : 0.0f;
+  }
+}
+
+// One row at a compile-time width. The wave's first batch arrives loaded;
+// each further batch is loaded before the previous one is processed. LUT:
+// codes through the bin table; otherwise thresholds are counted one by one.
+template <int NBITS, bool LUT, typename Tin, bool VEC>
+__device__ __forceinline__ void codebook_row(const Tin* __restrict__ Wr, int64_t blocks, float (&wa)[CB_BATCH][4],
+                                             const float* __restrict__ sTr, const u32x4_t* lut,
+                                             uint8_t* __restrict__ dst, float* __restrict__ absmax_row,
+                                             int wave, int lane) {
   constexpr int NT = (1 << NBITS) - 1;
-  constexpr int BATCH = 4;
   float tr[NT];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) tr[k] = Tr[k];
-#ifdef LQ_DEBUG
-  if (wave == 0 && lane == 0) {
-    bool inc = true;
-#pragma unroll
-    for (int k = 1; k < NT; ++k) inc = inc && (tr[k] > tr[k - 1]);
-    if (!inc) dbg_flag(LQ_DBG_THRESHOLDS);
-  }
-#endif
+  for (int k = 0; k < NT; ++k) tr[k] = sTr[k];
   const int g = lane >> 4, m = lane & 15;
-  for (int64_t c0 = wave; c0 * 4 < blocks; c0 += 4 * BATCH) {
-    float w[BATCH][4];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int64_t blk = (c0 + 4 * b) * 4 + g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[b][j] = 0.0f;
-      if (blk < blocks) load4<Tin, VEC>(Wr + blk * 64 + 4 * m, w[b]);
+  for (int64_t c0 = wave; c0 * 4 < blocks; c0 += 4 * CB_BATCH) {
+    float wb[CB_BATCH][4];
+    const bool more = (c0 + 4 * CB_BATCH) * 4 < blocks;   // uniform over the wave
+    if (more) cb_load_batch<Tin, VEC>(Wr, blocks, c0 + 4 * CB_BATCH, lane, wb);
 #ifdef LQ_DEBUG
-      if (!(__builtin_isfinite(w[b][0]) && __builtin_isfinite(w[b][1]) && __builtin_isfinite(w[b][2]) &&
-            __builtin_isfinite(w[b][3])))
+#pragma unroll
+    for (int b = 0; b < CB_BATCH; ++b)
+      if (!(__builtin_isfinite(wa[b][0]) && __builtin_isfinite(wa[b][1]) && __builtin_isfinite(wa[b][2]) &&
+            __builtin_isfinite(wa[b][3])))
         dbg_flag(LQ_DBG_NONFINITE);
 #endif
-    }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
+    for (int b = 0; b < CB_BATCH; ++b) {
       const int64_t blk = (c0 + 4 * b) * 4 + g;
       const bool live = blk < blocks;   // uniform over the 16-lane row
-      float mx = fmaxf(fmaxf(fabsf(w[b][0]), fabsf(w[b][1])), fmaxf(fabsf(w[b][2]), fabsf(w[b][3])));
+      float mx = fmaxf(fmaxf(fabsf(wa[b][0]), fabsf(wa[b][1])), fmaxf(fabsf(wa[b][2]), fabsf(wa[b][3])));
       mx = row16_max(mx);
-      uint32_t code[4];
+      // spread codes of the lane's 4 weights: bit j of byte p = bit p of code j
+      uint32_t sp = 0;
+      if (LUT) {
+        const bool fast_ok = (mx >= FLT_MIN) && (mx <= 0x1p125f);
+        const float r = fast_ok ? 1.0f / mx : 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = (mx > 0.0f) ? w[b][j] / mx : 0.0f;
-        uint32_t cj = 0;
+        for (int j = 0; j < 4; ++j) sp |= cb_code_spread(wa[b][j], mx, r, fast_ok, lut) << j;
+      } else {
 #pragma unroll
-        for (int k = 0; k < NT; ++k) cj += (x > tr[k]) ? 1u : 0u;
-        code[j] = cj;
+        for (int j = 0; j < 4; ++j) {
+          const float x = (mx > 0.0f) ? wa[b][j] / mx : 0.0f;
+          uint32_t cj = 0;
+#pragma unroll
+          for (int k = 0; k < NT; ++k) cj += (x > tr[k]) ? 1u : 0u;
+          sp |= spread_bits(cj) << j;
+        }
       }
 #pragma unroll
       for (int p = 0; p < NBITS; ++p) {
-        uint32_t nib = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) nib |= ((code[j] >> p) & 1u) << j;
+        const uint32_t nib = (sp >> (8 * p)) & 0xFu;
         const uint32_t word = row8_or(nib << (4 * (m & 7)));
         if (live && (m & 7) == 0)
           *reinterpret_cast<uint32_t*>(dst + blk * 8 * NBITS + 8 * p + 4 * (m >> 3)) = word;
       }
       if (live && m == 0) absmax_row[blk] = mx;
     }
+    if (more) {
+#pragma unroll
+      for (int b = 0; b < CB_BATCH; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wa[b][j] = wb[b][j];
+    }
   }
 }
 
+// One workgroup per row. The row's first weights, its width, offset and
+// thresholds are all requested at the start; the bin table is built while
+// the weights are in flight.
 template <typename Tin, bool VEC>
 __global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict__ W, int64_t K,
                                                            const uint8_t* __restrict__ row_bits,
@@ -501,23 +582,49 @@ __global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict
                                                            const float* __restrict__ T,
                                                            uint8_t* __restrict__ codes,
                                                            float* __restrict__ absmax) {
+  __shared__ u32x4_t sLut[CB_BINS];
+  __shared__ float sTr[16];
+  __shared__ int sBad;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
-  const int nb = min(max((int)row_bits[row], 1), 4);
-#ifdef LQ_DEBUG
-  if (threadIdx.x == 0 && nb != (int)row_bits[row]) dbg_flag(LQ_DBG_ROW_BITS);
-#endif
   const int64_t blocks = K / 64;
   const Tin* Wr = W + row * K;
-  const float* Tr = T + row * 15;
+  // the small loads first: waiting for them (the counter is in order) then
+  // does not wait for the weights
+  const int rb = (int)row_bits[row];
+  const float t = threadIdx.x < 15 ? T[row * 15 + threadIdx.x] : 4.0f;
   uint8_t* dst = codes + row_offset[row];
-  float* am = absmax + row * blocks;
-  switch (nb) {
-    case 1: codebook_row<1, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
-    case 2: codebook_row<2, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
-    case 3: codebook_row<3, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
-    default: codebook_row<4, Tin, VEC>(Wr, blocks, Tr, dst, am, wave, lane); break;
+  float wa[CB_BATCH][4];
+  cb_load_batch<Tin, VEC>(Wr, blocks, wave, lane, wa);
+  const int nb = min(max(rb, 1), 4);
+#ifdef LQ_DEBUG
+  if (threadIdx.x == 0 && nb != rb) dbg_flag(LQ_DBG_ROW_BITS);
+#endif
+  const int nt = (1 << nb) - 1;
+  if (threadIdx.x < 16) sTr[threadIdx.x] = threadIdx.x < nt ? t : 4.0f;
+  if (threadIdx.x == 0) sBad = 0;
+  __syncthreads();
+#ifdef LQ_DEBUG
+  if (threadIdx.x == 0) {
+    bool inc = true;
+    for (int k = 1; k < nt; ++k) inc = inc && (sTr[k] > sTr[k - 1]);
+    if (!inc) dbg_flag(LQ_DBG_THRESHOLDS);
   }
+#endif
+  cb_build_bins(sTr, nt, sLut, &sBad);
+  __syncthreads();
+  const bool lut = sBad == 0;
+  float* am = absmax + row * blocks;
+#define LQ_CB_ROW(NB)                                                                       \
+  if (lut) codebook_row<NB, true, Tin, VEC>(Wr, blocks, wa, sTr, sLut, dst, am, wave, lane); \
+  else codebook_row<NB, false, Tin, VEC>(Wr, blocks, wa, sTr, sLut, dst, am, wave, lane)
+  switch (nb) {
+    case 1: LQ_CB_ROW(1); break;
+    case 2: LQ_CB_ROW(2); break;
+    case 3: LQ_CB_ROW(3); break;
+    default: LQ_CB_ROW(4); break;
+  }
+#undef LQ_CB_ROW
 }
 
 }  // namespace
