@@ -194,3 +194,46 @@ def test_forward_row_ranges_match_whole(lq, torch):
         Ha, ta = lq.qlora_forward(qw, Xd[:m1].contiguous(), Ad, Bd, 32.0, out_dtype=torch.float32)
         Hb, tb = lq.qlora_forward(qw, Xd[m1:].contiguous(), Ad, Bd, 32.0, out_dtype=torch.float32)
         assert torch.equal(torch.cat([Ha, Hb]), H) and torch.equal(torch.cat([ta, tb]), t)
+
+
+@pytest.mark.parametrize("spacing", ["wide", "close"])
+def test_codebook_quantize_at_thresholds(lq, torch, spacing):
+    """Weights whose quotient w / c lands on one of the row's thresholds, or
+    a few float32 steps either side of it (block constant c: the block's own
+    absmax, stored in the block). Wide spacing (thresholds more than 1/64
+    apart) takes the code search through the row's bin table and its exact
+    fallback near a threshold; close spacing (two thresholds within 1/128)
+    counts thresholds directly. Both must match the oracle bit for bit
+    (LowRA page, section 4.1: thresholds per output channel)."""
+    rng = np.random.default_rng(41 if spacing == "wide" else 42)
+    N, K = 96, 512
+    bits = np.tile(np.array([1, 2, 3, 4], dtype=np.uint8), N // 4)
+    T = np.full((N, 15), 3.0, dtype=np.float32)
+    W = np.zeros((N, K), dtype=np.float32)
+    for i, b in enumerate(bits):
+        nt = (1 << int(b)) - 1
+        if spacing == "wide":
+            t = np.sort(rng.uniform(-0.9, 0.9, nt))
+            while nt > 1 and np.min(np.diff(t)) < 0.05:
+                t = np.sort(rng.uniform(-0.9, 0.9, nt))
+        else:
+            t = np.sort(rng.uniform(-0.9, 0.9, nt))
+            if nt > 1:
+                t[1] = t[0] + 1.0 / 256          # two thresholds in one bin
+                t = np.sort(t)
+        T[i, :nt] = t.astype(np.float32)
+        for blk in range(K // 64):
+            c = np.float32(rng.uniform(0.01, 0.3))
+            vals = []
+            for tk in T[i, :nt]:
+                w0 = np.float32(tk * c)
+                vals += [w0, np.nextafter(w0, np.float32(1)), np.nextafter(w0, np.float32(-1)),
+                         np.nextafter(np.nextafter(w0, np.float32(1)), np.float32(1))]
+            vals = np.array(vals[:63], dtype=np.float32)
+            W[i, blk * 64:blk * 64 + vals.size] = vals
+            W[i, blk * 64 + vals.size:blk * 64 + 63] = (c * rng.uniform(-1, 1, 63 - vals.size)).astype(np.float32)
+            W[i, blk * 64 + 63] = c
+    codes, absmax, _ = lq.quantize_codebook(dev(torch, W), dev(torch, bits), dev(torch, T))
+    packed, cc, _ = codebook.quantize(W, bits, T)
+    assert np.array_equal(host(absmax), cc)
+    assert np.array_equal(host(codes)[:packed.size], packed)
