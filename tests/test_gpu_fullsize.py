@@ -167,6 +167,46 @@ def test_prefill_layer_full_size(lq, torch, name):
     assert layer.rel_frobenius(bf16_to_f32(gx)[np.ix_(ms, cols)], gref) <= BF16_TOL
 
 
+def test_q_proj_forward_f32_elementwise_bound(lq, torch):
+    """q_proj forward with float32 H (4096 x 4096, 2048 tokens, r = 16) on
+    sampled (token, output) pairs, each element within a worst-case rounding
+    bound of the exact result from the bf16 inputs and the dequantized weight
+    (QLoRA page, eq. 5: H = X W'^T + s X A^T B^T). The MFMAs multiply bf16
+    pairs exactly and add in float32, so a K-term sum errs by at most
+    (K + c) u sum |x w'| (u = 2^-24) in any order; the LoRA term goes through
+    t = X A^T (same bound, r sums of K terms) and the hi/lo bfloat16 split of
+    s t (relative error below 2^-16), then a 2r-term sum."""
+    L = syn.LAYERS["q_proj"]
+    N, K, M, r, alpha = L.N, L.K, L.M, L.r, L.alpha
+    s = alpha / r
+    u = 2.0 ** -24
+    rng = np.random.default_rng(77)
+    W = syn.weight(L)
+    _, _, cp = oracle_constants(W)
+    _, _, qw = quantize_on_gpu(lq, torch, W)
+    X, A, B = syn.activations(L), syn.lora_a(L), syn.lora_b(L)
+    H, t = lq.qlora_forward(qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), alpha,
+                            out_dtype=torch.float32)
+    rows = sample(rng, N, 64)
+    ms = sample(rng, M, 64)
+    _, _, wd = oracle_rows(W, rows, cp)
+    x = X.f32[ms].astype(np.float64)
+    w = wd.astype(np.float64)
+    a = A.f32.astype(np.float64)
+    b = B.f32[rows].astype(np.float64)
+    t_ex = x @ a.T                                      # [m, r]
+    h_ex = x @ w.T + s * (t_ex @ b.T)
+    sxw = np.abs(x) @ np.abs(w).T
+    sxa = np.abs(x) @ np.abs(a).T                       # [m, r]
+    dt = (K + 4) * u * sxa + 2.0 ** -16 * np.abs(t_ex) * (1 + (K + 4) * u)
+    lora_abs = np.abs(t_ex) @ np.abs(b).T
+    bound = (K + 2 * r + 8) * u * (sxw + abs(s) * (lora_abs + dt @ np.abs(b).T)) + abs(s) * (dt @ np.abs(b).T)
+    err = np.abs(host(H)[np.ix_(ms, rows)].astype(np.float64) - h_ex)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    # the bound is loose by design (worst case); the typical error is far below it
+    assert float(np.median(err / bound)) < 0.05
+
+
 @pytest.fixture(scope="module")
 def decode_case(lq, torch):
     L = syn.LAYERS["decode"]
@@ -252,8 +292,9 @@ def test_loftq_full_size(lq, torch):
     oracle with the whole tensor's double quantization); its residual is
     bit-exact on the same rows; the rank-16 SVD of the step-1 residual is
     checked against the exact singular values of that residual (Ritz values
-    never above them, error left within 2e-3 of the optimum); five steps
-    leave less error than one."""
+    never above them and within 3% below: 8 power steps on a 2r-column
+    sketch separate this residual's flat spectrum that far; error left within
+    2e-3 of the optimum); five steps leave less error than one."""
     L = syn.LAYERS["q_proj"]
     N, K, r, l, q = L.N, L.K, L.r, 2 * L.r, 8
     W = syn.weight(L)
@@ -271,7 +312,7 @@ def test_loftq_full_size(lq, torch):
     assert np.array_equal(R1[rows].view(np.uint32), (W[rows] - wd_rows).view(np.uint32))
     so = np.linalg.svd(R1.astype(np.float64), compute_uv=False)
     s = host(s1)
-    assert np.all(s <= so[:r] * (1 + 1e-5)) and np.all(s >= 0.9 * so[:r])
+    assert np.all(s <= so[:r] * (1 + 1e-5)) and np.all(s >= 0.97 * so[:r])
     total = float(np.sum(so ** 2))
     opt = total - float(np.sum(so[:r] ** 2))
     assert opt <= host(ob1)[0] <= opt * (1 + 2e-3)
