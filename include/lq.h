@@ -231,9 +231,10 @@ size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * dequantized inside the GEMM (M <= 16 and K <= 33728 use the memory-bound
  * GEMV kernel, other shapes the MFMA GEMM; the environment variable
  * LQ_FORCE_PATH=gemm selects the GEMM at any M, a testing aid). A codebook
- * weight is first dequantized into the
- * workspace by its per-channel dequantization kernel ([LowRA] section 3),
- * then multiplied by the MFMA GEMM.
+ * weight at M <= 16 (K <= 32576) goes through its own GEMV kernel, which
+ * reads the bit-planes directly; at other shapes it is first dequantized
+ * into the workspace by its per-channel dequantization kernel ([LowRA]
+ * section 3), then multiplied by the MFMA GEMM.
  *   X  [M, K] bf16;  A [r, K] bf16;  B [N, r] bf16
  *   H  [M, N] of h_dtype (LQ_BF16 or LQ_F32), written
  *   t_save [M, r] float32, written if not NULL (for the backward)
@@ -260,16 +261,16 @@ int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for lq_dequant_gemm with M tokens and rank r: N * K * 2
- * bytes (rounded up to 256) for the dequantized weight of a codebook weight;
- * 0 for NF4 weights (the kernels form the LoRA-segment operands themselves). */
+ * bytes (rounded up to 256) for the dequantized weight of a codebook weight
+ * on the GEMM path; 0 for NF4 weights (the kernels form the LoRA-segment
+ * operands themselves) and for a codebook weight on its GEMV path. */
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
  * Second stage of the forward ([QLoRA] introduction): given t = X A^T,
  * H = X W'^T + (alpha / r) t B^T with W' dequantized inside the kernel (the
- * GEMV kernel for M <= 16 and K <= 33728 with NF4, else the MFMA GEMM, as for
- * lq_qlora_forward; a codebook weight is
- * dequantized into the workspace first). Arguments as lq_qlora_forward;
+ * GEMV kernels for M <= 16, else the MFMA GEMM, as for lq_qlora_forward; on
+ * the GEMM path a codebook weight is dequantized into the workspace first). Arguments as lq_qlora_forward;
  * t [M, r] float32 is read. The workspace (caller-owned,
  * lq_dequant_gemm_workspace bytes) receives the dequantized codebook weight;
  * it may be NULL when that size is 0.
