@@ -178,16 +178,14 @@ int run_backward(const QWeight& q, const uint16_t* X, const uint16_t* G, int64_t
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  // dB = s G^T t and dA = s u^T X in one launch, then grad_X
+  // partial sums of dB = s G^T t and dA = s u^T X in one launch
   SplitJobDesc job_b, job_a;
   const ColSkinnyReq req_b{pt2_t, G, q.N, scale, dB, true, part_b};
   const ColSkinnyReq req_a{pt2_u, X, q.K, scale, dA, false, part_a};
   e = launch_col_skinny(dB ? &req_b : nullptr, dA ? &req_a : nullptr, M, r, &job_b, &job_a, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  if (grad_X) {
-    e = launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s);
-    if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  }
+  // grad_X; its workgroups also finish dB and dA from the partial sums
+  if (grad_X) return launch_status(launch_gemm_bwd(q, G, M, u, A, r, scale, grad_X, gws, s, &job_b, &job_a));
   return launch_status(launch_reduce_splits2(job_b, job_a, s));
 }
 

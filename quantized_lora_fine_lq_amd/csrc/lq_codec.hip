@@ -38,7 +38,7 @@ namespace {
 // rounded quotient w / c -- the quotient is computed exactly and used
 // instead, so every code equals the one from IEEE division.
 // ---------------------------------------------------------------------------
-constexpr int kQuantPasses = 4;   // 16 blocks per pass per 256-thread WG
+constexpr int kQuantPasses = 4;   // 16 blocks per pass per 256-thread WG (profiling pass)
 
 template <typename Tin> struct Load4;
 template <> struct Load4<float> {
@@ -71,7 +71,7 @@ __device__ __forceinline__ uint32_t nf4_code(float w, float c, float r, bool fas
   return (uint32_t)(sB[jj] + (x > sT[jj] ? 1 : 0));
 }
 
-template <typename Tin>
+template <typename Tin, int P>
 __global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W, int64_t n_blocks,
                                                       uint8_t* __restrict__ codes,
                                                       float* __restrict__ absmax, Nf4Lut lut) {
@@ -83,22 +83,22 @@ __global__ __launch_bounds__(256) void k_quantize_nf4(const Tin* __restrict__ W,
   }
   __syncthreads();
   const int i16 = threadIdx.x & 15;
-  const int64_t blk0 = (int64_t)blockIdx.x * (16 * kQuantPasses) + (threadIdx.x >> 4);
-  f32x4_t v[kQuantPasses];
+  const int64_t blk0 = (int64_t)blockIdx.x * (16 * P) + (threadIdx.x >> 4);
+  f32x4_t v[P];
 #pragma unroll
-  for (int p = 0; p < kQuantPasses; ++p) {
+  for (int p = 0; p < P; ++p) {
     const int64_t blk = blk0 + 16 * p;
     v[p] = (blk < n_blocks) ? Load4<Tin>::go(W + blk * 64 + i16 * 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #ifdef LQ_DEBUG
 #pragma unroll
-  for (int p = 0; p < kQuantPasses; ++p)
+  for (int p = 0; p < P; ++p)
     if (!(__builtin_isfinite(v[p].x) && __builtin_isfinite(v[p].y) && __builtin_isfinite(v[p].z) &&
           __builtin_isfinite(v[p].w)))
       dbg_flag(LQ_DBG_NONFINITE);
 #endif
 #pragma unroll
-  for (int p = 0; p < kQuantPasses; ++p) {
+  for (int p = 0; p < P; ++p) {
     const int64_t blk = blk0 + 16 * p;
     float m = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
     m = row16_max(m);
@@ -632,18 +632,26 @@ __global__ __launch_bounds__(256) void k_quantize_codebook(const Tin* __restrict
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Passes of 16 blocks per workgroup: 2 up to 1.5 M blocks (more, shorter
+// workgroups: at 0.26 M and 0.7 M blocks 16.9 and 41.1 us against 18.9 and
+// 43.0 us with 4), 4 above (at 3.7 M blocks 192 against 197 us).
+template <typename Tin>
+static void launch_quantize_nf4_t(const Tin* W, int64_t n_blocks, uint8_t* codes, float* absmax, hipStream_t s) {
+  const Nf4Lut& lut = tables().lut;
+  if (n_blocks <= (int64_t)1536 * 1024)
+    hipLaunchKernelGGL((k_quantize_nf4<Tin, 2>), dim3((unsigned)((n_blocks + 31) / 32)), dim3(256), 0, s, W, n_blocks,
+                       codes, absmax, lut);
+  else
+    hipLaunchKernelGGL((k_quantize_nf4<Tin, 4>), dim3((unsigned)((n_blocks + 63) / 64)), dim3(256), 0, s, W, n_blocks,
+                       codes, absmax, lut);
+}
+
 hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8_t* codes,
                                float* absmax, hipStream_t s) {
-  const int64_t per_wg = 16 * kQuantPasses;
-  LQ_DASSERT(n_blocks > 0 && (n_blocks + per_wg - 1) / per_wg < (int64_t(1) << 31));
-  const dim3 grid((unsigned)((n_blocks + per_wg - 1) / per_wg));
-  const Nf4Lut& lut = tables().lut;
-  if (dtype == LQ_F32)
-    hipLaunchKernelGGL(k_quantize_nf4<float>, grid, dim3(256), 0, s, (const float*)W, n_blocks, codes, absmax, lut);
-  else if (dtype == LQ_BF16)
-    hipLaunchKernelGGL(k_quantize_nf4<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)W, n_blocks, codes, absmax, lut);
-  else
-    hipLaunchKernelGGL(k_quantize_nf4<_Float16>, grid, dim3(256), 0, s, (const _Float16*)W, n_blocks, codes, absmax, lut);
+  LQ_DASSERT(n_blocks > 0 && (n_blocks + 31) / 32 < (int64_t(1) << 31));
+  if (dtype == LQ_F32) launch_quantize_nf4_t((const float*)W, n_blocks, codes, absmax, s);
+  else if (dtype == LQ_BF16) launch_quantize_nf4_t((const uint16_t*)W, n_blocks, codes, absmax, s);
+  else launch_quantize_nf4_t((const _Float16*)W, n_blocks, codes, absmax, s);
   return hipGetLastError();
 }
 

@@ -39,6 +39,48 @@ constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int PITCH = BK + 8;  // bf16 per LDS row: 144 bytes, conflict-free b128 access
 constexpr int GEMM_THREADS = 512;
 
+// Split reductions of the backward (dB and dA): for each output i of a job,
+// out = scale * sum_s (part[s][i] + part[s][i + pair]) in split order, rows x
+// cols per job, optionally written transposed ([cols, rows]). Run by the
+// grad_X GEMM's workgroups after their tiles, or by k_reduce_splits2 when
+// there is no grad_X.
+struct SplitJob {
+  const float* part;
+  int splits;
+  int64_t rows, cols, srows, pair;
+  float scale;
+  float* out;
+  int transposed;
+};
+
+__device__ __forceinline__ void reduce_one(const SplitJob& jb, int64_t i) {
+  const int64_t sn = jb.srows * jb.cols;
+  const float* ps = jb.part + i;
+  float acc = 0.0f;
+  int s = 0;
+  for (; s + 4 <= jb.splits; s += 4) {   // four loads in flight, added in order
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* q = ps + (int64_t)(s + u) * sn;
+      v[u] = jb.pair ? q[0] + q[jb.pair] : q[0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += v[u];
+  }
+  for (; s < jb.splits; ++s) {
+    const float* q = ps + (int64_t)s * sn;
+    acc += jb.pair ? q[0] + q[jb.pair] : q[0];
+  }
+  acc *= jb.scale;
+  if (jb.transposed) {
+    const int64_t rr = i / jb.cols, cc = i % jb.cols;
+    jb.out[cc * jb.rows + rr] = acc;
+  } else {
+    jb.out[i] = acc;
+  }
+}
+
 struct GemmParams {
   const uint16_t* A;   // [M, Kc] bf16, row stride Kc
   int64_t M, Ncols, Kc;
@@ -53,6 +95,8 @@ struct GemmParams {
   QWeight w;
   Nf4Levels lv;
   const uint16_t* wbf; // dequantized weight [N, K] bf16 (codebook format), else null
+  SplitJob red[2];     // split reductions to run after the tiles (backward), n = rows * cols each
+  int64_t red_n[2];    // 0: none
 };
 
 __device__ __forceinline__ void zero(u32x4_t& v) { v = u32x4_t{0u, 0u, 0u, 0u}; }
@@ -359,6 +403,16 @@ struct ProdBwdBF16 {
   }
 };
 
+// The split reductions handed to this launch, grid-stride over all its
+// threads (each thread calls this exactly once, after its tile work).
+__device__ __forceinline__ void gemm_reduce_tail(const GemmParams& p) {
+  const int64_t n = p.red_n[0] + p.red_n[1];
+  for (int64_t i = (int64_t)blockIdx.x * GEMM_THREADS + threadIdx.x; i < n; i += (int64_t)gridDim.x * GEMM_THREADS) {
+    if (i < p.red_n[0]) reduce_one(p.red[0], i);
+    else reduce_one(p.red[1], i - p.red_n[0]);
+  }
+}
+
 template <class Prod, bool OUT_F32, bool TAIL>
 __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   // one LDS object with the pair table first: at LDS address 0 a lookup
@@ -516,9 +570,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
         *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(p.out) + grow * p.Ncols + gcol) =
             *reinterpret_cast<const u32x4_t*>(sC + row * CP + 8 * c);
     }
+    gemm_reduce_tail(p);
     return;
   }
-  if (kh != 0) return;
+  if (kh != 0) {
+    gemm_reduce_tail(p);
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -534,6 +592,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
         }
       }
     }
+  gemm_reduce_tail(p);
 }
 
 // ===========================================================================
@@ -1206,46 +1265,6 @@ __global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_
   }
 }
 
-// Two split reductions in one launch (dB and dA of the backward): for each
-// i < n1 + n2, out = scale * sum_s (part[s][i] + part[s][i + pair]) in split
-// order, rows x cols per job, optionally written transposed ([cols, rows]).
-struct SplitJob {
-  const float* part;
-  int splits;
-  int64_t rows, cols, srows, pair;
-  float scale;
-  float* out;
-  int transposed;
-};
-
-__device__ __forceinline__ void reduce_one(const SplitJob& jb, int64_t i) {
-  const int64_t sn = jb.srows * jb.cols;
-  const float* ps = jb.part + i;
-  float acc = 0.0f;
-  int s = 0;
-  for (; s + 4 <= jb.splits; s += 4) {   // four loads in flight, added in order
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float* q = ps + (int64_t)(s + u) * sn;
-      v[u] = jb.pair ? q[0] + q[jb.pair] : q[0];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc += v[u];
-  }
-  for (; s < jb.splits; ++s) {
-    const float* q = ps + (int64_t)s * sn;
-    acc += jb.pair ? q[0] + q[jb.pair] : q[0];
-  }
-  acc *= jb.scale;
-  if (jb.transposed) {
-    const int64_t rr = i / jb.cols, cc = i % jb.cols;
-    jb.out[cc * jb.rows + rr] = acc;
-  } else {
-    jb.out[i] = acc;
-  }
-}
-
 __global__ __launch_bounds__(256) void k_reduce_splits2(SplitJob j1, SplitJob j2) {
   const int64_t n1 = j1.out ? j1.rows * j1.cols : 0;
   const int64_t n2 = j2.out ? j2.rows * j2.cols : 0;
@@ -1388,6 +1407,8 @@ static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, in
   p.w = w;
   p.lv = tables().lv;
   p.wbf = nullptr;
+  p.red[0] = p.red[1] = SplitJob{nullptr, 0, 0, 0, 0, 0, 0.0f, nullptr, 0};
+  p.red_n[0] = p.red_n[1] = 0;
   return p;
 }
 
@@ -1425,9 +1446,17 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
 }
 
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
-                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st) {
+                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st,
+                           const SplitJobDesc* red_a, const SplitJobDesc* red_b) {
   GemmParams p = make_params(w, G, M, w.K, w.N, gX);
   set_lora(p, u, A, r, s, false);
+  const SplitJobDesc* rd[2] = {red_a, red_b};
+  for (int i = 0; i < 2; ++i) {
+    if (!rd[i] || !rd[i]->out) continue;
+    p.red[i] = SplitJob{rd[i]->part, rd[i]->splits, rd[i]->rows, rd[i]->cols, rd[i]->srows, rd[i]->pair,
+                        rd[i]->scale, rd[i]->out, rd[i]->transposed};
+    p.red_n[i] = rd[i]->rows * rd[i]->cols;
+  }
   hipError_t e = hipSuccess;
   const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
   LQ_DASSERT(M > 0 && w.N % 8 == 0 && w.K % 64 == 0 && tiles > 0 && tiles < (int64_t(1) << 31));

@@ -181,8 +181,12 @@ size_t gemm_ws_bytes(const QWeight& w, int64_t M, int r, bool fwd);
 hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype, uint16_t* ws,
                            hipStream_t st);
+// With red_a / red_b (may be null), the GEMM's workgroups also run those
+// split reductions after their tiles (the partial sums must be complete
+// before the launch), which saves the reduction's own launch.
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
-                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st);
+                           const uint16_t* A, int r, float s, uint16_t* gX, uint16_t* ws, hipStream_t st,
+                           const SplitJobDesc* red_a = nullptr, const SplitJobDesc* red_b = nullptr);
 // The decode GEMV handles NF4 weights whose per-workgroup constant table
 // fits in LDS (K <= 33728: one row group of 16 rows); others use the GEMM.
 bool gemv_supported(const QWeight& w);
