@@ -314,13 +314,13 @@ __global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, 
 }
 
 // ---------------------------------------------------------------------------
-// Dequant to bfloat16. A wave covers 2048 consecutive elements in 4 passes;
+// Dequant to bfloat16. A wave covers 512 P consecutive elements in P passes;
 // in pass d lane l handles elements 512d + 8l .. +7 (one dword of codes), so
 // each code load reads 256 contiguous bytes and each 16-byte store instruction
 // writes 1 KB contiguous. NF4: a 256-entry table in LDS maps a code byte to
 // its two float32 levels.
 // ---------------------------------------------------------------------------
-template <bool DQ>
+template <bool DQ, int P>
 __global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__ codes, QConst qc,
                                                      int64_t n, uint16_t* __restrict__ out,
                                                      Nf4Levels lv) {
@@ -328,13 +328,13 @@ __global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__
   pair[threadIdx.x] = f32x2_t{lv.q[threadIdx.x >> 4], lv.q[threadIdx.x & 15]};
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int64_t e_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2048 + 8 * lane;
+  const int64_t e_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (512 * P) + 8 * lane;
   const float mean = DQ ? *qc.dq_mean : 0.0f;
-  uint32_t w[4];
-  float c0[4], s2[4];
-  uint32_t q8[4];
+  uint32_t w[P];
+  float c0[P], s2[P];
+  uint32_t q8[P];
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < P; ++d) {
     const int64_t e = min(e_base + 512 * d, n - 8);   // n % 64 == 0; clamped lanes do not store
     w[d] = *reinterpret_cast<const uint32_t*>(codes + e / 2);
     const int64_t blk = e >> 6;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__
     }
   }
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int d = 0; d < P; ++d) {
     const int64_t e = e_base + 512 * d;
     const float cp = DQ ? __builtin_fmaf(e4m3_decode(q8[d]), s2[d], mean) : c0[d];
     u32x4_t o;
@@ -658,7 +658,9 @@ hipError_t launch_quantize_nf4(const void* W, int dtype, int64_t n_blocks, uint8
 static int64_t profile_grid(int64_t n_blocks) {
   const int64_t per_tile = 16 * kQuantPasses;
   const int64_t n_tiles = (n_blocks + per_tile - 1) / per_tile;
-  return std::min<int64_t>(n_tiles, 2048);   // 8 workgroups of 4 waves per CU
+  // 8 workgroups of 4 waves per CU; past 32 k tiles 32 per CU (decode size:
+  // 202 -> 194 us; at 4 k and 11 k tiles the larger grid was slower)
+  return std::min<int64_t>(n_tiles, n_tiles > 32768 ? 8192 : 2048);
 }
 
 size_t profile_ws_doubles(int64_t n_blocks) { return (size_t)(2 * profile_grid(n_blocks)); }
@@ -725,9 +727,17 @@ hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
   LQ_DASSERT(w.N > 0 && w.K % 64 == 0 && (w.N * w.K + 8191) / 8192 < (int64_t(1) << 31));
   if (w.format == LQ_FMT_NF4) {
     const int64_t n = w.N * w.K;
-    const dim3 grid((unsigned)((n + 8191) / 8192));
-    if (w.qc.absmax) hipLaunchKernelGGL(k_dequant_nf4<false>, grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
-    else hipLaunchKernelGGL(k_dequant_nf4<true>, grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+    // 8 passes per wave up to 24 M weights (fewer, longer workgroups: 10.1
+    // against 11.0 us at 16.8 M), 4 above (2 and 16 passes were slower)
+    const bool small = n <= (int64_t)24 << 20;
+    const dim3 grid((unsigned)((n + (small ? 16383 : 8191)) / (small ? 16384 : 8192)));
+    if (small) {
+      if (w.qc.absmax) hipLaunchKernelGGL((k_dequant_nf4<false, 8>), grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+      else hipLaunchKernelGGL((k_dequant_nf4<true, 8>), grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+    } else {
+      if (w.qc.absmax) hipLaunchKernelGGL((k_dequant_nf4<false, 4>), grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+      else hipLaunchKernelGGL((k_dequant_nf4<true, 4>), grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
+    }
   } else {
     const int64_t n_groups = w.N * w.K / 8;
     hipLaunchKernelGGL(k_dequant_codebook, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0,
