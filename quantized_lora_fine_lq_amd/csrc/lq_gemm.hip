@@ -599,10 +599,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
 // Decode GEMV (M <= 16), NF4. MFMA 16x16x32 with the tokens as the 16 A-rows
 // (rows >= M repeat row M-1; their outputs are not stored) and 16 weight rows
 // per MFMA tile. A workgroup owns RG row groups (16 RG weight rows); its 8
-// waves split the K/128 stages evenly. In a stage, lane (li, lg) of row group
+// waves share the K/128 stages. In a stage, lane (li, lg) of row group
 // g takes the 32 codes k = 32 lg + [0, 32) of row 16 g + li (one 16-byte
 // load, inside one 64-block) and the same k of token li (from global
-// memory, L2-resident; one X fragment serves all row groups). Codes are
+// memory, L2-resident; one X fragment serves all row groups). Wave w takes
+// stages w, w + 8, w + 16, ... Codes are
 // dequantized straight into MFMA B registers through a 256-entry LDS table
 // of level pairs (one 8-byte lookup per code byte). The block constants of
 // the workgroup's rows are decoded once into LDS at the start, so the main
@@ -754,7 +755,10 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
   const int nb = (int)(K / 64);
   const int pitch = nb + 1;                // odd pitch: the 16 rows of a lookup hit distinct banks
   const int ns = (int)((K + 127) / 128);   // stages; the last one is half empty when nb is odd
-  const int e0 = (int)((int64_t)wave * ns / GV_WAVES), e1 = (int)((int64_t)(wave + 1) * ns / GV_WAVES);
+  // stages wave, wave + 8, wave + 16, ...: the two stages that share a
+  // 128-byte line of a code row (stages 2j and 2j + 1) are read by two waves
+  // in the same iteration, so the line is fetched once
+  const int nsw = (ns - wave + GV_WAVES - 1) / GV_WAVES;
 
   const uint8_t* crow[RG];
 #pragma unroll
@@ -763,7 +767,7 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
 
   // first stage's loads go out before the constant table is built
   GvStage<RG> s0, s1;
-  gv_load<RG>(crow, xrow, lg, e0, e1, ns, nb, s0);
+  gv_load<RG>(crow, xrow, lg, wave, ns, ns, nb, s0);
 
   if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
   const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
@@ -819,11 +823,11 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
   // The scheduling barriers keep each stage's loads where they are issued
   // (left alone, the compiler sinks them next to their first use and the
   // wave then waits for them).
-  for (int st = e0; st < e1; st += 2) {
-    gv_load<RG>(crow, xrow, lg, st + 1, e1, ns, nb, s1);
+  for (int i = 0; i < nsw; i += 2) {
+    gv_load<RG>(crow, xrow, lg, wave + GV_WAVES * (i + 1), ns, ns, nb, s1);
     __builtin_amdgcn_sched_barrier(0);
     gv_compute<RG>(s0, sPair, sC, pitch, li, acc);
-    gv_load<RG>(crow, xrow, lg, st + 2, e1, ns, nb, s0);
+    gv_load<RG>(crow, xrow, lg, wave + GV_WAVES * (i + 2), ns, ns, nb, s0);
     __builtin_amdgcn_sched_barrier(0);
     gv_compute<RG>(s1, sPair, sC, pitch, li, acc);
   }
@@ -934,10 +938,13 @@ __device__ __forceinline__ f32x4_t cb_body(const GemvParams& p, unsigned char* l
   const int64_t N = p.w.N, K = p.w.K;
   const int nb = (int)(K / 64), pitch = nb + 1;
   const int ns = (int)((K + 127) / 128);
-  const int e0 = (int)((int64_t)wave * ns / GV_WAVES), e1 = (int)((int64_t)(wave + 1) * ns / GV_WAVES);
+  // stages wave, wave + 8, wave + 16, ...: the two stages that share a
+  // 128-byte line of a code row (stages 2j and 2j + 1) are read by two waves
+  // in the same iteration, so the line is fetched once
+  const int nsw = (ns - wave + GV_WAVES - 1) / GV_WAVES;
 
   CbStage s0, s1;
-  cb_load<PB>(rowp, bw, xrow, lg, e0, e1, ns, nb, s0);   // out before the tables are built
+  cb_load<PB>(rowp, bw, xrow, lg, wave, ns, ns, nb, s0);   // out before the tables are built
   const GvLora lr = gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + li, N - 1));
 
   if (threadIdx.x < 256) sLv[threadIdx.x] = p.w.levels[min(n0 + (threadIdx.x >> 4), N - 1) * 16 + (threadIdx.x & 15)];
@@ -968,11 +975,11 @@ __device__ __forceinline__ f32x4_t cb_body(const GemvParams& p, unsigned char* l
 
   const f32x2_t* tab = sTab + li * CB_TAB;
   f32x4_t acc = gv_lora_mfma(lr, f32x4_t{0.f, 0.f, 0.f, 0.f});
-  for (int st = e0; st < e1; st += 2) {
-    cb_load<PB>(rowp, bw, xrow, lg, st + 1, e1, ns, nb, s1);
+  for (int i = 0; i < nsw; i += 2) {
+    cb_load<PB>(rowp, bw, xrow, lg, wave + GV_WAVES * (i + 1), ns, ns, nb, s1);
     __builtin_amdgcn_sched_barrier(0);
     cb_compute<PB>(s0, tab, sC, pitch, li, acc);
-    cb_load<PB>(rowp, bw, xrow, lg, st + 2, e1, ns, nb, s0);
+    cb_load<PB>(rowp, bw, xrow, lg, wave + GV_WAVES * (i + 2), ns, ns, nb, s0);
     __builtin_amdgcn_sched_barrier(0);
     cb_compute<PB>(s1, tab, sC, pitch, li, acc);
   }
