@@ -127,8 +127,7 @@ size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
 // u, recomputed t, B^T, split t and u, partial sums of dB and of dA, GEMM
 // workspace
 size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
-  return 2 * align_up((size_t)M * r * sizeof(float)) + align_up((size_t)w.N * r * sizeof(uint16_t)) +
-         2 * align_up((size_t)2 * r * split_rows(M) * sizeof(uint16_t)) +
+  return 2 * align_up((size_t)M * r * sizeof(float)) + (r > 16 ? align_up((size_t)w.N * r * sizeof(uint16_t)) : 0) +
          align_up(col_skinny_ws_floats(M, w.N, r) * sizeof(float)) +
          align_up(col_skinny_ws_floats(M, w.K, r) * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
 }
@@ -157,9 +156,7 @@ int run_backward(const QWeight& q, const uint16_t* X, const uint16_t* G, int64_t
   Carver cv(workspace, ws_bytes);
   float* u = cv.take<float>((size_t)M * r);
   float* t_ws = cv.take<float>((size_t)M * r);
-  uint16_t* Bt = cv.take<uint16_t>((size_t)q.N * r);
-  uint16_t* pt2_t = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
-  uint16_t* pt2_u = cv.take<uint16_t>((size_t)2 * r * split_rows(M));
+  uint16_t* Bt = r > 16 ? cv.take<uint16_t>((size_t)q.N * r) : nullptr;
   float* part_b = cv.take<float>(col_skinny_ws_floats(M, q.N, r));
   float* part_a = cv.take<float>(col_skinny_ws_floats(M, q.K, r));
   uint16_t* gws = cv.take<uint16_t>(gemm_ws_bytes(q, M, r, false) / sizeof(uint16_t));
@@ -170,18 +167,22 @@ int run_backward(const QWeight& q, const uint16_t* X, const uint16_t* G, int64_t
   hipError_t e = hipSuccess;
   const float* t = t_saved;
   if (!t) {
-    e = launch_row_skinny(X, M, q.K, A, r, t_ws, nullptr, s);
+    e = launch_row_skinny(X, M, q.K, A, r, t_ws, s);
     if (e != hipSuccess) return LQ_ERR_LAUNCH;
     t = t_ws;
   }
-  e = launch_bwd_prep(B, q.N, r, Bt, t, M, pt2_t, s);
-  if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  e = launch_row_skinny(G, M, q.N, Bt, r, u, dA ? pt2_u : nullptr, s);
+  // u = G B: B read as given ([N, r]) up to r = 16, else transposed first
+  if (r <= 16) {
+    e = launch_row_skinny_rt(G, M, q.N, B, r, u, s);
+  } else {
+    e = launch_transpose_u16(B, q.N, r, Bt, s);
+    if (e == hipSuccess) e = launch_row_skinny(G, M, q.N, Bt, r, u, s);
+  }
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   // partial sums of dB = s G^T t and dA = s u^T X in one launch
   SplitJobDesc job_b, job_a;
-  const ColSkinnyReq req_b{pt2_t, G, q.N, scale, dB, true, part_b};
-  const ColSkinnyReq req_a{pt2_u, X, q.K, scale, dA, false, part_a};
+  const ColSkinnyReq req_b{t, G, q.N, scale, dB, true, part_b};
+  const ColSkinnyReq req_a{u, X, q.K, scale, dA, false, part_a};
   e = launch_col_skinny(dB ? &req_b : nullptr, dA ? &req_a : nullptr, M, r, &job_b, &job_a, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   // grad_X; its workgroups also finish dB and dA from the partial sums
@@ -309,7 +310,7 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
-  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, nullptr, s);
+  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (gemv) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
   else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, gws, s);
@@ -325,7 +326,7 @@ int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int
   if (M <= 0 || K <= 0 || K % 8 != 0 || r < 1 || r > 128) return LQ_ERR_SHAPE;
   (void)workspace;
   (void)ws_bytes;
-  return launch_status(launch_row_skinny(X, M, K, A, r, t, nullptr, (hipStream_t)stream));
+  return launch_status(launch_row_skinny(X, M, K, A, r, t, (hipStream_t)stream));
 }
 
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r) {

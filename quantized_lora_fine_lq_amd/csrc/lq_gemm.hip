@@ -1042,29 +1042,38 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_codebook(GemvParams p
 // and of R row 16jt + li, straight into MFMA registers, so the four lanes of
 // a row read whole 128-byte lines (R is small and stays in cache). The W
 // partial sums meet in LDS and are added in wave order, so no second pass is
-// needed. When pt2 is given, the result is also written split and
-// transposed for the column form: pt2 [2r][Mp] bf16 = [hi(out)^T ;
-// lo(out)^T], zero for rows M..Mp-1 (the grid then covers Mp rows).
-template <int JT, int W>
+// needed.
+// With RT > 0 the second operand is given transposed, Rt [C, r] (B for
+// u = G B; RT = 1: r % 8 == 0, rows read in 16-byte pieces; RT = 2: any r):
+// per 64-column block and 16 rows j, lane l loads row 64 bk + l of Rt (16
+// values) and writes it as column l of a 16 x 64 tile in the wave's own LDS
+// area, from which the fragments are read as above (no barrier: only the
+// wave itself touches the area, and its LDS operations run in order).
+constexpr int RS_TP = 72;   // bf16 per row of the transposed tile (144 bytes)
+
+template <int JT, int W, int RT>
 __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M, int64_t C,
                                                        const uint16_t* __restrict__ R, int r,
-                                                       float* __restrict__ out, uint16_t* __restrict__ pt2,
-                                                       int64_t Mp) {
-  __shared__ f32x4_t sPart[W][JT][64];
+                                                       float* __restrict__ out) {
+  constexpr int kPart = W * JT * 64 * 16, kTile = RT ? W * 16 * RS_TP * 2 : 0;
+  __shared__ __attribute__((aligned(16))) unsigned char sRaw[kPart > kTile ? kPart : kTile];
+  f32x4_t (*sPart)[JT][64] = reinterpret_cast<f32x4_t (*)[JT][64]>(sRaw);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint16_t* sT = reinterpret_cast<uint16_t*>(sRaw) + wave * 16 * RS_TP;   // RT: this wave's 16 x 64 tile
   const int li = lane & 15, lg = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const uint16_t* qrow = Q + min(row0 + li, M - 1) * C + 16 * lg;   // rows past M: not stored
   const uint16_t* rrow[JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) rrow[jt] = R + (int64_t)min(16 * jt + li, r - 1) * C + 16 * lg;
+  for (int jt = 0; jt < JT; ++jt) rrow[jt] = RT ? R : R + (int64_t)min(16 * jt + li, r - 1) * C + 16 * lg;
   const int64_t blocks = (C + 63) / 64;
   const int64_t per = (blocks + W - 1) / W;
   const int64_t b_begin = min(blocks, wave * per), b_end = min(blocks, b_begin + per);
   f32x4_t acc[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = JT <= 2 ? 4 : (JT <= 4 ? 2 : 1);   // 64-column blocks with loads in flight together
+  // 64-column blocks with loads in flight together
+  constexpr int U = RT ? (JT == 1 ? 4 : (JT == 2 ? 2 : 1)) : (JT <= 2 ? 4 : (JT <= 4 ? 2 : 1));
   for (int64_t bk = b_begin; bk < b_end; bk += U) {
     u32x4_t a[U][2], b[U][2][JT];
 #pragma unroll
@@ -1075,10 +1084,51 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
         const bool ok = bk + u < b_end && cc + 16 * lg + 8 <= C;
         const int64_t off = ok ? cc : -16 * lg;     // a lane past the end reads columns 0..7 and adds 0
         a[u][h] = ld16(qrow + off);
+        if constexpr (!RT) {
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) b[u][h][jt] = ld16(rrow[jt] + off);
+          for (int jt = 0; jt < JT; ++jt) b[u][h][jt] = ld16(rrow[jt] + off);
+        }
         if (!ok) zero(a[u][h]);
       }
+    if constexpr (RT) {
+      // rows 64 (bk + u) + lane of Rt, 16 values per jt (zero past C or r)
+      u32x4_t t[U][JT][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = 64 * (bk + u) + lane;
+        const bool live = bk + u < b_end && c < C;
+        const uint16_t* src = R + (live ? c : 0) * r;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int j0 = 16 * jt + 8 * q;
+            if constexpr (RT == 1) {
+              if (live && j0 < r) t[u][jt][q] = ld16(src + j0);
+              else zero(t[u][jt][q]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = (live && j0 + 2 * e < r) ? src[j0 + 2 * e] : 0u;
+                const uint32_t hi = (live && j0 + 2 * e + 1 < r) ? src[j0 + 2 * e + 1] : 0u;
+                t[u][jt][q][e] = lo | (hi << 16);
+              }
+            }
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              sT[(8 * q + e) * RS_TP + lane] = (uint16_t)(t[u][jt][q][e >> 1] >> (16 * (e & 1)));
+#pragma unroll
+          for (int h = 0; h < 2; ++h) b[u][h][jt] = ld16(sT + li * RS_TP + 16 * lg + 8 * h);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -1088,6 +1138,7 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
           acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][h]), as_bf16x8(b[u][h][jt]), acc[jt], 0,
                                                             0, 0);
   }
+  if constexpr (RT) __syncthreads();   // the partial sums reuse the tiles' LDS
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) sPart[wave][jt][lane] = acc[jt];
   __syncthreads();
@@ -1108,33 +1159,6 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
     for (int v = 0; v < 4; ++v) {
       const int64_t row = row0 + 4 * (ln >> 4) + v;
       if (row < M) out[row * r + j] = sum[v];
-      if (pt2 && row < Mp) {
-        float hi = 0.0f, lo = 0.0f;
-        if (row < M) split_bf16(sum[v], hi, lo);
-        pt2[(int64_t)j * Mp + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
-        pt2[(int64_t)(j + r) * Mp + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
-      }
-    }
-  }
-}
-
-// Set-up of the backward in one launch: Bt = B^T ([N, r] -> [r, N]) for the
-// row form u = G B, and pt2 = [hi(t)^T ; lo(t)^T] ([2r][Mp] bf16, zero for
-// rows M..Mp-1) for the column form dB = s G^T t.
-__global__ __launch_bounds__(256) void k_bwd_prep(const uint16_t* __restrict__ B, int64_t N, int r,
-                                                  uint16_t* __restrict__ Bt, const float* __restrict__ t, int64_t M,
-                                                  int64_t Mp, uint16_t* __restrict__ pt2) {
-  const int64_t nb = N * r, nt = (int64_t)r * Mp;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nb + nt; i += (int64_t)gridDim.x * 256) {
-    if (i < nb) {
-      const int64_t n = i / r, j = i % r;
-      Bt[j * N + n] = B[i];
-    } else {
-      const int64_t k = i - nb, j = k / Mp, m = k % Mp;
-      float hi = 0.0f, lo = 0.0f;
-      if (m < M) split_bf16(t[m * r + j], hi, lo);
-      pt2[j * Mp + m] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
-      pt2[(j + r) * Mp + m] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
     }
   }
 }
@@ -1149,10 +1173,10 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
 }
 
 // Column form: out(j, c) = scale * sum_m P[m][j] Q[m][c] for j < r, P float32
-// [M, r] small, Q bfloat16 [M, C] streamed once. P enters as pt2 = [hi(P)^T ;
-// lo(P)^T] (bfloat16 [2r, Mp], Mp = M rounded up to 32, zero padded; hi + lo
-// carries P to about 2^-17), so an MFMA A fragment is one 16-byte load. The
-// Q tile [32 m x 128 c] goes through LDS and is gathered along m for the B
+// [M, r] small, Q bfloat16 [M, C] streamed once. Per 32 rows of m, P is split
+// into [hi(P)^T ; lo(P)^T] (bfloat16 [2r][32]; hi + lo carries P to about
+// 2^-17) in LDS, so an MFMA A fragment is one 16-byte LDS read. The Q tile
+// [32 m x 128 c] goes through LDS too and is gathered along m for the B
 // fragments. Workgroup: 128 columns x one m-split, wave: 32 columns, MFMA
 // 32x32x16 over the 2r product rows; hi and lo rows are added in registers
 // when r % 32 == 0 or r == 16 (partner row in the same lane), otherwise both
@@ -1161,7 +1185,7 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
 // One job of the column form: product pt2^T-by-Q over its m-splits, in
 // `tiles` column tiles of 128.
 struct ColJob {
-  const uint16_t* pt2;
+  const float* P;
   const uint16_t* Q;
   int64_t C;
   int64_t m_per_split;
@@ -1172,14 +1196,16 @@ struct ColJob {
 
 // Two jobs share one launch (same M and r): workgroups x < j0.tiles take
 // job 0, the rest job 1; split rows y past a job's own split count exit.
+constexpr int CS_PP = 40;   // bf16 per LDS row of the split P tile (80 bytes)
+
 template <int JT2>
-__global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_t Mp, int64_t M, int r,
-                                                    int combine) {
+__global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_t M, int r, int combine) {
   __shared__ __attribute__((aligned(16))) uint16_t sQ[32 * (128 + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[32 * JT2 * CS_PP];
   const bool second = blockIdx.x >= j0.tiles;
   const ColJob jb = second ? j1 : j0;
   if ((int)blockIdx.y >= jb.splits) return;   // the whole workgroup
-  const uint16_t* __restrict__ pt2 = jb.pt2;
+  const float* __restrict__ P = jb.P;
   const uint16_t* __restrict__ Q = jb.Q;
   const int64_t C = jb.C, m_per_split = jb.m_per_split;
   float* __restrict__ part = jb.part;
@@ -1194,14 +1220,43 @@ __global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_
   for (int jt = 0; jt < JT2; ++jt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[jt][v] = 0.f;
-  // A-fragment rows (rows past 2r read row 0: their products are not used)
+  // A-fragment rows of the split tile (rows past 2r read row 0: their
+  // products are not used)
   const uint16_t* arow[JT2];
 #pragma unroll
   for (int jt = 0; jt < JT2; ++jt) {
     const int j = 32 * jt + li;
-    arow[jt] = pt2 + (int64_t)(j < rows2 ? j : 0) * Mp + 8 * lh;
+    arow[jt] = sP + (j < rows2 ? j : 0) * CS_PP + 8 * lh;
   }
+  // The 32 r values of P for one chunk of 32 rows: thread t takes elements
+  // t + 256 q (q < 2 JT2 covers 32 r since r <= 16 JT2); the next chunk's
+  // loads are issued before the current chunk's products.
+  constexpr int PQ = 2 * JT2;
+  float pv[PQ];
+  auto load_p = [&](int64_t mb) {
+#pragma unroll
+    for (int q = 0; q < PQ; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      const int row = idx / r;
+      const int64_t m = mb + row;
+      pv[q] = (idx < 32 * r && m < m_end) ? P[m * r + (idx - row * r)] : 0.0f;
+    }
+  };
+  load_p(m_begin);
   for (int64_t mb = m_begin; mb < m_end; mb += 32) {
+    // sP[j][m - mb] = hi(P[m][j]), sP[j + r][m - mb] = lo(P[m][j]); zero past m_end
+#pragma unroll
+    for (int q = 0; q < PQ; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      if (idx < 32 * r) {
+        const int row = idx / r, j = idx - row * r;
+        float hi, lo;
+        split_bf16(pv[q], hi, lo);
+        sP[j * CS_PP + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+        sP[(j + r) * CS_PP + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
+      }
+    }
+    load_p(mb + 32);
     for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
       const int row = idx / 16, cc = (idx % 16) * 8;
       const int64_t m = mb + row, c = c0 + cc;
@@ -1218,13 +1273,12 @@ __global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_
       }
       *reinterpret_cast<u32x4_t*>(sQ + row * (128 + 8) + cc) = v;
     }
-    // pt2 is zero past M (padding) and rows of Q past m_end are zero in LDS
+    __syncthreads();
     u32x4_t af[2][JT2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int jt = 0; jt < JT2; ++jt) af[s][jt] = ld16(arow[jt] + mb + 16 * s);
-    __syncthreads();
+      for (int jt = 0; jt < JT2; ++jt) af[s][jt] = ld16(arow[jt] + 16 * s);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4_t bv;
@@ -1292,15 +1346,11 @@ int col_skinny_splits(int64_t M, int64_t C) {
 
 }  // namespace
 
-int64_t split_rows(int64_t M) { return (M + 31) / 32 * 32; }
-
-hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
-                             float* out, uint16_t* pt2, hipStream_t s) {
-  const int64_t Mp = split_rows(M);
-  const int64_t rows = pt2 ? Mp : M;
-  const dim3 grid((unsigned)((rows + 15) / 16));
+hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r, float* out,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)((M + 15) / 16));
   switch ((r + 15) / 16) {
-#define LQ_RS(JT, W) case JT: hipLaunchKernelGGL((k_row_skinny<JT, W>), grid, dim3(64 * W), 0, s, Q, M, C, R, r, out, pt2, Mp); break;
+#define LQ_RS(JT, W) case JT: hipLaunchKernelGGL((k_row_skinny<JT, W, 0>), grid, dim3(64 * W), 0, s, Q, M, C, R, r, out); break;
     LQ_RS(1, 16) LQ_RS(2, 16) LQ_RS(3, 16) LQ_RS(4, 16) LQ_RS(5, 8) LQ_RS(6, 8) LQ_RS(7, 8) LQ_RS(8, 8)
 #undef LQ_RS
     default: return hipErrorInvalidValue;
@@ -1308,11 +1358,15 @@ hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* Bt, const float* t, int64_t M,
-                           uint16_t* pt2, hipStream_t s) {
-  const int64_t n = N * r + (int64_t)r * split_rows(M);
-  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 2048);
-  hipLaunchKernelGGL(k_bwd_prep, dim3(blocks), dim3(256), 0, s, B, N, r, Bt, t, M, split_rows(M), pt2);
+// Each workgroup transposes the whole of Rt for its 16 rows, so this form
+// pays only while that is small: r <= 16 (at r = 64 over 11008 columns it
+// cost more than a separate transpose launch).
+hipError_t launch_row_skinny_rt(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rt, int r, float* out,
+                                hipStream_t s) {
+  if (r > 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + 15) / 16));
+  if (r % 8 == 0) hipLaunchKernelGGL((k_row_skinny<1, 16, 1>), grid, dim3(1024), 0, s, Q, M, C, Rt, r, out);
+  else hipLaunchKernelGGL((k_row_skinny<1, 16, 2>), grid, dim3(1024), 0, s, Q, M, C, Rt, r, out);
   return hipGetLastError();
 }
 
@@ -1343,7 +1397,7 @@ hipError_t launch_col_skinny(const ColSkinnyReq* a, const ColSkinnyReq* b, int64
     const int64_t mchunks = (M + 31) / 32;
     const int64_t m_per_split = ((mchunks + splits - 1) / splits) * 32;
     const int real_splits = (int)((M + m_per_split - 1) / m_per_split);
-    job[njobs] = ColJob{q.pt2, q.Q, q.C, m_per_split, real_splits, (unsigned)((q.C + 127) / 128), q.ws};
+    job[njobs] = ColJob{q.P, q.Q, q.C, m_per_split, real_splits, (unsigned)((q.C + 127) / 128), q.ws};
     ymax = std::max(ymax, real_splits);
     ++njobs;
     SplitJobDesc* d = desc[i];
@@ -1360,7 +1414,7 @@ hipError_t launch_col_skinny(const ColSkinnyReq* a, const ColSkinnyReq* b, int64
   if (njobs == 0) return hipSuccess;
   const dim3 grid(job[0].tiles + (njobs > 1 ? job[1].tiles : 0u), (unsigned)ymax);
   switch ((2 * r + 31) / 32) {
-#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, job[0], job[1], split_rows(M), M, r, combine); break;
+#define LQ_CS(JT) case JT: hipLaunchKernelGGL(k_col_skinny<JT>, grid, dim3(256), 0, s, job[0], job[1], M, r, combine); break;
     LQ_CS(1) LQ_CS(2) LQ_CS(3) LQ_CS(4) LQ_CS(5) LQ_CS(6) LQ_CS(7) LQ_CS(8)
 #undef LQ_CS
     default: return hipErrorInvalidValue;

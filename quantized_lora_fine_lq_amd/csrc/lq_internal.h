@@ -126,19 +126,15 @@ hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t
                                     hipStream_t s);
 
 // Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R[j][c] with R
-// [r, C] row-major (C % 8 == 0); one launch, no workspace. If pt2 is not
-// null the result is also written as the column form's P operand
-// ([2r][split_rows(M)] bf16: hi and lo halves, transposed, zero padded).
-int64_t split_rows(int64_t M);
+// [r, C] row-major (C % 8 == 0); one launch, no workspace. The _rt variant
+// (r <= 16) takes the second operand transposed, Rt [C, r] row-major (u = G B).
 hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
-                             float* out, uint16_t* pt2, hipStream_t s);
-// Backward set-up: Bt = B^T ([N, r] -> [r, N]) and pt2 = the column form's P
-// operand from t (as launch_row_skinny writes it).
-hipError_t launch_bwd_prep(const uint16_t* B, int64_t N, int r, uint16_t* Bt, const float* t, int64_t M,
-                           uint16_t* pt2, hipStream_t s);
+                             float* out, hipStream_t s);
+hipError_t launch_row_skinny_rt(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rt, int r,
+                                float* out, hipStream_t s);
 hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* out, hipStream_t s);
-// Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c] with P given as
-// pt2 (see launch_row_skinny); written as
+// Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c] with P float32
+// [M, r] row-major; written as
 // out[j*C + c] (out_transposed = false, [r, C]) or out[c*r + j] ([C, r]).
 // launch_col_skinny writes partial sums into ws (col_skinny_ws_floats) and
 // describes the reduction that finishes it in *job; launch_reduce_splits2
@@ -153,10 +149,10 @@ struct SplitJobDesc {
   int transposed = 0;
 };
 size_t col_skinny_ws_floats(int64_t M, int64_t C, int r);
-// One column-form product: pt2 ([2r][Mp] split operand), Q [M, C], its
-// output and partial-sum workspace (col_skinny_ws_floats(M, C, r) floats).
+// One column-form product: P [M, r] float32, Q [M, C], its output and
+// partial-sum workspace (col_skinny_ws_floats(M, C, r) floats).
 struct ColSkinnyReq {
-  const uint16_t* pt2;
+  const float* P;
   const uint16_t* Q;
   int64_t C;
   float scale;

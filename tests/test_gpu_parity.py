@@ -340,7 +340,10 @@ def test_unit_vector_probe_bit_exact(lq, torch, M):
     (2056, 2048, 70, 16, 32.0),    # wide N, K with few rows: u's contraction ragged past 32 blocks
     (2048, 2048, 40, 64, 16.0),    # four 16-wide tiles over 32 column blocks
     (1024, 1024, 48, 128, 16.0),   # eight tiles (8 waves per workgroup)
-    (264, 256, 2050, 16, 32.0),    # many row groups, ragged M (split rows padded to 2080)
+    (264, 256, 2050, 16, 32.0),    # many row groups, ragged M
+    (200, 192, 45, 5, 10.0),       # r % 8 != 0: B rows read element by element in u = G B
+    (264, 320, 37, 13, 16.0),      # r % 8 != 0, N % 64 != 0
+    (136, 128, 40, 100, 16.0),     # r % 8 != 0 with seven 16-wide tiles
 ])
 @pytest.mark.parametrize("recompute_t", [False, True])
 def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
