@@ -260,10 +260,16 @@ size_t lq_lora_down_workspace(int64_t M, int64_t K, int32_t r);
 int lq_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* A, int32_t r, float* t,
                  void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for lq_dequant_gemm with M tokens and rank r: N * K * 2
- * bytes (rounded up to 256) for the dequantized weight of a codebook weight
- * on the GEMM path; 0 for NF4 weights (the kernels form the LoRA-segment
- * operands themselves) and for a codebook weight on its GEMV path. */
+/* Workspace bytes for lq_dequant_gemm with M tokens and rank r: on the GEMM
+ * path, N * K * 2 bytes (rounded up to 256) for the dequantized weight of a
+ * codebook weight, plus 256 KB of float32 partial sums per split output
+ * tile. The GEMM runs one 256 x 128 output tile per workgroup, one per CU,
+ * over 8 XCDs of 32 CUs, each XCD a contiguous range of tiles; when an XCD's
+ * last round would be at most half full (and K >= 1024), its last tiles are
+ * split into two halves of the contraction and a second launch adds them
+ * (e.g. M = 4096, N = 11008, K = 4096: 96 split tiles, 24 MiB). 0 for a
+ * weight on the GEMV path and for NF4 shapes that split nothing (the
+ * kernels form the LoRA-segment operands themselves). */
 size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
@@ -272,15 +278,16 @@ size_t lq_dequant_gemm_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * GEMV kernels for M <= 16, else the MFMA GEMM, as for lq_qlora_forward; on
  * the GEMM path a codebook weight is dequantized into the workspace first). Arguments as lq_qlora_forward;
  * t [M, r] float32 is read. The workspace (caller-owned,
- * lq_dequant_gemm_workspace bytes) receives the dequantized codebook weight;
- * it may be NULL when that size is 0.
+ * lq_dequant_gemm_workspace bytes) receives the dequantized codebook weight
+ * and the split tiles' partial sums; it may be NULL when that size is 0.
  */
 int lq_dequant_gemm(const lq_qweight* w, const uint16_t* X, int64_t M, const float* t,
                     const uint16_t* B, int32_t r, float alpha, void* H, int32_t h_dtype,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for lq_dequant_gemm_t: N * K * 2 (rounded up to 256) for a
- * codebook weight, 0 for NF4. */
+ * codebook weight, plus the split tiles' partial sums as for
+ * lq_dequant_gemm (output tiles of grad_X [M, K], contraction over N). */
 size_t lq_dequant_gemm_t_workspace(const lq_qweight* w, int64_t M, int32_t r);
 
 /*
@@ -311,7 +318,9 @@ size_t lq_backward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  *   grad_X, dA, dB may each be NULL to skip that output.
  * Requires N % 8 == 0 (LQ_ERR_SHAPE). For a codebook weight, grad_X
  * dequantizes it into the workspace first. The workspace
- * (lq_backward_workspace bytes) holds u, B^T and partial sums; the
+ * (lq_backward_workspace bytes) holds u, t when recomputed, B^T when
+ * r > 16, and partial sums (the column-form products' and, for grad_X, the
+ * split tiles' as for lq_dequant_gemm_t); the
  * call sets up whatever it needs, so its contents on entry do not matter.
  * Errors: as lq_qlora_forward.
  */

@@ -97,7 +97,38 @@ struct GemmParams {
   const uint16_t* wbf; // dequantized weight [N, K] bf16 (codebook format), else null
   SplitJob red[2];     // split reductions to run after the tiles (backward), n = rows * cols each
   int64_t red_n[2];    // 0: none
+  int cpx;             // CUs per XCD when the last tiles of each XCD are split in two k-halves, else 0
+  float* part;         // the split tiles' float32 partial sums, [2 per split tile][BM][BN]
 };
+
+// ---- tile schedule ------------------------------------------------------------
+// The 8 XCDs take workgroups round robin (workgroup b runs on XCD b % 8), and
+// each XCD owns a contiguous range of logical tiles. One workgroup fills a CU,
+// so an XCD of cpx CUs runs its tiles in rounds of cpx; when its last round
+// would be at most half full, its last tiles are each split into two
+// k-halves (twice as many workgroups, each half as long) whose float32
+// partial sums a second kernel adds. Workgroup b takes item b / 8 of XCD b % 8.
+__host__ __device__ inline int64_t xcd_tiles(int64_t total, int x) { return total / 8 + (x < total % 8 ? 1 : 0); }
+__host__ __device__ inline int64_t xcd_first(int64_t total, int x) {
+  return x * (total / 8) + (x < total % 8 ? x : total % 8);
+}
+__host__ __device__ inline int64_t xcd_splits(int64_t n_x, int cpx) {
+  if (cpx <= 0 || n_x < cpx) return 0;
+  const int64_t r = n_x % cpx;
+  return 2 * r <= cpx ? r : 0;
+}
+// Logical tile -> (M-tile, N-tile): groups of gm M-tiles with the N-tiles
+// outer inside a group, so the workgroups resident on one XCD at a time share
+// gm A row-tiles and a run of consecutive weight tiles in that XCD's L2.
+__host__ __device__ inline void tile_coords(int64_t t, int64_t tiles_m, int64_t tiles_n, int gm0, int64_t& tm,
+                                            int64_t& tn) {
+  const int64_t group = (int64_t)gm0 * tiles_n;
+  const int64_t first_m = (t / group) * gm0;
+  const int64_t gm = tiles_m - first_m < gm0 ? tiles_m - first_m : gm0;
+  const int64_t within = t % group;
+  tm = first_m + within % gm;
+  tn = within / gm;
+}
 
 __device__ __forceinline__ void zero(u32x4_t& v) { v = u32x4_t{0u, 0u, 0u, 0u}; }
 
@@ -237,10 +268,10 @@ struct ProdFwdNF4 {
   float c0, s2;
   uint32_t q8;
   float livef;           // 0 for a padding step past the end: tile of zeros
-  __device__ void init(const GemmParams& p, int64_t n0) {
+  __device__ void init(const GemmParams& p, int64_t n0, int ks) {
     const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
     const int64_t n = min(n0 + row, p.w.N - 1);   // rows past N: outputs never stored
-    const int64_t e0 = n * p.w.K + 16 * qq;
+    const int64_t e0 = n * p.w.K + 16 * qq + (int64_t)ks * BK;
     crow = p.w.codes + e0 / 2;
     blk0 = e0 >> 6;
   }
@@ -287,17 +318,19 @@ template <bool DQ>
 struct ProdBwdNF4 {
   static constexpr bool kSwz = true;
   int64_t kcol;          // first of the thread's 8 columns
+  int ks;                // first step of this workgroup's range of the contraction
   uint32_t code[2];
   float c0[2], s2[2];
   uint32_t q8[2];
   float livef[2];
-  __device__ void init(const GemmParams& p, int64_t n0) {
+  __device__ void init(const GemmParams& p, int64_t n0, int ks0) {
     const int cg = (threadIdx.x & 63) >> 2;
     kcol = min(n0 + 8 * cg, p.w.K - 8);   // columns past K: outputs never stored
+    ks = ks0;
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
     const int rp = 8 * (threadIdx.x >> 6) + 2 * (threadIdx.x & 3);   // first row of the pair in the step
-    const int it = min(step, nMain - 1);
+    const int it = ks + min(step, nMain - 1);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int64_t nrow = (int64_t)it * BK + rp + rr;
@@ -345,10 +378,10 @@ struct ProdFwdBF16 {
   const uint16_t* src;
   u32x4_t v[2];
   bool live;
-  __device__ void init(const GemmParams& p, int64_t n0) {
+  __device__ void init(const GemmParams& p, int64_t n0, int ks) {
     const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
     const int64_t n = min(n0 + row, p.w.N - 1);   // rows past N: outputs never stored
-    src = p.wbf + n * p.w.K + 16 * qq;
+    src = p.wbf + n * p.w.K + 16 * qq + (int64_t)ks * BK;
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
     live = step < nMain;
@@ -374,15 +407,17 @@ template <bool DQ>
 struct ProdBwdBF16 {
   static constexpr bool kSwz = false;
   int64_t kcol;
+  int ks;
   u32x4_t v[2];
   bool ok[2];
-  __device__ void init(const GemmParams& p, int64_t n0) {
+  __device__ void init(const GemmParams& p, int64_t n0, int ks0) {
     const int kq = threadIdx.x >> 5;
     kcol = min(n0 + 8 * kq, p.w.K - 8);   // columns past K: outputs never stored
+    ks = ks0;
   }
   __device__ void load(const GemmParams& p, int step, int nMain) {
     const int g = threadIdx.x & 31;
-    const int it = min(step, nMain - 1);
+    const int it = ks + min(step, nMain - 1);
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       const int64_t nrow = (int64_t)it * BK + 2 * g + rr;
@@ -426,32 +461,41 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   f32x2_t* sPair = lds.pair;
   uint16_t (*sA)[BM * PITCH] = lds.a;
   uint16_t (*sB)[BN * PITCH] = lds.b;
-  if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
 
-  // XCD-aware tile order: the 8 XCDs take workgroups round robin, so each
-  // XCD gets a contiguous range of logical tiles. Logical tiles run over
-  // groups of p.gm M-tiles with the N-tiles outer inside a group, so the
-  // workgroups resident on one XCD at a time share p.gm A row-tiles and a
-  // run of consecutive weight tiles in that XCD's L2.
+  // this workgroup's item of its XCD's schedule: a whole tile, or one k-half
+  // (half 0 or 1) of split tile number sidx
   const int64_t tiles_m = (p.M + BM - 1) / BM;
   const int64_t tiles_n = (p.Ncols + BN - 1) / BN;
   const int64_t total = tiles_m * tiles_n;
-  const int64_t b = blockIdx.x;
-  const int64_t per = total / 8, rem = total % 8;
-  const int64_t xcd = b % 8, local = b / 8;
-  const int64_t logical = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int64_t group = (int64_t)p.gm * tiles_n;
-  const int64_t first_m = (logical / group) * p.gm;
-  const int64_t gm = min((int64_t)p.gm, tiles_m - first_m);
-  const int64_t within = logical % group;
-  const int64_t tm = first_m + within % gm, tn = within / gm;
+  const int xcd = (int)(blockIdx.x % 8);
+  const int64_t local = blockIdx.x / 8;
+  const int64_t n_x = xcd_tiles(total, xcd), s_x = xcd_splits(n_x, p.cpx);
+  if (local >= n_x + s_x) {   // past this XCD's items (the grid is 8 x the longest list)
+    gemm_reduce_tail(p);
+    return;
+  }
+  const int64_t whole = n_x - s_x;
+  int64_t logical = xcd_first(total, xcd) + local, sidx = 0;
+  int half = -1;
+  if (local >= whole) {
+    const int64_t j = local - whole;
+    logical = xcd_first(total, xcd) + whole + j / 2;
+    half = (int)(j & 1);
+    for (int x = 0; x < xcd; ++x) sidx += xcd_splits(xcd_tiles(total, x), p.cpx);
+    sidx += j / 2;
+  }
+  int64_t tm, tn;
+  tile_coords(logical, tiles_m, tiles_n, p.gm, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int nK = (int)((p.Kc + BK - 1) / BK);
+  const int ks = half == 1 ? nK / 2 : 0;                      // first step of this item
+  const int nMain = half < 0 ? nK : (half == 0 ? nK / 2 : nK - nK / 2);
 
+  if (threadIdx.x < 256) sPair[threadIdx.x] = f32x2_t{p.lv.q[threadIdx.x >> 4], p.lv.q[threadIdx.x & 15]};
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wr = wave & 3, kh = wave >> 2;
   const int li = lane & 31, lh = lane >> 5;
   const float mean = p.w.qc.absmax ? 0.0f : *p.w.qc.dq_mean;
-  const int nMain = (int)((p.Kc + BK - 1) / BK);
   const uint16_t* ar[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -471,35 +515,36 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
   // issues the same loads (indices are clamped; a step past the end yields a
   // zero Bt tile), so each step is one basic block.
   Prod pa, pb;
-  pa.init(p, n0);
-  pb.init(p, n0);
+  pa.init(p, n0, ks);
+  pb.init(p, n0, ks);
   u32x4_t ra[4], rb[4];
   __syncthreads();  // sPair and producer tables ready
 
   pa.load(p, 0, nMain);
-  load_a_tile<TAIL>(p, 0, ar, ra);
+  load_a_tile<TAIL>(p, ks, ar, ra);
   pb.load(p, 1, nMain);
-  load_a_tile<TAIL>(p, min(1, nMain - 1), ar, rb);
+  load_a_tile<TAIL>(p, ks + min(1, nMain - 1), ar, rb);
   pa.store(p, sB[0], sPair, mean);
   store_a_tile(sA[0], ra);
   __syncthreads();
   for (int it = 0; it < nMain; it += 2) {
     pa.load(p, it + 2, nMain);
-    load_a_tile<TAIL>(p, min(it + 2, nMain - 1), ar, ra);
+    load_a_tile<TAIL>(p, ks + min(it + 2, nMain - 1), ar, ra);
     mfma_half<Prod::kSwz>(sA[0], sB[0], acc, wr, kh, li, lh);
     pb.store(p, sB[1], sPair, mean);
     store_a_tile(sA[1], rb);
     __syncthreads();
     pb.load(p, it + 3, nMain);
-    load_a_tile<TAIL>(p, min(it + 3, nMain - 1), ar, rb);
+    load_a_tile<TAIL>(p, ks + min(it + 3, nMain - 1), ar, rb);
     mfma_half<Prod::kSwz>(sA[1], sB[1], acc, wr, kh, li, lh);
     pa.store(p, sB[0], sPair, mean);
     store_a_tile(sA[0], ra);
     __syncthreads();
   }
 
-  // LoRA segment (R2 = 64 ceil(2r / 64) columns) through the same LDS tiles
-  const int nLora = p.R2 / BK;
+  // LoRA segment (R2 = 64 ceil(2r / 64) columns) through the same LDS tiles;
+  // of a split tile, only the first half adds it
+  const int nLora = half == 1 ? 0 : p.R2 / BK;
   for (int jt = 0; jt < nLora; ++jt) {
     lora_tiles<Prod::kSwz>(p, jt, m0, n0, sA[0], sB[0]);
     __syncthreads();
@@ -534,6 +579,22 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
         }
     }
     __syncthreads();
+  }
+
+  // a split tile's half: float32 partial sums, [BM][BN] row-major
+  if (half >= 0) {
+    if (kh == 0) {
+      float* dst = p.part + (2 * sidx + half) * (int64_t)(BM * BN);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            dst[(64 * wr + 32 * rt + 8 * (v >> 2) + 4 * lh + (v & 3)) * BN + 32 * ct + li] = acc[rt][ct][v];
+    }
+    gemm_reduce_tail(p);
+    return;
   }
 
   // epilogue (kh = 0 waves): lane holds column li of each 32x32 tile, rows
@@ -593,6 +654,44 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_dq_gemm(GemmParams p) {
       }
     }
   gemm_reduce_tail(p);
+}
+
+// The split tiles' two k-halves added (half 0 + half 1, in that order) and
+// stored; thread -> 4 consecutive columns of one row of one split tile.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void k_split_fixup(GemmParams p, int64_t n_split) {
+  const int64_t tiles_m = (p.M + BM - 1) / BM;
+  const int64_t tiles_n = (p.Ncols + BN - 1) / BN;
+  const int64_t total = tiles_m * tiles_n;
+  constexpr int PER_TILE = BM * BN / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_split * PER_TILE; i += (int64_t)gridDim.x * 256) {
+    const int64_t sidx = i / PER_TILE;
+    const int e = (int)(i % PER_TILE);
+    // the split tile's logical index: its XCD's range, last s_x tiles
+    int64_t base = 0, logical = 0;
+    for (int x = 0; x < 8; ++x) {
+      const int64_t n_x = xcd_tiles(total, x), s_x = xcd_splits(n_x, p.cpx);
+      if (sidx < base + s_x) {
+        logical = xcd_first(total, x) + n_x - s_x + (sidx - base);
+        break;
+      }
+      base += s_x;
+    }
+    int64_t tm, tn;
+    tile_coords(logical, tiles_m, tiles_n, p.gm, tm, tn);
+    const int row = e / (BN / 4), col = 4 * (e % (BN / 4));
+    const int64_t grow = tm * BM + row, gcol = tn * BN + col;
+    if (grow >= p.M) continue;
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.part + (2 * sidx) * (int64_t)(BM * BN) + row * BN + col);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p.part + (2 * sidx + 1) * (int64_t)(BM * BN) + row * BN + col);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (gcol + c >= p.Ncols) break;
+      const float v = a[c] + b[c];
+      if (OUT_F32) reinterpret_cast<float*>(p.out)[grow * p.Ncols + gcol + c] = v;
+      else reinterpret_cast<uint16_t*>(p.out)[grow * p.Ncols + gcol + c] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+    }
+  }
 }
 
 // ===========================================================================
@@ -1441,10 +1540,50 @@ int lora_seg_cols(int r) { return BK * ((2 * r + BK - 1) / BK); }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The GEMM's schedule on MI355X: 256 CUs in 8 XCDs of 32, one workgroup per
+// CU. Tiles are split only when each XCD has at least one full round and
+// the contraction has at least 16 steps.
+constexpr int kCusPerXcd = 32;
+static int split_cpx(int64_t M, int64_t Ncols, int64_t Kc) {
+  return (Kc + BK - 1) / BK >= 16 ? kCusPerXcd : 0;
+}
+static int64_t split_tiles(int64_t M, int64_t Ncols, int64_t Kc) {
+  const int cpx = split_cpx(M, Ncols, Kc);
+  const int64_t total = ((M + BM - 1) / BM) * ((Ncols + BN - 1) / BN);
+  int64_t n = 0;
+  for (int x = 0; x < 8; ++x) n += xcd_splits(xcd_tiles(total, x), cpx);
+  return n;
+}
+static int64_t gemm_grid(int64_t M, int64_t Ncols, int64_t Kc) {
+  const int cpx = split_cpx(M, Ncols, Kc);
+  const int64_t total = ((M + BM - 1) / BM) * ((Ncols + BN - 1) / BN);
+  int64_t longest = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t n_x = xcd_tiles(total, x);
+    longest = std::max(longest, n_x + xcd_splits(n_x, cpx));
+  }
+  return 8 * longest;
+}
+static size_t split_part_bytes(int64_t M, int64_t Ncols, int64_t Kc) {
+  return align256((size_t)split_tiles(M, Ncols, Kc) * 2 * BM * BN * sizeof(float));
+}
+
 // Workspace of the forward / backward GEMM: (codebook format) the dequantized
-// bf16 weight; none for NF4.
-size_t gemm_ws_bytes(const QWeight& w, int64_t, int, bool) {
-  return w.format == LQ_FMT_CODEBOOK ? align256((size_t)w.N * w.K * sizeof(uint16_t)) : 0;
+// bf16 weight, then the split tiles' partial sums (when the schedule splits).
+size_t gemm_ws_bytes(const QWeight& w, int64_t M, int, bool fwd) {
+  const size_t wbf = w.format == LQ_FMT_CODEBOOK ? align256((size_t)w.N * w.K * sizeof(uint16_t)) : 0;
+  return wbf + (fwd ? split_part_bytes(M, w.N, w.K) : split_part_bytes(M, w.K, w.N));
+}
+
+// Adds the split tiles' halves (a second launch, only when the schedule splits).
+template <bool OUT_F32>
+static hipError_t launch_split_fixup(const GemmParams& p, hipStream_t st) {
+  const int64_t n = split_tiles(p.M, p.Ncols, p.Kc);
+  if (n == 0) return hipSuccess;
+  const int64_t threads = n * (BM * BN / 4);
+  hipLaunchKernelGGL(k_split_fixup<OUT_F32>, dim3((unsigned)std::min<int64_t>((threads + 255) / 256, 4096)),
+                     dim3(256), 0, st, p, n);
+  return hipGetLastError();
 }
 
 // The LoRA segment's sources (read by the GEMM itself).
@@ -1470,6 +1609,8 @@ static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, in
   p.wbf = nullptr;
   p.red[0] = p.red[1] = SplitJob{nullptr, 0, 0, 0, 0, 0, 0.0f, nullptr, 0};
   p.red_n[0] = p.red_n[1] = 0;
+  p.cpx = split_cpx(M, Ncols, Kc);
+  p.part = nullptr;
   return p;
 }
 
@@ -1479,10 +1620,12 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   GemmParams p = make_params(w, X, M, w.N, w.K, H);
   set_lora(p, t, B, r, s, true);
   hipError_t e = hipSuccess;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
+  const int64_t tiles = gemm_grid(M, w.N, w.K);
   LQ_DASSERT(M > 0 && w.K % 64 == 0 && tiles > 0 && tiles < (int64_t(1) << 31));
   LQ_DASSERT(r >= 1 && r <= 128 && p.R2 % BK == 0);
   const dim3 grid((unsigned)tiles);
+  const size_t wbf_bytes = w.format == LQ_FMT_CODEBOOK ? align256((size_t)w.N * w.K * sizeof(uint16_t)) : 0;
+  p.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wbf_bytes);   // used only by split tiles
   const bool dq = w.qc.absmax == nullptr;
   const bool f32 = h_dtype == LQ_F32;
 #define LQ_LAUNCH_FWD(PROD)                                                                          \
@@ -1503,7 +1646,8 @@ hipError_t launch_gemm_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
     else hipLaunchKernelGGL((k_dq_gemm<ProdFwdBF16<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
   }
 #undef LQ_LAUNCH_FWD
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return f32 ? launch_split_fixup<true>(p, st) : launch_split_fixup<false>(p, st);
 }
 
 hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const float* u,
@@ -1519,10 +1663,12 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
     p.red_n[i] = rd[i]->rows * rd[i]->cols;
   }
   hipError_t e = hipSuccess;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((w.K + BN - 1) / BN);
+  const int64_t tiles = gemm_grid(M, w.K, w.N);
   LQ_DASSERT(M > 0 && w.N % 8 == 0 && w.K % 64 == 0 && tiles > 0 && tiles < (int64_t(1) << 31));
   LQ_DASSERT(r >= 1 && r <= 128 && p.R2 % BK == 0);
   const dim3 grid((unsigned)tiles);
+  const size_t wbf_bytes = w.format == LQ_FMT_CODEBOOK ? align256((size_t)w.N * w.K * sizeof(uint16_t)) : 0;
+  p.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + wbf_bytes);   // used only by split tiles
   const bool tail = w.N % BK != 0;   // contraction over N: last step partial
   if (w.format == LQ_FMT_CODEBOOK) {
     uint16_t* wbf = ws;
@@ -1538,7 +1684,8 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
     if (tail) hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, true>), grid, dim3(GEMM_THREADS), 0, st, p);
     else hipLaunchKernelGGL((k_dq_gemm<ProdBwdNF4<false>, false, false>), grid, dim3(GEMM_THREADS), 0, st, p);
   }
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_split_fixup<false>(p, st);
 }
 
 // Row groups per workgroup: 4, 2 or 1, the largest whose constant table

@@ -443,3 +443,28 @@ def test_codebook_forward_workspace_by_path(lq, monkeypatch):
     monkeypatch.delenv("LQ_FORCE_PATH")
     wide = lq.lq_qweight(1, 64, 16, 32768, 0x1000, 0x1000, None, None, None, 256, 0, 0x1000, 0x1000, 0x1000)
     assert lq.lib.lq_forward_workspace(ctypes.byref(wide), 1, 16) >= 16 * 32768 * 2
+
+
+def test_split_schedule_workspace(lq, monkeypatch):
+    """The GEMM's schedule on 8 XCDs of 32 CUs: when an XCD's last round of
+    256 x 128 tiles would be at most half full, its last tiles run as two
+    halves of the contraction, whose float32 partial sums (2 x 256 x 128 per
+    split tile) live in the workspace. q_proj (256 tiles, 32 per XCD) splits
+    none; mlp_up forward and mlp_down's grad_X (1376 tiles, 172 per XCD:
+    5 rounds and 12) split 12 per XCD; 1376 tiles with K = 960 (15 steps)
+    split none."""
+    monkeypatch.delenv("LQ_FORCE_PATH", raising=False)
+    L = lq.lib
+
+    def nf4(N, K):
+        return lq.lq_qweight(0, 64, N, K, 0x1000, None, 0x1000, 0x1000, 0x1000, 256, 0, None, None, None)
+    part = 96 * 2 * 256 * 128 * 4
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(nf4(4096, 4096)), 2048, 16) == 0
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(nf4(11008, 4096)), 4096, 64) == part
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(nf4(11008, 960)), 4096, 64) == 0
+    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(nf4(4096, 11008)), 4096, 64) == part
+    assert L.lq_dequant_gemm_t_workspace(ctypes.byref(nf4(11008, 4096)), 4096, 64) == 0
+    # 264 tiles (33 per XCD): one split tile per XCD
+    assert L.lq_dequant_gemm_workspace(ctypes.byref(nf4(132 * 128, 1024)), 512, 16) == 8 * 2 * 256 * 128 * 4
+    # the backward's workspace carries the same partial sums for grad_X
+    assert L.lq_backward_workspace(ctypes.byref(nf4(4096, 11008)), 4096, 64) > part

@@ -167,6 +167,42 @@ def test_prefill_layer_full_size(lq, torch, name):
     assert layer.rel_frobenius(bf16_to_f32(gx)[np.ix_(ms, cols)], gref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("direction", ["forward", "backward"])
+def test_split_tail_tiles(lq, torch, direction):
+    """264 output tiles of 256 x 128 (33 per XCD: one full round of 32 and one
+    more), so the last tile of every XCD runs as two halves of the
+    contraction whose partial sums a second kernel adds; every output column
+    on 64 sampled tokens against the oracle, bf16 and float32 forward
+    outputs and grad_X."""
+    M, r, alpha = 512, 16, 32.0
+    N, K = (132 * 128, 1024) if direction == "forward" else (1024, 132 * 128)
+    L = syn.small_layer(N, K, M, r, alpha, seed=901 if direction == "forward" else 902)
+    W = syn.weight(L)
+    rng = np.random.default_rng(L.workload_id)
+    c_ref, dqp, cp = oracle_constants(W)
+    codes, absmax, qw = quantize_on_gpu(lq, torch, W)
+    X, A, B, G = syn.activations(L), syn.lora_a(L), syn.lora_b(L), syn.grad_out(L)
+    Xd, Ad, Bd, Gd = (bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits),
+                      bf16_dev(torch, G.bits))
+    ms = np.unique(np.concatenate([sample(rng, 256, 32), 256 + sample(rng, 256, 32)]))   # both M-tiles
+    s = alpha / r
+    if direction == "forward":
+        _, _, wd = oracle_rows(W, np.arange(N), cp)           # every output row of W'
+        H, t = lq.qlora_forward(qw, Xd, Ad, Bd, alpha)
+        Href, _ = layer.forward(wd, X.f32[ms], A.f32, B.f32, alpha, r)
+        assert layer.rel_frobenius(bf16_to_f32(H)[ms], Href) <= BF16_TOL
+        H32 = lq.dequant_gemm(qw, Xd, t, Bd, alpha, out_dtype=torch.float32)
+        assert layer.rel_frobenius(host(H32)[ms], Href) <= F32_TOL
+    else:
+        cols, wd = oracle_col_blocks(W, np.arange(K // 64), cp)   # the whole W' by columns
+        assert np.array_equal(cols, np.arange(K))
+        t = lq.lora_down(Xd, Ad)
+        gx, _, _ = lq.qlora_backward(qw, Xd, Gd, Ad, Bd, alpha, t=t, need_dA=False, need_dB=False)
+        u64 = G.f32.astype(np.float64) @ B.f32.astype(np.float64)
+        gref = G.f32[ms].astype(np.float64) @ wd.astype(np.float64) + s * (u64[ms] @ A.f32.astype(np.float64))
+        assert layer.rel_frobenius(bf16_to_f32(gx)[ms], gref) <= BF16_TOL
+
+
 def test_q_proj_forward_f32_elementwise_bound(lq, torch):
     """q_proj forward with float32 H (4096 x 4096, 2048 tokens, r = 16) on
     sampled (token, output) pairs, each element within a worst-case rounding
