@@ -359,35 +359,73 @@ __global__ __launch_bounds__(256) void k_dequant_nf4(const uint8_t* __restrict__
   }
 }
 
-// Codebook dequant: one thread per 8 elements of a 64-block (one byte of
-// each bit-plane). Row i's levels live in levels[i*16 ...].
+// Codebook dequant: one workgroup per row. The row's 16 levels become an LDS
+// table of 256 level pairs whose index interleaves the bits of two adjacent
+// codes (bit 2p: plane p of the first code, bit 2p + 1: plane p of the
+// second), so a pair of codes is one 2-bit field of each plane byte and one
+// 8-byte lookup. Thread t takes groups of 8 elements t, t + 256, ... (one
+// byte of each bit-plane, one 16-byte store), two per pass; row i's levels live in
+// levels[i*16 ...]. Codes past a row's 2^b levels cannot occur (the planes
+// past its width are not read, so their bits are 0).
+template <bool DQ>
 __global__ __launch_bounds__(256) void k_dequant_codebook(const uint8_t* __restrict__ codes,
-                                                          QConst qc, int64_t N, int64_t K,
+                                                          QConst qc, int64_t K,
                                                           const uint8_t* __restrict__ row_bits,
                                                           const int64_t* __restrict__ row_offset,
                                                           const float* __restrict__ levels,
                                                           uint16_t* __restrict__ out) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;   // group of 8 elements
-  const int64_t groups_per_row = K / 8;
-  if (g >= N * groups_per_row) return;
-  const int64_t row = g / groups_per_row;
-  const int64_t k8 = g - row * groups_per_row;                 // 8-element group in row
-  const int64_t blk_in_row = k8 >> 3;
-  const int byte_in_plane = (int)(k8 & 7);
+  __shared__ f32x2_t sPair[256];
+  const int64_t row = blockIdx.x;
   const int nb = min(max((int)row_bits[row], 1), 4);
-  const uint8_t* src = codes + row_offset[row] + blk_in_row * 8 * nb;
-  uint32_t code[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int p = 0; p < nb; ++p) {
-    const uint32_t byte = src[8 * p + byte_in_plane];
+  const uint8_t* src = codes + row_offset[row];
+  {
+    const uint32_t i = threadIdx.x;
+    uint32_t f = 0, g = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) code[e] |= ((byte >> e) & 1u) << p;
+    for (int p = 0; p < 4; ++p) {
+      f |= ((i >> (2 * p)) & 1u) << p;
+      g |= ((i >> (2 * p + 1)) & 1u) << p;
+    }
+    sPair[i] = f32x2_t{levels[row * 16 + f], levels[row * 16 + g]};
   }
-  const float cp = block_const(qc, row * (K / 64) + blk_in_row);
-  const float* L = levels + row * 16;
-  u32x4_t o;
+  const float mean = DQ ? *qc.dq_mean : 0.0f;
+  __syncthreads();
+  // two groups per pass, all their loads issued before either is decoded
+  const int64_t groups = K / 8;
+  for (int64_t g0 = threadIdx.x; g0 < groups; g0 += 512) {
+    uint32_t pl[2][4], q8[2];
+    float s2[2], c0[2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(L[code[2 * e]] * cp, L[code[2 * e + 1]] * cp);
-  *reinterpret_cast<u32x4_t*>(out + row * K + k8 * 8) = o;
+    for (int h = 0; h < 2; ++h) {
+      const int64_t gi = min(g0 + 256 * h, groups - 1);   // a clamped group is decoded but not stored
+      const int64_t blk = gi >> 3;
+      const uint8_t* bsrc = src + blk * 8 * nb + (gi & 7);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) pl[h][p] = p < nb ? bsrc[8 * p] : 0u;
+      const int64_t cb = row * (K / 64) + blk;
+      if (DQ) {
+        q8[h] = qc.absmax_q[cb];
+        s2[h] = qc.dq_scale[cb >> 8];
+      } else {
+        c0[h] = qc.absmax[cb];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t gi = g0 + 256 * h;
+      const float cp = DQ ? __builtin_fmaf(e4m3_decode(q8[h]), s2[h], mean) : c0[h];
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t idx = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) idx |= ((pl[h][p] >> (2 * e)) & 3u) << (2 * p);
+        const f32x2_t q = sPair[idx];
+        o[e] = pack_bf16x2(q.x * cp, q.y * cp);
+      }
+      if (gi < groups) *reinterpret_cast<u32x4_t*>(out + row * K + gi * 8) = o;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -741,9 +779,12 @@ hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s) {
       else hipLaunchKernelGGL((k_dequant_nf4<true, 4>), grid, dim3(256), 0, s, w.codes, w.qc, n, out, tables().lv);
     }
   } else {
-    const int64_t n_groups = w.N * w.K / 8;
-    hipLaunchKernelGGL(k_dequant_codebook, dim3((unsigned)((n_groups + 255) / 256)), dim3(256), 0,
-                       s, w.codes, w.qc, w.N, w.K, w.row_bits, w.row_offset, w.levels, out);
+    if (w.qc.absmax)
+      hipLaunchKernelGGL(k_dequant_codebook<false>, dim3((unsigned)w.N), dim3(256), 0, s, w.codes, w.qc, w.K,
+                         w.row_bits, w.row_offset, w.levels, out);
+    else
+      hipLaunchKernelGGL(k_dequant_codebook<true>, dim3((unsigned)w.N), dim3(256), 0, s, w.codes, w.qc, w.K,
+                         w.row_bits, w.row_offset, w.levels, out);
   }
   return hipGetLastError();
 }
