@@ -203,6 +203,34 @@ def test_split_tail_tiles(lq, torch, direction):
         assert layer.rel_frobenius(bf16_to_f32(gx)[ms], gref) <= BF16_TOL
 
 
+def test_split_tail_tiles_codebook(lq, torch):
+    """The same 264-tile forward over a per-channel codebook weight (random
+    widths, levels and midpoint thresholds per row): the GEMM reads the
+    dequantized weight from the workspace, and the split tiles' partial sums
+    sit behind it in the same workspace."""
+    M, r, alpha = 512, 16, 32.0
+    N, K = 132 * 128, 1024
+    L = syn.small_layer(N, K, M, r, alpha, seed=903)
+    W = syn.weight(L)
+    rng = np.random.default_rng(L.workload_id)
+    bits = rng.integers(1, 5, N).astype(np.uint8)
+    Lv = np.zeros((N, 16), np.float32)
+    T = np.full((N, 15), 3.0, np.float32)
+    for i, b in enumerate(bits):
+        n = 1 << int(b)
+        Lv[i, :n] = np.sort(rng.uniform(-1.0, 1.0, n)).astype(np.float32)
+        T[i, :n - 1] = nf4.midpoint_thresholds(Lv[i, :n])
+    qw = lq.QWeight.from_codebook(dev(torch, W), dev(torch, bits), dev(torch, T), dev(torch, Lv))
+    _, _, cp = oracle_constants(W)
+    packed, _, _ = codebook.quantize(W, bits, T)
+    wd = codebook.dequant(packed, bits, Lv, cp, N, K)
+    X, A, B = syn.activations(L), syn.lora_a(L), syn.lora_b(L)
+    H, _ = lq.qlora_forward(qw, bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits), alpha)
+    ms = np.unique(np.concatenate([sample(rng, 256, 32), 256 + sample(rng, 256, 32)]))
+    Href, _ = layer.forward(wd, X.f32[ms], A.f32, B.f32, alpha, r)
+    assert layer.rel_frobenius(bf16_to_f32(H)[ms], Href) <= BF16_TOL
+
+
 def test_q_proj_forward_f32_elementwise_bound(lq, torch):
     """q_proj forward with float32 H (4096 x 4096, 2048 tokens, r = 16) on
     sampled (token, output) pairs, each element within a worst-case rounding
