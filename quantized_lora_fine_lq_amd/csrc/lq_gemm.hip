@@ -1276,7 +1276,7 @@ __global__ __launch_bounds__(256) void k_transpose_u16(const uint16_t* __restric
 // into [hi(P)^T ; lo(P)^T] (bfloat16 [2r][32]; hi + lo carries P to about
 // 2^-17) in LDS, so an MFMA A fragment is one 16-byte LDS read. The Q tile
 // [32 m x 128 c] goes through LDS too and is gathered along m for the B
-// fragments. Workgroup: 128 columns x one m-split, wave: 32 columns, MFMA
+// fragments. Both are loaded one chunk ahead. Workgroup: 128 columns x one m-split, wave: 32 columns, MFMA
 // 32x32x16 over the 2r product rows; hi and lo rows are added in registers
 // when r % 32 == 0 or r == 16 (partner row in the same lane), otherwise both
 // are kept. Each workgroup writes the partial sums of its m-split;
@@ -1341,22 +1341,13 @@ __global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_
       pv[q] = (idx < 32 * r && m < m_end) ? P[m * r + (idx - row * r)] : 0.0f;
     }
   };
-  load_p(m_begin);
-  for (int64_t mb = m_begin; mb < m_end; mb += 32) {
-    // sP[j][m - mb] = hi(P[m][j]), sP[j + r][m - mb] = lo(P[m][j]); zero past m_end
+  // the Q tile of a chunk: thread t takes 16-byte pieces t and t + 256 of the
+  // 32 x 128 tile (zero past m_end and C), loaded one chunk ahead as well
+  u32x4_t qv[2];
+  auto load_q = [&](int64_t mb) {
 #pragma unroll
-    for (int q = 0; q < PQ; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const int idx = threadIdx.x + 256 * q;
-      if (idx < 32 * r) {
-        const int row = idx / r, j = idx - row * r;
-        float hi, lo;
-        split_bf16(pv[q], hi, lo);
-        sP[j * CS_PP + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
-        sP[(j + r) * CS_PP + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
-      }
-    }
-    load_p(mb + 32);
-    for (int idx = threadIdx.x; idx < 32 * 16; idx += 256) {
       const int row = idx / 16, cc = (idx % 16) * 8;
       const int64_t m = mb + row, c = c0 + cc;
       u32x4_t v;
@@ -1370,8 +1361,31 @@ __global__ __launch_bounds__(256) void k_col_skinny(ColJob j0, ColJob j1, int64_
             v[e / 2] = lo | (hi << 16);
           }
       }
-      *reinterpret_cast<u32x4_t*>(sQ + row * (128 + 8) + cc) = v;
+      qv[q] = v;
     }
+  };
+  load_p(m_begin);
+  load_q(m_begin);
+  for (int64_t mb = m_begin; mb < m_end; mb += 32) {
+    // sP[j][m - mb] = hi(P[m][j]), sP[j + r][m - mb] = lo(P[m][j]); zero past m_end
+#pragma unroll
+    for (int q = 0; q < PQ; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      if (idx < 32 * r) {
+        const int row = idx / r, j = idx - row * r;
+        float hi, lo;
+        split_bf16(pv[q], hi, lo);
+        sP[j * CS_PP + row] = (uint16_t)(pack_bf16x2(hi, 0.f) & 0xFFFFu);
+        sP[(j + r) * CS_PP + row] = (uint16_t)(pack_bf16x2(lo, 0.f) & 0xFFFFu);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      *reinterpret_cast<u32x4_t*>(sQ + (idx / 16) * (128 + 8) + (idx % 16) * 8) = qv[q];
+    }
+    load_p(mb + 32);
+    load_q(mb + 32);
     __syncthreads();
     u32x4_t af[2][JT2];
 #pragma unroll
