@@ -1171,9 +1171,51 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
   f32x4_t acc[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr bool PIPE = RT == 0 && JT >= 3;
+  if constexpr (PIPE) {
+    // r > 32: two register sets of one block each, the loads of the next in
+    // flight while the current one is multiplied (blocks, then halves, then
+    // row tiles: the same accumulation order as one set at a time). At
+    // r = 64 over 11008 columns 65.0 -> 59.1 us; at r <= 32 the single set
+    // of up to four blocks below was faster.
+    constexpr int U = 1;
+    auto load = [&](int64_t bk, u32x4_t (&a)[U][2], u32x4_t (&b)[U][2][JT]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t cc = 64 * (bk + u) + 8 * h;   // + 16 lg in the row pointers
+          const bool ok = bk + u < b_end && cc + 16 * lg + 8 <= C;
+          const int64_t off = ok ? cc : -16 * lg;     // a lane past the end reads columns 0..7 and adds 0
+          a[u][h] = ld16(qrow + off);
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) b[u][h][jt] = ld16(rrow[jt] + off);
+          if (!ok) zero(a[u][h]);
+        }
+    };
+    auto mma = [&](const u32x4_t (&a)[U][2], const u32x4_t (&b)[U][2][JT]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt)
+            acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][h]), as_bf16x8(b[u][h][jt]), acc[jt],
+                                                              0, 0, 0);
+    };
+    u32x4_t a0[U][2], b0[U][2][JT], a1[U][2], b1[U][2][JT];
+    if (b_begin < b_end) load(b_begin, a0, b0);
+    for (int64_t bk = b_begin; bk < b_end; bk += 2 * U) {
+      if (bk + U < b_end) load(bk + U, a1, b1);
+      mma(a0, b0);
+      if (bk + U >= b_end) break;
+      if (bk + 2 * U < b_end) load(bk + 2 * U, a0, b0);
+      mma(a1, b1);
+    }
+  }
   // 64-column blocks with loads in flight together
-  constexpr int U = RT ? (JT == 1 ? 4 : (JT == 2 ? 2 : 1)) : (JT <= 2 ? 4 : (JT <= 4 ? 2 : 1));
-  for (int64_t bk = b_begin; bk < b_end; bk += U) {
+  constexpr int U = RT ? (JT == 1 ? 4 : (JT == 2 ? 2 : 1)) : (JT <= 2 ? 4 : 1);
+  for (int64_t bk = b_begin; !PIPE && bk < b_end; bk += U) {
     u32x4_t a[U][2], b[U][2][JT];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -1464,7 +1506,7 @@ hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint
   const dim3 grid((unsigned)((M + 15) / 16));
   switch ((r + 15) / 16) {
 #define LQ_RS(JT, W) case JT: hipLaunchKernelGGL((k_row_skinny<JT, W, 0>), grid, dim3(64 * W), 0, s, Q, M, C, R, r, out); break;
-    LQ_RS(1, 16) LQ_RS(2, 16) LQ_RS(3, 16) LQ_RS(4, 16) LQ_RS(5, 8) LQ_RS(6, 8) LQ_RS(7, 8) LQ_RS(8, 8)
+    LQ_RS(1, 16) LQ_RS(2, 16) LQ_RS(3, 8) LQ_RS(4, 8) LQ_RS(5, 8) LQ_RS(6, 8) LQ_RS(7, 8) LQ_RS(8, 8)
 #undef LQ_RS
     default: return hipErrorInvalidValue;
   }
