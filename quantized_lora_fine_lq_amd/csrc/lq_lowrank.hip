@@ -511,12 +511,15 @@ __global__ __launch_bounds__(256) void k_lowrank_sqerr(const float* __restrict__
   if (threadIdx.x == 0) part[blockIdx.x] = ((sW[0] + sW[1]) + sW[2]) + sW[3];
 }
 
+// Fixed-order sum of n partials: lane l adds partials l, l + 64, ... in
+// order, then the 64 lane sums are added pairwise (a fixed tree). One thread
+// adding all 1024 in sequence took 59 us.
 __global__ __launch_bounds__(64) void k_sum_doubles(const double* __restrict__ part, int n, double* __restrict__ out) {
-  if (threadIdx.x == 0) {
-    double v = 0.0;
-    for (int i = 0; i < n; ++i) v += part[i];
-    *out = v;
-  }
+  double v = 0.0;
+  for (int i = threadIdx.x; i < n; i += 64) v += part[i];
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = v + __shfl_xor(v, m);
+  if (threadIdx.x == 0) *out = v;
 }
 
 static unsigned grid_for(int64_t items, int64_t per_wg, int64_t cap) {
