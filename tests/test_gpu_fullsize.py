@@ -167,16 +167,19 @@ def test_prefill_layer_full_size(lq, torch, name):
     assert layer.rel_frobenius(bf16_to_f32(gx)[np.ix_(ms, cols)], gref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("direction", ["forward", "backward"])
+@pytest.mark.parametrize("direction", ["forward", "backward", "backward_ragged"])
 def test_split_tail_tiles(lq, torch, direction):
     """264 output tiles of 256 x 128 (33 per XCD: one full round of 32 and one
     more), so the last tile of every XCD runs as two halves of the
     contraction whose partial sums a second kernel adds; every output column
     on 64 sampled tokens against the oracle, bf16 and float32 forward
-    outputs and grad_X."""
+    outputs and grad_X (also with a contraction whose last step is partial,
+    which falls in the second half)."""
     M, r, alpha = 512, 16, 32.0
-    N, K = (132 * 128, 1024) if direction == "forward" else (1024, 132 * 128)
-    L = syn.small_layer(N, K, M, r, alpha, seed=901 if direction == "forward" else 902)
+    # backward_ragged: a contraction of 1000 rows (16 steps, the last one partial)
+    N, K = {"forward": (132 * 128, 1024), "backward": (1024, 132 * 128),
+            "backward_ragged": (1000, 132 * 128)}[direction]
+    L = syn.small_layer(N, K, M, r, alpha, seed={"forward": 901, "backward": 902, "backward_ragged": 904}[direction])
     W = syn.weight(L)
     rng = np.random.default_rng(L.workload_id)
     c_ref, dqp, cp = oracle_constants(W)
