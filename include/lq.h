@@ -230,7 +230,8 @@ size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
  * For an NF4 weight W' is never materialised in memory: packed codes are
  * dequantized inside the GEMM (M <= 16 and K <= 33728 use the memory-bound
  * GEMV kernel, other shapes the MFMA GEMM; the environment variable
- * LQ_FORCE_PATH=gemm selects the GEMM at any M, a testing aid). A codebook
+ * LQ_FORCE_PATH=gemm selects the GEMM at any M, a testing aid); for r <= 32
+ * the GEMV forms t itself, so the whole forward is one launch. A codebook
  * weight at M <= 16 (K <= 32576) goes through its own GEMV kernel, which
  * reads the bit-planes directly; at other shapes it is first dequantized
  * into the workspace by its per-channel dequantization kernel ([LowRA]

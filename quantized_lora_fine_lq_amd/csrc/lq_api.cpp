@@ -310,6 +310,9 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
   float* t = t_save ? t_save : t_ws;
   const float scale = alpha / (float)r;
+  // decode sizes with a small NF4 weight and r <= 32: the GEMV forms t itself
+  if (gemv && gemv_forms_t(q, M, r))
+    return launch_status(launch_gemv_fwd(q, X, M, nullptr, B, r, scale, H, h_dtype, s, A, t));
   hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, s);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
   if (gemv) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);

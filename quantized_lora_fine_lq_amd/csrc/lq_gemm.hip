@@ -713,14 +713,24 @@ __global__ __launch_bounds__(256) void k_split_fixup(GemmParams p, int64_t n_spl
 struct GemvParams {
   const uint16_t* X;   // [M, K]
   int64_t M;
-  const float* t;      // [M, r]
+  const float* t;      // [M, r], or null when the kernel forms t = X A^T itself
   const uint16_t* B;   // [N, r]
   int r;
   float s;
   void* out;
   QWeight w;
   Nf4Levels lv;
+  const uint16_t* A;   // [r, K] (t formed in the kernel)
+  float* t_out;        // [M, r]: t, written by workgroup 0 (t formed in the kernel), or null
 };
+
+// t = X A^T inside the NF4 decode kernel, for r <= GV_TR: every workgroup
+// forms it over the same stages as its main loop (wave w: stages w, w + 8,
+// ..., the X fragments of the main loop's layout and the matching 8-element
+// pieces of A's rows as the MFMA's second operand), the 8 waves' partial sums
+// are added in wave order in LDS, and the LoRA term is formed from that t.
+// One launch instead of two for the whole forward at decode sizes.
+constexpr int GV_TR = 32;
 
 constexpr int GV_WAVES = 8;        // K splits per workgroup
 constexpr int GV_CTAB = 8448;      // floats of LDS for the constant table (33 KB: two workgroups per CU)
@@ -836,13 +846,16 @@ __device__ __forceinline__ void gv_compute(const GvStage<RG>& st, const f32x2_t*
     }
 }
 
-template <int RG, bool DQ, bool OUT_F32>
+template <int RG, bool DQ, bool OUT_F32, bool TK>
 __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
   // one LDS object with the pair table first: at LDS address 0 a lookup
   // address is one shift of the code byte
+  constexpr int JTK = GV_TR / 16;
   struct __attribute__((aligned(16))) Lds {
     f32x2_t pair[256];
     float c[GV_CTAB];   // constants [16 RG rows][nb + 1]; then partial sums
+    f32x4_t tp[TK ? GV_WAVES * JTK * 64 : 1];   // TK: the waves' partial sums of t
+    float t[TK ? 16 * GV_TR : 1];              // TK: t [16 tokens][r]
   };
   __shared__ Lds lds;
   f32x2_t* sPair = lds.pair;
@@ -907,14 +920,62 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
       sC[rr * pitch + bl] = c;
     }
   }
+  if constexpr (TK) {
+    // this wave's partial t over its stages: MFMA rows = tokens (X rows li,
+    // clamped to M - 1), columns = rows 16 jt + li of A (clamped to r - 1;
+    // their sums are not used), the main loop's k layout
+    f32x4_t tacc[JTK];
+#pragma unroll
+    for (int jt = 0; jt < JTK; ++jt) tacc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* arow[JTK];
+#pragma unroll
+    for (int jt = 0; jt < JTK; ++jt) arow[jt] = p.A + (int64_t)min(16 * jt + li, p.r - 1) * K;
+    for (int i = 0; i < nsw; ++i) {
+      const int bl = 2 * (wave + GV_WAVES * i) + (lg >> 1);
+      const bool live = bl < nb;   // K/64 odd: the last stage's second block is past the row
+      const int64_t off = (int64_t)min(bl, nb - 1) * 64 + 32 * (lg & 1);
+      u32x4_t xa[4], aa[JTK][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = ld16(xrow + off + 8 * u);
+#pragma unroll
+        for (int jt = 0; jt < JTK; ++jt) aa[jt][u] = ld16(arow[jt] + off + 8 * u);
+        if (!live) xa[u] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int jt = 0; jt < JTK; ++jt)
+          if (jt == 0 || p.r > 16)   // r <= 16: one column tile
+            tacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[u]), as_bf16x8(aa[jt][u]), tacc[jt], 0,
+                                                               0, 0);
+    }
+#pragma unroll
+    for (int jt = 0; jt < JTK; ++jt) lds.tp[(wave * JTK + jt) * 64 + lane] = tacc[jt];
+  }
   __syncthreads();
+  if constexpr (TK) {
+    // t[m][j] = sum over the waves in order; lane (li, lg) of a partial holds
+    // tokens 4 lg + v of column li
+    for (int idx = threadIdx.x; idx < 16 * p.r; idx += 64 * GV_WAVES) {
+      const int m = idx / p.r, j = idx - m * p.r;
+      const int ln = (j & 15) + 16 * (m >> 2), v = m & 3;
+      float acc_t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < GV_WAVES; ++w) acc_t += lds.tp[(w * JTK + (j >> 4)) * 64 + ln][v];
+      lds.t[idx] = acc_t;
+      if (blockIdx.x == 0 && m < p.M && p.t_out) p.t_out[idx] = acc_t;
+    }
+    __syncthreads();
+  }
 
   // the LoRA operands are loaded only now, one row group at a time: held
   // through the table build they would cost registers
+  const float* tsrc = TK ? lds.t : p.t;
   f32x4_t acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    acc[g] = gv_lora_mfma(gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
+    acc[g] = gv_lora_mfma(gv_lora_load(tsrc, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
                           f32x4_t{0.f, 0.f, 0.f, 0.f});
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1767,21 +1828,37 @@ bool gemv_supported(const QWeight& w) {
   return w.format == LQ_FMT_NF4 && gemv_rg(w.N, w.K, 1) > 0;
 }
 
-template <int RG>
+// Every workgroup that forms t reads all of X and A (from L2) for it. That
+// pays while the grid is at most one workgroup per CU (measured: 17.5 ->
+// 12.3 us at 1024 x 1024, 19.9 -> 16.9 at 4096 x 4096 and 51.5 -> 46.9 at
+// N = 4096, K = 14336, 16 tokens) and costs once CUs hold two (8192 x 8192,
+// one token: 23.6 -> 33.3 us; 28672 x 8192: 46.1 -> 54.8).
+constexpr int64_t GV_TK_MAX_WGS = 8 * kCusPerXcd;
+
+bool gemv_forms_t(const QWeight& w, int64_t M, int r) {
+  if (w.format != LQ_FMT_NF4 || r > GV_TR || M < 1 || M > 16 || !gemv_supported(w)) return false;
+  const int rg = gemv_rg(w.N, w.K, M);
+  return (w.N + 16 * rg - 1) / (16 * rg) <= GV_TK_MAX_WGS;
+}
+
+template <int RG, bool TK>
 static void launch_gemv_rg(const GemvParams& p, bool dq, bool f32, hipStream_t st) {
   const dim3 grid((unsigned)((p.w.N + 16 * RG - 1) / (16 * RG))), block(64 * GV_WAVES);
-  if (dq && f32) hipLaunchKernelGGL((k_gemv_nf4<RG, true, true>), grid, block, 0, st, p);
-  else if (dq) hipLaunchKernelGGL((k_gemv_nf4<RG, true, false>), grid, block, 0, st, p);
-  else if (f32) hipLaunchKernelGGL((k_gemv_nf4<RG, false, true>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((k_gemv_nf4<RG, false, false>), grid, block, 0, st, p);
+  if (dq && f32) hipLaunchKernelGGL((k_gemv_nf4<RG, true, true, TK>), grid, block, 0, st, p);
+  else if (dq) hipLaunchKernelGGL((k_gemv_nf4<RG, true, false, TK>), grid, block, 0, st, p);
+  else if (f32) hipLaunchKernelGGL((k_gemv_nf4<RG, false, true, TK>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((k_gemv_nf4<RG, false, false, TK>), grid, block, 0, st, p);
 }
 
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
-                           hipStream_t st) {
+                           hipStream_t st, const uint16_t* A, float* t_out) {
   if (!gemv_supported(w)) return hipErrorInvalidValue;
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
+  p.A = A; p.t_out = t_out;
+  const bool tk = t == nullptr;   // form t = X A^T in the kernel (NF4, r <= GV_TR)
+  if (tk && (w.format != LQ_FMT_NF4 || !A || r > GV_TR)) return hipErrorInvalidValue;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
   if (w.format == LQ_FMT_CODEBOOK) {
     const size_t lds = cb_gemv_lds_bytes(w.K);
@@ -1795,9 +1872,15 @@ hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const
   }
   const int rg = gemv_rg(w.N, w.K, M);
   LQ_DASSERT(M >= 1 && M <= 16 && w.K % 64 == 0 && (int64_t)16 * rg * (w.K / 64 + 1) <= GV_CTAB);
-  if (rg == 4) launch_gemv_rg<4>(p, dq, f32, st);
-  else if (rg == 2) launch_gemv_rg<2>(p, dq, f32, st);
-  else launch_gemv_rg<1>(p, dq, f32, st);
+  if (tk) {
+    if (rg == 4) launch_gemv_rg<4, true>(p, dq, f32, st);
+    else if (rg == 2) launch_gemv_rg<2, true>(p, dq, f32, st);
+    else launch_gemv_rg<1, true>(p, dq, f32, st);
+  } else {
+    if (rg == 4) launch_gemv_rg<4, false>(p, dq, f32, st);
+    else if (rg == 2) launch_gemv_rg<2, false>(p, dq, f32, st);
+    else launch_gemv_rg<1, false>(p, dq, f32, st);
+  }
   return hipGetLastError();
 }
 

@@ -186,8 +186,12 @@ hipError_t launch_gemm_bwd(const QWeight& w, const uint16_t* G, int64_t M, const
 // The decode GEMV handles NF4 weights whose per-workgroup constant table
 // fits in LDS (K <= 33728: one row group of 16 rows); others use the GEMM.
 bool gemv_supported(const QWeight& w);
+bool gemv_forms_t(const QWeight& w, int64_t M, int r);
+// t == nullptr: the kernel forms t = X A^T itself (NF4 weights, r <= 32) and
+// writes it to t_out when that is not null; gemv_forms_t says when that is
+// the faster choice.
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
-                           hipStream_t st);
+                           hipStream_t st, const uint16_t* A = nullptr, float* t_out = nullptr);
 
 }  // namespace lq

@@ -306,6 +306,23 @@ def test_decode_gemv_full_size(lq, torch, decode_case, M):
     assert layer.rel_frobenius(host(H32)[:, rows], Href) <= F32_TOL
 
 
+@pytest.mark.parametrize("M", list(syn.DECODE_TOKENS))
+def test_decode_forward_full_size(lq, torch, decode_case, M):
+    """The whole forward at decode sizes (one launch: t = X A^T is formed
+    inside the GEMV): t in full and sampled rows of H."""
+    L, W, c_ref, dqp, cp, absmax, qw, rows = decode_case
+    _, _, wd_rows = oracle_rows(W, rows, cp)
+    X, A, B = syn.activations(L, M), syn.lora_a(L), syn.lora_b(L)
+    Xd, Ad, Bd = bf16_dev(torch, X.bits), bf16_dev(torch, A.bits), bf16_dev(torch, B.bits)
+    H, t = lq.qlora_forward(qw, Xd, Ad, Bd, L.alpha)
+    H32, t32 = lq.qlora_forward(qw, Xd, Ad, Bd, L.alpha, out_dtype=torch.float32)
+    Href, tref = layer.forward(wd_rows, X.f32, A.f32, B.f32[rows], L.alpha, L.r)
+    assert layer.rel_frobenius(host(t), tref) <= 1e-5
+    assert torch.equal(t, t32)
+    assert layer.rel_frobenius(bf16_to_f32(H)[:, rows], Href) <= BF16_TOL
+    assert layer.rel_frobenius(host(H32)[:, rows], Href) <= F32_TOL
+
+
 def test_codebook_layer_full_size(lq, torch):
     """1.75-bit per-channel layer with its tables learned on the GPU by the
     weighted Lloyd-Max learner (checked against the oracle's learner on

@@ -223,6 +223,9 @@ def oracle_wd(W, double=True):
     (256, 512, 4, 24, 8.0),        # r not a multiple of 16
     (100, 256, 40, 16, 32.0),      # N % 8 != 0: element-wise epilogue
     (136, 192, 600, 40, 16.0),     # three M tiles, two LoRA steps (2r = 80)
+    (256, 512, 16, 32, 8.0),       # GEMV forming t itself at its largest rank
+    (300, 1088, 7, 17, 16.0),      # same, two column tiles of t, odd K/64, ragged N
+    (200, 256, 9, 33, 16.0),       # rank just past that: t from the separate kernel
 ])
 def test_forward(lq, torch, N, K, M, r, alpha):
     L, W, X, A, B = make_layer(100 + M, N, K, M, r, alpha)
@@ -293,7 +296,8 @@ def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
     (40, 17024, 5, 8, False),      # same, K/64 not a multiple of 16, ragged N
 ])
 def test_decode_gemv_row_groups(lq, torch, monkeypatch, N, K, M, r, double):
-    """The decode kernel at every row-group count it launches with, against
+    """The decode kernel at every row-group count it launches with, forming t
+    itself (grids of at most 256 workgroups, r <= 32) or reading it, against
     the oracle and against the GEMM path on the same inputs."""
     rng = np.random.default_rng(N + K + M)
     W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -302,10 +306,11 @@ def test_decode_gemv_row_groups(lq, torch, monkeypatch, N, K, M, r, double):
     B = syn.to_bf16_bits((rng.standard_normal((N, r)) * 0.02).astype(np.float32))
     qw = lq.QWeight.from_weight(dev(torch, W), double_quantize=double)
     args = (qw, bf16_dev(torch, X), bf16_dev(torch, A), bf16_dev(torch, B), 32.0)
-    H, _ = lq.qlora_forward(*args)
+    H, t = lq.qlora_forward(*args)
     H32, _ = lq.qlora_forward(*args, out_dtype=torch.float32)
-    Href, _ = layer.forward(oracle_wd(W, double), syn.bf16_bits_to_f32(X), syn.bf16_bits_to_f32(A),
-                            syn.bf16_bits_to_f32(B), 32.0)
+    Href, tref = layer.forward(oracle_wd(W, double), syn.bf16_bits_to_f32(X), syn.bf16_bits_to_f32(A),
+                               syn.bf16_bits_to_f32(B), 32.0)
+    assert layer.rel_frobenius(host(t), tref) <= 1e-5
     assert layer.rel_frobenius(bf16_to_f32(H), Href) <= BF16_TOL
     assert layer.rel_frobenius(host(H32), Href) <= F32_TOL
     monkeypatch.setenv("LQ_FORCE_PATH", "gemm")
