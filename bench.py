@@ -3,9 +3,9 @@
 
 One step = the whole path on the Llama-7B q_proj workload (W 4096x4096
 float32 ~ N(0, 0.02^2), 2048 bf16 tokens = batch 4 x seq 512, LoRA r = 16,
-alpha = 32): NF4 quantize -> double quantization -> dequant to bf16 ->
-forward (t = X A^T, fused dequant-GEMM + LoRA) -> backward (u, dB, grad_X,
-dA). Inputs are resident in HBM before timing; four input sets are rotated
+alpha = 32): NF4 quantize -> double quantization and dequant to bf16 (one
+call) -> forward (t = X A^T, fused dequant-GEMM + LoRA) -> backward (u, dB,
+grad_X, dA). Inputs are resident in HBM before timing; four input sets are rotated
 so the 256 MB Infinity Cache cannot hold the step's working set.
 
 value = algorithmic GEMM + LoRA flops of the forward and backward per step
@@ -118,6 +118,8 @@ class Dev:
         self.ld_ws = torch.empty(max(self.ld_ws_bytes, 1), dtype=torch.uint8, device=dev)
         self.fw_ws_bytes = lq.lib.lq_dequant_gemm_workspace(self.qw.ref(), M, r)
         self.fw_ws = torch.empty(max(self.fw_ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.qf_ws_bytes = lq.lib.lq_forward_workspace(self.qw.ref(), M, r)
+        self.qf_ws = torch.empty(max(self.qf_ws_bytes, 1), dtype=torch.uint8, device=dev)
         if G is not None:
             self.gX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
             self.dA = torch.empty(r, K, dtype=torch.float32, device=dev)
@@ -146,9 +148,13 @@ class Calls:
         self.args_dq = (P(d.absmax), L.N * L.K // 64, 256, P(d.aq), P(d.s2), P(d.mu), P(d.dq_ws),
                         d.dq_ws_bytes, self.stream)
         self.args_deq = (d.qw.ref(), P(d.Wd), self.stream)
+        self.args_dqd = (P(d.absmax), L.N * L.K // 64, 256, P(d.aq), P(d.s2), P(d.mu), P(d.codes), P(d.Wd),
+                         P(d.dq_ws), d.dq_ws_bytes, self.stream)
         self.args_ld = (P(d.X), d.M, L.K, P(d.A), d.r, P(d.t), P(d.ld_ws), d.ld_ws_bytes, self.stream)
         self.args_fwd = (d.qw.ref(), P(d.X), d.M, P(d.t), P(d.B), d.r, self.alpha, P(d.H), 1,
                          P(d.fw_ws), d.fw_ws_bytes, self.stream)
+        self.args_qfwd = (d.qw.ref(), P(d.X), d.M, P(d.A), P(d.B), d.r, self.alpha, P(d.H), 1, P(d.t),
+                          P(d.qf_ws), d.qf_ws_bytes, self.stream)
         if d.G is not None:
             self.args_bwd = (d.qw.ref(), P(d.X), P(d.G), d.M, P(d.A), P(d.B), d.r, self.alpha, P(d.t),
                              P(d.gX), P(d.dA), P(d.dB), P(d.bw_ws), d.bw_ws_bytes, self.stream)
@@ -171,11 +177,17 @@ class Calls:
     def dequant(self):
         self.chk(self.lib.lq_dequant(*self.args_deq), "dequant")
 
+    def double_quant_dequant(self):
+        self.chk(self.lib.lq_double_quant_dequant(*self.args_dqd), "double_quant_dequant")
+
     def lora_down(self):
         self.chk(self.lib.lq_lora_down(*self.args_ld), "lora_down")
 
     def fwd_gemm(self):
         self.chk(self.lib.lq_dequant_gemm(*self.args_fwd), "dequant_gemm")
+
+    def qlora_forward(self):
+        self.chk(self.lib.lq_qlora_forward(*self.args_qfwd), "qlora_forward")
 
     def backward(self):
         self.chk(self.lib.lq_qlora_backward(*self.args_bwd), "backward")
@@ -187,8 +199,7 @@ class Calls:
         """One pass of the path; `ev` = (start, end) events put around the
         forward dequant-GEMM launch on the same stream."""
         self.quantize()
-        self.double_quant()
-        self.dequant()
+        self.double_quant_dequant()
         self.lora_down()
         if ev is not None:
             ev[0].record()
@@ -296,6 +307,7 @@ def codec_bytes(L, M=0):
         "profile": 4 * n,
         "double_quant": 4 * n_b + n_b + 4 * n_d + 4,
         "dequant": packed + 2 * n,
+        "double_quant_dequant": 4 * n_b + n // 2 + n_b + 4 * n_d + 4 + 2 * n,
         "gemv": packed + 2 * L.K * M + 2 * L.N * L.r + 2 * L.N * M + 4 * M * L.r,
     }
 
@@ -534,6 +546,9 @@ class CodecSet:
         self.double_quant = lambda: chk(lib.lq_double_quant(P(self.absmax), n // 64, 256, P(self.aq), P(self.s2),
                                                             P(self.mu), P(self.dq_ws), self.dq_b, st), "double_quant")
         self.dequant = lambda: chk(lib.lq_dequant(self.qw.ref(), P(self.Wd), st), "dequant")
+        self.double_quant_dequant = lambda: chk(lib.lq_double_quant_dequant(
+            P(self.absmax), n // 64, 256, P(self.aq), P(self.s2), P(self.mu), P(self.codes), P(self.Wd),
+            P(self.dq_ws), self.dq_b, st), "double_quant_dequant")
 
 
 def rotation_count(n_weights, min_bytes=1 << 30):
@@ -727,11 +742,8 @@ def main():
             rec("linear1k.dequant", time_arm(torch, [c1.dequant], arm_s), None, "us")
             rec("linear1k.lora_down", time_arm(torch, [c1.lora_down], arm_s), None, "us")
             rec("linear1k.dequant_gemm_fwd", time_arm(torch, [c1.fwd_gemm], arm_s), None, "us")
-
-            def fwd1():
-                c1.lora_down()
-                c1.fwd_gemm()
-            rec("linear1k.qlora_forward", time_arm(torch, [fwd1], arm_s), None, "us")
+            # the whole forward in one call (at 16 tokens the GEMV forms t itself)
+            rec("linear1k.qlora_forward", time_arm(torch, [c1.qlora_forward], arm_s), None, "us")
             del c1, d1
 
         if want("q_proj"):
@@ -746,6 +758,8 @@ def main():
                 rot(cb["double_quant"]))
             rec("q_proj.dequant", time_arm(torch, [c.dequant for c in cs], arm_s), cb["dequant"], "GB/s",
                 rot(cb["dequant"]))
+            rec("q_proj.double_quant_dequant", time_arm(torch, [c.double_quant_dequant for c in cs], arm_s),
+                cb["double_quant_dequant"], "GB/s", rot(cb["double_quant_dequant"]))
             del cs
             torch.cuda.empty_cache()
             rec("q_proj.lora_down", time_arm(torch, [c.lora_down for c in calls], arm_s), fl["lora_down"], "TFLOP/s")

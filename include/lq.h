@@ -219,6 +219,28 @@ int lq_double_quant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
  */
 int lq_dequant(const lq_qweight* w, uint16_t* out, void* stream);
 
+/*
+ * Double quantization followed by dequantization to bfloat16, in one call:
+ * the results of lq_double_quant on absmax, then of lq_dequant on the NF4
+ * weight whose packed codes are `codes` with the new double-quantized
+ * constants ([QLoRA] Contribution 2, and the introduction's dequantization
+ * to BFloat16). Up to 1024 double-quantization blocks (262144 constants,
+ * 16.7 M weights) the encoder and the dequantization are one kernel: each
+ * workgroup encodes 256 constants and dequantizes the 16384 weights they
+ * scale, so the constants are not read back. Larger weights run the two
+ * calls' kernels in turn.
+ *   absmax, absmax_q, dq_scale, dq_mean, workspace  as lq_double_quant
+ *     (workspace: lq_double_quant_workspace bytes)
+ *   codes [n_blocks * 32] packed NF4 codes (two per byte, first code in the
+ *         high nibble), read; out [n_blocks * 64] bfloat16, written (the
+ *         weight's row-major element order)
+ *   codes and out 16-byte aligned
+ * Errors: as lq_double_quant.
+ */
+int lq_double_quant_dequant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
+                            uint8_t* absmax_q, float* dq_scale, float* dq_mean, const uint8_t* codes,
+                            uint16_t* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for lq_qlora_forward with M tokens and rank r. */
 size_t lq_forward_workspace(const lq_qweight* w, int64_t M, int32_t r);
 

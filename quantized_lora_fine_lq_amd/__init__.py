@@ -62,6 +62,8 @@ SIGNATURES = {
     "lq_profile_nf4": (ctypes.c_int, [c_vp, c_i32, c_i64, c_i64, c_i32, ctypes.c_double, c_vp, c_vp, c_sz, c_vp]),
     "lq_double_quant_workspace": (c_sz, [c_i64, c_i32]),
     "lq_double_quant": (ctypes.c_int, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "lq_double_quant_dequant": (ctypes.c_int, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                               c_vp]),
     "lq_dequant": (ctypes.c_int, [QW_P, c_vp, c_vp]),
     "lq_forward_workspace": (c_sz, [QW_P, c_i64, c_i32]),
     "lq_qlora_forward": (ctypes.c_int, [QW_P, c_vp, c_i64, c_vp, c_vp, c_i32, c_f32, c_vp, c_i32,
@@ -221,6 +223,28 @@ def double_quant(absmax, dq_blocksize: int = 256):
     _check(lib.lq_double_quant(_ptr(absmax), n_b, dq_blocksize, _ptr(q), _ptr(s2), _ptr(mu), _ptr(ws),
                                ws_bytes, _stream(absmax.device)), "lq_double_quant")
     return q, s2, mu
+
+
+def double_quant_dequant(codes, absmax, shape, dq_blocksize: int = 256):
+    """NF4 codes uint8 [n_b*32] and absmax f32 [n_b] -> (absmax_q, dq_scale, dq_mean, W' bf16 of `shape`):
+    double quantization, then the dequantized weight from the new constants."""
+    torch = _torch()
+    _contig_cuda(absmax, "absmax")
+    _contig_cuda(codes, "codes")
+    n_b = absmax.numel()
+    if codes.numel() != 32 * n_b or shape[0] * shape[1] != 64 * n_b:
+        raise ValueError("codes, absmax and shape disagree")
+    n_d = (n_b + dq_blocksize - 1) // dq_blocksize
+    dev = absmax.device
+    q = torch.empty(n_b, dtype=torch.uint8, device=dev)
+    s2 = torch.empty(n_d, dtype=torch.float32, device=dev)
+    mu = torch.empty(1, dtype=torch.float32, device=dev)
+    out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=dev)
+    ws_bytes = lib.lq_double_quant_workspace(n_b, dq_blocksize)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.lq_double_quant_dequant(_ptr(absmax), n_b, dq_blocksize, _ptr(q), _ptr(s2), _ptr(mu), _ptr(codes),
+                                       _ptr(out), _ptr(ws), ws_bytes, _stream(dev)), "lq_double_quant_dequant")
+    return q, s2, mu, out
 
 
 class QWeight:

@@ -271,6 +271,20 @@ int lq_double_quant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
                                            (double*)workspace, (hipStream_t)stream));
 }
 
+int lq_double_quant_dequant(const float* absmax, int64_t n_blocks, int32_t dq_blocksize,
+                            uint8_t* absmax_q, float* dq_scale, float* dq_mean, const uint8_t* codes,
+                            uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!absmax || !absmax_q || !dq_scale || !dq_mean || !codes || !out) return LQ_ERR_ARG;
+  if (!al(absmax, 4) || !al(dq_scale, 4) || !al(dq_mean, 4) || !al(codes, kVec) || !al(out, kVec) ||
+      !al(workspace, kVec))
+    return LQ_ERR_ARG;
+  if (n_blocks <= 0) return LQ_ERR_SHAPE;
+  if (dq_blocksize != 256) return LQ_ERR_UNSUPPORTED;
+  if (!workspace || ws_bytes < lq_double_quant_workspace(n_blocks, dq_blocksize)) return LQ_ERR_WORKSPACE;
+  return launch_status(launch_double_quant_dequant(absmax, n_blocks, absmax_q, dq_scale, dq_mean, codes, out,
+                                                   (double*)workspace, (hipStream_t)stream));
+}
+
 int lq_dequant(const lq_qweight* w, uint16_t* out, void* stream) {
   QWeight q;
   const int st = check_qweight(w, &q);

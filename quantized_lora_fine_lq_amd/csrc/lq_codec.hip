@@ -270,18 +270,16 @@ __global__ __launch_bounds__(1024) void k_tree_reduce(const double* __restrict__
 // pairs, a butterfly over the 64 lanes, then the 4 wave sums in pairs, which
 // is the same perfect binary tree, so every workgroup gets the same value;
 // workgroup 0 stores it. This saves the launch of k_tree_reduce.
+// Thread t of workgroup J encodes constant 256 J + t; returns its code and
+// sets s2 (the block's scale) and mu.
 template <bool SUMS>
-__global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, int64_t n_b,
-                                                   const double* __restrict__ sums, int64_t n_sums,
-                                                   float* __restrict__ mean,
-                                                   uint8_t* __restrict__ absmax_q,
-                                                   float* __restrict__ dq_scale) {
-  __shared__ float wmax[4];
-  __shared__ double wsum[4];
+__device__ __forceinline__ uint32_t dq_encode_block(const float* __restrict__ c, int64_t n_b,
+                                                    const double* __restrict__ sums, int64_t n_sums,
+                                                    float* __restrict__ mean, float* wmax, double* wsum,
+                                                    float& s2, float& mu) {
   const int t = threadIdx.x;
   const int64_t j = (int64_t)blockIdx.x * 256 + t;
   const float cj = (j < n_b) ? c[j] : 0.0f;
-  float mu;
   if constexpr (SUMS) {
     double v[4];
 #pragma unroll
@@ -302,15 +300,80 @@ __global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, 
   if ((t & 63) == 0) wmax[t >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float s2 = a / 448.0f;
-  if (t == 0) dq_scale[blockIdx.x] = s2;
+  s2 = a / 448.0f;
   uint32_t code = 0;
   if (s2 > 0.0f) {
     float v = d / s2;
     v = fminf(fmaxf(v, -448.0f), 448.0f);
     code = e4m3_encode(v);
   }
+  return code;
+}
+
+template <bool SUMS>
+__global__ __launch_bounds__(256) void k_dq_encode(const float* __restrict__ c, int64_t n_b,
+                                                   const double* __restrict__ sums, int64_t n_sums,
+                                                   float* __restrict__ mean,
+                                                   uint8_t* __restrict__ absmax_q,
+                                                   float* __restrict__ dq_scale) {
+  __shared__ float wmax[4];
+  __shared__ double wsum[4];
+  float s2, mu;
+  const uint32_t code = dq_encode_block<SUMS>(c, n_b, sums, n_sums, mean, wmax, wsum, s2, mu);
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (threadIdx.x == 0) dq_scale[blockIdx.x] = s2;
   if (j < n_b) absmax_q[j] = (uint8_t)code;
+}
+
+// Double quantization and dequantization to bfloat16 in one launch (up to
+// 1024 double-quantization blocks, where the encoder forms the mean itself):
+// workgroup J encodes constants [256 J, 256 J + 256) as k_dq_encode<true>
+// does, keeps their decoded values c' = code * s2 + mu in LDS and
+// dequantizes the 16384 weights they scale with the arithmetic and layout of
+// k_dequant_nf4<true, 8> (wave w, pass d, lane l: elements
+// 16384 J + 4096 w + 512 d + 8 l .. +7), so the output has the bits of a
+// dequant of the stored constants. The code loads go out first.
+__global__ __launch_bounds__(256) void k_dq_encode_dequant(const float* __restrict__ c, int64_t n_b,
+                                                           const double* __restrict__ sums, int64_t n_sums,
+                                                           float* __restrict__ mean,
+                                                           uint8_t* __restrict__ absmax_q,
+                                                           float* __restrict__ dq_scale,
+                                                           const uint8_t* __restrict__ codes,
+                                                           uint16_t* __restrict__ out, Nf4Levels lv) {
+  __shared__ f32x2_t pair[256];
+  __shared__ float cdec[256];
+  __shared__ float wmax[4];
+  __shared__ double wsum[4];
+  constexpr int P = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = n_b * 64;
+  const int64_t e_base = (int64_t)blockIdx.x * 16384 + 4096 * wave + 8 * lane;
+  uint32_t w[P];
+#pragma unroll
+  for (int d = 0; d < P; ++d) {
+    const int64_t e = min(e_base + 512 * d, n - 8);   // n % 64 == 0; clamped lanes do not store
+    w[d] = *reinterpret_cast<const uint32_t*>(codes + e / 2);
+  }
+  pair[threadIdx.x] = f32x2_t{lv.q[threadIdx.x >> 4], lv.q[threadIdx.x & 15]};
+  float s2, mu;
+  const uint32_t code = dq_encode_block<true>(c, n_b, sums, n_sums, mean, wmax, wsum, s2, mu);
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (threadIdx.x == 0) dq_scale[blockIdx.x] = s2;
+  if (j < n_b) absmax_q[j] = (uint8_t)code;
+  cdec[threadIdx.x] = __builtin_fmaf(e4m3_decode(code), s2, mu);
+  __syncthreads();
+#pragma unroll
+  for (int d = 0; d < P; ++d) {
+    const int64_t e = e_base + 512 * d;
+    const float cp = cdec[64 * wave + 8 * d + (lane >> 3)];
+    u32x4_t o;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const f32x2_t q = pair[(w[d] >> (8 * b)) & 0xFFu];
+      o[b] = pack_bf16x2(q.x * cp, q.y * cp);
+    }
+    if (e < n) *reinterpret_cast<u32x4_t*>(out + e) = o;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -760,6 +823,30 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_b, uint8_t* absmax
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_dq_encode<false>, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b,
                      (const double*)nullptr, (int64_t)0, dq_mean, absmax_q, dq_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant_dequant(const float* absmax, int64_t n_b, uint8_t* absmax_q, float* dq_scale,
+                                      float* dq_mean, const uint8_t* codes, uint16_t* out, double* ws,
+                                      hipStream_t s) {
+  const int64_t n_d = (n_b + 255) / 256;
+  hipError_t e;
+  if (n_d > 1024) {   // the mean takes tree launches of its own: the two calls in turn
+    if ((e = launch_double_quant(absmax, n_b, absmax_q, dq_scale, dq_mean, ws, s)) != hipSuccess) return e;
+    QWeight w{};
+    w.format = LQ_FMT_NF4;
+    w.N = n_b;
+    w.K = 64;
+    w.codes = codes;
+    w.qc.absmax_q = absmax_q;
+    w.qc.dq_scale = dq_scale;
+    w.qc.dq_mean = dq_mean;
+    return launch_dequant(w, out, s);
+  }
+  hipLaunchKernelGGL(k_dq_block_sums, dim3((unsigned)n_d), dim3(64), 0, s, absmax, n_b, ws);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dq_encode_dequant, dim3((unsigned)n_d), dim3(256), 0, s, absmax, n_b, (const double*)ws,
+                     n_d, dq_mean, absmax_q, dq_scale, codes, out, tables().lv);
   return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ hipError_t launch_double_quant(const float* absmax, int64_t n_blocks, uint8_t* a
                                float* dq_scale, float* dq_mean, double* ws, hipStream_t s);
 size_t double_quant_ws_doubles(int64_t n_blocks);
 hipError_t launch_dequant(const QWeight& w, uint16_t* out, hipStream_t s);
+// launch_double_quant, then launch_dequant of the NF4 codes with the new
+// constants (one kernel after the block sums for up to 1024 DQ blocks).
+hipError_t launch_double_quant_dequant(const float* absmax, int64_t n_blocks, uint8_t* absmax_q,
+                                      float* dq_scale, float* dq_mean, const uint8_t* codes, uint16_t* out,
+                                      double* ws, hipStream_t s);
 size_t profile_ws_doubles(int64_t n_blocks);
 hipError_t launch_profile_nf4(const void* W, int dtype, int64_t n_blocks, double tau, double* stats,
                               double* ws, hipStream_t s);

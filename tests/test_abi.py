@@ -33,7 +33,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lq):
     names = declared_symbols()
-    assert len(names) == 37
+    assert len(names) == 38
     dbg = lq.load_debug_library()
     for name in names:
         assert hasattr(lq.lib, name), name
@@ -96,6 +96,12 @@ def test_validation_errors_without_launch(lq):
     assert L.lq_double_quant(fake, 1000, 256, fake, fake, fake, fake, 8, null) == lq.LQ_ERR_WORKSPACE
     assert L.lq_double_quant(fake, 0, 256, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_SHAPE
     assert L.lq_double_quant(null, 10, 256, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_ARG
+    dqd = L.lq_double_quant_dequant
+    assert dqd(fake, 1000, 128, fake, fake, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_UNSUPPORTED
+    assert dqd(fake, 1000, 256, fake, fake, fake, fake, fake, fake, 8, null) == lq.LQ_ERR_WORKSPACE
+    assert dqd(fake, 0, 256, fake, fake, fake, fake, fake, fake, 1 << 20, null) == lq.LQ_ERR_SHAPE
+    assert dqd(fake, 10, 256, fake, fake, fake, null, fake, fake, 1 << 20, null) == lq.LQ_ERR_ARG
+    assert dqd(fake, 10, 256, fake, fake, fake, fake, null, fake, 1 << 20, null) == lq.LQ_ERR_ARG
 
     def qw(**kw):
         d = dict(format=0, blocksize=64, N=128, K=256, codes=0x1000, absmax=0x1000, absmax_q=None,
@@ -312,6 +318,11 @@ def test_misaligned_pointers_rejected_before_launch(lq, which):
     assert L.lq_quantize_nf4(vp(a), 0, 4, 64, 64, vp(a), vp(a + 2), null) == ARG
     assert L.lq_profile_nf4(vp(a + 4), 0, 4, 4096, 64, 0.01, vp(a), vp(a), 1 << 20, null) == ARG
     assert L.lq_double_quant(vp(a + 2), 1000, 256, vp(a), vp(a), vp(a), vp(a), 1 << 20, null) == ARG
+    # double quant + dequant: the codes and the bf16 output need 16 bytes
+    for i in (0, 6, 7):
+        args = [vp(a), 1000, 256, vp(a), vp(a), vp(a), vp(a), vp(a), vp(a), 1 << 20, null]
+        args[i] = vp(a + (2 if i == 0 else 8))
+        assert L.lq_double_quant_dequant(*args) == ARG
 
     def qw(**kw):
         d = dict(format=0, blocksize=64, N=128, K=256, codes=a, absmax=a, absmax_q=None,

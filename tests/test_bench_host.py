@@ -41,6 +41,9 @@ def test_codec_bytes_follow_the_format(bench, N, K):
     consts = n // 64 + 4 * ((n // 64 + 255) // 256) + 4
     assert b["dequant"] == n // 2 + consts + 2 * n
     assert b["double_quant"] == 4 * (n // 64) + consts
+    # the two in one call: the float32 constants and the codes in, the
+    # double-quantized constants and the bf16 weight out
+    assert b["double_quant_dequant"] == 4 * (n // 64) + n // 2 + consts + 2 * n
     # decode GEMV at M tokens (t given): packed weight + X + B + H + t
     for M in (1, 4, 16):
         g = bench.codec_bytes(Layer(N, K, 16, M), M)["gemv"]

@@ -198,6 +198,33 @@ def test_dequant_bit_exact(lq, torch, double):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("N,K", [(8, 64), (300, 128), (1024, 1024), (4096, 4096), (4100, 4096)])
+def test_double_quant_dequant(lq, torch, N, K):
+    """Double quantization and dequantization in one call: the bits of the
+    two calls in turn (one kernel after the block sums up to 1024 DQ blocks,
+    4096 x 4096 being exactly that many; 4100 x 4096 has 1025 and runs the two
+    calls' kernels), and up to 1 M weights the oracle's bits (edge blocks,
+    a ragged last DQ block at 300 x 128)."""
+    rng = np.random.default_rng(N + K)
+    small = N * K <= 1 << 20
+    W = edge_weight(rng, N, K) if small else (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    codes, absmax = lq.quantize_nf4(dev(torch, W))
+    q, s2, mu, Wd = lq.double_quant_dequant(codes, absmax, (N, K))
+    q2, s22, mu2 = lq.double_quant(absmax)
+    Wd2 = lq.dequant(lq.QWeight(N, K, codes, absmax_q=q2, dq_scale=s22, dq_mean=mu2))
+    assert torch.equal(q, q2)
+    assert torch.equal(s2.view(torch.int32), s22.view(torch.int32))
+    assert torch.equal(mu.view(torch.int32), mu2.view(torch.int32))
+    assert torch.equal(Wd.view(torch.int16), Wd2.view(torch.int16))
+    if small:
+        packed, c, (oq, os2, omu), cp = oracle_qweight(W, True)
+        assert np.array_equal(host(q), oq)
+        assert np.array_equal(host(s2), os2)
+        assert host(mu)[0] == omu
+        want = nf4.dequant(packed, cp, W.shape)
+        assert np.array_equal(bf16_to_f32(Wd).view(np.uint32), want.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # forward / backward
 # ---------------------------------------------------------------------------
