@@ -4,8 +4,8 @@
 One step = the whole path on the Llama-7B q_proj workload (W 4096x4096
 float32 ~ N(0, 0.02^2), 2048 bf16 tokens = batch 4 x seq 512, LoRA r = 16,
 alpha = 32): NF4 quantize -> double quantization and dequant to bf16 (one
-call) -> forward (t = X A^T, fused dequant-GEMM + LoRA) -> backward (u, dB,
-grad_X, dA). Inputs are resident in HBM before timing; four input sets are rotated
+call) -> forward (one call: t = X A^T, fused dequant-GEMM + LoRA) ->
+backward (u, dB, grad_X, dA). Inputs are resident in HBM before timing; four input sets are rotated
 so the 256 MB Infinity Cache cannot hold the step's working set.
 
 value = algorithmic GEMM + LoRA flops of the forward and backward per step
@@ -197,13 +197,12 @@ class Calls:
 
     def step(self, ev=None):
         """One pass of the path; `ev` = (start, end) events put around the
-        forward dequant-GEMM launch on the same stream."""
+        forward call (t = X A^T, then the dequant-GEMM) on the same stream."""
         self.quantize()
         self.double_quant_dequant()
-        self.lora_down()
         if ev is not None:
             ev[0].record()
-        self.fwd_gemm()
+        self.qlora_forward()
         if ev is not None:
             ev[1].record()
         self.backward()
@@ -225,8 +224,8 @@ def make_devs(torch, lq, syn, name, n_sets, M=None, with_grad=True):
 
 
 def kernel_event_stride(steps):
-    """Steps between the timed steps whose forward dequant-GEMM gets its own
-    event pair: every 4th, or closer so that at least 5 launches are timed."""
+    """Steps between the timed steps whose forward call gets its own
+    event pair: every 4th, or closer so that at least 5 calls are timed."""
     return max(1, min(4, steps // 5))
 
 
@@ -631,7 +630,7 @@ def main():
     for i in range(args.warmup):
         calls[i % len(calls)].step()
     torch.cuda.synchronize()
-    # the forward dequant-GEMM inside the timed steps also gets event pairs
+    # the forward call inside the timed steps also gets event pairs
     # (every ev_stride-th step: each pair adds a few microseconds to its step)
     ev_stride = kernel_event_stride(args.steps)
     kev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -693,7 +692,9 @@ def main():
                        f"{len(calls)} input sets rotated, {ARM_WARMUP} warm-up launches, median batch",
                 "replicated_arm_us": round(f2[0] * 1e3, 2),
                 "noise_floor": round(abs(f1[0] - f2[0]) / (0.5 * (f1[0] + f2[0])), 4),
-                "in_step_avg_us": round(in_step_ms * 1e3, 2), "in_step_launches": len(kev),
+                "in_step_forward_call_us": round(in_step_ms * 1e3, 2), "in_step_calls": len(kev),
+                "in_step_note": "events around the whole lq_qlora_forward call inside timed steps "
+                                "(t = X A^T, then this GEMM)",
                 "algorithmic_flop_per_launch": fl["fwd_gemm"]}
     log("roofline", roofline)
 

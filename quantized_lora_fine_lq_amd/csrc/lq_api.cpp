@@ -2,6 +2,7 @@
 // kernel dispatch. No device memory is allocated here; every launch goes on
 // the caller's stream.
 #include <cmath>
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -120,14 +121,26 @@ int debug_check_weight(const QWeight& q, hipStream_t s) {
   return q.format == LQ_FMT_CODEBOOK ? debug_check_rows(q.N, q.K, q.row_bits, q.row_offset, s) : LQ_OK;
 }
 
+// Column parts of t = X A^T in the forward: only for the NF4 GEMV, which adds
+// them while staging t (the GEMM takes t whole: summing parts in its LoRA
+// step cost it registers it does not have).
+int forward_t_parts(const QWeight& w, int64_t M) {
+  return (use_gemv(w, M) && w.format == LQ_FMT_NF4) ? row_skinny_parts(M, w.K) : 1;
+}
+
+// t (as column-part partial sums), GEMM workspace
 size_t forward_ws(const QWeight& w, int64_t M, int32_t r) {
-  return align_up((size_t)M * r * sizeof(float)) + (use_gemv(w, M) ? 0 : align_up(gemm_ws_bytes(w, M, r, true)));
+  return align_up((size_t)forward_t_parts(w, M) * M * r * sizeof(float)) +
+         (use_gemv(w, M) ? 0 : align_up(gemm_ws_bytes(w, M, r, true)));
 }
 
 // u, recomputed t, B^T, split t and u, partial sums of dB and of dA, GEMM
-// workspace
+// workspace. (u and t are formed whole here: split into column parts, the
+// row-form product got 4 us faster at q_proj but the column form that adds
+// the parts 2.5 us slower.)
 size_t backward_ws(const QWeight& w, int64_t M, int32_t r) {
-  return 2 * align_up((size_t)M * r * sizeof(float)) + (r > 16 ? align_up((size_t)w.N * r * sizeof(uint16_t)) : 0) +
+  return 2 * align_up((size_t)M * r * sizeof(float)) +
+         (r > 16 ? align_up((size_t)w.N * r * sizeof(uint16_t)) : 0) +
          align_up(col_skinny_ws_floats(M, w.N, r) * sizeof(float)) +
          align_up(col_skinny_ws_floats(M, w.K, r) * sizeof(float)) + align_up(gemm_ws_bytes(w, M, r, false));
 }
@@ -317,8 +330,9 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   if (!workspace || ws_bytes < need) return LQ_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   Carver cv(workspace, ws_bytes);
-  float* t_ws = cv.take<float>((size_t)M * r);
   const bool gemv = use_gemv(q, M);
+  const int parts = forward_t_parts(q, M);
+  float* t_ws = cv.take<float>((size_t)parts * M * r);
   uint16_t* gws = gemv ? nullptr : cv.take<uint16_t>(gemm_ws_bytes(q, M, r, true) / sizeof(uint16_t));
   if (!cv.ok()) return LQ_ERR_WORKSPACE;
   if ((st = debug_check_weight(q, s)) != LQ_OK) return st;
@@ -327,10 +341,13 @@ int lq_qlora_forward(const lq_qweight* w, const uint16_t* X, int64_t M, const ui
   // decode sizes with a small NF4 weight and r <= 32: the GEMV forms t itself
   if (gemv && gemv_forms_t(q, M, r))
     return launch_status(launch_gemv_fwd(q, X, M, nullptr, B, r, scale, H, h_dtype, s, A, t));
-  hipError_t e = launch_row_skinny(X, M, q.K, A, r, t, s);
+  // t = X A^T; for the GEMV split into column parts, which the GEMV adds
+  // (storing t) while staging it
+  const float* tin = parts > 1 ? t_ws : t;
+  hipError_t e = launch_row_skinny(X, M, q.K, A, r, parts > 1 ? t_ws : t, s, parts);
   if (e != hipSuccess) return LQ_ERR_LAUNCH;
-  if (gemv) e = launch_gemv_fwd(q, X, M, t, B, r, scale, H, h_dtype, s);
-  else e = launch_gemm_fwd(q, X, M, t, B, r, scale, H, h_dtype, gws, s);
+  if (gemv) e = launch_gemv_fwd(q, X, M, tin, B, r, scale, H, h_dtype, s, nullptr, t_save, parts);
+  else e = launch_gemm_fwd(q, X, M, tin, B, r, scale, H, h_dtype, gws, s);
   return launch_status(e);
 }
 

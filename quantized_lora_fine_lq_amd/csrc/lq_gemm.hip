@@ -36,6 +36,7 @@ namespace {
 // k = 32h + 8s + e in sub-step s, a permutation of k that both operands share.
 // ===========================================================================
 constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int kCusPerXcd = 32;   // MI355X: 8 XCDs of 32 CUs
 constexpr int PITCH = BK + 8;  // bf16 per LDS row: 144 bytes, conflict-free b128 access
 constexpr int GEMM_THREADS = 512;
 
@@ -713,7 +714,9 @@ __global__ __launch_bounds__(256) void k_split_fixup(GemmParams p, int64_t n_spl
 struct GemvParams {
   const uint16_t* X;   // [M, K]
   int64_t M;
-  const float* t;      // [M, r], or null when the kernel forms t = X A^T itself
+  const float* t;      // [M, r] as tparts partial sums [tparts][M][r], or null when the kernel forms
+                       // t = X A^T itself
+  int tparts;
   const uint16_t* B;   // [N, r]
   int r;
   float s;
@@ -721,7 +724,8 @@ struct GemvParams {
   QWeight w;
   Nf4Levels lv;
   const uint16_t* A;   // [r, K] (t formed in the kernel)
-  float* t_out;        // [M, r]: t, written by workgroup 0 (t formed in the kernel), or null
+  float* t_out;        // [M, r]: t, written by workgroup 0 (formed in the kernel, or summed from
+                       // tparts > 1 partial sums), or null
 };
 
 // t = X A^T inside the NF4 decode kernel, for r <= GV_TR: every workgroup
@@ -855,7 +859,7 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
     f32x2_t pair[256];
     float c[GV_CTAB];   // constants [16 RG rows][nb + 1]; then partial sums
     f32x4_t tp[TK ? GV_WAVES * JTK * 64 : 1];   // TK: the waves' partial sums of t
-    float t[TK ? 16 * GV_TR : 1];              // TK: t [16 tokens][r]
+    float t[16 * 128];                         // t [tokens][r]
   };
   __shared__ Lds lds;
   f32x2_t* sPair = lds.pair;
@@ -952,6 +956,16 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
     }
 #pragma unroll
     for (int jt = 0; jt < JTK; ++jt) lds.tp[(wave * JTK + jt) * 64 + lane] = tacc[jt];
+  } else {
+    // t given: staged in LDS for the LoRA step, the sum of its tparts
+    // partial sums in part order (stored by workgroup 0 when t_out is set)
+    const int64_t nt = p.M * p.r;
+    for (int idx = threadIdx.x; idx < nt; idx += 64 * GV_WAVES) {
+      float v = p.t[idx];
+      for (int k = 1; k < p.tparts; ++k) v += p.t[k * nt + idx];
+      lds.t[idx] = v;
+      if (blockIdx.x == 0 && p.t_out) p.t_out[idx] = v;
+    }
   }
   __syncthreads();
   if constexpr (TK) {
@@ -971,11 +985,10 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
 
   // the LoRA operands are loaded only now, one row group at a time: held
   // through the table build they would cost registers
-  const float* tsrc = TK ? lds.t : p.t;
   f32x4_t acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
-    acc[g] = gv_lora_mfma(gv_lora_load(tsrc, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
+    acc[g] = gv_lora_mfma(gv_lora_load(lds.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
                           f32x4_t{0.f, 0.f, 0.f, 0.f});
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1211,7 +1224,7 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_codebook(GemvParams p
 // wave itself touches the area, and its LDS operations run in order).
 constexpr int RS_TP = 72;   // bf16 per row of the transposed tile (144 bytes)
 
-template <int JT, int W, int RT>
+template <int JT, int W, int RT, int UB>
 __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restrict__ Q, int64_t M, int64_t C,
                                                        const uint16_t* __restrict__ R, int r,
                                                        float* __restrict__ out) {
@@ -1226,9 +1239,14 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
   const uint16_t* rrow[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) rrow[jt] = RT ? R : R + (int64_t)min(16 * jt + li, r - 1) * C + 16 * lg;
+  // column part blockIdx.y of gridDim.y: a contiguous range of 64-column
+  // blocks, its partial sums stored at out + part * M * r
   const int64_t blocks = (C + 63) / 64;
-  const int64_t per = (blocks + W - 1) / W;
-  const int64_t b_begin = min(blocks, wave * per), b_end = min(blocks, b_begin + per);
+  const int64_t bpp = (blocks + gridDim.y - 1) / gridDim.y;
+  const int64_t p_begin = min(blocks, (int64_t)blockIdx.y * bpp), p_end = min(blocks, p_begin + bpp);
+  const int64_t per = (p_end - p_begin + W - 1) / W;
+  const int64_t b_begin = min(p_end, p_begin + wave * per), b_end = min(p_end, b_begin + per);
+  out += (int64_t)blockIdx.y * M * r;
   f32x4_t acc[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1274,8 +1292,10 @@ __global__ __launch_bounds__(64 * W) void k_row_skinny(const uint16_t* __restric
       mma(a1, b1);
     }
   }
-  // 64-column blocks with loads in flight together
-  constexpr int U = RT ? (JT == 1 ? 4 : (JT == 2 ? 2 : 1)) : (JT <= 2 ? 4 : 1);
+  // UB 64-column blocks with loads in flight together (every lane issues the
+  // loads of all UB blocks, live or not, and the time follows that count:
+  // the launcher sizes UB to the blocks a wave has)
+  constexpr int U = PIPE ? 1 : UB;
   for (int64_t bk = b_begin; !PIPE && bk < b_end; bk += U) {
     u32x4_t a[U][2], b[U][2][JT];
 #pragma unroll
@@ -1562,12 +1582,48 @@ int col_skinny_splits(int64_t M, int64_t C) {
 
 }  // namespace
 
+// A workgroup's time follows the load instructions its waves issue (about
+// 3 us + 0.4 us per 16 loads of a wave, the waves' loads taking turns), so
+// the columns are split into parts while the row groups leave CUs idle: at
+// 2048 rows (128 row groups) and 4096 columns two parts take 5.8 instead of
+// 9.4 us. Each part keeps at least one 64-column block per wave; at most 4.
+int row_skinny_parts(int64_t M, int64_t C) {
+  const int64_t groups = (M + 15) / 16, blocks = (C + 63) / 64;
+  int P = 1;
+  while (P < 4 && groups * 2 * P <= 8 * kCusPerXcd && blocks / (2 * P) >= 16) P *= 2;
+  return P;
+}
+
+// Blocks in flight per wave: as many as a wave has (1, 2 or 4; more take
+// further rounds).
+static int row_skinny_ub(int64_t C, int parts, int W) {
+  const int64_t blocks = (C + 63) / 64, bpp = (blocks + parts - 1) / parts, per = (bpp + W - 1) / W;
+  return per <= 1 ? 1 : (per <= 2 ? 2 : 4);
+}
+
 hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r, float* out,
-                             hipStream_t s) {
-  const dim3 grid((unsigned)((M + 15) / 16));
-  switch ((r + 15) / 16) {
-#define LQ_RS(JT, W) case JT: hipLaunchKernelGGL((k_row_skinny<JT, W, 0>), grid, dim3(64 * W), 0, s, Q, M, C, R, r, out); break;
-    LQ_RS(1, 16) LQ_RS(2, 16) LQ_RS(3, 8) LQ_RS(4, 8) LQ_RS(5, 8) LQ_RS(6, 8) LQ_RS(7, 8) LQ_RS(8, 8)
+                             hipStream_t s, int parts) {
+  if (parts < 1 || parts > 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + 15) / 16), (unsigned)parts);
+  const int jt = (r + 15) / 16;
+  if (jt <= 2) {
+    const int ub = row_skinny_ub(C, parts, 16);
+#define LQ_RS(JT, UB) hipLaunchKernelGGL((k_row_skinny<JT, 16, 0, UB>), grid, dim3(1024), 0, s, Q, M, C, R, r, out)
+    if (jt == 1) {
+      if (ub == 1) LQ_RS(1, 1);
+      else if (ub == 2) LQ_RS(1, 2);
+      else LQ_RS(1, 4);
+    } else {
+      if (ub == 1) LQ_RS(2, 1);
+      else if (ub == 2) LQ_RS(2, 2);
+      else LQ_RS(2, 4);
+    }
+#undef LQ_RS
+    return hipGetLastError();
+  }
+  switch (jt) {
+#define LQ_RS(JT) case JT: hipLaunchKernelGGL((k_row_skinny<JT, 8, 0, 1>), grid, dim3(512), 0, s, Q, M, C, R, r, out); break;
+    LQ_RS(3) LQ_RS(4) LQ_RS(5) LQ_RS(6) LQ_RS(7) LQ_RS(8)
 #undef LQ_RS
     default: return hipErrorInvalidValue;
   }
@@ -1578,11 +1634,21 @@ hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint
 // pays only while that is small: r <= 16 (at r = 64 over 11008 columns it
 // cost more than a separate transpose launch).
 hipError_t launch_row_skinny_rt(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rt, int r, float* out,
-                                hipStream_t s) {
-  if (r > 16) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((M + 15) / 16));
-  if (r % 8 == 0) hipLaunchKernelGGL((k_row_skinny<1, 16, 1>), grid, dim3(1024), 0, s, Q, M, C, Rt, r, out);
-  else hipLaunchKernelGGL((k_row_skinny<1, 16, 2>), grid, dim3(1024), 0, s, Q, M, C, Rt, r, out);
+                                hipStream_t s, int parts) {
+  if (r > 16 || parts < 1 || parts > 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((M + 15) / 16), (unsigned)parts);
+  const int ub = row_skinny_ub(C, parts, 16);
+#define LQ_RS(RT, UB) hipLaunchKernelGGL((k_row_skinny<1, 16, RT, UB>), grid, dim3(1024), 0, s, Q, M, C, Rt, r, out)
+  if (r % 8 == 0) {
+    if (ub == 1) LQ_RS(1, 1);
+    else if (ub == 2) LQ_RS(1, 2);
+    else LQ_RS(1, 4);
+  } else {
+    if (ub == 1) LQ_RS(2, 1);
+    else if (ub == 2) LQ_RS(2, 2);
+    else LQ_RS(2, 4);
+  }
+#undef LQ_RS
   return hipGetLastError();
 }
 
@@ -1657,10 +1723,9 @@ int lora_seg_cols(int r) { return BK * ((2 * r + BK - 1) / BK); }
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// The GEMM's schedule on MI355X: 256 CUs in 8 XCDs of 32, one workgroup per
-// CU. Tiles are split only when each XCD has at least one full round and
-// the contraction has at least 16 steps.
-constexpr int kCusPerXcd = 32;
+// The GEMM's schedule on MI355X (256 CUs in 8 XCDs of 32, kCusPerXcd), one
+// workgroup per CU. Tiles are split only when each XCD has at least one full
+// round and the contraction has at least 16 steps.
 static int split_cpx(int64_t M, int64_t Ncols, int64_t Kc) {
   return (Kc + BK - 1) / BK >= 16 ? kCusPerXcd : 0;
 }
@@ -1852,15 +1917,18 @@ static void launch_gemv_rg(const GemvParams& p, bool dq, bool f32, hipStream_t s
 
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
-                           hipStream_t st, const uint16_t* A, float* t_out) {
+                           hipStream_t st, const uint16_t* A, float* t_out, int t_parts) {
   if (!gemv_supported(w)) return hipErrorInvalidValue;
   GemvParams p;
   p.X = X; p.M = M; p.t = t; p.B = B; p.r = r; p.s = s; p.out = H; p.w = w; p.lv = tables().lv;
-  p.A = A; p.t_out = t_out;
   const bool tk = t == nullptr;   // form t = X A^T in the kernel (NF4, r <= GV_TR)
+  p.tparts = tk ? 1 : t_parts;
+  p.A = A;
+  p.t_out = (tk || t_parts > 1) ? t_out : nullptr;
   if (tk && (w.format != LQ_FMT_NF4 || !A || r > GV_TR)) return hipErrorInvalidValue;
   const bool dq = w.qc.absmax == nullptr, f32 = h_dtype == LQ_F32;
   if (w.format == LQ_FMT_CODEBOOK) {
+    if (p.tparts != 1) return hipErrorInvalidValue;   // the codebook kernel reads t as given
     const size_t lds = cb_gemv_lds_bytes(w.K);
     const dim3 grid((unsigned)((w.N + 15) / 16)), block(64 * GV_WAVES);
     LQ_DASSERT(M >= 1 && M <= 16 && w.K % 64 == 0 && lds <= 65536);

@@ -133,10 +133,14 @@ hipError_t launch_quantize_codebook(const void* W, int dtype, int64_t N, int64_t
 // Skinny products. Row form: out[m][j] = sum_c Q[m][c] * R[j][c] with R
 // [r, C] row-major (C % 8 == 0); one launch, no workspace. The _rt variant
 // (r <= 16) takes the second operand transposed, Rt [C, r] row-major (u = G B).
+// With parts > 1 (at most 4) the columns are split into that many ranges and
+// out holds their partial sums [parts][M][r], which the consumers add in
+// part order; row_skinny_parts(M, C) is the split the layer entry points use.
+int row_skinny_parts(int64_t M, int64_t C);
 hipError_t launch_row_skinny(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* R, int r,
-                             float* out, hipStream_t s);
+                             float* out, hipStream_t s, int parts = 1);
 hipError_t launch_row_skinny_rt(const uint16_t* Q, int64_t M, int64_t C, const uint16_t* Rt, int r,
-                                float* out, hipStream_t s);
+                                float* out, hipStream_t s, int parts = 1);
 hipError_t launch_transpose_u16(const uint16_t* in, int64_t N, int r, uint16_t* out, hipStream_t s);
 // Column form: out(j, c) = scale * sum_m P[m][j] * Q[m][c] with P float32
 // [M, r] row-major; written as
@@ -194,9 +198,11 @@ bool gemv_supported(const QWeight& w);
 bool gemv_forms_t(const QWeight& w, int64_t M, int r);
 // t == nullptr: the kernel forms t = X A^T itself (NF4 weights, r <= 32) and
 // writes it to t_out when that is not null; gemv_forms_t says when that is
-// the faster choice.
+// the faster choice. t given as t_parts > 1 partial sums: their sum is
+// written to t_out when that is not null.
 hipError_t launch_gemv_fwd(const QWeight& w, const uint16_t* X, int64_t M, const float* t,
                            const uint16_t* B, int r, float s, void* H, int h_dtype,
-                           hipStream_t st, const uint16_t* A = nullptr, float* t_out = nullptr);
+                           hipStream_t st, const uint16_t* A = nullptr, float* t_out = nullptr,
+                           int t_parts = 1);
 
 }  // namespace lq

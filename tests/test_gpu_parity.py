@@ -253,6 +253,9 @@ def oracle_wd(W, double=True):
     (256, 512, 16, 32, 8.0),       # GEMV forming t itself at its largest rank
     (300, 1088, 7, 17, 16.0),      # same, two column tiles of t, odd K/64, ragged N
     (200, 256, 9, 33, 16.0),       # rank just past that: t from the separate kernel
+    (520, 4096, 40, 24, 16.0),     # GEMM path, t over four 64-column blocks per wave
+    (8200, 4096, 5, 24, 16.0),     # t in four column parts, added (and stored) by the GEMV
+    (8200, 2112, 3, 40, 16.0),     # t in two column parts (one ragged), three 16-wide tiles
 ])
 def test_forward(lq, torch, N, K, M, r, alpha):
     L, W, X, A, B = make_layer(100 + M, N, K, M, r, alpha)
@@ -376,6 +379,9 @@ def test_unit_vector_probe_bit_exact(lq, torch, M):
     (200, 192, 45, 5, 10.0),       # r % 8 != 0: B rows read element by element in u = G B
     (264, 320, 37, 13, 16.0),      # r % 8 != 0, N % 64 != 0
     (136, 128, 40, 100, 16.0),     # r % 8 != 0 with seven 16-wide tiles
+    (4104, 256, 24, 16, 32.0),     # u over 65 column blocks (two rounds of four per wave), B as given
+    (4104, 256, 24, 40, 16.0),     # same, B transposed first
+    (520, 4096, 40, 16, 32.0),     # recomputed t over 64 column blocks
 ])
 @pytest.mark.parametrize("recompute_t", [False, True])
 def test_backward(lq, torch, N, K, M, r, alpha, recompute_t):
