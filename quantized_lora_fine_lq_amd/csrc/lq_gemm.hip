@@ -90,6 +90,7 @@ struct GemmParams {
   int r;
   float s;             // alpha / r
   int fwd;             // 1: Lb(n, j) = B[n][j]; 0: Lb(n, j) = A[j][n]
+  int lvec;            // 1: r % 8 == 0 and L 16-byte aligned (the segment tiles use 16-byte loads)
   int R2;              // 64 * ceil(2r / 64) columns of the LoRA segment
   int gm;              // M-tiles per group of the tile order
   void* out;           // [M, Ncols]
@@ -204,46 +205,88 @@ __device__ __forceinline__ void mfma_half(const uint16_t* sAt, const uint16_t* s
 // uses the main A tiles' thread mapping and row clamping; the Bt-side tile
 // maps thread -> row t/4, columns 16 (t % 4) .. +16 (rows past Ncols repeat
 // the last one: their outputs are never stored).
+//
+// Segment column c reads element seg_src(c, r) of its row: c, c - r, or 0
+// for a zero column (a valid element either way, zeroed afterwards), so no
+// load sits behind a branch. With r % 8 == 0 an aligned run of 8 segment
+// columns lies inside one part (hi, lo or zero) and is 8 consecutive elements
+// of the row, read as 16-byte loads when the rows are 16-byte aligned
+// (lvec: L, and B's rows in the forward). On this GPU 4-byte loads of whole
+// 256- and 512-byte rows (r = 64, 128) cost 10 us and more per step.
+__device__ __forceinline__ int seg_src(int c, int r) { return c < r ? c : (c < 2 * r ? c - r : 0); }
+
 template <bool SWZ>
 __device__ __forceinline__ void lora_tiles(const GemmParams& p, int jt, int64_t m0, int64_t n0,
                                            uint16_t* sA, uint16_t* sB) {
   const int cA = BK * jt + 8 * (threadIdx.x & 7);
+  float lv[4][8];
+  if (p.lvec) {
+    const int off = seg_src(cA, p.r);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* lrow = p.L + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.r + off;
+      const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(lrow);
+      const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(lrow + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lv[q][e] = v0[e];
+        lv[q][4 + e] = v1[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* lrow = p.L + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lv[q][e] = lrow[seg_src(cA + e, p.r)];
+    }
+  }
+  const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
+  const int64_t n = min(n0 + row, p.Ncols - 1);
+  const int cB = BK * jt + 16 * qq;
+  u32x4_t hb[2];
+  if (p.fwd && p.lvec) {
+    // B[n][.]: 8 bf16 of one part per 16-byte load, already in the tile's word order
+    const uint16_t* brow = p.lb + n * p.r;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) hb[hh] = ld16(brow + seg_src(cB + 8 * hh, p.r));
+  } else {
+    // Lb(n, j): B[n][j] (row n of B, stride 1) or A[j][n] (column n of A, stride Ncols)
+    const uint16_t* lbn = p.lb + (p.fwd ? n * p.r : n);
+    const int64_t lbs = p.fwd ? 1 : p.Ncols;
+    uint32_t h[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) h[e] = lbn[seg_src(cB + e, p.r) * lbs];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      hb[hh] = u32x4_t{h[8 * hh] | (h[8 * hh + 1] << 16), h[8 * hh + 2] | (h[8 * hh + 3] << 16),
+                       h[8 * hh + 4] | (h[8 * hh + 5] << 16), h[8 * hh + 6] | (h[8 * hh + 7] << 16)};
+  }
   u32x4_t ra[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float* lrow = p.L + min(m0 + (threadIdx.x >> 3) + 64 * q, p.M - 1) * p.r;
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = cA + e;
-      float x = 0.0f;
-      if (c < 2 * p.r) {
-        float hi, lo;
-        split_bf16(p.s * lrow[c < p.r ? c : c - p.r], hi, lo);
-        x = (c < p.r) ? hi : lo;
-      }
-      v[e] = x;
+      float hi, lo;
+      split_bf16(p.s * lv[q][e], hi, lo);
+      v[e] = c < p.r ? hi : (c < 2 * p.r ? lo : 0.0f);
     }
     ra[q] = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
   }
-  const int row = threadIdx.x >> 2, qq = threadIdx.x & 3;
-  const int64_t n = min(n0 + row, p.Ncols - 1);
-  uint32_t h[16];
+  // zero columns (c >= 2r) of the Bt side, 16-bit element by element
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int c = BK * jt + 16 * qq + e;
-    uint32_t x = 0;
-    if (c < 2 * p.r) {
-      const int j = c < p.r ? c : c - p.r;
-      x = p.fwd ? p.lb[n * p.r + j] : p.lb[(int64_t)j * p.Ncols + n];
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = cB + 8 * hh + 2 * w;
+      const uint32_t keep = (c < 2 * p.r ? 0x0000FFFFu : 0u) | (c + 1 < 2 * p.r ? 0xFFFF0000u : 0u);
+      hb[hh][w] &= keep;
     }
-    h[e] = x;
-  }
   store_a_tile(sA, ra);
-  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq) ^ bsw<SWZ>(row))) =
-      u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq + 1) ^ bsw<SWZ>(row))) =
-      u32x4_t{h[8] | (h[9] << 16), h[10] | (h[11] << 16), h[12] | (h[13] << 16), h[14] | (h[15] << 16)};
+  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq) ^ bsw<SWZ>(row))) = hb[0];
+  *reinterpret_cast<u32x4_t*>(sB + row * PITCH + 8 * ((2 * qq + 1) ^ bsw<SWZ>(row))) = hb[1];
 }
 
 // ---- Bt producers -----------------------------------------------------------
@@ -1776,13 +1819,14 @@ static void set_lora(GemmParams& p, const float* L, const uint16_t* lb, int r, f
   p.s = s;
   p.fwd = fwd ? 1 : 0;
   p.R2 = lora_seg_cols(r);
+  p.lvec = (r % 8 == 0 && reinterpret_cast<uintptr_t>(L) % 16 == 0) ? 1 : 0;
 }
 
 static GemmParams make_params(const QWeight& w, const uint16_t* A, int64_t M, int64_t Ncols, int64_t Kc,
                               void* out) {
   GemmParams p;
   p.A = A; p.M = M; p.Ncols = Ncols; p.Kc = Kc; p.out = out;
-  p.L = nullptr; p.lb = nullptr; p.r = 0; p.s = 0.0f; p.fwd = 1; p.R2 = 0;
+  p.L = nullptr; p.lb = nullptr; p.r = 0; p.s = 0.0f; p.fwd = 1; p.R2 = 0; p.lvec = 0;
   // 32 workgroups are resident per XCD: 2 A row-tiles x 16 weight tiles
   // minimise the bytes they pull into the XCD's L2.
   p.gm = (int)std::min<int64_t>(2, (M + BM - 1) / BM);

@@ -316,6 +316,50 @@ def test_forward_gemm_and_gemv_agree_at_boundary(lq, torch, monkeypatch):
     assert layer.rel_frobenius(host(H2), Href) <= F32_TOL
 
 
+@pytest.mark.parametrize("r", [8, 12, 40, 64, 128])
+def test_lora_segment_load_paths(lq, torch, r):
+    """The LoRA segment of both dequant-GEMMs (QLoRA page, introduction: the
+    s t B^T and s u A terms) reads t / u with 16-byte loads when r % 8 == 0 and
+    the array is 16-byte aligned, element by element otherwise. The same values
+    at a 4-byte offset (legal: t and u need only their natural alignment) take
+    the element path: outputs bit-identical to the aligned call, and both
+    against the oracle. r = 12 takes the element path either way."""
+    N, K, M, alpha = 264, 320, 300, 16.0
+    rng = np.random.default_rng(7100 + r)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    X = syn.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    G = syn.to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    A = syn.to_bf16_bits((rng.standard_normal((r, K)) * 0.05).astype(np.float32))
+    B = syn.to_bf16_bits((rng.standard_normal((N, r)) * 0.05).astype(np.float32))
+    t = rng.standard_normal((M, r)).astype(np.float32)
+    u = rng.standard_normal((M, r)).astype(np.float32)
+    qw = lq.QWeight.from_weight(dev(torch, W))
+    Xd, Gd, Ad, Bd = (bf16_dev(torch, a) for a in (X, G, A, B))
+
+    def placed(a, off):
+        buf = torch.zeros(a.size + 4, dtype=torch.float32, device="cuda")
+        v = buf[off:off + a.size].view(a.shape)
+        v.copy_(torch.from_numpy(a))
+        return v
+
+    t0, t1, u0, u1 = placed(t, 0), placed(t, 1), placed(u, 0), placed(u, 1)
+    assert t0.data_ptr() % 16 == 0 and t1.data_ptr() % 16 == 4
+    H0 = lq.dequant_gemm(qw, Xd, t0, Bd, alpha, out_dtype=torch.float32)
+    H1 = lq.dequant_gemm(qw, Xd, t1, Bd, alpha, out_dtype=torch.float32)
+    gx0 = lq.dequant_gemm_t(qw, Gd, u0, Ad, alpha)
+    gx1 = lq.dequant_gemm_t(qw, Gd, u1, Ad, alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(H0, H1) and torch.equal(gx0, gx1)
+    Wd = oracle_wd(W).astype(np.float64)
+    s = alpha / r
+    Xf, Gf = syn.bf16_bits_to_f32(X).astype(np.float64), syn.bf16_bits_to_f32(G).astype(np.float64)
+    Af, Bf = syn.bf16_bits_to_f32(A).astype(np.float64), syn.bf16_bits_to_f32(B).astype(np.float64)
+    Href = Xf @ Wd.T + s * (t.astype(np.float64) @ Bf.T)
+    gref = Gf @ Wd + s * (u.astype(np.float64) @ Af)
+    assert layer.rel_frobenius(host(H0), Href) <= F32_TOL
+    assert layer.rel_frobenius(bf16_to_f32(gx0), gref) <= BF16_TOL
+
+
 @pytest.mark.parametrize("N,K,M,r,double", [
     (16384, 256, 16, 16, True),    # 4 row groups per workgroup, K/64 not a multiple of 16
     (24576, 1024, 2, 16, True),    # 4 row groups at M <= 4
