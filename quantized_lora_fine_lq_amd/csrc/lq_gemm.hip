@@ -825,16 +825,31 @@ __device__ __forceinline__ u32x4_t dequant8_pair(uint32_t w, const f32x2_t* sPai
 // [B | B], taken in 32-column chunks, chunk w by wave w (r <= 128: at most 8
 // chunks). Lane (li, lg) supplies token li (rows past M repeat row M - 1)
 // and weight row `row` at columns 32 w + 8 lg + [0, 8); columns past 2r
-// are zero (waves past the last chunk add an all-zero product: no branch,
-// which keeps the kernels within the register budget of two workgroups per
-// CU). gv_lora_mfma adds the chunk to the wave's accumulator.
+// are zero. Waves whose whole chunk lies past 2r skip the loads (a
+// wave-uniform test, gv_lora_live) and add nothing. Every load reads a valid
+// element (a zero column reads column 0 and is masked after), so none sits
+// behind a branch: the compiler would otherwise wait for each guarded load
+// inside its branch, one latency per element. gv_lora_mfma adds the chunk to
+// the wave's accumulator.
 struct GvLora {
   u32x4_t a, b;
 };
+__device__ __forceinline__ bool gv_lora_live(int wave, int r) { return 32 * wave < 2 * r; }
 __device__ __forceinline__ GvLora gv_lora_load(const float* t, const uint16_t* B, int64_t M, int r, float s,
                                                int wave, int li, int lg, int64_t row) {
   const float* trow = t + min((int64_t)li, M - 1) * r;
   const uint16_t* brow = B + row * r;
+  float tv[4][2];
+  uint32_t bw[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 32 * wave + 8 * lg + 2 * q + e;
+      const int j = c < r ? c : (c < 2 * r ? c - r : 0);
+      tv[q][e] = trow[j];
+      bw[q][e] = brow[j];
+    }
   GvLora o;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -844,11 +859,10 @@ __device__ __forceinline__ GvLora gv_lora_load(const float* t, const uint16_t* B
     for (int e = 0; e < 2; ++e) {
       const int c = 32 * wave + 8 * lg + 2 * q + e;
       const bool in = c < 2 * r;
-      const int j = !in ? 0 : (c < r ? c : c - r);
       float hi, lo;
-      split_bf16(s * trow[j], hi, lo);
+      split_bf16(s * tv[q][e], hi, lo);
       av[e] = !in ? 0.0f : (c < r ? hi : lo);
-      bv[e] = in ? (uint32_t)brow[j] : 0u;
+      bv[e] = in ? bw[q][e] : 0u;
     }
     o.a[q] = pack_bf16x2(av[0], av[1]);
     o.b[q] = bv[0] | (bv[1] << 16);
@@ -1026,15 +1040,21 @@ __global__ __launch_bounds__(64 * GV_WAVES, 2) void k_gemv_nf4(GemvParams p) {
     __syncthreads();
   }
 
-  // the LoRA operands are loaded only now, one row group at a time: held
-  // through the table build they would cost registers
+  // the LoRA operands are loaded only now (held through the table build they
+  // would cost registers), all row groups' loads before the first MFMA
   f32x4_t acc[RG];
+  if (gv_lora_live(wave, p.r)) {
+    GvLora lo[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    acc[g] = gv_lora_mfma(gv_lora_load(lds.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1)),
-                          f32x4_t{0.f, 0.f, 0.f, 0.f});
-    __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < RG; ++g)
+      lo[g] = gv_lora_load(lds.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + 16 * g + li, N - 1));
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g] = gv_lora_mfma(lo[g], f32x4_t{0.f, 0.f, 0.f, 0.f});
+  } else {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // The scheduling barriers keep each stage's loads where they are issued
   // (left alone, the compiler sinks them next to their first use and the
@@ -1161,7 +1181,9 @@ __device__ __forceinline__ f32x4_t cb_body(const GemvParams& p, unsigned char* l
 
   CbStage s0, s1;
   cb_load<PB>(rowp, bw, xrow, lg, wave, ns, ns, nb, s0);   // out before the tables are built
-  const GvLora lr = gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + li, N - 1));
+  const bool lora_live = gv_lora_live(wave, p.r);
+  GvLora lr{};
+  if (lora_live) lr = gv_lora_load(p.t, p.B, p.M, p.r, p.s, wave, li, lg, min(n0 + li, N - 1));
 
   if (threadIdx.x < 256) sLv[threadIdx.x] = p.w.levels[min(n0 + (threadIdx.x >> 4), N - 1) * 16 + (threadIdx.x & 15)];
   const float mean = DQ ? *p.w.qc.dq_mean : 0.0f;
@@ -1190,7 +1212,7 @@ __device__ __forceinline__ f32x4_t cb_body(const GemvParams& p, unsigned char* l
   __syncthreads();
 
   const f32x2_t* tab = sTab + li * CB_TAB;
-  f32x4_t acc = gv_lora_mfma(lr, f32x4_t{0.f, 0.f, 0.f, 0.f});
+  f32x4_t acc = lora_live ? gv_lora_mfma(lr, f32x4_t{0.f, 0.f, 0.f, 0.f}) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < nsw; i += 2) {
     cb_load<PB>(rowp, bw, xrow, lg, wave + GV_WAVES * (i + 1), ns, ns, nb, s1);
     __builtin_amdgcn_sched_barrier(0);
