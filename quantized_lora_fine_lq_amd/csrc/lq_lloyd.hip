@@ -165,12 +165,16 @@ __global__ __launch_bounds__(NT) void k_lloyd(const Tin* __restrict__ W, int64_t
   uint64_t k[16];
   {
     const int e0 = t * 16;
-    const Tin* Wr = W + row * K + e0;
+    // threads past the row read its last 16 elements and zero them, so no
+    // load sits behind a branch (the compiler would wait for each one inside it)
+    const Tin* Wr = W + row * K + min(e0, Ki - 16);
     float w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = load_w<Tin>(Wr + i);
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      w[i] = (e0 < Ki) ? load_w<Tin>(Wr + i) : 0.0f;
+      if (e0 >= Ki) w[i] = 0.0f;
       m = fmaxf(m, fabsf(w[i]));
     }
     m = fmaxf(m, dpp_f32<DPP_QUAD_XOR1>(m));
